@@ -1,0 +1,26 @@
+"""CPU oracle for retention-scored KV eviction and renormalised decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package smoke check and the
+benchmark's CPU-baseline leg may import this package.  The HIP library never
+links, imports or calls it, and it shares no code with the HIP library.
+
+``reference`` is the plain, slow definition of every step in float64 (numpy),
+written from the pages:
+
+* "Make Each Token Count" (DBTrimKV): Method 2, geometric retention
+  r = beta^(t-i); Method 3, one global budget over every layer and head;
+  Method 4, paged per-head variable-length KV.
+* "Cache What Lasts" (TRIM-KV): Technical summary section 2, the retention
+  gate (beta in [0,1]), exponential decay beta^(t-i), evicting the lowest
+  current score when the budget M is exceeded.
+* "Trust the Mass" (ContourKV): Problem definition (renormalised forced
+  weights over the retained set), Method 1 (e_s(A)), Method 3 (dropped-mass
+  statistic and allocation).
+
+``brute`` restates selection and attention in pure Python for tiny inputs.
+
+Parity status: every function is pinned by the CPU tests in
+``tests/test_oracle_pins.py`` except the readings listed there as
+"parity unpinned" (tie direction, compaction layout, page-table format,
+allocation remainder rule), which only the written specification fixes.
+"""

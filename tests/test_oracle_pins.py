@@ -1,0 +1,428 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each block names the passage it follows.  Expected values come from closed
+forms, library routines (mpmath, torch.softmax in float64), exact rationals
+or brute force, never from the oracle itself.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import mpmath
+import numpy as np
+import pytest
+import torch
+
+from oracle import brute
+from oracle import reference as ref
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------------
+# helpers: an independent round-to-nearest float32 of an mpmath value
+# --------------------------------------------------------------------------
+def rn32(x: mpmath.mpf) -> np.float32:
+    if mpmath.isinf(x):
+        return np.float32(-np.inf if x < 0 else np.inf)
+    f0 = np.float32(float(x))
+    best = None
+    for c in (np.nextafter(f0, np.float32(-np.inf)), f0, np.nextafter(f0, np.float32(np.inf))):
+        d = abs(mpmath.mpf(float(c)) - x)
+        if best is None or d < best[1] or (d == best[1] and (int(np.float32(c).view(np.uint32)) & 1) == 0):
+            best = (c, d)
+    return np.float32(best[0])
+
+
+def mp_ln32(b: float) -> np.float32:
+    with mpmath.workdps(50):
+        if b == 0.0:
+            return np.float32(-np.inf)
+        return rn32(mpmath.log(mpmath.mpf(float(b))))
+
+
+def bits(a):
+    return np.asarray(a, np.float32).view(np.uint32)
+
+
+# --------------------------------------------------------------------------
+# a0: ln beta (DBTrimKV Method 2; TRIM-KV section 2, beta in [0,1])
+# --------------------------------------------------------------------------
+def test_ln_beta_special_values():
+    out = ref.ln_beta(np.array([1.0, 0.0], np.float32))
+    assert bits(out)[0] == 0, "beta = 1 must give +0.0 (no decay)"
+    assert out[1] == -np.inf, "beta = 0 must give -inf (forgotten at once)"
+
+
+def test_ln_beta_powers_of_two_closed_form():
+    # ln(2^-k) = -k ln 2, including subnormal beta
+    ks = np.arange(1, 150)
+    beta = np.ldexp(np.float32(1.0), -ks).astype(np.float32)
+    got = ref.ln_beta(beta)
+    with mpmath.workdps(50):
+        want = np.array([rn32(-int(k) * mpmath.log(2)) for k in ks], np.float32)
+    assert np.array_equal(bits(got), bits(want))
+
+
+# Inputs whose ln lies within 4 float64 ulps of a float32 rounding midpoint
+# (found by an exhaustive quad-precision scan of (0,1)); a plain
+# "float64 log then round" gets some of these wrong.
+HARD_LN_INPUTS = [0x064cb44b, 0x07c060fa, 0x0dc8bba4, 0x0f61ff63, 0x111c87f8, 0x145cb6d4,
+                  0x16c5ee7a, 0x1a8446cb, 0x1f116ab8, 0x2423c085, 0x28e3fa26, 0x29e6126b,
+                  0x29fd22f8, 0x2c4c24b7, 0x2e492984, 0x38dcbe38, 0x3bf86ef0, 0x3c413d3a]
+
+
+def test_ln_beta_hard_rounding_cases():
+    beta = np.array(HARD_LN_INPUTS, np.uint32).view(np.float32)
+    got = ref.ln_beta(beta)
+    want = np.array([mp_ln32(float(b)) for b in beta], np.float32)
+    assert np.array_equal(bits(got), bits(want))
+
+
+def test_ln_beta_random_correctly_rounded():
+    rng = np.random.default_rng(7)
+    beta = np.concatenate([
+        rng.beta(2, 2, 1500), rng.beta(50, 1, 1500), rng.beta(1, 20, 500),
+        1.0 - rng.random(300) * 1e-6,                                   # very close to 1
+    ]).astype(np.float32)
+    # plus raw float32 bit patterns over [0, 1]
+    beta = np.concatenate([beta, rng.integers(0, 0x3F800000, 2000, dtype=np.uint32).view(np.float32)])
+    got = ref.ln_beta(beta)
+    want = np.array([mp_ln32(float(b)) for b in beta], np.float32)
+    assert np.array_equal(bits(got), bits(want))
+
+
+def test_ln_beta_monotone():
+    rng = np.random.default_rng(8)
+    beta = np.sort(rng.random(20000).astype(np.float32))
+    assert np.all(np.diff(ref.ln_beta(beta).astype(np.float64)) >= 0)
+
+
+# --------------------------------------------------------------------------
+# a1: scores (DBTrimKV Method 2; TRIM-KV section 2, decay beta^(t-i))
+# --------------------------------------------------------------------------
+def test_score_relative_error_and_specials():
+    rng = np.random.default_rng(9)
+    beta = rng.beta(2, 2, 5000).astype(np.float32)
+    pos = rng.integers(0, 139263, 5000)
+    t = 139264
+    s32 = ref.score_f32(ref.ln_beta(beta), t, pos)
+    s64 = ref.score_f64(beta, t, pos)
+    assert np.max(np.abs(s32 - s64) / np.abs(s64)) <= 1e-6
+    # beta = 1 -> +0.0 at every age; beta = 0 -> -inf
+    z = ref.score_f32(ref.ln_beta(np.ones(4, np.float32)), 100, np.array([0, 50, 98, 99]))
+    assert np.all(bits(z) == 0)
+    z = ref.score_f32(ref.ln_beta(np.zeros(3, np.float32)), 100, np.array([0, 50, 99]))
+    assert np.all(z == -np.inf)
+
+
+def test_score_powers_of_two():
+    # beta = 2^-k, age a: s = -a k ln 2 within 1.5 float32 ulp
+    for k in (1, 3, 17):
+        for a in (1, 7, 4096, 139264):
+            s = float(ref.score_f32(ref.ln_beta(np.float32(2.0 ** -k)), a, 0).reshape(-1)[0])
+            with mpmath.workdps(40):
+                want = float(-a * k * mpmath.log(2))
+            assert abs(s - want) <= 1.5 * np.spacing(np.float32(abs(want)))
+
+
+def test_score_order_preserved_under_decay():
+    # Ranking by exact r = beta^(t-i) equals ranking by the float64 log-score
+    # wherever two log-scores differ by more than 4 ulps.
+    rng = np.random.default_rng(10)
+    n, t = 120, 300
+    beta = rng.beta(5, 1, n).astype(np.float32)
+    pos = rng.integers(0, t, n)
+    s64 = ref.score_f64(beta, t, pos)
+    r = [brute.retention_exact(float(b), int(t - p)) for b, p in zip(beta, pos)]
+    for i in range(n):
+        for j in range(i + 1, n):
+            if abs(s64[i] - s64[j]) > 4 * np.spacing(max(abs(s64[i]), abs(s64[j]))):
+                assert (s64[i] > s64[j]) == (r[i] > r[j])
+
+
+def test_score_ranking_monotone_in_t():
+    # if beta_a >= beta_b and a outranks b at step t, a outranks b later too
+    rng = np.random.default_rng(11)
+    beta = rng.beta(2, 2, 400).astype(np.float32)
+    pos = rng.integers(0, 1000, 400)
+    for t0 in (1000, 1500):
+        s0 = ref.score_f64(beta, t0, pos)
+        s1 = ref.score_f64(beta, t0 + 333, pos)
+        a, b = np.meshgrid(np.arange(400), np.arange(400), indexing="ij")
+        m = (beta[a] >= beta[b]) & (s0[a] > s0[b])
+        assert np.all(s1[a][m] > s1[b][m] - 1e-9)
+
+
+# --------------------------------------------------------------------------
+# a2: global top-M selection (DBTrimKV Method 3; TRIM-KV section 2)
+# --------------------------------------------------------------------------
+def _random_scores(rng, kind, lens):
+    out = []
+    for n in lens:
+        if kind == "cont":
+            s = -rng.random(n) * 10
+        elif kind == "alpha3":
+            s = rng.choice([-1.5, -0.25, 0.0], n)
+        elif kind == "equal":
+            s = np.full(n, -0.5)
+        elif kind == "zeros":
+            s = rng.choice([0.0, -0.0], n)
+        else:  # with -inf
+            s = np.where(rng.random(n) < 0.3, -np.inf, -rng.integers(0, 4, n).astype(np.float64))
+        out.append(s.astype(np.float32))
+    return out
+
+
+@pytest.mark.parametrize("kind", ["cont", "alpha3", "equal", "zeros", "inf"])
+def test_select_equals_full_sort(kind):
+    rng = np.random.default_rng(["cont", "alpha3", "equal", "zeros", "inf"].index(kind) + 100)
+    for trial in range(300):
+        H = int(rng.integers(1, 7))
+        lens = rng.integers(0, 40, H)
+        scores = _random_scores(rng, kind, lens)
+        n_seg = int(rng.integers(1, H + 1))
+        cuts = np.sort(rng.choice(np.arange(1, H), size=n_seg - 1, replace=False)) if n_seg > 1 else []
+        seg = np.concatenate([[0], cuts, [H]]).astype(np.int32)
+        budgets = []
+        for s in range(len(seg) - 1):
+            N = int(sum(lens[seg[s]:seg[s + 1]]))
+            budgets.append(int(rng.choice([0, 1, max(N - 1, 0), N, N + 5, int(rng.integers(0, N + 1))])))
+        keep, kept = ref.select_global(scores, seg, budgets)
+        for s in range(len(seg) - 1):
+            ent = [(float(scores[h][i]), h, i) for h in range(seg[s], seg[s + 1]) for i in range(lens[h])]
+            want = brute.select_sorted(ent, budgets[s])
+            got = set((h, i) for h in range(seg[s], seg[s + 1]) for i in np.flatnonzero(keep[h]))
+            assert got == want
+            assert sum(kept[seg[s]:seg[s + 1]]) == min(max(budgets[s], 0), sum(lens[seg[s]:seg[s + 1]]))
+
+
+def test_select_constant_beta_is_sliding_window():
+    # beta = c in (0,1) everywhere: the score only depends on age, so the
+    # kept set is the newest floor(M/H) of every head plus one more for the
+    # first M mod H heads (ties broken by head index).
+    H, n, t = 5, 64, 64
+    lnb = ref.ln_beta(np.full(n, 0.9, np.float32))
+    pos = np.arange(n)
+    scores = [ref.score_f32(lnb, t, pos) for _ in range(H)]
+    for M in (0, 1, 7, 63, 64, 100, 319, 320, 400):
+        keep, kept = ref.select_global(scores, [0, H], [M])
+        m = min(M, H * n)
+        for h in range(H):
+            w = m // H + (1 if h < m % H else 0)
+            want = np.zeros(n, bool)
+            want[n - w:] = True
+            assert np.array_equal(keep[h], want), (M, h)
+
+
+def test_select_beta_one_keeps_first_in_flat_order():
+    H, n = 4, 20
+    scores = [ref.score_f32(ref.ln_beta(np.ones(n, np.float32)), 50, np.arange(n)) for _ in range(H)]
+    for M in (0, 5, 20, 33, 80, 100):
+        keep, _ = ref.select_global(scores, [0, H], [M])
+        flat = np.concatenate(keep)
+        want = np.zeros(H * n, bool)
+        want[:min(M, H * n)] = True
+        assert np.array_equal(flat, want)
+
+
+def test_select_segments_independent():
+    rng = np.random.default_rng(12)
+    scores = _random_scores(rng, "alpha3", rng.integers(5, 30, 8))
+    keep, _ = ref.select_global(scores, [0, 3, 8], [10, 17])
+    k1, _ = ref.select_global(scores[:3], [0, 3], [10])
+    k2, _ = ref.select_global(scores[3:], [0, 5], [17])
+    for a, b in zip(keep, k1 + k2):
+        assert np.array_equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# a3: compaction (DBTrimKV Method 4; ContourKV section 2, physical budget)
+# --------------------------------------------------------------------------
+def test_compaction_round_trip_and_layout():
+    cache = synth.random_ragged_cache(13, n_heads=6, d=8, dtype="f32", max_len=70)
+    po, pi, ln = cache.page_off, cache.page_ids, cache.length
+    rng = np.random.default_rng(13)
+    keep = [rng.random(int(n)) < 0.4 for n in ln]
+    rows = {"k": ref.gather_heads(cache.k, po, pi, ln), "pos": ref.gather_heads(cache.pos, po, pi, ln)}
+    for reserve in (0, 1, 3):
+        dpo, dpi, dlen, out = ref.compact(rows, keep, reserve)
+        kept = np.array([k.sum() for k in keep])
+        assert np.array_equal(dlen, kept)
+        assert np.array_equal(np.diff(dpo), -(-(kept + reserve) // 16))
+        assert np.array_equal(dpi, np.arange(dpo[-1]))
+        for h in range(6):
+            assert np.array_equal(out["k"][h], rows["k"][h][keep[h]])
+            assert np.all(np.diff(out["pos"][h]) > 0)     # positions stay ascending
+
+
+# --------------------------------------------------------------------------
+# a4: renormalised decode attention (ContourKV problem definition, sections 1, 3)
+# --------------------------------------------------------------------------
+def _heads(rng, H, n, d):
+    K = [rng.standard_normal((int(x), d)) for x in n]
+    V = [rng.standard_normal((int(x), d)) for x in n]
+    return K, V
+
+
+def test_attention_zero_query_is_uniform():
+    rng = np.random.default_rng(14)
+    K, V = _heads(rng, 3, [9, 16, 5], 8)
+    keep = [rng.random(len(k)) < 0.5 for k in K]
+    for k in keep:
+        k[0] = True
+    keep[2][:] = False
+    keep[2][3] = True
+    out, dropped, _ = ref.decode_attn(K, V, np.zeros((3, 8)), 1, 0.3, keep=keep)
+    for h in range(3):
+        A = keep[h]
+        assert np.allclose(out[h], V[h][A].mean(0), atol=1e-14)
+        assert abs(dropped[h] - (1 - A.sum() / len(A))) < 1e-15
+
+
+def test_attention_full_set_matches_torch_softmax():
+    rng = np.random.default_rng(15)
+    K, V = _heads(rng, 2, [33, 17], 16)
+    q = rng.standard_normal((8, 16))
+    out, dropped, lse = ref.decode_attn(K, V, q, 4, 0.25)
+    for qh in range(8):
+        h = qh // 4
+        z = torch.tensor(K[h] @ q[qh] * 0.25, dtype=torch.float64)
+        p = torch.softmax(z, 0).numpy()
+        assert np.allclose(out[qh], p @ V[h], atol=1e-13)
+        assert dropped[qh] == 0.0
+        assert abs(lse[qh] - torch.logsumexp(z, 0).item()) < 1e-12
+
+
+def test_attention_single_and_empty_kept_set():
+    rng = np.random.default_rng(16)
+    K, V = _heads(rng, 2, [12, 0], 4)
+    keep = [np.zeros(12, bool), np.zeros(0, bool)]
+    keep[0][5] = True
+    q = rng.standard_normal((2, 4))
+    out, dropped, _ = ref.decode_attn(K, V, q, 1, 0.5, keep=keep)
+    assert np.allclose(out[0], V[0][5], atol=1e-15)
+    assert np.all(out[1] == 0) and dropped[1] == 1.0
+    keep[0][:] = False
+    out, dropped, lse = ref.decode_attn(K, V, q, 1, 0.5, keep=keep)
+    assert np.all(out[0] == 0) and dropped[0] == 1.0 and lse[0] == -np.inf
+
+
+def test_attention_renormalised_equals_softmax_over_kept_and_dilution():
+    rng = np.random.default_rng(17)
+    K, V = _heads(rng, 1, [50], 8)
+    q = rng.standard_normal((1, 8)) * 2
+    keep = [rng.random(50) < 0.3]
+    out, dropped, _ = ref.decode_attn(K, V, q, 1, 0.35, keep=keep)
+    A = keep[0]
+    z = K[0][A] @ q[0] * 0.35
+    p = torch.softmax(torch.tensor(z, dtype=torch.float64), 0).numpy()
+    assert np.allclose(out[0], p @ V[0][A], atol=1e-13)
+    zfull = torch.tensor(K[0] @ q[0] * 0.35, dtype=torch.float64)
+    pfull = torch.softmax(zfull, 0).numpy()
+    assert abs(dropped[0] - pfull[~A].sum()) < 1e-14
+    assert abs((1 - dropped[0]) - pfull[A].sum()) < 1e-14      # kept + dropped = 1
+    assert np.all(p >= pfull[A] - 1e-16)                        # dilution: p_j/kept >= p_j
+
+
+def test_attention_matches_direct_sums():
+    rng = np.random.default_rng(18)
+    K, V = _heads(rng, 3, [7, 21, 1], 6)
+    q = rng.standard_normal((6, 6))
+    keep = [rng.random(len(k)) < 0.6 for k in K]
+    out, dropped, _ = ref.decode_attn(K, V, q, 2, 0.4, keep=keep)
+    for qh in range(6):
+        h = qh // 2
+        o, d = brute.attention_direct(K[h].tolist(), V[h].tolist(), q[qh].tolist(), 0.4, keep[h].tolist())
+        assert np.allclose(out[qh], o, atol=1e-13) and abs(dropped[qh] - d) < 1e-14
+
+
+def test_attention_reference_mode_matches_mask_mode():
+    rng = np.random.default_rng(19)
+    K, V = _heads(rng, 2, [40, 25], 8)
+    q = rng.standard_normal((4, 8))
+    keep = [rng.random(len(k)) < 0.5 for k in K]
+    _, dmask, _ = ref.decode_attn(K, V, q, 2, 0.3, keep=keep)
+    _, _, lse_full = ref.decode_attn(K, V, q, 2, 0.3)
+    Kk = [k[m] for k, m in zip(K, keep)]
+    Vk = [v[m] for v, m in zip(V, keep)]
+    _, dref, _ = ref.decode_attn(Kk, Vk, q, 2, 0.3, lse_ref=lse_full)
+    assert np.allclose(dref, dmask, atol=1e-13)
+
+
+def test_subset_error():
+    rng = np.random.default_rng(20)
+    K, V = _heads(rng, 1, [10], 4)
+    q = rng.standard_normal((1, 4))
+    e = ref.subset_error(K, V, q, 1, 0.5, [np.ones(10, bool)])
+    assert e[0] < 1e-15
+    one = np.zeros(10, bool)
+    one[4] = True
+    mu, _, _ = ref.decode_attn(K, V, q, 1, 0.5)
+    e = ref.subset_error(K, V, q, 1, 0.5, [one])
+    assert abs(e[0] - np.linalg.norm(mu[0] - V[0][4])) < 1e-14
+
+
+# --------------------------------------------------------------------------
+# a5/a6: attention mass and allocation (ContourKV section 3)
+# --------------------------------------------------------------------------
+def test_mass_is_mean_softmax():
+    rng = np.random.default_rng(21)
+    K, _ = _heads(rng, 2, [30, 11], 8)
+    q = rng.standard_normal((6, 8))
+    mass, lse = ref.attn_mass(K, q, 3, 0.5)
+    for h in range(2):
+        assert abs(mass[h].sum() - 1) < 1e-14
+        want = np.zeros(len(K[h]))
+        for g in range(3):
+            want += torch.softmax(torch.tensor(K[h] @ q[h * 3 + g] * 0.5, dtype=torch.float64), 0).numpy() / 3
+        assert np.allclose(mass[h], want, atol=1e-15)
+    m1, _ = ref.attn_mass(K, q[[0, 3]], 1, 0.5)
+    p = torch.softmax(torch.tensor(K[0] @ q[0] * 0.5, dtype=torch.float64), 0).numpy()
+    assert np.allclose(m1[0], p, atol=1e-16)
+
+
+def test_allocation_rules():
+    # proportional, exact
+    b, mbar = ref.allocate([0.5, 0.75, 0.75], [100, 100, 100], 8)
+    assert list(b) == [4, 2, 2] and np.allclose(mbar, [0.5, 0.25, 0.25])
+    # uniform dropped mass: B/H each, leftover to the lowest heads
+    b, _ = ref.allocate([0.6] * 4, [100] * 4, 10)
+    assert list(b) == [3, 3, 2, 2]
+    # leftover goes to the largest fractional part
+    b, _ = ref.allocate([0.0, 0.5, 0.8], [100] * 3, 10)   # mbar 1, .5, .2 -> x 5.88, 2.94, 1.18
+    assert list(b) == [6, 3, 1]
+    # capped at the head length; excess offered again in remainder order
+    b, _ = ref.allocate([0.5, 0.75, 0.75], [1, 100, 100], 8)
+    assert list(b) == [1, 4, 3]
+    # budget above the cache: everything kept
+    b, _ = ref.allocate([0.2, 0.9], [5, 7], 100)
+    assert list(b) == [5, 7]
+    # zero dropped mass everywhere -> uniform
+    b, _ = ref.allocate([1.0, 1.0, 1.0], [50] * 3, 7)
+    assert list(b) == [3, 2, 2]
+    rng = np.random.default_rng(22)
+    for _ in range(200):
+        H = int(rng.integers(1, 30))
+        ks = rng.random(H)
+        ln = rng.integers(0, 500, H)
+        B = int(rng.integers(0, ln.sum() + 1))
+        b, _ = ref.allocate(ks, ln, B)
+        assert b.sum() == B and np.all(b <= ln) and np.all(b >= 0)
+
+
+# --------------------------------------------------------------------------
+# byte accounting and budgets (IndexMem section 1; the workloads' budgets)
+# --------------------------------------------------------------------------
+def test_closed_forms():
+    g = json.load(open(os.path.join(GOLDEN, "closed_forms.json")))
+    s = g["kv_bytes_70b_1m_tokens_bf16"]["shape"]
+    assert ref.kv_cache_bytes(s["layers"], s["kv_heads"], s["head_dim"], s["tokens"], s["elt_bytes"]) \
+        == g["kv_bytes_70b_1m_tokens_bf16"]["value"] == 320 * 2 ** 30
+    assert synth.WORKLOADS["llama8b_32k"].budget() == g["budget_8b_32k"]["value"]
+    assert synth.WORKLOADS["batched16_16k"].budget() == g["budget_batched_16k"]["value"]
+    w = synth.WORKLOADS["qwen8b_128k"]
+    assert int(math.floor(Fraction(1, 20) * w.n_heads * w.ctx + Fraction(1, 2))) == g["budget_128k_5pct"]["value"]
+    assert synth.WORKLOADS["tiny"].budget() == 256
