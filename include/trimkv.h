@@ -1,0 +1,248 @@
+/*
+ * trimkv.h -- C ABI of the retention-scored KV eviction + decode library
+ * (libtrimkv.so, HIP for gfx950 / MI355X).
+ *
+ * The method (DBTrimKV and TRIM-KV pages): every cached KV entry i of a head
+ * carries a retention beta_i in [0,1] fixed at creation; at decode step t its
+ * score is ln r = (t - i) ln beta_i.  One global budget M over all layers and
+ * heads keeps the top-M scores; evicted entries are physically removed from
+ * per-head page tables; decode attention runs over the retained entries with
+ * forced (renormalised) weights and also reports the softmax mass that was
+ * dropped (ContourKV page).
+ *
+ * Conventions shared by every entry point
+ *  - All data pointers are DEVICE memory owned by the caller; the library
+ *    never allocates, frees or keeps pointers after a call returns.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *    asynchronously; no entry point synchronises the device except
+ *    trimkv_validate_cache.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    negative status means nothing was launched.
+ *  - Outputs never alias inputs, except trimkv_append (in place).
+ *  - Calls that share a workspace or output buffers must be ordered (same
+ *    stream or explicit events); otherwise they race.
+ *
+ * Data layout ("paged, per-head variable length", DBTrimKV page, Method 4)
+ *  - A head is one flat KV head h = (b * L + l) * H_kv + h_kv.
+ *  - Page size is 16 entries.  Logical page c (0-based) of head h is CSR
+ *    entry page_off[h] + c; it lives in physical page page_ids[page_off[h]+c].
+ *    Entry i of head h is slot i % 16 of its logical page i / 16; entries
+ *    i < len[h] are valid, and their positions ascend with i.
+ *  - Pools: k, v [n_pages][16][head_dim] (bf16 or fp32), lnb [n_pages][16]
+ *    fp32 (ln beta), pos [n_pages][16] int32.
+ *  - "CSR plane": a per-slot array indexed by CSR slot
+ *    s = (page_off[h] + i / 16) * 16 + i % 16, of length
+ *    page_off[n_heads] * 16 (<= n_pages * 16).  Scores, keep flags and
+ *    attention masses are CSR planes, so selection streams them
+ *    contiguously whatever the physical page order.
+ */
+#ifndef TRIMKV_H
+#define TRIMKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TRIMKV_PAGE_SIZE 16
+
+/* element type of K, V and q */
+enum { TRIMKV_F32 = 0, TRIMKV_BF16 = 1 };
+
+/* status codes */
+enum {
+  TRIMKV_OK = 0,
+  TRIMKV_EINVAL = -1,       /* null / inconsistent arguments */
+  TRIMKV_EUNSUPPORTED = -2, /* page_size != 16, head_dim not 64/128, dtype, group > 16 */
+  TRIMKV_EWORKSPACE = -3,   /* workspace missing or smaller than trimkv_workspace_size() */
+  TRIMKV_ECAPACITY = -4,    /* destination pool too small for the worst case */
+  TRIMKV_EHIP = -5,         /* the HIP runtime reported an error */
+  TRIMKV_EINVARIANT = -6    /* trimkv_validate_cache found a broken precondition */
+};
+
+typedef struct trimkv_cache {
+  int32_t n_heads;   /* flat KV heads */
+  int32_t head_dim;  /* 64 or 128 */
+  int32_t page_size; /* must be 16 */
+  int32_t dtype;     /* TRIMKV_F32 or TRIMKV_BF16 */
+  int64_t n_pages;   /* pool capacity in pages */
+  void* k;           /* [n_pages][16][head_dim] */
+  void* v;           /* [n_pages][16][head_dim] */
+  float* lnb;        /* [n_pages][16]  ln(beta) */
+  int32_t* pos;      /* [n_pages][16]  token position */
+  int32_t* page_off; /* [n_heads + 1]  CSR offsets, page_off[0] = 0, nondecreasing */
+  int32_t* page_ids; /* [n_pages]      physical page of each CSR entry */
+  int32_t* len;      /* [n_heads]      valid entries per head */
+} trimkv_cache_t;
+
+/* operation ids for trimkv_workspace_size */
+enum {
+  TRIMKV_OP_SCORE = 0,
+  TRIMKV_OP_SELECT = 1,
+  TRIMKV_OP_COMPACT = 2,
+  TRIMKV_OP_DECODE_ATTN = 3,
+  TRIMKV_OP_ATTN_MASS = 4,
+  TRIMKV_OP_VALIDATE = 5
+};
+
+/*
+ * trimkv_log_beta -- lnb[i] = ln(beta[i]) rounded to nearest fp32.
+ * TRIM-KV page, section 2: beta in [0,1] is assigned once, when the token is
+ * created, so its logarithm is computed once per entry.  beta = 1 gives +0.0,
+ * beta = 0 gives -inf.  beta: [n] fp32, lnb: [n] fp32.  n >= 0.
+ * Errors: EINVAL (null pointer with n > 0, n < 0).
+ */
+int trimkv_log_beta(const float* beta, float* lnb, int64_t n, void* stream);
+
+/*
+ * trimkv_score -- retention score of every valid slot.
+ * DBTrimKV page, Method 2 (r = beta^(t-i)); TRIM-KV page, section 2.
+ * For each head h in segment s (heads seg_head_begin[s] .. seg_head_begin[s+1]-1)
+ * and valid entry i:  score[csr slot] = (float)(t[s] - pos) * lnb, one fp32
+ * product.  Padding slots of the head's pages receive a quiet NaN.
+ *   seg_head_begin: device int32 [n_seg + 1], 0 .. n_heads, nondecreasing
+ *   t:              device int32 [n_seg]; requires pos < t <= pos + 2^24
+ *   score:          device fp32 CSR plane
+ * Errors: EINVAL, EUNSUPPORTED.
+ */
+int trimkv_score(const trimkv_cache_t* cache, int32_t n_seg, const int32_t* seg_head_begin,
+                 const int32_t* t, float* score, void* stream);
+
+/*
+ * trimkv_select_global -- exact global top-M per segment.
+ * DBTrimKV page, Method 3 (one global budget: rank every cached entry of all
+ * layers and heads, keep the top M_global); TRIM-KV page, section 2 (evict the
+ * lowest current scores once the budget is exceeded).
+ * Total order: score descending (-0.0 == +0.0, -inf last), then flat head
+ * ascending, then slot ascending.  Segment s keeps exactly
+ * min(max(budget[s], 0), N_s) entries, N_s = valid entries of its heads.
+ *   score:   device fp32 CSR plane (any fp32 key: retention scores or masses;
+ *            valid slots must not be NaN)
+ *   budget:  device int64 [n_seg]
+ *   keep:    device uint8 CSR plane, out: 1 kept, 0 evicted (valid slots),
+ *            0 in padding slots
+ *   kept:    device int32 [n_heads], out: kept entries per head
+ *   keptsum: device fp64 [n_heads] or NULL, out: sum of the kept scores of
+ *            each head (slot order within 1024-slot chunks, chunks in order)
+ *   ws:      workspace of trimkv_workspace_size(TRIMKV_OP_SELECT, cache, n_seg, 0) bytes
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE.
+ */
+int trimkv_select_global(const trimkv_cache_t* cache, const float* score, int32_t n_seg,
+                         const int32_t* seg_head_begin, const int64_t* budget, uint8_t* keep,
+                         int32_t* kept, double* keptsum, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * trimkv_compact -- physical eviction: stable out-of-place compaction.
+ * DBTrimKV page, Method 4 (paged per-head variable length); ContourKV page,
+ * section 2 (the budget must shrink storage, not just mask it).
+ * Every kept entry of src (keep == 1) is copied, in slot order, to dst:
+ * head h gets ceil((kept_h + reserve) / 16) pages numbered by a prefix sum
+ * over heads in flat order, dst->page_ids[c] = c, dst->len[h] = kept_h.
+ * K, V, lnb and pos rows are copied bit for bit; padding slots are left
+ * unspecified.  `reserve` spare slots per head let trimkv_append add entries.
+ *   dst:           same n_heads/head_dim/dtype as src; its pools, page_off,
+ *                  page_ids and len are written; must not overlap src.
+ *   max_kept_total: host-side upper bound on the number of kept entries;
+ *                  dst->n_pages must be >= ceil((max_kept_total +
+ *                  n_heads*reserve)/16) + n_heads, else ECAPACITY.
+ *   pages_used:    device int64 [1], out: dst->page_off[n_heads]
+ *   ws:            trimkv_workspace_size(TRIMKV_OP_COMPACT, src, 0, 0) bytes
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, ECAPACITY.
+ */
+int trimkv_compact(const trimkv_cache_t* src, const uint8_t* keep, int32_t reserve,
+                   int64_t max_kept_total, trimkv_cache_t* dst, int64_t* pages_used, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/*
+ * trimkv_decode_attn -- renormalised GQA decode attention with dropped mass.
+ * ContourKV page, problem definition (keep a subset, renormalise the weights
+ * over it, weights not re-optimised) and section 3 (dropped mass = total
+ * softmax weight of the discarded keys).
+ * Q head qh uses KV head qh / group.  z_j = scale * <q, k_j>; U = valid
+ * entries of the head; A = U (keep == NULL) or {j : keep[j] == 1}.
+ *   out[qh]     = sum_{A} e^{z_j} v_j / sum_{A} e^{z_j}   (0 if A is empty)
+ *   dropped[qh] = sum_{U\A} e^{z_j} / sum_{U} e^{z_j}       (1 if A is empty)
+ *   lse_out[qh] = ln sum_{A} e^{z_j}                        (-inf if A is empty)
+ * With lse_ref (reference log-sum-exp of a larger set no longer stored,
+ * e.g. from trimkv_attn_mass), dropped[qh] = 1 - exp(lse_out - lse_ref).
+ * keep and lse_ref must not both be given.
+ *   q:       device [n_heads * group][head_dim], same dtype as K/V
+ *   group:   1 .. 16
+ *   out:     device fp32 [n_heads * group][head_dim]
+ *   dropped: device fp32 [n_heads * group]
+ *   lse_out: device fp32 [n_heads * group] or NULL
+ *   ws:      trimkv_workspace_size(TRIMKV_OP_DECODE_ATTN, cache, 0, group) bytes
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE.
+ */
+int trimkv_decode_attn(const trimkv_cache_t* cache, const uint8_t* keep, const float* lse_ref,
+                       const void* q, int32_t group, float scale, float* out, float* dropped,
+                       float* lse_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * trimkv_attn_mass -- query-aware attention mass of every cached key.
+ * ContourKV page, sections 1 and 3 (top-mass selection; the dropped-mass
+ * statistic).  For KV head h with Q heads g = 0..group-1:
+ *   lse_full[h*group+g] = ln sum_{j in U} e^{z_gj}
+ *   mass[csr slot j]    = (1/group) sum_g e^{z_gj - lse_full[h*group+g]}
+ * Padding slots receive a quiet NaN.
+ *   mass:     device fp32 CSR plane;  lse_full: device fp32 [n_heads * group]
+ *   ws:       trimkv_workspace_size(TRIMKV_OP_ATTN_MASS, cache, 0, group) bytes
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE.
+ */
+int trimkv_attn_mass(const trimkv_cache_t* cache, const void* q, int32_t group, float scale,
+                     float* mass, float* lse_full, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * trimkv_allocate -- per-head budgets proportional to dropped mass.
+ * ContourKV page, section 3 (give budget to the heads whose top-mass set
+ * leaves the most mass behind).  With keptsum_h the mass of head h's top-s
+ * set (trimkv_select_global on trimkv_attn_mass output):
+ *   mbar_h = 1 - keptsum_h;  S = sum_h mbar_h (fp64, head order);
+ *   x_h = (B * mbar_h) / S  (B / n_heads if S == 0);  b_h = floor(x_h);
+ *   the B - sum b_h leftover units go one each to the largest x_h - b_h
+ *   (ties: lower head); then b_h is capped at len_h and the excess is
+ *   offered again, one unit per head per pass in the same order, to heads
+ *   below their length.
+ *   keptsum: device fp64 [n_heads];  len: device int32 [n_heads]
+ *   mbar_out: device fp64 [n_heads] or NULL;  budget_out: device int64 [n_heads]
+ * Errors: EINVAL (n_heads < 1 or > 65536, total_budget < 0).
+ */
+int trimkv_allocate(const double* keptsum, const int32_t* len, int32_t n_heads,
+                    int64_t total_budget, double* mbar_out, int64_t* budget_out, void* stream);
+
+/*
+ * trimkv_append -- add one new entry per head at decode step *t.
+ * TRIM-KV page, section 2 (beta assigned when the token is created).
+ * Entry len[h] of head h receives k_new[h], v_new[h], lnb = ln(beta_new[h])
+ * (as trimkv_log_beta) and pos = *t - 1; then len[h] += 1.  The head must have
+ * a free slot in its pages (trimkv_compact with reserve >= 1); a head without
+ * one is left unchanged (trimkv_validate_cache reports it).
+ *   k_new, v_new: device [n_heads][head_dim] (cache dtype); beta_new: fp32 [n_heads]
+ *   t: device int32 [1]
+ * Errors: EINVAL, EUNSUPPORTED.
+ */
+int trimkv_append(trimkv_cache_t* cache, const void* k_new, const void* v_new,
+                  const float* beta_new, const int32_t* t, void* stream);
+
+/* Bytes of workspace an operation needs for this cache (0 if none). */
+size_t trimkv_workspace_size(int op, const trimkv_cache_t* cache, int32_t n_seg, int32_t group);
+
+/*
+ * trimkv_validate_cache -- debug check of the preconditions (synchronises):
+ * page_off nondecreasing, within n_pages; page_ids in range; len within the
+ * head's pages; pos ascending within each head and < *t; lnb <= 0 and not NaN.
+ * Returns TRIMKV_OK or TRIMKV_EINVARIANT (or an argument / HIP error).
+ *   t: device int32 [1];  ws: trimkv_workspace_size(TRIMKV_OP_VALIDATE, ...) bytes
+ */
+int trimkv_validate_cache(const trimkv_cache_t* cache, const int32_t* t, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* trimkv_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TRIMKV_H */

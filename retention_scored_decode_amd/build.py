@@ -1,0 +1,56 @@
+"""Builds libtrimkv.so (HIP for gfx950) in place, next to this file.
+
+    python -m retention_scored_decode_amd.build
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "libtrimkv.so")
+
+SOURCES = ["abi.hip", "score.hip", "select.hip", "compact.hip", "attn.hip", "alloc.hip"]
+# units whose results must be bit-reproducible: no contraction into FMA
+EXACT = {"score.hip", "alloc.hip"}
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+          # packed fp32 VALU forms stay off (compiler-generated v_pk_* fp32 ops)
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-I", INCLUDE, "-I", CSRC]
+
+
+def _compile(src):
+    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+    cmd = [HIPCC] + COMMON + (["-ffp-contract=off"] if src in EXACT else []) + \
+        ["-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s" % (src, err))
+    return obj
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    r = subprocess.run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

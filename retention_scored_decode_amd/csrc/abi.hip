@@ -1,0 +1,224 @@
+// C ABI entry points: host-side validation, then the internal launchers.
+// Nothing is enqueued unless every argument check passes.
+#include <limits.h>
+
+#include "common.h"
+#include "launch.h"
+
+using namespace trimkv;
+
+namespace {
+
+bool cache_shape_ok(const trimkv_cache_t* c, int* rc) {
+  if (!c || c->n_heads < 0 || c->n_pages < 0 || c->n_pages > INT32_MAX) {
+    *rc = TRIMKV_EINVAL;
+    return false;
+  }
+  if (c->page_size != TRIMKV_PAGE_SIZE || (c->head_dim != 64 && c->head_dim != 128) ||
+      (c->dtype != TRIMKV_F32 && c->dtype != TRIMKV_BF16)) {
+    *rc = TRIMKV_EUNSUPPORTED;
+    return false;
+  }
+  return true;
+}
+
+bool table_ok(const trimkv_cache_t* c) { return c->page_off && c->len && (c->n_pages == 0 || c->page_ids); }
+bool pools_ok(const trimkv_cache_t* c) { return c->n_pages == 0 || (c->k && c->v && c->lnb && c->pos); }
+
+int ws_check(void* ws, size_t have, size_t need) {
+  if (need == 0) return TRIMKV_OK;
+  return (ws && have >= need) ? TRIMKV_OK : TRIMKV_EWORKSPACE;
+}
+
+hipStream_t S(void* s) { return (hipStream_t)s; }
+
+// ---------------------------------------------------------------------------
+// validate_cache kernels
+// ---------------------------------------------------------------------------
+enum { BAD_TABLE = 1, BAD_LEN = 2, BAD_PAGEID = 4, BAD_POS_ORDER = 8, BAD_POS_T = 16, BAD_LNB = 32 };
+
+__global__ void k_check_table(const int32_t* page_off, const int32_t* len, int n_heads, int64_t n_pages,
+                              int32_t* flag) {
+  for (int h = blockIdx.x * blockDim.x + threadIdx.x; h < n_heads; h += gridDim.x * blockDim.x) {
+    const int64_t a = page_off[h], b = page_off[h + 1];
+    int bad = 0;
+    if (a < 0 || b < a || b > n_pages) bad |= BAD_TABLE;
+    if (len[h] < 0 || (int64_t)len[h] > (b - a) * PAGE) bad |= BAD_LEN;
+    if (bad) atomicOr(flag, bad);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0 && page_off[0] != 0) atomicOr(flag, BAD_TABLE);
+}
+
+__global__ void k_check_ids(const int32_t* page_off, const int32_t* page_ids, int n_heads, int64_t n_pages,
+                            int32_t* flag) {
+  const int64_t total = page_off[n_heads];
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += (int64_t)gridDim.x * blockDim.x)
+    if (page_ids[c] < 0 || page_ids[c] >= n_pages) atomicOr(flag, BAD_PAGEID);
+}
+
+__global__ void k_check_slots(const int32_t* page_off, const int32_t* page_ids, const int32_t* len,
+                              const int32_t* pos, const float* lnb, int n_heads, const int32_t* t, int32_t* flag) {
+  const int64_t total = page_off[n_heads];
+  const int64_t c = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int j = threadIdx.x & 15;
+  if (c >= total) return;
+  const int h = upper_index(page_off, n_heads + 1, c);
+  const int64_t i = (c - page_off[h]) * PAGE + j;
+  if (i >= len[h]) return;
+  const int64_t slot = (int64_t)page_ids[c] * PAGE + j;
+  int bad = 0;
+  if (pos[slot] >= t[0]) bad |= BAD_POS_T;
+  const float l = lnb[slot];
+  if (!(l <= 0.0f)) bad |= BAD_LNB;
+  if (i + 1 < len[h]) {
+    const int64_t i1 = i + 1;
+    const int64_t s1 = (int64_t)page_ids[page_off[h] + i1 / PAGE] * PAGE + i1 % PAGE;
+    if (pos[s1] <= pos[slot]) bad |= BAD_POS_ORDER;
+  }
+  if (bad) atomicOr(flag, bad);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* trimkv_strerror(int s) {
+  switch (s) {
+    case TRIMKV_OK: return "ok";
+    case TRIMKV_EINVAL: return "invalid argument";
+    case TRIMKV_EUNSUPPORTED: return "unsupported configuration";
+    case TRIMKV_EWORKSPACE: return "workspace missing or too small";
+    case TRIMKV_ECAPACITY: return "destination pool too small";
+    case TRIMKV_EHIP: return "HIP runtime error";
+    case TRIMKV_EINVARIANT: return "cache invariant violated";
+    default: return "unknown status";
+  }
+}
+
+size_t trimkv_workspace_size(int op, const trimkv_cache_t* c, int32_t n_seg, int32_t group) {
+  int rc;
+  if (!cache_shape_ok(c, &rc)) return 0;
+  switch (op) {
+    case TRIMKV_OP_SELECT: return n_seg >= 1 ? select_ws_layout(c, n_seg).total : 0;
+    case TRIMKV_OP_COMPACT: return compact_ws_layout(c).total;
+    case TRIMKV_OP_DECODE_ATTN: return (group >= 1 && group <= 16) ? attn_ws_layout(c, group).total : 0;
+    case TRIMKV_OP_ATTN_MASS: return (group >= 1 && group <= 16) ? mass_ws_layout(c, group).total : 0;
+    case TRIMKV_OP_VALIDATE: return 256;
+    default: return 0;
+  }
+}
+
+int trimkv_log_beta(const float* beta, float* lnb, int64_t n, void* stream) {
+  if (n < 0 || (n > 0 && (!beta || !lnb))) return TRIMKV_EINVAL;
+  return launch_log_beta(beta, lnb, n, S(stream));
+}
+
+int trimkv_score(const trimkv_cache_t* c, int32_t n_seg, const int32_t* seg, const int32_t* t, float* score,
+                 void* stream) {
+  int rc;
+  if (!cache_shape_ok(c, &rc)) return rc;
+  if (n_seg < 1 || !seg || !t || !score || !table_ok(c) || !c->lnb || !c->pos) return TRIMKV_EINVAL;
+  if (c->n_heads == 0 || c->n_pages == 0) return TRIMKV_OK;
+  return launch_score(c, n_seg, seg, t, score, S(stream));
+}
+
+int trimkv_select_global(const trimkv_cache_t* c, const float* score, int32_t n_seg, const int32_t* seg,
+                         const int64_t* budget, uint8_t* keep, int32_t* kept, double* keptsum, void* ws,
+                         size_t ws_bytes, void* stream) {
+  int rc;
+  if (!cache_shape_ok(c, &rc)) return rc;
+  if (n_seg < 1 || n_seg > c->n_heads || !score || !seg || !budget || !keep || !kept || !table_ok(c))
+    return TRIMKV_EINVAL;
+  if ((rc = ws_check(ws, ws_bytes, select_ws_layout(c, n_seg).total))) return rc;
+  return launch_select(c, score, n_seg, seg, budget, keep, kept, keptsum, ws, S(stream));
+}
+
+int trimkv_compact(const trimkv_cache_t* src, const uint8_t* keep, int32_t reserve, int64_t max_kept_total,
+                   trimkv_cache_t* dst, int64_t* pages_used, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if (!cache_shape_ok(src, &rc)) return rc;
+  if (!cache_shape_ok(dst, &rc)) return rc;
+  if (!keep || !pages_used || reserve < 0 || max_kept_total < 0 || !table_ok(src) || !pools_ok(src) ||
+      !table_ok(dst) || !pools_ok(dst) || !dst->page_ids)
+    return TRIMKV_EINVAL;
+  if (dst->n_heads != src->n_heads || dst->head_dim != src->head_dim || dst->dtype != src->dtype)
+    return TRIMKV_EINVAL;
+  if (dst->k == src->k || dst->v == src->v || dst->lnb == src->lnb || dst->pos == src->pos ||
+      dst->page_off == src->page_off || dst->len == src->len)
+    return TRIMKV_EINVAL;
+  const int64_t H = src->n_heads;
+  const int64_t need = (max_kept_total + H * reserve + PAGE - 1) / PAGE + H;
+  if (dst->n_pages < need) return TRIMKV_ECAPACITY;
+  if ((rc = ws_check(ws, ws_bytes, compact_ws_layout(src).total))) return rc;
+  if (H == 0) return TRIMKV_OK;
+  return launch_compact(src, keep, reserve, dst, pages_used, ws, S(stream));
+}
+
+int trimkv_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float* lse_ref, const void* q,
+                       int32_t group, float scale, float* out, float* dropped, float* lse_out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int rc;
+  if (!cache_shape_ok(c, &rc)) return rc;
+  if (group < 1 || group > 16) return TRIMKV_EUNSUPPORTED;
+  if ((keep && lse_ref) || !q || !out || !dropped || !table_ok(c) || !pools_ok(c)) return TRIMKV_EINVAL;
+  if ((rc = ws_check(ws, ws_bytes, attn_ws_layout(c, group).total))) return rc;
+  if (c->n_heads == 0) return TRIMKV_OK;
+  return launch_decode_attn(c, keep, lse_ref, q, group, scale, out, dropped, lse_out, ws, S(stream));
+}
+
+int trimkv_attn_mass(const trimkv_cache_t* c, const void* q, int32_t group, float scale, float* mass,
+                     float* lse_full, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if (!cache_shape_ok(c, &rc)) return rc;
+  if (group < 1 || group > 16) return TRIMKV_EUNSUPPORTED;
+  if (!q || !mass || !lse_full || !table_ok(c) || !pools_ok(c)) return TRIMKV_EINVAL;
+  if ((rc = ws_check(ws, ws_bytes, mass_ws_layout(c, group).total))) return rc;
+  if (c->n_heads == 0) return TRIMKV_OK;
+  return launch_attn_mass(c, q, group, scale, mass, lse_full, ws, S(stream));
+}
+
+int trimkv_allocate(const double* keptsum, const int32_t* len, int32_t n_heads, int64_t total_budget,
+                    double* mbar_out, int64_t* budget_out, void* stream) {
+  if (n_heads < 1 || n_heads > 16384 || total_budget < 0 || !keptsum || !len || !budget_out) return TRIMKV_EINVAL;
+  return launch_allocate(keptsum, len, n_heads, total_budget, mbar_out, budget_out, S(stream));
+}
+
+int trimkv_append(trimkv_cache_t* c, const void* k_new, const void* v_new, const float* beta_new, const int32_t* t,
+                  void* stream) {
+  int rc;
+  if (!cache_shape_ok(c, &rc)) return rc;
+  if (!k_new || !v_new || !beta_new || !t || !table_ok(c) || !pools_ok(c)) return TRIMKV_EINVAL;
+  if (c->n_heads == 0) return TRIMKV_OK;
+  return launch_append(c, k_new, v_new, beta_new, t, S(stream));
+}
+
+int trimkv_validate_cache(const trimkv_cache_t* c, const int32_t* t, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if (!cache_shape_ok(c, &rc)) return rc;
+  if (!t || !table_ok(c) || !pools_ok(c)) return TRIMKV_EINVAL;
+  if ((rc = ws_check(ws, ws_bytes, 256))) return rc;
+  if (c->n_heads == 0) return TRIMKV_OK;
+  hipStream_t st = S(stream);
+  int32_t* flag = (int32_t*)ws;
+  int32_t host = 0;
+  if (hipMemsetAsync(flag, 0, 4, st) != hipSuccess) return TRIMKV_EHIP;
+  hipLaunchKernelGGL(k_check_table, dim3(64), dim3(256), 0, st, c->page_off, c->len, c->n_heads, c->n_pages, flag);
+  if (hipMemcpyAsync(&host, flag, 4, hipMemcpyDeviceToHost, st) != hipSuccess) return TRIMKV_EHIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return TRIMKV_EHIP;
+  if (host) return TRIMKV_EINVARIANT;
+  hipLaunchKernelGGL(k_check_ids, dim3(256), dim3(256), 0, st, c->page_off, c->page_ids, c->n_heads, c->n_pages,
+                     flag);
+  if (hipMemcpyAsync(&host, flag, 4, hipMemcpyDeviceToHost, st) != hipSuccess) return TRIMKV_EHIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return TRIMKV_EHIP;
+  if (host) return TRIMKV_EINVARIANT;
+  if (c->n_pages > 0) {
+    const int64_t blocks = (c->n_pages + 15) / 16;
+    hipLaunchKernelGGL(k_check_slots, dim3((unsigned)blocks), dim3(256), 0, st, c->page_off, c->page_ids, c->len,
+                       c->pos, c->lnb, c->n_heads, t, flag);
+  }
+  if (hipMemcpyAsync(&host, flag, 4, hipMemcpyDeviceToHost, st) != hipSuccess) return TRIMKV_EHIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return TRIMKV_EHIP;
+  return host ? TRIMKV_EINVARIANT : TRIMKV_OK;
+}
+
+}  // extern "C"

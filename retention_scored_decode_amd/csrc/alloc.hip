@@ -1,0 +1,125 @@
+// Per-head budgets proportional to the dropped-mass statistic.
+//
+// ContourKV page, section 3: the dropped mass of a head's top-mass set
+// predicts where selection leaves a large gap, and the budget is given to
+// those ("flat") heads.  Here b_h is proportional to mbar_h = 1 - keptsum_h
+// with largest-remainder rounding, then capped at the head length with the
+// excess offered again in remainder order.
+#include "common.h"
+#include "launch.h"
+
+namespace trimkv {
+
+namespace {
+
+constexpr int NT = 1024;
+
+__device__ __forceinline__ int64_t block_sum(int64_t v, int64_t* tmp) {
+  int64_t tot;
+  block_exclusive_scan<NT>(v, tmp, &tot);
+  return tot;
+}
+
+__device__ __forceinline__ double xval(double S, int64_t B, double mbar, int H) {
+  return S > 0.0 ? ((double)B * mbar) / S : (double)B / (double)H;
+}
+
+// One block.  O(H^2 / NT) rank computation; H <= 16384.
+__global__ void __launch_bounds__(NT) k_allocate(const double* __restrict__ keptsum, const int32_t* __restrict__ len,
+                                                 int H, int64_t B, double* __restrict__ mbar_out,
+                                                 int64_t* __restrict__ b) {
+  __shared__ int64_t tmp[NT / WAVE + 1];
+  __shared__ double sS;
+  __shared__ int32_t srank[16384];
+  if (threadIdx.x == 0) {
+    double S = 0.0;
+    for (int h = 0; h < H; ++h) S += 1.0 - keptsum[h];
+    sS = S;
+  }
+  __syncthreads();
+  const double S = sS;
+  auto frac_of = [&](int h) {
+    const double x = xval(S, B, 1.0 - keptsum[h], H);
+    return x - floor(x);
+  };
+  // rank in (fraction desc, head asc) order
+  for (int h = threadIdx.x; h < H; h += NT) {
+    const double f = frac_of(h);
+    int32_t r = 0;
+    for (int o = 0; o < H; ++o) {
+      const double fo = frac_of(o);
+      r += (fo > f) || (fo == f && o < h);
+    }
+    srank[h] = r;
+  }
+  __syncthreads();
+  int64_t part = 0;
+  for (int h = threadIdx.x; h < H; h += NT) {
+    const double m = 1.0 - keptsum[h];
+    if (mbar_out) mbar_out[h] = m;
+    const int64_t fl = (int64_t)floor(xval(S, B, m, H));
+    b[h] = fl;
+    part += fl;
+  }
+  const int64_t R = B - block_sum(part, tmp);
+  int64_t excess = 0, maxroom = 0;
+  for (int h = threadIdx.x; h < H; h += NT) {
+    const int64_t rk = srank[h];
+    int64_t v = b[h] + R / H + (rk < R % H ? 1 : 0);
+    const int64_t L = len[h];
+    if (v > L) {
+      excess += v - L;
+      v = L;
+    }
+    b[h] = v;
+    maxroom = max(maxroom, L - v);
+  }
+  excess = block_sum(excess, tmp);
+  if (excess == 0) return;
+  // water-fill: largest k with F(k) = sum_h min(room_h, k) <= excess
+  __shared__ int64_t s_maxroom;
+  if (threadIdx.x == 0) s_maxroom = 0;
+  __syncthreads();
+  atomicMax((unsigned long long*)&s_maxroom, (unsigned long long)maxroom);
+  __syncthreads();
+  int64_t lo = 0, hi = s_maxroom;  // F(lo) <= excess
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    int64_t f = 0;
+    for (int h = threadIdx.x; h < H; h += NT) f += min((int64_t)len[h] - b[h], mid);
+    f = block_sum(f, tmp);
+    if (f <= excess) lo = mid; else hi = mid - 1;
+  }
+  const int64_t k = lo;
+  int64_t f = 0;
+  for (int h = threadIdx.x; h < H; h += NT) f += min((int64_t)len[h] - b[h], k);
+  const int64_t left = excess - block_sum(f, tmp);
+  // heads with room > k take one more unit, in rank order, while units remain
+  int64_t add[16];
+  int na = 0;
+  for (int h = threadIdx.x; h < H; h += NT) {
+    const int64_t room = (int64_t)len[h] - b[h];
+    int64_t v = b[h] + min(room, k);
+    if (room > k && left > 0) {
+      const int32_t rk = srank[h];
+      int64_t er = 0;
+      for (int o = 0; o < H; ++o)
+        if ((int64_t)len[o] - b[o] > k && srank[o] < rk) ++er;
+      if (er < left) v += 1;
+    }
+    if (na < 16) add[na++] = v;
+  }
+  __syncthreads();
+  na = 0;
+  for (int h = threadIdx.x; h < H; h += NT) b[h] = add[na++];
+}
+
+}  // namespace
+
+int launch_allocate(const double* keptsum, const int32_t* len, int n_heads, int64_t budget, double* mbar,
+                    int64_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_allocate, dim3(1), dim3(NT), 0, st, keptsum, len, n_heads, budget, mbar, out);
+  return check_launch();
+}
+
+}  // namespace trimkv

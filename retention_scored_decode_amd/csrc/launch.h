@@ -1,0 +1,53 @@
+// Internal launchers behind the C ABI (abi.hip validates, these enqueue).
+#pragma once
+
+#include "common.h"
+
+namespace trimkv {
+
+inline int check_launch() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? TRIMKV_OK : TRIMKV_EHIP;
+}
+
+// Byte offsets of the pieces of one workspace; every piece 256-B aligned.
+struct WsLayout {
+  size_t off[16];
+  size_t total;
+  int n;
+  void add(size_t bytes) {
+    size_t a = (total + 255) & ~size_t(255);
+    off[n++] = a;
+    total = a + bytes;
+  }
+  WsLayout() : total(0), n(0) {}
+};
+
+// Upper bound on the number of chunks of `cp` pages over all heads.
+inline int64_t max_chunks(const trimkv_cache_t* c, int cp) { return c->n_pages / cp + c->n_heads + 1; }
+
+WsLayout select_ws_layout(const trimkv_cache_t* c, int n_seg);
+WsLayout compact_ws_layout(const trimkv_cache_t* c);
+WsLayout attn_ws_layout(const trimkv_cache_t* c, int group);
+WsLayout mass_ws_layout(const trimkv_cache_t* c, int group);
+
+int launch_log_beta(const float* beta, float* lnb, int64_t n, hipStream_t st);
+int launch_score(const trimkv_cache_t* c, int n_seg, const int32_t* seg, const int32_t* t, float* score,
+                 hipStream_t st);
+int launch_append(trimkv_cache_t* c, const void* kn, const void* vn, const float* bn, const int32_t* t,
+                  hipStream_t st);
+int launch_select(const trimkv_cache_t* c, const float* score, int n_seg, const int32_t* seg,
+                  const int64_t* budget, uint8_t* keep, int32_t* kept, double* keptsum, void* ws,
+                  hipStream_t st);
+int launch_compact(const trimkv_cache_t* src, const uint8_t* keep, int reserve, trimkv_cache_t* dst,
+                   int64_t* pages_used, void* ws, hipStream_t st);
+int launch_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float* lse_ref, const void* q,
+                       int group, float scale, float* out, float* dropped, float* lse_out, void* ws,
+                       hipStream_t st);
+int launch_attn_mass(const trimkv_cache_t* c, const void* q, int group, float scale, float* mass,
+                     float* lse_full, void* ws, hipStream_t st);
+int launch_allocate(const double* keptsum, const int32_t* len, int n_heads, int64_t budget, double* mbar,
+                    int64_t* out, hipStream_t st);
+int launch_validate(const trimkv_cache_t* c, const int32_t* t, void* ws, hipStream_t st, int* bad);
+
+}  // namespace trimkv

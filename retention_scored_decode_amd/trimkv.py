@@ -1,0 +1,221 @@
+"""ctypes binding of libtrimkv.so: same names as the C ABI, argument
+marshalling only.  Tensors are passed as device pointers (``data_ptr()``),
+the stream is torch's current HIP stream unless one is given.  Every step of
+the path runs in the library's HIP kernels; there is no Python or CPU
+fallback: if the library is missing or the device is not a GPU, calls fail.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtrimkv.so")
+
+PAGE = 16
+F32, BF16 = 0, 1
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ECAPACITY, EHIP, EINVARIANT = 0, -1, -2, -3, -4, -5, -6
+OP_SCORE, OP_SELECT, OP_COMPACT, OP_DECODE_ATTN, OP_ATTN_MASS, OP_VALIDATE = range(6)
+
+EXPORTS = ["trimkv_log_beta", "trimkv_score", "trimkv_select_global", "trimkv_compact",
+           "trimkv_decode_attn", "trimkv_attn_mass", "trimkv_allocate", "trimkv_append",
+           "trimkv_workspace_size", "trimkv_validate_cache", "trimkv_strerror"]
+
+
+class TrimkvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s failed: %s (%d)" % (what, strerror(status), status))
+        self.status = status
+
+
+class CacheStruct(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("n_pages", ctypes.c_int64),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("lnb", ctypes.c_void_p),
+                ("pos", ctypes.c_void_p), ("page_off", ctypes.c_void_p), ("page_ids", ctypes.c_void_p),
+                ("len", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libtrimkv.so (built in place by retention_scored_decode_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libtrimkv.so is not built: run `python -m retention_scored_decode_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        cp = ctypes.POINTER(CacheStruct)
+        sig = {
+            "trimkv_log_beta": [vp, vp, i64, vp],
+            "trimkv_score": [cp, i32, vp, vp, vp, vp],
+            "trimkv_select_global": [cp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp],
+            "trimkv_compact": [cp, vp, i32, i64, cp, vp, vp, sz, vp],
+            "trimkv_decode_attn": [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp],
+            "trimkv_attn_mass": [cp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp],
+            "trimkv_allocate": [vp, vp, i32, i64, vp, vp, vp],
+            "trimkv_append": [cp, vp, vp, vp, vp, vp],
+            "trimkv_workspace_size": [ctypes.c_int, cp, i32, i32],
+            "trimkv_validate_cache": [cp, vp, vp, sz, vp],
+            "trimkv_strerror": [ctypes.c_int],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.trimkv_workspace_size.restype = ctypes.c_size_t
+        L.trimkv_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().trimkv_strerror(int(status)).decode()
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(rc: int, what: str):
+    if rc != OK:
+        raise TrimkvError(rc, what)
+
+
+class Cache:
+    """A paged KV pool plus its page table, as device tensors.
+
+    k, v [n_pages, 16, D] (torch.bfloat16 or float32), lnb [n_pages, 16] f32,
+    pos [n_pages, 16] i32, page_off [n_heads + 1] i32, page_ids [n_pages] i32,
+    length [n_heads] i32.
+    """
+
+    def __init__(self, k, v, lnb, pos, page_off, page_ids, length):
+        self.k, self.v, self.lnb, self.pos = k, v, lnb, pos
+        self.page_off, self.page_ids, self.length = page_off, page_ids, length
+        self._s = None
+
+    @classmethod
+    def empty(cls, n_heads: int, n_pages: int, head_dim: int, dtype: torch.dtype, device="cuda"):
+        return cls(torch.empty((n_pages, PAGE, head_dim), dtype=dtype, device=device),
+                   torch.empty((n_pages, PAGE, head_dim), dtype=dtype, device=device),
+                   torch.empty((n_pages, PAGE), dtype=torch.float32, device=device),
+                   torch.empty((n_pages, PAGE), dtype=torch.int32, device=device),
+                   torch.zeros(n_heads + 1, dtype=torch.int32, device=device),
+                   torch.empty(n_pages, dtype=torch.int32, device=device),
+                   torch.zeros(n_heads, dtype=torch.int32, device=device))
+
+    @property
+    def n_heads(self) -> int:
+        return int(self.length.shape[0])
+
+    @property
+    def n_pages(self) -> int:
+        return int(self.k.shape[0])
+
+    @property
+    def head_dim(self) -> int:
+        return int(self.k.shape[2])
+
+    @property
+    def dtype_code(self) -> int:
+        return BF16 if self.k.dtype == torch.bfloat16 else F32
+
+    def struct(self) -> CacheStruct:
+        s = CacheStruct(self.n_heads, self.head_dim, PAGE, self.dtype_code, self.n_pages,
+                        self.k.data_ptr(), self.v.data_ptr(), self.lnb.data_ptr(), self.pos.data_ptr(),
+                        self.page_off.data_ptr(), self.page_ids.data_ptr(), self.length.data_ptr())
+        self._s = s
+        return s
+
+
+def workspace_size(op: int, cache: Cache, n_seg: int = 0, group: int = 0) -> int:
+    return int(lib().trimkv_workspace_size(op, ctypes.byref(cache.struct()), n_seg, group))
+
+
+def workspace(op: int, cache: Cache, n_seg: int = 0, group: int = 0) -> torch.Tensor:
+    n = workspace_size(op, cache, n_seg, group)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=cache.k.device)
+
+
+def log_beta(beta: torch.Tensor, lnb: torch.Tensor, stream=None):
+    _check(lib().trimkv_log_beta(_p(beta), _p(lnb), beta.numel(), _stream(stream)), "trimkv_log_beta")
+
+
+def score(cache: Cache, seg_head_begin: torch.Tensor, t: torch.Tensor, out: torch.Tensor, stream=None):
+    n_seg = seg_head_begin.numel() - 1
+    _check(lib().trimkv_score(ctypes.byref(cache.struct()), n_seg, _p(seg_head_begin), _p(t), _p(out),
+                              _stream(stream)), "trimkv_score")
+
+
+def select_global(cache: Cache, score: torch.Tensor, seg_head_begin: torch.Tensor, budget: torch.Tensor,
+                  keep: torch.Tensor, kept: torch.Tensor, keptsum: Optional[torch.Tensor] = None,
+                  ws: Optional[torch.Tensor] = None, stream=None):
+    n_seg = seg_head_begin.numel() - 1
+    if ws is None:
+        ws = workspace(OP_SELECT, cache, n_seg)
+    _check(lib().trimkv_select_global(ctypes.byref(cache.struct()), _p(score), n_seg, _p(seg_head_begin),
+                                      _p(budget), _p(keep), _p(kept), _p(keptsum), _p(ws), ws.numel(),
+                                      _stream(stream)), "trimkv_select_global")
+
+
+def compact(src: Cache, keep: torch.Tensor, reserve: int, max_kept_total: int, dst: Cache,
+            pages_used: torch.Tensor, ws: Optional[torch.Tensor] = None, stream=None):
+    if ws is None:
+        ws = workspace(OP_COMPACT, src)
+    _check(lib().trimkv_compact(ctypes.byref(src.struct()), _p(keep), int(reserve), int(max_kept_total),
+                                ctypes.byref(dst.struct()), _p(pages_used), _p(ws), ws.numel(),
+                                _stream(stream)), "trimkv_compact")
+
+
+def decode_attn(cache: Cache, q: torch.Tensor, group: int, scale: float, out: torch.Tensor,
+                dropped: torch.Tensor, keep: Optional[torch.Tensor] = None,
+                lse_ref: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = None, stream=None):
+    if ws is None:
+        ws = workspace(OP_DECODE_ATTN, cache, 0, group)
+    _check(lib().trimkv_decode_attn(ctypes.byref(cache.struct()), _p(keep), _p(lse_ref), _p(q), int(group),
+                                    float(scale), _p(out), _p(dropped), _p(lse_out), _p(ws), ws.numel(),
+                                    _stream(stream)), "trimkv_decode_attn")
+
+
+def attn_mass(cache: Cache, q: torch.Tensor, group: int, scale: float, mass: torch.Tensor,
+              lse_full: torch.Tensor, ws: Optional[torch.Tensor] = None, stream=None):
+    if ws is None:
+        ws = workspace(OP_ATTN_MASS, cache, 0, group)
+    _check(lib().trimkv_attn_mass(ctypes.byref(cache.struct()), _p(q), int(group), float(scale), _p(mass),
+                                  _p(lse_full), _p(ws), ws.numel(), _stream(stream)), "trimkv_attn_mass")
+
+
+def allocate(keptsum: torch.Tensor, length: torch.Tensor, total_budget: int, budget_out: torch.Tensor,
+             mbar_out: Optional[torch.Tensor] = None, stream=None):
+    _check(lib().trimkv_allocate(_p(keptsum), _p(length), int(keptsum.numel()), int(total_budget),
+                                 _p(mbar_out), _p(budget_out), _stream(stream)), "trimkv_allocate")
+
+
+def append(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, beta_new: torch.Tensor, t: torch.Tensor,
+           stream=None):
+    _check(lib().trimkv_append(ctypes.byref(cache.struct()), _p(k_new), _p(v_new), _p(beta_new), _p(t),
+                               _stream(stream)), "trimkv_append")
+
+
+def validate_cache(cache: Cache, t: torch.Tensor, ws: Optional[torch.Tensor] = None, stream=None) -> int:
+    if ws is None:
+        ws = workspace(OP_VALIDATE, cache)
+    return int(lib().trimkv_validate_cache(ctypes.byref(cache.struct()), _p(t), _p(ws), ws.numel(),
+                                           _stream(stream)))

@@ -1,0 +1,107 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from retention_scored_decode_amd import trimkv as tk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared():
+    src = open(os.path.join(ROOT, "include", "trimkv.h")).read()
+    return sorted(set(re.findall(r"^\S.*?\b(trimkv_\w+)\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared()
+    assert len(names) == 11
+    L = tk.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(tk.EXPORTS) == names
+
+
+def fake_cache(n_heads=4, head_dim=128, dtype=tk.BF16, n_pages=64, page_size=16, nulls=()):
+    f = dict(k=0x1000, v=0x2000, lnb=0x3000, pos=0x4000, page_off=0x5000, page_ids=0x6000, len=0x7000)
+    for n in nulls:
+        f[n] = None
+    return tk.CacheStruct(n_heads, head_dim, page_size, dtype, n_pages, f["k"], f["v"], f["lnb"], f["pos"],
+                          f["page_off"], f["page_ids"], f["len"])
+
+
+P = ctypes.c_void_p
+X = P(0x8000)
+
+
+def test_strerror():
+    assert tk.strerror(0) == "ok"
+    assert "workspace" in tk.strerror(tk.EWORKSPACE)
+
+
+def test_unsupported_shapes():
+    L = tk.lib()
+    for kw in (dict(page_size=8), dict(head_dim=96), dict(dtype=7)):
+        c = fake_cache(**kw)
+        assert L.trimkv_score(ctypes.byref(c), 1, X, X, X, None) == tk.EUNSUPPORTED
+    c = fake_cache()
+    assert L.trimkv_decode_attn(ctypes.byref(c), None, None, X, 17, ctypes.c_float(1.0), X, X, None, X, 1 << 30,
+                                None) == tk.EUNSUPPORTED
+    assert L.trimkv_decode_attn(ctypes.byref(c), None, None, X, 0, ctypes.c_float(1.0), X, X, None, X, 1 << 30,
+                                None) == tk.EUNSUPPORTED
+
+
+def test_null_and_inconsistent_arguments():
+    L = tk.lib()
+    c = fake_cache()
+    assert L.trimkv_score(None, 1, X, X, X, None) == tk.EINVAL
+    assert L.trimkv_score(ctypes.byref(c), 0, X, X, X, None) == tk.EINVAL
+    assert L.trimkv_score(ctypes.byref(c), 1, None, X, X, None) == tk.EINVAL
+    assert L.trimkv_log_beta(None, None, 5, None) == tk.EINVAL
+    assert L.trimkv_log_beta(X, X, -1, None) == tk.EINVAL
+    # keep and lse_ref together
+    assert L.trimkv_decode_attn(ctypes.byref(c), X, X, X, 4, ctypes.c_float(1.0), X, X, None, X, 1 << 30,
+                                None) == tk.EINVAL
+    assert L.trimkv_select_global(ctypes.byref(c), X, 5, X, X, X, X, None, X, 1 << 30, None) == tk.EINVAL
+    bad = fake_cache(nulls=("page_off",))
+    assert L.trimkv_select_global(ctypes.byref(bad), X, 1, X, X, X, X, None, X, 1 << 30, None) == tk.EINVAL
+    assert L.trimkv_allocate(X, X, 0, 10, None, X, None) == tk.EINVAL
+    assert L.trimkv_allocate(X, X, 4, -1, None, X, None) == tk.EINVAL
+    assert L.trimkv_append(ctypes.byref(c), None, X, X, X, None) == tk.EINVAL
+
+
+def test_workspace_checks():
+    L = tk.lib()
+    c = fake_cache()
+    need = L.trimkv_workspace_size(tk.OP_SELECT, ctypes.byref(c), 1, 0)
+    assert need > 0
+    assert L.trimkv_select_global(ctypes.byref(c), X, 1, X, X, X, X, None, X, need - 1, None) == tk.EWORKSPACE
+    assert L.trimkv_select_global(ctypes.byref(c), X, 1, X, X, X, X, None, None, need, None) == tk.EWORKSPACE
+    need = L.trimkv_workspace_size(tk.OP_DECODE_ATTN, ctypes.byref(c), 0, 4)
+    assert L.trimkv_decode_attn(ctypes.byref(c), None, None, X, 4, ctypes.c_float(1.0), X, X, None, X, need - 1,
+                                None) == tk.EWORKSPACE
+    # workspace grows with the pool and the group
+    big = fake_cache(n_pages=1 << 16)
+    assert L.trimkv_workspace_size(tk.OP_DECODE_ATTN, ctypes.byref(big), 0, 4) > need
+    assert L.trimkv_workspace_size(tk.OP_DECODE_ATTN, ctypes.byref(c), 0, 8) > need
+    assert L.trimkv_workspace_size(99, ctypes.byref(c), 0, 0) == 0
+
+
+def test_compact_capacity_and_compatibility():
+    L = tk.lib()
+    src = fake_cache(n_heads=4, n_pages=64)
+    ws = L.trimkv_workspace_size(tk.OP_COMPACT, ctypes.byref(src), 0, 0)
+    # need ceil((100 + 4*1)/16) + 4 = 11 pages
+    small = tk.CacheStruct(4, 128, 16, tk.BF16, 10, 0x11000, 0x12000, 0x13000, 0x14000, 0x15000, 0x16000, 0x17000)
+    ok = tk.CacheStruct(4, 128, 16, tk.BF16, 11, 0x11000, 0x12000, 0x13000, 0x14000, 0x15000, 0x16000, 0x17000)
+    assert L.trimkv_compact(ctypes.byref(src), X, 1, 100, ctypes.byref(small), X, X, ws, None) == tk.ECAPACITY
+    other = tk.CacheStruct(4, 64, 16, tk.BF16, 11, 0x11000, 0x12000, 0x13000, 0x14000, 0x15000, 0x16000, 0x17000)
+    assert L.trimkv_compact(ctypes.byref(src), X, 1, 100, ctypes.byref(other), X, X, ws, None) == tk.EINVAL
+    assert L.trimkv_compact(ctypes.byref(src), X, -1, 100, ctypes.byref(ok), X, X, ws, None) == tk.EINVAL
+    assert L.trimkv_compact(ctypes.byref(src), X, 1, 100, ctypes.byref(ok), X, X, ws - 1, None) == tk.EWORKSPACE
+    # aliasing source and destination pools
+    assert L.trimkv_compact(ctypes.byref(src), X, 1, 100, ctypes.byref(src), X, X, ws, None) in (tk.EINVAL,
+                                                                                                   tk.ECAPACITY)
