@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""One eviction + decode step of retention-scored KV eviction on one MI355X.
+
+Workload: Llama-3.1-8B-shaped single sequence (32 layers x 8 KV heads x 32 Q
+heads, head_dim 128, bf16 K/V with 1% outlier channels x8), 32,768 cached
+tokens per head (8,388,608 entries), beta ~ 0.7 Beta(2,2) + 0.3 Beta(50,1),
+global budget M = 10% of entries (838,861), pages of 16 in a permuted pool.
+
+A step runs, on the caller's stream, with inputs resident in HBM:
+  score  (ln r = (t-i) ln beta for every entry)
+  select (exact global top-M, ties by (head, position))
+  attend (mask mode: renormalised output over the kept set + dropped mass)
+  compact (physical eviction into a fresh pool)
+  decode (plain mode over the compacted retained KV: the steady-state cost)
+Each stage is bracketed by HIP events on the launch stream.
+
+Prints one JSON line.  `value` is the retained-KV decode-attention bandwidth
+(algorithmic bytes / time of the plain-mode call); the global select+compact
+rate (entries/s) is reported beside it, with per-stage figures, the roofline
+of the dominant stage and the CPU oracle timed on a sample.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "retained-KV decode-attn GB/s + global select/compact entries/s, 8B-shape 32K ctx"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cold-reps", type=int, default=10, help="flushed repetitions of the decode stage")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="llama8b_32k")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the path is single-GPU (see DESIGN.md for how it would shard); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from retention_scored_decode_amd import trimkv as tk
+
+    w = synth.WORKLOADS[args.workload]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    pc = synth.build_cache(w, workers=min(16, os.cpu_count() or 1))
+    gen_s = time.time() - t0
+    print("[bench] generated %s in %.1f s" % (w.name, gen_s), file=sys.stderr, flush=True)
+
+    H, G, D = pc.n_heads, w.group, w.head_dim
+    N = int(pc.length.sum())
+    M = w.budget()
+    nq = H * G
+    scale = 1.0 / math.sqrt(D)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    beta = up(pc.beta)
+    lnb = torch.empty_like(beta)
+    tk.log_beta(beta, lnb)
+    src = tk.Cache(bf(pc.k), bf(pc.v), lnb, up(pc.pos), up(pc.page_off), up(pc.page_ids), up(pc.length))
+    del beta
+    seg = up(w.seg_head_begin())
+    t_dev = up(np.full(w.n_seg, w.t, np.int32))
+    budget = up(np.full(w.n_seg, M, np.int64))
+    q = bf(synth.queries(w))
+    cap = -(-(M * w.n_seg) // 16) + H
+    dst = tk.Cache.empty(H, cap, D, torch.bfloat16, device=dev)
+    score = torch.empty(pc.n_pages * 16, dtype=torch.float32, device=dev)
+    keep = torch.empty(pc.n_pages * 16, dtype=torch.uint8, device=dev)
+    kept = torch.empty(H, dtype=torch.int32, device=dev)
+    used = torch.zeros(1, dtype=torch.int64, device=dev)
+    out_m = torch.empty((nq, D), dtype=torch.float32, device=dev)
+    drop_m = torch.empty(nq, dtype=torch.float32, device=dev)
+    out_p = torch.empty((nq, D), dtype=torch.float32, device=dev)
+    drop_p = torch.empty(nq, dtype=torch.float32, device=dev)
+    ws_sel = tk.workspace(tk.OP_SELECT, src, w.n_seg)
+    ws_cmp = tk.workspace(tk.OP_COMPACT, src)
+    ws_att = tk.workspace(tk.OP_DECODE_ATTN, src, 0, G)
+    ws_dec = tk.workspace(tk.OP_DECODE_ATTN, dst, 0, G)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    stages = ["score", "select", "attend_mask", "compact", "decode"]
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        tk.score(src, seg, t_dev, score)
+        if ev: ev[1].record()
+        tk.select_global(src, score, seg, budget, keep, kept, ws=ws_sel)
+        if ev: ev[2].record()
+        tk.decode_attn(src, q, G, scale, out_m, drop_m, keep=keep, ws=ws_att)
+        if ev: ev[3].record()
+        tk.compact(src, keep, 0, M * w.n_seg, dst, used, ws=ws_cmp)
+        if ev: ev[4].record()
+        tk.decode_attn(dst, q, G, scale, out_p, drop_p, ws=ws_dec)
+        if ev: ev[5].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = {s: [] for s in stages}
+    for e in evs:
+        for j, s in enumerate(stages):
+            per[s].append(e[j].elapsed_time(e[j + 1]) * 1e-3)
+    t = {s: float(np.mean(v)) for s, v in per.items()}
+
+    # sanity of the step's results (not timed)
+    kept_np = kept.cpu().numpy()
+    if w.n_seg == 1:
+        assert int(kept_np.sum()) == min(M, N)
+    assert int(dst.length.sum().item()) == int(kept_np.sum())
+    dst_pages = int(used.item())
+
+    # decode stage again, each repetition after a 1 GiB write (cold caches)
+    cold = []
+    for _ in range(args.cold_reps):
+        flush.fill_(1)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        tk.decode_attn(dst, q, G, scale, out_p, drop_p, ws=ws_dec)
+        b.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b) * 1e-3)
+    t_cold = float(np.median(cold))
+
+    kept_total = int(kept_np.sum())
+    small = nq * D * 2 + nq * D * 4 + nq * 4
+    algo = {
+        "score": 12 * N,
+        "select": 4 * N,
+        "attend_mask": 256 * N + 256 * kept_total + small,
+        "compact": 1040 * kept_total + 4 * dst_pages,
+        "decode": 512 * kept_total + small + 4 * dst_pages + 8 * H,
+    }
+    stage_out = {}
+    for s in stages:
+        gbs = algo[s] / t[s] / 1e9
+        stage_out[s] = {"us": round(t[s] * 1e6, 2), "algo_bytes": algo[s], "GBps": round(gbs, 1),
+                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    dom = max(stages, key=lambda s: t[s])
+    sc_t = t["select"] + t["compact"]
+    value = algo["decode"] / t["decode"] / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "kv_heads": w.kv_heads, "q_per_kv": G, "head_dim": D,
+                   "ctx_per_head": w.ctx, "entries": N, "budget": M, "page": 16},
+        "select_compact_entries_per_s": round(N / sc_t, 1),
+        "select_compact_GBps": round((algo["select"] + algo["compact"]) / sc_t / 1e9, 1),
+        "decode_cold_GBps": round(algo["decode"] / t_cold / 1e9, 1),
+        "stages": stage_out,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(algo[dom] / t[dom] / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(algo[dom] / t[dom] / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, pc, M)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, pc, M):
+    """The oracle, untuned, on one host thread: ln beta + scores + the global
+    selection over every entry, then compaction rows and float64 decode
+    attention over the kept entries of a sample of KV heads."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import synth
+    from oracle import reference as ref
+
+    with threadpool_limits(limits=1):
+        H, G, D = pc.n_heads, w.group, w.head_dim
+        po, pi, ln = pc.page_off, pc.page_ids, pc.length
+        t0 = time.perf_counter()
+        lnb = [ref.ln_beta(b) for b in ref.gather_heads(pc.beta, po, pi, ln)]
+        pos = ref.gather_heads(pc.pos, po, pi, ln)
+        scores = [ref.score_f32(lnb[h], w.t, pos[h]) for h in range(H)]
+        t1 = time.perf_counter()
+        keep, kept = ref.select_global(scores, [0, H], [M])
+        t2 = time.perf_counter()
+        sample = list(range(0, H, 8))          # 32 of 256 KV heads
+        kslots = [ref.head_phys_slots(po, pi, ln, h)[keep[h]] for h in sample]
+        K = [synth.bf16_bits_to_f32(pc.k.reshape(-1, D)[s]).astype(np.float64) for s in kslots]
+        V = [synth.bf16_bits_to_f32(pc.v.reshape(-1, D)[s]).astype(np.float64) for s in kslots]
+        q = synth.bf16_bits_to_f32(synth.queries(w)).astype(np.float64)
+        qs = np.concatenate([q[h * G:(h + 1) * G] for h in sample])
+        t3 = time.perf_counter()
+        ref.decode_attn(K, V, qs, G, 1.0 / math.sqrt(D))
+        t4 = time.perf_counter()
+    ent = int(sum(len(k) for k in K))
+    gbs = (512 * ent + len(qs) * D * 6) / (t4 - t3) / 1e9
+    N = int(ln.sum())
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "decode attention over the kept entries of 32 of 256 KV heads (%d entries); "
+                      "scores + global selection over all %d entries" % (ent, N),
+            "select_entries_per_s": round(N / (t2 - t1), 1),
+            "score_s": round(t1 - t0, 2), "select_s": round(t2 - t1, 2), "attn_s": round(t4 - t3, 3)}
+
+
+if __name__ == "__main__":
+    main()

@@ -27,7 +27,8 @@ namespace trimkv {
 
 namespace {
 
-constexpr int CHA = 16;   // pages per work item
+constexpr int CHA_F32 = 16;  // pages per work item of the fp32 kernel (one key per thread)
+constexpr int CHA_MIN = 16;  // smallest item size (workspace bound)
 constexpr int NT = 256;
 constexpr int GMAX = 16;
 constexpr float LOG2E = 1.4426950408889634f;
@@ -54,7 +55,13 @@ struct AttnArgs {
   int group;
   float scale2;          // scale * log2(e)
   int64_t plane;         // logits plane stride (n_pages * 16)
+  int cha;               // pages per work item
   AttnWs w;
+  // outputs written by the merge of each head
+  const float* lse_ref;
+  float* out;
+  float* dropped;
+  float* lse_out;
 };
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -85,102 +92,132 @@ __device__ __forceinline__ float bcast_dyn(float v, int g) {
   }
 }
 
-__global__ void __launch_bounds__(1024) k_attn_prep(const int32_t* __restrict__ page_off, int n_heads, AttnWs w) {
+// Work list of (head, chunk of cha pages).
+__global__ void __launch_bounds__(1024) k_attn_prep(const int32_t* __restrict__ page_off,
+                                                    const int32_t* __restrict__ len, int n_heads, int cha,
+                                                    AttnWs w) {
   __shared__ int64_t tmp[1024 / WAVE + 1];
-  build_chunk_list<1024>(page_off, n_heads, CHA, w.item_off, w.item_head, tmp);
+  __shared__ PrepLDS L;
+  const int T = prep_chunks<1024>(page_off, len, n_heads, cha, L, tmp, w.item_off);
+  for (int it = blockIdx.x * 1024 + threadIdx.x; it < T; it += gridDim.x * 1024)
+    w.item_head[it] = n_heads <= PREP_HMAX ? upper_index(L.off, n_heads + 1, it)
+                                           : upper_index(w.item_off, n_heads + 1, it);
 }
 
-// Combine the 16 streams of a work-group and write the item's partial.
-// m/la/ld: this lane's stream values for g = lane % 16 (lanes with
-// lane % 16 >= G hold don't-care values); acc: this lane's dims slice.
-template <int D, int GM>
-__device__ __forceinline__ void combine_streams(float m, float la, float ld, float (&acc)[GM][D / 16], int G,
-                                                int item, const AttnWs& w, bool with_acc) {
-  constexpr int DS = D / 16;
-  __shared__ float sm[16][GMAX], sla[16][GMAX], sld[16][GMAX];
-  __shared__ float sacc[4][GM][D];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane >> 4, col = lane & 15;
-  const int stream = wave * 4 + r;
-  if (col < G) sm[stream][col] = m;
-  __syncthreads();
-  float scale_own[GM];
-  for_g<GM>([&](int g) {
+// Merge all partials of KV head h: per query head g, M = max of the item
+// maxima, kept and dropped sums rescaled to M, acc rescaled and divided by
+// the kept sum.  A head without items has an empty kept set: out = 0,
+// dropped = 1, lse = -inf.  One block per KV head; fixed summation order.
+template <int D>
+__global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
+  const AttnWs& w = a.w;
+  const int h = blockIdx.x;
+  const int G = a.group;
+  const int b = w.item_off[h], e = w.item_off[h + 1];
+  __shared__ float sM[GMAX], sLA[GMAX];
+  const int grp = threadIdx.x >> 4, sub = threadIdx.x & 15;  // 16 groups of 16 lanes
+  if (grp < G) {
     float M = -INFINITY;
-    if (g < G)
-      for (int s = 0; s < 16; ++s) M = fmaxf(M, sm[s][g]);
-    const float ms = g < G ? sm[stream][g] : -INFINITY;
-    scale_own[g] = (M == -INFINITY) ? 0.f : exp2f(ms - M);
-  });
-  if (col < G) {
-    float sc = 0.f;
-    for_g<GM>([&](int g) { if (g == col) sc = scale_own[g]; });
-    sla[stream][col] = la * sc;
-    sld[stream][col] = ld * sc;
-  }
-  if (with_acc) {
-    for_g<GM>([&](int g) {
+    for (int it = b + sub; it < e; it += 16) M = fmaxf(M, w.stats[((size_t)it * G + grp) * 3]);
 #pragma unroll
-      for (int d = 0; d < DS; ++d) {
-        float x = acc[g][d] * scale_own[g];
-        x += __shfl_xor(x, 16, 64);
-        x += __shfl_xor(x, 32, 64);
-        acc[g][d] = x;
+    for (int d = 8; d > 0; d >>= 1) M = fmaxf(M, __shfl_xor(M, d, 16));
+    float la = 0.f, ld = 0.f;
+    if (M != -INFINITY) {
+      for (int it = b + sub; it < e; it += 16) {
+        const float* st = w.stats + ((size_t)it * G + grp) * 3;
+        const float sc = exp2f(st[0] - M);
+        la += st[1] * sc;
+        ld += st[2] * sc;
       }
-    });
-    if (r == 0) {
-      for_g<GM>([&](int g) {
+    }
 #pragma unroll
-        for (int d = 0; d < DS; ++d) sacc[wave][g][col * DS + d] = acc[g][d];
-      });
+    for (int d = 8; d > 0; d >>= 1) {
+      la += __shfl_xor(la, d, 16);
+      ld += __shfl_xor(ld, d, 16);
+    }
+    if (sub == 0) {
+      sM[grp] = M;
+      sLA[grp] = la;
+      const int qh = h * G + grp;
+      const float l2 = la > 0.f ? M + log2f(la) : -INFINITY;  // base-2 LSE of the kept set
+      const float lse = l2 * LN2;
+      if (a.lse_out) a.lse_out[qh] = lse;
+      if (w.lse2) w.lse2[qh] = l2;
+      if (a.dropped) {
+        float dm = 1.f;
+        if (la > 0.f) dm = a.lse_ref ? -expm1f(lse - a.lse_ref[qh]) : ld / (la + ld);
+        a.dropped[qh] = dm;
+      }
     }
   }
   __syncthreads();
-  if (threadIdx.x < G) {
-    const int g = threadIdx.x;
-    float M = -INFINITY, a = 0.f, b = 0.f;
-    for (int s = 0; s < 16; ++s) {
-      M = fmaxf(M, sm[s][g]);
-      a += sla[s][g];
-      b += sld[s][g];
-    }
-    float* st = w.stats + ((size_t)item * G + g) * 3;
-    st[0] = M;
-    st[1] = a;
-    st[2] = b;
-  }
-  if (with_acc) {
+  if (with_out) {
     for (int i = threadIdx.x; i < G * D; i += NT) {
-      const int g = i / D, d = i % D;
-      float s = 0.f;
-      for_g<GM>([&](int gg) {
-        if (gg == g) s = sacc[0][gg][d] + sacc[1][gg][d] + sacc[2][gg][d] + sacc[3][gg][d];
-      });
-      w.acc[(size_t)item * G * D + i] = s;
+      const int g = i / D;
+      const float M = sM[g], la = sLA[g];
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+      if (M != -INFINITY) {
+        int it = b;
+        for (; it + 4 <= e; it += 4) {
+          s0 += w.acc[(size_t)it * G * D + i] * exp2f(w.stats[((size_t)it * G + g) * 3] - M);
+          s1 += w.acc[(size_t)(it + 1) * G * D + i] * exp2f(w.stats[((size_t)(it + 1) * G + g) * 3] - M);
+          s2 += w.acc[(size_t)(it + 2) * G * D + i] * exp2f(w.stats[((size_t)(it + 2) * G + g) * 3] - M);
+          s3 += w.acc[(size_t)(it + 3) * G * D + i] * exp2f(w.stats[((size_t)(it + 3) * G + g) * 3] - M);
+        }
+        for (; it < e; ++it) s0 += w.acc[(size_t)it * G * D + i] * exp2f(w.stats[((size_t)it * G + g) * 3] - M);
+      }
+      const float s = (s0 + s1) + (s2 + s3);
+      a.out[(size_t)h * G * D + i] = la > 0.f ? s / la : 0.f;
     }
   }
 }
+
+template <int D> struct VRow;
+template <> struct VRow<128> { typedef uint4 T; };
+template <> struct VRow<64> { typedef uint2 T; };
 
 // ---------------------------------------------------------------------------
 // bf16 K/V, MFMA logits.  LOGITS=false: attention partials; LOGITS=true:
 // write base-2 logits of every valid key and (max, sum) partials.
+//
+// One wave per work item (head, up to a.cha consecutive pages); waves never
+// wait for each other.  The item's page ids and keep words arrive with one
+// load each; every page's K and V tiles are loaded one page ahead.  Each
+// 16-lane row is an online-softmax stream over keys 4r..4r+3 of every page;
+// the four streams are combined with cross-lane operations at the end.
 // ---------------------------------------------------------------------------
 template <int D, int GM, bool LOGITS>
 __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
-  constexpr int KU = D / 32;   // uint4 of K per lane per page
-  constexpr int NK = D / 16;   // MFMAs per page
-  constexpr int DS = D / 16;   // V dims per lane
-  const int item = blockIdx.x;
+  constexpr int KU = D / 32;    // uint4 of K per lane per page
+  constexpr int NK = D / 16;    // MFMAs per page
+  constexpr int DS = D / 16;    // V dims per lane
+  typedef typename VRow<D>::T VT;
   const AttnWs& w = a.w;
-  if (item >= w.item_off[a.n_heads]) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane >> 4, col = lane & 15;
+  const int lane = threadIdx.x & 63, r = lane >> 4, col = lane & 15;
+  const int item = blockIdx.x * (NT / WAVE) + (threadIdx.x >> 6);
+  if (item >= w.item_off[a.n_heads]) return;   // per-wave exit: no block barriers below
   const int G = a.group;
   const int h = w.item_head[item];
   const int pbase = a.page_off[h];
   const int np = a.page_off[h + 1] - pbase;
-  const int p0 = (item - w.item_off[h]) * CHA;
-  const int p1 = min(p0 + CHA, np);
+  const int p0 = (item - w.item_off[h]) * a.cha;
+  const int cnt = min(a.cha, np - p0);   // pages of this item, 1..cha (cha <= 32)
   const int n = a.len[h];
   const uint16_t* kq = (const uint16_t*)a.q;
+
+  // lane l: page id of page l; keep words: lane l of kw[b] covers page 16b + l/4, keys 4(l%4)..+3
+  const int pid_l = lane < cnt ? a.page_ids[pbase + p0 + lane] : 0;
+  uint32_t kw0 = 0xFFFFFFFFu, kw1 = 0xFFFFFFFFu;
+  if (!LOGITS && a.keep) {
+    const uint8_t* kb = a.keep + (int64_t)(pbase + p0) * PAGE;
+    if (lane / 4 < cnt) kw0 = *reinterpret_cast<const uint32_t*>(kb + 4 * lane);
+    if (16 + lane / 4 < cnt) kw1 = *reinterpret_cast<const uint32_t*>(kb + 256 + 4 * lane);
+  }
+  auto kword = [&](int i) -> uint32_t {
+    if (LOGITS || !a.keep) return 0xFFFFFFFFu;
+    const uint32_t src = (i < 16) ? kw0 : kw1;
+    return (uint32_t)__shfl((int)src, ((i & 15) << 2) + r, WAVE);
+  };
 
   // B operand: query column g = col; MFMA kk covers dims 32*(kk/2) + 8r + 4*(kk%2) + [0,4)
   short4_t qop[NK];
@@ -205,32 +242,41 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
   const uint8_t* kbase = (const uint8_t*)a.k;
   const uint8_t* vbase = (const uint8_t*)a.v;
 
-  for (int p = p0 + wave; p < p1; p += 4) {
-    const int64_t phys = a.page_ids[pbase + p];
-    // ---- logits S[key = 4r + j][g = col] ----
+  auto load = [&](int i, uint32_t kwi, uint4 (&kd)[KU], VT (&vd)[4]) {
+    const int64_t phys = __builtin_amdgcn_readlane(pid_l, i);
     const uint8_t* krow = kbase + ((phys * PAGE + col) * D) * 2 + 16 * r;
-    uint4 kr[KU];
 #pragma unroll
-    for (int u = 0; u < KU; ++u) kr[u] = *reinterpret_cast<const uint4*>(krow + 64 * u);
+    for (int u = 0; u < KU; ++u) kd[u] = *reinterpret_cast<const uint4*>(krow + 64 * u);
+    if (!LOGITS) {
+      const int i0 = (p0 + i) * PAGE + 4 * r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (i0 + j < n && ((kwi >> (8 * j)) & 0xFFu))
+          vd[j] = *reinterpret_cast<const VT*>(vbase + ((phys * PAGE + 4 * r + j) * D + col * DS) * 2);
+      }
+    }
+  };
+
+  auto compute = [&](int i, uint32_t kwi, uint4 (&kc)[KU], VT (&vc)[4]) {
+    const int p = p0 + i;
+    // ---- logits S[key = 4r + j][g = col] ----
     float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
-      short4_t a0 = {(short)(kr[u].x & 0xFFFF), (short)(kr[u].x >> 16), (short)(kr[u].y & 0xFFFF),
-                     (short)(kr[u].y >> 16)};
-      short4_t a1 = {(short)(kr[u].z & 0xFFFF), (short)(kr[u].z >> 16), (short)(kr[u].w & 0xFFFF),
-                     (short)(kr[u].w >> 16)};
+      short4_t a0 = {(short)(kc[u].x & 0xFFFF), (short)(kc[u].x >> 16), (short)(kc[u].y & 0xFFFF),
+                     (short)(kc[u].y >> 16)};
+      short4_t a1 = {(short)(kc[u].z & 0xFFFF), (short)(kc[u].z >> 16), (short)(kc[u].w & 0xFFFF),
+                     (short)(kc[u].w >> 16)};
       s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a0, qop[2 * u], s, 0, 0, 0);
       s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a1, qop[2 * u + 1], s, 0, 0, 0);
     }
     const int i0 = p * PAGE + 4 * r;   // entry index of key 4r within the head
-    uint32_t kw = 0xFFFFFFFFu;         // keep bytes of keys 4r..4r+3
-    if (!LOGITS && a.keep) kw = *reinterpret_cast<const uint32_t*>(a.keep + (int64_t)(pbase + p) * PAGE + 4 * r);
     float z[4];
     bool valid[4], kept[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       valid[j] = i0 + j < n;
-      kept[j] = valid[j] && ((kw >> (8 * j)) & 0xFFu);
+      kept[j] = valid[j] && ((kwi >> (8 * j)) & 0xFFu);
       z[j] = valid[j] ? s[j] * a.scale2 : -INFINITY;
     }
     if (LOGITS) {
@@ -263,9 +309,6 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
     ld = ld * alpha + sd;
     if (!LOGITS) {
       // ---- P V: lanes of row r own dims [col*DS, col*DS+DS) of keys 4r..4r+3 ----
-      bool any = false;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) any |= kept[j];
       float av[GM];
       float pk[GM][4];
       for_g<GM>([&](int g) {
@@ -277,30 +320,77 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
 #pragma unroll
         for (int d = 0; d < DS; ++d) acc[g][d] *= av[g];
       });
-      if (any) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (kept[j]) {
-            const uint8_t* vrow = vbase + ((phys * PAGE + 4 * r + j) * D + col * DS) * 2;
-            float vf[DS];
-            if (DS == 8) {
-              const uint4 vv = *reinterpret_cast<const uint4*>(vrow);
-              vf[0] = bf16lo(vv.x); vf[1] = bf16hi(vv.x); vf[2] = bf16lo(vv.y); vf[3] = bf16hi(vv.y);
-              vf[4] = bf16lo(vv.z); vf[5] = bf16hi(vv.z); vf[6] = bf16lo(vv.w); vf[7] = bf16hi(vv.w);
-            } else {
-              const uint2 vv = *reinterpret_cast<const uint2*>(vrow);
-              vf[0] = bf16lo(vv.x); vf[1] = bf16hi(vv.x); vf[2] = bf16lo(vv.y); vf[3] = bf16hi(vv.y);
-            }
-            for_g<GM>([&](int g) {
-#pragma unroll
-              for (int d = 0; d < DS; ++d) acc[g][d] = fmaf(pk[g][j], vf[d], acc[g][d]);
-            });
+      for (int j = 0; j < 4; ++j) {
+        if (kept[j]) {
+          float vf[DS];
+          if constexpr (DS == 8) {
+            const uint4 vv = vc[j];
+            vf[0] = bf16lo(vv.x); vf[1] = bf16hi(vv.x); vf[2] = bf16lo(vv.y); vf[3] = bf16hi(vv.y);
+            vf[4] = bf16lo(vv.z); vf[5] = bf16hi(vv.z); vf[6] = bf16lo(vv.w); vf[7] = bf16hi(vv.w);
+          } else {
+            const uint2 vv = vc[j];
+            vf[0] = bf16lo(vv.x); vf[1] = bf16hi(vv.x); vf[2] = bf16lo(vv.y); vf[3] = bf16hi(vv.y);
           }
+          for_g<GM>([&](int g) {
+#pragma unroll
+            for (int d = 0; d < DS; ++d) acc[g][d] = fmaf(pk[g][j], vf[d], acc[g][d]);
+          });
         }
       }
     }
+  };
+
+  uint4 kA[KU], kB[KU];
+  VT vA[4], vB[4];
+  uint32_t kwA = kword(0), kwB = 0u;
+  load(0, kwA, kA, vA);
+  for (int i = 0; i < cnt; i += 2) {
+    if (i + 1 < cnt) {
+      kwB = kword(i + 1);
+      load(i + 1, kwB, kB, vB);
+    }
+    compute(i, kwA, kA, vA);
+    if (i + 1 >= cnt) break;
+    if (i + 2 < cnt) {
+      kwA = kword(i + 2);
+      load(i + 2, kwA, kA, vA);
+    }
+    compute(i + 1, kwB, kB, vB);
   }
-  combine_streams<D, GM>(m, la, ld, acc, G, item, w, !LOGITS);
+
+  // ---- combine the four row streams of the wave and write the partial ----
+  float M = fmaxf(m, __shfl_xor(m, 16, WAVE));
+  M = fmaxf(M, __shfl_xor(M, 32, WAVE));
+  const float sc = (M == -INFINITY) ? 0.f : exp2f(m - M);
+  float las = la * sc, lds = ld * sc;
+  las += __shfl_xor(las, 16, WAVE);
+  las += __shfl_xor(las, 32, WAVE);
+  lds += __shfl_xor(lds, 16, WAVE);
+  lds += __shfl_xor(lds, 32, WAVE);
+  if (r == 0 && col < G) {
+    float* st = w.stats + ((size_t)item * G + col) * 3;
+    st[0] = M;
+    st[1] = las;
+    st[2] = lds;
+  }
+  if (!LOGITS) {
+    for_g<GM>([&](int g) {
+      const float sg = bcast_dyn(sc, g);   // scale of this row's stream for query column g
+#pragma unroll
+      for (int d = 0; d < DS; ++d) {
+        float x = acc[g][d] * sg;
+        x += __shfl_xor(x, 16, WAVE);
+        x += __shfl_xor(x, 32, WAVE);
+        acc[g][d] = x;
+      }
+      if (r == 0 && g < G) {
+        float* dst = w.acc + ((size_t)item * G + g) * D + col * DS;
+#pragma unroll
+        for (int d = 0; d < DS; ++d) dst[d] = acc[g][d];
+      }
+    });
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -308,7 +398,7 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
 // ---------------------------------------------------------------------------
 template <int D, bool LOGITS>
 __global__ void __launch_bounds__(NT) k_attn_f32(AttnArgs a) {
-  constexpr int NKEY = CHA * PAGE;  // 256 keys per item = one per thread
+  constexpr int NKEY = CHA_F32 * PAGE;  // 256 keys per item = one per thread
   __shared__ float sq[GMAX][D];
   __shared__ float sp[GMAX][NKEY];
   __shared__ float red[NT / WAVE];
@@ -319,7 +409,7 @@ __global__ void __launch_bounds__(NT) k_attn_f32(AttnArgs a) {
   const int h = w.item_head[item];
   const int pbase = a.page_off[h];
   const int np = a.page_off[h + 1] - pbase;
-  const int p0 = (item - w.item_off[h]) * CHA;
+  const int p0 = (item - w.item_off[h]) * CHA_F32;
   const int n = a.len[h];
   const float* qf = (const float*)a.q;
   for (int i = threadIdx.x; i < G * D; i += NT) sq[i / D][i % D] = qf[(size_t)h * G * D + i];
@@ -374,87 +464,58 @@ __global__ void __launch_bounds__(NT) k_attn_f32(AttnArgs a) {
     }
   }
   __syncthreads();
-  if (LOGITS) return;
-  const float* vb = (const float*)a.v;
-  for (int i = t; i < G * D; i += NT) {
-    const int g = i / D, d = i % D;
-    float s = 0.f;
-    for (int k = 0; k < NKEY; ++k) {
-      const float pk = sp[g][k];
-      if (pk != 0.f) {
-        const int pp = p0 + k / PAGE;
-        const int64_t sl = (int64_t)a.page_ids[pbase + pp] * PAGE + k % PAGE;
-        s = fmaf(pk, vb[sl * D + d], s);
+  if (!LOGITS) {
+    const float* vb = (const float*)a.v;
+    for (int i = t; i < G * D; i += NT) {
+      const int g = i / D, d = i % D;
+      float s = 0.f;
+      for (int k = 0; k < NKEY; ++k) {
+        const float pk = sp[g][k];
+        if (pk != 0.f) {
+          const int pp = p0 + k / PAGE;
+          const int64_t sl = (int64_t)a.page_ids[pbase + pp] * PAGE + k % PAGE;
+          s = fmaf(pk, vb[sl * D + d], s);
+        }
       }
-    }
-    w.acc[(size_t)item * G * D + i] = s;
-  }
-}
-
-// Per query head: merge the partials of its KV head's items in order.
-template <int D>
-__global__ void __launch_bounds__(64) k_attn_merge(const AttnWs w, int group, const float* __restrict__ lse_ref,
-                                                   float* __restrict__ out, float* __restrict__ dropped,
-                                                   float* __restrict__ lse_out, float* __restrict__ lse2_out) {
-  const int qh = blockIdx.x;
-  const int h = qh / group, g = qh % group;
-  const int b = w.item_off[h], e = w.item_off[h + 1];
-  float M = -INFINITY;
-  for (int it = b; it < e; ++it) M = fmaxf(M, w.stats[((size_t)it * group + g) * 3]);
-  float la = 0.f, ld = 0.f;
-  constexpr int PER = D / 64;
-  float acc[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-  for (int it = b; it < e; ++it) {
-    const float* st = w.stats + ((size_t)it * group + g) * 3;
-    const float sc = (M == -INFINITY) ? 0.f : exp2f(st[0] - M);
-    la += st[1] * sc;
-    ld += st[2] * sc;
-    if (out) {
-      const float* ac = w.acc + ((size_t)it * group + g) * D;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) acc[k] += ac[threadIdx.x + 64 * k] * sc;
-    }
-  }
-  if (out) {
-    const float inv = la > 0.f ? 1.f / la : 0.f;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) out[(size_t)qh * D + threadIdx.x + 64 * k] = acc[k] * inv;
-  }
-  if (threadIdx.x == 0) {
-    const float l2 = la > 0.f ? M + log2f(la) : -INFINITY;  // base-2 LSE of the kept set
-    const float lse = l2 * LN2;
-    if (lse_out) lse_out[qh] = lse;
-    if (lse2_out) lse2_out[qh] = l2;
-    if (dropped) {
-      float dm;
-      if (lse_ref) dm = la > 0.f ? -expm1f(lse - lse_ref[qh]) : 1.f;
-      else dm = (la + ld) > 0.f ? ld / (la + ld) : 1.f;
-      if (!(la > 0.f)) dm = 1.f;
-      dropped[qh] = dm;
+      w.acc[(size_t)item * G * D + i] = s;
     }
   }
 }
 
-// mass[j] = (1/G) sum_g 2^(z2_gj - lse2_g); NaN in padding slots
+// mass[j] = (1/G) sum_g 2^(z2_gj - lse2_g); NaN in padding slots.
+// 64 CSR pages per block, 4 slots per thread.
 __global__ void __launch_bounds__(256) k_mass(const int32_t* __restrict__ page_off, const int32_t* __restrict__ len,
                                               int n_heads, int group, int64_t plane, const AttnWs w,
                                               float* __restrict__ mass) {
+  __shared__ PageHeads sh;
   const int64_t total = page_off[n_heads];
-  const int64_t c = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int j = threadIdx.x & 15;
+  const int64_t c0 = (int64_t)blockIdx.x * 64;
+  if (c0 >= total) return;
+  const PageHeads r = block_page_heads(page_off, n_heads, c0, min(c0 + 63, total - 1), &sh);
+  const int64_t c = c0 + (threadIdx.x >> 2);
+  const int j0 = (threadIdx.x & 3) * 4;
   if (c >= total) return;
-  const int h = upper_index(page_off, n_heads + 1, c);
-  const int64_t i = (c - page_off[h]) * PAGE + j;
-  const int64_t slot = c * PAGE + j;
-  float out = qnan();
-  if (i < len[h]) {
-    float s = 0.f;
-    for (int g = 0; g < group; ++g) s += exp2f(w.logits[(int64_t)g * plane + slot] - w.lse2[(size_t)h * group + g]);
-    out = s / (float)group;
+  const int h = r.hf == r.hl ? r.hf : head_in_range(page_off, r, c);
+  const int64_t i0 = (c - page_off[h]) * PAGE + j0;
+  const int64_t n = len[h];
+  const int64_t slot = c * PAGE + j0;
+  float o[4] = {qnan(), qnan(), qnan(), qnan()};
+  if (i0 < n) {
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < group; ++g) {
+      const float4 z = *reinterpret_cast<const float4*>(w.logits + (int64_t)g * plane + slot);
+      const float l2 = w.lse2[(size_t)h * group + g];
+      s[0] += exp2f(z.x - l2);
+      s[1] += exp2f(z.y - l2);
+      s[2] += exp2f(z.z - l2);
+      s[3] += exp2f(z.w - l2);
+    }
+    const float inv = 1.f / (float)group;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (i0 + k < n) o[k] = s[k] * inv;
   }
-  mass[slot] = out;
+  *reinterpret_cast<float4*>(mass + slot) = make_float4(o[0], o[1], o[2], o[3]);
 }
 
 AttnWs carve(const trimkv_cache_t* c, int group, void* ws, bool mass) {
@@ -474,13 +535,15 @@ int gm_for(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : g <= 8 ? 8 : 1
 
 template <bool LOGITS>
 int launch_main(const trimkv_cache_t* c, AttnArgs& a, hipStream_t st) {
-  const int64_t W = max_chunks(c, CHA);
-  const dim3 grid((unsigned)W), blk(NT);
+  const int64_t W = max_chunks(c, a.cha);   // bound on the number of items
+  const dim3 blk(NT);
   if (c->dtype == TRIMKV_F32) {
+    const dim3 grid((unsigned)W);   // one item per block
     if (c->head_dim == 128) hipLaunchKernelGGL((k_attn_f32<128, LOGITS>), grid, blk, 0, st, a);
     else hipLaunchKernelGGL((k_attn_f32<64, LOGITS>), grid, blk, 0, st, a);
     return TRIMKV_OK;
   }
+  const dim3 grid((unsigned)((W + NT / WAVE - 1) / (NT / WAVE)));   // one item per wave
   const int gm = gm_for(a.group);
 #define TRIMKV_BF16(DD, GG) hipLaunchKernelGGL((k_attn_bf16<DD, GG, LOGITS>), grid, blk, 0, st, a)
   if (c->head_dim == 128) {
@@ -507,7 +570,7 @@ int launch_main(const trimkv_cache_t* c, AttnArgs& a, hipStream_t st) {
 }  // namespace
 
 WsLayout attn_ws_layout(const trimkv_cache_t* c, int group) {
-  const int64_t W = max_chunks(c, CHA);
+  const int64_t W = max_chunks(c, CHA_MIN);
   WsLayout L;
   L.add(((int64_t)c->n_heads + 1) * 4);
   L.add(W * 4);
@@ -517,7 +580,7 @@ WsLayout attn_ws_layout(const trimkv_cache_t* c, int group) {
 }
 
 WsLayout mass_ws_layout(const trimkv_cache_t* c, int group) {
-  const int64_t W = max_chunks(c, CHA);
+  const int64_t W = max_chunks(c, CHA_MIN);
   WsLayout L;
   L.add(((int64_t)c->n_heads + 1) * 4);
   L.add(W * 4);
@@ -532,37 +595,32 @@ int launch_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float
                        int group, float scale, float* out, float* dropped, float* lse_out, void* ws,
                        hipStream_t st) {
   AttnWs w = carve(c, group, ws, false);
-  hipLaunchKernelGGL(k_attn_prep, dim3(1), dim3(1024), 0, st, c->page_off, c->n_heads, w);
+  // items of 32 pages when every key is read (mask mode), 16 otherwise
+  const int cha = c->dtype == TRIMKV_F32 ? CHA_F32 : (keep ? 32 : 16);
+  hipLaunchKernelGGL(k_attn_prep, dim3(prep_grid(c->n_heads, max_chunks(c, cha), 2048)), dim3(1024), 0, st,
+                     c->page_off, c->len, c->n_heads, cha, w);
   AttnArgs a{c->page_off, c->page_ids, c->len, c->k, c->v, keep, q, c->n_heads, group, scale * LOG2E,
-             c->n_pages * PAGE, w};
+             c->n_pages * PAGE, cha, w, lse_ref, out, dropped, lse_out};
   int rc = launch_main<false>(c, a, st);
   if (rc) return rc;
-  const int nq = c->n_heads * group;
-  if (c->head_dim == 128)
-    hipLaunchKernelGGL(k_attn_merge<128>, dim3(nq), dim3(64), 0, st, w, group, lse_ref, out, dropped, lse_out,
-                       (float*)nullptr);
-  else
-    hipLaunchKernelGGL(k_attn_merge<64>, dim3(nq), dim3(64), 0, st, w, group, lse_ref, out, dropped, lse_out,
-                       (float*)nullptr);
+  if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(c->n_heads), dim3(NT), 0, st, a, 1);
+  else hipLaunchKernelGGL(k_attn_merge<64>, dim3(c->n_heads), dim3(NT), 0, st, a, 1);
   return check_launch();
 }
 
 int launch_attn_mass(const trimkv_cache_t* c, const void* q, int group, float scale, float* mass,
                      float* lse_full, void* ws, hipStream_t st) {
   AttnWs w = carve(c, group, ws, true);
-  hipLaunchKernelGGL(k_attn_prep, dim3(1), dim3(1024), 0, st, c->page_off, c->n_heads, w);
+  const int cha = c->dtype == TRIMKV_F32 ? CHA_F32 : 32;
+  hipLaunchKernelGGL(k_attn_prep, dim3(prep_grid(c->n_heads, max_chunks(c, cha), 2048)), dim3(1024), 0, st,
+                     c->page_off, c->len, c->n_heads, cha, w);
   AttnArgs a{c->page_off, c->page_ids, c->len, c->k, c->v, nullptr, q, c->n_heads, group, scale * LOG2E,
-             c->n_pages * PAGE, w};
+             c->n_pages * PAGE, cha, w, nullptr, nullptr, nullptr, lse_full};
   int rc = launch_main<true>(c, a, st);
   if (rc) return rc;
-  const int nq = c->n_heads * group;
-  if (c->head_dim == 128)
-    hipLaunchKernelGGL(k_attn_merge<128>, dim3(nq), dim3(64), 0, st, w, group, (const float*)nullptr,
-                       (float*)nullptr, (float*)nullptr, lse_full, w.lse2);
-  else
-    hipLaunchKernelGGL(k_attn_merge<64>, dim3(nq), dim3(64), 0, st, w, group, (const float*)nullptr,
-                       (float*)nullptr, (float*)nullptr, lse_full, w.lse2);
-  const int64_t blocks = (c->n_pages + 15) / 16;
+  if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(c->n_heads), dim3(NT), 0, st, a, 0);
+  else hipLaunchKernelGGL(k_attn_merge<64>, dim3(c->n_heads), dim3(NT), 0, st, a, 0);
+  const int64_t blocks = (c->n_pages + 63) / 64;
   hipLaunchKernelGGL(k_mass, dim3((unsigned)blocks), dim3(256), 0, st, c->page_off, c->len, c->n_heads, group,
                      c->n_pages * PAGE, w, mass);
   return check_launch();

@@ -118,6 +118,120 @@ __device__ void block_scan_runs(int n, Load load, int64_t* __restrict__ out, int
   if (threadIdx.x == 0) out[n] = tot;
 }
 
+// ---------------------------------------------------------------------------
+// Heads of the CSR pages [c0, c0 + npages) for a block: the first and last
+// head are found once (thread 0, binary search over page_off) and shared;
+// a page between them is then located by a search over that short range.
+// ---------------------------------------------------------------------------
+struct PageHeads {
+  int hf, hl;
+};
+
+__device__ __forceinline__ PageHeads block_page_heads(const int32_t* __restrict__ page_off, int n_heads, int64_t c0,
+                                                      int64_t clast, PageHeads* sh) {
+  if (threadIdx.x == 0) {
+    sh->hf = upper_index(page_off, n_heads + 1, c0);
+    sh->hl = upper_index(page_off, n_heads + 1, clast);
+  }
+  __syncthreads();
+  return *sh;
+}
+
+__device__ __forceinline__ int head_in_range(const int32_t* __restrict__ page_off, PageHeads r, int64_t c) {
+  int lo = r.hf, hi = r.hl + 1;  // page_off[lo] <= c < page_off[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)page_off[mid] <= c) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------------------
+// Chunk list shared by the prep kernels.  Every block rebuilds, in LDS, the
+// exclusive scan over heads of ceil(pages(h) / cp) together with copies of
+// page_off and len (n_heads <= PREP_HMAX); block 0 also stores the scan to
+// chunk_off_g.  With more heads the caller launches a single block and the
+// scan lives in chunk_off_g (global memory) instead.
+// ---------------------------------------------------------------------------
+constexpr int PREP_HMAX = 4096;
+
+struct PrepLDS {
+  int32_t off[PREP_HMAX + 1];
+  int32_t pg[PREP_HMAX + 1];
+  int32_t len[PREP_HMAX];
+};
+
+template <int NT>
+__device__ int prep_chunks(const int32_t* __restrict__ page_off, const int32_t* __restrict__ len, int n_heads,
+                           int cp, PrepLDS& L, int64_t* tmp, int32_t* __restrict__ chunk_off_g) {
+  const bool lds = n_heads <= PREP_HMAX;
+  int64_t carry = 0;
+  for (int base = 0; base < n_heads; base += NT) {
+    const int h = base + threadIdx.x;
+    int64_t n = 0;
+    if (h < n_heads) {
+      const int32_t a = page_off[h], b = page_off[h + 1];
+      n = ((int64_t)b - a + cp - 1) / cp;
+      if (lds) {
+        L.pg[h] = a;
+        L.len[h] = len[h];
+        if (h == n_heads - 1) L.pg[n_heads] = b;
+      }
+    }
+    int64_t tot;
+    const int64_t ex = block_exclusive_scan<NT>(n, tmp, &tot);
+    if (h < n_heads) {
+      if (lds) L.off[h] = (int32_t)(carry + ex);
+      if (!lds || blockIdx.x == 0) chunk_off_g[h] = (int32_t)(carry + ex);
+    }
+    carry += tot;
+  }
+  if (threadIdx.x == 0) {
+    if (lds) L.off[n_heads] = (int32_t)carry;
+    if (!lds || blockIdx.x == 0) chunk_off_g[n_heads] = (int32_t)carry;
+  }
+  __syncthreads();
+  return (int)carry;
+}
+
+// Head, first chunk of the head, first CSR page, valid entries and pages of
+// chunk c (after prep_chunks).
+struct ChunkInfo {
+  int h, c0, page0, nv, npg;
+};
+
+__device__ __forceinline__ ChunkInfo chunk_info(const PrepLDS& L, const int32_t* __restrict__ chunk_off_g,
+                                                const int32_t* __restrict__ page_off,
+                                                const int32_t* __restrict__ len, int n_heads, int cp, int c) {
+  ChunkInfo r;
+  if (n_heads <= PREP_HMAX) {
+    r.h = upper_index(L.off, n_heads + 1, c);
+    r.c0 = L.off[r.h];
+    const int64_t e0 = (int64_t)(c - r.c0) * cp * PAGE;
+    const int64_t v = (int64_t)L.len[r.h] - e0;
+    r.nv = (int)(v < 0 ? 0 : (v > cp * PAGE ? cp * PAGE : v));
+    r.page0 = L.pg[r.h] + (int)(e0 / PAGE);
+    const int np = L.pg[r.h + 1] - r.page0;
+    r.npg = np > cp ? cp : np;
+  } else {
+    r.h = upper_index(chunk_off_g, n_heads + 1, c);
+    r.c0 = chunk_off_g[r.h];
+    const int64_t e0 = (int64_t)(c - r.c0) * cp * PAGE;
+    const int64_t v = (int64_t)len[r.h] - e0;
+    r.nv = (int)(v < 0 ? 0 : (v > cp * PAGE ? cp * PAGE : v));
+    r.page0 = page_off[r.h] + (int)(e0 / PAGE);
+    const int np = page_off[r.h + 1] - r.page0;
+    r.npg = np > cp ? cp : np;
+  }
+  return r;
+}
+
+inline int prep_grid(int n_heads, int64_t tmax, int per_block) {
+  if (n_heads > PREP_HMAX) return 1;
+  int64_t b = (tmax + per_block - 1) / per_block;
+  return (int)(b < 1 ? 1 : (b > 128 ? 128 : b));
+}
+
 // bf16 bits -> fp32
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -8,6 +8,10 @@
 // Head h receives ceil((kept_h + reserve) / 16) destination pages numbered
 // by a prefix sum over heads; kept rows keep their slot order, so positions
 // stay ascending within every head.
+//
+// Kernels: prep (chunk list), count (kept per chunk and per head), head scan
+// (destination page table), scatter (row copies; a chunk's offset within its
+// head is the sum of the counts of the head's earlier chunks).
 #include <algorithm>
 
 #include "common.h"
@@ -21,24 +25,25 @@ constexpr int CP = 64;
 constexpr int CS = CP * PAGE;
 constexpr int NT = 256;
 
+// chunk metadata: x = head, y = first chunk of the head, z = first CSR page,
+// w = valid entries | (pages of the chunk << 16)
 struct CmpWs {
   int32_t* chunk_off;   // [H + 1]
-  int32_t* chunk_head;  // [Tmax]
+  int4* meta;           // [Tmax]
   int32_t* cnt;         // [Tmax] kept entries per chunk
-  int64_t* pk;          // [Tmax + 1] exclusive prefix over chunks of cnt
+  int32_t* head_kept;   // [H]
 };
 
-__global__ void __launch_bounds__(1024) k_cmp_prep(const int32_t* __restrict__ page_off, int n_heads, CmpWs w) {
+__global__ void __launch_bounds__(1024) k_cmp_prep(const int32_t* __restrict__ page_off,
+                                                   const int32_t* __restrict__ len, int n_heads, CmpWs w) {
   __shared__ int64_t tmp[1024 / WAVE + 1];
-  build_chunk_list<1024>(page_off, n_heads, CP, w.chunk_off, w.chunk_head, tmp);
-}
-
-__device__ __forceinline__ void geom(const int32_t* page_off, const int32_t* len, const CmpWs& w, int c, int h,
-                                     int* nv, int64_t* e0, int64_t* csr0) {
-  *e0 = (int64_t)(c - w.chunk_off[h]) * CS;
-  int64_t v = (int64_t)len[h] - *e0;
-  *nv = (int)(v < 0 ? 0 : (v > CS ? CS : v));
-  *csr0 = (int64_t)page_off[h] * PAGE + *e0;
+  __shared__ PrepLDS L;
+  for (int h = blockIdx.x * 1024 + threadIdx.x; h < n_heads; h += gridDim.x * 1024) w.head_kept[h] = 0;
+  const int T = prep_chunks<1024>(page_off, len, n_heads, CP, L, tmp, w.chunk_off);
+  for (int c = blockIdx.x * 1024 + threadIdx.x; c < T; c += gridDim.x * 1024) {
+    const ChunkInfo ci = chunk_info(L, w.chunk_off, page_off, len, n_heads, CP, c);
+    w.meta[c] = make_int4(ci.h, ci.c0, ci.page0, ci.nv | (ci.npg << 16));
+  }
 }
 
 __device__ __forceinline__ uint32_t keep_bits(const uint8_t* keep, int64_t csr0, int i0, int nv) {
@@ -51,35 +56,30 @@ __device__ __forceinline__ uint32_t keep_bits(const uint8_t* keep, int64_t csr0,
   return m;
 }
 
-__global__ void __launch_bounds__(NT) k_cmp_count(const int32_t* __restrict__ page_off,
-                                                  const int32_t* __restrict__ len, int n_heads,
-                                                  const uint8_t* __restrict__ keep, CmpWs w) {
+__global__ void __launch_bounds__(NT) k_cmp_count(int n_heads, const uint8_t* __restrict__ keep, CmpWs w) {
   __shared__ int64_t tmp[NT / WAVE + 1];
   const int c = blockIdx.x;
   if (c >= w.chunk_off[n_heads]) return;
-  const int h = w.chunk_head[c];
-  int nv;
-  int64_t e0, csr0;
-  geom(page_off, len, w, c, h, &nv, &e0, &csr0);
-  const uint32_t m = keep_bits(keep, csr0, threadIdx.x * 4, nv);
+  const int4 m = w.meta[c];
+  const uint32_t bits = keep_bits(keep, (int64_t)m.z * PAGE, threadIdx.x * 4, m.w & 0xFFFF);
   int64_t tot;
-  block_exclusive_scan<NT>((int64_t)__popc(m), tmp, &tot);
-  if (threadIdx.x == 0) w.cnt[c] = (int32_t)tot;
+  block_exclusive_scan<NT>((int64_t)__popc(bits), tmp, &tot);
+  if (threadIdx.x == 0) {
+    w.cnt[c] = (int32_t)tot;
+    if (tot) atomicAdd(w.head_kept + m.x, (int32_t)tot);
+  }
 }
 
-__global__ void __launch_bounds__(1024) k_cmp_scan(int n_heads, int reserve, CmpWs w, int32_t* __restrict__ dst_off,
-                                                   int32_t* __restrict__ dst_len, int64_t* __restrict__ pages_used) {
+__global__ void __launch_bounds__(1024) k_cmp_headscan(int n_heads, int reserve, CmpWs w,
+                                                       int32_t* __restrict__ dst_off, int32_t* __restrict__ dst_len,
+                                                       int64_t* __restrict__ pages_used) {
   __shared__ int64_t tmp[1024 / WAVE + 1];
-  const int T = w.chunk_off[n_heads];
-  const int32_t* cnt = w.cnt;
-  block_scan_runs<1024>(T, [cnt](int i) { return (int64_t)cnt[i]; }, w.pk, tmp);
-  __syncthreads();
   int64_t carry = 0;
   for (int base = 0; base < n_heads; base += 1024) {
     const int h = base + threadIdx.x;
     int64_t pages = 0;
     if (h < n_heads) {
-      const int64_t kh = w.pk[w.chunk_off[h + 1]] - w.pk[w.chunk_off[h]];
+      const int64_t kh = w.head_kept[h];
       dst_len[h] = (int32_t)kh;
       pages = (kh + reserve + PAGE - 1) / PAGE;
     }
@@ -95,9 +95,7 @@ __global__ void __launch_bounds__(1024) k_cmp_scan(int n_heads, int reserve, Cmp
 }
 
 template <int ROWB>
-__global__ void __launch_bounds__(NT) k_cmp_scatter(const int32_t* __restrict__ page_off,
-                                                    const int32_t* __restrict__ page_ids,
-                                                    const int32_t* __restrict__ len, int n_heads,
+__global__ void __launch_bounds__(NT) k_cmp_scatter(int n_heads, const int32_t* __restrict__ page_ids,
                                                     const uint8_t* __restrict__ src_k,
                                                     const uint8_t* __restrict__ src_v,
                                                     const float* __restrict__ src_lnb,
@@ -109,47 +107,68 @@ __global__ void __launch_bounds__(NT) k_cmp_scatter(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ dst_pos, int64_t dst_pages) {
   constexpr int LPR = ROWB / 16;  // lanes per row (16 B each)
   constexpr int RPI = NT / LPR;   // rows per iteration
+  constexpr int UNR = 4;          // row iterations whose loads are issued together
   __shared__ int64_t tmp[NT / WAVE + 1];
   __shared__ int64_t src_slot[CS];
   __shared__ int32_t pids[CP];
-  // identity page ids of the destination pool
-  // (writes are bounded by the destination capacity even if the caller's
-  // max_kept_total promise was wrong)
+  // identity page ids of the destination pool (writes are bounded by the
+  // destination capacity even if the caller's max_kept_total was wrong)
   const int64_t total_dst = min((int64_t)dst_off[n_heads], dst_pages);
   for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < total_dst; i += (int64_t)gridDim.x * NT)
     dst_ids[i] = (int32_t)i;
   const int c = blockIdx.x;
   if (c >= w.chunk_off[n_heads]) return;
-  const int h = w.chunk_head[c];
-  int nv;
-  int64_t e0, csr0;
-  geom(page_off, len, w, c, h, &nv, &e0, &csr0);
   if (w.cnt[c] == 0) return;
+  const int4 m = w.meta[c];
+  const int h = m.x, nv = m.w & 0xFFFF;
+  const int64_t csr0 = (int64_t)m.z * PAGE;
+  // kept entries of the head's earlier chunks
+  int64_t before = 0;
+  for (int j = m.y + threadIdx.x; j < c; j += NT) before += w.cnt[j];
   const int npg = (nv + PAGE - 1) / PAGE;
-  if (threadIdx.x < npg) pids[threadIdx.x] = page_ids[page_off[h] + e0 / PAGE + threadIdx.x];
+  if (threadIdx.x < npg) pids[threadIdx.x] = page_ids[m.z + threadIdx.x];
+  int64_t tb;
+  block_exclusive_scan<NT>(before, tmp, &tb);
   const int i0 = threadIdx.x * 4;
-  const uint32_t m = keep_bits(keep, csr0, i0, nv);
+  const uint32_t bits = keep_bits(keep, csr0, i0, nv);
   int64_t nk;
-  int64_t r = block_exclusive_scan<NT>((int64_t)__popc(m), tmp, &nk);  // syncs: pids visible
+  int64_t r = block_exclusive_scan<NT>((int64_t)__popc(bits), tmp, &nk);  // syncs: pids visible
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    if (m & (1u << k)) {
+    if (bits & (1u << k)) {
       const int i = i0 + k;
       src_slot[r++] = (int64_t)pids[i / PAGE] * PAGE + (i % PAGE);
     }
   }
   __syncthreads();
-  const int64_t dbase = (int64_t)dst_off[h] * PAGE + (w.pk[c] - w.pk[w.chunk_off[h]]);
+  const int64_t dbase = (int64_t)dst_off[h] * PAGE + tb;
+  const int64_t dcap = dst_pages * PAGE;
   const int part = threadIdx.x % LPR;
-  for (int row = threadIdx.x / LPR; row < nk; row += RPI) {
-    const int64_t s = src_slot[row];
+  for (int row0 = threadIdx.x / LPR; row0 < nk; row0 += RPI * UNR) {
+    uint4 kv[UNR], vv[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      // rows past the end re-read the last kept row (not stored)
+      const int row = min(row0 + u * RPI, (int)nk - 1);
+      const int64_t s = src_slot[row];
+      kv[u] = *reinterpret_cast<const uint4*>(src_k + s * ROWB + part * 16);
+      vv[u] = *reinterpret_cast<const uint4*>(src_v + s * ROWB + part * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int row = row0 + u * RPI;
+      const int64_t d = dbase + row;
+      if (row < nk && d < dcap) {
+        *reinterpret_cast<uint4*>(dst_k + d * ROWB + part * 16) = kv[u];
+        *reinterpret_cast<uint4*>(dst_v + d * ROWB + part * 16) = vv[u];
+      }
+    }
+  }
+  // ln beta and position of the kept rows
+  for (int row = threadIdx.x; row < nk; row += NT) {
     const int64_t d = dbase + row;
-    if (d >= dst_pages * PAGE) break;
-    const uint4 kv = *reinterpret_cast<const uint4*>(src_k + s * ROWB + part * 16);
-    const uint4 vv = *reinterpret_cast<const uint4*>(src_v + s * ROWB + part * 16);
-    *reinterpret_cast<uint4*>(dst_k + d * ROWB + part * 16) = kv;
-    *reinterpret_cast<uint4*>(dst_v + d * ROWB + part * 16) = vv;
-    if (part == 0) {
+    if (d < dcap) {
+      const int64_t s = src_slot[row];
       dst_lnb[d] = src_lnb[s];
       dst_pos[d] = src_pos[s];
     }
@@ -159,8 +178,8 @@ __global__ void __launch_bounds__(NT) k_cmp_scatter(const int32_t* __restrict__ 
 CmpWs carve(const trimkv_cache_t* c, void* ws) {
   WsLayout L = compact_ws_layout(c);
   char* b = (char*)ws;
-  return CmpWs{(int32_t*)(b + L.off[0]), (int32_t*)(b + L.off[1]), (int32_t*)(b + L.off[2]),
-               (int64_t*)(b + L.off[3])};
+  return CmpWs{(int32_t*)(b + L.off[0]), (int4*)(b + L.off[1]), (int32_t*)(b + L.off[2]),
+               (int32_t*)(b + L.off[3])};
 }
 
 }  // namespace
@@ -169,9 +188,9 @@ WsLayout compact_ws_layout(const trimkv_cache_t* c) {
   const int64_t T = max_chunks(c, CP);
   WsLayout L;
   L.add(((int64_t)c->n_heads + 1) * 4);
+  L.add(T * 16);
   L.add(T * 4);
-  L.add(T * 4);
-  L.add((T + 1) * 8);
+  L.add((int64_t)c->n_heads * 4);
   return L;
 }
 
@@ -180,15 +199,16 @@ int launch_compact(const trimkv_cache_t* src, const uint8_t* keep, int reserve, 
   CmpWs w = carve(src, ws);
   const int64_t T = max_chunks(src, CP);
   const int H = src->n_heads;
-  hipLaunchKernelGGL(k_cmp_prep, dim3(1), dim3(1024), 0, st, src->page_off, H, w);
-  hipLaunchKernelGGL(k_cmp_count, dim3((unsigned)T), dim3(NT), 0, st, src->page_off, src->len, H, keep, w);
-  hipLaunchKernelGGL(k_cmp_scan, dim3(1), dim3(1024), 0, st, H, reserve, w, dst->page_off, dst->len, pages_used);
+  hipLaunchKernelGGL(k_cmp_prep, dim3(prep_grid(H, T, 1024)), dim3(1024), 0, st, src->page_off, src->len, H, w);
+  hipLaunchKernelGGL(k_cmp_count, dim3((unsigned)T), dim3(NT), 0, st, H, keep, w);
+  hipLaunchKernelGGL(k_cmp_headscan, dim3(1), dim3(1024), 0, st, H, reserve, w, dst->page_off, dst->len,
+                     pages_used);
   const int elt = src->dtype == TRIMKV_BF16 ? 2 : 4;
   const int rowb = src->head_dim * elt;
-#define TRIMKV_SCATTER(RB)                                                                                    \
-  hipLaunchKernelGGL(k_cmp_scatter<RB>, dim3((unsigned)T), dim3(NT), 0, st, src->page_off, src->page_ids,     \
-                     src->len, H, (const uint8_t*)src->k, (const uint8_t*)src->v, src->lnb, src->pos, keep, w, \
-                     dst->page_off, dst->page_ids, (uint8_t*)dst->k, (uint8_t*)dst->v, dst->lnb, dst->pos, dst->n_pages)
+#define TRIMKV_SCATTER(RB)                                                                                   \
+  hipLaunchKernelGGL(k_cmp_scatter<RB>, dim3((unsigned)T), dim3(NT), 0, st, H, src->page_ids,                \
+                     (const uint8_t*)src->k, (const uint8_t*)src->v, src->lnb, src->pos, keep, w, dst->page_off, \
+                     dst->page_ids, (uint8_t*)dst->k, (uint8_t*)dst->v, dst->lnb, dst->pos, dst->n_pages)
   switch (rowb) {
     case 128: TRIMKV_SCATTER(128); break;
     case 256: TRIMKV_SCATTER(256); break;

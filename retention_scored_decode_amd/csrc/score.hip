@@ -46,7 +46,7 @@ __global__ void __launch_bounds__(256) k_log_beta(const float* __restrict__ beta
     lnb[i] = ln_f32_cr(beta[i]);
 }
 
-// One thread per CSR slot; 16 pages per block.
+// 64 CSR pages per block, 4 slots per thread (16-byte loads and stores).
 __global__ void __launch_bounds__(256) k_score(const int32_t* __restrict__ page_off,
                                                const int32_t* __restrict__ page_ids,
                                                const int32_t* __restrict__ len,
@@ -54,20 +54,30 @@ __global__ void __launch_bounds__(256) k_score(const int32_t* __restrict__ page_
                                                const int32_t* __restrict__ pos, int n_heads,
                                                const int32_t* __restrict__ seg_head_begin, int n_seg,
                                                const int32_t* __restrict__ t, float* __restrict__ score) {
+  __shared__ PageHeads sh;
   const int64_t total = page_off[n_heads];
-  const int64_t c = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int j = threadIdx.x & 15;
+  const int64_t c0 = (int64_t)blockIdx.x * 64;
+  if (c0 >= total) return;
+  const PageHeads r = block_page_heads(page_off, n_heads, c0, min(c0 + 63, total - 1), &sh);
+  const int64_t c = c0 + (threadIdx.x >> 2);
+  const int j0 = (threadIdx.x & 3) * 4;
   if (c >= total) return;
-  const int h = upper_index(page_off, n_heads + 1, c);
+  const int h = r.hf == r.hl ? r.hf : head_in_range(page_off, r, c);
   const int s = upper_index(seg_head_begin, n_seg + 1, h);
-  const int64_t i = (c - page_off[h]) * PAGE + j;
-  float out = qnan();
-  if (i < len[h]) {
-    const int64_t slot = (int64_t)page_ids[c] * PAGE + j;
-    const float age = (float)(t[s] - pos[slot]);
-    out = __fmul_rn(age, lnb[slot]);
+  const int64_t i0 = (c - page_off[h]) * PAGE + j0;
+  const int64_t n = len[h];
+  float4 out = make_float4(qnan(), qnan(), qnan(), qnan());
+  if (i0 < n) {
+    const int64_t slot = (int64_t)page_ids[c] * PAGE + j0;
+    const float4 l = *reinterpret_cast<const float4*>(lnb + slot);
+    const int4 p = *reinterpret_cast<const int4*>(pos + slot);
+    const int tt = t[s];
+    out.x = __fmul_rn((float)(tt - p.x), l.x);
+    if (i0 + 1 < n) out.y = __fmul_rn((float)(tt - p.y), l.y);
+    if (i0 + 2 < n) out.z = __fmul_rn((float)(tt - p.z), l.z);
+    if (i0 + 3 < n) out.w = __fmul_rn((float)(tt - p.w), l.w);
   }
-  score[c * PAGE + j] = out;
+  *reinterpret_cast<float4*>(score + c * PAGE + j0) = out;
 }
 
 // One wave per head: write entry len[h] and bump len[h].
@@ -106,7 +116,7 @@ int launch_log_beta(const float* beta, float* lnb, int64_t n, hipStream_t st) {
 
 int launch_score(const trimkv_cache_t* c, int n_seg, const int32_t* seg, const int32_t* t, float* score,
                  hipStream_t st) {
-  int64_t blocks = (c->n_pages + 15) / 16;
+  int64_t blocks = (c->n_pages + 63) / 64;
   if (blocks == 0) return TRIMKV_OK;
   hipLaunchKernelGGL(k_score, dim3((unsigned)blocks), dim3(256), 0, st, c->page_off, c->page_ids, c->len,
                      c->lnb, c->pos, c->n_heads, seg, n_seg, t, score);

@@ -9,14 +9,16 @@
 //   1. scores -> order-preserving uint32 keys (-0.0 == +0.0);
 //   2. three radix passes (11, 11, 10 bits) find K*, the M-th largest key,
 //      and need = M - #{key > K*}: per-block LDS histograms, flushed with
-//      device atomics into a per-segment histogram; the last block to finish
-//      a segment scans its histogram and narrows the prefix;
-//   3. per 1024-slot chunk: #{key > K*} and #{key == K*};
-//   4. one block scans the tie counts in (head, slot) order: chunk c keeps
-//      gt_c + clamp(need - E_c, 0, eq_c), E_c = ties in earlier chunks;
-//   5. per chunk: keep = key > K*, or key == K* and its tie rank < need.
-// Since CSR order within a segment is head order and, within a head, slot
-// (= position) order, this realises "score desc, head asc, position asc".
+//      device atomics into a per-segment histogram; every block of the next
+//      kernel scans the finished histogram of its segment to narrow the
+//      prefix (no inter-block waits, no cache flushes inside a kernel);
+//   3. one pass over 1024-slot chunks in (head, slot) order: each chunk
+//      counts its ties (key == K*), obtains the ties of all earlier chunks of
+//      its segment by a decoupled look-back (one wave reads 64 predecessor
+//      words at a time; value and flag share one 64-bit word), and keeps
+//      key > K* plus the ties whose rank in the segment is below `need`.
+// CSR order within a segment is head order and, within a head, slot
+// (= position) order, so this realises "score desc, head asc, position asc".
 #include <algorithm>
 
 #include "common.h"
@@ -31,258 +33,198 @@ constexpr int CS = CP * PAGE;   // slots per chunk
 constexpr int NT = 256;         // threads per chunk block (4 slots each)
 constexpr int CPB = 8;          // chunks per histogram block
 constexpr int HIST_WORDS = 2048 + 2048 + 1024;
+constexpr uint32_t SPIN_LIMIT = 1u << 26;
 
 enum { MODE_NORMAL = 0, MODE_ALL = 1, MODE_NONE = 2 };
 
 struct SegState {
   int64_t remaining;  // 1-based rank of the target key among keys matching `prefix`
   int64_t n_valid;
+  int64_t ties;       // keys in the located bin (after the last pass: keys equal to K*)
   uint32_t prefix;
   int32_t mode;
   int32_t chunk_begin, chunk_end;
 };
 
+// chunk metadata: x = head, y = segment, z = first CSR page,
+// w = valid entries | (pages of the chunk << 16)
 struct SelWs {
   int32_t* chunk_off;   // [H + 1]
-  int32_t* chunk_head;  // [Tmax]
-  int32_t* seg_of;      // [H]
-  SegState* seg;        // [n_seg]
+  int4* meta;           // [Tmax]
+  SegState* seg;        // [4][n_seg]: state before radix pass 0, 1, 2 and the final state
+  int n_seg;
   uint32_t* hist;       // [n_seg][HIST_WORDS]
-  uint32_t* done;       // [n_seg][4]
-  int32_t* cnt;         // [Tmax][2]  (gt, eq)
-  int64_t* p_gt;        // [Tmax + 1] exclusive prefix over chunks of gt
-  int64_t* p_eq;        // [Tmax + 1] exclusive prefix over chunks of eq
+  uint64_t* look;       // [Tmax] look-back words: 0 | flag<<62 | value
+  uint32_t* ticket;     // [2 + n_seg]: [1] error flag, [2 + s] ticket of segment s
+  uint32_t* error;      // nonzero if a look-back wait timed out
   double* part;         // [Tmax]
 };
 
-struct CacheView {
-  const int32_t* page_off;
-  const int32_t* len;
-  int n_heads;
-};
+constexpr uint64_t LB_AGG = 1ull << 62, LB_PREFIX = 2ull << 62, LB_VAL = (1ull << 62) - 1;
 
 __device__ __forceinline__ int pass_bits(int pass) { return pass == 2 ? 10 : 11; }
 __device__ __forceinline__ uint32_t* pass_hist(const SelWs& w, int s, int pass) {
   return w.hist + (size_t)s * HIST_WORDS + (pass == 0 ? 0 : pass == 1 ? 2048 : 4096);
 }
 
-// valid entries and first CSR slot of chunk c of head h
-__device__ __forceinline__ void chunk_geom(const CacheView& cv, const SelWs& w, int c, int h, int* nv,
-                                           int64_t* csr0, int* nslots) {
-  const int64_t e0 = (int64_t)(c - w.chunk_off[h]) * CS;
-  const int64_t np = (int64_t)cv.page_off[h + 1] - cv.page_off[h];
-  int64_t v = (int64_t)cv.len[h] - e0;
-  *nv = (int)(v < 0 ? 0 : (v > CS ? CS : v));
-  *csr0 = (int64_t)cv.page_off[h] * PAGE + e0;
-  int64_t ns = np * PAGE - e0;
-  *nslots = (int)(ns > CS ? CS : ns);
-}
-
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(1024) k_sel_prep(CacheView cv, int n_seg, const int32_t* __restrict__ seg_hb,
-                                                   const int64_t* __restrict__ budget, SelWs w) {
-  // every block: clear histograms and completion counters
-  const size_t nclear = (size_t)n_seg * HIST_WORDS;
-  for (size_t i = (size_t)blockIdx.x * 1024 + threadIdx.x; i < nclear; i += (size_t)gridDim.x * 1024)
-    w.hist[i] = 0u;
-  for (size_t i = (size_t)blockIdx.x * 1024 + threadIdx.x; i < (size_t)n_seg * 4; i += (size_t)gridDim.x * 1024)
-    w.done[i] = 0u;
-  if (blockIdx.x != 0) return;
+// prep: chunk list + metadata + segment state (block 0); every block clears
+// histograms, kept[] and look-back words.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024) k_sel_prep(const int32_t* __restrict__ page_off,
+                                                   const int32_t* __restrict__ len, int n_heads, int n_seg,
+                                                   const int32_t* __restrict__ seg_hb,
+                                                   const int64_t* __restrict__ budget, int64_t tmax, SelWs w,
+                                                   int32_t* __restrict__ kept) {
+  const size_t gtid = (size_t)blockIdx.x * 1024 + threadIdx.x, gstride = (size_t)gridDim.x * 1024;
+  for (size_t i = gtid; i < (size_t)n_seg * HIST_WORDS; i += gstride) w.hist[i] = 0u;
+  for (size_t i = gtid; i < (size_t)tmax; i += gstride) w.look[i] = 0ull;
+  for (size_t i = gtid; i < (size_t)n_heads; i += gstride) kept[i] = 0;
+  for (size_t i = gtid; i < (size_t)n_seg + 2; i += gstride) w.ticket[i] = 0u;
   __shared__ int64_t tmp[1024 / WAVE + 1];
-  build_chunk_list<1024>(cv.page_off, cv.n_heads, CP, w.chunk_off, w.chunk_head, tmp);
-  __syncthreads();
-  for (int s = threadIdx.x; s < n_seg; s += 1024) {
-    const int hb = seg_hb[s], he = seg_hb[s + 1];
-    for (int h = hb; h < he; ++h) w.seg_of[h] = s;
-    SegState st;
-    st.remaining = budget[s];
-    st.n_valid = 0;
-    st.prefix = 0u;
-    st.chunk_begin = w.chunk_off[hb];
-    st.chunk_end = w.chunk_off[he];
-    st.mode = (budget[s] <= 0 || st.chunk_begin == st.chunk_end) ? MODE_NONE : MODE_NORMAL;
-    w.seg[s] = st;
+  __shared__ PrepLDS L;
+  const int T = prep_chunks<1024>(page_off, len, n_heads, CP, L, tmp, w.chunk_off);
+  const bool single = n_heads > PREP_HMAX;   // then one block and a global scan
+  if (blockIdx.x == 0) {
+    for (int s = threadIdx.x; s < n_seg; s += 1024) {
+      const int hb = seg_hb[s], he = seg_hb[s + 1];
+      SegState st;
+      st.remaining = budget[s];
+      st.n_valid = 0;
+      st.ties = 0;
+      st.prefix = 0u;
+      st.chunk_begin = single ? w.chunk_off[hb] : L.off[hb];
+      st.chunk_end = single ? w.chunk_off[he] : L.off[he];
+      st.mode = (budget[s] <= 0 || st.chunk_begin == st.chunk_end) ? MODE_NONE : MODE_NORMAL;
+      w.seg[s] = st;
+    }
+  }
+  for (int c = blockIdx.x * 1024 + threadIdx.x; c < T; c += gridDim.x * 1024) {
+    const ChunkInfo ci = chunk_info(L, w.chunk_off, page_off, len, n_heads, CP, c);
+    const int s = upper_index(seg_hb, n_seg + 1, ci.h);
+    w.meta[c] = make_int4(ci.h, s, ci.page0, ci.nv | (ci.npg << 16));
   }
 }
 
-// Last block of a segment: locate the bin holding the target rank.
-__device__ void sel_find(const SelWs& w, int s, int pass) {
+// State of segment s after radix pass `pass`, computed by a whole block from
+// the finished histogram of that pass (every thread gets the result); the
+// designated block stores it as the state before the next pass.
+__device__ SegState state_after(const SelWs& w, int s, int pass, bool store) {
   __shared__ int64_t tmp[NT / WAVE + 1];
-  const int nb = pass == 2 ? 1024 : 2048;
-  const int per = nb / NT;  // 8 or 4
-  const uint32_t* g = pass_hist(w, s, pass);
-  uint32_t c[8];
-  int64_t tsum = 0;
-  for (int k = 0; k < per; ++k) {
-    c[k] = __hip_atomic_load(g + threadIdx.x * per + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    tsum += c[k];
-  }
-  int64_t total;
-  const int64_t ex = block_exclusive_scan<NT>(tsum, tmp, &total);
-  const int64_t above = total - ex - tsum;  // keys in bins of higher threads
-  SegState st = w.seg[s];
-  if (pass == 0) {
-    if (threadIdx.x == 0) {
-      w.seg[s].n_valid = total;
-      if (st.remaining >= total) w.seg[s].mode = total == 0 ? MODE_NONE : MODE_ALL;
+  __shared__ uint32_t sh_prefix;
+  __shared__ int64_t sh_rem, sh_ties;
+  SegState st = w.seg[(size_t)pass * w.n_seg + s];
+  if (st.mode == MODE_NORMAL) {
+    const int nb = pass == 2 ? 1024 : 2048;
+    const int per = nb / NT;  // 8 or 4
+    const uint32_t* g = pass_hist(w, s, pass);
+    uint32_t c[8];
+    int64_t tsum = 0;
+    for (int k = 0; k < per; ++k) {
+      c[k] = g[threadIdx.x * per + k];
+      tsum += c[k];
     }
-    if (st.remaining >= total) return;
-  }
-  const int64_t r = st.remaining;
-  if (above < r && r <= above + tsum) {
-    int64_t cum = above;
-    for (int k = per - 1; k >= 0; --k) {
-      if (cum + c[k] >= r) {
-        w.seg[s].remaining = r - cum;
-        w.seg[s].prefix = (st.prefix << pass_bits(pass)) | (uint32_t)(threadIdx.x * per + k);
-        break;
+    int64_t total;
+    const int64_t ex = block_exclusive_scan<NT>(tsum, tmp, &total);
+    const int64_t above = total - ex - tsum;  // keys in bins of higher threads
+    if (pass == 0) {
+      st.n_valid = total;
+      if (st.remaining >= total) st.mode = total == 0 ? MODE_NONE : MODE_ALL;
+    }
+    if (st.mode == MODE_NORMAL) {
+      const int64_t r = st.remaining;
+      if (above < r && r <= above + tsum) {
+        int64_t cum = above;
+        for (int k = per - 1; k >= 0; --k) {
+          if (cum + c[k] >= r) {
+            sh_rem = r - cum;
+            sh_ties = c[k];
+            sh_prefix = (st.prefix << pass_bits(pass)) | (uint32_t)(threadIdx.x * per + k);
+            break;
+          }
+          cum += c[k];
+        }
       }
-      cum += c[k];
+      __syncthreads();
+      st.remaining = sh_rem;
+      st.prefix = sh_prefix;
+      st.ties = sh_ties;
+      __syncthreads();
     }
   }
+  if (store && threadIdx.x == 0) w.seg[(size_t)(pass + 1) * w.n_seg + s] = st;
+  return st;
 }
 
 template <int PASS>
-__global__ void __launch_bounds__(NT) k_sel_hist(CacheView cv, const float* __restrict__ score, SelWs w) {
+__device__ __forceinline__ void hist_add(uint32_t* lh, uint32_t key, uint32_t pre) {
+  if (PASS == 0) {
+    atomicAdd(&lh[key >> 21], 1u);
+  } else if (PASS == 1) {
+    if ((key >> 21) == pre) atomicAdd(&lh[(key >> 10) & 2047u], 1u);
+  } else {
+    if ((key >> 10) == pre) atomicAdd(&lh[key & 1023u], 1u);
+  }
+}
+
+// Block b histograms chunks [b*CPB, b*CPB + CPB): metadata first, then every
+// key load in flight while the previous pass's bin is located.
+template <int PASS>
+__global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __restrict__ score, SelWs w) {
   constexpr int NB = PASS == 2 ? 1024 : 2048;
   __shared__ uint32_t lh[NB];
-  __shared__ int sh_mode, sh_last;
-  __shared__ uint32_t sh_prefix;
-  const int T = w.chunk_off[cv.n_heads];
+  __shared__ int4 sm[CPB];
+  const int T = w.chunk_off[n_heads];
   const int c0 = blockIdx.x * CPB;
   if (c0 >= T) return;
-  const int c1 = min(c0 + CPB, T);
+  const int nc = min(CPB, T - c0);
+  if (threadIdx.x < nc) sm[threadIdx.x] = w.meta[c0 + threadIdx.x];
   for (int b = threadIdx.x; b < NB; b += NT) lh[b] = 0u;
-  int cur = -1;
-  auto flush = [&](int s) {
-    __syncthreads();
-    uint32_t* g = pass_hist(w, s, PASS);
-    for (int b = threadIdx.x; b < NB; b += NT) {
-      uint32_t v = lh[b];
-      if (v) { atomicAdd(g + b, v); lh[b] = 0u; }
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const SegState& st = w.seg[s];
-      const int nblk = (st.chunk_end - 1) / CPB - st.chunk_begin / CPB + 1;
-      uint32_t old = __hip_atomic_fetch_add(w.done + (size_t)s * 4 + PASS, 1u, __ATOMIC_ACQ_REL,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-      sh_last = (old + 1u == (uint32_t)nblk);
-    }
-    __syncthreads();
-    if (sh_last) {
-      __threadfence();
-      sel_find(w, s, PASS);
-    }
-    __syncthreads();
-  };
-  for (int c = c0; c < c1; ++c) {
-    const int h = w.chunk_head[c];
-    const int s = w.seg_of[h];
-    if (s != cur) {
-      if (cur >= 0 && sh_mode == MODE_NORMAL) flush(cur);
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        sh_mode = w.seg[s].mode;
-        sh_prefix = w.seg[s].prefix;
-      }
-      __syncthreads();
-      cur = s;
-    }
-    if (sh_mode != MODE_NORMAL) continue;
-    int nv, nslots;
-    int64_t csr0;
-    chunk_geom(cv, w, c, h, &nv, &csr0, &nslots);
-    const int i0 = threadIdx.x * 4;
-    if (i0 < nv) {
-      const float4 sv = *reinterpret_cast<const float4*>(score + csr0 + i0);
-      const float a[4] = {sv.x, sv.y, sv.z, sv.w};
-      const uint32_t pre = sh_prefix;
+  __syncthreads();
+  float4 kv[CPB];
+  const int i0 = threadIdx.x * 4;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (i0 + k < nv) {
-          const uint32_t key = score_key(a[k]);
-          if (PASS == 0) {
-            atomicAdd(&lh[key >> 21], 1u);
-          } else if (PASS == 1) {
-            if ((key >> 21) == pre) atomicAdd(&lh[(key >> 10) & 2047u], 1u);
-          } else {
-            if ((key >> 10) == pre) atomicAdd(&lh[key & 1023u], 1u);
-          }
+  for (int i = 0; i < CPB; ++i) {
+    if (i < nc && i0 < (sm[i].w & 0xFFFF))
+      kv[i] = *reinterpret_cast<const float4*>(score + (int64_t)sm[i].z * PAGE + i0);
+  }
+  int i = 0;
+  while (i < nc) {
+    // run of consecutive chunks of one segment
+    const int s = sm[i].y;
+    int e = i + 1;
+    while (e < nc && sm[e].y == s) ++e;
+    SegState st;
+    if (PASS == 0) {
+      st = w.seg[s];
+    } else {
+      const int first_blk = w.seg[s].chunk_begin / CPB;
+      st = state_after(w, s, PASS - 1, (int)blockIdx.x == first_blk);
+    }
+    if (st.mode == MODE_NORMAL) {
+      const uint32_t pre = st.prefix;
+#pragma unroll
+      for (int k = 0; k < CPB; ++k) {
+        if (k >= i && k < e) {
+          const int nv = sm[k].w & 0xFFFF;
+          const float a[4] = {kv[k].x, kv[k].y, kv[k].z, kv[k].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (i0 + j < nv) hist_add<PASS>(lh, score_key(a[j]), pre);
         }
       }
-    }
-  }
-  if (cur >= 0 && sh_mode == MODE_NORMAL) flush(cur);
-}
-
-__device__ __forceinline__ int64_t block_sum_i64(int64_t v, int64_t* tmp) {
-  int64_t tot;
-  block_exclusive_scan<NT>(v, tmp, &tot);
-  return tot;
-}
-
-__global__ void __launch_bounds__(NT) k_sel_count(CacheView cv, const float* __restrict__ score, SelWs w) {
-  __shared__ int64_t tmp[NT / WAVE + 1];
-  const int c = blockIdx.x;
-  const int T = w.chunk_off[cv.n_heads];
-  if (c >= T) return;
-  const int h = w.chunk_head[c];
-  const SegState st = w.seg[w.seg_of[h]];
-  int nv, nslots;
-  int64_t csr0;
-  chunk_geom(cv, w, c, h, &nv, &csr0, &nslots);
-  int gt = 0, eq = 0;
-  const int i0 = threadIdx.x * 4;
-  if (st.mode == MODE_ALL) {
-    gt = max(0, min(4, nv - i0));
-  } else if (st.mode == MODE_NORMAL && i0 < nv) {
-    const float4 sv = *reinterpret_cast<const float4*>(score + csr0 + i0);
-    const float a[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (i0 + k < nv) {
-        const uint32_t key = score_key(a[k]);
-        gt += key > st.prefix;
-        eq += key == st.prefix;
+      __syncthreads();
+      uint32_t* g = pass_hist(w, s, PASS);
+      for (int b = threadIdx.x; b < NB; b += NT) {
+        const uint32_t v = lh[b];
+        if (v) {
+          atomicAdd(g + b, v);
+          lh[b] = 0u;
+        }
       }
+      __syncthreads();
     }
-  }
-  const int64_t packed = ((int64_t)gt << 32) | (int64_t)eq;
-  const int64_t tot = block_sum_i64(packed, tmp);
-  if (threadIdx.x == 0) {
-    w.cnt[2 * (size_t)c] = (int32_t)(tot >> 32);
-    w.cnt[2 * (size_t)c + 1] = (int32_t)(tot & 0xFFFFFFFF);
-  }
-}
-
-// Prefix sums of (gt, eq) over all chunks; kept[h] follows by telescoping:
-// the ties a head takes from its consecutive chunks are
-// clamp(need - E_first, 0, E_end - E_first), E = ties before, in the segment.
-__global__ void __launch_bounds__(1024) k_sel_scan(CacheView cv, SelWs w, int32_t* __restrict__ kept) {
-  __shared__ int64_t tmp[1024 / WAVE + 1];
-  const int H = cv.n_heads;
-  const int T = w.chunk_off[H];
-  const int32_t* cnt = w.cnt;
-  block_scan_runs<1024>(T, [cnt](int i) { return (int64_t)cnt[2 * (size_t)i]; }, w.p_gt, tmp);
-  block_scan_runs<1024>(T, [cnt](int i) { return (int64_t)cnt[2 * (size_t)i + 1]; }, w.p_eq, tmp);
-  __syncthreads();
-  for (int h = threadIdx.x; h < H; h += 1024) {
-    const SegState st = w.seg[w.seg_of[h]];
-    const int cb = w.chunk_off[h], ce = w.chunk_off[h + 1];
-    const int64_t gt = w.p_gt[ce] - w.p_gt[cb];
-    int64_t k = 0;
-    if (st.mode == MODE_ALL) {
-      k = gt;
-    } else if (st.mode == MODE_NORMAL) {
-      const int64_t e_first = w.p_eq[cb] - w.p_eq[st.chunk_begin];
-      const int64_t e_end = w.p_eq[ce] - w.p_eq[st.chunk_begin];
-      int64_t take = st.remaining - e_first;
-      take = take < 0 ? 0 : (take > e_end - e_first ? e_end - e_first : take);
-      k = gt + take;
-    }
-    kept[h] = (int32_t)k;
+    i = e;
   }
 }
 
@@ -299,21 +241,41 @@ __device__ __forceinline__ double block_sum_f64(double v, double* tmpd) {
   return r;
 }
 
-__global__ void __launch_bounds__(NT) k_sel_decide(CacheView cv, const float* __restrict__ score, SelWs w,
-                                                   uint8_t* __restrict__ keep, int want_sum) {
+// ---------------------------------------------------------------------------
+// decide: chunks in ticket order; ties of earlier chunks of the segment by a
+// decoupled look-back; keep flags; kept[head] by atomics.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __restrict__ score, SelWs w,
+                                                   uint8_t* __restrict__ keep, int32_t* __restrict__ kept,
+                                                   int want_sum) {
   __shared__ int64_t tmp[NT / WAVE + 1];
   __shared__ double tmpd[NT / WAVE];
-  const int c = blockIdx.x;
-  const int T = w.chunk_off[cv.n_heads];
+  __shared__ int sh_c;
+  __shared__ int64_t sh_excl;
+  int c = blockIdx.x;
+  const int T = w.chunk_off[n_heads];
   if (c >= T) return;
-  const int h = w.chunk_head[c];
-  const SegState st = w.seg[w.seg_of[h]];
-  int nv, nslots;
-  int64_t csr0;
-  chunk_geom(cv, w, c, h, &nv, &csr0, &nslots);
+  int4 m = w.meta[c];
+  const int cb = w.seg[m.y].chunk_begin;
+  const SegState st = state_after(w, m.y, 2, c == cb);
+  // Ranks among the ties are needed only when the ties straddle the budget
+  // (more keys equal K* than `need`); otherwise every tie is kept and chunks
+  // are independent.  In the straddling case the segment's blocks take
+  // chunks in the order of a per-segment ticket, so every chunk a block waits
+  // for belongs to a block that is already running.
+  const bool ranked = st.mode == MODE_NORMAL && st.ties > st.remaining;
+  if (ranked) {
+    if (threadIdx.x == 0) sh_c = cb + (int)atomicAdd(w.ticket + 2 + m.y, 1u);
+    __syncthreads();
+    c = sh_c;
+    m = w.meta[c];
+  }
+  const int nv = m.w & 0xFFFF;
+  const int nslots = (m.w >> 16) * PAGE;   // slots of the chunk's pages
+  const int64_t csr0 = (int64_t)m.z * PAGE;
   const int i0 = threadIdx.x * 4;
   float a[4] = {0.f, 0.f, 0.f, 0.f};
-  if (i0 < nv && st.mode != MODE_NONE) {
+  if (i0 < nv) {
     const float4 sv = *reinterpret_cast<const float4*>(score + csr0 + i0);
     a[0] = sv.x; a[1] = sv.y; a[2] = sv.z; a[3] = sv.w;
   }
@@ -331,8 +293,50 @@ __global__ void __launch_bounds__(NT) k_sel_decide(CacheView cv, const float* __
 #pragma unroll
     for (int k = 0; k < 4; ++k) gtm |= (uint32_t)(i0 + k < nv) << k;
   }
-  int64_t tot;
-  int64_t rank = (w.p_eq[c] - w.p_eq[st.chunk_begin]) + block_exclusive_scan<NT>((int64_t)__popc(eqm), tmp, &tot);
+  int64_t eq_total;
+  int64_t rank = block_exclusive_scan<NT>((int64_t)__popc(eqm), tmp, &eq_total);
+  if (ranked) {
+    if (threadIdx.x < WAVE) {
+      const int lane = threadIdx.x;
+      int64_t excl = 0;
+      if (c != cb) {
+        if (lane == 0)
+          __hip_atomic_store(w.look + c, LB_AGG | (uint64_t)eq_total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int base = c - 1;   // window: chunks base, base-1, ..., base-63
+        uint32_t spins = 0;
+        while (true) {
+          const int j = base - lane;
+          // before the segment's first chunk: a zero prefix
+          const uint64_t v = j >= cb ? __hip_atomic_load(w.look + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                     : LB_PREFIX;
+          const uint64_t zm = __ballot(v == 0ull);
+          const uint64_t pm = __ballot((v & ~LB_VAL) == LB_PREFIX);
+          const int first = pm ? __ffsll((long long)pm) - 1 : WAVE;   // nearest prefix in the window
+          const uint64_t need = first == WAVE ? ~0ull : ((2ull << first) - 1ull);
+          if (zm & need) {  // a predecessor has not published yet
+            if (++spins > SPIN_LIMIT) {  // never expected; keeps every wave finite
+              if (lane == 0) atomicOr(w.error, 1u);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            continue;
+          }
+          int64_t val = (lane <= first) ? (int64_t)(v & LB_VAL) : 0;
+          for (int d = WAVE / 2; d > 0; d >>= 1) val += __shfl_xor(val, d, WAVE);
+          excl += val;
+          if (pm) break;
+          base -= WAVE;
+        }
+      }
+      if (lane == 0) {
+        __hip_atomic_store(w.look + c, LB_PREFIX | (uint64_t)(excl + eq_total), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        sh_excl = excl;
+      }
+    }
+    __syncthreads();
+    rank += sh_excl;
+  }
   uint32_t km = gtm;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -345,6 +349,9 @@ __global__ void __launch_bounds__(NT) k_sel_decide(CacheView cv, const float* __
     const uint32_t word = (km & 1u) | ((km & 2u) << 7) | ((km & 4u) << 14) | ((km & 8u) << 21);
     *reinterpret_cast<uint32_t*>(keep + csr0 + i0) = word;
   }
+  int64_t kcount;
+  block_exclusive_scan<NT>((int64_t)__popc(km), tmp, &kcount);
+  if (threadIdx.x == 0 && kcount) atomicAdd(kept + m.x, (int32_t)kcount);
   if (want_sum) {
     double sum = 0.0;
 #pragma unroll
@@ -355,9 +362,9 @@ __global__ void __launch_bounds__(NT) k_sel_decide(CacheView cv, const float* __
   }
 }
 
-__global__ void k_sel_headsum(CacheView cv, SelWs w, double* __restrict__ keptsum) {
+__global__ void k_sel_headsum(int n_heads, SelWs w, double* __restrict__ keptsum) {
   const int h = blockIdx.x * blockDim.x + threadIdx.x;
-  if (h >= cv.n_heads) return;
+  if (h >= n_heads) return;
   double s = 0.0;
   for (int c = w.chunk_off[h]; c < w.chunk_off[h + 1]; ++c) s += w.part[c];
   keptsum[h] = s;
@@ -368,15 +375,14 @@ SelWs carve(const trimkv_cache_t* c, int n_seg, void* ws) {
   char* b = (char*)ws;
   SelWs w;
   w.chunk_off = (int32_t*)(b + L.off[0]);
-  w.chunk_head = (int32_t*)(b + L.off[1]);
-  w.seg_of = (int32_t*)(b + L.off[2]);
-  w.seg = (SegState*)(b + L.off[3]);
-  w.hist = (uint32_t*)(b + L.off[4]);
-  w.done = (uint32_t*)(b + L.off[5]);
-  w.cnt = (int32_t*)(b + L.off[6]);
-  w.p_gt = (int64_t*)(b + L.off[7]);
-  w.p_eq = (int64_t*)(b + L.off[8]);
-  w.part = (double*)(b + L.off[9]);
+  w.meta = (int4*)(b + L.off[1]);
+  w.seg = (SegState*)(b + L.off[2]);
+  w.n_seg = n_seg;
+  w.hist = (uint32_t*)(b + L.off[3]);
+  w.look = (uint64_t*)(b + L.off[4]);
+  w.ticket = (uint32_t*)(b + L.off[5]);
+  w.error = w.ticket + 1;
+  w.part = (double*)(b + L.off[6]);
   return w;
 }
 
@@ -387,14 +393,11 @@ WsLayout select_ws_layout(const trimkv_cache_t* c, int n_seg) {
   const int64_t H = c->n_heads;
   WsLayout L;
   L.add((H + 1) * 4);
-  L.add(T * 4);
-  L.add(H * 4);
-  L.add((size_t)n_seg * sizeof(SegState));
+  L.add(T * 16);
+  L.add((size_t)4 * n_seg * sizeof(SegState));
   L.add((size_t)n_seg * HIST_WORDS * 4);
-  L.add((size_t)n_seg * 16);
   L.add(T * 8);
-  L.add((T + 1) * 8);
-  L.add((T + 1) * 8);
+  L.add(((size_t)n_seg + 2) * 4);
   L.add(T * 8);
   return L;
 }
@@ -403,19 +406,18 @@ int launch_select(const trimkv_cache_t* c, const float* score, int n_seg, const 
                   const int64_t* budget, uint8_t* keep, int32_t* kept, double* keptsum, void* ws,
                   hipStream_t st) {
   SelWs w = carve(c, n_seg, ws);
-  CacheView cv{c->page_off, c->len, c->n_heads};
   const int64_t T = max_chunks(c, CP);
-  int prep_blocks = (int)std::min<int64_t>(64, ((int64_t)n_seg * HIST_WORDS + 1023) / 1024 + 1);
-  hipLaunchKernelGGL(k_sel_prep, dim3(prep_blocks), dim3(1024), 0, st, cv, n_seg, seg, budget, w);
+  const int prep_blocks = prep_grid(c->n_heads, T, 1024);
+  hipLaunchKernelGGL(k_sel_prep, dim3(prep_blocks), dim3(1024), 0, st, c->page_off, c->len, c->n_heads, n_seg, seg,
+                     budget, T, w, kept);
   const unsigned hb = (unsigned)((T + CPB - 1) / CPB);
-  hipLaunchKernelGGL(k_sel_hist<0>, dim3(hb), dim3(NT), 0, st, cv, score, w);
-  hipLaunchKernelGGL(k_sel_hist<1>, dim3(hb), dim3(NT), 0, st, cv, score, w);
-  hipLaunchKernelGGL(k_sel_hist<2>, dim3(hb), dim3(NT), 0, st, cv, score, w);
-  hipLaunchKernelGGL(k_sel_count, dim3((unsigned)T), dim3(NT), 0, st, cv, score, w);
-  hipLaunchKernelGGL(k_sel_scan, dim3(1), dim3(1024), 0, st, cv, w, kept);
-  hipLaunchKernelGGL(k_sel_decide, dim3((unsigned)T), dim3(NT), 0, st, cv, score, w, keep, keptsum != nullptr);
+  hipLaunchKernelGGL(k_sel_hist<0>, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w);
+  hipLaunchKernelGGL(k_sel_hist<1>, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w);
+  hipLaunchKernelGGL(k_sel_hist<2>, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w);
+  hipLaunchKernelGGL(k_sel_decide, dim3((unsigned)T), dim3(NT), 0, st, c->n_heads, score, w, keep, kept,
+                     keptsum != nullptr);
   if (keptsum)
-    hipLaunchKernelGGL(k_sel_headsum, dim3((unsigned)((c->n_heads + 255) / 256)), dim3(256), 0, st, cv, w,
+    hipLaunchKernelGGL(k_sel_headsum, dim3((unsigned)((c->n_heads + 255) / 256)), dim3(256), 0, st, c->n_heads, w,
                        keptsum);
   return check_launch();
 }

@@ -143,8 +143,9 @@ def _rng(seed: int, stream: int, index: int = 0) -> np.random.Generator:
 
 def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """float64 -> float32 (RNE) -> bfloat16 (RNE); returns uint16 bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    # finite inputs only: the rounding increment cannot carry out of 32 bits
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return r.astype(np.uint16)
 
 
@@ -251,7 +252,7 @@ def empty_pool(n_pages: int, d: int, dtype: str):
 
 
 def build_cache(w: Workload, heads: Optional[list] = None, lengths: Optional[np.ndarray] = None,
-                perm: Optional[np.ndarray] = None, extra_pages: int = 0) -> PagedCache:
+                perm: Optional[np.ndarray] = None, extra_pages: int = 0, workers: int = 1) -> PagedCache:
     """Prefill pool for workload w.
 
     Every head holds positions 0..len-1 in slot order (len = ctx unless
@@ -271,10 +272,11 @@ def build_cache(w: Workload, heads: Optional[list] = None, lengths: Optional[np.
     if perm is None:
         perm = _rng(w.seed, S_PERM).permutation(n_pages).astype(np.int32)
     k, v, beta, pos = empty_pool(n_pages, D, w.dtype)
-    for h in range(H):
+
+    def fill(h):
         n = int(lengths[h])
         if n == 0:
-            continue
+            return
         bh = head_beta(w, h)[:n]
         kh, vh = head_kv(w, h)
         kh, vh = kh[:n], vh[:n]
@@ -284,6 +286,15 @@ def build_cache(w: Workload, heads: Optional[list] = None, lengths: Optional[np.
         v.reshape(-1, D)[slots] = vh
         beta.reshape(-1)[slots] = bh
         pos.reshape(-1)[slots] = np.arange(n, dtype=np.int32)
+
+    # heads write disjoint slots, so threads may fill them concurrently
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(fill, range(H)))
+    else:
+        for h in range(H):
+            fill(h)
     return PagedCache(k, v, beta, pos, page_off.astype(np.int32), perm.astype(np.int32),
                       lengths.copy(), D, w.dtype)
 
