@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--cold-reps", type=int, default=10, help="flushed repetitions of the decode stage")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="llama8b_32k")
+    ap.add_argument("--calib", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args()
 
 
@@ -77,11 +79,10 @@ def main():
     def bf(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
-    beta = up(pc.beta)
-    lnb = torch.empty_like(beta)
-    tk.log_beta(beta, lnb)
-    src = tk.Cache(bf(pc.k), bf(pc.v), lnb, up(pc.pos), up(pc.page_off), up(pc.page_ids), up(pc.length))
-    del beta
+    meta = torch.zeros((pc.n_pages, 2, 16), dtype=torch.int32, device=dev)
+    meta[:, 1, :] = up(pc.pos)
+    tk.log_beta(up(pc.beta), meta, out_page_stride=32)
+    src = tk.Cache(bf(pc.k), bf(pc.v), meta, up(pc.page_off), up(pc.page_ids), up(pc.length))
     seg = up(w.seg_head_begin())
     t_dev = up(np.full(w.n_seg, w.t, np.int32))
     budget = up(np.full(w.n_seg, M, np.int64))
@@ -152,6 +153,14 @@ def main():
         torch.cuda.synchronize()
         cold.append(a.elapsed_time(b) * 1e-3)
     t_cold = float(np.median(cold))
+
+    if args.calib:
+        src_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        src_buf.fill_(3)
+        torch.cuda.synchronize()
+        flush.copy_(src_buf)        # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src_buf
 
     kept_total = int(kept_np.sum())
     small = nq * D * 2 + nq * D * 4 + nq * 4

@@ -28,8 +28,11 @@
  *    entry page_off[h] + c; it lives in physical page page_ids[page_off[h]+c].
  *    Entry i of head h is slot i % 16 of its logical page i / 16; entries
  *    i < len[h] are valid, and their positions ascend with i.
- *  - Pools: k, v [n_pages][16][head_dim] (bf16 or fp32), lnb [n_pages][16]
- *    fp32 (ln beta), pos [n_pages][16] int32.
+ *  - Pools: k, v [n_pages][16][head_dim] (bf16 or fp32); meta
+ *    [n_pages][2][16] 32-bit words: for page p, meta[p][0][j] holds ln(beta)
+ *    (fp32 bits) of slot j and meta[p][1][j] its token position (int32).  A
+ *    page's metadata is one 128-byte block, so reading it costs one cache
+ *    line whatever the physical page order.
  *  - "CSR plane": a per-slot array indexed by CSR slot
  *    s = (page_off[h] + i / 16) * 16 + i % 16, of length
  *    page_off[n_heads] * 16 (<= n_pages * 16).  Scores, keep flags and
@@ -70,8 +73,7 @@ typedef struct trimkv_cache {
   int64_t n_pages;   /* pool capacity in pages */
   void* k;           /* [n_pages][16][head_dim] */
   void* v;           /* [n_pages][16][head_dim] */
-  float* lnb;        /* [n_pages][16]  ln(beta) */
-  int32_t* pos;      /* [n_pages][16]  token position */
+  uint32_t* meta;    /* [n_pages][2][16]  ln(beta) (fp32 bits), then position (int32) */
   int32_t* page_off; /* [n_heads + 1]  CSR offsets, page_off[0] = 0, nondecreasing */
   int32_t* page_ids; /* [n_pages]      physical page of each CSR entry */
   int32_t* len;      /* [n_heads]      valid entries per head */
@@ -88,13 +90,17 @@ enum {
 };
 
 /*
- * trimkv_log_beta -- lnb[i] = ln(beta[i]) rounded to nearest fp32.
+ * trimkv_log_beta -- ln(beta[i]) rounded to nearest fp32, for i < n.
  * TRIM-KV page, section 2: beta in [0,1] is assigned once, when the token is
  * created, so its logarithm is computed once per entry.  beta = 1 gives +0.0,
- * beta = 0 gives -inf.  beta: [n] fp32, lnb: [n] fp32.  n >= 0.
- * Errors: EINVAL (null pointer with n > 0, n < 0).
+ * beta = 0 gives -inf.
+ *   beta: [n] fp32, contiguous
+ *   lnb:  output; element i goes to lnb[(i / 16) * out_page_stride + i % 16]:
+ *         out_page_stride 16 writes a contiguous array, 32 writes the ln(beta)
+ *         half of a cache's meta plane (lnb = (float*)meta).
+ * Errors: EINVAL (null pointer with n > 0, n < 0, out_page_stride < 16).
  */
-int trimkv_log_beta(const float* beta, float* lnb, int64_t n, void* stream);
+int trimkv_log_beta(const float* beta, float* lnb, int64_t n, int32_t out_page_stride, void* stream);
 
 /*
  * trimkv_score -- retention score of every valid slot.
@@ -140,7 +146,7 @@ int trimkv_select_global(const trimkv_cache_t* cache, const float* score, int32_
  * Every kept entry of src (keep == 1) is copied, in slot order, to dst:
  * head h gets ceil((kept_h + reserve) / 16) pages numbered by a prefix sum
  * over heads in flat order, dst->page_ids[c] = c, dst->len[h] = kept_h.
- * K, V, lnb and pos rows are copied bit for bit; padding slots are left
+ * K, V rows and their ln(beta) and position are copied bit for bit; padding slots are left
  * unspecified.  `reserve` spare slots per head let trimkv_append add entries.
  *   dst:           same n_heads/head_dim/dtype as src; its pools, page_off,
  *                  page_ids and len are written; must not overlap src.
@@ -215,8 +221,8 @@ int trimkv_allocate(const double* keptsum, const int32_t* len, int32_t n_heads,
 /*
  * trimkv_append -- add one new entry per head at decode step *t.
  * TRIM-KV page, section 2 (beta assigned when the token is created).
- * Entry len[h] of head h receives k_new[h], v_new[h], lnb = ln(beta_new[h])
- * (as trimkv_log_beta) and pos = *t - 1; then len[h] += 1.  The head must have
+ * Entry len[h] of head h receives k_new[h], v_new[h], ln(beta_new[h]) (as
+ * trimkv_log_beta) and position *t - 1; then len[h] += 1.  The head must have
  * a free slot in its pages (trimkv_compact with reserve >= 1); a head without
  * one is left unchanged (trimkv_validate_cache reports it).
  *   k_new, v_new: device [n_heads][head_dim] (cache dtype); beta_new: fp32 [n_heads]
@@ -232,7 +238,8 @@ size_t trimkv_workspace_size(int op, const trimkv_cache_t* cache, int32_t n_seg,
 /*
  * trimkv_validate_cache -- debug check of the preconditions (synchronises):
  * page_off nondecreasing, within n_pages; page_ids in range; len within the
- * head's pages; pos ascending within each head and < *t; lnb <= 0 and not NaN.
+ * head's pages; positions ascending within each head and < *t; ln(beta) <= 0
+ * and not NaN.
  * Returns TRIMKV_OK or TRIMKV_EINVARIANT (or an argument / HIP error).
  *   t: device int32 [1];  ws: trimkv_workspace_size(TRIMKV_OP_VALIDATE, ...) bytes
  */

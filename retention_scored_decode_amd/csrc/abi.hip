@@ -23,7 +23,7 @@ bool cache_shape_ok(const trimkv_cache_t* c, int* rc) {
 }
 
 bool table_ok(const trimkv_cache_t* c) { return c->page_off && c->len && (c->n_pages == 0 || c->page_ids); }
-bool pools_ok(const trimkv_cache_t* c) { return c->n_pages == 0 || (c->k && c->v && c->lnb && c->pos); }
+bool pools_ok(const trimkv_cache_t* c) { return c->n_pages == 0 || (c->k && c->v && c->meta); }
 
 int ws_check(void* ws, size_t have, size_t need) {
   if (need == 0) return TRIMKV_OK;
@@ -57,7 +57,7 @@ __global__ void k_check_ids(const int32_t* page_off, const int32_t* page_ids, in
 }
 
 __global__ void k_check_slots(const int32_t* page_off, const int32_t* page_ids, const int32_t* len,
-                              const int32_t* pos, const float* lnb, int n_heads, const int32_t* t, int32_t* flag) {
+                              const uint32_t* meta, int n_heads, const int32_t* t, int32_t* flag) {
   const int64_t total = page_off[n_heads];
   const int64_t c = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int j = threadIdx.x & 15;
@@ -65,15 +65,16 @@ __global__ void k_check_slots(const int32_t* page_off, const int32_t* page_ids, 
   const int h = upper_index(page_off, n_heads + 1, c);
   const int64_t i = (c - page_off[h]) * PAGE + j;
   if (i >= len[h]) return;
-  const int64_t slot = (int64_t)page_ids[c] * PAGE + j;
+  const uint32_t* mp = meta + (int64_t)page_ids[c] * (2 * PAGE);
+  const int32_t pos = (int32_t)mp[PAGE + j];
   int bad = 0;
-  if (pos[slot] >= t[0]) bad |= BAD_POS_T;
-  const float l = lnb[slot];
+  if (pos >= t[0]) bad |= BAD_POS_T;
+  const float l = __uint_as_float(mp[j]);
   if (!(l <= 0.0f)) bad |= BAD_LNB;
   if (i + 1 < len[h]) {
     const int64_t i1 = i + 1;
-    const int64_t s1 = (int64_t)page_ids[page_off[h] + i1 / PAGE] * PAGE + i1 % PAGE;
-    if (pos[s1] <= pos[slot]) bad |= BAD_POS_ORDER;
+    const uint32_t* mp1 = meta + (int64_t)page_ids[page_off[h] + i1 / PAGE] * (2 * PAGE);
+    if ((int32_t)mp1[PAGE + i1 % PAGE] <= pos) bad |= BAD_POS_ORDER;
   }
   if (bad) atomicOr(flag, bad);
 }
@@ -108,16 +109,16 @@ size_t trimkv_workspace_size(int op, const trimkv_cache_t* c, int32_t n_seg, int
   }
 }
 
-int trimkv_log_beta(const float* beta, float* lnb, int64_t n, void* stream) {
-  if (n < 0 || (n > 0 && (!beta || !lnb))) return TRIMKV_EINVAL;
-  return launch_log_beta(beta, lnb, n, S(stream));
+int trimkv_log_beta(const float* beta, float* lnb, int64_t n, int32_t out_page_stride, void* stream) {
+  if (n < 0 || out_page_stride < PAGE || (n > 0 && (!beta || !lnb))) return TRIMKV_EINVAL;
+  return launch_log_beta(beta, lnb, n, out_page_stride, S(stream));
 }
 
 int trimkv_score(const trimkv_cache_t* c, int32_t n_seg, const int32_t* seg, const int32_t* t, float* score,
                  void* stream) {
   int rc;
   if (!cache_shape_ok(c, &rc)) return rc;
-  if (n_seg < 1 || !seg || !t || !score || !table_ok(c) || !c->lnb || !c->pos) return TRIMKV_EINVAL;
+  if (n_seg < 1 || !seg || !t || !score || !table_ok(c) || !c->meta) return TRIMKV_EINVAL;
   if (c->n_heads == 0 || c->n_pages == 0) return TRIMKV_OK;
   return launch_score(c, n_seg, seg, t, score, S(stream));
 }
@@ -143,7 +144,7 @@ int trimkv_compact(const trimkv_cache_t* src, const uint8_t* keep, int32_t reser
     return TRIMKV_EINVAL;
   if (dst->n_heads != src->n_heads || dst->head_dim != src->head_dim || dst->dtype != src->dtype)
     return TRIMKV_EINVAL;
-  if (dst->k == src->k || dst->v == src->v || dst->lnb == src->lnb || dst->pos == src->pos ||
+  if (dst->k == src->k || dst->v == src->v || dst->meta == src->meta ||
       dst->page_off == src->page_off || dst->len == src->len)
     return TRIMKV_EINVAL;
   const int64_t H = src->n_heads;
@@ -214,7 +215,7 @@ int trimkv_validate_cache(const trimkv_cache_t* c, const int32_t* t, void* ws, s
   if (c->n_pages > 0) {
     const int64_t blocks = (c->n_pages + 15) / 16;
     hipLaunchKernelGGL(k_check_slots, dim3((unsigned)blocks), dim3(256), 0, st, c->page_off, c->page_ids, c->len,
-                       c->pos, c->lnb, c->n_heads, t, flag);
+                       c->meta, c->n_heads, t, flag);
   }
   if (hipMemcpyAsync(&host, flag, 4, hipMemcpyDeviceToHost, st) != hipSuccess) return TRIMKV_EHIP;
   if (hipStreamSynchronize(st) != hipSuccess) return TRIMKV_EHIP;

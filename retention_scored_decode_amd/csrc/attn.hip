@@ -242,17 +242,23 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
   const uint8_t* kbase = (const uint8_t*)a.k;
   const uint8_t* vbase = (const uint8_t*)a.v;
 
+  // Every load is issued unconditionally so the compiler can count outstanding
+  // loads exactly and wait only for the page being processed: a V row that is
+  // not needed (dropped or past the end) is read from the start of the page's
+  // K tile instead, a line this wave has just requested.
   auto load = [&](int i, uint32_t kwi, uint4 (&kd)[KU], VT (&vd)[4]) {
     const int64_t phys = __builtin_amdgcn_readlane(pid_l, i);
-    const uint8_t* krow = kbase + ((phys * PAGE + col) * D) * 2 + 16 * r;
+    const uint8_t* kpage = kbase + phys * PAGE * D * 2;
+    const uint8_t* krow = kpage + col * D * 2 + 16 * r;
 #pragma unroll
     for (int u = 0; u < KU; ++u) kd[u] = *reinterpret_cast<const uint4*>(krow + 64 * u);
     if (!LOGITS) {
       const int i0 = (p0 + i) * PAGE + 4 * r;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (i0 + j < n && ((kwi >> (8 * j)) & 0xFFu))
-          vd[j] = *reinterpret_cast<const VT*>(vbase + ((phys * PAGE + 4 * r + j) * D + col * DS) * 2);
+        const bool need = i0 + j < n && ((kwi >> (8 * j)) & 0xFFu);
+        const uint8_t* src = need ? vbase + ((phys * PAGE + 4 * r + j) * D + col * DS) * 2 : kpage;
+        vd[j] = *reinterpret_cast<const VT*>(src);
       }
     }
   };
@@ -341,22 +347,30 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
     }
   };
 
-  uint4 kA[KU], kB[KU];
-  VT vA[4], vB[4];
-  uint32_t kwA = kword(0), kwB = 0u;
-  load(0, kwA, kA, vA);
-  for (int i = 0; i < cnt; i += 2) {
-    if (i + 1 < cnt) {
-      kwB = kword(i + 1);
-      load(i + 1, kwB, kB, vB);
+  // ring of LA + 1 page buffers: page ii + LA is loaded while page ii is
+  // processed (indices past the item's last page reload that page)
+  constexpr int LA = GM <= 4 ? 3 : (GM <= 8 ? 2 : 1);
+  constexpr int NB = LA + 1;
+  uint4 kb[NB][KU];
+  VT vb[NB][4];
+  uint32_t kwb[NB];
+#pragma unroll
+  for (int u = 0; u < LA; ++u) {
+    const int pi = min(u, cnt - 1);
+    kwb[u] = kword(pi);
+    load(pi, kwb[u], kb[u], vb[u]);
+  }
+  for (int i = 0; i < cnt; i += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int ii = i + u;
+      if (ii >= cnt) break;
+      const int nb = (u + LA) % NB;
+      const int pi = min(ii + LA, cnt - 1);
+      kwb[nb] = kword(pi);
+      load(pi, kwb[nb], kb[nb], vb[nb]);
+      compute(ii, kwb[u], kb[u], vb[u]);
     }
-    compute(i, kwA, kA, vA);
-    if (i + 1 >= cnt) break;
-    if (i + 2 < cnt) {
-      kwA = kword(i + 2);
-      load(i + 2, kwA, kA, vA);
-    }
-    compute(i + 1, kwB, kB, vB);
   }
 
   // ---- combine the four row streams of the wave and write the partial ----

@@ -98,13 +98,12 @@ template <int ROWB>
 __global__ void __launch_bounds__(NT) k_cmp_scatter(int n_heads, const int32_t* __restrict__ page_ids,
                                                     const uint8_t* __restrict__ src_k,
                                                     const uint8_t* __restrict__ src_v,
-                                                    const float* __restrict__ src_lnb,
-                                                    const int32_t* __restrict__ src_pos,
+                                                    const uint32_t* __restrict__ src_meta,
                                                     const uint8_t* __restrict__ keep, CmpWs w,
                                                     const int32_t* __restrict__ dst_off,
                                                     int32_t* __restrict__ dst_ids, uint8_t* __restrict__ dst_k,
-                                                    uint8_t* __restrict__ dst_v, float* __restrict__ dst_lnb,
-                                                    int32_t* __restrict__ dst_pos, int64_t dst_pages) {
+                                                    uint8_t* __restrict__ dst_v, uint32_t* __restrict__ dst_meta,
+                                                    int64_t dst_pages) {
   constexpr int LPR = ROWB / 16;  // lanes per row (16 B each)
   constexpr int RPI = NT / LPR;   // rows per iteration
   constexpr int UNR = 4;          // row iterations whose loads are issued together
@@ -164,13 +163,15 @@ __global__ void __launch_bounds__(NT) k_cmp_scatter(int n_heads, const int32_t* 
       }
     }
   }
-  // ln beta and position of the kept rows
+  // ln beta and position of the kept rows (one 128-byte metadata block per page)
   for (int row = threadIdx.x; row < nk; row += NT) {
     const int64_t d = dbase + row;
     if (d < dcap) {
       const int64_t s = src_slot[row];
-      dst_lnb[d] = src_lnb[s];
-      dst_pos[d] = src_pos[s];
+      const uint32_t* sm = src_meta + (s / PAGE) * (2 * PAGE) + s % PAGE;
+      uint32_t* dm = dst_meta + (d / PAGE) * (2 * PAGE) + d % PAGE;
+      dm[0] = sm[0];
+      dm[PAGE] = sm[PAGE];
     }
   }
 }
@@ -207,8 +208,8 @@ int launch_compact(const trimkv_cache_t* src, const uint8_t* keep, int reserve, 
   const int rowb = src->head_dim * elt;
 #define TRIMKV_SCATTER(RB)                                                                                   \
   hipLaunchKernelGGL(k_cmp_scatter<RB>, dim3((unsigned)T), dim3(NT), 0, st, H, src->page_ids,                \
-                     (const uint8_t*)src->k, (const uint8_t*)src->v, src->lnb, src->pos, keep, w, dst->page_off, \
-                     dst->page_ids, (uint8_t*)dst->k, (uint8_t*)dst->v, dst->lnb, dst->pos, dst->n_pages)
+                     (const uint8_t*)src->k, (const uint8_t*)src->v, src->meta, keep, w, dst->page_off,           \
+                     dst->page_ids, (uint8_t*)dst->k, (uint8_t*)dst->v, dst->meta, dst->n_pages)
   switch (rowb) {
     case 128: TRIMKV_SCATTER(128); break;
     case 256: TRIMKV_SCATTER(256); break;

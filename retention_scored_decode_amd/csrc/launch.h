@@ -31,7 +31,7 @@ WsLayout compact_ws_layout(const trimkv_cache_t* c);
 WsLayout attn_ws_layout(const trimkv_cache_t* c, int group);
 WsLayout mass_ws_layout(const trimkv_cache_t* c, int group);
 
-int launch_log_beta(const float* beta, float* lnb, int64_t n, hipStream_t st);
+int launch_log_beta(const float* beta, float* lnb, int64_t n, int out_page_stride, hipStream_t st);
 int launch_score(const trimkv_cache_t* c, int n_seg, const int32_t* seg, const int32_t* t, float* score,
                  hipStream_t st);
 int launch_append(trimkv_cache_t* c, const void* kn, const void* vn, const float* bn, const int32_t* t,

@@ -40,18 +40,17 @@ __device__ __forceinline__ float ln_f32_cr(float x) {
 }
 
 __global__ void __launch_bounds__(256) k_log_beta(const float* __restrict__ beta, float* __restrict__ lnb,
-                                                  int64_t n) {
+                                                  int64_t n, int out_page_stride) {
   int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-    lnb[i] = ln_f32_cr(beta[i]);
+    lnb[(i / PAGE) * out_page_stride + i % PAGE] = ln_f32_cr(beta[i]);
 }
 
 // 64 CSR pages per block, 4 slots per thread (16-byte loads and stores).
 __global__ void __launch_bounds__(256) k_score(const int32_t* __restrict__ page_off,
                                                const int32_t* __restrict__ page_ids,
                                                const int32_t* __restrict__ len,
-                                               const float* __restrict__ lnb,
-                                               const int32_t* __restrict__ pos, int n_heads,
+                                               const uint32_t* __restrict__ meta, int n_heads,
                                                const int32_t* __restrict__ seg_head_begin, int n_seg,
                                                const int32_t* __restrict__ t, float* __restrict__ score) {
   __shared__ PageHeads sh;
@@ -68,9 +67,10 @@ __global__ void __launch_bounds__(256) k_score(const int32_t* __restrict__ page_
   const int64_t n = len[h];
   float4 out = make_float4(qnan(), qnan(), qnan(), qnan());
   if (i0 < n) {
-    const int64_t slot = (int64_t)page_ids[c] * PAGE + j0;
-    const float4 l = *reinterpret_cast<const float4*>(lnb + slot);
-    const int4 p = *reinterpret_cast<const int4*>(pos + slot);
+    // ln(beta) and positions of one page share a 128-byte block
+    const uint32_t* mp = meta + (int64_t)page_ids[c] * (2 * PAGE) + j0;
+    const float4 l = *reinterpret_cast<const float4*>(mp);
+    const int4 p = *reinterpret_cast<const int4*>(mp + PAGE);
     const int tt = t[s];
     out.x = __fmul_rn((float)(tt - p.x), l.x);
     if (i0 + 1 < n) out.y = __fmul_rn((float)(tt - p.y), l.y);
@@ -85,8 +85,8 @@ template <typename T, int D>
 __global__ void __launch_bounds__(64) k_append(const int32_t* __restrict__ page_off,
                                                const int32_t* __restrict__ page_ids,
                                                int32_t* __restrict__ len, T* __restrict__ k,
-                                               T* __restrict__ v, float* __restrict__ lnb,
-                                               int32_t* __restrict__ pos, const T* __restrict__ k_new,
+                                               T* __restrict__ v, uint32_t* __restrict__ meta,
+                                               const T* __restrict__ k_new,
                                                const T* __restrict__ v_new,
                                                const float* __restrict__ beta_new,
                                                const int32_t* __restrict__ t) {
@@ -94,23 +94,24 @@ __global__ void __launch_bounds__(64) k_append(const int32_t* __restrict__ page_
   const int n = len[h];
   const int64_t cap = (int64_t)(page_off[h + 1] - page_off[h]) * PAGE;
   if (n >= cap) return;
-  const int64_t slot = (int64_t)page_ids[page_off[h] + n / PAGE] * PAGE + n % PAGE;
+  const int64_t page = page_ids[page_off[h] + n / PAGE];
+  const int64_t slot = page * PAGE + n % PAGE;
   for (int d = threadIdx.x; d < D; d += 64) {
     k[slot * D + d] = k_new[(int64_t)h * D + d];
     v[slot * D + d] = v_new[(int64_t)h * D + d];
   }
   if (threadIdx.x == 0) {
-    lnb[slot] = ln_f32_cr(beta_new[h]);
-    pos[slot] = t[0] - 1;
+    meta[page * (2 * PAGE) + n % PAGE] = __float_as_uint(ln_f32_cr(beta_new[h]));
+    meta[page * (2 * PAGE) + PAGE + n % PAGE] = (uint32_t)(t[0] - 1);
     len[h] = n + 1;
   }
 }
 
-int launch_log_beta(const float* beta, float* lnb, int64_t n, hipStream_t st) {
+int launch_log_beta(const float* beta, float* lnb, int64_t n, int out_page_stride, hipStream_t st) {
   if (n == 0) return TRIMKV_OK;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(k_log_beta, dim3((unsigned)blocks), dim3(256), 0, st, beta, lnb, n);
+  hipLaunchKernelGGL(k_log_beta, dim3((unsigned)blocks), dim3(256), 0, st, beta, lnb, n, out_page_stride);
   return check_launch();
 }
 
@@ -119,7 +120,7 @@ int launch_score(const trimkv_cache_t* c, int n_seg, const int32_t* seg, const i
   int64_t blocks = (c->n_pages + 63) / 64;
   if (blocks == 0) return TRIMKV_OK;
   hipLaunchKernelGGL(k_score, dim3((unsigned)blocks), dim3(256), 0, st, c->page_off, c->page_ids, c->len,
-                     c->lnb, c->pos, c->n_heads, seg, n_seg, t, score);
+                     c->meta, c->n_heads, seg, n_seg, t, score);
   return check_launch();
 }
 
@@ -127,7 +128,7 @@ template <typename T, int D>
 static void append_t(trimkv_cache_t* c, const void* kn, const void* vn, const float* bn, const int32_t* t,
                      hipStream_t st) {
   hipLaunchKernelGGL((k_append<T, D>), dim3(c->n_heads), dim3(64), 0, st, c->page_off, c->page_ids, c->len,
-                     (T*)c->k, (T*)c->v, c->lnb, c->pos, (const T*)kn, (const T*)vn, bn, t);
+                     (T*)c->k, (T*)c->v, c->meta, (const T*)kn, (const T*)vn, bn, t);
 }
 
 int launch_append(trimkv_cache_t* c, const void* kn, const void* vn, const float* bn, const int32_t* t,

@@ -34,9 +34,8 @@ class TrimkvError(RuntimeError):
 class CacheStruct(ctypes.Structure):
     _fields_ = [("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("n_pages", ctypes.c_int64),
-                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("lnb", ctypes.c_void_p),
-                ("pos", ctypes.c_void_p), ("page_off", ctypes.c_void_p), ("page_ids", ctypes.c_void_p),
-                ("len", ctypes.c_void_p)]
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("meta", ctypes.c_void_p),
+                ("page_off", ctypes.c_void_p), ("page_ids", ctypes.c_void_p), ("len", ctypes.c_void_p)]
 
 
 _lib = None
@@ -52,7 +51,7 @@ def lib():
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         cp = ctypes.POINTER(CacheStruct)
         sig = {
-            "trimkv_log_beta": [vp, vp, i64, vp],
+            "trimkv_log_beta": [vp, vp, i64, i32, vp],
             "trimkv_score": [cp, i32, vp, vp, vp, vp],
             "trimkv_select_global": [cp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_compact": [cp, vp, i32, i64, cp, vp, vp, sz, vp],
@@ -100,13 +99,13 @@ def _check(rc: int, what: str):
 class Cache:
     """A paged KV pool plus its page table, as device tensors.
 
-    k, v [n_pages, 16, D] (torch.bfloat16 or float32), lnb [n_pages, 16] f32,
-    pos [n_pages, 16] i32, page_off [n_heads + 1] i32, page_ids [n_pages] i32,
-    length [n_heads] i32.
+    k, v [n_pages, 16, D] (torch.bfloat16 or float32); meta [n_pages, 2, 16]
+    int32 (row 0: ln beta as fp32 bits, row 1: positions); page_off
+    [n_heads + 1] i32, page_ids [n_pages] i32, length [n_heads] i32.
     """
 
-    def __init__(self, k, v, lnb, pos, page_off, page_ids, length):
-        self.k, self.v, self.lnb, self.pos = k, v, lnb, pos
+    def __init__(self, k, v, meta, page_off, page_ids, length):
+        self.k, self.v, self.meta = k, v, meta
         self.page_off, self.page_ids, self.length = page_off, page_ids, length
         self._s = None
 
@@ -114,11 +113,20 @@ class Cache:
     def empty(cls, n_heads: int, n_pages: int, head_dim: int, dtype: torch.dtype, device="cuda"):
         return cls(torch.empty((n_pages, PAGE, head_dim), dtype=dtype, device=device),
                    torch.empty((n_pages, PAGE, head_dim), dtype=dtype, device=device),
-                   torch.empty((n_pages, PAGE), dtype=torch.float32, device=device),
-                   torch.empty((n_pages, PAGE), dtype=torch.int32, device=device),
+                   torch.empty((n_pages, 2, PAGE), dtype=torch.int32, device=device),
                    torch.zeros(n_heads + 1, dtype=torch.int32, device=device),
                    torch.empty(n_pages, dtype=torch.int32, device=device),
                    torch.zeros(n_heads, dtype=torch.int32, device=device))
+
+    @property
+    def lnb(self) -> torch.Tensor:
+        """[n_pages, 16] float32 view of the ln(beta) half of meta."""
+        return self.meta[:, 0, :].view(torch.float32)
+
+    @property
+    def pos(self) -> torch.Tensor:
+        """[n_pages, 16] int32 view of the positions half of meta."""
+        return self.meta[:, 1, :]
 
     @property
     def n_heads(self) -> int:
@@ -138,7 +146,7 @@ class Cache:
 
     def struct(self) -> CacheStruct:
         s = CacheStruct(self.n_heads, self.head_dim, PAGE, self.dtype_code, self.n_pages,
-                        self.k.data_ptr(), self.v.data_ptr(), self.lnb.data_ptr(), self.pos.data_ptr(),
+                        self.k.data_ptr(), self.v.data_ptr(), self.meta.data_ptr(),
                         self.page_off.data_ptr(), self.page_ids.data_ptr(), self.length.data_ptr())
         self._s = s
         return s
@@ -153,8 +161,11 @@ def workspace(op: int, cache: Cache, n_seg: int = 0, group: int = 0) -> torch.Te
     return torch.empty(max(n, 1), dtype=torch.uint8, device=cache.k.device)
 
 
-def log_beta(beta: torch.Tensor, lnb: torch.Tensor, stream=None):
-    _check(lib().trimkv_log_beta(_p(beta), _p(lnb), beta.numel(), _stream(stream)), "trimkv_log_beta")
+def log_beta(beta: torch.Tensor, lnb: torch.Tensor, out_page_stride: int = PAGE, stream=None):
+    """lnb[(i // 16) * out_page_stride + i % 16] = ln(beta[i]); pass a cache's
+    meta (and out_page_stride=32) to fill its ln(beta) half."""
+    _check(lib().trimkv_log_beta(_p(beta), _p(lnb), beta.numel(), int(out_page_stride), _stream(stream)),
+           "trimkv_log_beta")
 
 
 def score(cache: Cache, seg_head_begin: torch.Tensor, t: torch.Tensor, out: torch.Tensor, stream=None):

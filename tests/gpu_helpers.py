@@ -34,12 +34,13 @@ def kv_f64(a: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def upload(pc: synth.PagedCache) -> tk.Cache:
-    """Device copy of a host cache; ln(beta) computed on the GPU (a0)."""
-    beta = cuda(pc.beta, np.float32)
-    lnb = torch.empty_like(beta)
-    tk.log_beta(beta, lnb)
-    return tk.Cache(kv_dev(pc.k, pc.dtype), kv_dev(pc.v, pc.dtype), lnb, cuda(pc.pos, np.int32),
-                    cuda(pc.page_off, np.int32), cuda(pc.page_ids, np.int32), cuda(pc.length, np.int32))
+    """Device copy of a host cache; ln(beta) computed on the GPU (a0) straight
+    into the cache's metadata blocks."""
+    meta = torch.zeros((pc.n_pages, 2, 16), dtype=torch.int32, device="cuda")
+    meta[:, 1, :] = cuda(pc.pos, np.int32)
+    tk.log_beta(cuda(pc.beta, np.float32), meta, out_page_stride=32)
+    return tk.Cache(kv_dev(pc.k, pc.dtype), kv_dev(pc.v, pc.dtype), meta, cuda(pc.page_off, np.int32),
+                    cuda(pc.page_ids, np.int32), cuda(pc.length, np.int32))
 
 
 class OracleView:
@@ -86,7 +87,10 @@ def download_cache(c: tk.Cache):
     f = lambda t: t.cpu().numpy()
     k = c.k.view(torch.int16).cpu().numpy().view(np.uint16) if c.k.dtype == torch.bfloat16 else f(c.k)
     v = c.v.view(torch.int16).cpu().numpy().view(np.uint16) if c.v.dtype == torch.bfloat16 else f(c.v)
-    return f(c.page_off), f(c.page_ids), f(c.length), k, v, f(c.lnb), f(c.pos)
+    meta = f(c.meta)
+    lnb = np.ascontiguousarray(meta[:, 0, :]).view(np.float32)
+    pos = np.ascontiguousarray(meta[:, 1, :])
+    return f(c.page_off), f(c.page_ids), f(c.length), k, v, lnb, pos
 
 
 def f32_bits(a):

@@ -26,10 +26,10 @@ def test_exports_every_declared_symbol():
 
 
 def fake_cache(n_heads=4, head_dim=128, dtype=tk.BF16, n_pages=64, page_size=16, nulls=()):
-    f = dict(k=0x1000, v=0x2000, lnb=0x3000, pos=0x4000, page_off=0x5000, page_ids=0x6000, len=0x7000)
+    f = dict(k=0x1000, v=0x2000, meta=0x3000, page_off=0x5000, page_ids=0x6000, len=0x7000)
     for n in nulls:
         f[n] = None
-    return tk.CacheStruct(n_heads, head_dim, page_size, dtype, n_pages, f["k"], f["v"], f["lnb"], f["pos"],
+    return tk.CacheStruct(n_heads, head_dim, page_size, dtype, n_pages, f["k"], f["v"], f["meta"],
                           f["page_off"], f["page_ids"], f["len"])
 
 
@@ -60,8 +60,9 @@ def test_null_and_inconsistent_arguments():
     assert L.trimkv_score(None, 1, X, X, X, None) == tk.EINVAL
     assert L.trimkv_score(ctypes.byref(c), 0, X, X, X, None) == tk.EINVAL
     assert L.trimkv_score(ctypes.byref(c), 1, None, X, X, None) == tk.EINVAL
-    assert L.trimkv_log_beta(None, None, 5, None) == tk.EINVAL
-    assert L.trimkv_log_beta(X, X, -1, None) == tk.EINVAL
+    assert L.trimkv_log_beta(None, None, 5, 16, None) == tk.EINVAL
+    assert L.trimkv_log_beta(X, X, -1, 16, None) == tk.EINVAL
+    assert L.trimkv_log_beta(X, X, 5, 8, None) == tk.EINVAL
     # keep and lse_ref together
     assert L.trimkv_decode_attn(ctypes.byref(c), X, X, X, 4, ctypes.c_float(1.0), X, X, None, X, 1 << 30,
                                 None) == tk.EINVAL
@@ -95,10 +96,10 @@ def test_compact_capacity_and_compatibility():
     src = fake_cache(n_heads=4, n_pages=64)
     ws = L.trimkv_workspace_size(tk.OP_COMPACT, ctypes.byref(src), 0, 0)
     # need ceil((100 + 4*1)/16) + 4 = 11 pages
-    small = tk.CacheStruct(4, 128, 16, tk.BF16, 10, 0x11000, 0x12000, 0x13000, 0x14000, 0x15000, 0x16000, 0x17000)
-    ok = tk.CacheStruct(4, 128, 16, tk.BF16, 11, 0x11000, 0x12000, 0x13000, 0x14000, 0x15000, 0x16000, 0x17000)
+    small = tk.CacheStruct(4, 128, 16, tk.BF16, 10, 0x11000, 0x12000, 0x13000, 0x15000, 0x16000, 0x17000)
+    ok = tk.CacheStruct(4, 128, 16, tk.BF16, 11, 0x11000, 0x12000, 0x13000, 0x15000, 0x16000, 0x17000)
     assert L.trimkv_compact(ctypes.byref(src), X, 1, 100, ctypes.byref(small), X, X, ws, None) == tk.ECAPACITY
-    other = tk.CacheStruct(4, 64, 16, tk.BF16, 11, 0x11000, 0x12000, 0x13000, 0x14000, 0x15000, 0x16000, 0x17000)
+    other = tk.CacheStruct(4, 64, 16, tk.BF16, 11, 0x11000, 0x12000, 0x13000, 0x15000, 0x16000, 0x17000)
     assert L.trimkv_compact(ctypes.byref(src), X, 1, 100, ctypes.byref(other), X, X, ws, None) == tk.EINVAL
     assert L.trimkv_compact(ctypes.byref(src), X, -1, 100, ctypes.byref(ok), X, X, ws, None) == tk.EINVAL
     assert L.trimkv_compact(ctypes.byref(src), X, 1, 100, ctypes.byref(ok), X, X, ws - 1, None) == tk.EWORKSPACE

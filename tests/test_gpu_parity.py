@@ -54,6 +54,13 @@ def test_log_beta_specials_and_hard_cases():
     tk.log_beta(cuda(x), out)
     got = out.cpu().numpy()
     assert np.array_equal(f32_bits(got), f32_bits(ref.ln_beta(x)))
+    # strided output (the ln beta half of metadata blocks); the other half untouched
+    n = (x.size // 16) * 16
+    meta = torch.full((n // 16, 2, 16), 7, dtype=torch.int32, device="cuda")
+    tk.log_beta(cuda(x[:n]), meta, out_page_stride=32)
+    mh = meta.cpu().numpy()
+    assert np.array_equal(mh[:, 0, :].reshape(-1).view(np.uint32), f32_bits(ref.ln_beta(x[:n])))
+    assert np.all(mh[:, 1, :] == 7)
 
 
 EXH_CHUNK = 1 << 26
