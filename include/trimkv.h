@@ -37,7 +37,8 @@
  *    s = (page_off[h] + i / 16) * 16 + i % 16, of length
  *    page_off[n_heads] * 16 (<= n_pages * 16).  Scores, keep flags and
  *    attention masses are CSR planes, so selection streams them
- *    contiguously whatever the physical page order.
+ *    contiguously whatever the physical page order.  Keep planes (uint8)
+ *    must start on a 16-byte boundary (EINVAL otherwise).
  */
 #ifndef TRIMKV_H
 #define TRIMKV_H
@@ -155,6 +156,10 @@ int trimkv_select_global(const trimkv_cache_t* cache, const float* score, int32_
  *                  n_heads*reserve)/16) + n_heads, else ECAPACITY.
  *   pages_used:    device int64 [1], out: dst->page_off[n_heads]
  *   ws:            trimkv_workspace_size(TRIMKV_OP_COMPACT, src, 0, 0) bytes
+ *                  (it holds an 8-byte (source, destination) slot pair per
+ *                  kept entry, so it grows with src->n_pages)
+ * Slots are carried as 32-bit indices: n_pages * 16 of src and dst must fit
+ * in 32 bits (EUNSUPPORTED otherwise).
  * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, ECAPACITY.
  */
 int trimkv_compact(const trimkv_cache_t* src, const uint8_t* keep, int32_t reserve,

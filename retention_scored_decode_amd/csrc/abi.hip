@@ -128,7 +128,8 @@ int trimkv_select_global(const trimkv_cache_t* c, const float* score, int32_t n_
                          size_t ws_bytes, void* stream) {
   int rc;
   if (!cache_shape_ok(c, &rc)) return rc;
-  if (n_seg < 1 || n_seg > c->n_heads || !score || !seg || !budget || !keep || !kept || !table_ok(c))
+  if (n_seg < 1 || n_seg > c->n_heads || !score || !seg || !budget || !keep || !kept || !table_ok(c) ||
+      ((uintptr_t)keep & 15))
     return TRIMKV_EINVAL;
   if ((rc = ws_check(ws, ws_bytes, select_ws_layout(c, n_seg).total))) return rc;
   return launch_select(c, score, n_seg, seg, budget, keep, kept, keptsum, ws, S(stream));
@@ -140,8 +141,11 @@ int trimkv_compact(const trimkv_cache_t* src, const uint8_t* keep, int32_t reser
   if (!cache_shape_ok(src, &rc)) return rc;
   if (!cache_shape_ok(dst, &rc)) return rc;
   if (!keep || !pages_used || reserve < 0 || max_kept_total < 0 || !table_ok(src) || !pools_ok(src) ||
-      !table_ok(dst) || !pools_ok(dst) || !dst->page_ids)
+      !table_ok(dst) || !pools_ok(dst) || !dst->page_ids || ((uintptr_t)keep & 15))
     return TRIMKV_EINVAL;
+  // slots are carried as 32-bit indices
+  if (src->n_pages * PAGE > (int64_t)UINT32_MAX || dst->n_pages * PAGE > (int64_t)UINT32_MAX)
+    return TRIMKV_EUNSUPPORTED;
   if (dst->n_heads != src->n_heads || dst->head_dim != src->head_dim || dst->dtype != src->dtype)
     return TRIMKV_EINVAL;
   if (dst->k == src->k || dst->v == src->v || dst->meta == src->meta ||
@@ -152,7 +156,7 @@ int trimkv_compact(const trimkv_cache_t* src, const uint8_t* keep, int32_t reser
   if (dst->n_pages < need) return TRIMKV_ECAPACITY;
   if ((rc = ws_check(ws, ws_bytes, compact_ws_layout(src).total))) return rc;
   if (H == 0) return TRIMKV_OK;
-  return launch_compact(src, keep, reserve, dst, pages_used, ws, S(stream));
+  return launch_compact(src, keep, reserve, max_kept_total, dst, pages_used, ws, S(stream));
 }
 
 int trimkv_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float* lse_ref, const void* q,
@@ -161,7 +165,8 @@ int trimkv_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float
   int rc;
   if (!cache_shape_ok(c, &rc)) return rc;
   if (group < 1 || group > 16) return TRIMKV_EUNSUPPORTED;
-  if ((keep && lse_ref) || !q || !out || !dropped || !table_ok(c) || !pools_ok(c)) return TRIMKV_EINVAL;
+  if ((keep && lse_ref) || !q || !out || !dropped || !table_ok(c) || !pools_ok(c) || ((uintptr_t)keep & 15))
+    return TRIMKV_EINVAL;
   if ((rc = ws_check(ws, ws_bytes, attn_ws_layout(c, group).total))) return rc;
   if (c->n_heads == 0) return TRIMKV_OK;
   return launch_decode_attn(c, keep, lse_ref, q, group, scale, out, dropped, lse_out, ws, S(stream));

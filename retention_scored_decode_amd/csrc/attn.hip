@@ -34,9 +34,11 @@ constexpr int GMAX = 16;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
+enum { A_PLAIN = 0, A_MASK = 1, A_LOGITS = 2 };
+
 struct AttnWs {
   int32_t* item_off;   // [H + 1]
-  int32_t* item_head;  // [Wmax]
+  int4* item;          // [Wmax + 4] (head, first CSR page, valid entries, pages)
   float* stats;        // [Wmax][G][3]   (max2, kept sum, dropped sum)
   float* acc;          // [Wmax][G][D]
   float* lse2;         // [H * G] base-2 LSE (mass op)
@@ -70,7 +72,7 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 template <int L>
 __device__ __forceinline__ float bcast_row(float v) {
   // DPP row_newbcast: every lane of a 16-lane row reads lane L of that row
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + L, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + L, 0xF, 0xF, true));
 }
 
 template <int GM, typename F>
@@ -92,16 +94,17 @@ __device__ __forceinline__ float bcast_dyn(float v, int g) {
   }
 }
 
-// Work list of (head, chunk of cha pages).
+// Work list of (head, chunk of cha pages): one 16-byte record per item.
 __global__ void __launch_bounds__(1024) k_attn_prep(const int32_t* __restrict__ page_off,
                                                     const int32_t* __restrict__ len, int n_heads, int cha,
                                                     AttnWs w) {
   __shared__ int64_t tmp[1024 / WAVE + 1];
   __shared__ PrepLDS L;
   const int T = prep_chunks<1024>(page_off, len, n_heads, cha, L, tmp, w.item_off);
-  for (int it = blockIdx.x * 1024 + threadIdx.x; it < T; it += gridDim.x * 1024)
-    w.item_head[it] = n_heads <= PREP_HMAX ? upper_index(L.off, n_heads + 1, it)
-                                           : upper_index(w.item_off, n_heads + 1, it);
+  for (int it = blockIdx.x * 1024 + threadIdx.x; it < T; it += gridDim.x * 1024) {
+    const ChunkInfo ci = chunk_info(L, w.item_off, page_off, len, n_heads, cha, it);
+    w.item[it] = make_int4(ci.h, ci.page0, ci.nv, ci.npg);
+  }
 }
 
 // Merge all partials of KV head h: per query head g, M = max of the item
@@ -176,64 +179,69 @@ template <int D> struct VRow;
 template <> struct VRow<128> { typedef uint4 T; };
 template <> struct VRow<64> { typedef uint2 T; };
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// Threshold (log2 units) of the lazily updated running maximum: between two
+// rescalings every exp2(z - m) stays below 2^RESCALE_T, far inside fp32.
+constexpr float RESCALE_T = 10.f;
+
 // ---------------------------------------------------------------------------
-// bf16 K/V, MFMA logits.  LOGITS=false: attention partials; LOGITS=true:
-// write base-2 logits of every valid key and (max, sum) partials.
+// bf16 K/V, MFMA logits.  MODE: A_PLAIN (every valid key kept), A_MASK (keep
+// plane; dropped keys only enter the dropped sum, their V is not read),
+// A_LOGITS (write base-2 logits of every valid key, (max, sum) partials).
 //
 // One wave per work item (head, up to a.cha consecutive pages); waves never
-// wait for each other.  The item's page ids and keep words arrive with one
-// load each; every page's K and V tiles are loaded one page ahead.  Each
-// 16-lane row is an online-softmax stream over keys 4r..4r+3 of every page;
-// the four streams are combined with cross-lane operations at the end.
+// wait for each other.  S = K q^T on v_mfma_f32_16x16x32_bf16: lane (r, col)
+// feeds key `col`, dims 32u + 8r .. +7 of K and the same dims of query head
+// `col`, straight from 16-byte loads; it receives S[key 4r + j][head col].
+// Each 16-lane row r is an online-softmax stream over keys 4r..4r+3 of every
+// page; its running maximum is raised only when a logit exceeds it by more
+// than RESCALE_T (a wave-uniform branch), so the common page costs one FMA
+// and one exp2 per logit.  P V runs on the VALU in fp32.  K and V tiles of
+// page i + LA are in flight while page i is processed.
 // ---------------------------------------------------------------------------
-template <int D, int GM, bool LOGITS>
+template <int D, int GM, int MODE>
 __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
-  constexpr int KU = D / 32;    // uint4 of K per lane per page
-  constexpr int NK = D / 16;    // MFMAs per page
+  constexpr int KU = D / 32;    // 16-byte K pieces per lane per page = MFMAs per page
   constexpr int DS = D / 16;    // V dims per lane
+  constexpr bool LOGITS = MODE == A_LOGITS;
   typedef typename VRow<D>::T VT;
   const AttnWs& w = a.w;
   const int lane = threadIdx.x & 63, r = lane >> 4, col = lane & 15;
   const int item = blockIdx.x * (NT / WAVE) + (threadIdx.x >> 6);
-  if (item >= w.item_off[a.n_heads]) return;   // per-wave exit: no block barriers below
+  const int total = w.item_off[a.n_heads];
+  const int4 rec = w.item[item];   // (head, first CSR page, valid entries, pages); padded past the end
+  if (item >= total) return;       // per-wave exit: no block barriers below
   const int G = a.group;
-  const int h = w.item_head[item];
-  const int pbase = a.page_off[h];
-  const int np = a.page_off[h + 1] - pbase;
-  const int p0 = (item - w.item_off[h]) * a.cha;
-  const int cnt = min(a.cha, np - p0);   // pages of this item, 1..cha (cha <= 32)
-  const int n = a.len[h];
-  const uint16_t* kq = (const uint16_t*)a.q;
+  const int h = rec.x, page0 = rec.y, nv = rec.z, cnt = rec.w;
 
   // lane l: page id of page l; keep words: lane l of kw[b] covers page 16b + l/4, keys 4(l%4)..+3
-  const int pid_l = lane < cnt ? a.page_ids[pbase + p0 + lane] : 0;
+  const int pid_l = lane < cnt ? a.page_ids[page0 + lane] : 0;
   uint32_t kw0 = 0xFFFFFFFFu, kw1 = 0xFFFFFFFFu;
-  if (!LOGITS && a.keep) {
-    const uint8_t* kb = a.keep + (int64_t)(pbase + p0) * PAGE;
+  if (MODE == A_MASK) {
+    const uint8_t* kb = a.keep + (int64_t)page0 * PAGE;
     if (lane / 4 < cnt) kw0 = *reinterpret_cast<const uint32_t*>(kb + 4 * lane);
     if (16 + lane / 4 < cnt) kw1 = *reinterpret_cast<const uint32_t*>(kb + 256 + 4 * lane);
   }
   auto kword = [&](int i) -> uint32_t {
-    if (LOGITS || !a.keep) return 0xFFFFFFFFu;
+    if (MODE != A_MASK) return 0xFFFFFFFFu;
     const uint32_t src = (i < 16) ? kw0 : kw1;
     return (uint32_t)__shfl((int)src, ((i & 15) << 2) + r, WAVE);
   };
 
-  // B operand: query column g = col; MFMA kk covers dims 32*(kk/2) + 8r + 4*(kk%2) + [0,4)
-  short4_t qop[NK];
+  // B operand of MFMA u: dims 32u + 8r .. +7 of query head col (zero for col >= G)
+  uint4 qop[KU];
+  {
+    const uint8_t* qrow = (const uint8_t*)a.q + ((size_t)h * G + (col < G ? col : 0)) * D * 2 + 16 * r;
 #pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    short4_t x = {0, 0, 0, 0};
-    if (col < G) {
-      const uint16_t* src = kq + ((size_t)h * G + col) * D + 32 * (kk / 2) + 8 * r + 4 * (kk % 2);
-      const uint2 u = *reinterpret_cast<const uint2*>(src);
-      x[0] = (short)(u.x & 0xFFFF); x[1] = (short)(u.x >> 16);
-      x[2] = (short)(u.y & 0xFFFF); x[3] = (short)(u.y >> 16);
+    for (int u = 0; u < KU; ++u) {
+      qop[u] = *reinterpret_cast<const uint4*>(qrow + 64 * u);
+      if (col >= G) qop[u] = make_uint4(0, 0, 0, 0);
     }
-    qop[kk] = x;
   }
 
   float m = -INFINITY, la = 0.f, ld = 0.f;
+  float nm = INFINITY;   // -m, or +inf while m = -inf (every finite logit then forces an update)
   float acc[GM][DS];
   for_g<GM>([&](int g) {
 #pragma unroll
@@ -241,6 +249,8 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
   });
   const uint8_t* kbase = (const uint8_t*)a.k;
   const uint8_t* vbase = (const uint8_t*)a.v;
+  const uint32_t koff = col * D * 2 + 16 * r;            // this lane's K bytes within a page
+  const uint32_t voff = (4 * r * D + col * DS) * 2;      // this lane's V bytes of key 4r
 
   // Every load is issued unconditionally so the compiler can count outstanding
   // loads exactly and wait only for the page being processed: a V row that is
@@ -248,99 +258,113 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
   // K tile instead, a line this wave has just requested.
   auto load = [&](int i, uint32_t kwi, uint4 (&kd)[KU], VT (&vd)[4]) {
     const int64_t phys = __builtin_amdgcn_readlane(pid_l, i);
-    const uint8_t* kpage = kbase + phys * PAGE * D * 2;
-    const uint8_t* krow = kpage + col * D * 2 + 16 * r;
+    const uint8_t* kpage = kbase + phys * (PAGE * D * 2);
+    const uint8_t* vpage = vbase + phys * (PAGE * D * 2);
 #pragma unroll
-    for (int u = 0; u < KU; ++u) kd[u] = *reinterpret_cast<const uint4*>(krow + 64 * u);
-    if (!LOGITS) {
-      const int i0 = (p0 + i) * PAGE + 4 * r;
+    for (int u = 0; u < KU; ++u) kd[u] = *reinterpret_cast<const uint4*>(kpage + koff + 64 * u);
+    if (MODE == A_PLAIN) {
+      // every row of an allocated page is readable; rows past the end are
+      // zeroed before use
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vd[j] = *reinterpret_cast<const VT*>(vpage + voff + j * D * 2);
+    } else if (MODE == A_MASK) {
+      const int i0 = i * PAGE + 4 * r;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bool need = i0 + j < n && ((kwi >> (8 * j)) & 0xFFu);
-        const uint8_t* src = need ? vbase + ((phys * PAGE + 4 * r + j) * D + col * DS) * 2 : kpage;
+        const bool need = i0 + j < nv && ((kwi >> (8 * j)) & 0xFFu);
+        const uint8_t* src = need ? vpage + voff + j * D * 2 : kpage + col * 16;
         vd[j] = *reinterpret_cast<const VT*>(src);
       }
     }
   };
 
   auto compute = [&](int i, uint32_t kwi, uint4 (&kc)[KU], VT (&vc)[4]) {
-    const int p = p0 + i;
-    // ---- logits S[key = 4r + j][g = col] ----
     float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      short4_t a0 = {(short)(kc[u].x & 0xFFFF), (short)(kc[u].x >> 16), (short)(kc[u].y & 0xFFFF),
-                     (short)(kc[u].y >> 16)};
-      short4_t a1 = {(short)(kc[u].z & 0xFFFF), (short)(kc[u].z >> 16), (short)(kc[u].w & 0xFFFF),
-                     (short)(kc[u].w >> 16)};
-      s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a0, qop[2 * u], s, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a1, qop[2 * u + 1], s, 0, 0, 0);
-    }
-    const int i0 = p * PAGE + 4 * r;   // entry index of key 4r within the head
-    float z[4];
-    bool valid[4], kept[4];
+    for (int u = 0; u < KU; ++u)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kc[u]),
+                                                  __builtin_bit_cast(bf16x8_t, qop[u]), s, 0, 0, 0);
+    const int i0 = i * PAGE + 4 * r;      // entry of key 4r within the item
+    const bool full = (i + 1) * PAGE <= nv;   // wave-uniform
+    float pj[4];
+    bool slow = !full;
+    if (full) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      valid[j] = i0 + j < n;
-      kept[j] = valid[j] && ((kwi >> (8 * j)) & 0xFFu);
-      z[j] = valid[j] ? s[j] * a.scale2 : -INFINITY;
+      for (int j = 0; j < 4; ++j) pj[j] = fmaf(s[j], a.scale2, nm);
+      slow = __any(fmaxf(fmaxf(pj[0], pj[1]), fmaxf(pj[2], pj[3])) > RESCALE_T);
     }
+    float alpha = 1.f;
+    if (slow) {
+      float z[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) z[j] = i0 + j < nv ? s[j] * a.scale2 : -INFINITY;
+      const float mn = fmaxf(m, fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+      if (mn != -INFINITY) {
+        alpha = exp2f(m - mn);   // 0 while m = -inf
+        m = mn;
+        nm = -mn;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pj[j] = z[j] - m;
+      la *= alpha;
+      ld *= alpha;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pj[j] = __builtin_amdgcn_exp2f(pj[j]);   // exp2(-inf) = 0; NaN only while m = -inf
+    if (slow && m == -INFINITY) pj[0] = pj[1] = pj[2] = pj[3] = 0.f;
     if (LOGITS) {
       if (col < G) {
-        float* dst = w.logits + (int64_t)col * a.plane + (int64_t)(pbase + p) * PAGE + 4 * r;
+        float* dst = w.logits + (int64_t)col * a.plane + (int64_t)(page0 + i) * PAGE + 4 * r;
+        if (full) {
+          *reinterpret_cast<float4*>(dst) = make_float4(s[0] * a.scale2, s[1] * a.scale2, s[2] * a.scale2,
+                                                        s[3] * a.scale2);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (valid[j]) dst[j] = z[j];
+          for (int j = 0; j < 4; ++j)
+            if (i0 + j < nv) dst[j] = s[j] * a.scale2;
+        }
       }
     }
-    const float pm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    const float mn = fmaxf(m, pm);
-    float alpha, pj[4];
-    if (mn == -INFINITY) {
-      alpha = 1.f;
-      pj[0] = pj[1] = pj[2] = pj[3] = 0.f;
-    } else {
-      alpha = exp2f(m - mn);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pj[j] = valid[j] ? exp2f(z[j] - mn) : 0.f;
-    }
-    m = mn;
-    float sk = 0.f, sd = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (kept[j]) sk += pj[j];
-      else sd += pj[j];
-    }
-    la = la * alpha + sk;
-    ld = ld * alpha + sd;
-    if (!LOGITS) {
-      // ---- P V: lanes of row r own dims [col*DS, col*DS+DS) of keys 4r..4r+3 ----
-      float av[GM];
-      float pk[GM][4];
-      for_g<GM>([&](int g) {
-        av[g] = bcast_dyn(alpha, g);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pk[g][j] = bcast_dyn(kept[j] ? pj[j] : 0.f, g);
-      });
-      for_g<GM>([&](int g) {
-#pragma unroll
-        for (int d = 0; d < DS; ++d) acc[g][d] *= av[g];
-      });
+    if (MODE == A_MASK) {
+      float sk = 0.f, sd = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (kept[j]) {
+        const bool kept = ((kwi >> (8 * j)) & 0xFFu) && (full || i0 + j < nv);
+        sk += kept ? pj[j] : 0.f;
+        sd += kept ? 0.f : pj[j];
+        if (!kept) pj[j] = 0.f;
+      }
+      la += sk;
+      ld += sd;
+    } else {
+      la += (pj[0] + pj[1]) + (pj[2] + pj[3]);
+    }
+    if (!LOGITS) {
+      if (slow) {
+        for_g<GM>([&](int g) {
+          const float av = bcast_dyn(alpha, g);
+#pragma unroll
+          for (int d = 0; d < DS; ++d) acc[g][d] *= av;
+        });
+      }
+      // P V: lanes of row r own dims [col*DS, col*DS+DS) of keys 4r..4r+3
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool kept = MODE == A_PLAIN ? true : (((kwi >> (8 * j)) & 0xFFu) && (full || i0 + j < nv));
+        if (MODE == A_PLAIN || kept) {
+          VT vv = vc[j];
+          if (MODE == A_PLAIN && !full && i0 + j >= nv) vv = VT{};   // unwritten rows may hold non-finite bits
           float vf[DS];
           if constexpr (DS == 8) {
-            const uint4 vv = vc[j];
             vf[0] = bf16lo(vv.x); vf[1] = bf16hi(vv.x); vf[2] = bf16lo(vv.y); vf[3] = bf16hi(vv.y);
             vf[4] = bf16lo(vv.z); vf[5] = bf16hi(vv.z); vf[6] = bf16lo(vv.w); vf[7] = bf16hi(vv.w);
           } else {
-            const uint2 vv = vc[j];
             vf[0] = bf16lo(vv.x); vf[1] = bf16hi(vv.x); vf[2] = bf16lo(vv.y); vf[3] = bf16hi(vv.y);
           }
           for_g<GM>([&](int g) {
+            const float pk = bcast_dyn(pj[j], g);
 #pragma unroll
-            for (int d = 0; d < DS; ++d) acc[g][d] = fmaf(pk[g][j], vf[d], acc[g][d]);
+            for (int d = 0; d < DS; ++d) acc[g][d] = fmaf(pk, vf[d], acc[g][d]);
           });
         }
       }
@@ -349,7 +373,7 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
 
   // ring of LA + 1 page buffers: page ii + LA is loaded while page ii is
   // processed (indices past the item's last page reload that page)
-  constexpr int LA = GM <= 4 ? 3 : (GM <= 8 ? 2 : 1);
+  constexpr int LA = GM <= 4 ? 2 : 1;
   constexpr int NB = LA + 1;
   uint4 kb[NB][KU];
   VT vb[NB][4];
@@ -420,23 +444,19 @@ __global__ void __launch_bounds__(NT) k_attn_f32(AttnArgs a) {
   const int item = blockIdx.x;
   if (item >= w.item_off[a.n_heads]) return;
   const int G = a.group;
-  const int h = w.item_head[item];
-  const int pbase = a.page_off[h];
-  const int np = a.page_off[h + 1] - pbase;
-  const int p0 = (item - w.item_off[h]) * CHA_F32;
-  const int n = a.len[h];
+  const int4 rec = w.item[item];
+  const int h = rec.x, page0 = rec.y, nv = rec.z, cnt = rec.w;
   const float* qf = (const float*)a.q;
   for (int i = threadIdx.x; i < G * D; i += NT) sq[i / D][i % D] = qf[(size_t)h * G * D + i];
   __syncthreads();
   const int t = threadIdx.x;
-  const int p = p0 + t / PAGE;
-  const int e = p * PAGE + t % PAGE;
-  const bool valid = p < np && e < n;
+  const int p = t / PAGE;   // page within the item
+  const bool valid = p < cnt && t < nv;
   int64_t slot = 0;
   bool kept = valid;
   if (valid) {
-    slot = (int64_t)a.page_ids[pbase + p] * PAGE + t % PAGE;
-    if (!LOGITS && a.keep) kept = a.keep[(int64_t)(pbase + p) * PAGE + t % PAGE] != 0;
+    slot = (int64_t)a.page_ids[page0 + p] * PAGE + t % PAGE;
+    if (!LOGITS && a.keep) kept = a.keep[(int64_t)(page0 + p) * PAGE + t % PAGE] != 0;
   }
   const float* krow = (const float*)a.k + slot * D;
   for (int g = 0; g < G; ++g) {
@@ -445,7 +465,7 @@ __global__ void __launch_bounds__(NT) k_attn_f32(AttnArgs a) {
       float dot = 0.f;
       for (int d = 0; d < D; ++d) dot = fmaf(sq[g][d], krow[d], dot);
       z = dot * a.scale2;
-      if (LOGITS) w.logits[(int64_t)g * a.plane + (int64_t)(pbase + p) * PAGE + t % PAGE] = z;
+      if (LOGITS) w.logits[(int64_t)g * a.plane + (int64_t)(page0 + p) * PAGE + t % PAGE] = z;
     }
     sp[g][t] = z;
   }
@@ -486,8 +506,7 @@ __global__ void __launch_bounds__(NT) k_attn_f32(AttnArgs a) {
       for (int k = 0; k < NKEY; ++k) {
         const float pk = sp[g][k];
         if (pk != 0.f) {
-          const int pp = p0 + k / PAGE;
-          const int64_t sl = (int64_t)a.page_ids[pbase + pp] * PAGE + k % PAGE;
+          const int64_t sl = (int64_t)a.page_ids[page0 + k / PAGE] * PAGE + k % PAGE;
           s = fmaf(pk, vb[sl * D + d], s);
         }
       }
@@ -537,7 +556,7 @@ AttnWs carve(const trimkv_cache_t* c, int group, void* ws, bool mass) {
   char* b = (char*)ws;
   AttnWs w;
   w.item_off = (int32_t*)(b + L.off[0]);
-  w.item_head = (int32_t*)(b + L.off[1]);
+  w.item = (int4*)(b + L.off[1]);
   w.stats = (float*)(b + L.off[2]);
   w.acc = (float*)(b + L.off[3]);
   w.lse2 = mass ? (float*)(b + L.off[4]) : nullptr;
@@ -547,8 +566,9 @@ AttnWs carve(const trimkv_cache_t* c, int group, void* ws, bool mass) {
 
 int gm_for(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : g <= 8 ? 8 : 16; }
 
-template <bool LOGITS>
+template <int MODE>
 int launch_main(const trimkv_cache_t* c, AttnArgs& a, hipStream_t st) {
+  constexpr bool LOGITS = MODE == A_LOGITS;
   const int64_t W = max_chunks(c, a.cha);   // bound on the number of items
   const dim3 blk(NT);
   if (c->dtype == TRIMKV_F32) {
@@ -559,7 +579,7 @@ int launch_main(const trimkv_cache_t* c, AttnArgs& a, hipStream_t st) {
   }
   const dim3 grid((unsigned)((W + NT / WAVE - 1) / (NT / WAVE)));   // one item per wave
   const int gm = gm_for(a.group);
-#define TRIMKV_BF16(DD, GG) hipLaunchKernelGGL((k_attn_bf16<DD, GG, LOGITS>), grid, blk, 0, st, a)
+#define TRIMKV_BF16(DD, GG) hipLaunchKernelGGL((k_attn_bf16<DD, GG, MODE>), grid, blk, 0, st, a)
   if (c->head_dim == 128) {
     switch (gm) {
       case 1: TRIMKV_BF16(128, 1); break;
@@ -587,7 +607,7 @@ WsLayout attn_ws_layout(const trimkv_cache_t* c, int group) {
   const int64_t W = max_chunks(c, CHA_MIN);
   WsLayout L;
   L.add(((int64_t)c->n_heads + 1) * 4);
-  L.add(W * 4);
+  L.add((W + 4) * 16);
   L.add(W * group * 3 * 4);
   L.add(W * group * (int64_t)c->head_dim * 4);
   return L;
@@ -597,7 +617,7 @@ WsLayout mass_ws_layout(const trimkv_cache_t* c, int group) {
   const int64_t W = max_chunks(c, CHA_MIN);
   WsLayout L;
   L.add(((int64_t)c->n_heads + 1) * 4);
-  L.add(W * 4);
+  L.add((W + 4) * 16);
   L.add(W * group * 3 * 4);
   L.add(0);
   L.add((int64_t)c->n_heads * group * 4);
@@ -615,7 +635,7 @@ int launch_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float
                      c->page_off, c->len, c->n_heads, cha, w);
   AttnArgs a{c->page_off, c->page_ids, c->len, c->k, c->v, keep, q, c->n_heads, group, scale * LOG2E,
              c->n_pages * PAGE, cha, w, lse_ref, out, dropped, lse_out};
-  int rc = launch_main<false>(c, a, st);
+  int rc = keep ? launch_main<A_MASK>(c, a, st) : launch_main<A_PLAIN>(c, a, st);
   if (rc) return rc;
   if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(c->n_heads), dim3(NT), 0, st, a, 1);
   else hipLaunchKernelGGL(k_attn_merge<64>, dim3(c->n_heads), dim3(NT), 0, st, a, 1);
@@ -630,7 +650,7 @@ int launch_attn_mass(const trimkv_cache_t* c, const void* q, int group, float sc
                      c->page_off, c->len, c->n_heads, cha, w);
   AttnArgs a{c->page_off, c->page_ids, c->len, c->k, c->v, nullptr, q, c->n_heads, group, scale * LOG2E,
              c->n_pages * PAGE, cha, w, nullptr, nullptr, nullptr, lse_full};
-  int rc = launch_main<true>(c, a, st);
+  int rc = launch_main<A_LOGITS>(c, a, st);
   if (rc) return rc;
   if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(c->n_heads), dim3(NT), 0, st, a, 0);
   else hipLaunchKernelGGL(k_attn_merge<64>, dim3(c->n_heads), dim3(NT), 0, st, a, 0);
