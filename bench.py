@@ -43,11 +43,140 @@ def parse():
     ap.add_argument("--workload", default="llama8b_32k")
     ap.add_argument("--calib", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="write profiles/pmc_<workload>.md from two rocprofv3 --pmc databases "
+                         "(FETCH_SIZE, WRITE_SIZE) of a --calib run, then exit")
+    ap.add_argument("--trace-summary", metavar="KERNEL_STATS_CSV",
+                    help="write profiles/kernel_stats_<workload>.md from a rocprofv3 --kernel-trace --stats "
+                         "csv of this benchmark, then exit")
     return ap.parse_args()
+
+
+def trace_summary(workload, csv_path):
+    """Per-kernel call count and average duration from rocprofv3 --stats."""
+    import csv
+    rows = list(csv.DictReader(open(csv_path)))
+    out = os.path.join(ROOT, "profiles", "kernel_stats_%s.md" % workload)
+    with open(out, "w") as fh:
+        fh.write("# Kernel durations, %s workload (rocprofv3 --kernel-trace --stats)\n\n" % workload)
+        fh.write("Command (repository root):\n\n    rocprofv3 --kernel-trace --stats --output-format csv "
+                 "-d gpurun_out/prof -o c2 -- python -u bench.py --steps 5 --warmup 1 --cold-reps 2 "
+                 "--no-cpu-baseline\n    python bench.py --trace-summary gpurun_out/prof/c2_kernel_stats.csv\n\n")
+        fh.write("A run is 1 + 5 pipeline steps (score, select, mask-mode attention, compaction, plain "
+                 "decode) plus 2 flushed plain-decode repetitions, so the plain-decode average mixes "
+                 "6 warm and 2 cold calls.\n\n")
+        fh.write("| kernel | calls | average us | min us | max us | share % |\n|---|---|---|---|---|---|\n")
+        for r in rows:
+            fh.write("| %s | %s | %.1f | %.1f | %.1f | %s |\n" % (
+                short_kernel(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                float(r["MaxNs"]) / 1e3, r["Percentage"]))
+    print("wrote", out)
+
+
+# main kernel(s) of each stage, as rocprofv3 names them, and the sources they are built from
+STAGE_KERNEL = {
+    "score": ("k_score", ["score.hip", "common.h"]),
+    "select": ("k_sel_hist<0..2> + k_sel_decide", ["select.hip", "common.h"]),
+    "attend_mask": ("k_attn_bf16<128, 4, 1>", ["attn.hip", "common.h"]),
+    "compact": ("k_cmp_copy<256>", ["compact.hip", "common.h"]),
+    "decode": ("k_attn_bf16<128, 4, 0>", ["attn.hip", "common.h"]),
+}
+CSRC = os.path.join(ROOT, "retention_scored_decode_amd", "csrc")
+
+
+def source_hash(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_kernel(name):
+    import re
+    n = re.sub(r"\(.*", "", name.replace("(anonymous namespace)::", "").replace("trimkv::", ""))
+    return n.replace("void ", "").strip()
+
+
+def pmc_summary(workload, fetch_db, write_db):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of every kernel, scaled by the
+    same counters on the 1 GiB calibration copy, into profiles/pmc_<workload>.md."""
+    import sqlite3
+    import statistics
+
+    def load(db):
+        c = sqlite3.connect(db)
+        cols = [r[1] for r in c.execute("pragma table_info(counters_collection)")]
+        ci = {k: i for i, k in enumerate(cols)}
+        vals = {}
+        for r in c.execute("select * from counters_collection"):
+            vals.setdefault(short_kernel(r[ci["kernel_name"]]), []).append(float(r[ci["value"]]))
+        return vals
+
+    fetch, write = load(fetch_db), load(write_db)
+    gib_kib = float(1 << 20)
+    f_copy = max(fetch.get("__amd_rocclr_copyBuffer", [0.0]))
+    w_copy = max(write.get("__amd_rocclr_copyBuffer", [0.0]))
+    if f_copy <= 0 or w_copy <= 0:
+        raise SystemExit("no calibration copy in the databases (run bench.py --calib under rocprofv3)")
+    fr, fw = gib_kib / f_copy, gib_kib / w_copy
+    rows, data = [], {}
+    for k in sorted(set(fetch) & set(write)):
+        if k.startswith("__amd") or k.startswith("at::"):
+            continue
+        fk, wk = statistics.mean(fetch[k]), statistics.mean(write[k])
+        data[k] = {"fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                   "traffic_bytes": round((fk * fr + wk * fw) * 1024)}
+        rows.append("| %s | %d | %.0f | %.0f | %.1f |" % (k, len(fetch[k]), fk, wk,
+                                                        (fk * fr + wk * fw) * 1024 / 1e6))
+    hashes = {s: source_hash(f) for s, (_, f) in STAGE_KERNEL.items()}
+    out = os.path.join(ROOT, "profiles", "pmc_%s.md" % workload)
+    with open(out, "w") as fh:
+        fh.write("# HBM traffic per dispatch, %s workload (rocprofv3 PMC)\n\n" % workload)
+        fh.write("Commands (repository root, one counter per run):\n\n")
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            fh.write("    rocprofv3 --pmc %s -d gpurun_out/pmc_%s -o run -- python -u bench.py --steps 2 "
+                     "--warmup 1 --cold-reps 1 --no-cpu-baseline --calib\n" % (c, c))
+        fh.write("    python bench.py --pmc-summary gpurun_out/pmc_FETCH_SIZE/run_results.db "
+                 "gpurun_out/pmc_WRITE_SIZE/run_results.db\n\n")
+        fh.write("Calibration: the 1 GiB device copy reads FETCH_SIZE %.0f KiB and WRITE_SIZE %.0f KiB, "
+                 "so traffic = FETCH x %.3f + WRITE x %.3f (KiB -> bytes x 1024).\n\n" % (f_copy, w_copy, fr, fw))
+        fh.write("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | traffic MB |\n|---|---|---|---|---|\n")
+        fh.write("\n".join(rows) + "\n\n")
+        fh.write("Machine-readable (source hashes of the kernels' files at measurement time):\n\n```json\n")
+        fh.write(json.dumps({"read_factor": fr, "write_factor": fw, "source_hash": hashes, "kernels": data},
+                            indent=1))
+        fh.write("\n```\n")
+    print("wrote", out)
+
+
+def traffic_for(workload, stage):
+    """HBM bytes per launch of the stage's main kernel from the committed
+    counter summary, or None if there is none or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", "pmc_%s.md" % workload)
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    try:
+        blob = json.loads(txt.split("```json", 1)[1].split("```", 1)[0])
+    except (IndexError, ValueError):
+        return None
+    kname, files = STAGE_KERNEL[stage]
+    if blob.get("source_hash", {}).get(stage) != source_hash(files):
+        return None
+    k = blob.get("kernels", {}).get(kname)
+    return None if k is None else int(k["traffic_bytes"])
 
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.workload, *args.pmc_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.workload, args.trace_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the path is single-GPU (see DESIGN.md for how it would shard); "
               "run with --gpus 1", file=sys.stderr)
@@ -105,34 +234,56 @@ def main():
 
     stages = ["score", "select", "attend_mask", "compact", "decode"]
 
-    def step(ev=None):
+    def step(ev=None, kev=None):
+        # ev: stage boundaries; kev: (start, stop) pairs around each stage's main kernel(s)
+        def arm(j):
+            if kev:
+                tk.profile_next(kev[j][0], kev[j][1])
         if ev: ev[0].record()
+        arm(0)
         tk.score(src, seg, t_dev, score)
         if ev: ev[1].record()
+        arm(1)
         tk.select_global(src, score, seg, budget, keep, kept, ws=ws_sel)
         if ev: ev[2].record()
+        arm(2)
         tk.decode_attn(src, q, G, scale, out_m, drop_m, keep=keep, ws=ws_att)
         if ev: ev[3].record()
+        arm(3)
         tk.compact(src, keep, 0, M * w.n_seg, dst, used, ws=ws_cmp)
         if ev: ev[4].record()
+        arm(4)
         tk.decode_attn(dst, q, G, scale, out_p, drop_p, ws=ws_dec)
         if ev: ev[5].record()
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    kevs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in stages]
+            for _ in range(args.steps)]
+    for kk in kevs:            # create the events' handles before the library records them
+        for a, b in kk:
+            a.record()
+            b.record()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    # the same steps again with each stage's main kernel(s) bracketed by events
+    # inside the library call (separately, so the extra records do not touch the stage times)
+    for i in range(args.steps):
+        step(None, kevs[i])
+    torch.cuda.synchronize()
     per = {s: [] for s in stages}
-    for e in evs:
+    kper = {s: [] for s in stages}
+    for e, kk in zip(evs, kevs):
         for j, s in enumerate(stages):
             per[s].append(e[j].elapsed_time(e[j + 1]) * 1e-3)
+            kper[s].append(kk[j][0].elapsed_time(kk[j][1]) * 1e-3)
     t = {s: float(np.mean(v)) for s, v in per.items()}
+    kt = {s: float(np.mean(v)) for s, v in kper.items()}
 
     # sanity of the step's results (not timed)
     kept_np = kept.cpu().numpy()
@@ -175,7 +326,8 @@ def main():
     for s in stages:
         gbs = algo[s] / t[s] / 1e9
         stage_out[s] = {"us": round(t[s] * 1e6, 2), "algo_bytes": algo[s], "GBps": round(gbs, 1),
-                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+                        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "main_kernel": STAGE_KERNEL[s][0],
+                        "main_kernel_us": round(kt[s] * 1e6, 2)}
     dom = max(stages, key=lambda s: t[s])
     sc_t = t["select"] + t["compact"]
     value = algo["decode"] / t["decode"] / 1e9
@@ -198,9 +350,11 @@ def main():
         "select_compact_GBps": round((algo["select"] + algo["compact"]) / sc_t / 1e9, 1),
         "decode_cold_GBps": round(algo["decode"] / t_cold / 1e9, 1),
         "stages": stage_out,
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(algo[dom] / t[dom] / 1e9, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(algo[dom] / t[dom] / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+        "roofline": {"stage": dom, "kernel": STAGE_KERNEL[dom][0], "bound": "hbm",
+                     "achieved": round(algo[dom] / kt[dom] / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(algo[dom] / kt[dom] / 1e9 / HBM_PEAK_GBS, 4),
+                     "kernel_us": round(kt[dom] * 1e6, 2), "algo_bytes": algo[dom],
+                     "traffic": traffic_for(w.name, dom)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, pc, M)
@@ -227,7 +381,7 @@ def cpu_baseline(w, pc, M):
         t1 = time.perf_counter()
         keep, kept = ref.select_global(scores, [0, H], [M])
         t2 = time.perf_counter()
-        sample = list(range(0, H, 8))          # 32 of 256 KV heads
+        sample = list(range(H))                # every KV head
         kslots = [ref.head_phys_slots(po, pi, ln, h)[keep[h]] for h in sample]
         K = [synth.bf16_bits_to_f32(pc.k.reshape(-1, D)[s]).astype(np.float64) for s in kslots]
         V = [synth.bf16_bits_to_f32(pc.v.reshape(-1, D)[s]).astype(np.float64) for s in kslots]
@@ -240,8 +394,8 @@ def cpu_baseline(w, pc, M):
     gbs = (512 * ent + len(qs) * D * 6) / (t4 - t3) / 1e9
     N = int(ln.sum())
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "decode attention over the kept entries of 32 of 256 KV heads (%d entries); "
-                      "scores + global selection over all %d entries" % (ent, N),
+            "sample": "float64 decode attention over the kept entries of all %d KV heads (%d entries); "
+                      "scores + global selection over all %d entries" % (H, ent, N),
             "select_entries_per_s": round(N / (t2 - t1), 1),
             "score_s": round(t1 - t0, 2), "select_s": round(t2 - t1, 2), "attn_s": round(t4 - t3, 3)}
 

@@ -254,6 +254,19 @@ int trimkv_validate_cache(const trimkv_cache_t* cache, const int32_t* t, void* w
 /* Static description of a status code. */
 const char* trimkv_strerror(int status);
 
+/*
+ * trimkv_profile_next -- measurement hook, not part of the method.
+ * The next call on this host thread that launches its main kernel(s)
+ * records `start` (a hipEvent_t created by the caller) on its stream right
+ * before them and `stop` right after, then disarms the hook.  Main kernels:
+ * trimkv_score -> the score kernel; trimkv_select_global -> the three
+ * histogram passes and the decision pass; trimkv_compact -> the row copy;
+ * trimkv_decode_attn / trimkv_attn_mass -> the attention kernel (not its
+ * work-list preparation or the merge).  Both NULL disarms.
+ * Errors: EINVAL (exactly one of the two is NULL).
+ */
+int trimkv_profile_next(void* start, void* stop);
+
 #ifdef __cplusplus
 }
 #endif

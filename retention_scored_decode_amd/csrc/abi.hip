@@ -81,7 +81,28 @@ __global__ void k_check_slots(const int32_t* page_off, const int32_t* page_ids, 
 
 }  // namespace
 
+namespace {
+thread_local hipEvent_t g_prof_start = nullptr;
+thread_local hipEvent_t g_prof_stop = nullptr;
+}  // namespace
+
+void trimkv::prof_begin(hipStream_t st) {
+  if (g_prof_start) hipEventRecord(g_prof_start, st);
+}
+
+void trimkv::prof_end(hipStream_t st) {
+  if (g_prof_stop) hipEventRecord(g_prof_stop, st);
+  g_prof_start = g_prof_stop = nullptr;
+}
+
 extern "C" {
+
+int trimkv_profile_next(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr)) return TRIMKV_EINVAL;
+  g_prof_start = (hipEvent_t)start;
+  g_prof_stop = (hipEvent_t)stop;
+  return TRIMKV_OK;
+}
 
 const char* trimkv_strerror(int s) {
   switch (s) {

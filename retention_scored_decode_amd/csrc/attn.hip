@@ -635,7 +635,9 @@ int launch_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float
                      c->page_off, c->len, c->n_heads, cha, w);
   AttnArgs a{c->page_off, c->page_ids, c->len, c->k, c->v, keep, q, c->n_heads, group, scale * LOG2E,
              c->n_pages * PAGE, cha, w, lse_ref, out, dropped, lse_out};
+  prof_begin(st);
   int rc = keep ? launch_main<A_MASK>(c, a, st) : launch_main<A_PLAIN>(c, a, st);
+  prof_end(st);
   if (rc) return rc;
   if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(c->n_heads), dim3(NT), 0, st, a, 1);
   else hipLaunchKernelGGL(k_attn_merge<64>, dim3(c->n_heads), dim3(NT), 0, st, a, 1);
@@ -650,7 +652,9 @@ int launch_attn_mass(const trimkv_cache_t* c, const void* q, int group, float sc
                      c->page_off, c->len, c->n_heads, cha, w);
   AttnArgs a{c->page_off, c->page_ids, c->len, c->k, c->v, nullptr, q, c->n_heads, group, scale * LOG2E,
              c->n_pages * PAGE, cha, w, nullptr, nullptr, nullptr, lse_full};
+  prof_begin(st);
   int rc = launch_main<A_LOGITS>(c, a, st);
+  prof_end(st);
   if (rc) return rc;
   if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(c->n_heads), dim3(NT), 0, st, a, 0);
   else hipLaunchKernelGGL(k_attn_merge<64>, dim3(c->n_heads), dim3(NT), 0, st, a, 0);

@@ -243,12 +243,14 @@ int launch_compact(const trimkv_cache_t* src, const uint8_t* keep, int reserve, 
   hipLaunchKernelGGL(k_cmp_copy<RB>, dim3(grid), dim3(NT), 0, st, H, (const uint8_t*)src->k,                 \
                      (const uint8_t*)src->v, src->meta, w, dst->page_off, dst->page_ids, (uint8_t*)dst->k,    \
                      (uint8_t*)dst->v, dst->meta, dst->n_pages, src->n_pages * PAGE)
+  prof_begin(st);
   switch (rowb) {
     case 128: TRIMKV_COPY(128); break;
     case 256: TRIMKV_COPY(256); break;
     case 512: TRIMKV_COPY(512); break;
     default: return TRIMKV_EUNSUPPORTED;
   }
+  prof_end(st);
 #undef TRIMKV_COPY
   return check_launch();
 }

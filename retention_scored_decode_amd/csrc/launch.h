@@ -10,6 +10,11 @@ inline int check_launch() {
   return e == hipSuccess ? TRIMKV_OK : TRIMKV_EHIP;
 }
 
+// Measurement hook (trimkv_profile_next): events recorded on the call's
+// stream right before and right after the call's main kernel(s).
+void prof_begin(hipStream_t st);
+void prof_end(hipStream_t st);
+
 // Byte offsets of the pieces of one workspace; every piece 256-B aligned.
 struct WsLayout {
   size_t off[16];

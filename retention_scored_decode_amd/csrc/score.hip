@@ -119,8 +119,10 @@ int launch_score(const trimkv_cache_t* c, int n_seg, const int32_t* seg, const i
                  hipStream_t st) {
   int64_t blocks = (c->n_pages + 63) / 64;
   if (blocks == 0) return TRIMKV_OK;
+  prof_begin(st);
   hipLaunchKernelGGL(k_score, dim3((unsigned)blocks), dim3(256), 0, st, c->page_off, c->page_ids, c->len,
                      c->meta, c->n_heads, seg, n_seg, t, score);
+  prof_end(st);
   return check_launch();
 }
 

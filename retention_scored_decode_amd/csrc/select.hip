@@ -411,11 +411,13 @@ int launch_select(const trimkv_cache_t* c, const float* score, int n_seg, const 
   hipLaunchKernelGGL(k_sel_prep, dim3(prep_blocks), dim3(1024), 0, st, c->page_off, c->len, c->n_heads, n_seg, seg,
                      budget, T, w, kept);
   const unsigned hb = (unsigned)((T + CPB - 1) / CPB);
+  prof_begin(st);
   hipLaunchKernelGGL(k_sel_hist<0>, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w);
   hipLaunchKernelGGL(k_sel_hist<1>, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w);
   hipLaunchKernelGGL(k_sel_hist<2>, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w);
   hipLaunchKernelGGL(k_sel_decide, dim3((unsigned)T), dim3(NT), 0, st, c->n_heads, score, w, keep, kept,
                      keptsum != nullptr);
+  prof_end(st);
   if (keptsum)
     hipLaunchKernelGGL(k_sel_headsum, dim3((unsigned)((c->n_heads + 255) / 256)), dim3(256), 0, st, c->n_heads, w,
                        keptsum);

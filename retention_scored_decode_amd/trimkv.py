@@ -22,7 +22,7 @@ OP_SCORE, OP_SELECT, OP_COMPACT, OP_DECODE_ATTN, OP_ATTN_MASS, OP_VALIDATE = ran
 
 EXPORTS = ["trimkv_log_beta", "trimkv_score", "trimkv_select_global", "trimkv_compact",
            "trimkv_decode_attn", "trimkv_attn_mass", "trimkv_allocate", "trimkv_append",
-           "trimkv_workspace_size", "trimkv_validate_cache", "trimkv_strerror"]
+           "trimkv_workspace_size", "trimkv_validate_cache", "trimkv_strerror", "trimkv_profile_next"]
 
 
 class TrimkvError(RuntimeError):
@@ -62,6 +62,7 @@ def lib():
             "trimkv_workspace_size": [ctypes.c_int, cp, i32, i32],
             "trimkv_validate_cache": [cp, vp, vp, sz, vp],
             "trimkv_strerror": [ctypes.c_int],
+            "trimkv_profile_next": [vp, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -223,6 +224,14 @@ def append(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, beta_new: tor
            stream=None):
     _check(lib().trimkv_append(ctypes.byref(cache.struct()), _p(k_new), _p(v_new), _p(beta_new), _p(t),
                                _stream(stream)), "trimkv_append")
+
+
+def profile_next(start, stop):
+    """Arm the measurement hook: the next call's main kernel(s) are bracketed
+    by the two torch.cuda.Event objects (already recorded once, so their
+    handles exist), on that call's stream."""
+    h = lambda e: None if e is None else ctypes.c_void_p(e.cuda_event)
+    _check(lib().trimkv_profile_next(h(start), h(stop)), "trimkv_profile_next")
 
 
 def validate_cache(cache: Cache, t: torch.Tensor, ws: Optional[torch.Tensor] = None, stream=None) -> int:

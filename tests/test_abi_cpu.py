@@ -18,7 +18,7 @@ def declared():
 
 def test_exports_every_declared_symbol():
     names = declared()
-    assert len(names) == 11
+    assert len(names) == 12
     L = tk.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -126,3 +126,10 @@ def test_keep_plane_alignment_and_slot_width():
     dst = tk.CacheStruct(4, 128, 16, tk.BF16, 11, 0x11000, 0x12000, 0x13000, 0x15000, 0x16000, 0x17000)
     assert L.trimkv_compact(ctypes.byref(huge), X, 1, 100, ctypes.byref(dst), X, X, big_ws,
                             None) == tk.EUNSUPPORTED
+
+
+def test_profile_hook_arguments():
+    L = tk.lib()
+    assert L.trimkv_profile_next(None, None) == tk.OK
+    assert L.trimkv_profile_next(X, None) == tk.EINVAL
+    assert L.trimkv_profile_next(None, X) == tk.EINVAL
