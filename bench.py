@@ -77,9 +77,9 @@ def trace_summary(workload, csv_path):
 STAGE_KERNEL = {
     "score": ("k_score", ["score.hip", "common.h"]),
     "select": ("k_sel_hist<0..2> + k_sel_decide", ["select.hip", "common.h"]),
-    "attend_mask": ("k_attn_bf16<128, 4, 1>", ["attn.hip", "common.h"]),
+    "attend_mask": ("k_attn_bf16<128, 1>", ["attn.hip", "common.h"]),
     "compact": ("k_cmp_copy<256>", ["compact.hip", "common.h"]),
-    "decode": ("k_attn_bf16<128, 4, 0>", ["attn.hip", "common.h"]),
+    "decode": ("k_attn_bf16<128, 0>", ["attn.hip", "common.h"]),
 }
 CSRC = os.path.join(ROOT, "retention_scored_decode_amd", "csrc")
 

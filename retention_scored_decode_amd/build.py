@@ -11,8 +11,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-BUILD = os.path.join(ROOT, "_build")
-LIB = os.path.join(HERE, "libtrimkv.so")
+BUILD = os.environ.get("TRIMKV_BUILD_DIR", os.path.join(ROOT, "_build"))
+LIB = os.environ.get("TRIMKV_LIB_OUT", os.path.join(HERE, "libtrimkv.so"))
+# per-unit flags: attention keeps MFMA accumulators in ordinary VGPRs (its
+# occasional rescale is VALU work on the same registers)
+UNIT_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# extra hipcc flags, e.g. -DTRIMKV_CHA_PLAIN=24 (tuning knobs of the kernels)
+EXTRA = os.environ.get("TRIMKV_EXTRA_FLAGS", "").split()
 
 SOURCES = ["abi.hip", "score.hip", "select.hip", "compact.hip", "attn.hip", "alloc.hip"]
 # units whose results must be bit-reproducible: no contraction into FMA
@@ -27,7 +32,7 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
 
 def _compile(src):
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC] + COMMON + (["-ffp-contract=off"] if src in EXACT else []) + \
+    cmd = [HIPCC] + COMMON + EXTRA + UNIT_FLAGS.get(src, []) + (["-ffp-contract=off"] if src in EXACT else []) + \
         ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)

@@ -8,17 +8,19 @@
 // each key's attention mass.  DBTrimKV page, Method 4: paged per-head
 // variable-length KV.
 //
-// Split-K over work items = (KV head, chunk of 16 pages).  A work-group of
-// four waves handles one item; every (wave, 16-lane row) is an independent
-// online-softmax stream over 4 keys of each page it visits.  All G query
-// heads of the KV head are processed together, so K and V are read once.
-//
-// bf16 path: S = K q^T on MFMA (v_mfma_f32_16x16x16_bf16: 16 keys x 16
-// query columns, G <= 16 of them live), P V on the VALU with fp32
-// accumulation.  Logits are kept in base 2 (scale * log2 e folded in).
-// Partials (max, kept sum, dropped sum, acc[G][D]) are merged per query head
-// in a fixed order by a second kernel, so results are run-to-run identical.
+// bf16 caches: the CSR page list (all heads, in order) is split evenly over
+// exactly as many waves as the GPU holds at once; a wave streams its pages
+// and writes one partial (running max, kept sum, dropped sum, O[G][D]) per
+// head its range touches, at index wave + head (unique: both ranges are
+// monotone).  All G query heads of a KV head are processed together, so K
+// and V are read once.  K and V pages reach LDS through direct global->LDS
+// loads; S = K q^T and O += P V run on MFMA.  A second kernel merges the
+// partials of each head in a fixed order, so results are run-to-run
+// identical.  fp32 caches (small configurations) use one block per
+// (head, 16-page chunk) and VALU arithmetic.
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "launch.h"
@@ -27,20 +29,21 @@ namespace trimkv {
 
 namespace {
 
-constexpr int CHA_F32 = 16;  // pages per work item of the fp32 kernel (one key per thread)
-constexpr int CHA_MIN = 16;  // smallest item size (workspace bound)
+constexpr int CHA_F32 = 16;     // pages per work item of the fp32 kernel (one key per thread)
 constexpr int NT = 256;
 constexpr int GMAX = 16;
+constexpr int FLAT_WMAX = 8192;   // most waves of one bf16 launch (workspace bound)
+constexpr int LDS_HMAX = 1024;    // heads whose page offsets each block copies into LDS
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
 enum { A_PLAIN = 0, A_MASK = 1, A_LOGITS = 2 };
 
 struct AttnWs {
-  int32_t* item_off;   // [H + 1]
-  int4* item;          // [Wmax + 4] (head, first CSR page, valid entries, pages)
-  float* stats;        // [Wmax][G][3]   (max2, kept sum, dropped sum)
-  float* acc;          // [Wmax][G][D]
+  int32_t* item_off;   // [H + 1]          (fp32 work list)
+  int4* item;          // [Tmax + 4]       (fp32 work list: head, first CSR page, valid entries, pages)
+  float* stats;        // [Smax][G][3]     partials: base-2 running max, kept sum, dropped sum
+  float* acc;          // [Smax][G][D]     partials: unnormalised outputs
   float* lse2;         // [H * G] base-2 LSE (mass op)
   float* logits;       // [G][n_pages * 16] (mass op)
 };
@@ -57,7 +60,8 @@ struct AttnArgs {
   int group;
   float scale2;          // scale * log2(e)
   int64_t plane;         // logits plane stride (n_pages * 16)
-  int cha;               // pages per work item
+  int cha;               // pages per work item (fp32 path)
+  int waves;             // waves of the launch (bf16 path; 0 = fp32 work list)
   AttnWs w;
   // outputs written by the merge of each head
   const float* lse_ref;
@@ -68,32 +72,17 @@ struct AttnArgs {
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // plain vector loads/stores (no struct copies)
 
-template <int L>
-__device__ __forceinline__ float bcast_row(float v) {
-  // DPP row_newbcast: every lane of a 16-lane row reads lane L of that row
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + L, 0xF, 0xF, true));
-}
+// Read-only inputs addressed with wave-uniform indices are read through the
+// constant address space, which turns them into scalar loads.
+typedef const __attribute__((address_space(4))) int32_t* c_i32;
+typedef const __attribute__((address_space(4))) u32x4* c_u32x4;
 
-template <int GM, typename F>
-__device__ __forceinline__ void for_g(F f) {
-#pragma unroll
-  for (int g = 0; g < GM; ++g) f(g);
-}
-
-__device__ __forceinline__ float bcast_dyn(float v, int g) {
-  switch (g) {
-    case 0: return bcast_row<0>(v);   case 1: return bcast_row<1>(v);
-    case 2: return bcast_row<2>(v);   case 3: return bcast_row<3>(v);
-    case 4: return bcast_row<4>(v);   case 5: return bcast_row<5>(v);
-    case 6: return bcast_row<6>(v);   case 7: return bcast_row<7>(v);
-    case 8: return bcast_row<8>(v);   case 9: return bcast_row<9>(v);
-    case 10: return bcast_row<10>(v); case 11: return bcast_row<11>(v);
-    case 12: return bcast_row<12>(v); case 13: return bcast_row<13>(v);
-    case 14: return bcast_row<14>(v); default: return bcast_row<15>(v);
-  }
-}
-
+// Work list of (head, chunk of cha pages) for the fp32 path: one 16-byte record per item.
 // Work list of (head, chunk of cha pages): one 16-byte record per item.
 __global__ void __launch_bounds__(1024) k_attn_prep(const int32_t* __restrict__ page_off,
                                                     const int32_t* __restrict__ len, int n_heads, int cha,
@@ -107,27 +96,50 @@ __global__ void __launch_bounds__(1024) k_attn_prep(const int32_t* __restrict__ 
   }
 }
 
-// Merge all partials of KV head h: per query head g, M = max of the item
-// maxima, kept and dropped sums rescaled to M, acc rescaled and divided by
-// the kept sum.  A head without items has an empty kept set: out = 0,
+
+// First CSR page of the flat range of wave w out of W over P pages, and the
+// wave whose range holds page p.
+__device__ __forceinline__ int64_t flat_begin(int64_t w, int64_t W, int64_t P) { return w * P / W; }
+__device__ __forceinline__ int64_t flat_wave(int64_t p, int64_t W, int64_t P) { return ((p + 1) * W - 1) / P; }
+
+// Merge all partials of KV head h: per query head g, M = max of the partial
+// maxima, kept and dropped sums rescaled to M, O rescaled and divided by the
+// kept sum.  A head without partials has an empty kept set: out = 0,
 // dropped = 1, lse = -inf.  One block per KV head; fixed summation order.
+// Partials of head h: fp32 path, items item_off[h] .. item_off[h+1]-1; bf16
+// path, index w + h for every wave w whose range meets the head's pages.
 template <int D>
 __global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
   const AttnWs& w = a.w;
   const int h = blockIdx.x;
   const int G = a.group;
-  const int b = w.item_off[h], e = w.item_off[h + 1];
+  int b, e, add;
+  const int64_t P = a.page_off[a.n_heads];
+  if (a.waves) {
+    const int64_t p0 = a.page_off[h], p1 = a.page_off[h + 1];
+    b = 0, e = 0, add = h;
+    if (p1 > p0) {
+      b = (int)flat_wave(p0, a.waves, P);
+      e = (int)flat_wave(p1 - 1, a.waves, P) + 1;
+    }
+  } else {
+    b = w.item_off[h], e = w.item_off[h + 1], add = 0;
+  }
+  // waves with an empty range (fewer pages than waves) wrote no partial
+  auto has = [&](int it) { return !a.waves || flat_begin(it, a.waves, P) < flat_begin(it + 1, a.waves, P); };
   __shared__ float sM[GMAX], sLA[GMAX];
   const int grp = threadIdx.x >> 4, sub = threadIdx.x & 15;  // 16 groups of 16 lanes
   if (grp < G) {
     float M = -INFINITY;
-    for (int it = b + sub; it < e; it += 16) M = fmaxf(M, w.stats[((size_t)it * G + grp) * 3]);
+    for (int it = b + sub; it < e; it += 16)
+      if (has(it)) M = fmaxf(M, w.stats[((size_t)(it + add) * G + grp) * 3]);
 #pragma unroll
     for (int d = 8; d > 0; d >>= 1) M = fmaxf(M, __shfl_xor(M, d, 16));
     float la = 0.f, ld = 0.f;
     if (M != -INFINITY) {
       for (int it = b + sub; it < e; it += 16) {
-        const float* st = w.stats + ((size_t)it * G + grp) * 3;
+        if (!has(it)) continue;
+        const float* st = w.stats + ((size_t)(it + add) * G + grp) * 3;
         const float sc = exp2f(st[0] - M);
         la += st[1] * sc;
         ld += st[2] * sc;
@@ -160,14 +172,18 @@ __global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
       const float M = sM[g], la = sLA[g];
       float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
       if (M != -INFINITY) {
+        auto term = [&](int it) {
+          const size_t pi = (size_t)(it + add);
+          return has(it) ? w.acc[pi * G * D + i] * exp2f(w.stats[(pi * G + g) * 3] - M) : 0.f;
+        };
         int it = b;
         for (; it + 4 <= e; it += 4) {
-          s0 += w.acc[(size_t)it * G * D + i] * exp2f(w.stats[((size_t)it * G + g) * 3] - M);
-          s1 += w.acc[(size_t)(it + 1) * G * D + i] * exp2f(w.stats[((size_t)(it + 1) * G + g) * 3] - M);
-          s2 += w.acc[(size_t)(it + 2) * G * D + i] * exp2f(w.stats[((size_t)(it + 2) * G + g) * 3] - M);
-          s3 += w.acc[(size_t)(it + 3) * G * D + i] * exp2f(w.stats[((size_t)(it + 3) * G + g) * 3] - M);
+          s0 += term(it);
+          s1 += term(it + 1);
+          s2 += term(it + 2);
+          s3 += term(it + 3);
         }
-        for (; it < e; ++it) s0 += w.acc[(size_t)it * G * D + i] * exp2f(w.stats[((size_t)it * G + g) * 3] - M);
+        for (; it < e; ++it) s0 += term(it);
       }
       const float s = (s0 + s1) + (s2 + s3);
       a.out[(size_t)h * G * D + i] = la > 0.f ? s / la : 0.f;
@@ -175,116 +191,227 @@ __global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
   }
 }
 
-template <int D> struct VRow;
-template <> struct VRow<128> { typedef uint4 T; };
-template <> struct VRow<64> { typedef uint2 T; };
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n only
+constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// LDS operand reads as inline assembly (see the staging notes in the kernel);
+// their results may be used only after lds_wait_all, which ties every result
+// register to the wait so no use can be scheduled before it.
+__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+
+__device__ __forceinline__ short4_t lds_read_tr_b64(uint32_t addr) {
+  short4_t v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+
+template <int NK, int NV>
+__device__ __forceinline__ void lds_wait_all(u32x4 (&k)[NK], short4_t (&v)[NV]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int u = 0; u < NK; ++u) asm volatile("" : "+v"(k[u]));
+#pragma unroll
+  for (int n = 0; n < NV; ++n) asm volatile("" : "+v"(v[n]));
+}
+
+// 16-byte chunks of zeros: the source of V rows that take no part
+__device__ const uint32_t kZeroChunks[64 * 4] = {};
 
 // Threshold (log2 units) of the lazily updated running maximum: between two
 // rescalings every exp2(z - m) stays below 2^RESCALE_T, far inside fp32.
 constexpr float RESCALE_T = 10.f;
 
+// Page tiles in LDS, one K and one V tile per wave and buffer.  A tile is 16
+// rows of CH 16-byte chunks; chunk c of row k is stored at chunk position
+// c ^ swz(k) of its row.  The swizzles make every LDS access of the kernel
+// free of bank conflicts: the K operand reads (16 lanes = 16 keys, one chunk
+// each) and the transposing V reads (lanes of a half-wave touch 8 rows x 2
+// chunks).
+template <int D>
+struct Tile {
+  static constexpr int CH = D / 8;    // 16-byte chunks per row
+  static constexpr int LPP = CH / 4;  // 16-byte loads per lane per tile
+  static __device__ __forceinline__ int slot_k(int k, int c) { return k * CH + (c ^ (D == 128 ? k : (k >> 1))); }
+  static __device__ __forceinline__ int slot_v(int k, int c) {
+    return k * CH + (c ^ (D == 128 ? ((2 * k) & 15) : ((2 * (k >> 1)) & 7)));
+  }
+};
+
+__device__ __forceinline__ short4_t pack_hi(const float (&p)[4]) {
+  // upper halves of the fp32 bit patterns: bf16 truncations of p
+  const uint32_t w0 = __builtin_amdgcn_perm(__float_as_uint(p[1]), __float_as_uint(p[0]), 0x07060302u);
+  const uint32_t w1 = __builtin_amdgcn_perm(__float_as_uint(p[3]), __float_as_uint(p[2]), 0x07060302u);
+  return __builtin_bit_cast(short4_t, make_uint2(w0, w1));
+}
+
+__device__ __forceinline__ short4_t pack_rne(float a, float b, float c, float d) {
+  const bf16x2_t x = __builtin_convertvector((float2_t){a, b}, bf16x2_t);
+  const bf16x2_t y = __builtin_convertvector((float2_t){c, d}, bf16x2_t);
+  return __builtin_bit_cast(short4_t, make_uint2(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, y)));
+}
+
+__device__ __forceinline__ uint32_t pick4(u32x4 v, int q) {
+  return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+}
+
 // ---------------------------------------------------------------------------
-// bf16 K/V, MFMA logits.  MODE: A_PLAIN (every valid key kept), A_MASK (keep
-// plane; dropped keys only enter the dropped sum, their V is not read),
-// A_LOGITS (write base-2 logits of every valid key, (max, sum) partials).
+// bf16 K/V.  MODE: A_PLAIN (every valid key kept), A_MASK (keep plane;
+// dropped keys only enter the dropped sum and their V rows are not read),
+// A_LOGITS (base-2 logits of every valid key and (max, sum) partials).
 //
-// One wave per work item (head, up to a.cha consecutive pages); waves never
-// wait for each other.  S = K q^T on v_mfma_f32_16x16x32_bf16: lane (r, col)
-// feeds key `col`, dims 32u + 8r .. +7 of K and the same dims of query head
-// `col`, straight from 16-byte loads; it receives S[key 4r + j][head col].
-// Each 16-lane row r is an online-softmax stream over keys 4r..4r+3 of every
-// page; its running maximum is raised only when a logit exceeds it by more
-// than RESCALE_T (a wave-uniform branch), so the common page costs one FMA
-// and one exp2 per logit.  P V runs on the VALU in fp32.  K and V tiles of
-// page i + LA are in flight while page i is processed.
+// Wave w of W streams CSR pages [w P / W, (w + 1) P / W) and, per head
+// segment of that range, writes the partial with index w + head.  Each
+// page's K and V tiles are loaded with direct global->LDS loads (contiguous
+// 1 KB per instruction; two pages in flight) into the wave's swizzled LDS
+// tiles and read back as MFMA operands:
+//   S = K q^T     v_mfma_f32_16x16x32_bf16: key = lane % 16, 8 dims per lane;
+//                 lane (r, col) receives S[key 4r + j][query head col];
+//   O += P V      v_mfma_f32_16x16x16_bf16, A = P exactly as S is laid out
+//                 (row = query head, keys 4r..4r+3), B = V through the
+//                 transposing LDS read; P is split into a bf16 truncation and
+//                 a bf16 remainder (two MFMAs), so each weight carries a
+//                 relative error below 2^-16.
+// One running maximum per query head (shared by the four 16-lane rows) is
+// raised only when a logit exceeds it by more than RESCALE_T, a wave-uniform
+// branch; the common page costs one FMA and one exp2 per logit.
 // ---------------------------------------------------------------------------
-template <int D, int GM, int MODE>
+template <int D, int MODE>
 __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
-  constexpr int KU = D / 32;    // 16-byte K pieces per lane per page = MFMAs per page
-  constexpr int DS = D / 16;    // V dims per lane
+  typedef Tile<D> TL;
+  constexpr int CH = TL::CH, LPP = TL::LPP;
+  constexpr int KU = D / 32;    // QK MFMAs per page
+  constexpr int NV = D / 16;    // PV output column blocks
   constexpr bool LOGITS = MODE == A_LOGITS;
-  typedef typename VRow<D>::T VT;
+  // load instructions per page; pages in flight are tracked by vmcnt (the
+  // logits mode also stores inside the loop and keeps a single page in flight)
+  constexpr int PER_PAGE = LOGITS ? 0 : 2 * LPP;
+  __shared__ u32x4 lds_k[NT / WAVE][2][16 * CH];
+  __shared__ u32x4 lds_v[NT / WAVE][2][LOGITS ? 1 : 16 * CH];
+  __shared__ int32_t s_pg[LDS_HMAX + 1];
   const AttnWs& w = a.w;
-  const int lane = threadIdx.x & 63, r = lane >> 4, col = lane & 15;
-  const int item = blockIdx.x * (NT / WAVE) + (threadIdx.x >> 6);
-  const int total = w.item_off[a.n_heads];
-  const int4 rec = w.item[item];   // (head, first CSR page, valid entries, pages); padded past the end
-  if (item >= total) return;       // per-wave exit: no block barriers below
-  const int G = a.group;
-  const int h = rec.x, page0 = rec.y, nv = rec.z, cnt = rec.w;
-
-  // lane l: page id of page l; keep words: lane l of kw[b] covers page 16b + l/4, keys 4(l%4)..+3
-  const int pid_l = lane < cnt ? a.page_ids[page0 + lane] : 0;
-  uint32_t kw0 = 0xFFFFFFFFu, kw1 = 0xFFFFFFFFu;
-  if (MODE == A_MASK) {
-    const uint8_t* kb = a.keep + (int64_t)page0 * PAGE;
-    if (lane / 4 < cnt) kw0 = *reinterpret_cast<const uint32_t*>(kb + 4 * lane);
-    if (16 + lane / 4 < cnt) kw1 = *reinterpret_cast<const uint32_t*>(kb + 256 + 4 * lane);
+  const int lane = threadIdx.x & 63, r = lane >> 4, col = lane & 15, wv = threadIdx.x >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(wv);
+  const int H = a.n_heads, G = a.group;
+  const bool lpg = H <= LDS_HMAX;
+  if (lpg) {
+    for (int i = threadIdx.x; i <= H; i += NT) s_pg[i] = a.page_off[i];
+    __syncthreads();
   }
-  auto kword = [&](int i) -> uint32_t {
-    if (MODE != A_MASK) return 0xFFFFFFFFu;
-    const uint32_t src = (i < 16) ? kw0 : kw1;
-    return (uint32_t)__shfl((int)src, ((i & 15) << 2) + r, WAVE);
-  };
-
-  // B operand of MFMA u: dims 32u + 8r .. +7 of query head col (zero for col >= G)
-  uint4 qop[KU];
-  {
-    const uint8_t* qrow = (const uint8_t*)a.q + ((size_t)h * G + (col < G ? col : 0)) * D * 2 + 16 * r;
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      qop[u] = *reinterpret_cast<const uint4*>(qrow + 64 * u);
-      if (col >= G) qop[u] = make_uint4(0, 0, 0, 0);
+  const c_i32 cpo = (c_i32)a.page_off;
+  const c_i32 cids = (c_i32)a.page_ids;
+  const c_i32 clen = (c_i32)a.len;
+  // page offsets are wave-uniform; readfirstlane keeps everything derived from them in scalar registers
+  auto pg = [&](int hh) -> int { return __builtin_amdgcn_readfirstlane(lpg ? s_pg[hh] : cpo[hh]); };
+  auto head_of = [&](int p) -> int {   // head whose pages hold CSR page p
+    int lo = 0, hi = H + 1;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pg(mid) <= p) lo = mid; else hi = mid;
     }
-  }
+    return lo;
+  };
+  const int64_t P = pg(H);
+  const int W = a.waves;
+  const int wave = blockIdx.x * (NT / WAVE) + wu;
+  int p = (int)flat_begin(wave, W, P);
+  const int pend = (int)flat_begin(wave + 1, W, P);
+  if (p >= pend) return;   // per-wave exit: no block barriers below
 
-  float m = -INFINITY, la = 0.f, ld = 0.f;
-  float nm = INFINITY;   // -m, or +inf while m = -inf (every finite logit then forces an update)
-  float acc[GM][DS];
-  for_g<GM>([&](int g) {
-#pragma unroll
-    for (int d = 0; d < DS; ++d) acc[g][d] = 0.f;
-  });
   const uint8_t* kbase = (const uint8_t*)a.k;
   const uint8_t* vbase = (const uint8_t*)a.v;
-  const uint32_t koff = col * D * 2 + 16 * r;            // this lane's K bytes within a page
-  const uint32_t voff = (4 * r * D + col * DS) * 2;      // this lane's V bytes of key 4r
+  // per-lane byte offsets within a page of the chunks each load instruction
+  // fetches: LDS slot s of a tile receives the chunk the swizzle places there
+  uint32_t gk[LPP], gv[LPP];
+#pragma unroll
+  for (int u = 0; u < LPP; ++u) {
+    const int sl = 64 * u + lane, row = sl / CH;
+    gk[u] = row * (D * 2) + ((sl % CH) ^ (TL::slot_k(row, 0) - row * CH)) * 16;
+    gv[u] = row * (D * 2) + ((sl % CH) ^ (TL::slot_v(row, 0) - row * CH)) * 16;
+  }
+  // LDS byte offsets of this lane's operand chunks within a tile
+  const int vrow = 4 * r + (col >> 2), vhalf = col & 1, vc = (col & 3) >> 1;
+  uint32_t koff[KU], voff[LOGITS ? 1 : NV];
+#pragma unroll
+  for (int u = 0; u < KU; ++u) koff[u] = TL::slot_k(col, 4 * u + r) * 16;
+  if (!LOGITS) {
+#pragma unroll
+    for (int n = 0; n < NV; ++n) voff[n] = TL::slot_v(vrow, 2 * n + vc) * 16 + 8 * vhalf;
+  }
+  typedef __attribute__((address_space(1))) const void* gptr;
+  typedef __attribute__((address_space(3))) void* lptr;
 
-  // Every load is issued unconditionally so the compiler can count outstanding
-  // loads exactly and wait only for the page being processed: a V row that is
-  // not needed (dropped or past the end) is read from the start of the page's
-  // K tile instead, a line this wave has just requested.
-  auto load = [&](int i, uint32_t kwi, uint4 (&kd)[KU], VT (&vd)[4]) {
-    const int64_t phys = __builtin_amdgcn_readlane(pid_l, i);
-    const uint8_t* kpage = kbase + phys * (PAGE * D * 2);
-    const uint8_t* vpage = vbase + phys * (PAGE * D * 2);
+  int h = head_of(p);
+  while (true) {
+    // ---- one head segment: CSR pages [p, send) of head h ----
+    const int hb = pg(h);
+    const int send = min(pend, pg(h + 1));
+    const int page0 = p, cnt = send - p;
+    const int v0 = clen[h] - (p - hb) * PAGE;
+    const int nv = v0 < 0 ? 0 : (v0 > cnt * PAGE ? cnt * PAGE : v0);   // valid entries of the segment
+    const c_u32x4 ckeep = (c_u32x4)(a.keep + (int64_t)page0 * PAGE);   // 16 keep bytes per page
+
+    // B operand of QK MFMA u: dims 32u + 8r .. +7 of query head col (zero for col >= G)
+    u32x4 qop[KU];
+    {
+      const uint8_t* qrow = (const uint8_t*)a.q + ((size_t)h * G + (col < G ? col : 0)) * D * 2 + 16 * r;
 #pragma unroll
-    for (int u = 0; u < KU; ++u) kd[u] = *reinterpret_cast<const uint4*>(kpage + koff + 64 * u);
-    if (MODE == A_PLAIN) {
-      // every row of an allocated page is readable; rows past the end are
-      // zeroed before use
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vd[j] = *reinterpret_cast<const VT*>(vpage + voff + j * D * 2);
-    } else if (MODE == A_MASK) {
-      const int i0 = i * PAGE + 4 * r;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool need = i0 + j < nv && ((kwi >> (8 * j)) & 0xFFu);
-        const uint8_t* src = need ? vpage + voff + j * D * 2 : kpage + col * 16;
-        vd[j] = *reinterpret_cast<const VT*>(src);
+      for (int u = 0; u < KU; ++u) {
+        qop[u] = *reinterpret_cast<const u32x4*>(qrow + 64 * u);
+        if (col >= G) qop[u] = (u32x4){0u, 0u, 0u, 0u};
       }
     }
-  };
+    float m = -INFINITY, la = 0.f, ld = 0.f;
+    float nm = INFINITY;   // -m, or +inf while m = -inf (every finite logit then forces an update)
+    float4_t acc[LOGITS ? 1 : NV];
+#pragma unroll
+    for (int n = 0; n < (LOGITS ? 1 : NV); ++n) acc[n] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int i, uint32_t kwi, uint4 (&kc)[KU], VT (&vc)[4]) {
+    auto dma = [&](auto B, int i) {
+      constexpr int buf = decltype(B)::value;
+      const int64_t phys = cids[page0 + i];
+      const uint8_t* kpage = kbase + phys * (PAGE * D * 2);
+      const uint8_t* vpage = vbase + phys * (PAGE * D * 2);
+#pragma unroll
+      for (int u = 0; u < LPP; ++u)
+        __builtin_amdgcn_global_load_lds((gptr)(kpage + gk[u]), (lptr)(&lds_k[wu][buf][64 * u]), 16, 0, 0);
+      if (!LOGITS) {
+        const bool full = (i + 1) * PAGE <= nv;   // wave-uniform
+        if (MODE == A_PLAIN && full) {
+#pragma unroll
+          for (int u = 0; u < LPP; ++u)
+            __builtin_amdgcn_global_load_lds((gptr)(vpage + gv[u]), (lptr)(&lds_v[wu][buf][64 * u]), 16, 0, 0);
+        } else {
+          u32x4 kw4 = (u32x4){~0u, ~0u, ~0u, ~0u};
+          if (MODE == A_MASK) kw4 = ckeep[i];
+#pragma unroll
+          for (int u = 0; u < LPP; ++u) {
+            const int row = (64 * u + lane) / CH;
+            bool need = i * PAGE + row < nv;
+            if (MODE == A_MASK) need &= ((pick4(kw4, row >> 2) >> (8 * (row & 3))) & 0xFFu) != 0;
+            // rows that take no part read zeros
+            const uint8_t* src = need ? vpage + gv[u] : reinterpret_cast<const uint8_t*>(kZeroChunks) + 16 * lane;
+            __builtin_amdgcn_global_load_lds((gptr)src, (lptr)(&lds_v[wu][buf][64 * u]), 16, 0, 0);
+          }
+        }
+      }
+    };
+
+  auto math = [&](int i, const u32x4 (&kop)[KU], const short4_t (&vop)[LOGITS ? 1 : NV], uint32_t kwr) {
+    // ---- S = K q^T ----
     float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < KU; ++u)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kc[u]),
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[u]),
                                                   __builtin_bit_cast(bf16x8_t, qop[u]), s, 0, 0, 0);
-    const int i0 = i * PAGE + 4 * r;      // entry of key 4r within the item
+    const int i0 = i * PAGE + 4 * r;          // entry of key 4r within the item
     const bool full = (i + 1) * PAGE <= nv;   // wave-uniform
     float pj[4];
     bool slow = !full;
@@ -293,12 +420,15 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
       for (int j = 0; j < 4; ++j) pj[j] = fmaf(s[j], a.scale2, nm);
       slow = __any(fmaxf(fmaxf(pj[0], pj[1]), fmaxf(pj[2], pj[3])) > RESCALE_T);
     }
-    float alpha = 1.f;
     if (slow) {
       float z[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) z[j] = i0 + j < nv ? s[j] * a.scale2 : -INFINITY;
-      const float mn = fmaxf(m, fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+      float pm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      pm = fmaxf(pm, __shfl_xor(pm, 16, WAVE));
+      pm = fmaxf(pm, __shfl_xor(pm, 32, WAVE));   // maximum of the page for query head col
+      const float mn = fmaxf(m, pm);
+      float alpha = 1.f;
       if (mn != -INFINITY) {
         alpha = exp2f(m - mn);   // 0 while m = -inf
         m = mn;
@@ -308,9 +438,18 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
       for (int j = 0; j < 4; ++j) pj[j] = z[j] - m;
       la *= alpha;
       ld *= alpha;
+      if (!LOGITS) {
+        // output row g = 4r + j belongs to query head 4r + j: its factor lives in lane 4r + j
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float aj = __shfl(alpha, 4 * r + j, WAVE);
+#pragma unroll
+          for (int n = 0; n < NV; ++n) acc[n][j] *= aj;
+        }
+      }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pj[j] = __builtin_amdgcn_exp2f(pj[j]);   // exp2(-inf) = 0; NaN only while m = -inf
+    for (int j = 0; j < 4; ++j) pj[j] = __builtin_amdgcn_exp2f(pj[j]);   // exp2(-inf) = 0
     if (slow && m == -INFINITY) pj[0] = pj[1] = pj[2] = pj[3] = 0.f;
     if (LOGITS) {
       if (col < G) {
@@ -324,12 +463,14 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
             if (i0 + j < nv) dst[j] = s[j] * a.scale2;
         }
       }
+      la += (pj[0] + pj[1]) + (pj[2] + pj[3]);
+      return;
     }
     if (MODE == A_MASK) {
       float sk = 0.f, sd = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bool kept = ((kwi >> (8 * j)) & 0xFFu) && (full || i0 + j < nv);
+        const bool kept = ((kwr >> (8 * j)) & 0xFFu) && (full || i0 + j < nv);
         sk += kept ? pj[j] : 0.f;
         sd += kept ? 0.f : pj[j];
         if (!kept) pj[j] = 0.f;
@@ -339,95 +480,79 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
     } else {
       la += (pj[0] + pj[1]) + (pj[2] + pj[3]);
     }
-    if (!LOGITS) {
-      if (slow) {
-        for_g<GM>([&](int g) {
-          const float av = bcast_dyn(alpha, g);
+    // ---- O += P V (P = hi + lo, both bf16) ----
+    const short4_t phi = pack_hi(pj);
+    float rem[4];
 #pragma unroll
-          for (int d = 0; d < DS; ++d) acc[g][d] *= av;
-        });
-      }
-      // P V: lanes of row r own dims [col*DS, col*DS+DS) of keys 4r..4r+3
+    for (int j = 0; j < 4; ++j) rem[j] = pj[j] - __uint_as_float(__float_as_uint(pj[j]) & 0xFFFF0000u);
+    const short4_t plo = pack_rne(rem[0], rem[1], rem[2], rem[3]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool kept = MODE == A_PLAIN ? true : (((kwi >> (8 * j)) & 0xFFu) && (full || i0 + j < nv));
-        if (MODE == A_PLAIN || kept) {
-          VT vv = vc[j];
-          if (MODE == A_PLAIN && !full && i0 + j >= nv) vv = VT{};   // unwritten rows may hold non-finite bits
-          float vf[DS];
-          if constexpr (DS == 8) {
-            vf[0] = bf16lo(vv.x); vf[1] = bf16hi(vv.x); vf[2] = bf16lo(vv.y); vf[3] = bf16hi(vv.y);
-            vf[4] = bf16lo(vv.z); vf[5] = bf16hi(vv.z); vf[6] = bf16lo(vv.w); vf[7] = bf16hi(vv.w);
-          } else {
-            vf[0] = bf16lo(vv.x); vf[1] = bf16hi(vv.x); vf[2] = bf16lo(vv.y); vf[3] = bf16hi(vv.y);
-          }
-          for_g<GM>([&](int g) {
-            const float pk = bcast_dyn(pj[j], g);
-#pragma unroll
-            for (int d = 0; d < DS; ++d) acc[g][d] = fmaf(pk, vf[d], acc[g][d]);
-          });
-        }
-      }
+    for (int n = 0; n < NV; ++n) {
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vop[n], acc[n], 0, 0, 0);
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vop[n], acc[n], 0, 0, 0);
     }
   };
 
-  // ring of LA + 1 page buffers: page ii + LA is loaded while page ii is
-  // processed (indices past the item's last page reload that page)
-  constexpr int LA = GM <= 4 ? 2 : 1;
-  constexpr int NB = LA + 1;
-  uint4 kb[NB][KU];
-  VT vb[NB][4];
-  uint32_t kwb[NB];
-#pragma unroll
-  for (int u = 0; u < LA; ++u) {
-    const int pi = min(u, cnt - 1);
-    kwb[u] = kword(pi);
-    load(pi, kwb[u], kb[u], vb[u]);
-  }
-  for (int i = 0; i < cnt; i += NB) {
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int ii = i + u;
-      if (ii >= cnt) break;
-      const int nb = (u + LA) % NB;
-      const int pi = min(ii + LA, cnt - 1);
-      kwb[nb] = kword(pi);
-      load(pi, kwb[nb], kb[nb], vb[nb]);
-      compute(ii, kwb[u], kb[u], vb[u]);
-    }
-  }
 
-  // ---- combine the four row streams of the wave and write the partial ----
-  float M = fmaxf(m, __shfl_xor(m, 16, WAVE));
-  M = fmaxf(M, __shfl_xor(M, 32, WAVE));
-  const float sc = (M == -INFINITY) ? 0.f : exp2f(m - M);
-  float las = la * sc, lds = ld * sc;
-  las += __shfl_xor(las, 16, WAVE);
-  las += __shfl_xor(las, 32, WAVE);
-  lds += __shfl_xor(lds, 16, WAVE);
-  lds += __shfl_xor(lds, 32, WAVE);
-  if (r == 0 && col < G) {
-    float* st = w.stats + ((size_t)item * G + col) * 3;
-    st[0] = M;
-    st[1] = las;
-    st[2] = lds;
-  }
-  if (!LOGITS) {
-    for_g<GM>([&](int g) {
-      const float sg = bcast_dyn(sc, g);   // scale of this row's stream for query column g
+    // Page i + 1 is in flight while page i is read and computed; page i + 2
+    // is requested as soon as page i's operands are in registers.  The
+    // operand reads are inline assembly with explicit waits: the compiler
+    // would otherwise wait for every outstanding page before any LDS read.
+    auto step = [&](auto B, int i) {
+      constexpr int buf = decltype(B)::value;
+      uint32_t kwr = ~0u;
+      if (MODE == A_MASK) kwr = pick4(ckeep[i], r);   // keep word of keys 4r..4r+3
+      asm volatile("" ::: "memory");
+      if (PER_PAGE && i + 1 < cnt) __builtin_amdgcn_s_waitcnt(wait_vm(PER_PAGE));
+      else __builtin_amdgcn_s_waitcnt(wait_vm(0));
+      const uint32_t kl = lds_addr(&lds_k[wu][buf][0]), vl = lds_addr(&lds_v[wu][buf][0]);
+      u32x4 kop[KU];
+      short4_t vop[LOGITS ? 1 : NV];
 #pragma unroll
-      for (int d = 0; d < DS; ++d) {
-        float x = acc[g][d] * sg;
-        x += __shfl_xor(x, 16, WAVE);
-        x += __shfl_xor(x, 32, WAVE);
-        acc[g][d] = x;
-      }
-      if (r == 0 && g < G) {
-        float* dst = w.acc + ((size_t)item * G + g) * D + col * DS;
+      for (int u = 0; u < KU; ++u) kop[u] = lds_read_b128(kl + koff[u]);
+      if (!LOGITS) {
 #pragma unroll
-        for (int d = 0; d < DS; ++d) dst[d] = acc[g][d];
+        for (int n = 0; n < NV; ++n) vop[n] = lds_read_tr_b64(vl + voff[n]);
       }
-    });
+      lds_wait_all(kop, vop);   // the tile may be overwritten once these reads are done
+      if (i + 2 < cnt) dma(B, i + 2);
+      asm volatile("" ::: "memory");
+      math(i, kop, vop, kwr);
+    };
+    dma(std::integral_constant<int, 0>{}, 0);
+    if (cnt > 1) dma(std::integral_constant<int, 1>{}, 1);
+    for (int i = 0; i < cnt; i += 2) {
+      step(std::integral_constant<int, 0>{}, i);
+      if (i + 1 < cnt) step(std::integral_constant<int, 1>{}, i + 1);
+    }
+
+    // ---- partial of this segment: the maximum is common to the four rows ----
+    const size_t part = (size_t)wave + h;
+    la += __shfl_xor(la, 16, WAVE);
+    la += __shfl_xor(la, 32, WAVE);
+    ld += __shfl_xor(ld, 16, WAVE);
+    ld += __shfl_xor(ld, 32, WAVE);
+    if (r == 0 && col < G) {
+      float* st = w.stats + (part * G + col) * 3;
+      st[0] = m;
+      st[1] = la;
+      st[2] = ld;
+    }
+    if (!LOGITS) {
+      // lane (r, col) holds O[query head 4r + j][dim 16n + col]
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int g = 4 * r + j;
+        if (g < G) {
+          float* dst = w.acc + (part * G + g) * D + col;
+#pragma unroll
+          for (int n = 0; n < NV; ++n) dst[16 * n] = acc[n][j];
+        }
+      }
+    }
+    p = send;
+    if (p >= pend) break;
+    h = head_of(p);
   }
 }
 
@@ -515,6 +640,7 @@ __global__ void __launch_bounds__(NT) k_attn_f32(AttnArgs a) {
   }
 }
 
+
 // mass[j] = (1/G) sum_g 2^(z2_gj - lse2_g); NaN in padding slots.
 // 64 CSR pages per block, 4 slots per thread.
 __global__ void __launch_bounds__(256) k_mass(const int32_t* __restrict__ page_off, const int32_t* __restrict__ len,
@@ -551,6 +677,7 @@ __global__ void __launch_bounds__(256) k_mass(const int32_t* __restrict__ page_o
   *reinterpret_cast<float4*>(mass + slot) = make_float4(o[0], o[1], o[2], o[3]);
 }
 
+
 AttnWs carve(const trimkv_cache_t* c, int group, void* ws, bool mass) {
   WsLayout L = mass ? mass_ws_layout(c, group) : attn_ws_layout(c, group);
   char* b = (char*)ws;
@@ -564,61 +691,69 @@ AttnWs carve(const trimkv_cache_t* c, int group, void* ws, bool mass) {
   return w;
 }
 
-int gm_for(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : g <= 8 ? 8 : 16; }
+// Waves that the device holds at once for a kernel of NT threads per block
+// (cached per kernel and device).
+template <typename K>
+int resident_waves(K kernel) {
+  struct Entry { const void* k; int dev; int waves; };
+  static thread_local Entry cache[16];
+  static thread_local int used = 0;
+  int dev = 0;
+  hipGetDevice(&dev);
+  for (int i = 0; i < used; ++i)
+    if (cache[i].k == (const void*)kernel && cache[i].dev == dev) return cache[i].waves;
+  int cus = 0, blocks = 0;
+  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, NT, 0) != hipSuccess) blocks = 1;
+  const int wv = std::min(FLAT_WMAX, std::max(1, blocks) * std::max(1, cus) * (NT / WAVE));
+  if (used < 16) cache[used++] = Entry{(const void*)kernel, dev, wv};
+  return wv;
+}
 
 template <int MODE>
 int launch_main(const trimkv_cache_t* c, AttnArgs& a, hipStream_t st) {
   constexpr bool LOGITS = MODE == A_LOGITS;
-  const int64_t W = max_chunks(c, a.cha);   // bound on the number of items
   const dim3 blk(NT);
   if (c->dtype == TRIMKV_F32) {
-    const dim3 grid((unsigned)W);   // one item per block
-    if (c->head_dim == 128) hipLaunchKernelGGL((k_attn_f32<128, LOGITS>), grid, blk, 0, st, a);
-    else hipLaunchKernelGGL((k_attn_f32<64, LOGITS>), grid, blk, 0, st, a);
+    const int64_t T = max_chunks(c, CHA_F32);   // bound on the number of items
+    if (c->head_dim == 128) hipLaunchKernelGGL((k_attn_f32<128, LOGITS>), dim3((unsigned)T), blk, 0, st, a);
+    else hipLaunchKernelGGL((k_attn_f32<64, LOGITS>), dim3((unsigned)T), blk, 0, st, a);
     return TRIMKV_OK;
   }
-  const dim3 grid((unsigned)((W + NT / WAVE - 1) / (NT / WAVE)));   // one item per wave
-  const int gm = gm_for(a.group);
-#define TRIMKV_BF16(DD, GG) hipLaunchKernelGGL((k_attn_bf16<DD, GG, MODE>), grid, blk, 0, st, a)
-  if (c->head_dim == 128) {
-    switch (gm) {
-      case 1: TRIMKV_BF16(128, 1); break;
-      case 2: TRIMKV_BF16(128, 2); break;
-      case 4: TRIMKV_BF16(128, 4); break;
-      case 8: TRIMKV_BF16(128, 8); break;
-      default: TRIMKV_BF16(128, 16); break;
-    }
-  } else {
-    switch (gm) {
-      case 1: TRIMKV_BF16(64, 1); break;
-      case 2: TRIMKV_BF16(64, 2); break;
-      case 4: TRIMKV_BF16(64, 4); break;
-      case 8: TRIMKV_BF16(64, 8); break;
-      default: TRIMKV_BF16(64, 16); break;
-    }
-  }
-#undef TRIMKV_BF16
+  auto go = [&](auto kernel) {
+    a.waves = resident_waves(kernel);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(a.waves / (NT / WAVE))), blk, 0, st, a);
+  };
+  if (c->head_dim == 128) go(k_attn_bf16<128, MODE>);
+  else go(k_attn_bf16<64, MODE>);
   return TRIMKV_OK;
+}
+
+// Partial slots: fp32 work items, or flat waves + heads.
+int64_t partial_slots(const trimkv_cache_t* c) {
+  return c->dtype == TRIMKV_F32 ? max_chunks(c, CHA_F32) : (int64_t)FLAT_WMAX + c->n_heads;
 }
 
 }  // namespace
 
 WsLayout attn_ws_layout(const trimkv_cache_t* c, int group) {
-  const int64_t W = max_chunks(c, CHA_MIN);
+  const int64_t S = partial_slots(c);
+  const int64_t T = c->dtype == TRIMKV_F32 ? max_chunks(c, CHA_F32) : 0;
   WsLayout L;
   L.add(((int64_t)c->n_heads + 1) * 4);
-  L.add((W + 4) * 16);
-  L.add(W * group * 3 * 4);
-  L.add(W * group * (int64_t)c->head_dim * 4);
+  L.add((T + 4) * 16);
+  L.add(S * group * 3 * 4);
+  L.add(S * group * (int64_t)c->head_dim * 4);
   return L;
 }
 
 WsLayout mass_ws_layout(const trimkv_cache_t* c, int group) {
-  const int64_t W = max_chunks(c, CHA_MIN);
+  const int64_t S = partial_slots(c);
+  const int64_t T = c->dtype == TRIMKV_F32 ? max_chunks(c, CHA_F32) : 0;
   WsLayout L;
   L.add(((int64_t)c->n_heads + 1) * 4);
-  L.add((W + 4) * 16);
-  L.add(W * group * 3 * 4);
+  L.add((T + 4) * 16);
+  L.add(S * group * 3 * 4);
   L.add(0);
   L.add((int64_t)c->n_heads * group * 4);
   L.add((int64_t)group * c->n_pages * PAGE * 4);
@@ -629,12 +764,12 @@ int launch_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float
                        int group, float scale, float* out, float* dropped, float* lse_out, void* ws,
                        hipStream_t st) {
   AttnWs w = carve(c, group, ws, false);
-  // items of 32 pages when every key is read (mask mode), 16 otherwise
-  const int cha = c->dtype == TRIMKV_F32 ? CHA_F32 : (keep ? 32 : 16);
-  hipLaunchKernelGGL(k_attn_prep, dim3(prep_grid(c->n_heads, max_chunks(c, cha), 2048)), dim3(1024), 0, st,
-                     c->page_off, c->len, c->n_heads, cha, w);
+  const bool f32 = c->dtype == TRIMKV_F32;
+  if (f32)
+    hipLaunchKernelGGL(k_attn_prep, dim3(prep_grid(c->n_heads, max_chunks(c, CHA_F32), 2048)), dim3(1024), 0, st,
+                       c->page_off, c->len, c->n_heads, CHA_F32, w);
   AttnArgs a{c->page_off, c->page_ids, c->len, c->k, c->v, keep, q, c->n_heads, group, scale * LOG2E,
-             c->n_pages * PAGE, cha, w, lse_ref, out, dropped, lse_out};
+             c->n_pages * PAGE, CHA_F32, 0, w, lse_ref, out, dropped, lse_out};
   prof_begin(st);
   int rc = keep ? launch_main<A_MASK>(c, a, st) : launch_main<A_PLAIN>(c, a, st);
   prof_end(st);
@@ -647,11 +782,12 @@ int launch_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float
 int launch_attn_mass(const trimkv_cache_t* c, const void* q, int group, float scale, float* mass,
                      float* lse_full, void* ws, hipStream_t st) {
   AttnWs w = carve(c, group, ws, true);
-  const int cha = c->dtype == TRIMKV_F32 ? CHA_F32 : 32;
-  hipLaunchKernelGGL(k_attn_prep, dim3(prep_grid(c->n_heads, max_chunks(c, cha), 2048)), dim3(1024), 0, st,
-                     c->page_off, c->len, c->n_heads, cha, w);
+  const bool f32 = c->dtype == TRIMKV_F32;
+  if (f32)
+    hipLaunchKernelGGL(k_attn_prep, dim3(prep_grid(c->n_heads, max_chunks(c, CHA_F32), 2048)), dim3(1024), 0, st,
+                       c->page_off, c->len, c->n_heads, CHA_F32, w);
   AttnArgs a{c->page_off, c->page_ids, c->len, c->k, c->v, nullptr, q, c->n_heads, group, scale * LOG2E,
-             c->n_pages * PAGE, cha, w, nullptr, nullptr, nullptr, lse_full};
+             c->n_pages * PAGE, CHA_F32, 0, w, nullptr, nullptr, nullptr, lse_full};
   prof_begin(st);
   int rc = launch_main<A_LOGITS>(c, a, st);
   prof_end(st);

@@ -84,10 +84,18 @@ def test_workspace_checks():
     need = L.trimkv_workspace_size(tk.OP_DECODE_ATTN, ctypes.byref(c), 0, 4)
     assert L.trimkv_decode_attn(ctypes.byref(c), None, None, X, 4, ctypes.c_float(1.0), X, X, None, X, need - 1,
                                 None) == tk.EWORKSPACE
-    # workspace grows with the pool and the group
+    # bf16 decode workspace: partials of a bounded number of waves (+ heads), growing with heads and group;
+    # fp32 work lists and the mass logits grow with the pool
     big = fake_cache(n_pages=1 << 16)
-    assert L.trimkv_workspace_size(tk.OP_DECODE_ATTN, ctypes.byref(big), 0, 4) > need
+    assert L.trimkv_workspace_size(tk.OP_DECODE_ATTN, ctypes.byref(big), 0, 4) == need
+    assert L.trimkv_workspace_size(tk.OP_DECODE_ATTN, ctypes.byref(fake_cache(n_heads=512)), 0, 4) > need
     assert L.trimkv_workspace_size(tk.OP_DECODE_ATTN, ctypes.byref(c), 0, 8) > need
+    f32 = fake_cache(dtype=tk.F32, head_dim=64)
+    f32big = fake_cache(dtype=tk.F32, head_dim=64, n_pages=1 << 16)
+    assert L.trimkv_workspace_size(tk.OP_DECODE_ATTN, ctypes.byref(f32big), 0, 4) > \
+        L.trimkv_workspace_size(tk.OP_DECODE_ATTN, ctypes.byref(f32), 0, 4)
+    assert L.trimkv_workspace_size(tk.OP_ATTN_MASS, ctypes.byref(big), 0, 4) > \
+        L.trimkv_workspace_size(tk.OP_ATTN_MASS, ctypes.byref(c), 0, 4)
     assert L.trimkv_workspace_size(99, ctypes.byref(c), 0, 0) == 0
 
 
