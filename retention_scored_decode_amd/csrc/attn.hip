@@ -374,9 +374,9 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int n = 0; n < (LOGITS ? 1 : NV); ++n) acc[n] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-    auto dma = [&](auto B, int i) {
+    // page i's loads; phys = its physical page, kw4 = its 16 keep bytes (mask mode)
+    auto dma = [&](auto B, int i, int64_t phys, u32x4 kw4) {
       constexpr int buf = decltype(B)::value;
-      const int64_t phys = cids[page0 + i];
       const uint8_t* kpage = kbase + phys * (PAGE * D * 2);
       const uint8_t* vpage = vbase + phys * (PAGE * D * 2);
 #pragma unroll
@@ -389,8 +389,6 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
           for (int u = 0; u < LPP; ++u)
             __builtin_amdgcn_global_load_lds((gptr)(vpage + gv[u]), (lptr)(&lds_v[wu][buf][64 * u]), 16, 0, 0);
         } else {
-          u32x4 kw4 = (u32x4){~0u, ~0u, ~0u, ~0u};
-          if (MODE == A_MASK) kw4 = ckeep[i];
 #pragma unroll
           for (int u = 0; u < LPP; ++u) {
             const int row = (64 * u + lane) / CH;
@@ -498,10 +496,17 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
     // is requested as soon as page i's operands are in registers.  The
     // operand reads are inline assembly with explicit waits: the compiler
     // would otherwise wait for every outstanding page before any LDS read.
+    // The page id and keep bytes that a step needs are read one step earlier
+    // (scalar loads), so no load is issued behind a dependent table read.
+    const u32x4 all_kept = (u32x4){~0u, ~0u, ~0u, ~0u};
+    auto keep4 = [&](int i) -> u32x4 { return MODE == A_MASK ? ckeep[i] : all_kept; };
+    int64_t id_n = cnt > 2 ? cids[page0 + 2] : 0;        // page of the next load (i + 2)
+    u32x4 kwd_n = cnt > 2 ? keep4(2) : all_kept;         // its keep bytes
+    u32x4 kwm_n = keep4(0);                              // keep bytes of the next page computed
     auto step = [&](auto B, int i) {
       constexpr int buf = decltype(B)::value;
-      uint32_t kwr = ~0u;
-      if (MODE == A_MASK) kwr = pick4(ckeep[i], r);   // keep word of keys 4r..4r+3
+      const u32x4 kwm = kwm_n;
+      const uint32_t kwr = pick4(kwm, r);   // keep word of keys 4r..4r+3 (mask mode)
       asm volatile("" ::: "memory");
       if (PER_PAGE && i + 1 < cnt) __builtin_amdgcn_s_waitcnt(wait_vm(PER_PAGE));
       else __builtin_amdgcn_s_waitcnt(wait_vm(0));
@@ -515,12 +520,17 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
         for (int n = 0; n < NV; ++n) vop[n] = lds_read_tr_b64(vl + voff[n]);
       }
       lds_wait_all(kop, vop);   // the tile may be overwritten once these reads are done
-      if (i + 2 < cnt) dma(B, i + 2);
+      if (i + 2 < cnt) dma(B, i + 2, id_n, kwd_n);
+      if (i + 3 < cnt) {
+        id_n = cids[page0 + i + 3];
+        kwd_n = keep4(i + 3);
+      }
+      if (i + 1 < cnt) kwm_n = keep4(i + 1);
       asm volatile("" ::: "memory");
       math(i, kop, vop, kwr);
     };
-    dma(std::integral_constant<int, 0>{}, 0);
-    if (cnt > 1) dma(std::integral_constant<int, 1>{}, 1);
+    dma(std::integral_constant<int, 0>{}, 0, cids[page0], keep4(0));
+    if (cnt > 1) dma(std::integral_constant<int, 1>{}, 1, cids[page0 + 1], keep4(1));
     for (int i = 0; i < cnt; i += 2) {
       step(std::integral_constant<int, 0>{}, i);
       if (i + 1 < cnt) step(std::integral_constant<int, 1>{}, i + 1);
