@@ -172,14 +172,20 @@ __device__ __forceinline__ void hist_add(uint32_t* lh, uint32_t key, uint32_t pr
 template <int PASS>
 __global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __restrict__ score, SelWs w) {
   constexpr int NB = PASS == 2 ? 1024 : 2048;
-  __shared__ uint32_t lh[NB];
+  // Pass 0 counts every key, and retention scores fall into few bins: each
+  // 16-lane row of a wave adds into its own copy of the histogram (copies
+  // offset by one bank), so at most 16 lanes contend for one LDS word.
+  constexpr int COPIES = PASS == 0 ? 4 : 1;
+  constexpr int CSTRIDE = NB + 1;
+  __shared__ uint32_t lh[COPIES * CSTRIDE];
+  uint32_t* lhc = lh + (COPIES > 1 ? ((threadIdx.x & (WAVE - 1)) >> 4) * CSTRIDE : 0);
   __shared__ int4 sm[CPB];
   const int T = w.chunk_off[n_heads];
   const int c0 = blockIdx.x * CPB;
   if (c0 >= T) return;
   const int nc = min(CPB, T - c0);
   if (threadIdx.x < nc) sm[threadIdx.x] = w.meta[c0 + threadIdx.x];
-  for (int b = threadIdx.x; b < NB; b += NT) lh[b] = 0u;
+  for (int b = threadIdx.x; b < COPIES * CSTRIDE; b += NT) lh[b] = 0u;
   __syncthreads();
   float4 kv[CPB];
   const int i0 = threadIdx.x * 4;
@@ -210,17 +216,19 @@ __global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __res
           const float a[4] = {kv[k].x, kv[k].y, kv[k].z, kv[k].w};
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (i0 + j < nv) hist_add<PASS>(lh, score_key(a[j]), pre);
+            if (i0 + j < nv) hist_add<PASS>(lhc, score_key(a[j]), pre);
         }
       }
       __syncthreads();
       uint32_t* g = pass_hist(w, s, PASS);
       for (int b = threadIdx.x; b < NB; b += NT) {
-        const uint32_t v = lh[b];
-        if (v) {
-          atomicAdd(g + b, v);
-          lh[b] = 0u;
+        uint32_t v = 0;
+#pragma unroll
+        for (int cp = 0; cp < COPIES; ++cp) {
+          v += lh[cp * CSTRIDE + b];
+          lh[cp * CSTRIDE + b] = 0u;
         }
+        if (v) atomicAdd(g + b, v);
       }
       __syncthreads();
     }
@@ -242,8 +250,15 @@ __device__ __forceinline__ double block_sum_f64(double v, double* tmpd) {
 }
 
 // ---------------------------------------------------------------------------
-// decide: chunks in ticket order; ties of earlier chunks of the segment by a
-// decoupled look-back; keep flags; kept[head] by atomics.
+// decide: block b handles chunk positions b*CPB .. b*CPB + CPB - 1.  The state
+// after the last radix pass is computed once per segment run of the block.
+// In the common case every key equal to K* is kept and chunks are
+// independent.  When the ties straddle the budget (more keys equal K* than
+// `need`), the chunks of that segment are processed in the order of a
+// per-segment ticket, one at a time, with a decoupled look-back for the ties
+// of earlier chunks; a ticket is taken only when its chunk is processed, so
+// every chunk a block waits for belongs to a block that is already running.
+// keep flags; kept[head] by atomics; optional per-chunk kept-score sums.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __restrict__ score, SelWs w,
                                                    uint8_t* __restrict__ keep, int32_t* __restrict__ kept,
@@ -252,113 +267,137 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
   __shared__ double tmpd[NT / WAVE];
   __shared__ int sh_c;
   __shared__ int64_t sh_excl;
-  int c = blockIdx.x;
+  __shared__ int4 sm[CPB];
   const int T = w.chunk_off[n_heads];
-  if (c >= T) return;
-  int4 m = w.meta[c];
-  const int cb = w.seg[m.y].chunk_begin;
-  const SegState st = state_after(w, m.y, 2, c == cb);
-  // Ranks among the ties are needed only when the ties straddle the budget
-  // (more keys equal K* than `need`); otherwise every tie is kept and chunks
-  // are independent.  In the straddling case the segment's blocks take
-  // chunks in the order of a per-segment ticket, so every chunk a block waits
-  // for belongs to a block that is already running.
-  const bool ranked = st.mode == MODE_NORMAL && st.ties > st.remaining;
-  if (ranked) {
-    if (threadIdx.x == 0) sh_c = cb + (int)atomicAdd(w.ticket + 2 + m.y, 1u);
-    __syncthreads();
-    c = sh_c;
-    m = w.meta[c];
-  }
-  const int nv = m.w & 0xFFFF;
-  const int nslots = (m.w >> 16) * PAGE;   // slots of the chunk's pages
-  const int64_t csr0 = (int64_t)m.z * PAGE;
+  const int c0 = blockIdx.x * CPB;
+  if (c0 >= T) return;
+  const int nc = min(CPB, T - c0);
+  if (threadIdx.x < nc) sm[threadIdx.x] = w.meta[c0 + threadIdx.x];
+  __syncthreads();
   const int i0 = threadIdx.x * 4;
-  float a[4] = {0.f, 0.f, 0.f, 0.f};
-  if (i0 < nv) {
-    const float4 sv = *reinterpret_cast<const float4*>(score + csr0 + i0);
-    a[0] = sv.x; a[1] = sv.y; a[2] = sv.z; a[3] = sv.w;
-  }
-  uint32_t gtm = 0, eqm = 0;
-  if (st.mode == MODE_NORMAL) {
+  // keys of the block's own chunk positions, all loads in flight at once
+  float4 kv[CPB];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (i0 + k < nv) {
-        const uint32_t key = score_key(a[k]);
-        gtm |= (uint32_t)(key > st.prefix) << k;
-        eqm |= (uint32_t)(key == st.prefix) << k;
-      }
+  for (int k = 0; k < CPB; ++k)
+    if (k < nc && i0 < (sm[k].w & 0xFFFF))
+      kv[k] = *reinterpret_cast<const float4*>(score + (int64_t)sm[k].z * PAGE + i0);
+  int run_seg = -1;
+  SegState st;
+#pragma unroll
+  for (int k = 0; k < CPB; ++k) {
+    if (k >= nc) break;
+    int4 m = sm[k];
+    if (m.y != run_seg) {   // block-uniform
+      run_seg = m.y;
+      const int first_blk = w.seg[m.y].chunk_begin / CPB;
+      st = state_after(w, m.y, 2, (int)blockIdx.x == first_blk);
     }
-  } else if (st.mode == MODE_ALL) {
+    const int cb = st.chunk_begin;
+    const bool ranked = st.mode == MODE_NORMAL && st.ties > st.remaining;
+    int c = c0 + k;
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    if (ranked) {
+      // process the segment's chunk of the next ticket instead of position c
+      if (threadIdx.x == 0) sh_c = cb + (int)atomicAdd(w.ticket + 2 + m.y, 1u);
+      __syncthreads();
+      c = sh_c;
+      m = w.meta[c];
+      if (i0 < (m.w & 0xFFFF)) {
+        const float4 sv = *reinterpret_cast<const float4*>(score + (int64_t)m.z * PAGE + i0);
+        a[0] = sv.x; a[1] = sv.y; a[2] = sv.z; a[3] = sv.w;
+      }
+    } else if (i0 < (m.w & 0xFFFF)) {
+      a[0] = kv[k].x; a[1] = kv[k].y; a[2] = kv[k].z; a[3] = kv[k].w;
+    }
+    const int nv = m.w & 0xFFFF;
+    const int nslots = (m.w >> 16) * PAGE;   // slots of the chunk's pages
+    const int64_t csr0 = (int64_t)m.z * PAGE;
+    uint32_t gtm = 0, eqm = 0;
+    if (st.mode == MODE_NORMAL) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) gtm |= (uint32_t)(i0 + k < nv) << k;
-  }
-  int64_t eq_total;
-  int64_t rank = block_exclusive_scan<NT>((int64_t)__popc(eqm), tmp, &eq_total);
-  if (ranked) {
-    if (threadIdx.x < WAVE) {
-      const int lane = threadIdx.x;
-      int64_t excl = 0;
-      if (c != cb) {
-        if (lane == 0)
-          __hip_atomic_store(w.look + c, LB_AGG | (uint64_t)eq_total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        int base = c - 1;   // window: chunks base, base-1, ..., base-63
-        uint32_t spins = 0;
-        while (true) {
-          const int j = base - lane;
-          // before the segment's first chunk: a zero prefix
-          const uint64_t v = j >= cb ? __hip_atomic_load(w.look + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                     : LB_PREFIX;
-          const uint64_t zm = __ballot(v == 0ull);
-          const uint64_t pm = __ballot((v & ~LB_VAL) == LB_PREFIX);
-          const int first = pm ? __ffsll((long long)pm) - 1 : WAVE;   // nearest prefix in the window
-          const uint64_t need = first == WAVE ? ~0ull : ((2ull << first) - 1ull);
-          if (zm & need) {  // a predecessor has not published yet
-            if (++spins > SPIN_LIMIT) {  // never expected; keeps every wave finite
-              if (lane == 0) atomicOr(w.error, 1u);
-              break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-            continue;
-          }
-          int64_t val = (lane <= first) ? (int64_t)(v & LB_VAL) : 0;
-          for (int d = WAVE / 2; d > 0; d >>= 1) val += __shfl_xor(val, d, WAVE);
-          excl += val;
-          if (pm) break;
-          base -= WAVE;
+      for (int j = 0; j < 4; ++j) {
+        if (i0 + j < nv) {
+          const uint32_t key = score_key(a[j]);
+          gtm |= (uint32_t)(key > st.prefix) << j;
+          eqm |= (uint32_t)(key == st.prefix) << j;
         }
       }
-      if (lane == 0) {
-        __hip_atomic_store(w.look + c, LB_PREFIX | (uint64_t)(excl + eq_total), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        sh_excl = excl;
+    } else if (st.mode == MODE_ALL) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) gtm |= (uint32_t)(i0 + j < nv) << j;
+    }
+    int64_t rank = 0;
+    if (ranked) {
+      int64_t eq_total;
+      rank = block_exclusive_scan<NT>((int64_t)__popc(eqm), tmp, &eq_total);
+      if (threadIdx.x < WAVE) {
+        const int lane = threadIdx.x;
+        int64_t excl = 0;
+        if (c != cb) {
+          if (lane == 0)
+            __hip_atomic_store(w.look + c, LB_AGG | (uint64_t)eq_total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          int base = c - 1;   // window: chunks base, base-1, ..., base-63
+          uint32_t spins = 0;
+          while (true) {
+            const int j = base - lane;
+            // before the segment's first chunk: a zero prefix
+            const uint64_t v = j >= cb ? __hip_atomic_load(w.look + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                       : LB_PREFIX;
+            const uint64_t zm = __ballot(v == 0ull);
+            const uint64_t pm = __ballot((v & ~LB_VAL) == LB_PREFIX);
+            const int first = pm ? __ffsll((long long)pm) - 1 : WAVE;   // nearest prefix in the window
+            const uint64_t need = first == WAVE ? ~0ull : ((2ull << first) - 1ull);
+            if (zm & need) {  // a predecessor has not published yet
+              if (++spins > SPIN_LIMIT) {  // never expected; keeps every wave finite
+                if (lane == 0) atomicOr(w.error, 1u);
+                break;
+              }
+              __builtin_amdgcn_s_sleep(1);
+              continue;
+            }
+            int64_t val = (lane <= first) ? (int64_t)(v & LB_VAL) : 0;
+            for (int d = WAVE / 2; d > 0; d >>= 1) val += __shfl_xor(val, d, WAVE);
+            excl += val;
+            if (pm) break;
+            base -= WAVE;
+          }
+        }
+        if (lane == 0) {
+          __hip_atomic_store(w.look + c, LB_PREFIX | (uint64_t)(excl + eq_total), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+          sh_excl = excl;
+        }
       }
+      __syncthreads();
+      rank += sh_excl;
     }
-    __syncthreads();
-    rank += sh_excl;
-  }
-  uint32_t km = gtm;
+    uint32_t km = gtm;
+    if (ranked) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    if (eqm & (1u << k)) {
-      if (rank < st.remaining) km |= 1u << k;
-      ++rank;
+      for (int j = 0; j < 4; ++j) {
+        if (eqm & (1u << j)) {
+          if (rank < st.remaining) km |= 1u << j;
+          ++rank;
+        }
+      }
+    } else {
+      km |= eqm;   // every tie is kept
     }
-  }
-  if (i0 < nslots) {
-    const uint32_t word = (km & 1u) | ((km & 2u) << 7) | ((km & 4u) << 14) | ((km & 8u) << 21);
-    *reinterpret_cast<uint32_t*>(keep + csr0 + i0) = word;
-  }
-  int64_t kcount;
-  block_exclusive_scan<NT>((int64_t)__popc(km), tmp, &kcount);
-  if (threadIdx.x == 0 && kcount) atomicAdd(kept + m.x, (int32_t)kcount);
-  if (want_sum) {
-    double sum = 0.0;
+    if (i0 < nslots) {
+      const uint32_t word = (km & 1u) | ((km & 2u) << 7) | ((km & 4u) << 14) | ((km & 8u) << 21);
+      *reinterpret_cast<uint32_t*>(keep + csr0 + i0) = word;
+    }
+    int64_t kcount;
+    block_exclusive_scan<NT>((int64_t)__popc(km), tmp, &kcount);
+    if (threadIdx.x == 0 && kcount) atomicAdd(kept + m.x, (int32_t)kcount);
+    if (want_sum) {
+      double sum = 0.0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (km & (1u << k)) sum += (double)a[k];
-    const double bs = block_sum_f64(sum, tmpd);
-    if (threadIdx.x == 0) w.part[c] = bs;
+      for (int j = 0; j < 4; ++j)
+        if (km & (1u << j)) sum += (double)a[j];
+      const double bs = block_sum_f64(sum, tmpd);
+      if (threadIdx.x == 0) w.part[c] = bs;
+    }
   }
 }
 
@@ -415,7 +454,7 @@ int launch_select(const trimkv_cache_t* c, const float* score, int n_seg, const 
   hipLaunchKernelGGL(k_sel_hist<0>, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w);
   hipLaunchKernelGGL(k_sel_hist<1>, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w);
   hipLaunchKernelGGL(k_sel_hist<2>, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w);
-  hipLaunchKernelGGL(k_sel_decide, dim3((unsigned)T), dim3(NT), 0, st, c->n_heads, score, w, keep, kept,
+  hipLaunchKernelGGL(k_sel_decide, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, keep, kept,
                      keptsum != nullptr);
   prof_end(st);
   if (keptsum)
