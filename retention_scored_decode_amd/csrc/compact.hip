@@ -9,13 +9,14 @@
 // by a prefix sum over heads; kept rows keep their slot order, so positions
 // stay ascending within every head.
 //
-// Kernels: prep (chunk list of 64 pages), count (kept per chunk and per
-// head; one wave per chunk), head scan (destination page table and the
-// number of kept entries before each head), index (one wave per chunk: the
-// (source slot, destination slot) pair of every kept entry, in kept order)
-// and copy (a grid-stride row gather over the pair list: random 256-byte
-// reads, contiguous writes).  Planning is kept out of the copy so that every
-// wave of the copy issues its row loads after a single dependent load.
+// Kernels: count (one block per head: kept entries of the head), index (one
+// block per head: the kept entries of all earlier heads and their destination
+// pages by a strided reduction over the head counts, then the (source slot,
+// destination slot) pair of every kept entry in kept order, staged through LDS
+// so that the pair list is written with coalesced stores) and copy (a
+// grid-stride row gather over the pair list: random 256-byte reads,
+// contiguous writes).  Planning is kept out of the copy so that every wave of
+// the copy issues its row loads after a single dependent load.
 #include <algorithm>
 
 #include "common.h"
@@ -25,40 +26,22 @@ namespace trimkv {
 
 namespace {
 
-constexpr int CP = 64;          // pages per chunk: one keep byte per lane-slot, 16 per lane
-constexpr int NT = 256;
-constexpr int CPB = NT / WAVE;  // chunks per block of the count and index kernels
+constexpr int NT = 256;     // copy kernel
+constexpr int NTP = 1024;   // planning kernels: one block per head, one page per thread and tile
+constexpr int NWP = NTP / WAVE;
 
-// chunk metadata: x = head, y = first chunk of the head, z = first CSR page,
-// w = valid entries | (pages of the chunk << 16)
 struct CmpWs {
-  int32_t* chunk_off;   // [H + 1]
-  int4* meta;           // [Tmax + CPB]
-  int32_t* cnt;         // [Tmax] kept entries per chunk
   int32_t* head_kept;   // [H]
-  int64_t* kept_before; // [H + 1] kept entries of the earlier heads; [H] = total
+  int64_t* total;       // [1] kept entries over all heads
   uint2* pairs;         // [n_pages * 16] (source slot, destination slot) per kept entry
 };
 
-__global__ void __launch_bounds__(1024) k_cmp_prep(const int32_t* __restrict__ page_off,
-                                                   const int32_t* __restrict__ len, int n_heads, CmpWs w) {
-  __shared__ int64_t tmp[1024 / WAVE + 1];
-  __shared__ PrepLDS L;
-  for (int h = blockIdx.x * 1024 + threadIdx.x; h < n_heads; h += gridDim.x * 1024) w.head_kept[h] = 0;
-  const int T = prep_chunks<1024>(page_off, len, n_heads, CP, L, tmp, w.chunk_off);
-  for (int c = blockIdx.x * 1024 + threadIdx.x; c < T; c += gridDim.x * 1024) {
-    const ChunkInfo ci = chunk_info(L, w.chunk_off, page_off, len, n_heads, CP, c);
-    w.meta[c] = make_int4(ci.h, ci.c0, ci.page0, ci.nv | (ci.npg << 16));
-  }
-}
-
-// Bit b (0..15) set iff keep byte b of this lane's 16 bytes is nonzero and
-// the slot is valid.  Lane l of a chunk's wave covers page l of the chunk.
-__device__ __forceinline__ uint32_t lane_keep_mask(const uint8_t* __restrict__ keep, int page0, int nv,
-                                                   int lane) {
-  const int nvb = min(max(nv - 16 * lane, 0), 16);
+// Bit b (0..15) set iff keep byte b of page p of a head is nonzero and the
+// slot is valid (below nv, the head's valid entries).
+__device__ __forceinline__ uint32_t page_keep_mask(const uint8_t* __restrict__ keep, int page0, int nv, int p) {
+  const int nvb = min(max(nv - PAGE * p, 0), PAGE);
   if (nvb == 0) return 0u;
-  const uint4 q = *reinterpret_cast<const uint4*>(keep + ((int64_t)page0 + lane) * PAGE);
+  const uint4 q = *reinterpret_cast<const uint4*>(keep + ((int64_t)page0 + p) * PAGE);
   auto nz4 = [](uint32_t x) -> uint32_t {   // one bit per nonzero byte
     const uint32_t t = (((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
     return ((t >> 7) & 1u) | ((t >> 14) & 2u) | ((t >> 21) & 4u) | ((t >> 28) & 8u);
@@ -67,86 +50,139 @@ __device__ __forceinline__ uint32_t lane_keep_mask(const uint8_t* __restrict__ k
   return m & ((1u << nvb) - 1u);
 }
 
-__device__ __forceinline__ int wave_sum(int v) {
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
   for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d, WAVE);
   return v;
 }
 
-__global__ void __launch_bounds__(NT) k_cmp_count(int n_heads, const uint8_t* __restrict__ keep, CmpWs w) {
-  const int lane = threadIdx.x & (WAVE - 1);
-  const int c = blockIdx.x * CPB + (threadIdx.x >> 6);
-  const int T = w.chunk_off[n_heads];
-  const int4 m = w.meta[c];   // padded: in bounds for every launched wave
-  if (c >= T) return;
-  const int n = wave_sum(__popc(lane_keep_mask(keep, m.z, m.w & 0xFFFF, lane)));
-  if (lane == 0) {
-    w.cnt[c] = n;
-    if (n) atomicAdd(w.head_kept + m.x, n);
-  }
+// Valid entries of a head: its length, bounded by the slots of its pages.
+__device__ __forceinline__ int head_valid(const int32_t* __restrict__ page_off, const int32_t* __restrict__ len,
+                                          int h, int* p0) {
+  *p0 = page_off[h];
+  const int64_t slots = ((int64_t)page_off[h + 1] - *p0) * PAGE;
+  return (int)min((int64_t)max(len[h], 0), slots);
 }
 
-__global__ void __launch_bounds__(1024) k_cmp_headscan(int n_heads, int reserve, CmpWs w,
-                                                       int32_t* __restrict__ dst_off, int32_t* __restrict__ dst_len,
-                                                       int64_t* __restrict__ pages_used) {
-  __shared__ int64_t tmp[1024 / WAVE + 1];
-  int64_t carry = 0, kcarry = 0;
-  for (int base = 0; base < n_heads; base += 1024) {
-    const int h = base + threadIdx.x;
-    int64_t pages = 0, kh = 0;
-    if (h < n_heads) {
-      kh = w.head_kept[h];
-      dst_len[h] = (int32_t)kh;
-      pages = (kh + reserve + PAGE - 1) / PAGE;
-    }
-    int64_t tot, ktot;
-    const int64_t ex = block_exclusive_scan<1024>(pages, tmp, &tot);
-    const int64_t kex = block_exclusive_scan<1024>(kh, tmp, &ktot);
-    if (h < n_heads) {
-      dst_off[h] = (int32_t)(carry + ex);
-      w.kept_before[h] = kcarry + kex;
-    }
-    carry += tot;
-    kcarry += ktot;
-  }
-  if (threadIdx.x == 0) {
-    dst_off[n_heads] = (int32_t)carry;
-    w.kept_before[n_heads] = kcarry;
-    pages_used[0] = carry;
-  }
-}
-
-// One wave per chunk: the kept entries of the chunk in slot order get
-// consecutive kept indices after those of the head's earlier chunks.
-__global__ void __launch_bounds__(NT) k_cmp_index(int n_heads, const int32_t* __restrict__ page_ids,
-                                                  const uint8_t* __restrict__ keep, CmpWs w,
-                                                  const int32_t* __restrict__ dst_off, int64_t cap) {
-  const int lane = threadIdx.x & (WAVE - 1);
-  const int c = blockIdx.x * CPB + (threadIdx.x >> 6);
-  const int T = w.chunk_off[n_heads];
-  const int4 m = w.meta[c];
-  if (c >= T) return;
-  const int h = m.x, nv = m.w & 0xFFFF, npg = m.w >> 16;
-  int before = 0;
-  for (int j = m.y + lane; j < c; j += WAVE) before += w.cnt[j];
-  const int pid = lane < npg ? page_ids[m.z + lane] : 0;
-  const uint32_t mask = lane_keep_mask(keep, m.z, nv, lane);
-  before = wave_sum(before);
-  // exclusive prefix of the per-lane counts
-  const int cntl = __popc(mask);
-  int inc = cntl;
+__global__ void __launch_bounds__(NTP) k_cmp_count(const int32_t* __restrict__ page_off,
+                                                   const int32_t* __restrict__ len,
+                                                   const uint8_t* __restrict__ keep, CmpWs w) {
+  __shared__ int part[NWP];
+  const int h = blockIdx.x;
+  int p0;
+  const int nv = head_valid(page_off, len, h, &p0);
+  const int np = (nv + PAGE - 1) / PAGE;
+  int n = 0;
+  // four pages per thread in flight
+  for (int p = threadIdx.x; p < np; p += 4 * NTP) {
+    uint32_t m[4];
 #pragma unroll
-  for (int d = 1; d < WAVE; d <<= 1) {
-    const int o = __shfl_up(inc, d, WAVE);
-    if (lane >= d) inc += o;
+    for (int u = 0; u < 4; ++u) m[u] = page_keep_mask(keep, p0, nv, p + u * NTP);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) n += __popc(m[u]);
   }
-  const int64_t k0 = w.kept_before[h] + before + (inc - cntl);
-  const uint32_t d0 = (uint32_t)dst_off[h] * PAGE + (uint32_t)(before + inc - cntl);
-  uint32_t mm = mask;
-  for (int r = 0; mm; ++r) {
-    const int b = __ffs(mm) - 1;
-    mm &= mm - 1;
-    if (k0 + r < cap) w.pairs[k0 + r] = make_uint2((uint32_t)pid * PAGE + b, d0 + r);
+  n = wave_sum(n);
+  if ((threadIdx.x & (WAVE - 1)) == 0) part[threadIdx.x / WAVE] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int t = 0;
+    for (int i = 0; i < NWP; ++i) t += part[i];
+    w.head_kept[h] = t;
+  }
+}
+
+// Destination layout: head h owns ceil((kept_h + reserve) / 16) pages,
+// numbered by a prefix sum over heads; its kept entries fill them in kept
+// order.  Every block recomputes the prefix of its own head from the head
+// counts (a strided reduction: O(H / 1024) loads per thread).
+__global__ void __launch_bounds__(NTP) k_cmp_index(int n_heads, int reserve, const int32_t* __restrict__ page_off,
+                                                   const int32_t* __restrict__ len,
+                                                   const int32_t* __restrict__ page_ids,
+                                                   const uint8_t* __restrict__ keep, CmpWs w,
+                                                   int32_t* __restrict__ dst_off, int32_t* __restrict__ dst_len,
+                                                   int64_t* __restrict__ pages_used, int64_t cap) {
+  __shared__ uint32_t stage[NWP][WAVE * PAGE];   // source slots of each wave's kept entries
+  __shared__ int64_t red[2][NWP];
+  __shared__ int wtot[NWP];
+  const int h = blockIdx.x;
+  const int lane = threadIdx.x & (WAVE - 1), wid = threadIdx.x / WAVE;
+  int p0;
+  const int nv = head_valid(page_off, len, h, &p0);
+  const int np = (nv + PAGE - 1) / PAGE;
+  // first tile's keep bits and page ids, in flight during the head prefix
+  uint32_t mask = page_keep_mask(keep, p0, nv, threadIdx.x);
+  int pid = (int)threadIdx.x < np ? page_ids[p0 + threadIdx.x] : 0;
+  int64_t kb = 0, pb = 0;
+  for (int j = threadIdx.x; j < h; j += NTP) {
+    const int64_t kj = w.head_kept[j];
+    kb += kj;
+    pb += (kj + reserve + PAGE - 1) / PAGE;
+  }
+  kb = wave_sum(kb);
+  pb = wave_sum(pb);
+  if (lane == 0) {
+    red[0][wid] = kb;
+    red[1][wid] = pb;
+  }
+  __syncthreads();
+  kb = 0;
+  pb = 0;
+#pragma unroll
+  for (int i = 0; i < NWP; ++i) {
+    kb += red[0][i];
+    pb += red[1][i];
+  }
+  const int kh = w.head_kept[h];
+  if (threadIdx.x == 0) {
+    dst_off[h] = (int32_t)pb;
+    dst_len[h] = kh;
+    if (h == n_heads - 1) {
+      const int64_t pend = pb + ((int64_t)kh + reserve + PAGE - 1) / PAGE;
+      dst_off[n_heads] = (int32_t)pend;
+      pages_used[0] = pend;
+      w.total[0] = kb + kh;
+    }
+  }
+  const uint32_t d_base = (uint32_t)pb * PAGE;
+  int carry = 0;   // kept entries of the head's earlier tiles
+  for (int t0 = 0; t0 < np; t0 += NTP) {
+    // next tile's loads ahead of this tile's scan
+    const int pn = t0 + NTP + (int)threadIdx.x;
+    const uint32_t mask_n = page_keep_mask(keep, p0, nv, pn);
+    const int pid_n = pn < np ? page_ids[p0 + pn] : 0;
+    const int cnt = __popc(mask);
+    int inc = cnt;
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) {
+      const int o = __shfl_up(inc, d, WAVE);
+      if (lane >= d) inc += o;
+    }
+    const int wt = __shfl(inc, WAVE - 1, WAVE);
+    uint32_t mm = mask;
+    for (int r = inc - cnt; mm; ++r) {
+      const int b = __ffs(mm) - 1;
+      mm &= mm - 1;
+      stage[wid][r] = (uint32_t)pid * PAGE + b;
+    }
+    if (lane == 0) wtot[wid] = wt;
+    __syncthreads();
+    int wex = 0, ttot = 0;
+#pragma unroll
+    for (int i = 0; i < NWP; ++i) {
+      const int x = wtot[i];
+      wex += i < wid ? x : 0;
+      ttot += x;
+    }
+    const int o = carry + wex;   // ordinal within the head of the wave's first entry
+    for (int j = lane; j < wt; j += WAVE) {
+      const int64_t k = kb + o + j;
+      if (k < cap) w.pairs[k] = make_uint2(stage[wid][j], d_base + (uint32_t)(o + j));
+    }
+    carry += ttot;
+    mask = mask_n;
+    pid = pid_n;
+    __syncthreads();   // stage and wtot are rewritten by the next tile
   }
 }
 
@@ -168,7 +204,7 @@ __global__ void __launch_bounds__(NT) k_cmp_copy(int n_heads, const uint8_t* __r
   const int64_t total_dst = min((int64_t)dst_off[n_heads], dst_pages);
   for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < total_dst; i += (int64_t)gridDim.x * NT)
     dst_ids[i] = (int32_t)i;
-  const int64_t total = min(w.kept_before[n_heads], pair_cap);
+  const int64_t total = min(w.total[0], pair_cap);
   if (total == 0) return;
   const int64_t dcap = dst_pages * PAGE;
   const int part = threadIdx.x % LPR;
@@ -202,20 +238,15 @@ __global__ void __launch_bounds__(NT) k_cmp_copy(int n_heads, const uint8_t* __r
 CmpWs carve(const trimkv_cache_t* c, void* ws) {
   WsLayout L = compact_ws_layout(c);
   char* b = (char*)ws;
-  return CmpWs{(int32_t*)(b + L.off[0]), (int4*)(b + L.off[1]), (int32_t*)(b + L.off[2]),
-               (int32_t*)(b + L.off[3]), (int64_t*)(b + L.off[4]), (uint2*)(b + L.off[5])};
+  return CmpWs{(int32_t*)(b + L.off[0]), (int64_t*)(b + L.off[1]), (uint2*)(b + L.off[2])};
 }
 
 }  // namespace
 
 WsLayout compact_ws_layout(const trimkv_cache_t* c) {
-  const int64_t T = max_chunks(c, CP);
   WsLayout L;
-  L.add(((int64_t)c->n_heads + 1) * 4);
-  L.add((T + CPB) * 16);
-  L.add(T * 4);
   L.add((int64_t)c->n_heads * 4);
-  L.add(((int64_t)c->n_heads + 1) * 8);
+  L.add(8);
   L.add(c->n_pages * PAGE * 8);
   return L;
 }
@@ -223,15 +254,10 @@ WsLayout compact_ws_layout(const trimkv_cache_t* c) {
 int launch_compact(const trimkv_cache_t* src, const uint8_t* keep, int reserve, int64_t max_kept_total,
                    trimkv_cache_t* dst, int64_t* pages_used, void* ws, hipStream_t st) {
   CmpWs w = carve(src, ws);
-  const int64_t T = max_chunks(src, CP);
   const int H = src->n_heads;
-  const unsigned cgrid = (unsigned)((T + CPB - 1) / CPB);
-  hipLaunchKernelGGL(k_cmp_prep, dim3(prep_grid(H, T, 1024)), dim3(1024), 0, st, src->page_off, src->len, H, w);
-  hipLaunchKernelGGL(k_cmp_count, dim3(cgrid), dim3(NT), 0, st, H, keep, w);
-  hipLaunchKernelGGL(k_cmp_headscan, dim3(1), dim3(1024), 0, st, H, reserve, w, dst->page_off, dst->len,
-                     pages_used);
-  hipLaunchKernelGGL(k_cmp_index, dim3(cgrid), dim3(NT), 0, st, H, src->page_ids, keep, w, dst->page_off,
-                     src->n_pages * PAGE);
+  hipLaunchKernelGGL(k_cmp_count, dim3(H), dim3(NTP), 0, st, src->page_off, src->len, keep, w);
+  hipLaunchKernelGGL(k_cmp_index, dim3(H), dim3(NTP), 0, st, H, reserve, src->page_off, src->len, src->page_ids,
+                     keep, w, dst->page_off, dst->len, pages_used, src->n_pages * PAGE);
   const int elt = src->dtype == TRIMKV_BF16 ? 2 : 4;
   const int rowb = src->head_dim * elt;
   // enough blocks for every destination page id and every row of the bound

@@ -31,7 +31,10 @@ namespace {
 constexpr int CP = 64;          // pages per chunk
 constexpr int CS = CP * PAGE;   // slots per chunk
 constexpr int NT = 256;         // threads per chunk block (4 slots each)
-constexpr int CPB = 8;          // chunks per histogram block
+#ifndef TRIMKV_SEL_CPB
+#define TRIMKV_SEL_CPB 8
+#endif
+constexpr int CPB = TRIMKV_SEL_CPB;   // chunks per histogram and decision block
 constexpr int HIST_WORDS = 2048 + 2048 + 1024;
 constexpr uint32_t SPIN_LIMIT = 1u << 26;
 
@@ -172,20 +175,14 @@ __device__ __forceinline__ void hist_add(uint32_t* lh, uint32_t key, uint32_t pr
 template <int PASS>
 __global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __restrict__ score, SelWs w) {
   constexpr int NB = PASS == 2 ? 1024 : 2048;
-  // Pass 0 counts every key, and retention scores fall into few bins: each
-  // 16-lane row of a wave adds into its own copy of the histogram (copies
-  // offset by one bank), so at most 16 lanes contend for one LDS word.
-  constexpr int COPIES = PASS == 0 ? 4 : 1;
-  constexpr int CSTRIDE = NB + 1;
-  __shared__ uint32_t lh[COPIES * CSTRIDE];
-  uint32_t* lhc = lh + (COPIES > 1 ? ((threadIdx.x & (WAVE - 1)) >> 4) * CSTRIDE : 0);
+  __shared__ uint32_t lh[NB];
   __shared__ int4 sm[CPB];
   const int T = w.chunk_off[n_heads];
   const int c0 = blockIdx.x * CPB;
   if (c0 >= T) return;
   const int nc = min(CPB, T - c0);
   if (threadIdx.x < nc) sm[threadIdx.x] = w.meta[c0 + threadIdx.x];
-  for (int b = threadIdx.x; b < COPIES * CSTRIDE; b += NT) lh[b] = 0u;
+  for (int b = threadIdx.x; b < NB; b += NT) lh[b] = 0u;
   __syncthreads();
   float4 kv[CPB];
   const int i0 = threadIdx.x * 4;
@@ -216,18 +213,14 @@ __global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __res
           const float a[4] = {kv[k].x, kv[k].y, kv[k].z, kv[k].w};
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (i0 + j < nv) hist_add<PASS>(lhc, score_key(a[j]), pre);
+            if (i0 + j < nv) hist_add<PASS>(lh, score_key(a[j]), pre);
         }
       }
       __syncthreads();
       uint32_t* g = pass_hist(w, s, PASS);
       for (int b = threadIdx.x; b < NB; b += NT) {
-        uint32_t v = 0;
-#pragma unroll
-        for (int cp = 0; cp < COPIES; ++cp) {
-          v += lh[cp * CSTRIDE + b];
-          lh[cp * CSTRIDE + b] = 0u;
-        }
+        const uint32_t v = lh[b];
+        lh[b] = 0u;
         if (v) atomicAdd(g + b, v);
       }
       __syncthreads();
