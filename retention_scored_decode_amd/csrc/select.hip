@@ -30,12 +30,27 @@ namespace {
 
 constexpr int CP = 64;          // pages per chunk
 constexpr int CS = CP * PAGE;   // slots per chunk
-constexpr int NT = 256;         // threads per chunk block (4 slots each)
+constexpr int NT = 1024;        // threads per histogram and decision block
+constexpr int GT = CS / 4;      // threads per chunk (4 slots each)
+constexpr int CG = NT / GT;     // chunks in flight per block: thread t works on chunk t / GT of each round
 #ifndef TRIMKV_SEL_CPB
-#define TRIMKV_SEL_CPB 8
+#define TRIMKV_SEL_CPB 32
 #endif
-constexpr int CPB = TRIMKV_SEL_CPB;   // chunks per histogram and decision block
-constexpr int HIST_WORDS = 2048 + 2048 + 1024;
+constexpr int CPB = TRIMKV_SEL_CPB;   // chunks per block
+constexpr int RND = CPB / CG;         // rounds of CG chunks
+static_assert(CPB % CG == 0 && CPB <= NT, "chunk rounds");
+#ifndef TRIMKV_SEL_HCOPIES
+#define TRIMKV_SEL_HCOPIES 4
+#endif
+#ifndef TRIMKV_SEL_BSTRIDE
+#define TRIMKV_SEL_BSTRIDE 1
+#endif
+// Histogram layout per segment and pass: HC copies (block b adds into copy
+// b % HC) of NB bins BS words apart; readers sum the copies.
+constexpr int HC = TRIMKV_SEL_HCOPIES;
+constexpr int BS = TRIMKV_SEL_BSTRIDE;
+__host__ __device__ constexpr int copy_words(int nb) { return nb * BS + (HC > 1 ? 32 : 0); }
+constexpr int HIST_WORDS = HC * (2 * copy_words(2048) + copy_words(1024));
 constexpr uint32_t SPIN_LIMIT = 1u << 26;
 
 enum { MODE_NORMAL = 0, MODE_ALL = 1, MODE_NONE = 2 };
@@ -67,7 +82,7 @@ constexpr uint64_t LB_AGG = 1ull << 62, LB_PREFIX = 2ull << 62, LB_VAL = (1ull <
 
 __device__ __forceinline__ int pass_bits(int pass) { return pass == 2 ? 10 : 11; }
 __device__ __forceinline__ uint32_t* pass_hist(const SelWs& w, int s, int pass) {
-  return w.hist + (size_t)s * HIST_WORDS + (pass == 0 ? 0 : pass == 1 ? 2048 : 4096);
+  return w.hist + (size_t)s * HIST_WORDS + (pass == 0 ? 0 : pass == 1 ? 1 : 2) * HC * copy_words(2048);
 }
 
 // ---------------------------------------------------------------------------
@@ -111,24 +126,27 @@ __global__ void __launch_bounds__(1024) k_sel_prep(const int32_t* __restrict__ p
 
 // State of segment s after radix pass `pass`, computed by a whole block from
 // the finished histogram of that pass (every thread gets the result); the
-// designated block stores it as the state before the next pass.
-__device__ SegState state_after(const SelWs& w, int s, int pass, bool store) {
+// block holding the segment's first chunk stores it as the state before the
+// next pass.  The histogram words are loaded together with the state.
+__device__ SegState state_after(const SelWs& w, int s, int pass) {
   __shared__ int64_t tmp[NT / WAVE + 1];
   __shared__ uint32_t sh_prefix;
   __shared__ int64_t sh_rem, sh_ties;
+  const int nb = pass == 2 ? 1024 : 2048;
+  const int per = nb / NT;  // 2 or 1
+  const uint32_t* g = pass_hist(w, s, pass);
+  uint32_t c[2] = {0u, 0u};
+  for (int k = 0; k < per; ++k) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int r = 0; r < HC; ++r) v += g[r * copy_words(nb) + (threadIdx.x * per + k) * BS];
+    c[k] = v;
+  }
   SegState st = w.seg[(size_t)pass * w.n_seg + s];
+  const int64_t tsum = (int64_t)c[0] + c[1];
+  int64_t total;
+  const int64_t ex = block_exclusive_scan<NT>(tsum, tmp, &total);   // a histogram not filled reads zero
   if (st.mode == MODE_NORMAL) {
-    const int nb = pass == 2 ? 1024 : 2048;
-    const int per = nb / NT;  // 8 or 4
-    const uint32_t* g = pass_hist(w, s, pass);
-    uint32_t c[8];
-    int64_t tsum = 0;
-    for (int k = 0; k < per; ++k) {
-      c[k] = g[threadIdx.x * per + k];
-      tsum += c[k];
-    }
-    int64_t total;
-    const int64_t ex = block_exclusive_scan<NT>(tsum, tmp, &total);
     const int64_t above = total - ex - tsum;  // keys in bins of higher threads
     if (pass == 0) {
       st.n_valid = total;
@@ -155,8 +173,16 @@ __device__ SegState state_after(const SelWs& w, int s, int pass, bool store) {
       __syncthreads();
     }
   }
-  if (store && threadIdx.x == 0) w.seg[(size_t)(pass + 1) * w.n_seg + s] = st;
+  if (threadIdx.x == 0 && (int)blockIdx.x == st.chunk_begin / CPB) w.seg[(size_t)(pass + 1) * w.n_seg + s] = st;
   return st;
+}
+
+// Chunk metadata from LDS, in scalar registers: every wave works on one
+// chunk per round.
+__device__ __forceinline__ int4 umeta(const int4* sm, int k) {
+  const int4 m = sm[k];
+  return make_int4(__builtin_amdgcn_readfirstlane(m.x), __builtin_amdgcn_readfirstlane(m.y),
+                   __builtin_amdgcn_readfirstlane(m.z), __builtin_amdgcn_readfirstlane(m.w));
 }
 
 template <int PASS>
@@ -170,58 +196,74 @@ __device__ __forceinline__ void hist_add(uint32_t* lh, uint32_t key, uint32_t pr
   }
 }
 
-// Block b histograms chunks [b*CPB, b*CPB + CPB): metadata first, then every
-// key load in flight while the previous pass's bin is located.
+// Block b histograms chunks [b*CPB, b*CPB + CPB), CG chunks per round
+// (GT threads of 4 slots per chunk): metadata first, then every key load in
+// flight while the previous pass's bin is located.  The block's histogram is
+// merged into the segment's once per segment run, so the number of device
+// atomics per bin falls with the number of chunks per block.
 template <int PASS>
 __global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __restrict__ score, SelWs w) {
   constexpr int NB = PASS == 2 ? 1024 : 2048;
   __shared__ uint32_t lh[NB];
   __shared__ int4 sm[CPB];
-  const int T = w.chunk_off[n_heads];
   const int c0 = blockIdx.x * CPB;
+  int4 mv = make_int4(0, 0, 0, 0);
+  if (threadIdx.x < CPB) mv = w.meta[c0 + threadIdx.x];   // padded by CPB entries
+  const int T = w.chunk_off[n_heads];
   if (c0 >= T) return;
   const int nc = min(CPB, T - c0);
-  if (threadIdx.x < nc) sm[threadIdx.x] = w.meta[c0 + threadIdx.x];
+  if (threadIdx.x < nc) sm[threadIdx.x] = mv;
   for (int b = threadIdx.x; b < NB; b += NT) lh[b] = 0u;
   __syncthreads();
-  float4 kv[CPB];
-  const int i0 = threadIdx.x * 4;
+  const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / GT), i0 = (threadIdx.x % GT) * 4;
+  uint32_t kk[RND][4];
+  SegState st0;
+  {
+    float4 kv[RND];
 #pragma unroll
-  for (int i = 0; i < CPB; ++i) {
-    if (i < nc && i0 < (sm[i].w & 0xFFFF))
-      kv[i] = *reinterpret_cast<const float4*>(score + (int64_t)sm[i].z * PAGE + i0);
+    for (int r = 0; r < RND; ++r) {
+      const int k = r * CG + grp;
+      const int4 m = umeta(sm, k);
+      kv[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k < nc && i0 < (m.w & 0xFFFF)) kv[r] = *reinterpret_cast<const float4*>(score + (int64_t)m.z * PAGE + i0);
+    }
+    // state for the first segment run while the keys are in flight
+    if (PASS > 0) st0 = state_after(w, sm[0].y, PASS - 1);
+#pragma unroll
+    for (int r = 0; r < RND; ++r) {
+      kk[r][0] = score_key(kv[r].x);
+      kk[r][1] = score_key(kv[r].y);
+      kk[r][2] = score_key(kv[r].z);
+      kk[r][3] = score_key(kv[r].w);
+    }
   }
   int i = 0;
   while (i < nc) {
-    // run of consecutive chunks of one segment
+    // run of consecutive chunks of one segment (block-uniform)
     const int s = sm[i].y;
     int e = i + 1;
     while (e < nc && sm[e].y == s) ++e;
     SegState st;
-    if (PASS == 0) {
-      st = w.seg[s];
-    } else {
-      const int first_blk = w.seg[s].chunk_begin / CPB;
-      st = state_after(w, s, PASS - 1, (int)blockIdx.x == first_blk);
-    }
+    if (PASS == 0) st = w.seg[s];
+    else st = i == 0 ? st0 : state_after(w, s, PASS - 1);
     if (st.mode == MODE_NORMAL) {
       const uint32_t pre = st.prefix;
 #pragma unroll
-      for (int k = 0; k < CPB; ++k) {
+      for (int r = 0; r < RND; ++r) {
+        const int k = r * CG + grp;
         if (k >= i && k < e) {
-          const int nv = sm[k].w & 0xFFFF;
-          const float a[4] = {kv[k].x, kv[k].y, kv[k].z, kv[k].w};
+          const int nv = umeta(sm, k).w & 0xFFFF;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (i0 + j < nv) hist_add<PASS>(lh, score_key(a[j]), pre);
+            if (i0 + j < nv) hist_add<PASS>(lh, kk[r][j], pre);
         }
       }
       __syncthreads();
-      uint32_t* g = pass_hist(w, s, PASS);
+      uint32_t* g = pass_hist(w, s, PASS) + (blockIdx.x % HC) * copy_words(NB);
       for (int b = threadIdx.x; b < NB; b += NT) {
         const uint32_t v = lh[b];
         lh[b] = 0u;
-        if (v) atomicAdd(g + b, v);
+        if (v) atomicAdd(g + b * BS, v);
       }
       __syncthreads();
     }
@@ -242,155 +284,239 @@ __device__ __forceinline__ double block_sum_f64(double v, double* tmpd) {
   return r;
 }
 
+__device__ __forceinline__ int block_sum_i32(int v, int* red) {
+  for (int d = WAVE / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, WAVE);
+  if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = v;
+  __syncthreads();
+  int r = 0;
+  if (threadIdx.x == 0)
+    for (int i = 0; i < NT / WAVE; ++i) r += red[i];
+  __syncthreads();
+  return r;   // valid in thread 0
+}
+
+// Keep bits of four consecutive slots (bit j: slot i0 + j) under state st.
+__device__ __forceinline__ void classify(const SegState& st, const uint32_t (&key)[4], int i0, int nv,
+                                         uint32_t& gtm, uint32_t& eqm) {
+  gtm = 0;
+  eqm = 0;
+  if (st.mode == MODE_NORMAL) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (i0 + j < nv) {
+        gtm |= (uint32_t)(key[j] > st.prefix) << j;
+        eqm |= (uint32_t)(key[j] == st.prefix) << j;
+      }
+    }
+  } else if (st.mode == MODE_ALL) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gtm |= (uint32_t)(i0 + j < nv) << j;
+  }
+}
+
+__device__ __forceinline__ uint32_t keep_word(uint32_t km) {
+  return (km & 1u) | ((km & 2u) << 7) | ((km & 4u) << 14) | ((km & 8u) << 21);
+}
+
 // ---------------------------------------------------------------------------
 // decide: block b handles chunk positions b*CPB .. b*CPB + CPB - 1.  The state
 // after the last radix pass is computed once per segment run of the block.
 // In the common case every key equal to K* is kept and chunks are
-// independent.  When the ties straddle the budget (more keys equal K* than
-// `need`), the chunks of that segment are processed in the order of a
-// per-segment ticket, one at a time, with a decoupled look-back for the ties
-// of earlier chunks; a ticket is taken only when its chunk is processed, so
-// every chunk a block waits for belongs to a block that is already running.
-// keep flags; kept[head] by atomics; optional per-chunk kept-score sums.
+// independent: keep words, then one kept-count atomic per head run.  When
+// the ties straddle the budget (more keys equal K* than `need`), the chunks
+// of that segment are processed in the order of a per-segment ticket, one at
+// a time (by the block's first GT threads), with a decoupled look-back for
+// the ties of earlier chunks; a ticket is taken only when its chunk is
+// processed, so every chunk a block waits for belongs to a block that is
+// already running.  Optional per-chunk kept-score sums (fixed-order trees).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __restrict__ score, SelWs w,
                                                    uint8_t* __restrict__ keep, int32_t* __restrict__ kept,
                                                    int want_sum) {
   __shared__ int64_t tmp[NT / WAVE + 1];
   __shared__ double tmpd[NT / WAVE];
+  __shared__ int red[NT / WAVE];
   __shared__ int sh_c;
   __shared__ int64_t sh_excl;
   __shared__ int4 sm[CPB];
-  const int T = w.chunk_off[n_heads];
   const int c0 = blockIdx.x * CPB;
+  int4 mv = make_int4(0, 0, 0, 0);
+  if (threadIdx.x < CPB) mv = w.meta[c0 + threadIdx.x];   // padded by CPB entries
+  const int T = w.chunk_off[n_heads];
   if (c0 >= T) return;
   const int nc = min(CPB, T - c0);
-  if (threadIdx.x < nc) sm[threadIdx.x] = w.meta[c0 + threadIdx.x];
+  if (threadIdx.x < nc) sm[threadIdx.x] = mv;
   __syncthreads();
-  const int i0 = threadIdx.x * 4;
+  const int lane = threadIdx.x & (WAVE - 1), wid = threadIdx.x / WAVE;
+  const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / GT), i0 = (threadIdx.x % GT) * 4;
   // keys of the block's own chunk positions, all loads in flight at once
-  float4 kv[CPB];
+  uint32_t kk[RND][4];
+  SegState st0;
+  {
+    float4 kv[RND];
 #pragma unroll
-  for (int k = 0; k < CPB; ++k)
-    if (k < nc && i0 < (sm[k].w & 0xFFFF))
-      kv[k] = *reinterpret_cast<const float4*>(score + (int64_t)sm[k].z * PAGE + i0);
-  int run_seg = -1;
-  SegState st;
-#pragma unroll
-  for (int k = 0; k < CPB; ++k) {
-    if (k >= nc) break;
-    int4 m = sm[k];
-    if (m.y != run_seg) {   // block-uniform
-      run_seg = m.y;
-      const int first_blk = w.seg[m.y].chunk_begin / CPB;
-      st = state_after(w, m.y, 2, (int)blockIdx.x == first_blk);
+    for (int r = 0; r < RND; ++r) {
+      const int k = r * CG + grp;
+      const int4 m = umeta(sm, k);
+      kv[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k < nc && i0 < (m.w & 0xFFFF)) kv[r] = *reinterpret_cast<const float4*>(score + (int64_t)m.z * PAGE + i0);
     }
-    const int cb = st.chunk_begin;
+    // state for the first segment run while the keys are in flight
+    st0 = state_after(w, sm[0].y, 2);
+#pragma unroll
+    for (int r = 0; r < RND; ++r) {
+      kk[r][0] = score_key(kv[r].x);
+      kk[r][1] = score_key(kv[r].y);
+      kk[r][2] = score_key(kv[r].z);
+      kk[r][3] = score_key(kv[r].w);
+    }
+  }
+  int i = 0;
+  while (i < nc) {
+    const int sg = sm[i].y;
+    int e = i + 1;
+    while (e < nc && sm[e].y == sg) ++e;
+    const SegState st = i == 0 ? st0 : state_after(w, sg, 2);
     const bool ranked = st.mode == MODE_NORMAL && st.ties > st.remaining;
-    int c = c0 + k;
-    float a[4] = {0.f, 0.f, 0.f, 0.f};
-    if (ranked) {
-      // process the segment's chunk of the next ticket instead of position c
-      if (threadIdx.x == 0) sh_c = cb + (int)atomicAdd(w.ticket + 2 + m.y, 1u);
-      __syncthreads();
-      c = sh_c;
-      m = w.meta[c];
-      if (i0 < (m.w & 0xFFFF)) {
-        const float4 sv = *reinterpret_cast<const float4*>(score + (int64_t)m.z * PAGE + i0);
-        a[0] = sv.x; a[1] = sv.y; a[2] = sv.z; a[3] = sv.w;
-      }
-    } else if (i0 < (m.w & 0xFFFF)) {
-      a[0] = kv[k].x; a[1] = kv[k].y; a[2] = kv[k].z; a[3] = kv[k].w;
-    }
-    const int nv = m.w & 0xFFFF;
-    const int nslots = (m.w >> 16) * PAGE;   // slots of the chunk's pages
-    const int64_t csr0 = (int64_t)m.z * PAGE;
-    uint32_t gtm = 0, eqm = 0;
-    if (st.mode == MODE_NORMAL) {
+    if (!ranked) {
+      uint32_t kmr[RND];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (i0 + j < nv) {
-          const uint32_t key = score_key(a[j]);
-          gtm |= (uint32_t)(key > st.prefix) << j;
-          eqm |= (uint32_t)(key == st.prefix) << j;
+      for (int r = 0; r < RND; ++r) {
+        const int k = r * CG + grp;
+        kmr[r] = 0;
+        if (k >= i && k < e) {
+          const int4 m = umeta(sm, k);
+          const int nv = m.w & 0xFFFF;
+          uint32_t gtm, eqm;
+          classify(st, kk[r], i0, nv, gtm, eqm);
+          kmr[r] = gtm | eqm;   // every tie is kept
+          if (i0 < (m.w >> 16) * PAGE) *reinterpret_cast<uint32_t*>(keep + (int64_t)m.z * PAGE + i0) = keep_word(kmr[r]);
         }
       }
-    } else if (st.mode == MODE_ALL) {
+      // kept entries per head: one block sum and one atomic per head run
+      int j = i;
+      while (j < e) {
+        const int h = sm[j].x;
+        int f = j + 1;
+        while (f < e && sm[f].x == h) ++f;
+        int n = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) gtm |= (uint32_t)(i0 + j < nv) << j;
-    }
-    int64_t rank = 0;
-    if (ranked) {
-      int64_t eq_total;
-      rank = block_exclusive_scan<NT>((int64_t)__popc(eqm), tmp, &eq_total);
-      if (threadIdx.x < WAVE) {
-        const int lane = threadIdx.x;
-        int64_t excl = 0;
-        if (c != cb) {
-          if (lane == 0)
-            __hip_atomic_store(w.look + c, LB_AGG | (uint64_t)eq_total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          int base = c - 1;   // window: chunks base, base-1, ..., base-63
-          uint32_t spins = 0;
-          while (true) {
-            const int j = base - lane;
-            // before the segment's first chunk: a zero prefix
-            const uint64_t v = j >= cb ? __hip_atomic_load(w.look + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                       : LB_PREFIX;
-            const uint64_t zm = __ballot(v == 0ull);
-            const uint64_t pm = __ballot((v & ~LB_VAL) == LB_PREFIX);
-            const int first = pm ? __ffsll((long long)pm) - 1 : WAVE;   // nearest prefix in the window
-            const uint64_t need = first == WAVE ? ~0ull : ((2ull << first) - 1ull);
-            if (zm & need) {  // a predecessor has not published yet
-              if (++spins > SPIN_LIMIT) {  // never expected; keeps every wave finite
-                if (lane == 0) atomicOr(w.error, 1u);
-                break;
-              }
-              __builtin_amdgcn_s_sleep(1);
-              continue;
-            }
-            int64_t val = (lane <= first) ? (int64_t)(v & LB_VAL) : 0;
-            for (int d = WAVE / 2; d > 0; d >>= 1) val += __shfl_xor(val, d, WAVE);
-            excl += val;
-            if (pm) break;
-            base -= WAVE;
+        for (int r = 0; r < RND; ++r) {
+          const int k = r * CG + grp;
+          if (k >= j && k < f) n += __popc(kmr[r]);
+        }
+        n = block_sum_i32(n, red);
+        if (threadIdx.x == 0 && n) atomicAdd(kept + h, n);
+        j = f;
+      }
+      if (want_sum) {
+#pragma unroll
+        for (int r = 0; r < RND; ++r) {
+          const int k = r * CG + grp;
+          const bool mine = k >= i && k < e;
+          double sum = 0.0;
+          if (mine && kmr[r]) {   // scores read again: only keys stay in registers
+            const float4 sv = *reinterpret_cast<const float4*>(score + (int64_t)umeta(sm, k).z * PAGE + i0);
+            const float a[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (kmr[r] & (1u << q)) sum += (double)a[q];
           }
-        }
-        if (lane == 0) {
-          __hip_atomic_store(w.look + c, LB_PREFIX | (uint64_t)(excl + eq_total), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-          sh_excl = excl;
-        }
-      }
-      __syncthreads();
-      rank += sh_excl;
-    }
-    uint32_t km = gtm;
-    if (ranked) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (eqm & (1u << j)) {
-          if (rank < st.remaining) km |= 1u << j;
-          ++rank;
+          for (int d = WAVE / 2; d > 0; d >>= 1) sum += __shfl_xor(sum, d, WAVE);
+          if (lane == 0) tmpd[wid] = sum;
+          __syncthreads();
+          if (mine && threadIdx.x % GT == 0) {
+            double t = 0.0;
+            for (int q = 0; q < GT / WAVE; ++q) t += tmpd[grp * (GT / WAVE) + q];
+            w.part[c0 + k] = t;
+          }
+          __syncthreads();
         }
       }
     } else {
-      km |= eqm;   // every tie is kept
-    }
-    if (i0 < nslots) {
-      const uint32_t word = (km & 1u) | ((km & 2u) << 7) | ((km & 4u) << 14) | ((km & 8u) << 21);
-      *reinterpret_cast<uint32_t*>(keep + csr0 + i0) = word;
-    }
-    int64_t kcount;
-    block_exclusive_scan<NT>((int64_t)__popc(km), tmp, &kcount);
-    if (threadIdx.x == 0 && kcount) atomicAdd(kept + m.x, (int32_t)kcount);
-    if (want_sum) {
-      double sum = 0.0;
+      const int cb = st.chunk_begin;
+      const bool act = threadIdx.x < GT;
+      for (int pos = i; pos < e; ++pos) {
+        // process the segment's chunk of the next ticket
+        if (threadIdx.x == 0) sh_c = cb + (int)atomicAdd(w.ticket + 2 + sg, 1u);
+        __syncthreads();
+        const int c = sh_c;
+        const int4 m = w.meta[c];
+        const int nv = m.w & 0xFFFF;
+        float a[4] = {0.f, 0.f, 0.f, 0.f};
+        if (act && i0 < nv) {
+          const float4 sv = *reinterpret_cast<const float4*>(score + (int64_t)m.z * PAGE + i0);
+          a[0] = sv.x; a[1] = sv.y; a[2] = sv.z; a[3] = sv.w;
+        }
+        uint32_t gtm = 0, eqm = 0;
+        if (act) {
+          const uint32_t key[4] = {score_key(a[0]), score_key(a[1]), score_key(a[2]), score_key(a[3])};
+          classify(st, key, i0, nv, gtm, eqm);
+        }
+        int64_t eq_total;
+        int64_t rank = block_exclusive_scan<NT>((int64_t)__popc(eqm), tmp, &eq_total);
+        if (threadIdx.x < WAVE) {
+          int64_t excl = 0;
+          if (c != cb) {
+            if (lane == 0)
+              __hip_atomic_store(w.look + c, LB_AGG | (uint64_t)eq_total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            int base = c - 1;   // window: chunks base, base-1, ..., base-63
+            uint32_t spins = 0;
+            while (true) {
+              const int jj = base - lane;
+              // before the segment's first chunk: a zero prefix
+              const uint64_t v = jj >= cb ? __hip_atomic_load(w.look + jj, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                          : LB_PREFIX;
+              const uint64_t zm = __ballot(v == 0ull);
+              const uint64_t pm = __ballot((v & ~LB_VAL) == LB_PREFIX);
+              const int first = pm ? __ffsll((long long)pm) - 1 : WAVE;   // nearest prefix in the window
+              const uint64_t need = first == WAVE ? ~0ull : ((2ull << first) - 1ull);
+              if (zm & need) {  // a predecessor has not published yet
+                if (++spins > SPIN_LIMIT) {  // never expected; keeps every wave finite
+                  if (lane == 0) atomicOr(w.error, 1u);
+                  break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+                continue;
+              }
+              int64_t val = (lane <= first) ? (int64_t)(v & LB_VAL) : 0;
+              for (int d = WAVE / 2; d > 0; d >>= 1) val += __shfl_xor(val, d, WAVE);
+              excl += val;
+              if (pm) break;
+              base -= WAVE;
+            }
+          }
+          if (lane == 0) {
+            __hip_atomic_store(w.look + c, LB_PREFIX | (uint64_t)(excl + eq_total), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            sh_excl = excl;
+          }
+        }
+        __syncthreads();
+        rank += sh_excl;
+        uint32_t km = gtm;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (km & (1u << j)) sum += (double)a[j];
-      const double bs = block_sum_f64(sum, tmpd);
-      if (threadIdx.x == 0) w.part[c] = bs;
+        for (int q = 0; q < 4; ++q) {
+          if (eqm & (1u << q)) {
+            if (rank < st.remaining) km |= 1u << q;
+            ++rank;
+          }
+        }
+        if (act && i0 < (m.w >> 16) * PAGE)
+          *reinterpret_cast<uint32_t*>(keep + (int64_t)m.z * PAGE + i0) = keep_word(km);
+        const int n = block_sum_i32(__popc(km), red);
+        if (threadIdx.x == 0 && n) atomicAdd(kept + m.x, n);
+        if (want_sum) {
+          double sum = 0.0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (km & (1u << q)) sum += (double)a[q];
+          const double bs = block_sum_f64(sum, tmpd);
+          if (threadIdx.x == 0) w.part[c] = bs;
+        }
+      }
     }
+    i = e;
   }
 }
 
@@ -425,7 +551,7 @@ WsLayout select_ws_layout(const trimkv_cache_t* c, int n_seg) {
   const int64_t H = c->n_heads;
   WsLayout L;
   L.add((H + 1) * 4);
-  L.add(T * 16);
+  L.add((T + CPB) * 16);
   L.add((size_t)4 * n_seg * sizeof(SegState));
   L.add((size_t)n_seg * HIST_WORDS * 4);
   L.add(T * 8);
