@@ -102,17 +102,19 @@ __global__ void __launch_bounds__(1024) k_attn_prep(const int32_t* __restrict__ 
 __device__ __forceinline__ int64_t flat_begin(int64_t w, int64_t W, int64_t P) { return w * P / W; }
 __device__ __forceinline__ int64_t flat_wave(int64_t p, int64_t W, int64_t P) { return ((p + 1) * W - 1) / P; }
 
-// Merge all partials of KV head h: per query head g, M = max of the partial
+// Merge all partials of query row g of KV head h: M = max of the partial
 // maxima, kept and dropped sums rescaled to M, O rescaled and divided by the
 // kept sum.  A head without partials has an empty kept set: out = 0,
-// dropped = 1, lse = -inf.  One block per KV head; fixed summation order.
-// Partials of head h: fp32 path, items item_off[h] .. item_off[h+1]-1; bf16
-// path, index w + h for every wave w whose range meets the head's pages.
+// dropped = 1, lse = -inf.  One block per query row; every partial's loads
+// are issued together; fixed summation order.  Partials of head h: fp32
+// path, items item_off[h] .. item_off[h+1]-1; bf16 path, index w + h for
+// every wave w whose range meets the head's pages.
 template <int D>
 __global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
   const AttnWs& w = a.w;
-  const int h = blockIdx.x;
   const int G = a.group;
+  const int h = blockIdx.x / G, g = blockIdx.x % G;
+  const int t = threadIdx.x, lane = t & (WAVE - 1), wid = t / WAVE;
   int b, e, add;
   const int64_t P = a.page_off[a.n_heads];
   if (a.waves) {
@@ -127,67 +129,89 @@ __global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
   }
   // waves with an empty range (fewer pages than waves) wrote no partial
   auto has = [&](int it) { return !a.waves || flat_begin(it, a.waves, P) < flat_begin(it + 1, a.waves, P); };
-  __shared__ float sM[GMAX], sLA[GMAX];
-  const int grp = threadIdx.x >> 4, sub = threadIdx.x & 15;  // 16 groups of 16 lanes
-  if (grp < G) {
-    float M = -INFINITY;
-    for (int it = b + sub; it < e; it += 16)
-      if (has(it)) M = fmaxf(M, w.stats[((size_t)(it + add) * G + grp) * 3]);
+  auto stat = [&](int it, int k) { return w.stats[((size_t)(it + add) * G + g) * 3 + k]; };
+  __shared__ float red[2][NT / WAVE];
+  __shared__ float sw[NT];
+  __shared__ float sacc[NT];
+  float M = -INFINITY;
+  for (int it = b + t; it < e; it += NT)
+    if (has(it)) M = fmaxf(M, stat(it, 0));
 #pragma unroll
-    for (int d = 8; d > 0; d >>= 1) M = fmaxf(M, __shfl_xor(M, d, 16));
-    float la = 0.f, ld = 0.f;
-    if (M != -INFINITY) {
-      for (int it = b + sub; it < e; it += 16) {
-        if (!has(it)) continue;
-        const float* st = w.stats + ((size_t)(it + add) * G + grp) * 3;
-        const float sc = exp2f(st[0] - M);
-        la += st[1] * sc;
-        ld += st[2] * sc;
-      }
-    }
+  for (int d = WAVE / 2; d > 0; d >>= 1) M = fmaxf(M, __shfl_xor(M, d, WAVE));
+  if (lane == 0) red[0][wid] = M;
+  __syncthreads();
+  M = red[0][0];
 #pragma unroll
-    for (int d = 8; d > 0; d >>= 1) {
-      la += __shfl_xor(la, d, 16);
-      ld += __shfl_xor(ld, d, 16);
-    }
-    if (sub == 0) {
-      sM[grp] = M;
-      sLA[grp] = la;
-      const int qh = h * G + grp;
-      const float l2 = la > 0.f ? M + log2f(la) : -INFINITY;  // base-2 LSE of the kept set
-      const float lse = l2 * LN2;
-      if (a.lse_out) a.lse_out[qh] = lse;
-      if (w.lse2) w.lse2[qh] = l2;
-      if (a.dropped) {
-        float dm = 1.f;
-        if (la > 0.f) dm = a.lse_ref ? -expm1f(lse - a.lse_ref[qh]) : ld / (la + ld);
-        a.dropped[qh] = dm;
-      }
+  for (int i = 1; i < NT / WAVE; ++i) M = fmaxf(M, red[0][i]);
+  __syncthreads();
+  float la = 0.f, ld = 0.f;
+  if (M != -INFINITY) {
+    for (int it = b + t; it < e; it += NT) {
+      if (!has(it)) continue;
+      const float sc = exp2f(stat(it, 0) - M);
+      la += stat(it, 1) * sc;
+      ld += stat(it, 2) * sc;
     }
   }
+#pragma unroll
+  for (int d = WAVE / 2; d > 0; d >>= 1) {
+    la += __shfl_xor(la, d, WAVE);
+    ld += __shfl_xor(ld, d, WAVE);
+  }
+  if (lane == 0) {
+    red[0][wid] = la;
+    red[1][wid] = ld;
+  }
   __syncthreads();
-  if (with_out) {
-    for (int i = threadIdx.x; i < G * D; i += NT) {
-      const int g = i / D;
-      const float M = sM[g], la = sLA[g];
-      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-      if (M != -INFINITY) {
-        auto term = [&](int it) {
-          const size_t pi = (size_t)(it + add);
-          return has(it) ? w.acc[pi * G * D + i] * exp2f(w.stats[(pi * G + g) * 3] - M) : 0.f;
-        };
-        int it = b;
-        for (; it + 4 <= e; it += 4) {
-          s0 += term(it);
-          s1 += term(it + 1);
-          s2 += term(it + 2);
-          s3 += term(it + 3);
-        }
-        for (; it < e; ++it) s0 += term(it);
-      }
-      const float s = (s0 + s1) + (s2 + s3);
-      a.out[(size_t)h * G * D + i] = la > 0.f ? s / la : 0.f;
+  la = 0.f;
+  ld = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / WAVE; ++i) {
+    la += red[0][i];
+    ld += red[1][i];
+  }
+  if (t == 0) {
+    const int qh = h * G + g;
+    const float l2 = la > 0.f ? M + log2f(la) : -INFINITY;  // base-2 LSE of the kept set
+    const float lse = l2 * LN2;
+    if (a.lse_out) a.lse_out[qh] = lse;
+    if (w.lse2) w.lse2[qh] = l2;
+    if (a.dropped) {
+      float dm = 1.f;
+      if (la > 0.f) dm = a.lse_ref ? -expm1f(lse - a.lse_ref[qh]) : ld / (la + ld);
+      a.dropped[qh] = dm;
     }
+  }
+  if (!with_out) return;
+  // output: SPLIT threads per dimension, each over every SPLIT-th partial
+  constexpr int SPLIT = NT / D;
+  constexpr int UN = 8;
+  const int d = t % D, part = t / D;
+  float s = 0.f;
+  for (int it0 = b; it0 < e; it0 += NT) {
+    const int n = min(NT, e - it0);
+    if (t < n) sw[t] = (M != -INFINITY && has(it0 + t)) ? exp2f(stat(it0 + t, 0) - M) : 0.f;
+    __syncthreads();
+    for (int j0 = part; j0 < n; j0 += SPLIT * UN) {
+      float v[UN], wt[UN];
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const int j = j0 + u * SPLIT;
+        wt[u] = j < n ? sw[j] : 0.f;
+        v[u] = wt[u] != 0.f ? w.acc[((size_t)(it0 + j + add) * G + g) * D + d] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < UN; ++u) s += v[u] * wt[u];
+    }
+    __syncthreads();
+  }
+  sacc[t] = s;
+  __syncthreads();
+  if (part == 0) {
+    float tot = sacc[d];
+#pragma unroll
+    for (int q = 1; q < SPLIT; ++q) tot += sacc[q * D + d];
+    a.out[((size_t)h * G + g) * D + d] = la > 0.f ? tot / la : 0.f;
   }
 }
 
@@ -784,8 +808,8 @@ int launch_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float
   int rc = keep ? launch_main<A_MASK>(c, a, st) : launch_main<A_PLAIN>(c, a, st);
   prof_end(st);
   if (rc) return rc;
-  if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(c->n_heads), dim3(NT), 0, st, a, 1);
-  else hipLaunchKernelGGL(k_attn_merge<64>, dim3(c->n_heads), dim3(NT), 0, st, a, 1);
+  if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(c->n_heads * group), dim3(NT), 0, st, a, 1);
+  else hipLaunchKernelGGL(k_attn_merge<64>, dim3(c->n_heads * group), dim3(NT), 0, st, a, 1);
   return check_launch();
 }
 
@@ -802,8 +826,8 @@ int launch_attn_mass(const trimkv_cache_t* c, const void* q, int group, float sc
   int rc = launch_main<A_LOGITS>(c, a, st);
   prof_end(st);
   if (rc) return rc;
-  if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(c->n_heads), dim3(NT), 0, st, a, 0);
-  else hipLaunchKernelGGL(k_attn_merge<64>, dim3(c->n_heads), dim3(NT), 0, st, a, 0);
+  if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(c->n_heads * group), dim3(NT), 0, st, a, 0);
+  else hipLaunchKernelGGL(k_attn_merge<64>, dim3(c->n_heads * group), dim3(NT), 0, st, a, 0);
   const int64_t blocks = (c->n_pages + 63) / 64;
   hipLaunchKernelGGL(k_mass, dim3((unsigned)blocks), dim3(256), 0, st, c->page_off, c->len, c->n_heads, group,
                      c->n_pages * PAGE, w, mass);
