@@ -139,11 +139,11 @@ __global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
 #pragma unroll
   for (int d = WAVE / 2; d > 0; d >>= 1) M = fmaxf(M, __shfl_xor(M, d, WAVE));
   if (lane == 0) red[0][wid] = M;
-  __syncthreads();
+  lds_barrier();
   M = red[0][0];
 #pragma unroll
   for (int i = 1; i < NT / WAVE; ++i) M = fmaxf(M, red[0][i]);
-  __syncthreads();
+  lds_barrier();
   float la = 0.f, ld = 0.f;
   if (M != -INFINITY) {
     for (int it = b + t; it < e; it += NT) {
@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
     red[0][wid] = la;
     red[1][wid] = ld;
   }
-  __syncthreads();
+  lds_barrier();
   la = 0.f;
   ld = 0.f;
 #pragma unroll
@@ -191,7 +191,7 @@ __global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
   for (int it0 = b; it0 < e; it0 += NT) {
     const int n = min(NT, e - it0);
     if (t < n) sw[t] = (M != -INFINITY && has(it0 + t)) ? exp2f(stat(it0 + t, 0) - M) : 0.f;
-    __syncthreads();
+    lds_barrier();
     for (int j0 = part; j0 < n; j0 += SPLIT * UN) {
       float v[UN], wt[UN];
 #pragma unroll
@@ -203,10 +203,10 @@ __global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
 #pragma unroll
       for (int u = 0; u < UN; ++u) s += v[u] * wt[u];
     }
-    __syncthreads();
+    lds_barrier();
   }
   sacc[t] = s;
-  __syncthreads();
+  lds_barrier();
   if (part == 0) {
     float tot = sacc[d];
 #pragma unroll

@@ -36,6 +36,18 @@ __device__ __forceinline__ int upper_index(const int32_t* a, int n, int64_t x) {
 }
 
 // ---------------------------------------------------------------------------
+// Workgroup barrier ordering LDS only.  __syncthreads() also drains every
+// outstanding global store and atomic of the wave (a workgroup release on
+// all address spaces); where a barrier only hands LDS data between threads
+// this one waits for LDS operations alone.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ---------------------------------------------------------------------------
 // Block-wide exclusive scan of one int64 per thread (blockDim.x == NT).
 // `tmp` is LDS of NT/64 + 1 int64.  Returns the exclusive prefix; *total is
 // the block sum.  All threads must call it.
@@ -51,7 +63,7 @@ __device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t* tmp,
     if (lane >= d) x += y;
   }
   if (lane == WAVE - 1) tmp[wid] = x;
-  __syncthreads();
+  lds_barrier();
   if (threadIdx.x == 0) {
     int64_t run = 0;
     for (int w = 0; w < NT / WAVE; ++w) {
@@ -61,10 +73,10 @@ __device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t* tmp,
     }
     tmp[NT / WAVE] = run;
   }
-  __syncthreads();
+  lds_barrier();
   int64_t r = tmp[wid] + x - v;
   *total = tmp[NT / WAVE];
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 

@@ -26,6 +26,8 @@ namespace trimkv {
 
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int NT = 256;     // copy kernel
 constexpr int NTP = 1024;   // planning kernels: one block per head, one page per thread and tile
 constexpr int NWP = NTP / WAVE;
@@ -84,7 +86,7 @@ __global__ void __launch_bounds__(NTP) k_cmp_count(const int32_t* __restrict__ p
   }
   n = wave_sum(n);
   if ((threadIdx.x & (WAVE - 1)) == 0) part[threadIdx.x / WAVE] = n;
-  __syncthreads();
+  lds_barrier();
   if (threadIdx.x == 0) {
     int t = 0;
     for (int i = 0; i < NWP; ++i) t += part[i];
@@ -125,7 +127,7 @@ __global__ void __launch_bounds__(NTP) k_cmp_index(int n_heads, int reserve, con
     red[0][wid] = kb;
     red[1][wid] = pb;
   }
-  __syncthreads();
+  lds_barrier();
   kb = 0;
   pb = 0;
 #pragma unroll
@@ -166,7 +168,7 @@ __global__ void __launch_bounds__(NTP) k_cmp_index(int n_heads, int reserve, con
       stage[wid][r] = (uint32_t)pid * PAGE + b;
     }
     if (lane == 0) wtot[wid] = wt;
-    __syncthreads();
+    lds_barrier();
     int wex = 0, ttot = 0;
 #pragma unroll
     for (int i = 0; i < NWP; ++i) {
@@ -182,12 +184,15 @@ __global__ void __launch_bounds__(NTP) k_cmp_index(int n_heads, int reserve, con
     carry += ttot;
     mask = mask_n;
     pid = pid_n;
-    __syncthreads();   // stage and wtot are rewritten by the next tile
+    lds_barrier();   // stage and wtot are rewritten by the next tile
   }
 }
 
 // Grid-stride copy of kept rows: LPR lanes of 16 bytes per row, UNR rows per
-// lane group in flight.  Rows are read at random, written contiguously.
+// lane group in flight.  Rows are read at random, written contiguously.  K
+// and V rows are stored non-temporally: the compacted pool is read next by
+// decode attention, and write-back lines left in the caches would otherwise
+// be evicted during that read, competing with it for HBM.
 template <int ROWB>
 __global__ void __launch_bounds__(NT) k_cmp_copy(int n_heads, const uint8_t* __restrict__ src_k,
                                                  const uint8_t* __restrict__ src_v,
@@ -211,15 +216,15 @@ __global__ void __launch_bounds__(NT) k_cmp_copy(int n_heads, const uint8_t* __r
   for (int64_t k0 = (int64_t)blockIdx.x * RPB * UNR + threadIdx.x / LPR; k0 < total;
        k0 += (int64_t)gridDim.x * RPB * UNR) {
     uint2 pr[UNR];
-    uint4 kv[UNR], vv[UNR];
+    u32x4 kv[UNR], vv[UNR];
     uint32_t mv[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) pr[u] = w.pairs[min(k0 + u * RPB, total - 1)];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t s = pr[u].x;
-      kv[u] = *reinterpret_cast<const uint4*>(src_k + s * ROWB + part * 16);
-      vv[u] = *reinterpret_cast<const uint4*>(src_v + s * ROWB + part * 16);
+      kv[u] = *reinterpret_cast<const u32x4*>(src_k + s * ROWB + part * 16);
+      vv[u] = *reinterpret_cast<const u32x4*>(src_v + s * ROWB + part * 16);
       // lanes 0 and 1 of a row carry its ln(beta) and position
       mv[u] = src_meta[(s / PAGE) * (2 * PAGE) + (part & 1) * PAGE + s % PAGE];
     }
@@ -227,8 +232,8 @@ __global__ void __launch_bounds__(NT) k_cmp_copy(int n_heads, const uint8_t* __r
     for (int u = 0; u < UNR; ++u) {
       const int64_t d = pr[u].y;
       if (k0 + u * RPB < total && d < dcap) {
-        *reinterpret_cast<uint4*>(dst_k + d * ROWB + part * 16) = kv[u];
-        *reinterpret_cast<uint4*>(dst_v + d * ROWB + part * 16) = vv[u];
+        __builtin_nontemporal_store(kv[u], reinterpret_cast<u32x4*>(dst_k + d * ROWB + part * 16));
+        __builtin_nontemporal_store(vv[u], reinterpret_cast<u32x4*>(dst_v + d * ROWB + part * 16));
         if (part < 2) dst_meta[(d / PAGE) * (2 * PAGE) + part * PAGE + d % PAGE] = mv[u];
       }
     }

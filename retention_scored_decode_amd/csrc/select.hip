@@ -20,6 +20,7 @@
 // CSR order within a segment is head order and, within a head, slot
 // (= position) order, so this realises "score desc, head asc, position asc".
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -166,11 +167,11 @@ __device__ SegState state_after(const SelWs& w, int s, int pass) {
           cum += c[k];
         }
       }
-      __syncthreads();
+      lds_barrier();
       st.remaining = sh_rem;
       st.prefix = sh_prefix;
       st.ties = sh_ties;
-      __syncthreads();
+      lds_barrier();
     }
   }
   if (threadIdx.x == 0 && (int)blockIdx.x == st.chunk_begin / CPB) w.seg[(size_t)(pass + 1) * w.n_seg + s] = st;
@@ -185,15 +186,27 @@ __device__ __forceinline__ int4 umeta(const int4* sm, int k) {
                    __builtin_amdgcn_readfirstlane(m.z), __builtin_amdgcn_readfirstlane(m.w));
 }
 
-template <int PASS>
-__device__ __forceinline__ void hist_add(uint32_t* lh, uint32_t key, uint32_t pre) {
-  if (PASS == 0) {
-    atomicAdd(&lh[key >> 21], 1u);
-  } else if (PASS == 1) {
-    if ((key >> 21) == pre) atomicAdd(&lh[(key >> 10) & 2047u], 1u);
-  } else {
-    if ((key >> 10) == pre) atomicAdd(&lh[key & 1023u], 1u);
-  }
+// Smallest fp32 value whose key is >= K, for 1 <= K <= 2^32: a score s has
+// key(s) >= K exactly when s is not NaN and s >= key_floor(K) (the float
+// comparison also equates -0.0 and +0.0, as the keys do).  NaN when no value
+// qualifies.  Lets later passes classify scores with two float comparisons
+// and convert to keys only the few that fall inside the located bin.
+__device__ __forceinline__ float key_floor(uint64_t K) {
+  if (K <= 0x007FFFFFull) return -INFINITY;                              // at or below the key of -inf
+  if (K < 0x80000000ull) return __uint_as_float(~(uint32_t)K);           // negative values, -0.0
+  if (K <= 0xFF800000ull) return __uint_as_float((uint32_t)K & 0x7FFFFFFFu);   // +0.0 .. +inf
+  return qnan();
+}
+
+// Marks values as changed at this point so that quantities derived from
+// them are computed where used rather than hoisted out of the segment-run
+// loop (32 extra live registers).  Emits no instruction.
+template <typename T>
+__device__ __forceinline__ void opaque(T (&x)[RND][4]) {
+#pragma unroll
+  for (int r = 0; r < RND; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(x[r][j]));
 }
 
 // Block b histograms chunks [b*CPB, b*CPB + CPB), CG chunks per round
@@ -204,6 +217,8 @@ __device__ __forceinline__ void hist_add(uint32_t* lh, uint32_t key, uint32_t pr
 template <int PASS>
 __global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __restrict__ score, SelWs w) {
   constexpr int NB = PASS == 2 ? 1024 : 2048;
+  constexpr int SH = PASS == 0 ? 32 : PASS == 1 ? 21 : 10;   // key bits below the known prefix
+  constexpr int BSH = SH - (PASS == 2 ? 10 : 11);               // shift of this pass's bin
   __shared__ uint32_t lh[NB];
   __shared__ int4 sm[CPB];
   const int c0 = blockIdx.x * CPB;
@@ -214,9 +229,9 @@ __global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __res
   const int nc = min(CPB, T - c0);
   if (threadIdx.x < nc) sm[threadIdx.x] = mv;
   for (int b = threadIdx.x; b < NB; b += NT) lh[b] = 0u;
-  __syncthreads();
+  lds_barrier();
   const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / GT), i0 = (threadIdx.x % GT) * 4;
-  uint32_t kk[RND][4];
+  float a[RND][4];
   SegState st0;
   {
     float4 kv[RND];
@@ -227,14 +242,14 @@ __global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __res
       kv[r] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (k < nc && i0 < (m.w & 0xFFFF)) kv[r] = *reinterpret_cast<const float4*>(score + (int64_t)m.z * PAGE + i0);
     }
-    // state for the first segment run while the keys are in flight
+    // state for the first segment run while the scores are in flight
     if (PASS > 0) st0 = state_after(w, sm[0].y, PASS - 1);
 #pragma unroll
     for (int r = 0; r < RND; ++r) {
-      kk[r][0] = score_key(kv[r].x);
-      kk[r][1] = score_key(kv[r].y);
-      kk[r][2] = score_key(kv[r].z);
-      kk[r][3] = score_key(kv[r].w);
+      a[r][0] = kv[r].x;
+      a[r][1] = kv[r].y;
+      a[r][2] = kv[r].z;
+      a[r][3] = kv[r].w;
     }
   }
   int i = 0;
@@ -246,26 +261,43 @@ __global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __res
     SegState st;
     if (PASS == 0) st = w.seg[s];
     else st = i == 0 ? st0 : state_after(w, s, PASS - 1);
+    opaque(a);
     if (st.mode == MODE_NORMAL) {
       const uint32_t pre = st.prefix;
+      // keys of the located bin: [lo, hi); lo == 0 holds NaN, which no float
+      // comparison finds, so that bin is classified on the keys themselves
+      const uint64_t lo = PASS == 0 ? 0 : (uint64_t)pre << SH, hi = PASS == 0 ? 0 : (uint64_t)(pre + 1) << SH;
+      const bool by_key = PASS == 0 || lo == 0;
+      const float flo = key_floor(lo), fhi = key_floor(hi);
+      // one loop per classification, chosen once per run (block-uniform)
+      auto count = [&](auto exact) {
 #pragma unroll
-      for (int r = 0; r < RND; ++r) {
-        const int k = r * CG + grp;
-        if (k >= i && k < e) {
-          const int nv = umeta(sm, k).w & 0xFFFF;
+        for (int r = 0; r < RND; ++r) {
+          const int k = r * CG + grp;
+          if (k >= i && k < e) {
+            const int nv = umeta(sm, k).w & 0xFFFF;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (i0 + j < nv) hist_add<PASS>(lh, kk[r][j], pre);
+            for (int j = 0; j < 4; ++j) {
+              if (i0 + j < nv) {
+                bool in;
+                if constexpr (decltype(exact)::value) in = PASS == 0 || (score_key(a[r][j]) >> SH) == pre;
+                else in = a[r][j] >= flo && !(a[r][j] >= fhi);
+                if (in) atomicAdd(&lh[(score_key(a[r][j]) >> BSH) & (NB - 1)], 1u);
+              }
+            }
+          }
         }
-      }
-      __syncthreads();
+      };
+      if (by_key) count(std::true_type{});
+      else count(std::false_type{});
+      lds_barrier();
       uint32_t* g = pass_hist(w, s, PASS) + (blockIdx.x % HC) * copy_words(NB);
       for (int b = threadIdx.x; b < NB; b += NT) {
         const uint32_t v = lh[b];
         lh[b] = 0u;
         if (v) atomicAdd(g + b * BS, v);
       }
-      __syncthreads();
+      lds_barrier();
     }
     i = e;
   }
@@ -276,36 +308,51 @@ __device__ __forceinline__ double block_sum_f64(double v, double* tmpd) {
   for (int d = WAVE / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, WAVE);
   const int wid = threadIdx.x / WAVE;
   if ((threadIdx.x & (WAVE - 1)) == 0) tmpd[wid] = v;
-  __syncthreads();
+  lds_barrier();
   double r = 0.0;
   if (threadIdx.x == 0)
     for (int i = 0; i < NT / WAVE; ++i) r += tmpd[i];
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 
 __device__ __forceinline__ int block_sum_i32(int v, int* red) {
   for (int d = WAVE / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, WAVE);
   if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = v;
-  __syncthreads();
+  lds_barrier();
   int r = 0;
   if (threadIdx.x == 0)
     for (int i = 0; i < NT / WAVE; ++i) r += red[i];
-  __syncthreads();
+  lds_barrier();
   return r;   // valid in thread 0
 }
 
-// Keep bits of four consecutive slots (bit j: slot i0 + j) under state st.
-__device__ __forceinline__ void classify(const SegState& st, const uint32_t (&key)[4], int i0, int nv,
-                                         uint32_t& gtm, uint32_t& eqm) {
+// Keep bits of four consecutive slots (bit j: slot i0 + j) under state st:
+// gtm marks key > K*, eqm key == K* (K* = st.prefix after the last pass),
+// decided on the scores with K*'s float bounds.
+__device__ __forceinline__ void classify(const SegState& st, const float (&a)[4], int i0, int nv, uint32_t& gtm,
+                                         uint32_t& eqm) {
   gtm = 0;
   eqm = 0;
   if (st.mode == MODE_NORMAL) {
+    const uint32_t ks = st.prefix;
+    if (ks != 0u) {
+      const float fa = key_floor((uint64_t)ks + 1), fe = key_floor(ks);   // fe: the value whose key is K*
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (i0 + j < nv) {
-        gtm |= (uint32_t)(key[j] > st.prefix) << j;
-        eqm |= (uint32_t)(key[j] == st.prefix) << j;
+      for (int j = 0; j < 4; ++j) {
+        if (i0 + j < nv) {
+          gtm |= (uint32_t)(a[j] >= fa) << j;
+          eqm |= (uint32_t)(a[j] == fe) << j;
+        }
+      }
+    } else {   // K* is the key of NaN, below every other score
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (i0 + j < nv) {
+          const bool nan = a[j] != a[j];
+          gtm |= (uint32_t)!nan << j;
+          eqm |= (uint32_t)nan << j;
+        }
       }
     }
   } else if (st.mode == MODE_ALL) {
@@ -346,11 +393,11 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
   if (c0 >= T) return;
   const int nc = min(CPB, T - c0);
   if (threadIdx.x < nc) sm[threadIdx.x] = mv;
-  __syncthreads();
+  lds_barrier();
   const int lane = threadIdx.x & (WAVE - 1), wid = threadIdx.x / WAVE;
   const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / GT), i0 = (threadIdx.x % GT) * 4;
-  // keys of the block's own chunk positions, all loads in flight at once
-  uint32_t kk[RND][4];
+  // scores of the block's own chunk positions, all loads in flight at once
+  float ka[RND][4];
   SegState st0;
   {
     float4 kv[RND];
@@ -361,14 +408,14 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
       kv[r] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (k < nc && i0 < (m.w & 0xFFFF)) kv[r] = *reinterpret_cast<const float4*>(score + (int64_t)m.z * PAGE + i0);
     }
-    // state for the first segment run while the keys are in flight
+    // state for the first segment run while the scores are in flight
     st0 = state_after(w, sm[0].y, 2);
 #pragma unroll
     for (int r = 0; r < RND; ++r) {
-      kk[r][0] = score_key(kv[r].x);
-      kk[r][1] = score_key(kv[r].y);
-      kk[r][2] = score_key(kv[r].z);
-      kk[r][3] = score_key(kv[r].w);
+      ka[r][0] = kv[r].x;
+      ka[r][1] = kv[r].y;
+      ka[r][2] = kv[r].z;
+      ka[r][3] = kv[r].w;
     }
   }
   int i = 0;
@@ -377,22 +424,36 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
     int e = i + 1;
     while (e < nc && sm[e].y == sg) ++e;
     const SegState st = i == 0 ? st0 : state_after(w, sg, 2);
+    opaque(ka);
     const bool ranked = st.mode == MODE_NORMAL && st.ties > st.remaining;
     if (!ranked) {
+      // every tie is kept: key >= K*, i.e. (K* above the key of NaN) one
+      // comparison with the smallest value whose key is K*
       uint32_t kmr[RND];
+      auto mark = [&](auto cmp_only) {
 #pragma unroll
-      for (int r = 0; r < RND; ++r) {
-        const int k = r * CG + grp;
-        kmr[r] = 0;
-        if (k >= i && k < e) {
-          const int4 m = umeta(sm, k);
-          const int nv = m.w & 0xFFFF;
-          uint32_t gtm, eqm;
-          classify(st, kk[r], i0, nv, gtm, eqm);
-          kmr[r] = gtm | eqm;   // every tie is kept
-          if (i0 < (m.w >> 16) * PAGE) *reinterpret_cast<uint32_t*>(keep + (int64_t)m.z * PAGE + i0) = keep_word(kmr[r]);
+        for (int r = 0; r < RND; ++r) {
+          const int k = r * CG + grp;
+          kmr[r] = 0;
+          if (k >= i && k < e) {
+            const int4 m = umeta(sm, k);
+            const int nv = m.w & 0xFFFF;
+            if constexpr (decltype(cmp_only)::value) {
+              const float fe = key_floor(st.prefix);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) kmr[r] |= (uint32_t)(i0 + j < nv && ka[r][j] >= fe) << j;
+            } else {
+              uint32_t gtm, eqm;
+              classify(st, ka[r], i0, nv, gtm, eqm);
+              kmr[r] = gtm | eqm;
+            }
+            if (i0 < (m.w >> 16) * PAGE)
+              *reinterpret_cast<uint32_t*>(keep + (int64_t)m.z * PAGE + i0) = keep_word(kmr[r]);
+          }
         }
-      }
+      };
+      if (st.mode == MODE_NORMAL && st.prefix != 0u) mark(std::true_type{});
+      else mark(std::false_type{});
       // kept entries per head: one block sum and one atomic per head run
       int j = i;
       while (j < e) {
@@ -415,22 +476,20 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
           const int k = r * CG + grp;
           const bool mine = k >= i && k < e;
           double sum = 0.0;
-          if (mine && kmr[r]) {   // scores read again: only keys stay in registers
-            const float4 sv = *reinterpret_cast<const float4*>(score + (int64_t)umeta(sm, k).z * PAGE + i0);
-            const float a[4] = {sv.x, sv.y, sv.z, sv.w};
+          if (mine) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              if (kmr[r] & (1u << q)) sum += (double)a[q];
+              if (kmr[r] & (1u << q)) sum += (double)ka[r][q];
           }
           for (int d = WAVE / 2; d > 0; d >>= 1) sum += __shfl_xor(sum, d, WAVE);
           if (lane == 0) tmpd[wid] = sum;
-          __syncthreads();
+          lds_barrier();
           if (mine && threadIdx.x % GT == 0) {
             double t = 0.0;
             for (int q = 0; q < GT / WAVE; ++q) t += tmpd[grp * (GT / WAVE) + q];
             w.part[c0 + k] = t;
           }
-          __syncthreads();
+          lds_barrier();
         }
       }
     } else {
@@ -439,7 +498,7 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
       for (int pos = i; pos < e; ++pos) {
         // process the segment's chunk of the next ticket
         if (threadIdx.x == 0) sh_c = cb + (int)atomicAdd(w.ticket + 2 + sg, 1u);
-        __syncthreads();
+        lds_barrier();
         const int c = sh_c;
         const int4 m = w.meta[c];
         const int nv = m.w & 0xFFFF;
@@ -449,10 +508,7 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
           a[0] = sv.x; a[1] = sv.y; a[2] = sv.z; a[3] = sv.w;
         }
         uint32_t gtm = 0, eqm = 0;
-        if (act) {
-          const uint32_t key[4] = {score_key(a[0]), score_key(a[1]), score_key(a[2]), score_key(a[3])};
-          classify(st, key, i0, nv, gtm, eqm);
-        }
+        if (act) classify(st, a, i0, nv, gtm, eqm);
         int64_t eq_total;
         int64_t rank = block_exclusive_scan<NT>((int64_t)__popc(eqm), tmp, &eq_total);
         if (threadIdx.x < WAVE) {
@@ -492,7 +548,7 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
             sh_excl = excl;
           }
         }
-        __syncthreads();
+        lds_barrier();
         rank += sh_excl;
         uint32_t km = gtm;
 #pragma unroll

@@ -147,8 +147,8 @@ def check_select(pc, per_head_scores, seg, budgets, keptsum=True):
             want = float(np.sum(per_head_scores[h][want_keep[h]].astype(np.float64)))
             if np.isfinite(want):
                 assert abs(ks[h] - want) <= 1e-12 * max(1.0, abs(want)), h
-            else:
-                assert ks[h] == want
+            else:   # inf or NaN sums (infinite or NaN scores kept)
+                assert ks[h] == want or (np.isnan(want) and np.isnan(ks[h])), h
     return keep
 
 
@@ -163,9 +163,12 @@ def test_select_parity_workloads(name):
     check_select(pc, scores, seg, [w.budget()] * w.n_seg)
 
 
-@pytest.mark.parametrize("kind", ["alpha3", "equal", "zeros", "inf", "cont"])
+KINDS = ["alpha3", "equal", "zeros", "inf", "cont", "nan"]
+
+
+@pytest.mark.parametrize("kind", KINDS)
 def test_select_parity_adversarial(kind):
-    rng = np.random.default_rng(["alpha3", "equal", "zeros", "inf", "cont"].index(kind))
+    rng = np.random.default_rng(KINDS.index(kind))
     for trial in range(4):
         H = int(rng.integers(3, 12))
         pc = synth.random_ragged_cache(100 + trial, n_heads=H, d=64, dtype="bf16", max_len=2500)
@@ -178,6 +181,9 @@ def test_select_parity_adversarial(kind):
             sc = [rng.choice([0.0, -0.0], n).astype(np.float32) for n in lens]
         elif kind == "inf":
             sc = [np.where(rng.random(n) < 0.3, -np.inf, -rng.integers(0, 3, n)).astype(np.float32) for n in lens]
+        elif kind == "nan":   # NaN ranks below every score, -inf included
+            sc = [np.where(rng.random(n) < 0.2, np.nan,
+                           rng.choice([-np.inf, -2.0, -0.0, 0.0, 1.5], n)).astype(np.float32) for n in lens]
         else:
             sc = [(-rng.random(n) * 50).astype(np.float32) for n in lens]
         n_seg = int(rng.integers(1, 4))
@@ -188,6 +194,26 @@ def test_select_parity_adversarial(kind):
                         [int(rng.integers(0, n + 1)) for n in N]):
             announce("select adversarial", kind, trial, budgets)
             check_select(pc, sc, seg, budgets)
+
+
+@pytest.mark.parametrize("kind", ["alpha3", "equal"])
+def test_select_ranked_many_lists(kind):
+    """Ties straddling the budget in segments that span many 32-chunk blocks,
+    so the ties are ranked across candidate lists by the in-order look-back;
+    segment boundaries fall inside blocks."""
+    rng = np.random.default_rng(7 + ["alpha3", "equal"].index(kind))
+    H = 40
+    pc = synth.random_ragged_cache(900, n_heads=H, d=64, dtype="bf16", max_len=20000, min_len=6000)
+    lens = pc.length
+    if kind == "alpha3":
+        sc = [rng.choice([-1.5, -0.25, 0.0], n).astype(np.float32) for n in lens]
+    else:
+        sc = [np.full(n, -0.5, np.float32) for n in lens]
+    seg = np.array([0, 7, 23, H], np.int32)
+    N = [int(lens[seg[s]:seg[s + 1]].sum()) for s in range(3)]
+    for budgets in ([n // 3 for n in N], [int(rng.integers(1, n)) for n in N]):
+        announce("select ranked", kind, budgets)
+        check_select(pc, sc, seg, budgets)
 
 
 # --------------------------------------------------------------------------
