@@ -18,8 +18,9 @@ def retention_exact(beta: float, age: int) -> Fraction:
 
 def select_sorted(entries, budget):
     """entries: list of (score, head, index).  Keep the first min(M, N) of a
-    full sort by score descending, then head, then index ascending."""
-    ranked = sorted(entries, key=lambda e: (-e[0], e[1], e[2]))
+    full sort by score descending, then head, then index ascending; a NaN
+    score ranks below every other score (-inf included)."""
+    ranked = sorted(entries, key=lambda e: (math.isnan(e[0]), 0.0 if math.isnan(e[0]) else -e[0], e[1], e[2]))
     return set((h, i) for _, h, i in ranked[:max(0, min(budget, len(ranked)))])
 
 

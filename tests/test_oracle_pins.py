@@ -170,15 +170,20 @@ def _random_scores(rng, kind, lens):
             s = np.full(n, -0.5)
         elif kind == "zeros":
             s = rng.choice([0.0, -0.0], n)
+        elif kind == "nan":  # NaN, -inf, signed zeros and finite values
+            s = np.where(rng.random(n) < 0.25, np.nan, rng.choice([-np.inf, -2.0, -0.0, 0.0, 1.5], n))
         else:  # with -inf
             s = np.where(rng.random(n) < 0.3, -np.inf, -rng.integers(0, 4, n).astype(np.float64))
         out.append(s.astype(np.float32))
     return out
 
 
-@pytest.mark.parametrize("kind", ["cont", "alpha3", "equal", "zeros", "inf"])
+SORT_KINDS = ["cont", "alpha3", "equal", "zeros", "inf", "nan"]
+
+
+@pytest.mark.parametrize("kind", SORT_KINDS)
 def test_select_equals_full_sort(kind):
-    rng = np.random.default_rng(["cont", "alpha3", "equal", "zeros", "inf"].index(kind) + 100)
+    rng = np.random.default_rng(SORT_KINDS.index(kind) + 100)
     for trial in range(300):
         H = int(rng.integers(1, 7))
         lens = rng.integers(0, 40, H)
