@@ -250,7 +250,7 @@ def main():
         tk.decode_attn(src, q, G, scale, out_m, drop_m, keep=keep, ws=ws_att)
         if ev: ev[3].record()
         arm(3)
-        tk.compact(src, keep, 0, M * w.n_seg, dst, used, ws=ws_cmp)
+        tk.compact(src, keep, 0, M * w.n_seg, dst, used, ws=ws_cmp, kept=kept)
         if ev: ev[4].record()
         arm(4)
         tk.decode_attn(dst, q, G, scale, out_p, drop_p, ws=ws_dec)

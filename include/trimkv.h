@@ -122,11 +122,11 @@ int trimkv_score(const trimkv_cache_t* cache, int32_t n_seg, const int32_t* seg_
  * DBTrimKV page, Method 3 (one global budget: rank every cached entry of all
  * layers and heads, keep the top M_global); TRIM-KV page, section 2 (evict the
  * lowest current scores once the budget is exceeded).
- * Total order: score descending (-0.0 == +0.0, -inf last), then flat head
- * ascending, then slot ascending.  Segment s keeps exactly
- * min(max(budget[s], 0), N_s) entries, N_s = valid entries of its heads.
- *   score:   device fp32 CSR plane (any fp32 key: retention scores or masses;
- *            valid slots must not be NaN)
+ * Total order: score descending (-0.0 == +0.0, -inf below every finite
+ * score, NaN below -inf), then flat head ascending, then slot ascending.
+ * Segment s keeps exactly min(max(budget[s], 0), N_s) entries, N_s = valid
+ * entries of its heads.
+ *   score:   device fp32 CSR plane (any fp32 key: retention scores or masses)
  *   budget:  device int64 [n_seg]
  *   keep:    device uint8 CSR plane, out: 1 kept, 0 evicted (valid slots),
  *            0 in padding slots
@@ -149,6 +149,11 @@ int trimkv_select_global(const trimkv_cache_t* cache, const float* score, int32_
  * over heads in flat order, dst->page_ids[c] = c, dst->len[h] = kept_h.
  * K, V rows and their ln(beta) and position are copied bit for bit; padding slots are left
  * unspecified.  `reserve` spare slots per head let trimkv_append add entries.
+ *   kept:          device int32 [n_heads] or NULL: the number of nonzero keep
+ *                  bytes of each head's valid slots, as trimkv_select_global
+ *                  wrote it for this keep plane; NULL counts them here (one
+ *                  more kernel).  Counts that disagree with keep give an
+ *                  unspecified layout (writes stay inside dst and ws).
  *   dst:           same n_heads/head_dim/dtype as src; its pools, page_off,
  *                  page_ids and len are written; must not overlap src.
  *   max_kept_total: host-side upper bound on the number of kept entries;
@@ -162,7 +167,7 @@ int trimkv_select_global(const trimkv_cache_t* cache, const float* score, int32_
  * in 32 bits (EUNSUPPORTED otherwise).
  * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, ECAPACITY.
  */
-int trimkv_compact(const trimkv_cache_t* src, const uint8_t* keep, int32_t reserve,
+int trimkv_compact(const trimkv_cache_t* src, const uint8_t* keep, const int32_t* kept, int32_t reserve,
                    int64_t max_kept_total, trimkv_cache_t* dst, int64_t* pages_used, void* ws,
                    size_t ws_bytes, void* stream);
 

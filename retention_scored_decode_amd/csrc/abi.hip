@@ -156,8 +156,9 @@ int trimkv_select_global(const trimkv_cache_t* c, const float* score, int32_t n_
   return launch_select(c, score, n_seg, seg, budget, keep, kept, keptsum, ws, S(stream));
 }
 
-int trimkv_compact(const trimkv_cache_t* src, const uint8_t* keep, int32_t reserve, int64_t max_kept_total,
-                   trimkv_cache_t* dst, int64_t* pages_used, void* ws, size_t ws_bytes, void* stream) {
+int trimkv_compact(const trimkv_cache_t* src, const uint8_t* keep, const int32_t* kept, int32_t reserve,
+                   int64_t max_kept_total, trimkv_cache_t* dst, int64_t* pages_used, void* ws, size_t ws_bytes,
+                   void* stream) {
   int rc;
   if (!cache_shape_ok(src, &rc)) return rc;
   if (!cache_shape_ok(dst, &rc)) return rc;
@@ -177,7 +178,7 @@ int trimkv_compact(const trimkv_cache_t* src, const uint8_t* keep, int32_t reser
   if (dst->n_pages < need) return TRIMKV_ECAPACITY;
   if ((rc = ws_check(ws, ws_bytes, compact_ws_layout(src).total))) return rc;
   if (H == 0) return TRIMKV_OK;
-  return launch_compact(src, keep, reserve, max_kept_total, dst, pages_used, ws, S(stream));
+  return launch_compact(src, keep, kept, reserve, max_kept_total, dst, pages_used, ws, S(stream));
 }
 
 int trimkv_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float* lse_ref, const void* q,

@@ -33,7 +33,7 @@ constexpr int NTP = 1024;   // planning kernels: one block per head, one page pe
 constexpr int NWP = NTP / WAVE;
 
 struct CmpWs {
-  int32_t* head_kept;   // [H]
+  int32_t* head_kept;   // [H] kept entries per head (the caller's counts when given)
   int64_t* total;       // [1] kept entries over all heads
   uint2* pairs;         // [n_pages * 16] (source slot, destination slot) per kept entry
 };
@@ -179,7 +179,7 @@ __global__ void __launch_bounds__(NTP) k_cmp_index(int n_heads, int reserve, con
     const int o = carry + wex;   // ordinal within the head of the wave's first entry
     for (int j = lane; j < wt; j += WAVE) {
       const int64_t k = kb + o + j;
-      if (k < cap) w.pairs[k] = make_uint2(stage[wid][j], d_base + (uint32_t)(o + j));
+      if (k >= 0 && k < cap) w.pairs[k] = make_uint2(stage[wid][j], d_base + (uint32_t)(o + j));
     }
     carry += ttot;
     mask = mask_n;
@@ -256,11 +256,12 @@ WsLayout compact_ws_layout(const trimkv_cache_t* c) {
   return L;
 }
 
-int launch_compact(const trimkv_cache_t* src, const uint8_t* keep, int reserve, int64_t max_kept_total,
-                   trimkv_cache_t* dst, int64_t* pages_used, void* ws, hipStream_t st) {
+int launch_compact(const trimkv_cache_t* src, const uint8_t* keep, const int32_t* kept, int reserve,
+                   int64_t max_kept_total, trimkv_cache_t* dst, int64_t* pages_used, void* ws, hipStream_t st) {
   CmpWs w = carve(src, ws);
   const int H = src->n_heads;
-  hipLaunchKernelGGL(k_cmp_count, dim3(H), dim3(NTP), 0, st, src->page_off, src->len, keep, w);
+  if (kept) w.head_kept = const_cast<int32_t*>(kept);   // only read from here on
+  else hipLaunchKernelGGL(k_cmp_count, dim3(H), dim3(NTP), 0, st, src->page_off, src->len, keep, w);
   hipLaunchKernelGGL(k_cmp_index, dim3(H), dim3(NTP), 0, st, H, reserve, src->page_off, src->len, src->page_ids,
                      keep, w, dst->page_off, dst->len, pages_used, src->n_pages * PAGE);
   const int elt = src->dtype == TRIMKV_BF16 ? 2 : 4;

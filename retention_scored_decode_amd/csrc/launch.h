@@ -44,8 +44,8 @@ int launch_append(trimkv_cache_t* c, const void* kn, const void* vn, const float
 int launch_select(const trimkv_cache_t* c, const float* score, int n_seg, const int32_t* seg,
                   const int64_t* budget, uint8_t* keep, int32_t* kept, double* keptsum, void* ws,
                   hipStream_t st);
-int launch_compact(const trimkv_cache_t* src, const uint8_t* keep, int reserve, int64_t max_kept_total,
-                   trimkv_cache_t* dst, int64_t* pages_used, void* ws, hipStream_t st);
+int launch_compact(const trimkv_cache_t* src, const uint8_t* keep, const int32_t* kept, int reserve,
+                   int64_t max_kept_total, trimkv_cache_t* dst, int64_t* pages_used, void* ws, hipStream_t st);
 int launch_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float* lse_ref, const void* q,
                        int group, float scale, float* out, float* dropped, float* lse_out, void* ws,
                        hipStream_t st);

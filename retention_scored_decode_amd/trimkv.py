@@ -54,7 +54,7 @@ def lib():
             "trimkv_log_beta": [vp, vp, i64, i32, vp],
             "trimkv_score": [cp, i32, vp, vp, vp, vp],
             "trimkv_select_global": [cp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp],
-            "trimkv_compact": [cp, vp, i32, i64, cp, vp, vp, sz, vp],
+            "trimkv_compact": [cp, vp, vp, i32, i64, cp, vp, vp, sz, vp],
             "trimkv_decode_attn": [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp],
             "trimkv_attn_mass": [cp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp],
             "trimkv_allocate": [vp, vp, i32, i64, vp, vp, vp],
@@ -187,10 +187,11 @@ def select_global(cache: Cache, score: torch.Tensor, seg_head_begin: torch.Tenso
 
 
 def compact(src: Cache, keep: torch.Tensor, reserve: int, max_kept_total: int, dst: Cache,
-            pages_used: torch.Tensor, ws: Optional[torch.Tensor] = None, stream=None):
+            pages_used: torch.Tensor, ws: Optional[torch.Tensor] = None, stream=None,
+            kept: Optional[torch.Tensor] = None):
     if ws is None:
         ws = workspace(OP_COMPACT, src)
-    _check(lib().trimkv_compact(ctypes.byref(src.struct()), _p(keep), int(reserve), int(max_kept_total),
+    _check(lib().trimkv_compact(ctypes.byref(src.struct()), _p(keep), _p(kept), int(reserve), int(max_kept_total),
                                 ctypes.byref(dst.struct()), _p(pages_used), _p(ws), ws.numel(),
                                 _stream(stream)), "trimkv_compact")
 

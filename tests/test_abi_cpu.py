@@ -106,13 +106,13 @@ def test_compact_capacity_and_compatibility():
     # need ceil((100 + 4*1)/16) + 4 = 11 pages
     small = tk.CacheStruct(4, 128, 16, tk.BF16, 10, 0x11000, 0x12000, 0x13000, 0x15000, 0x16000, 0x17000)
     ok = tk.CacheStruct(4, 128, 16, tk.BF16, 11, 0x11000, 0x12000, 0x13000, 0x15000, 0x16000, 0x17000)
-    assert L.trimkv_compact(ctypes.byref(src), X, 1, 100, ctypes.byref(small), X, X, ws, None) == tk.ECAPACITY
+    assert L.trimkv_compact(ctypes.byref(src), X, None, 1, 100, ctypes.byref(small), X, X, ws, None) == tk.ECAPACITY
     other = tk.CacheStruct(4, 64, 16, tk.BF16, 11, 0x11000, 0x12000, 0x13000, 0x15000, 0x16000, 0x17000)
-    assert L.trimkv_compact(ctypes.byref(src), X, 1, 100, ctypes.byref(other), X, X, ws, None) == tk.EINVAL
-    assert L.trimkv_compact(ctypes.byref(src), X, -1, 100, ctypes.byref(ok), X, X, ws, None) == tk.EINVAL
-    assert L.trimkv_compact(ctypes.byref(src), X, 1, 100, ctypes.byref(ok), X, X, ws - 1, None) == tk.EWORKSPACE
+    assert L.trimkv_compact(ctypes.byref(src), X, None, 1, 100, ctypes.byref(other), X, X, ws, None) == tk.EINVAL
+    assert L.trimkv_compact(ctypes.byref(src), X, None, -1, 100, ctypes.byref(ok), X, X, ws, None) == tk.EINVAL
+    assert L.trimkv_compact(ctypes.byref(src), X, None, 1, 100, ctypes.byref(ok), X, X, ws - 1, None) == tk.EWORKSPACE
     # aliasing source and destination pools
-    assert L.trimkv_compact(ctypes.byref(src), X, 1, 100, ctypes.byref(src), X, X, ws, None) in (tk.EINVAL,
+    assert L.trimkv_compact(ctypes.byref(src), X, None, 1, 100, ctypes.byref(src), X, X, ws, None) in (tk.EINVAL,
                                                                                                    tk.ECAPACITY)
 
 
@@ -122,7 +122,7 @@ def test_keep_plane_alignment_and_slot_width():
     ok = tk.CacheStruct(4, 128, 16, tk.BF16, 11, 0x11000, 0x12000, 0x13000, 0x15000, 0x16000, 0x17000)
     ws = L.trimkv_workspace_size(tk.OP_COMPACT, ctypes.byref(src), 0, 0)
     odd = ctypes.c_void_p(0x1008)   # keep planes start on 16-byte boundaries
-    assert L.trimkv_compact(ctypes.byref(src), odd, 1, 100, ctypes.byref(ok), X, X, ws, None) == tk.EINVAL
+    assert L.trimkv_compact(ctypes.byref(src), odd, None, 1, 100, ctypes.byref(ok), X, X, ws, None) == tk.EINVAL
     need = L.trimkv_workspace_size(tk.OP_DECODE_ATTN, ctypes.byref(src), 0, 4)
     assert L.trimkv_decode_attn(ctypes.byref(src), odd, None, X, 4, ctypes.c_float(1.0), X, X, None, X, need,
                                 None) == tk.EINVAL
@@ -132,7 +132,7 @@ def test_keep_plane_alignment_and_slot_width():
     huge = fake_cache(n_heads=4, n_pages=1 << 28)
     big_ws = L.trimkv_workspace_size(tk.OP_COMPACT, ctypes.byref(huge), 0, 0)
     dst = tk.CacheStruct(4, 128, 16, tk.BF16, 11, 0x11000, 0x12000, 0x13000, 0x15000, 0x16000, 0x17000)
-    assert L.trimkv_compact(ctypes.byref(huge), X, 1, 100, ctypes.byref(dst), X, X, big_ws,
+    assert L.trimkv_compact(ctypes.byref(huge), X, None, 1, 100, ctypes.byref(dst), X, X, big_ws,
                             None) == tk.EUNSUPPORTED
 
 

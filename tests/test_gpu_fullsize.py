@@ -57,7 +57,7 @@ def test_full_size_pipeline(full_c2):
     cap = -(-M // 16) + H
     dst = tk.Cache.empty(H, cap, D, torch.bfloat16)
     used = torch.zeros(1, dtype=torch.int64, device="cuda")
-    tk.compact(c, keep, 0, M, dst, used)
+    tk.compact(c, keep, 0, M, dst, used, kept=kept)
     out_p = torch.empty((nq, D), dtype=torch.float32, device="cuda")
     drop_p = torch.empty(nq, dtype=torch.float32, device="cuda")
     lse_p = torch.empty(nq, dtype=torch.float32, device="cuda")

@@ -219,7 +219,9 @@ def test_select_ranked_many_lists(kind):
 # --------------------------------------------------------------------------
 # a3: compaction
 # --------------------------------------------------------------------------
-def check_compact(pc, keep_heads, reserve):
+def check_compact(pc, keep_heads, reserve, given_counts=False):
+    """given_counts: pass the per-head kept counts (as selection writes them)
+    instead of letting compaction count the keep plane."""
     c = upload(pc)
     ov = OracleView(pc)
     kept_total = int(sum(int(k.sum()) for k in keep_heads))
@@ -229,7 +231,8 @@ def check_compact(pc, keep_heads, reserve):
     keep_plane = plane_from_heads([k.astype(np.uint8) for k in keep_heads], pc.page_off, pc.length, pc.n_pages,
                                   fill=0, dtype=np.uint8)
     used = torch.zeros(1, dtype=torch.int64, device="cuda")
-    tk.compact(c, cuda(keep_plane), reserve, kept_total, dst, used)
+    counts = cuda(np.array([int(k.sum()) for k in keep_heads], np.int32)) if given_counts else None
+    tk.compact(c, cuda(keep_plane), reserve, kept_total, dst, used, kept=counts)
     po, pi, ln, k, v, lnb, pos = download_cache(dst)
     wpo, wpi, wlen, rows = ref.compact({"k": ov.k_raw, "v": ov.v_raw, "lnb": ov.lnb, "pos": ov.pos}, keep_heads,
                                        reserve)
@@ -256,6 +259,7 @@ def test_compact_parity_workloads(name):
     scores = ov.scores(seg_t(seg, [w.t] * w.n_seg, pc.n_heads))
     keep, _ = ref.select_global(scores, seg, [w.budget()] * w.n_seg)
     check_compact(pc, keep, reserve=w.reserve)
+    check_compact(pc, keep, reserve=w.reserve, given_counts=True)
 
 
 def test_compact_ragged_edges():
@@ -266,7 +270,7 @@ def test_compact_ragged_edges():
             keep = [rng.random(int(n)) < p_keep for n in pc.length]
             for reserve in (0, 1, 17):
                 announce("compact ragged", dtype, d, p_keep, reserve)
-                check_compact(pc, keep, reserve)
+                check_compact(pc, keep, reserve, given_counts=reserve == 1)
 
 
 # --------------------------------------------------------------------------
