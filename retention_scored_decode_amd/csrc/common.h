@@ -139,11 +139,30 @@ struct PageHeads {
   int hf, hl;
 };
 
+// upper_index by a whole wave: 64 probes per step (one per lane) and a
+// ballot, so n entries take ceil(log64 n) dependent loads instead of log2 n.
+// Every lane returns the same index.
+__device__ __forceinline__ int wave_upper_index(const int32_t* __restrict__ a, int n, int64_t x) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  int lo = 0, hi = n;  // invariant: a[lo] <= x, answer in [lo, hi)
+  while (hi - lo > 1) {
+    const int step = (hi - lo + WAVE - 1) / WAVE;
+    const int i = lo + lane * step;
+    const uint64_t le = __ballot(i < hi && (int64_t)a[i] <= x);   // a prefix of the lanes, lane 0 included
+    lo += (63 - __clzll((long long)le)) * step;
+    hi = min(lo + step, hi);
+  }
+  return lo;
+}
+
+// Heads of the first and last CSR page of a block (waves 0 and 1 search in
+// parallel; blockDim.x >= 128).
 __device__ __forceinline__ PageHeads block_page_heads(const int32_t* __restrict__ page_off, int n_heads, int64_t c0,
                                                       int64_t clast, PageHeads* sh) {
-  if (threadIdx.x == 0) {
-    sh->hf = upper_index(page_off, n_heads + 1, c0);
-    sh->hl = upper_index(page_off, n_heads + 1, clast);
+  const int wid = threadIdx.x / WAVE;
+  if (wid < 2) {
+    const int h = wave_upper_index(page_off, n_heads + 1, wid == 0 ? c0 : clast);
+    if ((threadIdx.x & (WAVE - 1)) == 0) (wid == 0 ? sh->hf : sh->hl) = h;
   }
   __syncthreads();
   return *sh;
