@@ -29,6 +29,11 @@ namespace trimkv {
 
 namespace {
 
+// Cache policy of the K/V page loads: non-temporal.  Every K/V byte is read
+// once per call, and streaming reads that do not allocate in the caches
+// reached 6.9-7.1 TB/s here against 5.0-6.3 TB/s for ordinary loads.
+constexpr int CPOL_NT = 2;
+
 constexpr int CHA_F32 = 16;     // pages per work item of the fp32 kernel (one key per thread)
 constexpr int NT = 256;
 constexpr int GMAX = 16;
@@ -405,13 +410,13 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
       const uint8_t* vpage = vbase + phys * (PAGE * D * 2);
 #pragma unroll
       for (int u = 0; u < LPP; ++u)
-        __builtin_amdgcn_global_load_lds((gptr)(kpage + gk[u]), (lptr)(&lds_k[wu][buf][64 * u]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gptr)(kpage + gk[u]), (lptr)(&lds_k[wu][buf][64 * u]), 16, 0, CPOL_NT);
       if (!LOGITS) {
         const bool full = (i + 1) * PAGE <= nv;   // wave-uniform
         if (MODE == A_PLAIN && full) {
 #pragma unroll
           for (int u = 0; u < LPP; ++u)
-            __builtin_amdgcn_global_load_lds((gptr)(vpage + gv[u]), (lptr)(&lds_v[wu][buf][64 * u]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gptr)(vpage + gv[u]), (lptr)(&lds_v[wu][buf][64 * u]), 16, 0, CPOL_NT);
         } else {
 #pragma unroll
           for (int u = 0; u < LPP; ++u) {

@@ -190,9 +190,10 @@ __global__ void __launch_bounds__(NTP) k_cmp_index(int n_heads, int reserve, con
 
 // Grid-stride copy of kept rows: LPR lanes of 16 bytes per row, UNR rows per
 // lane group in flight.  Rows are read at random, written contiguously.  K
-// and V rows are stored non-temporally: the compacted pool is read next by
-// decode attention, and write-back lines left in the caches would otherwise
-// be evicted during that read, competing with it for HBM.
+// and V rows are loaded and stored non-temporally: each is touched once, and
+// the compacted pool is read next by decode attention, where write-back lines
+// left in the caches would otherwise be evicted during that read, competing
+// with it for HBM.
 template <int ROWB>
 __global__ void __launch_bounds__(NT) k_cmp_copy(int n_heads, const uint8_t* __restrict__ src_k,
                                                  const uint8_t* __restrict__ src_v,
@@ -223,8 +224,8 @@ __global__ void __launch_bounds__(NT) k_cmp_copy(int n_heads, const uint8_t* __r
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t s = pr[u].x;
-      kv[u] = *reinterpret_cast<const u32x4*>(src_k + s * ROWB + part * 16);
-      vv[u] = *reinterpret_cast<const u32x4*>(src_v + s * ROWB + part * 16);
+      kv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src_k + s * ROWB + part * 16));
+      vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src_v + s * ROWB + part * 16));
       // lanes 0 and 1 of a row carry its ln(beta) and position
       mv[u] = src_meta[(s / PAGE) * (2 * PAGE) + (part & 1) * PAGE + s % PAGE];
     }
