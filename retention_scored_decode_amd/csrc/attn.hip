@@ -38,7 +38,10 @@ constexpr int CHA_F32 = 16;     // pages per work item of the fp32 kernel (one k
 constexpr int NT = 256;
 constexpr int GMAX = 16;
 constexpr int FLAT_WMAX = 8192;   // most waves of one bf16 launch (workspace bound)
-constexpr int LDS_HMAX = 1024;    // heads whose page offsets each block copies into LDS
+// Threads per block of the bf16 kernel: four waves, each staging two K and
+// two V pages (16 KB at D = 128) in LDS.  Measured against two- and one-wave
+// blocks (more waves per CU): those were 5% and 25% slower.
+constexpr int NTA = 256;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -313,7 +316,7 @@ __device__ __forceinline__ uint32_t pick4(u32x4 v, int q) {
 // branch; the common page costs one FMA and one exp2 per logit.
 // ---------------------------------------------------------------------------
 template <int D, int MODE>
-__global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
+__global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
   typedef Tile<D> TL;
   constexpr int CH = TL::CH, LPP = TL::LPP;
   constexpr int KU = D / 32;    // QK MFMAs per page
@@ -322,34 +325,23 @@ __global__ void __launch_bounds__(NT) k_attn_bf16(AttnArgs a) {
   // load instructions per page; pages in flight are tracked by vmcnt (the
   // logits mode also stores inside the loop and keeps a single page in flight)
   constexpr int PER_PAGE = LOGITS ? 0 : 2 * LPP;
-  __shared__ u32x4 lds_k[NT / WAVE][2][16 * CH];
-  __shared__ u32x4 lds_v[NT / WAVE][2][LOGITS ? 1 : 16 * CH];
-  __shared__ int32_t s_pg[LDS_HMAX + 1];
+  __shared__ u32x4 lds_k[NTA / WAVE][2][16 * CH];
+  __shared__ u32x4 lds_v[NTA / WAVE][2][LOGITS ? 1 : 16 * CH];
   const AttnWs& w = a.w;
   const int lane = threadIdx.x & 63, r = lane >> 4, col = lane & 15, wv = threadIdx.x >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(wv);
   const int H = a.n_heads, G = a.group;
-  const bool lpg = H <= LDS_HMAX;
-  if (lpg) {
-    for (int i = threadIdx.x; i <= H; i += NT) s_pg[i] = a.page_off[i];
-    __syncthreads();
-  }
   const c_i32 cpo = (c_i32)a.page_off;
   const c_i32 cids = (c_i32)a.page_ids;
   const c_i32 clen = (c_i32)a.len;
   // page offsets are wave-uniform; readfirstlane keeps everything derived from them in scalar registers
-  auto pg = [&](int hh) -> int { return __builtin_amdgcn_readfirstlane(lpg ? s_pg[hh] : cpo[hh]); };
-  auto head_of = [&](int p) -> int {   // head whose pages hold CSR page p
-    int lo = 0, hi = H + 1;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (pg(mid) <= p) lo = mid; else hi = mid;
-    }
-    return lo;
+  auto pg = [&](int hh) -> int { return __builtin_amdgcn_readfirstlane(cpo[hh]); };
+  auto head_of = [&](int p) -> int {   // head whose pages hold CSR page p (64 probes per step)
+    return __builtin_amdgcn_readfirstlane(wave_upper_index(a.page_off, H + 1, p));
   };
   const int64_t P = pg(H);
   const int W = a.waves;
-  const int wave = blockIdx.x * (NT / WAVE) + wu;
+  const int wave = blockIdx.x * (NTA / WAVE) + wu;
   int p = (int)flat_begin(wave, W, P);
   const int pend = (int)flat_begin(wave + 1, W, P);
   if (p >= pend) return;   // per-wave exit: no block barriers below
@@ -730,7 +722,7 @@ AttnWs carve(const trimkv_cache_t* c, int group, void* ws, bool mass) {
   return w;
 }
 
-// Waves that the device holds at once for a kernel of NT threads per block
+// Waves that the device holds at once for a kernel of NTA threads per block
 // (cached per kernel and device).
 template <typename K>
 int resident_waves(K kernel) {
@@ -743,8 +735,8 @@ int resident_waves(K kernel) {
     if (cache[i].k == (const void*)kernel && cache[i].dev == dev) return cache[i].waves;
   int cus = 0, blocks = 0;
   hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, NT, 0) != hipSuccess) blocks = 1;
-  const int wv = std::min(FLAT_WMAX, std::max(1, blocks) * std::max(1, cus) * (NT / WAVE));
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, NTA, 0) != hipSuccess) blocks = 1;
+  const int wv = std::min(FLAT_WMAX, std::max(1, blocks) * std::max(1, cus) * (NTA / WAVE));
   if (used < 16) cache[used++] = Entry{(const void*)kernel, dev, wv};
   return wv;
 }
@@ -761,7 +753,7 @@ int launch_main(const trimkv_cache_t* c, AttnArgs& a, hipStream_t st) {
   }
   auto go = [&](auto kernel) {
     a.waves = resident_waves(kernel);
-    hipLaunchKernelGGL(kernel, dim3((unsigned)(a.waves / (NT / WAVE))), blk, 0, st, a);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(a.waves / (NTA / WAVE))), dim3(NTA), 0, st, a);
   };
   if (c->head_dim == 128) go(k_attn_bf16<128, MODE>);
   else go(k_attn_bf16<64, MODE>);
