@@ -34,23 +34,14 @@ constexpr int CS = CP * PAGE;   // slots per chunk
 constexpr int NT = 1024;        // threads per histogram and decision block
 constexpr int GT = CS / 4;      // threads per chunk (4 slots each)
 constexpr int CG = NT / GT;     // chunks in flight per block: thread t works on chunk t / GT of each round
-#ifndef TRIMKV_SEL_CPB
-#define TRIMKV_SEL_CPB 32
-#endif
-constexpr int CPB = TRIMKV_SEL_CPB;   // chunks per block
-constexpr int RND = CPB / CG;         // rounds of CG chunks
+constexpr int CPB = 32;         // chunks per block
+constexpr int RND = CPB / CG;   // rounds of CG chunks
 static_assert(CPB % CG == 0 && CPB <= NT, "chunk rounds");
-#ifndef TRIMKV_SEL_HCOPIES
-#define TRIMKV_SEL_HCOPIES 4
-#endif
-#ifndef TRIMKV_SEL_BSTRIDE
-#define TRIMKV_SEL_BSTRIDE 1
-#endif
 // Histogram layout per segment and pass: HC copies (block b adds into copy
-// b % HC) of NB bins BS words apart; readers sum the copies.
-constexpr int HC = TRIMKV_SEL_HCOPIES;
-constexpr int BS = TRIMKV_SEL_BSTRIDE;
-__host__ __device__ constexpr int copy_words(int nb) { return nb * BS + (HC > 1 ? 32 : 0); }
+// b % HC), 32 words apart, so that each copy's bins take only a quarter of
+// the device atomics; readers sum the copies.
+constexpr int HC = 4;
+__host__ __device__ constexpr int copy_words(int nb) { return nb + 32; }
 constexpr int HIST_WORDS = HC * (2 * copy_words(2048) + copy_words(1024));
 constexpr uint32_t SPIN_LIMIT = 1u << 26;
 
@@ -140,7 +131,7 @@ __device__ SegState state_after(const SelWs& w, int s, int pass) {
   for (int k = 0; k < per; ++k) {
     uint32_t v = 0;
 #pragma unroll
-    for (int r = 0; r < HC; ++r) v += g[r * copy_words(nb) + (threadIdx.x * per + k) * BS];
+    for (int r = 0; r < HC; ++r) v += g[r * copy_words(nb) + threadIdx.x * per + k];
     c[k] = v;
   }
   SegState st = w.seg[(size_t)pass * w.n_seg + s];
@@ -295,7 +286,7 @@ __global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __res
       for (int b = threadIdx.x; b < NB; b += NT) {
         const uint32_t v = lh[b];
         lh[b] = 0u;
-        if (v) atomicAdd(g + b * BS, v);
+        if (v) atomicAdd(g + b, v);
       }
       lds_barrier();
     }

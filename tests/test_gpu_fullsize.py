@@ -117,3 +117,178 @@ def test_full_size_pipeline(full_c2):
     assert np.all((dm >= 0) & (dm <= 1))
     assert np.max(np.abs(op - om)) <= OUT_TOL
     say("attention checked on", len(sample), "heads; modes agree on all", H)
+
+
+def test_full_size_batched_pipeline():
+    """The 16-sequence batched workload at full size (4096 KV heads of 16K
+    tokens, 16 per-sequence budgets): scores bit-exact for every head,
+    selection bit-exact for every segment against the oracle on the same
+    fp32 scores, compacted page table for every head, rows and both attention
+    modes on a sample of heads."""
+    w = synth.WORKLOADS["batched16_16k"]
+    t0 = time.time()
+    pc = synth.build_cache(w, workers=min(16, os.cpu_count() or 1))
+    say("generated", w.name, "in %.1f s" % (time.time() - t0))
+    H, G, D = pc.n_heads, w.group, w.head_dim
+    M = w.budget()
+    segs = w.seg_head_begin()
+    c = upload(pc)
+    seg = cuda(segs, np.int32)
+    score = torch.empty(pc.n_pages * 16, dtype=torch.float32, device="cuda")
+    tk.score(c, seg, cuda(np.full(w.n_seg, w.t, np.int32)), score)
+    keep = torch.empty(pc.n_pages * 16, dtype=torch.uint8, device="cuda")
+    kept = torch.empty(H, dtype=torch.int32, device="cuda")
+    tk.select_global(c, score, seg, cuda(np.full(w.n_seg, M, np.int64)), keep, kept)
+    q_bits = synth.queries(w)
+    q_dev = torch.from_numpy(np.ascontiguousarray(q_bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+    q64 = synth.bf16_bits_to_f32(q_bits).astype(np.float64)
+    scale = 1.0 / math.sqrt(D)
+    nq = H * G
+    out_m = torch.empty((nq, D), dtype=torch.float32, device="cuda")
+    drop_m = torch.empty(nq, dtype=torch.float32, device="cuda")
+    tk.decode_attn(c, q_dev, G, scale, out_m, drop_m, keep=keep)
+    total = M * w.n_seg
+    dst = tk.Cache.empty(H, -(-total // 16) + H, D, torch.bfloat16)
+    used = torch.zeros(1, dtype=torch.int64, device="cuda")
+    tk.compact(c, keep, 0, total, dst, used, kept=kept)
+    out_p = torch.empty((nq, D), dtype=torch.float32, device="cuda")
+    drop_p = torch.empty(nq, dtype=torch.float32, device="cuda")
+    tk.decode_attn(dst, q_dev, G, scale, out_p, drop_p)
+    torch.cuda.synchronize()
+    say("GPU pipeline done")
+
+    po, pi, ln = pc.page_off, pc.page_ids, pc.length
+    lnb = [ref.ln_beta(b) for b in ref.gather_heads(pc.beta, po, pi, ln)]
+    pos = ref.gather_heads(pc.pos, po, pi, ln)
+    got_scores = heads_from_plane(score.cpu().numpy(), po, ln)
+    for h in range(H):
+        assert np.array_equal(f32_bits(got_scores[h]), f32_bits(ref.score_f32(lnb[h], w.t, pos[h]))), ("score", h)
+    say("scores bit-exact")
+    want_keep, want_kept = ref.select_global(got_scores, segs, [M] * w.n_seg)
+    got_keep = heads_from_plane(keep.cpu().numpy(), po, ln)
+    for h in range(H):
+        assert np.array_equal(got_keep[h].astype(bool), want_keep[h]), ("keep", h)
+    assert np.array_equal(kept.cpu().numpy(), want_kept)
+    for s in range(w.n_seg):
+        assert int(want_kept[segs[s]:segs[s + 1]].sum()) == M
+    say("selection bit-exact in all", w.n_seg, "segments")
+
+    dpo, dpi, dln, dk, dv, dlnb, dpos = download_cache(dst)
+    wpo, _, wln = ref.compact_layout(want_kept, 0)
+    assert np.array_equal(dpo, wpo) and np.array_equal(dln, wln)
+    assert int(used.item()) == int(wpo[-1])
+    sample = list(range(0, H, 331)) + [H - 1]
+    flat_k, flat_v = pc.k.reshape(-1, D), pc.v.reshape(-1, D)
+    for h in sample:
+        src = ref.head_phys_slots(po, pi, ln, h)[want_keep[h]]
+        assert np.array_equal(ref.gather_heads(dk, dpo, dpi, dln)[h], flat_k[src]), ("k rows", h)
+        assert np.array_equal(ref.gather_heads(dv, dpo, dpi, dln)[h], flat_v[src]), ("v rows", h)
+        assert np.array_equal(ref.gather_heads(dpos, dpo, dpi, dln)[h], pos[h][want_keep[h]])
+    say("compaction checked")
+
+    om, dm, op, dp = (x.cpu().numpy() for x in (out_m, drop_m, out_p, drop_p))
+    K = [kv_f64(flat_k[ref.head_phys_slots(po, pi, ln, h)], pc.dtype) for h in sample]
+    V = [kv_f64(flat_v[ref.head_phys_slots(po, pi, ln, h)], pc.dtype) for h in sample]
+    qs = np.concatenate([q64[h * G:(h + 1) * G] for h in sample])
+    rows = np.concatenate([np.arange(h * G, (h + 1) * G) for h in sample])
+    kp = [want_keep[h] for h in sample]
+    wout, wdrop, _ = ref.decode_attn(K, V, qs, G, scale, keep=kp)
+    assert np.max(np.abs(om[rows] - wout)) <= OUT_TOL
+    assert np.max(np.abs(dm[rows] - wdrop)) <= DROP_TOL
+    wout2, _, _ = ref.decode_attn([k[m] for k, m in zip(K, kp)], [v[m] for v, m in zip(V, kp)], qs, G, scale)
+    assert np.max(np.abs(op[rows] - wout2)) <= OUT_TOL
+    assert np.all(dp == 0.0) and np.all(np.isfinite(op)) and np.all((dm >= 0) & (dm <= 1))
+    assert np.max(np.abs(op - om)) <= OUT_TOL
+    say("attention checked on", len(sample), "heads; modes agree on all", H)
+
+
+def test_full_size_long_context_mass_pipeline():
+    """The 128K-token workload at full size (288 KV heads): attention mass,
+    per-head top-1024 by mass, dropped-mass budgets, per-head top-b_h,
+    compaction and reference-mode attention.  Both selections and the
+    allocation are checked for every head against the oracle on the same
+    fp32 masses and fp64 kept sums; masses, rows and attention on a sample
+    of heads against the float64 oracle."""
+    w = synth.WORKLOADS["qwen8b_128k"]
+    t0 = time.time()
+    pc = synth.build_cache(w, workers=min(16, os.cpu_count() or 1))
+    say("generated", w.name, "in %.1f s" % (time.time() - t0))
+    H, G, D = pc.n_heads, w.group, w.head_dim
+    c = upload(pc)
+    q_bits = synth.queries(w)
+    q_dev = torch.from_numpy(np.ascontiguousarray(q_bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+    q64 = synth.bf16_bits_to_f32(q_bits).astype(np.float64)
+    scale = 1.0 / math.sqrt(D)
+    mass = torch.empty(pc.n_pages * 16, dtype=torch.float32, device="cuda")
+    lse = torch.empty(H * G, dtype=torch.float32, device="cuda")
+    tk.attn_mass(c, q_dev, G, scale, mass, lse)
+    segs = np.arange(H + 1, dtype=np.int32)
+    seg = cuda(segs)
+    keep = torch.empty(pc.n_pages * 16, dtype=torch.uint8, device="cuda")
+    kept = torch.empty(H, dtype=torch.int32, device="cuda")
+    ks = torch.empty(H, dtype=torch.float64, device="cuda")
+    tk.select_global(c, mass, seg, cuda(np.full(H, w.mass_topk), np.int64), keep, kept, ks)
+    keep1 = keep.cpu().numpy()
+    B = w.budget()
+    b = torch.empty(H, dtype=torch.int64, device="cuda")
+    tk.allocate(ks, c.length, B, b)
+    tk.select_global(c, mass, seg, b, keep, kept)
+    dst = tk.Cache.empty(H, -(-B // 16) + H, D, torch.bfloat16)
+    used = torch.zeros(1, dtype=torch.int64, device="cuda")
+    tk.compact(c, keep, 0, B, dst, used, kept=kept)
+    out = torch.empty((H * G, D), dtype=torch.float32, device="cuda")
+    dropped = torch.empty(H * G, dtype=torch.float32, device="cuda")
+    tk.decode_attn(dst, q_dev, G, scale, out, dropped, lse_ref=lse)
+    torch.cuda.synchronize()
+    say("GPU pipeline done")
+
+    po, pi, ln = pc.page_off, pc.page_ids, pc.length
+    gm = heads_from_plane(mass.cpu().numpy(), po, ln)
+    # masses and full LSE on sampled heads (float64 oracle)
+    sample = [0, 97, 200, H - 1]
+    flat_k, flat_v = pc.k.reshape(-1, D), pc.v.reshape(-1, D)
+    K = [kv_f64(flat_k[ref.head_phys_slots(po, pi, ln, h)], pc.dtype) for h in sample]
+    V = [kv_f64(flat_v[ref.head_phys_slots(po, pi, ln, h)], pc.dtype) for h in sample]
+    qs = np.concatenate([q64[h * G:(h + 1) * G] for h in sample])
+    rows = np.concatenate([np.arange(h * G, (h + 1) * G) for h in sample])
+    wm, wlse = ref.attn_mass(K, qs, G, scale)
+    for i, h in enumerate(sample):
+        assert np.all(np.abs(gm[h] - wm[i]) <= 1e-5 * wm[i] + 1e-12), ("mass", h)
+    assert np.max(np.abs(lse.cpu().numpy()[rows] - wlse)) <= 1e-4
+    say("mass checked on", len(sample), "heads")
+    # selections and allocation, every head, on the same fp32 masses
+    want1, _ = ref.select_global(gm, segs, [w.mass_topk] * H)
+    got1 = heads_from_plane(keep1, po, ln)
+    for h in range(H):
+        assert np.array_equal(got1[h].astype(bool), want1[h]), ("top-mass keep", h)
+    ksum = ks.cpu().numpy()
+    for h in range(H):
+        want = float(np.sum(gm[h][want1[h]].astype(np.float64)))
+        assert abs(ksum[h] - want) <= 1e-12 * max(1.0, abs(want)), ("keptsum", h)
+    bh = b.cpu().numpy()
+    wb, _ = ref.allocate(ksum, ln, B)
+    assert bh.sum() == B and np.all(bh <= ln) and np.max(np.abs(bh - wb)) <= 1
+    want2, want_kept2 = ref.select_global(gm, segs, bh)
+    got2 = heads_from_plane(keep.cpu().numpy(), po, ln)
+    for h in range(H):
+        assert np.array_equal(got2[h].astype(bool), want2[h]), ("budget keep", h)
+    assert np.array_equal(kept.cpu().numpy(), want_kept2)
+    say("selections and allocation checked on all", H, "heads")
+    # compaction: page table for every head, rows on the sample
+    dpo, dpi, dln, dk, dv, _, dpos = download_cache(dst)
+    wpo, _, wln = ref.compact_layout(want_kept2, 0)
+    assert np.array_equal(dpo, wpo) and np.array_equal(dln, wln)
+    pos = ref.gather_heads(pc.pos, po, pi, ln)
+    for h in sample:
+        src = ref.head_phys_slots(po, pi, ln, h)[want2[h]]
+        assert np.array_equal(ref.gather_heads(dk, dpo, dpi, dln)[h], flat_k[src]), ("k rows", h)
+        assert np.array_equal(ref.gather_heads(dpos, dpo, dpi, dln)[h], pos[h][want2[h]])
+    # reference-mode attention on the sample
+    kp = [want2[h] for h in sample]
+    wout, wdrop, _ = ref.decode_attn([k[m] for k, m in zip(K, kp)], [v[m] for v, m in zip(V, kp)], qs, G, scale,
+                                     lse_ref=wlse)
+    o, dr = out.cpu().numpy(), dropped.cpu().numpy()
+    assert np.max(np.abs(o[rows] - wout)) <= OUT_TOL
+    assert np.max(np.abs(dr[rows] - wdrop)) <= DROP_TOL
+    assert np.all(np.isfinite(o)) and np.all((dr >= -DROP_TOL) & (dr <= 1 + DROP_TOL))
+    say("compaction and attention checked on", len(sample), "heads")
