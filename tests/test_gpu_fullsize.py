@@ -17,7 +17,7 @@ import torch
 import synth
 from oracle import reference as ref
 from retention_scored_decode_amd import trimkv as tk
-from gpu_helpers import DROP_TOL, OUT_TOL, cuda, download_cache, f32_bits, heads_from_plane, kv_f64, upload
+from gpu_helpers import DROP_TOL, OUT_TOL, cuda, download_cache, f32_bits, heads_from_plane, kv_dev, kv_f64, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -292,3 +292,94 @@ def test_full_size_long_context_mass_pipeline():
     assert np.max(np.abs(dr[rows] - wdrop)) <= DROP_TOL
     assert np.all(np.isfinite(o)) and np.all((dr >= -DROP_TOL) & (dr <= 1 + DROP_TOL))
     say("compaction and attention checked on", len(sample), "heads")
+
+
+def test_full_size_streaming_steps():
+    """The streaming workload at full size (112 KV heads, 64K-token prefill,
+    GQA 7, fixed budget of 458,752 entries, one reserve slot per head): the
+    first three generated steps (append, score, select, mask-mode attention,
+    compaction into the other pool).  Selection and the compacted page table,
+    positions and ln(beta) are checked for every head at every step; K/V rows
+    and attention on a sample of heads."""
+    w = synth.WORKLOADS["stream_gqa7"]
+    t0 = time.time()
+    pc = synth.build_cache(w, workers=min(16, os.cpu_count() or 1))
+    say("generated", w.name, "in %.1f s" % (time.time() - t0))
+    H, G, D = pc.n_heads, w.group, w.head_dim
+    M = w.budget()
+    scale = 1.0 / math.sqrt(D)
+    cur = upload(pc)
+    cap = -(-(M + H) // 16) + H
+    pools = [tk.Cache.empty(H, cap, D, torch.bfloat16) for _ in range(2)]
+    po, pi, ln = pc.page_off, pc.page_ids, pc.length
+    sample = [0, 45, H - 1]
+    flat_k, flat_v = pc.k.reshape(-1, D), pc.v.reshape(-1, D)
+    # oracle state: ln(beta) and positions of every head; K/V rows of the sample
+    st_lnb = [ref.ln_beta(b) for b in ref.gather_heads(pc.beta, po, pi, ln)]
+    st_pos = ref.gather_heads(pc.pos, po, pi, ln)
+    st_k = {h: flat_k[ref.head_phys_slots(po, pi, ln, h)] for h in sample}
+    st_v = {h: flat_v[ref.head_phys_slots(po, pi, ln, h)] for h in sample}
+    seg = cuda(np.array([0, H], np.int32))
+    bud = cuda(np.array([M], np.int64))
+    for s in range(1, 4):
+        t = w.ctx + s
+        beta, kn, vn, qn = synth.stream_step(w, s)
+        t_dev = cuda(np.array([t], np.int32))
+        tk.append(cur, kv_dev(kn, "bf16"), kv_dev(vn, "bf16"), cuda(beta, np.float32), t_dev)
+        score = torch.empty(cur.n_pages * 16, dtype=torch.float32, device="cuda")
+        tk.score(cur, seg, t_dev, score)
+        keep = torch.empty(cur.n_pages * 16, dtype=torch.uint8, device="cuda")
+        kept = torch.empty(H, dtype=torch.int32, device="cuda")
+        tk.select_global(cur, score, seg, bud, keep, kept)
+        q_dev = kv_dev(qn, "bf16")
+        out = torch.empty((H * G, D), dtype=torch.float32, device="cuda")
+        dropped = torch.empty(H * G, dtype=torch.float32, device="cuda")
+        tk.decode_attn(cur, q_dev, G, scale, out, dropped, keep=keep)
+        dst = pools[s % 2]
+        used = torch.zeros(1, dtype=torch.int64, device="cuda")
+        tk.compact(cur, keep, 1, M, dst, used, kept=kept)
+        torch.cuda.synchronize()
+        # oracle step: append, score, select
+        lnb_new = ref.ln_beta(beta)
+        for h in range(H):
+            st_lnb[h] = np.append(st_lnb[h], lnb_new[h])
+            st_pos[h] = np.append(st_pos[h], np.int32(t - 1))
+        for h in sample:
+            st_k[h] = np.concatenate([st_k[h], kn[h:h + 1]])
+            st_v[h] = np.concatenate([st_v[h], vn[h:h + 1]])
+        scores = [ref.score_f32(st_lnb[h], t, st_pos[h]) for h in range(H)]
+        wkeep, wkept = ref.select_global(scores, [0, H], [M])
+        cpo, cpi, cln = (x.cpu().numpy() for x in (cur.page_off, cur.page_ids, cur.length))
+        got = heads_from_plane(keep.cpu().numpy(), cpo, cln)
+        for h in range(H):
+            assert np.array_equal(got[h].astype(bool), wkeep[h]), (s, "keep", h)
+        assert np.array_equal(kept.cpu().numpy(), wkept), s
+        # attention on the sample (float64 oracle over the step's full cache)
+        q64 = synth.bf16_bits_to_f32(qn).astype(np.float64)
+        qs = np.concatenate([q64[h * G:(h + 1) * G] for h in sample])
+        rows = np.concatenate([np.arange(h * G, (h + 1) * G) for h in sample])
+        K = [kv_f64(st_k[h], "bf16") for h in sample]
+        V = [kv_f64(st_v[h], "bf16") for h in sample]
+        wout, wdrop, _ = ref.decode_attn(K, V, qs, G, scale, keep=[wkeep[h] for h in sample])
+        o, dr = out.cpu().numpy(), dropped.cpu().numpy()
+        assert np.max(np.abs(o[rows] - wout)) <= OUT_TOL, s
+        assert np.max(np.abs(dr[rows] - wdrop)) <= DROP_TOL, s
+        # compaction: every head's page table, positions and ln(beta); rows on the sample
+        st_lnb = [st_lnb[h][wkeep[h]] for h in range(H)]
+        st_pos = [st_pos[h][wkeep[h]] for h in range(H)]
+        for h in sample:
+            st_k[h] = st_k[h][wkeep[h]]
+            st_v[h] = st_v[h][wkeep[h]]
+        dpo, dpi, dln, dk, dv, dlnb, dpos = download_cache(dst)
+        wpo, _, wln = ref.compact_layout(wkept, 1)
+        assert np.array_equal(dpo, wpo) and np.array_equal(dln, wln), s
+        gpos, glnb = ref.gather_heads(dpos, dpo, dpi, dln), ref.gather_heads(dlnb, dpo, dpi, dln)
+        for h in range(H):
+            assert np.array_equal(gpos[h], st_pos[h]), (s, "pos", h)
+            assert np.array_equal(f32_bits(glnb[h]), f32_bits(st_lnb[h])), (s, "lnb", h)
+        gk, gv = ref.gather_heads(dk, dpo, dpi, dln), ref.gather_heads(dv, dpo, dpi, dln)
+        for h in sample:
+            assert np.array_equal(gk[h], st_k[h]) and np.array_equal(gv[h], st_v[h]), (s, "rows", h)
+        say("step", s, "checked: selection and metadata on all", H, "heads; rows and attention on", len(sample))
+        cur = dst
+    assert tk.validate_cache(cur, cuda(np.array([w.ctx + 4], np.int32))) == tk.OK
