@@ -370,6 +370,32 @@ def test_subset_error():
     assert abs(e[0] - np.linalg.norm(mu[0] - V[0][4])) < 1e-14
 
 
+def test_subset_error_decomposition():
+    """The dense output splits as mu = (1 - d) m_A + d m_D (d the dropped
+    mass, m_D the output renormalised over the dropped keys), so
+    e_s(A) = d ||m_A - m_D||.  m_A, m_D and d come from direct sums (brute
+    force), not from the oracle.  Empty A: m_A = 0, so e = ||mu||."""
+    rng = np.random.default_rng(31)
+    for trial in range(40):
+        n, d = int(rng.integers(2, 14)), int(rng.integers(1, 6))
+        K = [rng.standard_normal((n, d)) * 2]
+        V = [rng.standard_normal((n, d))]
+        q = rng.standard_normal((1, d))
+        keep = rng.random(n) < 0.5
+        keep[int(rng.integers(0, n))] = True
+        e = ref.subset_error(K, V, q, 1, 0.7, [keep])[0]
+        oa, dm = brute.attention_direct(K[0].tolist(), V[0].tolist(), q[0].tolist(), 0.7, keep.tolist())
+        if keep.all():
+            assert e < 1e-14
+            continue
+        od, _ = brute.attention_direct(K[0].tolist(), V[0].tolist(), q[0].tolist(), 0.7, (~keep).tolist())
+        want = dm * math.sqrt(math.fsum((x - y) ** 2 for x, y in zip(oa, od)))
+        assert abs(e - want) <= 1e-13 * max(1.0, want), trial
+    mu, _ = brute.attention_direct(K[0].tolist(), V[0].tolist(), q[0].tolist(), 0.7, [True] * len(K[0]))
+    e0 = ref.subset_error(K, V, q, 1, 0.7, [np.zeros(len(K[0]), bool)])[0]
+    assert abs(e0 - math.sqrt(math.fsum(x * x for x in mu))) < 1e-13
+
+
 # --------------------------------------------------------------------------
 # a5/a6: attention mass and allocation (ContourKV section 3)
 # --------------------------------------------------------------------------
