@@ -285,6 +285,30 @@ def main():
     t = {s: float(np.mean(v)) for s, v in per.items()}
     kt = {s: float(np.mean(v)) for s, v in kper.items()}
 
+    # e_s(A) output (ContourKV section 1): mask-mode attention over the source
+    # cache with this step's keep plane that also forms the dense output and
+    # || mu - m_A ||; timed on its own after the steps, not part of a step
+    ws_err = tk.workspace(tk.OP_DECODE_ERR, src, 0, G)
+    mu = torch.empty((nq, D), dtype=torch.float32, device=dev)
+    err = torch.empty(nq, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        tk.decode_attn_err(src, q, G, scale, keep, out_m, drop_m, err, mu=mu, ws=ws_err)
+    e_t, e_k = [], []
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ka.record()
+        kb.record()
+        torch.cuda.synchronize()
+        tk.profile_next(ka, kb)
+        a.record()
+        tk.decode_attn_err(src, q, G, scale, keep, out_m, drop_m, err, mu=mu, ws=ws_err)
+        b.record()
+        torch.cuda.synchronize()
+        e_t.append(a.elapsed_time(b) * 1e-3)
+        e_k.append(ka.elapsed_time(kb) * 1e-3)
+    assert bool(torch.isfinite(err).all())
+
     # sanity of the step's results (not timed)
     kept_np = kept.cpu().numpy()
     if w.n_seg == 1:
@@ -328,6 +352,14 @@ def main():
         stage_out[s] = {"us": round(t[s] * 1e6, 2), "algo_bytes": algo[s], "GBps": round(gbs, 1),
                         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "main_kernel": STAGE_KERNEL[s][0],
                         "main_kernel_us": round(kt[s] * 1e6, 2)}
+    err_algo = 512 * N + small + nq * D * 4
+    err_t, err_kt = float(np.mean(e_t)), float(np.mean(e_k))
+    extras = {"attend_err": {"us": round(err_t * 1e6, 2), "algo_bytes": err_algo,
+                             "GBps": round(err_algo / err_t / 1e9, 1),
+                             "frac_hbm": round(err_algo / err_t / 1e9 / HBM_PEAK_GBS, 4),
+                             "main_kernel": "k_attn_bf16<128, 3>", "main_kernel_us": round(err_kt * 1e6, 2),
+                             "what": "mask-mode attention over every entry plus the dense output and "
+                                     "||mu - m_A|| per query head; outside the timed step"}}
     dom = max(stages, key=lambda s: t[s])
     sc_t = t["select"] + t["compact"]
     value = algo["decode"] / t["decode"] / 1e9
@@ -350,6 +382,7 @@ def main():
         "select_compact_GBps": round((algo["select"] + algo["compact"]) / sc_t / 1e9, 1),
         "decode_cold_GBps": round(algo["decode"] / t_cold / 1e9, 1),
         "stages": stage_out,
+        "extras": extras,
         "roofline": {"stage": dom, "kernel": STAGE_KERNEL[dom][0], "bound": "hbm",
                      "achieved": round(algo[dom] / kt[dom] / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(algo[dom] / kt[dom] / 1e9 / HBM_PEAK_GBS, 4),

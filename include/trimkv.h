@@ -87,7 +87,8 @@ enum {
   TRIMKV_OP_COMPACT = 2,
   TRIMKV_OP_DECODE_ATTN = 3,
   TRIMKV_OP_ATTN_MASS = 4,
-  TRIMKV_OP_VALIDATE = 5
+  TRIMKV_OP_VALIDATE = 5,
+  TRIMKV_OP_DECODE_ERR = 6
 };
 
 /*
@@ -195,6 +196,28 @@ int trimkv_compact(const trimkv_cache_t* src, const uint8_t* keep, const int32_t
 int trimkv_decode_attn(const trimkv_cache_t* cache, const uint8_t* keep, const float* lse_ref,
                        const void* q, int32_t group, float scale, float* out, float* dropped,
                        float* lse_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * trimkv_decode_attn_err -- mask-mode decode attention that also measures
+ * what the forced weights cost: e_s(A) = || mu - m_A ||_2 per query head.
+ * ContourKV page, section 1 (theoretical analysis): mu is the dense
+ * attention output over every valid entry U of the head, m_A the output
+ * renormalised over the kept set A; the norm is the Euclidean norm over the
+ * head_dim output components (the page leaves the norm unnamed).
+ *   keep:    device uint8 CSR plane (16-byte aligned), A = {j : keep[j] == 1}
+ *   out, dropped: as trimkv_decode_attn with this keep plane (out = m_A)
+ *   mu:      device fp32 [n_heads * group][head_dim] or NULL: the dense output
+ *            (0 for a head without valid entries)
+ *   err:     device fp32 [n_heads * group]: || mu - m_A ||_2, with m_A = 0 when
+ *            A is empty (so err = || mu ||)
+ *   ws:      trimkv_workspace_size(TRIMKV_OP_DECODE_ERR, cache, 0, group) bytes
+ * Reads every V row (the mask mode reads only the kept ones).  bf16 caches
+ * only (EUNSUPPORTED for fp32).
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE.
+ */
+int trimkv_decode_attn_err(const trimkv_cache_t* cache, const uint8_t* keep, const void* q, int32_t group,
+                           float scale, float* out, float* dropped, float* mu, float* err, void* ws,
+                           size_t ws_bytes, void* stream);
 
 /*
  * trimkv_attn_mass -- query-aware attention mass of every cached key.

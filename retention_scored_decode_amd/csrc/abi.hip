@@ -126,6 +126,7 @@ size_t trimkv_workspace_size(int op, const trimkv_cache_t* c, int32_t n_seg, int
     case TRIMKV_OP_DECODE_ATTN: return (group >= 1 && group <= 16) ? attn_ws_layout(c, group).total : 0;
     case TRIMKV_OP_ATTN_MASS: return (group >= 1 && group <= 16) ? mass_ws_layout(c, group).total : 0;
     case TRIMKV_OP_VALIDATE: return 256;
+    case TRIMKV_OP_DECODE_ERR: return (group >= 1 && group <= 16) ? err_ws_layout(c, group).total : 0;
     default: return 0;
   }
 }
@@ -192,6 +193,19 @@ int trimkv_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float
   if ((rc = ws_check(ws, ws_bytes, attn_ws_layout(c, group).total))) return rc;
   if (c->n_heads == 0) return TRIMKV_OK;
   return launch_decode_attn(c, keep, lse_ref, q, group, scale, out, dropped, lse_out, ws, S(stream));
+}
+
+int trimkv_decode_attn_err(const trimkv_cache_t* c, const uint8_t* keep, const void* q, int32_t group, float scale,
+                           float* out, float* dropped, float* mu, float* err, void* ws, size_t ws_bytes,
+                           void* stream) {
+  int rc;
+  if (!cache_shape_ok(c, &rc)) return rc;
+  if (group < 1 || group > 16 || c->dtype != TRIMKV_BF16) return TRIMKV_EUNSUPPORTED;
+  if (!keep || !q || !out || !dropped || !err || !table_ok(c) || !pools_ok(c) || ((uintptr_t)keep & 15))
+    return TRIMKV_EINVAL;
+  if ((rc = ws_check(ws, ws_bytes, err_ws_layout(c, group).total))) return rc;
+  if (c->n_heads == 0) return TRIMKV_OK;
+  return launch_decode_attn_err(c, keep, q, group, scale, out, dropped, mu, err, ws, S(stream));
 }
 
 int trimkv_attn_mass(const trimkv_cache_t* c, const void* q, int32_t group, float scale, float* mass,

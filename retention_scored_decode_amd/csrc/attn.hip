@@ -45,13 +45,14 @@ constexpr int NTA = 256;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
-enum { A_PLAIN = 0, A_MASK = 1, A_LOGITS = 2 };
+enum { A_PLAIN = 0, A_MASK = 1, A_LOGITS = 2, A_ERR = 3 };
 
 struct AttnWs {
   int32_t* item_off;   // [H + 1]          (fp32 work list)
   int4* item;          // [Tmax + 4]       (fp32 work list: head, first CSR page, valid entries, pages)
   float* stats;        // [Smax][G][3]     partials: base-2 running max, kept sum, dropped sum
   float* acc;          // [Smax][G][D]     partials: unnormalised outputs
+  float* acc2;         // [Smax][G][D]     partials of the dropped keys (error mode), else null
   float* lse2;         // [H * G] base-2 LSE (mass op)
   float* logits;       // [G][n_pages * 16] (mass op)
 };
@@ -76,6 +77,8 @@ struct AttnArgs {
   float* out;
   float* dropped;
   float* lse_out;
+  float* mu;             // error mode: dense output over every key, or null
+  float* err;            // error mode: || mu - out ||_2 per query head
 };
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -191,35 +194,63 @@ __global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
     }
   }
   if (!with_out) return;
-  // output: SPLIT threads per dimension, each over every SPLIT-th partial
+  // output: SPLIT threads per dimension, each over every SPLIT-th partial;
+  // with w.acc2 (error mode) the dropped keys' sums are merged alongside
   constexpr int SPLIT = NT / D;
   constexpr int UN = 8;
+  const bool err = w.acc2 != nullptr;   // block-uniform
   const int d = t % D, part = t / D;
-  float s = 0.f;
+  float s = 0.f, s2 = 0.f;
   for (int it0 = b; it0 < e; it0 += NT) {
     const int n = min(NT, e - it0);
     if (t < n) sw[t] = (M != -INFINITY && has(it0 + t)) ? exp2f(stat(it0 + t, 0) - M) : 0.f;
     lds_barrier();
     for (int j0 = part; j0 < n; j0 += SPLIT * UN) {
-      float v[UN], wt[UN];
+      float v[UN], v2[UN], wt[UN];
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
         const int j = j0 + u * SPLIT;
         wt[u] = j < n ? sw[j] : 0.f;
-        v[u] = wt[u] != 0.f ? w.acc[((size_t)(it0 + j + add) * G + g) * D + d] : 0.f;
+        const size_t at = ((size_t)(it0 + j + add) * G + g) * D + d;
+        v[u] = wt[u] != 0.f ? w.acc[at] : 0.f;
+        v2[u] = err && wt[u] != 0.f ? w.acc2[at] : 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < UN; ++u) s += v[u] * wt[u];
+      for (int u = 0; u < UN; ++u) {
+        s += v[u] * wt[u];
+        s2 += v2[u] * wt[u];
+      }
     }
     lds_barrier();
   }
   sacc[t] = s;
+  if (err) sw[t] = s2;   // sw is free after the last batch
   lds_barrier();
   if (part == 0) {
-    float tot = sacc[d];
+    float tot = sacc[d], tot2 = 0.f;
 #pragma unroll
     for (int q = 1; q < SPLIT; ++q) tot += sacc[q * D + d];
-    a.out[((size_t)h * G + g) * D + d] = la > 0.f ? tot / la : 0.f;
+    const float mA = la > 0.f ? tot / la : 0.f;
+    a.out[((size_t)h * G + g) * D + d] = mA;
+    if (err) {
+      tot2 = sw[d];
+#pragma unroll
+      for (int q = 1; q < SPLIT; ++q) tot2 += sw[q * D + d];
+      // dense output over every key: kept and dropped sums share the maximum
+      const float mu = la + ld > 0.f ? (tot + tot2) / (la + ld) : 0.f;
+      if (a.mu) a.mu[((size_t)h * G + g) * D + d] = mu;
+      sacc[d] = (mu - mA) * (mu - mA);
+    }
+  }
+  if (err) {   // e_s(A) = || mu - m_A ||_2, fixed-order sum over the D dimensions
+    lds_barrier();
+    if (t < WAVE) {
+      float q2 = 0.f;
+      for (int k = t; k < D; k += WAVE) q2 += sacc[k];
+#pragma unroll
+      for (int k = WAVE / 2; k > 0; k >>= 1) q2 += __shfl_xor(q2, k, WAVE);
+      if (t == 0) a.err[(size_t)h * G + g] = sqrtf(q2);
+    }
   }
 }
 
@@ -297,6 +328,8 @@ __device__ __forceinline__ uint32_t pick4(u32x4 v, int q) {
 // ---------------------------------------------------------------------------
 // bf16 K/V.  MODE: A_PLAIN (every valid key kept), A_MASK (keep plane;
 // dropped keys only enter the dropped sum and their V rows are not read),
+// A_ERR (as A_MASK, and the dropped keys' P V goes to a second accumulator,
+// so that the merge has the dense output as well; every V row is read),
 // A_LOGITS (base-2 logits of every valid key and (max, sum) partials).
 //
 // Wave w of W streams CSR pages [w P / W, (w + 1) P / W) and, per head
@@ -322,6 +355,8 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
   constexpr int KU = D / 32;    // QK MFMAs per page
   constexpr int NV = D / 16;    // PV output column blocks
   constexpr bool LOGITS = MODE == A_LOGITS;
+  constexpr bool MASKED = MODE == A_MASK || MODE == A_ERR;
+  constexpr bool ERR = MODE == A_ERR;
   // load instructions per page; pages in flight are tracked by vmcnt (the
   // logits mode also stores inside the loop and keeps a single page in flight)
   constexpr int PER_PAGE = LOGITS ? 0 : 2 * LPP;
@@ -391,9 +426,11 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
     }
     float m = -INFINITY, la = 0.f, ld = 0.f;
     float nm = INFINITY;   // -m, or +inf while m = -inf (every finite logit then forces an update)
-    float4_t acc[LOGITS ? 1 : NV];
+    float4_t acc[LOGITS ? 1 : NV], acc2[ERR ? NV : 1];
 #pragma unroll
     for (int n = 0; n < (LOGITS ? 1 : NV); ++n) acc[n] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < (ERR ? NV : 1); ++n) acc2[n] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
     // page i's loads; phys = its physical page, kw4 = its 16 keep bytes (mask mode)
     auto dma = [&](auto B, int i, int64_t phys, u32x4 kw4) {
@@ -405,7 +442,7 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
         __builtin_amdgcn_global_load_lds((gptr)(kpage + gk[u]), (lptr)(&lds_k[wu][buf][64 * u]), 16, 0, CPOL_NT);
       if (!LOGITS) {
         const bool full = (i + 1) * PAGE <= nv;   // wave-uniform
-        if (MODE == A_PLAIN && full) {
+        if ((MODE == A_PLAIN || ERR) && full) {
 #pragma unroll
           for (int u = 0; u < LPP; ++u)
             __builtin_amdgcn_global_load_lds((gptr)(vpage + gv[u]), (lptr)(&lds_v[wu][buf][64 * u]), 16, 0, CPOL_NT);
@@ -464,6 +501,10 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
           const float aj = __shfl(alpha, 4 * r + j, WAVE);
 #pragma unroll
           for (int n = 0; n < NV; ++n) acc[n][j] *= aj;
+          if (ERR) {
+#pragma unroll
+            for (int n = 0; n < NV; ++n) acc2[n][j] *= aj;
+          }
         }
       }
     }
@@ -485,13 +526,15 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
       la += (pj[0] + pj[1]) + (pj[2] + pj[3]);
       return;
     }
-    if (MODE == A_MASK) {
+    float pd[4] = {0.f, 0.f, 0.f, 0.f};   // weights of the dropped keys (error mode)
+    if (MASKED) {
       float sk = 0.f, sd = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bool kept = ((kwr >> (8 * j)) & 0xFFu) && (full || i0 + j < nv);
         sk += kept ? pj[j] : 0.f;
         sd += kept ? 0.f : pj[j];
+        if (ERR) pd[j] = kept ? 0.f : pj[j];
         if (!kept) pj[j] = 0.f;
       }
       la += sk;
@@ -510,6 +553,18 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vop[n], acc[n], 0, 0, 0);
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vop[n], acc[n], 0, 0, 0);
     }
+    if (ERR) {   // dropped keys: same split, second accumulator
+      const short4_t dhi = pack_hi(pd);
+      float drem[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) drem[j] = pd[j] - __uint_as_float(__float_as_uint(pd[j]) & 0xFFFF0000u);
+      const short4_t dlo = pack_rne(drem[0], drem[1], drem[2], drem[3]);
+#pragma unroll
+      for (int n = 0; n < NV; ++n) {
+        acc2[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dhi, vop[n], acc2[n], 0, 0, 0);
+        acc2[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dlo, vop[n], acc2[n], 0, 0, 0);
+      }
+    }
   };
 
 
@@ -520,7 +575,7 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
     // The page id and keep bytes that a step needs are read one step earlier
     // (scalar loads), so no load is issued behind a dependent table read.
     const u32x4 all_kept = (u32x4){~0u, ~0u, ~0u, ~0u};
-    auto keep4 = [&](int i) -> u32x4 { return MODE == A_MASK ? ckeep[i] : all_kept; };
+    auto keep4 = [&](int i) -> u32x4 { return MASKED ? ckeep[i] : all_kept; };
     int64_t id_n = cnt > 2 ? cids[page0 + 2] : 0;        // page of the next load (i + 2)
     u32x4 kwd_n = cnt > 2 ? keep4(2) : all_kept;         // its keep bytes
     u32x4 kwm_n = keep4(0);                              // keep bytes of the next page computed
@@ -578,6 +633,11 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
           float* dst = w.acc + (part * G + g) * D + col;
 #pragma unroll
           for (int n = 0; n < NV; ++n) dst[16 * n] = acc[n][j];
+          if (ERR) {
+            float* dst2 = w.acc2 + (part * G + g) * D + col;
+#pragma unroll
+            for (int n = 0; n < NV; ++n) dst2[16 * n] = acc2[n][j];
+          }
         }
       }
     }
@@ -709,14 +769,15 @@ __global__ void __launch_bounds__(256) k_mass(const int32_t* __restrict__ page_o
 }
 
 
-AttnWs carve(const trimkv_cache_t* c, int group, void* ws, bool mass) {
-  WsLayout L = mass ? mass_ws_layout(c, group) : attn_ws_layout(c, group);
+AttnWs carve(const trimkv_cache_t* c, int group, void* ws, bool mass, bool err = false) {
+  WsLayout L = mass ? mass_ws_layout(c, group) : err ? err_ws_layout(c, group) : attn_ws_layout(c, group);
   char* b = (char*)ws;
   AttnWs w;
   w.item_off = (int32_t*)(b + L.off[0]);
   w.item = (int4*)(b + L.off[1]);
   w.stats = (float*)(b + L.off[2]);
   w.acc = (float*)(b + L.off[3]);
+  w.acc2 = err ? (float*)(b + L.off[4]) : nullptr;
   w.lse2 = mass ? (float*)(b + L.off[4]) : nullptr;
   w.logits = mass ? (float*)(b + L.off[5]) : nullptr;
   return w;
@@ -746,6 +807,7 @@ int launch_main(const trimkv_cache_t* c, AttnArgs& a, hipStream_t st) {
   constexpr bool LOGITS = MODE == A_LOGITS;
   const dim3 blk(NT);
   if (c->dtype == TRIMKV_F32) {
+    if (MODE == A_ERR) return TRIMKV_EUNSUPPORTED;
     const int64_t T = max_chunks(c, CHA_F32);   // bound on the number of items
     if (c->head_dim == 128) hipLaunchKernelGGL((k_attn_f32<128, LOGITS>), dim3((unsigned)T), blk, 0, st, a);
     else hipLaunchKernelGGL((k_attn_f32<64, LOGITS>), dim3((unsigned)T), blk, 0, st, a);
@@ -778,6 +840,12 @@ WsLayout attn_ws_layout(const trimkv_cache_t* c, int group) {
   return L;
 }
 
+WsLayout err_ws_layout(const trimkv_cache_t* c, int group) {
+  WsLayout L = attn_ws_layout(c, group);
+  L.add(partial_slots(c) * group * (int64_t)c->head_dim * 4);   // dropped keys' partial outputs
+  return L;
+}
+
 WsLayout mass_ws_layout(const trimkv_cache_t* c, int group) {
   const int64_t S = partial_slots(c);
   const int64_t T = c->dtype == TRIMKV_F32 ? max_chunks(c, CHA_F32) : 0;
@@ -803,6 +871,20 @@ int launch_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float
              c->n_pages * PAGE, CHA_F32, 0, w, lse_ref, out, dropped, lse_out};
   prof_begin(st);
   int rc = keep ? launch_main<A_MASK>(c, a, st) : launch_main<A_PLAIN>(c, a, st);
+  prof_end(st);
+  if (rc) return rc;
+  if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(c->n_heads * group), dim3(NT), 0, st, a, 1);
+  else hipLaunchKernelGGL(k_attn_merge<64>, dim3(c->n_heads * group), dim3(NT), 0, st, a, 1);
+  return check_launch();
+}
+
+int launch_decode_attn_err(const trimkv_cache_t* c, const uint8_t* keep, const void* q, int group, float scale,
+                           float* out, float* dropped, float* mu, float* err, void* ws, hipStream_t st) {
+  AttnWs w = carve(c, group, ws, false, true);
+  AttnArgs a{c->page_off, c->page_ids, c->len, c->k, c->v, keep, q, c->n_heads, group, scale * LOG2E,
+             c->n_pages * PAGE, CHA_F32, 0, w, nullptr, out, dropped, nullptr, mu, err};
+  prof_begin(st);
+  int rc = launch_main<A_ERR>(c, a, st);
   prof_end(st);
   if (rc) return rc;
   if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(c->n_heads * group), dim3(NT), 0, st, a, 1);

@@ -32,6 +32,7 @@ struct WsLayout {
 inline int64_t max_chunks(const trimkv_cache_t* c, int cp) { return c->n_pages / cp + c->n_heads + 1; }
 
 WsLayout select_ws_layout(const trimkv_cache_t* c, int n_seg);
+WsLayout err_ws_layout(const trimkv_cache_t* c, int group);
 WsLayout compact_ws_layout(const trimkv_cache_t* c);
 WsLayout attn_ws_layout(const trimkv_cache_t* c, int group);
 WsLayout mass_ws_layout(const trimkv_cache_t* c, int group);
@@ -46,6 +47,8 @@ int launch_select(const trimkv_cache_t* c, const float* score, int n_seg, const 
                   hipStream_t st);
 int launch_compact(const trimkv_cache_t* src, const uint8_t* keep, const int32_t* kept, int reserve,
                    int64_t max_kept_total, trimkv_cache_t* dst, int64_t* pages_used, void* ws, hipStream_t st);
+int launch_decode_attn_err(const trimkv_cache_t* c, const uint8_t* keep, const void* q, int group, float scale,
+                           float* out, float* dropped, float* mu, float* err, void* ws, hipStream_t st);
 int launch_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float* lse_ref, const void* q,
                        int group, float scale, float* out, float* dropped, float* lse_out, void* ws,
                        hipStream_t st);

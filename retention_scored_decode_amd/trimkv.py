@@ -18,10 +18,10 @@ LIB_PATH = os.path.join(_HERE, "libtrimkv.so")
 PAGE = 16
 F32, BF16 = 0, 1
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ECAPACITY, EHIP, EINVARIANT = 0, -1, -2, -3, -4, -5, -6
-OP_SCORE, OP_SELECT, OP_COMPACT, OP_DECODE_ATTN, OP_ATTN_MASS, OP_VALIDATE = range(6)
+OP_SCORE, OP_SELECT, OP_COMPACT, OP_DECODE_ATTN, OP_ATTN_MASS, OP_VALIDATE, OP_DECODE_ERR = range(7)
 
 EXPORTS = ["trimkv_log_beta", "trimkv_score", "trimkv_select_global", "trimkv_compact",
-           "trimkv_decode_attn", "trimkv_attn_mass", "trimkv_allocate", "trimkv_append",
+           "trimkv_decode_attn", "trimkv_decode_attn_err", "trimkv_attn_mass", "trimkv_allocate", "trimkv_append",
            "trimkv_workspace_size", "trimkv_validate_cache", "trimkv_strerror", "trimkv_profile_next"]
 
 
@@ -56,6 +56,7 @@ def lib():
             "trimkv_select_global": [cp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_compact": [cp, vp, vp, i32, i64, cp, vp, vp, sz, vp],
             "trimkv_decode_attn": [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp],
+            "trimkv_decode_attn_err": [cp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_attn_mass": [cp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp],
             "trimkv_allocate": [vp, vp, i32, i64, vp, vp, vp],
             "trimkv_append": [cp, vp, vp, vp, vp, vp],
@@ -205,6 +206,16 @@ def decode_attn(cache: Cache, q: torch.Tensor, group: int, scale: float, out: to
     _check(lib().trimkv_decode_attn(ctypes.byref(cache.struct()), _p(keep), _p(lse_ref), _p(q), int(group),
                                     float(scale), _p(out), _p(dropped), _p(lse_out), _p(ws), ws.numel(),
                                     _stream(stream)), "trimkv_decode_attn")
+
+
+def decode_attn_err(cache: Cache, q: torch.Tensor, group: int, scale: float, keep: torch.Tensor,
+                    out: torch.Tensor, dropped: torch.Tensor, err: torch.Tensor, mu: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None, stream=None):
+    if ws is None:
+        ws = workspace(OP_DECODE_ERR, cache, 0, group)
+    _check(lib().trimkv_decode_attn_err(ctypes.byref(cache.struct()), _p(keep), _p(q), int(group), float(scale),
+                                        _p(out), _p(dropped), _p(mu), _p(err), _p(ws), ws.numel(),
+                                        _stream(stream)), "trimkv_decode_attn_err")
 
 
 def attn_mass(cache: Cache, q: torch.Tensor, group: int, scale: float, mass: torch.Tensor,

@@ -18,7 +18,7 @@ def declared():
 
 def test_exports_every_declared_symbol():
     names = declared()
-    assert len(names) == 12
+    assert len(names) == 13
     L = tk.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -72,6 +72,26 @@ def test_null_and_inconsistent_arguments():
     assert L.trimkv_allocate(X, X, 0, 10, None, X, None) == tk.EINVAL
     assert L.trimkv_allocate(X, X, 4, -1, None, X, None) == tk.EINVAL
     assert L.trimkv_append(ctypes.byref(c), None, X, X, X, None) == tk.EINVAL
+
+
+def test_decode_err_argument_checks():
+    """trimkv_decode_attn_err: mask mode only (keep and err required), bf16
+    caches only, its own workspace (the decode workspace plus a second set of
+    partial outputs)."""
+    L = tk.lib()
+    c = fake_cache()
+    F = ctypes.c_float(1.0)
+    need = L.trimkv_workspace_size(tk.OP_DECODE_ERR, ctypes.byref(c), 0, 4)
+    assert need > L.trimkv_workspace_size(tk.OP_DECODE_ATTN, ctypes.byref(c), 0, 4)
+    assert L.trimkv_decode_attn_err(ctypes.byref(c), None, X, 4, F, X, X, None, X, X, need, None) == tk.EINVAL
+    assert L.trimkv_decode_attn_err(ctypes.byref(c), X, X, 4, F, X, X, None, None, X, need, None) == tk.EINVAL
+    assert L.trimkv_decode_attn_err(ctypes.byref(c), X, X, 4, F, X, X, None, X, X, need - 1, None) == tk.EWORKSPACE
+    assert L.trimkv_decode_attn_err(ctypes.byref(c), X, X, 17, F, X, X, None, X, X, need, None) == tk.EUNSUPPORTED
+    f32 = fake_cache(dtype=tk.F32, head_dim=64)
+    assert L.trimkv_decode_attn_err(ctypes.byref(f32), X, X, 4, F, X, X, None, X, X, 1 << 30, None) == \
+        tk.EUNSUPPORTED
+    odd = ctypes.c_void_p(0x10008)
+    assert L.trimkv_decode_attn_err(ctypes.byref(c), odd, X, 4, F, X, X, None, X, X, need, None) == tk.EINVAL
 
 
 def test_workspace_checks():

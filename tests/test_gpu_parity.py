@@ -332,6 +332,53 @@ def test_attention_modes(dtype, d, group):
                ref.decode_attn(kk, vv, q64, group, sc, lse_ref=lse_full.astype(np.float32).astype(np.float64)))
 
 
+@pytest.mark.parametrize("d,group", [(128, 4), (128, 7), (128, 1), (128, 16), (64, 4)])
+def test_attention_error_output(d, group):
+    """e_s(A) = ||mu - m_A||_2 (ContourKV section 1) beside the mask-mode
+    outputs.  mu and m_A are checked element-wise against the float64
+    oracle (2e-3); the norm against the oracle's within the bound those
+    imply, 2 * sqrt(D) * 2e-3, and against the norm of the GPU's own mu and
+    m_A within fp32 rounding.  Heads with an empty kept set and a fully
+    kept set are included, and (D = 128, G = 4) heads of 0, 1, 16 and 17
+    entries."""
+    rng = np.random.default_rng(700 + d + group)
+    if (d, group) == (128, 4):   # edge lengths: no entries, one, one page, a page and one
+        w = W["llama8b_32k"].scaled(layers=1, ctx=900)
+        pc = synth.build_cache(w, lengths=np.array([600, 300, 0, 1, 16, 17, 900, 5], np.int32))
+    else:
+        pc = synth.random_ragged_cache(800 + group, n_heads=9, d=d, dtype="bf16", max_len=900)
+    ov = OracleView(pc)
+    q_dev, q64 = make_q(rng, pc.n_heads * group, d, "bf16", scale=1.5)
+    c = upload(pc)
+    sc = scale_of(d)
+    keep = [rng.random(int(n)) < 0.3 for n in pc.length]
+    keep[0][:] = False
+    keep[1][:] = True
+    plane = plane_from_heads([k.astype(np.uint8) for k in keep], pc.page_off, pc.length, pc.n_pages, 0, np.uint8)
+    nq = pc.n_heads * group
+    out = torch.full((nq, d), np.nan, dtype=torch.float32, device="cuda")
+    mu = torch.full((nq, d), np.nan, dtype=torch.float32, device="cuda")
+    dropped = torch.full((nq,), np.nan, dtype=torch.float32, device="cuda")
+    err = torch.full((nq,), np.nan, dtype=torch.float32, device="cuda")
+    announce("attn err", d, group, "lengths", pc.length.tolist())
+    tk.decode_attn_err(c, q_dev, group, sc, cuda(plane), out, dropped, err, mu=mu)
+    o, m, dr, e = (x.cpu().numpy() for x in (out, mu, dropped, err))
+    wout, wdrop, _ = ref.decode_attn(ov.k, ov.v, q64, group, sc, keep=keep)
+    wmu, _, _ = ref.decode_attn(ov.k, ov.v, q64, group, sc)
+    werr = ref.subset_error(ov.k, ov.v, q64, group, sc, keep)
+    assert np.max(np.abs(o - wout)) <= OUT_TOL
+    assert np.max(np.abs(m - wmu)) <= OUT_TOL
+    assert np.max(np.abs(dr - wdrop)) <= DROP_TOL
+    assert np.all(np.abs(e - werr) <= 2 * math.sqrt(d) * OUT_TOL)
+    own = np.sqrt(((m.astype(np.float64) - o.astype(np.float64)) ** 2).sum(axis=1))
+    assert np.all(np.abs(e - own) <= 1e-5 * np.maximum(1.0, own))
+    fully = np.arange(group, 2 * group)   # head 1 keeps everything
+    assert np.all(e[fully] <= 1e-5)
+    # the errorless mask mode gives the same kept-set outputs
+    o2, d2, _ = run_attn(c, q_dev, group, sc, keep_plane=plane)
+    assert np.max(np.abs(o2 - o)) <= 1e-6 and np.max(np.abs(d2 - dr)) <= 1e-7
+
+
 def test_attention_edge_lengths_and_determinism():
     rng = np.random.default_rng(11)
     w = SMALL["c2s"].scaled(layers=1, kv_heads=6)
