@@ -297,6 +297,40 @@ def allocate(keptsum, length, total_budget):
     return b, mbar
 
 
+def allocate_floor(keptsum, length, total_budget, floor):
+    """ContourKV section 3 with its recency floor: every head first keeps its
+    most recent min(w, len_h) entries; the budget left, max(B - sum of the
+    floors, 0), follows the dropped mass exactly as in allocate(), capped at
+    the entries above each head's floor.  Returns (per-head totals b_h =
+    floor_h + share_h, mbar)."""
+    length = np.asarray(length, np.int64)
+    fl = np.minimum(int(floor), length)
+    share, mbar = allocate(keptsum, length - fl, max(int(total_budget) - int(fl.sum()), 0))
+    return share + fl, mbar
+
+
+def select_floor(per_head_scores, budgets, floor):
+    """Per head: the most recent min(w, len_h) entries (the last slots, since
+    positions ascend in slot order), plus the top b_h - floor_h of the other
+    entries by score descending, then position ascending (-0.0 == +0.0, NaN
+    lowest, as in select_global).  Returns keep flags per head."""
+    keep = []
+    for h, sc in enumerate(per_head_scores):
+        n = len(sc)
+        fl = min(int(floor), n)
+        k = np.zeros(n, dtype=bool)
+        k[n - fl:] = True
+        rest = np.asarray(sc[:n - fl], np.float64)
+        rest = np.where(rest == 0.0, 0.0, rest)
+        key = np.where(np.isnan(rest), -np.inf, -rest)        # ascending sort = score descending
+        nan_last = np.isnan(rest).astype(np.int64)
+        order = np.lexsort((np.arange(n - fl), key, nan_last))
+        m = max(0, min(int(budgets[h]) - fl, n - fl))
+        k[order[:m]] = True
+        keep.append(k)
+    return keep
+
+
 # --------------------------------------------------------------------------
 # byte accounting (IndexMem section 1: a 70B model needs ~320 GB of KV at 1M tokens)
 # --------------------------------------------------------------------------

@@ -415,6 +415,40 @@ def test_mass_is_mean_softmax():
     assert np.allclose(m1[0], p, atol=1e-16)
 
 
+def test_recency_floor_selection_and_allocation():
+    """ContourKV recency floor.  Selection equals a brute-force sort of the
+    non-floor entries plus the floor; w = 0 reduces to the plain per-head
+    selection and allocation; every total stays within [floor_h, len_h] and
+    sums to the budget when the floors fit (else the floors alone are kept)."""
+    rng = np.random.default_rng(41)
+    for trial in range(200):
+        H = int(rng.integers(1, 6))
+        lens = rng.integers(0, 30, H)
+        sc = [rng.choice([-1.0, 0.0, 0.5, 2.0, np.nan, np.inf], int(n)).astype(np.float32) for n in lens]
+        w = int(rng.integers(0, 8))
+        b = [int(rng.integers(0, n + 3)) for n in lens]
+        got = ref.select_floor(sc, b, w)
+        for h in range(H):
+            n, fl = int(lens[h]), min(w, int(lens[h]))
+            ent = [(float(sc[h][i]), h, i) for i in range(n - fl)]
+            want = brute.select_sorted(ent, b[h] - fl) | {(h, i) for i in range(n - fl, n)}
+            assert set((h, i) for i in np.flatnonzero(got[h])) == want, trial
+        if w == 0:
+            plain, _ = ref.select_global(sc, np.arange(H + 1), b)
+            assert all(np.array_equal(x, y) for x, y in zip(got, plain))
+        ks = rng.random(H)
+        B = int(rng.integers(0, int(lens.sum()) + 5))
+        bt, _ = ref.allocate_floor(ks, lens, B, w)
+        fl = np.minimum(w, lens)
+        assert np.all(bt >= fl) and np.all(bt <= lens)
+        if B >= fl.sum():
+            assert bt.sum() == min(B, int(lens.sum()))
+        else:
+            assert np.array_equal(bt, fl)
+        if w == 0:
+            assert np.array_equal(bt, ref.allocate(ks, lens, B)[0])
+
+
 def test_allocation_rules():
     # proportional, exact
     b, mbar = ref.allocate([0.5, 0.75, 0.75], [100, 100, 100], 8)
