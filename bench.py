@@ -309,6 +309,27 @@ def main():
         e_k.append(ka.elapsed_time(kb) * 1e-3)
     assert bool(torch.isfinite(err).all())
 
+    # ContourKV recency floor pieces on this cache's heads (w = 64): the floor
+    # marked in a scratch copy of the score plane and the floor-first
+    # allocation (latency-bound kernels; times only)
+    plane2 = score.clone()
+    ks_in = torch.rand(H, dtype=torch.float64, device=dev)
+    b_fl = torch.empty(H, dtype=torch.int64, device=dev)
+    f_mark, f_alloc = [], []
+    tk.mark_recent(src, 64, plane2)          # first launches load the kernels
+    tk.allocate_floor(ks_in, src.length, M, 64, b_fl)
+    for _ in range(args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        tk.mark_recent(src, 64, plane2)
+        ev[1].record()
+        tk.allocate_floor(ks_in, src.length, M, 64, b_fl)
+        ev[2].record()
+        torch.cuda.synchronize()
+        f_mark.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+        f_alloc.append(ev[1].elapsed_time(ev[2]) * 1e-3)
+    assert int(b_fl.sum().item()) == M
+
     # sanity of the step's results (not timed)
     kept_np = kept.cpu().numpy()
     if w.n_seg == 1:
@@ -359,7 +380,11 @@ def main():
                              "frac_hbm": round(err_algo / err_t / 1e9 / HBM_PEAK_GBS, 4),
                              "main_kernel": "k_attn_bf16<128, 3>", "main_kernel_us": round(err_kt * 1e6, 2),
                              "what": "mask-mode attention over every entry plus the dense output and "
-                                     "||mu - m_A|| per query head; outside the timed step"}}
+                                     "||mu - m_A|| per query head; outside the timed step"},
+              "recency_floor": {"mark_us": round(float(np.median(f_mark)) * 1e6, 2),
+                                "allocate_us": round(float(np.median(f_alloc)) * 1e6, 2),
+                                "what": "trimkv_mark_recent (w = 64 on %d heads) and trimkv_allocate_floor; "
+                                        "latency-bound" % H}}
     dom = max(stages, key=lambda s: t[s])
     sc_t = t["select"] + t["compact"]
     value = algo["decode"] / t["decode"] / 1e9

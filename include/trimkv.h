@@ -246,10 +246,36 @@ int trimkv_attn_mass(const trimkv_cache_t* cache, const void* q, int32_t group, 
  *   below their length.
  *   keptsum: device fp64 [n_heads];  len: device int32 [n_heads]
  *   mbar_out: device fp64 [n_heads] or NULL;  budget_out: device int64 [n_heads]
- * Errors: EINVAL (n_heads < 1 or > 65536, total_budget < 0).
+ * Errors: EINVAL (n_heads < 1 or > 16384, total_budget < 0).
  */
 int trimkv_allocate(const double* keptsum, const int32_t* len, int32_t n_heads,
                     int64_t total_budget, double* mbar_out, int64_t* budget_out, void* stream);
+
+/*
+ * trimkv_allocate_floor -- trimkv_allocate with ContourKV's recency floor.
+ * ContourKV page, section 3 (a recency floor kept in every head while the
+ * budget goes to the flat heads).  Head h first keeps its most recent
+ * floor_h = min(floor, len_h) entries; B' = max(total_budget - sum_h floor_h,
+ * 0) is shared out by the rule of trimkv_allocate with caps len_h - floor_h;
+ * budget_out[h] = floor_h + share_h (so the floors are kept even when their
+ * sum exceeds total_budget).  floor = 0 gives trimkv_allocate.
+ *   arguments as trimkv_allocate;  floor >= 0
+ * Errors: EINVAL (as trimkv_allocate, or floor < 0).
+ */
+int trimkv_allocate_floor(const double* keptsum, const int32_t* len, int32_t n_heads, int64_t total_budget,
+                          int32_t floor, double* mbar_out, int64_t* budget_out, void* stream);
+
+/*
+ * trimkv_mark_recent -- mark each head's recency floor in a CSR plane.
+ * ContourKV page, section 3 (recency floor).  plane[csr slot of entry i of
+ * head h] = +inf for len_h - min(floor, len_h) <= i < len_h, every other slot
+ * unchanged.  A per-head trimkv_select_global with budget_out of
+ * trimkv_allocate_floor on a plane of finite scores (attention masses) then
+ * keeps the floor plus the top share_h of the other entries.
+ *   plane: device fp32 CSR plane;  floor >= 0
+ * Errors: EINVAL, EUNSUPPORTED (cache shape).
+ */
+int trimkv_mark_recent(const trimkv_cache_t* cache, int32_t floor, float* plane, void* stream);
 
 /*
  * trimkv_append -- add one new entry per head at decode step *t.

@@ -225,6 +225,21 @@ int trimkv_allocate(const double* keptsum, const int32_t* len, int32_t n_heads, 
   return launch_allocate(keptsum, len, n_heads, total_budget, mbar_out, budget_out, S(stream));
 }
 
+int trimkv_allocate_floor(const double* keptsum, const int32_t* len, int32_t n_heads, int64_t total_budget,
+                          int32_t floor, double* mbar_out, int64_t* budget_out, void* stream) {
+  if (n_heads < 1 || n_heads > 16384 || total_budget < 0 || floor < 0 || !keptsum || !len || !budget_out)
+    return TRIMKV_EINVAL;
+  return launch_allocate_floor(keptsum, len, n_heads, total_budget, floor, mbar_out, budget_out, S(stream));
+}
+
+int trimkv_mark_recent(const trimkv_cache_t* c, int32_t floor, float* plane, void* stream) {
+  int rc;
+  if (!cache_shape_ok(c, &rc)) return rc;
+  if (floor < 0 || !plane || !table_ok(c)) return TRIMKV_EINVAL;
+  if (c->n_heads == 0) return TRIMKV_OK;
+  return launch_mark_recent(c, floor, plane, S(stream));
+}
+
 int trimkv_append(trimkv_cache_t* c, const void* k_new, const void* v_new, const float* beta_new, const int32_t* t,
                   void* stream) {
   int rc;

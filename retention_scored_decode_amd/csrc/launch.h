@@ -54,6 +54,9 @@ int launch_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float
                        hipStream_t st);
 int launch_attn_mass(const trimkv_cache_t* c, const void* q, int group, float scale, float* mass,
                      float* lse_full, void* ws, hipStream_t st);
+int launch_allocate_floor(const double* keptsum, const int32_t* len, int n_heads, int64_t budget, int floor_w,
+                          double* mbar, int64_t* out, hipStream_t st);
+int launch_mark_recent(const trimkv_cache_t* c, int floor_w, float* plane, hipStream_t st);
 int launch_allocate(const double* keptsum, const int32_t* len, int n_heads, int64_t budget, double* mbar,
                     int64_t* out, hipStream_t st);
 int launch_validate(const trimkv_cache_t* c, const int32_t* t, void* ws, hipStream_t st, int* bad);

@@ -21,7 +21,8 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ECAPACITY, EHIP, EINVARIANT = 0, -1, -2, -
 OP_SCORE, OP_SELECT, OP_COMPACT, OP_DECODE_ATTN, OP_ATTN_MASS, OP_VALIDATE, OP_DECODE_ERR = range(7)
 
 EXPORTS = ["trimkv_log_beta", "trimkv_score", "trimkv_select_global", "trimkv_compact",
-           "trimkv_decode_attn", "trimkv_decode_attn_err", "trimkv_attn_mass", "trimkv_allocate", "trimkv_append",
+           "trimkv_decode_attn", "trimkv_decode_attn_err", "trimkv_attn_mass", "trimkv_allocate",
+           "trimkv_allocate_floor", "trimkv_mark_recent", "trimkv_append",
            "trimkv_workspace_size", "trimkv_validate_cache", "trimkv_strerror", "trimkv_profile_next"]
 
 
@@ -59,6 +60,8 @@ def lib():
             "trimkv_decode_attn_err": [cp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_attn_mass": [cp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp],
             "trimkv_allocate": [vp, vp, i32, i64, vp, vp, vp],
+            "trimkv_allocate_floor": [vp, vp, i32, i64, i32, vp, vp, vp],
+            "trimkv_mark_recent": [cp, i32, vp, vp],
             "trimkv_append": [cp, vp, vp, vp, vp, vp],
             "trimkv_workspace_size": [ctypes.c_int, cp, i32, i32],
             "trimkv_validate_cache": [cp, vp, vp, sz, vp],
@@ -230,6 +233,17 @@ def allocate(keptsum: torch.Tensor, length: torch.Tensor, total_budget: int, bud
              mbar_out: Optional[torch.Tensor] = None, stream=None):
     _check(lib().trimkv_allocate(_p(keptsum), _p(length), int(keptsum.numel()), int(total_budget),
                                  _p(mbar_out), _p(budget_out), _stream(stream)), "trimkv_allocate")
+
+
+def allocate_floor(keptsum: torch.Tensor, length: torch.Tensor, total_budget: int, floor: int,
+                   budget_out: torch.Tensor, mbar_out: Optional[torch.Tensor] = None, stream=None):
+    _check(lib().trimkv_allocate_floor(_p(keptsum), _p(length), int(keptsum.numel()), int(total_budget), int(floor),
+                                       _p(mbar_out), _p(budget_out), _stream(stream)), "trimkv_allocate_floor")
+
+
+def mark_recent(cache: Cache, floor: int, plane: torch.Tensor, stream=None):
+    _check(lib().trimkv_mark_recent(ctypes.byref(cache.struct()), int(floor), _p(plane), _stream(stream)),
+           "trimkv_mark_recent")
 
 
 def append(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, beta_new: torch.Tensor, t: torch.Tensor,

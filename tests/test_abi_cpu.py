@@ -18,7 +18,7 @@ def declared():
 
 def test_exports_every_declared_symbol():
     names = declared()
-    assert len(names) == 13
+    assert len(names) == 15
     L = tk.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -92,6 +92,18 @@ def test_decode_err_argument_checks():
         tk.EUNSUPPORTED
     odd = ctypes.c_void_p(0x10008)
     assert L.trimkv_decode_attn_err(ctypes.byref(c), odd, X, 4, F, X, X, None, X, X, need, None) == tk.EINVAL
+
+
+def test_recency_floor_argument_checks():
+    L = tk.lib()
+    assert L.trimkv_allocate_floor(X, X, 4, 10, -1, None, X, None) == tk.EINVAL
+    assert L.trimkv_allocate_floor(X, X, 0, 10, 4, None, X, None) == tk.EINVAL
+    assert L.trimkv_allocate_floor(X, X, 4, -1, 4, None, X, None) == tk.EINVAL
+    assert L.trimkv_allocate_floor(X, X, 4, 10, 4, None, None, None) == tk.EINVAL
+    c = fake_cache()
+    assert L.trimkv_mark_recent(ctypes.byref(c), -1, X, None) == tk.EINVAL
+    assert L.trimkv_mark_recent(ctypes.byref(c), 4, None, None) == tk.EINVAL
+    assert L.trimkv_mark_recent(ctypes.byref(fake_cache(page_size=8)), 4, X, None) == tk.EUNSUPPORTED
 
 
 def test_workspace_checks():

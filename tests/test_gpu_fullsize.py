@@ -205,8 +205,8 @@ def test_full_size_batched_pipeline():
 def test_full_size_long_context_mass_pipeline():
     """The 128K-token workload at full size (288 KV heads): attention mass,
     per-head top-1024 by mass, dropped-mass budgets, per-head top-b_h,
-    compaction and reference-mode attention.  Both selections and the
-    allocation are checked for every head against the oracle on the same
+    compaction and reference-mode attention, then the recency-floor variant.
+    Selections and allocations are checked for every head against the oracle on the same
     fp32 masses and fp64 kept sums; masses, rows and attention on a sample
     of heads against the float64 oracle."""
     w = synth.WORKLOADS["qwen8b_128k"]
@@ -292,6 +292,19 @@ def test_full_size_long_context_mass_pipeline():
     assert np.max(np.abs(dr[rows] - wdrop)) <= DROP_TOL
     assert np.all(np.isfinite(o)) and np.all((dr >= -DROP_TOL) & (dr <= 1 + DROP_TOL))
     say("compaction and attention checked on", len(sample), "heads")
+    # ContourKV recency floor (w = 128) on the same masses: allocation and
+    # selection for every head
+    wf = 128
+    tk.allocate_floor(ks, c.length, B, wf, b)
+    tk.mark_recent(c, wf, mass)
+    tk.select_global(c, mass, seg, b, keep, kept)
+    bf = b.cpu().numpy()
+    assert np.array_equal(bf, ref.allocate_floor(ksum, ln, B, wf)[0])
+    want3 = ref.select_floor(gm, bf, wf)
+    got3 = heads_from_plane(keep.cpu().numpy(), po, ln)
+    for h in range(H):
+        assert np.array_equal(got3[h].astype(bool), want3[h]), ("floor keep", h)
+    say("recency floor checked on all", H, "heads")
 
 
 def test_full_size_streaming_steps():

@@ -549,6 +549,49 @@ def test_dropped_mass_budget_pipeline():
     assert np.max(np.abs(dropped.cpu().numpy() - (1 - kept_mass))) <= DROP_TOL
 
 
+@pytest.mark.parametrize("floor", [0, 64, 700])
+def test_recency_floor_pipeline(floor):
+    """ContourKV recency floor: top-mass per head -> kept sums -> floor-first
+    allocation -> floor marked in the mass plane -> per-head selection.  The
+    allocation and the selection are compared exactly with the oracle on the
+    GPU's own masses and kept sums; floor 700 exceeds the budget (only the
+    floors are kept), floor 0 is the plain rule."""
+    w = W["qwen8b_128k"].scaled(layers=1, ctx=3000, mass_topk=256)
+    lengths = np.array([3000, 500, 40, 0, 2999, 1000, 64, 65], np.int32)
+    pc = synth.build_cache(w, lengths=lengths)
+    H, G = pc.n_heads, w.group
+    q = synth.queries(w)
+    c = upload(pc)
+    sc = scale_of(128)
+    announce("recency floor", floor)
+    mass = torch.empty(pc.n_pages * 16, dtype=torch.float32, device="cuda")
+    lse = torch.empty(H * G, dtype=torch.float32, device="cuda")
+    tk.attn_mass(c, kv_dev(q, "bf16"), G, sc, mass, lse)
+    segs = np.arange(H + 1, dtype=np.int32)
+    keep = torch.empty(pc.n_pages * 16, dtype=torch.uint8, device="cuda")
+    kept = torch.empty(H, dtype=torch.int32, device="cuda")
+    ks = torch.empty(H, dtype=torch.float64, device="cuda")
+    tk.select_global(c, mass, cuda(segs), cuda(np.full(H, w.mass_topk), np.int64), keep, kept, ks)
+    B = int(0.05 * lengths.sum())
+    b = torch.empty(H, dtype=torch.int64, device="cuda")
+    tk.allocate_floor(ks, c.length, B, floor, b)
+    gm = heads_from_plane(mass.cpu().numpy(), pc.page_off, pc.length)
+    tk.mark_recent(c, floor, mass)
+    tk.select_global(c, mass, cuda(segs), b, keep, kept)
+    bh = b.cpu().numpy()
+    wb, _ = ref.allocate_floor(ks.cpu().numpy(), lengths, B, floor)
+    assert np.array_equal(bh, wb)
+    want = ref.select_floor(gm, bh, floor)
+    got = heads_from_plane(keep.cpu().numpy(), pc.page_off, pc.length)
+    for h in range(H):
+        assert np.array_equal(got[h].astype(bool), want[h]), h
+    assert np.array_equal(kept.cpu().numpy(), [int(k.sum()) for k in want])
+    marked = heads_from_plane(mass.cpu().numpy(), pc.page_off, pc.length)
+    for h in range(H):
+        n, fl = int(lengths[h]), min(floor, int(lengths[h]))
+        assert np.all(np.isposinf(marked[h][n - fl:])) and np.array_equal(marked[h][:n - fl], gm[h][:n - fl])
+
+
 # --------------------------------------------------------------------------
 # a7 + streaming: append -> score -> select -> attention (mask) -> compact
 # --------------------------------------------------------------------------
