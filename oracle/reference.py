@@ -222,6 +222,44 @@ def decode_attn(k_heads, v_heads, q, group, scale, keep=None, lse_ref=None):
     return out, dropped, lse
 
 
+def decode_attn_gated(k_heads, v_heads, q, group, scale, gate_heads, keep=None):
+    """Retention-gated decode attention (TRIM-KV section 2, attention
+    modulation: the retention score multiplies each attention weight),
+    applied at decode time and renormalised.  Per Q head qh (h = qh // group),
+    with ln r_j = gate_heads[h][j] (the retention score of entry j):
+    w_j = e^{z_j} r_j, z_j = scale <q, k_j>;
+    out = sum_{A} w_j v_j / sum_{A} w_j; dropped = sum_{U\\A} w_j / sum_{U} w_j;
+    lse = ln sum_{A} w_j.  keep=None means A = U.  Zero total weight over A
+    (A empty, or r_j = 0 on all of A): out = 0, lse = -inf; dropped = 1 then.
+
+    Returns out [n_q, D], dropped [n_q], lse [n_q]; all float64.
+    """
+    q = np.asarray(q, np.float64)
+    nq, d = q.shape
+    out = np.zeros((nq, d))
+    dropped = np.ones(nq)
+    lse = np.full(nq, -np.inf)
+    for qh in range(nq):
+        h = qh // group
+        K = np.asarray(k_heads[h], np.float64)
+        V = np.asarray(v_heads[h], np.float64)
+        n = K.shape[0]
+        if n == 0:
+            continue
+        A = np.ones(n, bool) if keep is None else np.asarray(keep[h], bool)
+        y = scale * (K @ q[qh]) + np.asarray(gate_heads[h], np.float64)   # ln w_j
+        m = y.max()
+        if m == -np.inf:
+            continue
+        w = np.exp(y - m)
+        la, ld = w[A].sum(), w[~A].sum()
+        if la > 0.0:
+            out[qh] = (w[A] @ V[A]) / la
+            lse[qh] = m + math.log(la)
+        dropped[qh] = ld / (la + ld)
+    return out, dropped, lse
+
+
 def subset_error(k_heads, v_heads, q, group, scale, keep):
     """e_s(A) = || mu - m_A ||_2 per Q head: mu the dense output over U,
     m_A the forced-weight output over A (ContourKV section 1)."""

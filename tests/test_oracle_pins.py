@@ -397,6 +397,74 @@ def test_subset_error_decomposition():
 
 
 # --------------------------------------------------------------------------
+# retention-gated attention (TRIM-KV section 2, attention modulation)
+# --------------------------------------------------------------------------
+def test_gated_attention_direct_weights():
+    """Weights e^{z_j} * beta_j^(t - pos_j) formed as a product with pow (not
+    in the log domain), sums by fsum; the oracle is given ln r = the float64
+    score.  Includes beta = 0 (weight 0) and beta = 1 (weight e^z)."""
+    rng = np.random.default_rng(41)
+    for trial in range(40):
+        n, d = int(rng.integers(1, 12)), int(rng.integers(1, 6))
+        K = rng.standard_normal((n, d))
+        V = rng.standard_normal((n, d))
+        q = rng.standard_normal((1, d))
+        beta = rng.uniform(0.2, 1.0, n)
+        beta[rng.random(n) < 0.15] = 0.0
+        beta[rng.random(n) < 0.15] = 1.0
+        pos = rng.permutation(40)[:n]
+        t = 40 + int(rng.integers(0, 5))
+        keep = rng.random(n) < 0.6
+        gate = ref.score_f64(beta, t, pos)
+        out, dropped, lse = ref.decode_attn_gated([K], [V], q, 1, 0.8, [gate], keep=[keep])
+        w = [math.exp(0.8 * math.fsum(a * b for a, b in zip(K[j], q[0]))) * float(beta[j]) ** (t - int(pos[j]))
+             for j in range(n)]
+        la = math.fsum(w[j] for j in range(n) if keep[j])
+        lu = math.fsum(w)
+        if la == 0.0:
+            assert np.all(out[0] == 0) and lse[0] == -np.inf and dropped[0] == 1.0
+            continue
+        want = [math.fsum(w[j] * V[j][c] for j in range(n) if keep[j]) / la for c in range(d)]
+        assert np.allclose(out[0], want, rtol=1e-12, atol=1e-13), trial
+        assert abs(dropped[0] - (lu - la) / lu) < 1e-13
+        assert abs(lse[0] - math.log(la)) < 1e-12 * max(1.0, abs(math.log(la)))
+
+
+def test_gated_attention_reductions():
+    """beta = 1 everywhere is ungated attention; a gate constant over a head
+    changes only lse (by that constant); q = 0 with one beta makes the
+    weights geometric, whose sums have closed forms; beta = 0 on every entry
+    of a head (age > 0) leaves no weight: out 0, dropped 1."""
+    rng = np.random.default_rng(42)
+    K, V = [rng.standard_normal((n, 6)) for n in (9, 0, 20)], [rng.standard_normal((n, 6)) for n in (9, 0, 20)]
+    q = rng.standard_normal((6, 6))
+    keep = [rng.random(len(k)) < 0.5 for k in K]
+    zero = [np.zeros(len(k)) for k in K]
+    for kp in (None, keep):
+        a = ref.decode_attn(K, V, q, 2, 0.6, keep=kp)
+        b = ref.decode_attn_gated(K, V, q, 2, 0.6, zero, keep=kp)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+        c = ref.decode_attn_gated(K, V, q, 2, 0.6, [np.full(len(k), -3.25) for k in K], keep=kp)
+        assert np.allclose(c[0], a[0], atol=1e-14) and np.allclose(c[1], a[1], atol=1e-14)
+        fin = np.isfinite(a[2])
+        assert np.allclose(c[2][fin], a[2][fin] - 3.25, atol=1e-13) and np.all(c[2][~fin] == -np.inf)
+    # geometric: n entries at positions 0..n-1, t = n, v_i = i, weights x^(n-i)
+    for n, x in ((1, 0.5), (7, 0.9), (30, 0.97), (12, 0.25)):
+        Kg = [np.ones((n, 1))]
+        Vg = [np.arange(n, dtype=np.float64).reshape(n, 1)]
+        gate = [ref.score_f64(np.full(n, x), n, np.arange(n))]
+        out, dropped, _ = ref.decode_attn_gated(Kg, Vg, np.zeros((1, 1)), 1, 1.0, gate)
+        s1 = x * (1 - x ** n) / (1 - x)                                     # sum_{k=1..n} x^k
+        sk = x * (1 - (n + 1) * x ** n + n * x ** (n + 1)) / (1 - x) ** 2   # sum_{k=1..n} k x^k
+        assert abs(out[0, 0] - (n * s1 - sk) / s1) < 1e-12 * n and dropped[0] == 0.0
+    gate = [np.full(9, -np.inf), np.zeros(0), ref.score_f64(np.linspace(0.5, 1.0, 20), 30, np.arange(20))]
+    out, dropped, lse = ref.decode_attn_gated(K, V, q, 2, 0.6, gate)
+    assert np.all(out[:4] == 0) and np.all(dropped[:4] == 1) and np.all(lse[:4] == -np.inf)
+    assert np.all(np.isfinite(lse[4:]))
+
+
+# --------------------------------------------------------------------------
 # a5/a6: attention mass and allocation (ContourKV section 3)
 # --------------------------------------------------------------------------
 def test_mass_is_mean_softmax():
