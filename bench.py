@@ -169,6 +169,33 @@ def traffic_for(workload, stage):
     return None if k is None else int(k["traffic_bytes"])
 
 
+def timed_calls(call, reps):
+    """Mean seconds per call of `reps` calls issued back to back between two
+    events (so host launch latency overlaps the previous call), and the mean
+    main-kernel time of `reps` single calls bracketed inside the library."""
+    for _ in range(2):
+        call()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    per_call = a.elapsed_time(b) * 1e-3 / reps
+    ks = []
+    for _ in range(reps):
+        ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ka.record()
+        kb.record()
+        torch.cuda.synchronize()
+        tk.profile_next(ka, kb)
+        call()
+        torch.cuda.synchronize()
+        ks.append(ka.elapsed_time(kb) * 1e-3)
+    return per_call, float(np.mean(ks))
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -291,23 +318,18 @@ def main():
     ws_err = tk.workspace(tk.OP_DECODE_ERR, src, 0, G)
     mu = torch.empty((nq, D), dtype=torch.float32, device=dev)
     err = torch.empty(nq, dtype=torch.float32, device=dev)
-    for _ in range(2):
-        tk.decode_attn_err(src, q, G, scale, keep, out_m, drop_m, err, mu=mu, ws=ws_err)
-    e_t, e_k = [], []
-    for _ in range(args.steps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ka.record()
-        kb.record()
-        torch.cuda.synchronize()
-        tk.profile_next(ka, kb)
-        a.record()
-        tk.decode_attn_err(src, q, G, scale, keep, out_m, drop_m, err, mu=mu, ws=ws_err)
-        b.record()
-        torch.cuda.synchronize()
-        e_t.append(a.elapsed_time(b) * 1e-3)
-        e_k.append(ka.elapsed_time(kb) * 1e-3)
+    e_t, e_k = timed_calls(lambda: tk.decode_attn_err(src, q, G, scale, keep, out_m, drop_m, err, mu=mu, ws=ws_err),
+                           args.steps)
     assert bool(torch.isfinite(err).all())
+
+    # retention-gated decode attention (TRIM-KV section 2 modulation, at
+    # decode time) over the compacted cache the last step left: the decode
+    # stage's reads plus ln beta and position of every kept entry
+    out_g = torch.empty((nq, D), dtype=torch.float32, device=dev)
+    drop_g = torch.empty(nq, dtype=torch.float32, device=dev)
+    g_t, g_k = timed_calls(lambda: tk.decode_attn_gated(dst, seg, t_dev, q, G, scale, out_g, drop_g, ws=ws_dec),
+                           args.steps)
+    assert bool(torch.isfinite(out_g).all())
 
     # ContourKV recency floor pieces on this cache's heads (w = 64): the floor
     # marked in a scratch copy of the score plane and the floor-first
@@ -374,13 +396,21 @@ def main():
                         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "main_kernel": STAGE_KERNEL[s][0],
                         "main_kernel_us": round(kt[s] * 1e6, 2)}
     err_algo = 512 * N + small + nq * D * 4
-    err_t, err_kt = float(np.mean(e_t)), float(np.mean(e_k))
+    err_t, err_kt = e_t, e_k
+    g_algo = algo["decode"] + 8 * kept_total
+    g_tm, g_km = g_t, g_k
     extras = {"attend_err": {"us": round(err_t * 1e6, 2), "algo_bytes": err_algo,
                              "GBps": round(err_algo / err_t / 1e9, 1),
                              "frac_hbm": round(err_algo / err_t / 1e9 / HBM_PEAK_GBS, 4),
                              "main_kernel": "k_attn_bf16<128, 3>", "main_kernel_us": round(err_kt * 1e6, 2),
                              "what": "mask-mode attention over every entry plus the dense output and "
                                      "||mu - m_A|| per query head; outside the timed step"},
+              "gated_decode": {"us": round(g_tm * 1e6, 2), "algo_bytes": g_algo,
+                               "GBps": round(g_algo / g_tm / 1e9, 1),
+                               "frac_hbm": round(g_algo / g_tm / 1e9 / HBM_PEAK_GBS, 4),
+                               "main_kernel": "k_attn_bf16<128, 4>", "main_kernel_us": round(g_km * 1e6, 2),
+                               "what": "retention-gated attention (weights e^z r renormalised) over the "
+                                       "compacted cache; outside the timed step"},
               "recency_floor": {"mark_us": round(float(np.median(f_mark)) * 1e6, 2),
                                 "allocate_us": round(float(np.median(f_alloc)) * 1e6, 2),
                                 "what": "trimkv_mark_recent (w = 64 on %d heads) and trimkv_allocate_floor; "

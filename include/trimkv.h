@@ -198,6 +198,27 @@ int trimkv_decode_attn(const trimkv_cache_t* cache, const uint8_t* keep, const f
                        float* lse_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * trimkv_decode_attn_gated -- retention-gated decode attention.
+ * TRIM-KV page, section 2 (attention modulation: the retention score
+ * multiplies the attention weights; the page applies it in training) used
+ * at decode time.  As trimkv_decode_attn with every weight e^{z_j} replaced
+ * by e^{z_j} * r_j, r_j = beta_j^(t - pos_j): the logit gains
+ * ln r_j = fp32(t - pos_j) * ln beta_j, formed exactly as trimkv_score forms
+ * the score (t of the head's segment, ln beta and position from meta).
+ *   out[qh]     = sum_{A} e^{z_j} r_j v_j / sum_{A} e^{z_j} r_j   (0 if A is empty)
+ *   dropped[qh] = sum_{U\A} e^{z_j} r_j / sum_{U} e^{z_j} r_j     (1 if A is empty)
+ *   lse_out[qh] = ln sum_{A} e^{z_j} r_j                          (-inf if A is empty)
+ * keep == NULL means A = U.  Entries with beta = 0 need t > pos (0 * -inf).
+ *   n_seg, seg_head_begin, t: as trimkv_score (device int32)
+ *   other arguments as trimkv_decode_attn (no lse_ref); bf16 caches only
+ *   ws: trimkv_workspace_size(TRIMKV_OP_DECODE_ATTN, cache, 0, group) bytes
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE.
+ */
+int trimkv_decode_attn_gated(const trimkv_cache_t* cache, int32_t n_seg, const int32_t* seg_head_begin,
+                             const int32_t* t, const uint8_t* keep, const void* q, int32_t group, float scale,
+                             float* out, float* dropped, float* lse_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * trimkv_decode_attn_err -- mask-mode decode attention that also measures
  * what the forced weights cost: e_s(A) = || mu - m_A ||_2 per query head.
  * ContourKV page, section 1 (theoretical analysis): mu is the dense

@@ -195,6 +195,20 @@ int trimkv_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float
   return launch_decode_attn(c, keep, lse_ref, q, group, scale, out, dropped, lse_out, ws, S(stream));
 }
 
+int trimkv_decode_attn_gated(const trimkv_cache_t* c, int32_t n_seg, const int32_t* seg, const int32_t* t,
+                             const uint8_t* keep, const void* q, int32_t group, float scale, float* out, float* dropped,
+                             float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if (!cache_shape_ok(c, &rc)) return rc;
+  if (group < 1 || group > 16 || c->dtype != TRIMKV_BF16) return TRIMKV_EUNSUPPORTED;
+  if (n_seg < 1 || n_seg > c->n_heads || !seg || !t || !q || !out || !dropped || !table_ok(c) || !pools_ok(c) ||
+      ((uintptr_t)keep & 15))
+    return TRIMKV_EINVAL;
+  if ((rc = ws_check(ws, ws_bytes, attn_ws_layout(c, group).total))) return rc;
+  if (c->n_heads == 0) return TRIMKV_OK;
+  return launch_decode_attn_gated(c, n_seg, seg, t, keep, q, group, scale, out, dropped, lse_out, ws, S(stream));
+}
+
 int trimkv_decode_attn_err(const trimkv_cache_t* c, const uint8_t* keep, const void* q, int32_t group, float scale,
                            float* out, float* dropped, float* mu, float* err, void* ws, size_t ws_bytes,
                            void* stream) {

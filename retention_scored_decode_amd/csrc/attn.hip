@@ -45,7 +45,7 @@ constexpr int NTA = 256;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
-enum { A_PLAIN = 0, A_MASK = 1, A_LOGITS = 2, A_ERR = 3 };
+enum { A_PLAIN = 0, A_MASK = 1, A_LOGITS = 2, A_ERR = 3, A_GPLAIN = 4, A_GMASK = 5 };
 
 struct AttnWs {
   int32_t* item_off;   // [H + 1]          (fp32 work list)
@@ -79,6 +79,11 @@ struct AttnArgs {
   float* lse_out;
   float* mu;             // error mode: dense output over every key, or null
   float* err;            // error mode: || mu - out ||_2 per query head
+  // retention-gated modes: ln r = fp32(t - pos) * ln beta joins each logit
+  const uint32_t* meta;  // [n_pages][2][16]: ln beta bits, positions
+  const int32_t* seg;    // [n_seg + 1] first head of each segment
+  const int32_t* tseg;   // [n_seg] decode step of each segment
+  int n_seg;
 };
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -330,7 +335,10 @@ __device__ __forceinline__ uint32_t pick4(u32x4 v, int q) {
 // dropped keys only enter the dropped sum and their V rows are not read),
 // A_ERR (as A_MASK, and the dropped keys' P V goes to a second accumulator,
 // so that the merge has the dense output as well; every V row is read),
-// A_LOGITS (base-2 logits of every valid key and (max, sum) partials).
+// A_LOGITS (base-2 logits of every valid key and (max, sum) partials),
+// A_GPLAIN / A_GMASK (as A_PLAIN / A_MASK with retention-gated weights: each
+// base-2 logit gains ln r * log2(e), r = beta^(t - pos), read from the page's
+// metadata line together with its K and V).
 //
 // Wave w of W streams CSR pages [w P / W, (w + 1) P / W) and, per head
 // segment of that range, writes the partial with index w + head.  Each
@@ -355,11 +363,12 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
   constexpr int KU = D / 32;    // QK MFMAs per page
   constexpr int NV = D / 16;    // PV output column blocks
   constexpr bool LOGITS = MODE == A_LOGITS;
-  constexpr bool MASKED = MODE == A_MASK || MODE == A_ERR;
+  constexpr bool MASKED = MODE == A_MASK || MODE == A_ERR || MODE == A_GMASK;
   constexpr bool ERR = MODE == A_ERR;
+  constexpr bool GATED = MODE == A_GPLAIN || MODE == A_GMASK;
   // load instructions per page; pages in flight are tracked by vmcnt (the
   // logits mode also stores inside the loop and keeps a single page in flight)
-  constexpr int PER_PAGE = LOGITS ? 0 : 2 * LPP;
+  constexpr int PER_PAGE = LOGITS ? 0 : 2 * LPP + (GATED ? 2 : 0);
   __shared__ u32x4 lds_k[NTA / WAVE][2][16 * CH];
   __shared__ u32x4 lds_v[NTA / WAVE][2][LOGITS ? 1 : 16 * CH];
   const AttnWs& w = a.w;
@@ -413,6 +422,16 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
     const int v0 = clen[h] - (p - hb) * PAGE;
     const int nv = v0 < 0 ? 0 : (v0 > cnt * PAGE ? cnt * PAGE : v0);   // valid entries of the segment
     const c_u32x4 ckeep = (c_u32x4)(a.keep + (int64_t)page0 * PAGE);   // 16 keep bytes per page
+    int t_h = 0;   // decode step of the head's segment (gated modes)
+    if (GATED) {
+      const c_i32 cseg = (c_i32)a.seg;
+      int lo = 0, hi = a.n_seg;   // last segment whose first head is <= h
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cseg[mid] <= h) lo = mid; else hi = mid;
+      }
+      t_h = __builtin_amdgcn_readfirstlane(((c_i32)a.tseg)[lo]);
+    }
 
     // B operand of QK MFMA u: dims 32u + 8r .. +7 of query head col (zero for col >= G)
     u32x4 qop[KU];
@@ -433,6 +452,9 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
     for (int n = 0; n < (ERR ? NV : 1); ++n) acc2[n] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
     // page i's loads; phys = its physical page, kw4 = its 16 keep bytes (mask mode)
+    // gated modes: ln beta bits and positions of keys 4r..4r+3 of the page in
+    // buffer b (loaded with the page, two pages in flight like the tiles)
+    u32x4 g_lnb[GATED ? 2 : 1], g_pos[GATED ? 2 : 1];
     auto dma = [&](auto B, int i, int64_t phys, u32x4 kw4) {
       constexpr int buf = decltype(B)::value;
       const uint8_t* kpage = kbase + phys * (PAGE * D * 2);
@@ -442,7 +464,7 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
         __builtin_amdgcn_global_load_lds((gptr)(kpage + gk[u]), (lptr)(&lds_k[wu][buf][64 * u]), 16, 0, CPOL_NT);
       if (!LOGITS) {
         const bool full = (i + 1) * PAGE <= nv;   // wave-uniform
-        if ((MODE == A_PLAIN || ERR) && full) {
+        if ((MODE == A_PLAIN || MODE == A_GPLAIN || ERR) && full) {
 #pragma unroll
           for (int u = 0; u < LPP; ++u)
             __builtin_amdgcn_global_load_lds((gptr)(vpage + gv[u]), (lptr)(&lds_v[wu][buf][64 * u]), 16, 0, CPOL_NT);
@@ -451,35 +473,50 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
           for (int u = 0; u < LPP; ++u) {
             const int row = (64 * u + lane) / CH;
             bool need = i * PAGE + row < nv;
-            if (MODE == A_MASK) need &= ((pick4(kw4, row >> 2) >> (8 * (row & 3))) & 0xFFu) != 0;
+            if (MODE == A_MASK || MODE == A_GMASK) need &= ((pick4(kw4, row >> 2) >> (8 * (row & 3))) & 0xFFu) != 0;
             // rows that take no part read zeros
             const uint8_t* src = need ? vpage + gv[u] : reinterpret_cast<const uint8_t*>(kZeroChunks) + 16 * lane;
             __builtin_amdgcn_global_load_lds((gptr)src, (lptr)(&lds_v[wu][buf][64 * u]), 16, 0, 0);
           }
         }
       }
+      if (GATED) {   // counted in PER_PAGE: issued after the page's tiles
+        const uint32_t* mrow = a.meta + phys * (2 * PAGE) + 4 * r;
+        g_lnb[buf & (GATED ? 1 : 0)] = *reinterpret_cast<const u32x4*>(mrow);
+        g_pos[buf & (GATED ? 1 : 0)] = *reinterpret_cast<const u32x4*>(mrow + PAGE);
+      }
     };
 
-  auto math = [&](int i, const u32x4 (&kop)[KU], const short4_t (&vop)[LOGITS ? 1 : NV], uint32_t kwr) {
+  auto math = [&](int i, const u32x4 (&kop)[KU], const short4_t (&vop)[LOGITS ? 1 : NV], uint32_t kwr,
+                  u32x4 glnb, u32x4 gpos) {
     // ---- S = K q^T ----
     float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < KU; ++u)
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[u]),
                                                   __builtin_bit_cast(bf16x8_t, qop[u]), s, 0, 0, 0);
+    // base-2 offset of each logit: 0, or ln r * log2(e) with ln r formed as
+    // the score kernel forms it (one fp32 product)
+    float gate[4] = {0.f, 0.f, 0.f, 0.f};
+    if (GATED) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        gate[j] = __fmul_rn((float)(t_h - (int)gpos[j]), __uint_as_float(glnb[j])) * LOG2E;
+    }
     const int i0 = i * PAGE + 4 * r;          // entry of key 4r within the item
     const bool full = (i + 1) * PAGE <= nv;   // wave-uniform
     float pj[4];
     bool slow = !full;
     if (full) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pj[j] = fmaf(s[j], a.scale2, nm);
-      slow = __any(fmaxf(fmaxf(pj[0], pj[1]), fmaxf(pj[2], pj[3])) > RESCALE_T);
+      for (int j = 0; j < 4; ++j) pj[j] = fmaf(s[j], a.scale2, GATED ? gate[j] + nm : nm);
+      // NaN (gated: a -inf gate while m = -inf) takes the exact path too
+      slow = __any(!(fmaxf(fmaxf(pj[0], pj[1]), fmaxf(pj[2], pj[3])) <= RESCALE_T));
     }
     if (slow) {
       float z[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) z[j] = i0 + j < nv ? s[j] * a.scale2 : -INFINITY;
+      for (int j = 0; j < 4; ++j) z[j] = i0 + j < nv ? (GATED ? fmaf(s[j], a.scale2, gate[j]) : s[j] * a.scale2) : -INFINITY;
       float pm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
       pm = fmaxf(pm, __shfl_xor(pm, 16, WAVE));
       pm = fmaxf(pm, __shfl_xor(pm, 32, WAVE));   // maximum of the page for query head col
@@ -603,7 +640,7 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
       }
       if (i + 1 < cnt) kwm_n = keep4(i + 1);
       asm volatile("" ::: "memory");
-      math(i, kop, vop, kwr);
+      math(i, kop, vop, kwr, g_lnb[buf & (GATED ? 1 : 0)], g_pos[buf & (GATED ? 1 : 0)]);
     };
     dma(std::integral_constant<int, 0>{}, 0, cids[page0], keep4(0));
     if (cnt > 1) dma(std::integral_constant<int, 1>{}, 1, cids[page0 + 1], keep4(1));
@@ -807,7 +844,7 @@ int launch_main(const trimkv_cache_t* c, AttnArgs& a, hipStream_t st) {
   constexpr bool LOGITS = MODE == A_LOGITS;
   const dim3 blk(NT);
   if (c->dtype == TRIMKV_F32) {
-    if (MODE == A_ERR) return TRIMKV_EUNSUPPORTED;
+    if (MODE == A_ERR || MODE == A_GPLAIN || MODE == A_GMASK) return TRIMKV_EUNSUPPORTED;
     const int64_t T = max_chunks(c, CHA_F32);   // bound on the number of items
     if (c->head_dim == 128) hipLaunchKernelGGL((k_attn_f32<128, LOGITS>), dim3((unsigned)T), blk, 0, st, a);
     else hipLaunchKernelGGL((k_attn_f32<64, LOGITS>), dim3((unsigned)T), blk, 0, st, a);
@@ -885,6 +922,22 @@ int launch_decode_attn_err(const trimkv_cache_t* c, const uint8_t* keep, const v
              c->n_pages * PAGE, CHA_F32, 0, w, nullptr, out, dropped, nullptr, mu, err};
   prof_begin(st);
   int rc = launch_main<A_ERR>(c, a, st);
+  prof_end(st);
+  if (rc) return rc;
+  if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(c->n_heads * group), dim3(NT), 0, st, a, 1);
+  else hipLaunchKernelGGL(k_attn_merge<64>, dim3(c->n_heads * group), dim3(NT), 0, st, a, 1);
+  return check_launch();
+}
+
+int launch_decode_attn_gated(const trimkv_cache_t* c, int n_seg, const int32_t* seg, const int32_t* t,
+                             const uint8_t* keep, const void* q, int group, float scale, float* out, float* dropped,
+                             float* lse_out, void* ws, hipStream_t st) {
+  AttnWs w = carve(c, group, ws, false);
+  AttnArgs a{c->page_off, c->page_ids, c->len, c->k, c->v, keep, q, c->n_heads, group, scale * LOG2E,
+             c->n_pages * PAGE, CHA_F32, 0, w, nullptr, out, dropped, lse_out, nullptr, nullptr,
+             c->meta, seg, t, n_seg};
+  prof_begin(st);
+  int rc = keep ? launch_main<A_GMASK>(c, a, st) : launch_main<A_GPLAIN>(c, a, st);
   prof_end(st);
   if (rc) return rc;
   if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(c->n_heads * group), dim3(NT), 0, st, a, 1);

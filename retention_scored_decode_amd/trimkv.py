@@ -21,7 +21,8 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ECAPACITY, EHIP, EINVARIANT = 0, -1, -2, -
 OP_SCORE, OP_SELECT, OP_COMPACT, OP_DECODE_ATTN, OP_ATTN_MASS, OP_VALIDATE, OP_DECODE_ERR = range(7)
 
 EXPORTS = ["trimkv_log_beta", "trimkv_score", "trimkv_select_global", "trimkv_compact",
-           "trimkv_decode_attn", "trimkv_decode_attn_err", "trimkv_attn_mass", "trimkv_allocate",
+           "trimkv_decode_attn", "trimkv_decode_attn_gated", "trimkv_decode_attn_err", "trimkv_attn_mass",
+           "trimkv_allocate",
            "trimkv_allocate_floor", "trimkv_mark_recent", "trimkv_append",
            "trimkv_workspace_size", "trimkv_validate_cache", "trimkv_strerror", "trimkv_profile_next"]
 
@@ -58,6 +59,7 @@ def lib():
             "trimkv_compact": [cp, vp, vp, i32, i64, cp, vp, vp, sz, vp],
             "trimkv_decode_attn": [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp],
             "trimkv_decode_attn_err": [cp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp],
+            "trimkv_decode_attn_gated": [cp, i32, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp],
             "trimkv_attn_mass": [cp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp],
             "trimkv_allocate": [vp, vp, i32, i64, vp, vp, vp],
             "trimkv_allocate_floor": [vp, vp, i32, i64, i32, vp, vp, vp],
@@ -209,6 +211,17 @@ def decode_attn(cache: Cache, q: torch.Tensor, group: int, scale: float, out: to
     _check(lib().trimkv_decode_attn(ctypes.byref(cache.struct()), _p(keep), _p(lse_ref), _p(q), int(group),
                                     float(scale), _p(out), _p(dropped), _p(lse_out), _p(ws), ws.numel(),
                                     _stream(stream)), "trimkv_decode_attn")
+
+
+def decode_attn_gated(cache: Cache, seg: torch.Tensor, t: torch.Tensor, q: torch.Tensor, group: int, scale: float,
+                      out: torch.Tensor, dropped: torch.Tensor, keep: Optional[torch.Tensor] = None,
+                      lse_out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    if ws is None:
+        ws = workspace(OP_DECODE_ATTN, cache, 0, group)
+    _check(lib().trimkv_decode_attn_gated(ctypes.byref(cache.struct()), int(seg.numel()) - 1, _p(seg), _p(t),
+                                          _p(keep), _p(q), int(group), float(scale), _p(out), _p(dropped),
+                                          _p(lse_out), _p(ws), ws.numel(), _stream(stream)),
+           "trimkv_decode_attn_gated")
 
 
 def decode_attn_err(cache: Cache, q: torch.Tensor, group: int, scale: float, keep: torch.Tensor,

@@ -18,7 +18,7 @@ def declared():
 
 def test_exports_every_declared_symbol():
     names = declared()
-    assert len(names) == 15
+    assert len(names) == 16
     L = tk.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -92,6 +92,26 @@ def test_decode_err_argument_checks():
         tk.EUNSUPPORTED
     odd = ctypes.c_void_p(0x10008)
     assert L.trimkv_decode_attn_err(ctypes.byref(c), odd, X, 4, F, X, X, None, X, X, need, None) == tk.EINVAL
+
+
+def test_gated_argument_checks():
+    """trimkv_decode_attn_gated: segment list and t required (as
+    trimkv_score), bf16 caches only, the decode workspace."""
+    L = tk.lib()
+    c = fake_cache()
+    F = ctypes.c_float(1.0)
+    need = L.trimkv_workspace_size(tk.OP_DECODE_ATTN, ctypes.byref(c), 0, 4)
+    g = L.trimkv_decode_attn_gated
+    assert g(ctypes.byref(c), 1, X, X, None, X, 4, F, X, X, None, X, need - 1, None) == tk.EWORKSPACE
+    assert g(ctypes.byref(c), 0, X, X, None, X, 4, F, X, X, None, X, need, None) == tk.EINVAL
+    assert g(ctypes.byref(c), 5, X, X, None, X, 4, F, X, X, None, X, need, None) == tk.EINVAL
+    assert g(ctypes.byref(c), 1, None, X, None, X, 4, F, X, X, None, X, need, None) == tk.EINVAL
+    assert g(ctypes.byref(c), 1, X, None, None, X, 4, F, X, X, None, X, need, None) == tk.EINVAL
+    assert g(ctypes.byref(c), 1, X, X, None, X, 4, F, X, None, None, X, need, None) == tk.EINVAL
+    assert g(ctypes.byref(c), 1, X, X, ctypes.c_void_p(0x10008), X, 4, F, X, X, None, X, need, None) == tk.EINVAL
+    assert g(ctypes.byref(c), 1, X, X, None, X, 17, F, X, X, None, X, need, None) == tk.EUNSUPPORTED
+    f32 = fake_cache(dtype=tk.F32, head_dim=64)
+    assert g(ctypes.byref(f32), 1, X, X, None, X, 4, F, X, X, None, X, 1 << 30, None) == tk.EUNSUPPORTED
 
 
 def test_recency_floor_argument_checks():

@@ -332,6 +332,52 @@ def test_attention_modes(dtype, d, group):
                ref.decode_attn(kk, vv, q64, group, sc, lse_ref=lse_full.astype(np.float32).astype(np.float64)))
 
 
+@pytest.mark.parametrize("d,group", [(128, 4), (128, 7), (128, 1), (128, 16), (64, 4), (64, 3)])
+def test_gated_attention(d, group):
+    """Retention-gated decode attention (TRIM-KV section 2, attention
+    modulation, at decode time): weights e^{z_j} r_j renormalised, plain and
+    mask modes, against the float64 oracle given the float32 scores as ln r.
+    Two segments with their own t; beta = 0 and 1 sprinkled in; head 0 has
+    beta = 0 everywhere (no weight: out 0, dropped 1), head 1 beta = 0 on its
+    first 40 entries (whole pages of -inf gates before any finite logit)."""
+    rng = np.random.default_rng(900 + d + group)
+    pc = synth.random_ragged_cache(950 + group, n_heads=9, d=d, dtype="bf16", max_len=900, min_len=60, t=1000,
+                                   beta_dist=("beta", 20.0, 1.0))
+    pc.length[5] = 0   # an empty head
+    beta = pc.beta.reshape(-1)
+    for h in range(pc.n_heads):
+        sl = ref.head_phys_slots(pc.page_off, pc.page_ids, pc.length, h)
+        beta[sl[rng.random(len(sl)) < 0.05]] = 0.0
+        beta[sl[rng.random(len(sl)) < 0.05]] = 1.0
+        if h == 0:
+            beta[sl] = 0.0
+        if h == 1:
+            beta[sl[:40]] = 0.0
+            beta[sl[40:]] = 1.0
+    ov = OracleView(pc)
+    seg = np.array([0, 4, pc.n_heads], np.int32)
+    t_seg = np.array([1000, 1003], np.int32)
+    t_h = seg_t(seg, t_seg, pc.n_heads)
+    gate = [g.astype(np.float64) for g in ov.scores(t_h)]
+    q_dev, q64 = make_q(rng, pc.n_heads * group, d, "bf16", scale=1.5)
+    c = upload(pc)
+    sc = scale_of(d)
+    nq = pc.n_heads * group
+    keep = [rng.random(int(n)) < 0.3 for n in pc.length]
+    plane = plane_from_heads([k.astype(np.uint8) for k in keep], pc.page_off, pc.length, pc.n_pages, 0, np.uint8)
+    for kp in (None, keep):
+        out = torch.full((nq, d), np.nan, dtype=torch.float32, device="cuda")
+        dropped = torch.full((nq,), np.nan, dtype=torch.float32, device="cuda")
+        lse = torch.full((nq,), np.nan, dtype=torch.float32, device="cuda")
+        announce("attn gated", d, group, "mask" if kp is not None else "plain", "lengths", pc.length.tolist())
+        tk.decode_attn_gated(c, cuda(seg), cuda(t_seg), q_dev, group, sc, out, dropped,
+                             keep=None if kp is None else cuda(plane), lse_out=lse)
+        got = tuple(x.cpu().numpy() for x in (out, dropped, lse))
+        want = ref.decode_attn_gated(ov.k, ov.v, q64, group, sc, gate, keep=kp)
+        check_attn(got, want)
+        assert np.all(got[0][:group] == 0) and np.all(got[1][:group] == 1)
+
+
 @pytest.mark.parametrize("d,group", [(128, 4), (128, 7), (128, 1), (128, 16), (64, 4)])
 def test_attention_error_output(d, group):
     """e_s(A) = ||mu - m_A||_2 (ContourKV section 1) beside the mask-mode
