@@ -39,3 +39,16 @@ def attention_direct(K, V, q, scale, keep):
     else:
         out = [0.0] * len(q)
     return out, ld / (la + ld)
+
+
+def shift_in_place(pool, slots_of_head, keep):
+    """Stable in-place compaction of one head, one entry at a time: the j-th
+    kept entry (in slot order) is written to the head's j-th slot.  pool is a
+    list of per-physical-slot values, modified in place; slots_of_head lists
+    the head's physical slots in slot order."""
+    j = 0
+    for i, k in enumerate(keep):
+        if k:
+            pool[slots_of_head[j]] = pool[slots_of_head[i]]
+            j += 1
+    return j

@@ -181,6 +181,31 @@ def compact(rows_by_head, keep, reserve):
 
 
 # --------------------------------------------------------------------------
+# incremental eviction: in place, within each head's own pages
+# --------------------------------------------------------------------------
+def compact_inplace_layout(kept, reserve, home_off, home_ids):
+    """Page table after in-place eviction (DBTrimKV Method 4: per-head paged
+    storage; ContourKV section 2: eviction shrinks storage, here without a
+    second pool).  Every head keeps its kept entries, in slot order, in the
+    first slots of its own pages, so its content equals the out-of-place
+    compaction's; its page list becomes the first
+    min(ceil((kept_h + reserve)/16), home pages of h) pages of its home list,
+    with page_off a prefix sum over heads in flat order; len = kept.
+
+    Returns (page_off, page_ids, len) as int64 arrays."""
+    kept = np.asarray(kept, np.int64)
+    home_off = np.asarray(home_off, np.int64)
+    home_ids = np.asarray(home_ids, np.int64)
+    want = -(-(kept + int(reserve)) // PAGE)
+    pages = np.minimum(want, np.diff(home_off))
+    page_off = np.zeros(len(kept) + 1, np.int64)
+    np.cumsum(pages, out=page_off[1:])
+    page_ids = np.concatenate([home_ids[home_off[h]:home_off[h] + pages[h]] for h in range(len(kept))] +
+                              [np.zeros(0, np.int64)])
+    return page_off, page_ids, kept.copy()
+
+
+# --------------------------------------------------------------------------
 # a4: renormalised decode attention with dropped mass
 # --------------------------------------------------------------------------
 def decode_attn(k_heads, v_heads, q, group, scale, keep=None, lse_ref=None):

@@ -263,6 +263,43 @@ def test_compaction_round_trip_and_layout():
             assert np.all(np.diff(out["pos"][h]) > 0)     # positions stay ascending
 
 
+def test_inplace_compaction_layout_and_sequential_shift():
+    """In-place eviction: a one-entry-at-a-time shift over a tiny pool (brute
+    force, in pure Python) leaves every head's kept rows, in order, in the
+    first slots of its own pages; read back through the oracle's new table
+    they equal the out-of-place rows.  The table is the home prefix of
+    ceil((kept + reserve)/16) pages, clamped to the home list; rows of other
+    heads are untouched."""
+    rng = np.random.default_rng(17)
+    for trial in range(30):
+        H = int(rng.integers(1, 6))
+        length = rng.integers(0, 60, H)
+        extra = rng.integers(0, 3, H)                            # spare home pages per head
+        home_pages = -(-length // 16) + extra
+        home_off = np.concatenate([[0], np.cumsum(home_pages)]).astype(np.int64)
+        n_pages = int(home_off[-1]) + 2
+        home_ids = rng.permutation(n_pages)[:home_off[-1]].astype(np.int64)
+        pool = list(rng.integers(0, 1 << 30, n_pages * 16))
+        keep = [rng.random(int(n)) < rng.uniform(0.2, 1.0) for n in length]
+        slots = [[int(home_ids[home_off[h] + i // 16]) * 16 + i % 16 for i in range(int(length[h]))]
+                 for h in range(H)]
+        rows = [[pool[x] for x in slots[h]] for h in range(H)]
+        reserve = int(rng.integers(0, 40))
+        before = list(pool)
+        kept = [brute.shift_in_place(pool, slots[h], keep[h].tolist()) for h in range(H)]
+        po, pi, ln = ref.compact_inplace_layout(kept, reserve, home_off, home_ids)
+        assert np.array_equal(ln, [int(k.sum()) for k in keep])
+        for h in range(H):
+            n = min(-(-(kept[h] + reserve) // 16), int(home_pages[h]))
+            assert po[h + 1] - po[h] == n
+            assert np.array_equal(pi[po[h]:po[h + 1]], home_ids[home_off[h]:home_off[h] + n])
+            got = [pool[int(pi[po[h] + j // 16]) * 16 + j % 16] for j in range(kept[h])]
+            assert got == [r for r, k in zip(rows[h], keep[h]) if k], (trial, h)
+        # slots outside every head's pages are untouched
+        owned = set(x for h in range(H) for x in slots[h])
+        assert all(pool[x] == before[x] for x in range(len(pool)) if x not in owned)
+
+
 # --------------------------------------------------------------------------
 # a4: renormalised decode attention (ContourKV problem definition, sections 1, 3)
 # --------------------------------------------------------------------------
