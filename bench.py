@@ -173,6 +173,9 @@ def timed_calls(call, reps):
     """Mean seconds per call of `reps` calls issued back to back between two
     events (so host launch latency overlaps the previous call), and the mean
     main-kernel time of `reps` single calls bracketed inside the library."""
+    import numpy as np
+    import torch
+    from retention_scored_decode_amd import trimkv as tk
     for _ in range(2):
         call()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -88,7 +88,8 @@ enum {
   TRIMKV_OP_DECODE_ATTN = 3,
   TRIMKV_OP_ATTN_MASS = 4,
   TRIMKV_OP_VALIDATE = 5,
-  TRIMKV_OP_DECODE_ERR = 6
+  TRIMKV_OP_DECODE_ERR = 6,
+  TRIMKV_OP_COMPACT_INPLACE = 7
 };
 
 /*
@@ -171,6 +172,39 @@ int trimkv_select_global(const trimkv_cache_t* cache, const float* score, int32_
 int trimkv_compact(const trimkv_cache_t* src, const uint8_t* keep, const int32_t* kept, int32_t reserve,
                    int64_t max_kept_total, trimkv_cache_t* dst, int64_t* pages_used, void* ws,
                    size_t ws_bytes, void* stream);
+
+/*
+ * trimkv_compact_inplace -- incremental eviction inside each head's own pages.
+ * DBTrimKV page, Method 4 (paged per-head storage) and ContourKV page,
+ * section 2 (eviction must shrink storage), without a second pool: suited to
+ * streaming decode, where each step drops a few entries per head.
+ * Every head keeps its kept entries (keep == 1), in slot order, in the first
+ * slots of its own pages; only the entries after its first dropped entry
+ * move.  The head's new page list is the first
+ * min(ceil((kept_h + reserve) / 16), home pages of h) pages of its home list,
+ * numbered by a prefix sum over heads into new_page_off / new_page_ids; then
+ * cache->len[h] = kept_h.  The pools and len of `cache` are updated in place;
+ * its page_off / page_ids are only read.  The caller's next view of the
+ * cache is {the same pools, new_page_off, new_page_ids, len}.
+ *   cache:        current view; each head's page list must be a prefix of its
+ *                 home list (true of a home table itself and of every table
+ *                 this call writes); n_pages * 16 must fit in 32 bits
+ *   keep, kept:   as trimkv_compact (kept may be NULL: counted here)
+ *   reserve:      spare slots per head for trimkv_append, within the head's
+ *                 home pages
+ *   home_off, home_ids: device int32 [n_heads + 1] and [home_off[n_heads]]:
+ *                 each head's own pages (for example the prefill table)
+ *   new_page_off: device int32 [n_heads + 1], out
+ *   new_page_ids: device int32 [home_off[n_heads]], out; both distinct from
+ *                 the cache's and the home table's arrays
+ *   ws:           trimkv_workspace_size(TRIMKV_OP_COMPACT_INPLACE, cache, 0, 0) bytes
+ * Counts that disagree with keep give an unspecified layout, with len
+ * clamped to the new pages.  Calls that overlap on one cache race.
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE.
+ */
+int trimkv_compact_inplace(trimkv_cache_t* cache, const uint8_t* keep, const int32_t* kept, int32_t reserve,
+                           const int32_t* home_off, const int32_t* home_ids, int32_t* new_page_off,
+                           int32_t* new_page_ids, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * trimkv_decode_attn -- renormalised GQA decode attention with dropped mass.

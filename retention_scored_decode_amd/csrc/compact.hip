@@ -241,6 +241,120 @@ __global__ void __launch_bounds__(NT) k_cmp_copy(int n_heads, const uint8_t* __r
   }
 }
 
+// ---------------------------------------------------------------------------
+// Incremental eviction in place: every head keeps its kept entries, in slot
+// order, in the first slots of its own pages, and its page list becomes the
+// first min(ceil((kept + reserve) / 16), home pages) pages of its home list
+// (the head's own allocation, of which the current list is a prefix).  Only
+// entries after the head's first dropped entry move, each to an earlier
+// slot, so a streaming step that drops a few entries per head moves a
+// suffix of each head instead of rewriting the cache into a second pool.
+//
+// One block per head walks the head in windows of NTP slots: a block scan of
+// the keep flags gives every kept entry its destination slot, and the
+// window's moves run in passes whose rows are all read before any is
+// written.  A destination never lies after its source and sources increase
+// from pass to pass, so no pass overwrites a row a later pass still reads,
+// and only this pass's reads can be overwritten by this pass's writes.
+template <int ROWB>
+__global__ void __launch_bounds__(NTP) k_cmp_shift(int n_heads, int reserve, const int32_t* __restrict__ page_off,
+                                                   const int32_t* __restrict__ page_ids, int32_t* __restrict__ len,
+                                                   const uint8_t* __restrict__ keep,
+                                                   const int32_t* __restrict__ head_kept,
+                                                   const int32_t* __restrict__ home_off,
+                                                   const int32_t* __restrict__ home_ids,
+                                                   int32_t* __restrict__ new_off, int32_t* __restrict__ new_ids,
+                                                   uint8_t* __restrict__ pk, uint8_t* __restrict__ pv,
+                                                   uint32_t* __restrict__ meta) {
+  constexpr int LPR = ROWB / 16;          // lanes per row
+  constexpr int GROUPS = NTP / LPR;       // row groups per block
+  constexpr int UNR = 4;                  // rows per group in flight
+  constexpr int PASS = GROUPS * UNR;      // rows per pass
+  __shared__ uint32_t s_src[NTP], s_dst[NTP];
+  __shared__ int64_t red[NWP + 1];
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & (WAVE - 1), wid = tid / WAVE;
+  auto pages_of = [&](int j) -> int64_t {
+    const int64_t want = ((int64_t)max(head_kept[j], 0) + reserve + PAGE - 1) / PAGE;
+    return min(want, (int64_t)home_off[j + 1] - home_off[j]);
+  };
+  // the new page list: a prefix sum over the earlier heads, then the head's home prefix
+  int64_t pb = 0;
+  for (int j = tid; j < h; j += NTP) pb += pages_of(j);
+  pb = wave_sum(pb);
+  if (lane == 0) red[wid] = pb;
+  lds_barrier();
+  pb = 0;
+#pragma unroll
+  for (int i = 0; i < NWP; ++i) pb += red[i];
+  const int64_t nh = pages_of(h);
+  const int64_t hb = home_off[h];
+  for (int64_t c = tid; c < nh; c += NTP) new_ids[pb + c] = home_ids[hb + c];
+  if (tid == 0) {
+    new_off[h] = (int32_t)pb;
+    if (h == n_heads - 1) new_off[n_heads] = (int32_t)(pb + nh);
+  }
+  lds_barrier();   // red is the scan's scratch below
+
+  int p0;
+  const int nv = head_valid(page_off, len, h, &p0);
+  const int part = tid % LPR, grp = tid / LPR;
+  int carry = 0;   // kept entries before the window
+  for (int s0 = 0; s0 < nv; s0 += NTP) {
+    const int i = s0 + tid;
+    int kf = 0;
+    uint32_t src = 0;
+    if (i < nv) {
+      kf = keep[((int64_t)p0 + i / PAGE) * PAGE + i % PAGE] != 0;
+      src = (uint32_t)page_ids[p0 + i / PAGE] * PAGE + i % PAGE;
+    }
+    int64_t tot64;
+    const int rank = (int)block_exclusive_scan<NTP>(kf, red, &tot64);
+    const int tot = (int)tot64;
+    if (carry == s0 && tot == min(NTP, nv - s0)) {   // nothing dropped yet: every entry stays
+      carry += tot;
+      continue;
+    }
+    if (kf) {
+      const int j = carry + rank;
+      s_src[rank] = src;
+      s_dst[rank] = (uint32_t)page_ids[p0 + j / PAGE] * PAGE + j % PAGE;
+    }
+    lds_barrier();
+    for (int r0 = 0; r0 < tot; r0 += PASS) {
+      u32x4 kv[UNR], vv[UNR];
+      uint32_t mv[UNR], dsl[UNR];
+      bool mov[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int r = r0 + grp + u * GROUPS;
+        const uint32_t s = r < tot ? s_src[r] : 0u;
+        dsl[u] = r < tot ? s_dst[r] : 0u;
+        mov[u] = r < tot && s != dsl[u];
+        if (mov[u]) {
+          kv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pk + (int64_t)s * ROWB + part * 16));
+          vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pv + (int64_t)s * ROWB + part * 16));
+          mv[u] = meta[(int64_t)(s / PAGE) * (2 * PAGE) + (part & 1) * PAGE + s % PAGE];
+        }
+      }
+      // every row of the pass is in registers before any thread overwrites one
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        if (mov[u]) {
+          const int64_t d = dsl[u];
+          __builtin_nontemporal_store(kv[u], reinterpret_cast<u32x4*>(pk + d * ROWB + part * 16));
+          __builtin_nontemporal_store(vv[u], reinterpret_cast<u32x4*>(pv + d * ROWB + part * 16));
+          if (part < 2) meta[(d / PAGE) * (2 * PAGE) + part * PAGE + d % PAGE] = mv[u];
+        }
+      }
+    }
+    carry += tot;
+    lds_barrier();   // s_src and s_dst are rewritten by the next window
+  }
+  if (tid == 0) len[h] = (int32_t)min((int64_t)carry, nh * PAGE);
+}
+
 CmpWs carve(const trimkv_cache_t* c, void* ws) {
   WsLayout L = compact_ws_layout(c);
   char* b = (char*)ws;
@@ -255,6 +369,34 @@ WsLayout compact_ws_layout(const trimkv_cache_t* c) {
   L.add(8);
   L.add(c->n_pages * PAGE * 8);
   return L;
+}
+
+int launch_compact_inplace(trimkv_cache_t* c, const uint8_t* keep, const int32_t* kept, int reserve,
+                           const int32_t* home_off, const int32_t* home_ids, int32_t* new_off, int32_t* new_ids,
+                           void* ws, hipStream_t st) {
+  const int H = c->n_heads;
+  CmpWs w{};
+  if (kept) {
+    w.head_kept = const_cast<int32_t*>(kept);
+  } else {
+    w.head_kept = (int32_t*)ws;
+    hipLaunchKernelGGL(k_cmp_count, dim3(H), dim3(NTP), 0, st, c->page_off, c->len, keep, w);
+  }
+  const int elt = c->dtype == TRIMKV_BF16 ? 2 : 4;
+#define TRIMKV_SHIFT(RB)                                                                                        \
+  hipLaunchKernelGGL(k_cmp_shift<RB>, dim3(H), dim3(NTP), 0, st, H, reserve, c->page_off, c->page_ids, c->len, \
+                     keep, w.head_kept, home_off, home_ids, new_off, new_ids, (uint8_t*)c->k, (uint8_t*)c->v,   \
+                     c->meta)
+  prof_begin(st);
+  switch (c->head_dim * elt) {
+    case 128: TRIMKV_SHIFT(128); break;
+    case 256: TRIMKV_SHIFT(256); break;
+    case 512: TRIMKV_SHIFT(512); break;
+    default: return TRIMKV_EUNSUPPORTED;
+  }
+  prof_end(st);
+#undef TRIMKV_SHIFT
+  return check_launch();
 }
 
 int launch_compact(const trimkv_cache_t* src, const uint8_t* keep, const int32_t* kept, int reserve,

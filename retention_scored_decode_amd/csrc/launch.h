@@ -47,6 +47,9 @@ int launch_select(const trimkv_cache_t* c, const float* score, int n_seg, const 
                   hipStream_t st);
 int launch_compact(const trimkv_cache_t* src, const uint8_t* keep, const int32_t* kept, int reserve,
                    int64_t max_kept_total, trimkv_cache_t* dst, int64_t* pages_used, void* ws, hipStream_t st);
+int launch_compact_inplace(trimkv_cache_t* c, const uint8_t* keep, const int32_t* kept, int reserve,
+                           const int32_t* home_off, const int32_t* home_ids, int32_t* new_off, int32_t* new_ids,
+                           void* ws, hipStream_t st);
 int launch_decode_attn_gated(const trimkv_cache_t* c, int n_seg, const int32_t* seg, const int32_t* t,
                              const uint8_t* keep, const void* q, int group, float scale, float* out, float* dropped,
                              float* lse_out, void* ws, hipStream_t st);

@@ -18,11 +18,11 @@ LIB_PATH = os.path.join(_HERE, "libtrimkv.so")
 PAGE = 16
 F32, BF16 = 0, 1
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ECAPACITY, EHIP, EINVARIANT = 0, -1, -2, -3, -4, -5, -6
-OP_SCORE, OP_SELECT, OP_COMPACT, OP_DECODE_ATTN, OP_ATTN_MASS, OP_VALIDATE, OP_DECODE_ERR = range(7)
+OP_SCORE, OP_SELECT, OP_COMPACT, OP_DECODE_ATTN, OP_ATTN_MASS, OP_VALIDATE, OP_DECODE_ERR, OP_COMPACT_INPLACE = range(8)
 
 EXPORTS = ["trimkv_log_beta", "trimkv_score", "trimkv_select_global", "trimkv_compact",
            "trimkv_decode_attn", "trimkv_decode_attn_gated", "trimkv_decode_attn_err", "trimkv_attn_mass",
-           "trimkv_allocate",
+           "trimkv_allocate", "trimkv_compact_inplace",
            "trimkv_allocate_floor", "trimkv_mark_recent", "trimkv_append",
            "trimkv_workspace_size", "trimkv_validate_cache", "trimkv_strerror", "trimkv_profile_next"]
 
@@ -57,6 +57,7 @@ def lib():
             "trimkv_score": [cp, i32, vp, vp, vp, vp],
             "trimkv_select_global": [cp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_compact": [cp, vp, vp, i32, i64, cp, vp, vp, sz, vp],
+            "trimkv_compact_inplace": [cp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_decode_attn": [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp],
             "trimkv_decode_attn_err": [cp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_decode_attn_gated": [cp, i32, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp],
@@ -200,6 +201,19 @@ def compact(src: Cache, keep: torch.Tensor, reserve: int, max_kept_total: int, d
     _check(lib().trimkv_compact(ctypes.byref(src.struct()), _p(keep), _p(kept), int(reserve), int(max_kept_total),
                                 ctypes.byref(dst.struct()), _p(pages_used), _p(ws), ws.numel(),
                                 _stream(stream)), "trimkv_compact")
+
+
+def compact_inplace(cache: Cache, keep: torch.Tensor, reserve: int, home_off: torch.Tensor,
+                    home_ids: torch.Tensor, new_page_off: torch.Tensor, new_page_ids: torch.Tensor,
+                    kept: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None) -> Cache:
+    """Evict in place; returns the new view (same pools and length tensor,
+    the new page table)."""
+    if ws is None:
+        ws = workspace(OP_COMPACT_INPLACE, cache)
+    _check(lib().trimkv_compact_inplace(ctypes.byref(cache.struct()), _p(keep), _p(kept), int(reserve),
+                                        _p(home_off), _p(home_ids), _p(new_page_off), _p(new_page_ids),
+                                        _p(ws), ws.numel(), _stream(stream)), "trimkv_compact_inplace")
+    return Cache(cache.k, cache.v, cache.meta, new_page_off, new_page_ids, cache.length)
 
 
 def decode_attn(cache: Cache, q: torch.Tensor, group: int, scale: float, out: torch.Tensor,

@@ -18,7 +18,7 @@ def declared():
 
 def test_exports_every_declared_symbol():
     names = declared()
-    assert len(names) == 16
+    assert len(names) == 17
     L = tk.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -112,6 +112,28 @@ def test_gated_argument_checks():
     assert g(ctypes.byref(c), 1, X, X, None, X, 17, F, X, X, None, X, need, None) == tk.EUNSUPPORTED
     f32 = fake_cache(dtype=tk.F32, head_dim=64)
     assert g(ctypes.byref(f32), 1, X, X, None, X, 4, F, X, X, None, X, 1 << 30, None) == tk.EUNSUPPORTED
+
+
+def test_compact_inplace_argument_checks():
+    """trimkv_compact_inplace: the new table must not alias the current or
+    the home table; keep aligned; slots in 32 bits; its own small workspace."""
+    L = tk.lib()
+    c = fake_cache()
+    need = L.trimkv_workspace_size(tk.OP_COMPACT_INPLACE, ctypes.byref(c), 0, 0)
+    assert need >= 4 * 4
+    f = L.trimkv_compact_inplace
+    A, B, C, D = (ctypes.c_void_p(x) for x in (0x21000, 0x22000, 0x23000, 0x24000))
+    assert f(ctypes.byref(c), X, None, 1, A, B, C, D, X, need - 1, None) == tk.EWORKSPACE
+    assert f(ctypes.byref(c), X, None, -1, A, B, C, D, X, need, None) == tk.EINVAL
+    assert f(ctypes.byref(c), None, None, 1, A, B, C, D, X, need, None) == tk.EINVAL
+    assert f(ctypes.byref(c), X, None, 1, None, B, C, D, X, need, None) == tk.EINVAL
+    assert f(ctypes.byref(c), X, None, 1, A, B, None, D, X, need, None) == tk.EINVAL
+    assert f(ctypes.byref(c), X, None, 1, A, B, ctypes.c_void_p(0x5000), D, X, need, None) == tk.EINVAL  # page_off
+    assert f(ctypes.byref(c), X, None, 1, A, B, C, ctypes.c_void_p(0x6000), X, need, None) == tk.EINVAL  # page_ids
+    assert f(ctypes.byref(c), X, None, 1, A, B, A, D, X, need, None) == tk.EINVAL
+    assert f(ctypes.byref(c), ctypes.c_void_p(0x10008), None, 1, A, B, C, D, X, need, None) == tk.EINVAL
+    huge = fake_cache(n_pages=1 << 28)
+    assert f(ctypes.byref(huge), X, None, 1, A, B, C, D, X, 1 << 20, None) == tk.EUNSUPPORTED
 
 
 def test_recency_floor_argument_checks():

@@ -696,3 +696,122 @@ def test_streaming_steps():
             assert np.array_equal(ref.gather_heads(k, po, pi, ln)[h], st["k"][h])
         cur = dst
     assert tk.validate_cache(cur, cuda(np.array([w.ctx + w.steps + 1], np.int32))) == tk.OK
+
+
+# --------------------------------------------------------------------------
+# incremental eviction in place (each head inside its own pages)
+# --------------------------------------------------------------------------
+def check_inplace(pc, cur, keep, reserve, home_off, home_ids, kept_given):
+    """Run trimkv_compact_inplace on the device view `cur` of host cache pc
+    (whose current rows are those of pc) and compare with the oracle."""
+    H = pc.n_heads
+    ov = OracleView(pc)
+    plane = plane_from_heads([k.astype(np.uint8) for k in keep], pc.page_off, pc.length, pc.n_pages, 0, np.uint8)
+    wk = np.array([int(k.sum()) for k in keep], np.int32)
+    new_off = torch.full((H + 1,), -1, dtype=torch.int32, device="cuda")
+    new_ids = torch.full((max(int(home_off[-1]), 1),), -1, dtype=torch.int32, device="cuda")
+    view = tk.compact_inplace(cur, cuda(plane), reserve, cuda(home_off, np.int32), cuda(home_ids, np.int32),
+                              new_off, new_ids, kept=cuda(wk) if kept_given else None)
+    wpo, wpi, wlen = ref.compact_inplace_layout(wk, reserve, home_off, home_ids)
+    po, pi, ln, k, v, lnb, pos = download_cache(view)
+    assert np.array_equal(po, wpo) and np.array_equal(ln, wlen)
+    assert np.array_equal(pi[:wpo[-1]], wpi)
+    for name, plane_now, want in (("k", k, ov.k_raw), ("v", v, ov.v_raw), ("pos", pos, ov.pos)):
+        got = ref.gather_heads(plane_now, po, pi[:max(int(po[-1]), 1)], ln)
+        for h in range(H):
+            assert np.array_equal(got[h], want[h][keep[h]]), (name, h)
+    got = ref.gather_heads(lnb, po, pi[:max(int(po[-1]), 1)], ln)
+    for h in range(H):
+        assert np.array_equal(f32_bits(got[h]), f32_bits(ov.lnb[h][keep[h]])), ("lnb", h)
+    return view
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
+def test_compact_inplace(dtype, d):
+    """Keep patterns per head: everything, nothing, random 30%, one drop
+    near the start, one near the end, every other entry; lengths of 0, 1,
+    16, 17 and up to 2500 (several 1024-slot windows).  The home table is the
+    cache's own (current view = home); reserve 0, 3 and 40 (clamped to the
+    home pages); counts given and counted."""
+    rng = np.random.default_rng(1100 + d)
+    pc = synth.random_ragged_cache(1200 + d, n_heads=12, d=d, dtype=dtype, max_len=2500, reserve=20)
+    pc.length[:4] = [0, 1, 16, 17]
+    for reserve, kept_given in ((0, True), (3, False), (40, True)):
+        keep = []
+        for h, n in enumerate(pc.length):
+            n = int(n)
+            pat = h % 6
+            if pat == 0:
+                kp = np.ones(n, bool)
+            elif pat == 1:
+                kp = np.zeros(n, bool)
+            elif pat == 2:
+                kp = rng.random(n) < 0.3
+            elif pat == 3:
+                kp = np.ones(n, bool)
+                kp[min(2, n - 1):min(3, n)] = False
+            elif pat == 4:
+                kp = np.ones(n, bool)
+                kp[max(n - 3, 0):max(n - 2, 0)] = False
+            else:
+                kp = np.arange(n) % 2 == 0
+            keep.append(kp)
+        announce("compact in place", dtype, d, "reserve", reserve, "lengths", pc.length.tolist())
+        cur = upload(pc)
+        check_inplace(pc, cur, keep, reserve, pc.page_off.astype(np.int64), pc.page_ids.astype(np.int64),
+                      kept_given)
+
+
+def test_streaming_steps_inplace():
+    """The streaming loop with in-place eviction: append -> score -> select ->
+    compact in place, every step checked against the oracle's selection and
+    kept rows (content equals the out-of-place rule); the home table is the
+    prefill table and every later view a prefix of it."""
+    w = SMALL["c5s"]
+    pc = synth.build_cache(w)
+    ov = OracleView(pc)
+    H, D = pc.n_heads, w.head_dim
+    M = w.budget()
+    cur = upload(pc)
+    home_off, home_ids = cur.page_off.clone(), cur.page_ids.clone()
+    home_off_np = pc.page_off.astype(np.int64)
+    home_ids_np = pc.page_ids.astype(np.int64)
+    tables = [(torch.empty(H + 1, dtype=torch.int32, device="cuda"),
+               torch.empty(int(home_off_np[-1]), dtype=torch.int32, device="cuda")) for _ in range(2)]
+    st = {"lnb": ov.lnb, "pos": ov.pos, "k": ov.k_raw, "v": ov.v_raw}
+    seg = cuda(np.array([0, H], np.int32))
+    bud = cuda(np.array([M], np.int64))
+    for s in range(1, w.steps + 1):
+        t = w.ctx + s
+        announce("stream step in place", s)
+        beta, kn, vn, _ = synth.stream_step(w, s)
+        t_dev = cuda(np.array([t], np.int32))
+        tk.append(cur, kv_dev(kn, "bf16"), kv_dev(vn, "bf16"), cuda(beta, np.float32), t_dev)
+        score = torch.empty(cur.n_pages * 16, dtype=torch.float32, device="cuda")
+        tk.score(cur, seg, t_dev, score)
+        keep = torch.empty(cur.n_pages * 16, dtype=torch.uint8, device="cuda")
+        kept = torch.empty(H, dtype=torch.int32, device="cuda")
+        tk.select_global(cur, score, seg, bud, keep, kept)
+        no, ni = tables[s % 2]
+        cur = tk.compact_inplace(cur, keep, 1, home_off, home_ids, no, ni, kept=kept)
+        lnb_new = ref.ln_beta(beta)
+        for h in range(H):
+            st["lnb"][h] = np.append(st["lnb"][h], lnb_new[h])
+            st["pos"][h] = np.append(st["pos"][h], np.int32(t - 1))
+            st["k"][h] = np.concatenate([st["k"][h], kn[h:h + 1]])
+            st["v"][h] = np.concatenate([st["v"][h], vn[h:h + 1]])
+        scores = [ref.score_f32(st["lnb"][h], t, st["pos"][h]) for h in range(H)]
+        wkeep, wkept = ref.select_global(scores, [0, H], [M])
+        assert np.array_equal(kept.cpu().numpy(), wkept), s
+        _, _, _, rows = ref.compact(st, wkeep, 1)
+        st = rows
+        wpo, wpi, wlen = ref.compact_inplace_layout(wkept, 1, home_off_np, home_ids_np)
+        po, pi, ln, k, v, lnb, pos = download_cache(cur)
+        assert np.array_equal(po, wpo) and np.array_equal(ln, wlen) and np.array_equal(pi[:wpo[-1]], wpi), s
+        pi = pi[:wpo[-1]]
+        for h in range(H):
+            assert np.array_equal(ref.gather_heads(pos, po, pi, ln)[h], st["pos"][h])
+            assert np.array_equal(f32_bits(ref.gather_heads(lnb, po, pi, ln)[h]), f32_bits(st["lnb"][h]))
+            assert np.array_equal(ref.gather_heads(k, po, pi, ln)[h], st["k"][h])
+            assert np.array_equal(ref.gather_heads(v, po, pi, ln)[h], st["v"][h])
+    assert tk.validate_cache(cur, cuda(np.array([w.ctx + w.steps + 1], np.int32))) == tk.OK
