@@ -355,6 +355,66 @@ def main():
         f_alloc.append(ev[1].elapsed_time(ev[2]) * 1e-3)
     assert int(b_fl.sum().item()) == M
 
+    # incremental eviction on streaming steps: the last step's kept set,
+    # compacted with 64 spare slots per head, becomes the home pool; each
+    # repetition appends one entry per head, scores, selects the same budget
+    # and evicts, once out of place into a scratch pool and once in place
+    # (both timed; the in-place result carries on to the next repetition)
+    RES = 64
+    cap_s = -(-(M * w.n_seg + H * RES) // 16) + H
+    home = tk.Cache.empty(H, cap_s, D, torch.bfloat16, device=dev)
+    used_h = torch.zeros(1, dtype=torch.int64, device=dev)
+    tk.compact(src, keep, RES, M * w.n_seg, home, used_h, ws=ws_cmp, kept=kept)
+    home_off, home_ids = home.page_off.clone(), home.page_ids.clone()
+    scratch = tk.Cache.empty(H, cap_s, D, torch.bfloat16, device=dev)
+    tables = [(torch.empty(H + 1, dtype=torch.int32, device=dev), torch.empty(cap_s, dtype=torch.int32, device=dev))
+              for _ in range(2)]
+    score_s = torch.empty(cap_s * 16, dtype=torch.float32, device=dev)
+    keep_s = torch.empty(cap_s * 16, dtype=torch.uint8, device=dev)
+    kept_s = torch.empty(H, dtype=torch.int32, device=dev)
+    used_s = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws_sel_s = tk.workspace(tk.OP_SELECT, home, w.n_seg)
+    ws_cmp_s = tk.workspace(tk.OP_COMPACT, home)
+    ws_inp = tk.workspace(tk.OP_COMPACT_INPLACE, home)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed + 77)
+    view = home
+    i_t, o_t, moved, valid = [], [], 0, 0
+    for s_ in range(1, args.steps + 3):
+        t_s = up(np.full(w.n_seg, w.t + s_, np.int32))
+        kn = (torch.randn((H, D), generator=gen, device=dev)).to(torch.bfloat16)
+        vn = (torch.randn((H, D), generator=gen, device=dev)).to(torch.bfloat16)
+        bn = torch.rand(H, generator=gen, device=dev) * 0.5 + 0.5
+        tk.append(view, kn, vn, bn, t_s[:1])
+        tk.score(view, seg, t_s, score_s)
+        tk.select_global(view, score_s, seg, budget, keep_s, kept_s, ws=ws_sel_s)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        tk.compact(view, keep_s, RES, M * w.n_seg, scratch, used_s, ws=ws_cmp_s, kept=kept_s)
+        ev[1].record()
+        nt_ = tables[s_ % 2]
+        len_before = view.length.clone()
+        view_next = tk.compact_inplace(view, keep_s, RES, home_off, home_ids, nt_[0], nt_[1], kept=kept_s, ws=ws_inp)
+        ev[2].record()
+        torch.cuda.synchronize()
+        if s_ > 2:   # the first repetitions load the kernels
+            o_t.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+            i_t.append(ev[1].elapsed_time(ev[2]) * 1e-3)
+            # entries that moved: every kept entry after its head's first dropped one
+            po_, ln_ = view.page_off.cpu().numpy(), len_before.cpu().numpy()
+            kp_ = keep_s[:int(po_[-1]) * 16].cpu().numpy()
+            for h in range(H):
+                n_ = int(ln_[h])
+                f_ = kp_[int(po_[h]) * 16:int(po_[h]) * 16 + n_]
+                z_ = np.flatnonzero(f_ == 0)
+                if len(z_):
+                    moved += int(np.count_nonzero(f_[z_[0]:]))
+                valid += n_
+        view = view_next
+    assert int(view.length.sum().item()) == M * w.n_seg
+    n_rep = len(i_t)
+    inp_algo = (1040 * moved + valid) / n_rep
+
     # sanity of the step's results (not timed)
     kept_np = kept.cpu().numpy()
     if w.n_seg == 1:
@@ -414,6 +474,15 @@ def main():
                                "main_kernel": "k_attn_bf16<128, 4>", "main_kernel_us": round(g_km * 1e6, 2),
                                "what": "retention-gated attention (weights e^z r renormalised) over the "
                                        "compacted cache; outside the timed step"},
+              "incremental_eviction": {
+                  "inplace_us": round(float(np.mean(i_t)) * 1e6, 2),
+                  "out_of_place_us": round(float(np.mean(o_t)) * 1e6, 2),
+                  "moved_entries_per_step": round(moved / n_rep, 1),
+                  "algo_bytes": int(inp_algo),
+                  "GBps": round(inp_algo / float(np.mean(i_t)) / 1e9, 1),
+                  "what": "streaming steps on this cache's kept set (append one entry per head, select %d, "
+                          "evict %d): trimkv_compact_inplace against trimkv_compact into a second pool"
+                          % (M, H)},
               "recency_floor": {"mark_us": round(float(np.median(f_mark)) * 1e6, 2),
                                 "allocate_us": round(float(np.median(f_alloc)) * 1e6, 2),
                                 "what": "trimkv_mark_recent (w = 64 on %d heads) and trimkv_allocate_floor; "
