@@ -27,38 +27,74 @@ __device__ __forceinline__ double xval(double S, int64_t B, double mbar, int H) 
   return S > 0.0 ? ((double)B * mbar) / S : (double)B / (double)H;
 }
 
-// One block.  O(H^2 / NT) rank computation; H <= 16384.
+// One block; H <= 16384.  Values every thread needs (the dropped masses for
+// the head-order sum S, then the fractional parts for the ranks) are staged
+// through LDS one chunk of NT heads at a time, each computed once.
 __global__ void __launch_bounds__(NT) k_allocate(const double* __restrict__ keptsum, const int32_t* __restrict__ len,
                                                  int H, int64_t B_total, int floor_w, double* __restrict__ mbar_out,
                                                  int64_t* __restrict__ b) {
   __shared__ int64_t tmp[NT / WAVE + 1];
   __shared__ double sS;
+  __shared__ double sbuf[NT];
   __shared__ int32_t srank[16384];
   auto fl_of = [&](int h) -> int64_t { return min((int64_t)floor_w, (int64_t)len[h]); };
   auto cap = [&](int h) -> int64_t { return (int64_t)len[h] - fl_of(h); };   // entries above the floor
   int64_t fsum = 0;
   for (int h = threadIdx.x; h < H; h += NT) fsum += fl_of(h);
   const int64_t B = max(B_total - block_sum(fsum, tmp), (int64_t)0);
-  if (threadIdx.x == 0) {
-    double S = 0.0;
-    for (int h = 0; h < H; ++h) S += 1.0 - keptsum[h];
-    sS = S;
+  // S = sum of the dropped masses in head order (one thread adds, chunk by chunk)
+  double S = 0.0;
+  for (int c0 = 0; c0 < H; c0 += NT) {
+    const int h = c0 + (int)threadIdx.x;
+    if (h < H) sbuf[threadIdx.x] = 1.0 - keptsum[h];
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int n = min(NT, H - c0);
+      for (int i = 0; i < n; ++i) S += sbuf[i];
+    }
+    __syncthreads();
   }
+  if (threadIdx.x == 0) sS = S;
   __syncthreads();
-  const double S = sS;
+  S = sS;
   auto frac_of = [&](int h) {
     const double x = xval(S, B, 1.0 - keptsum[h], H);
     return x - floor(x);
   };
-  // rank in (fraction desc, head asc) order
-  for (int h = threadIdx.x; h < H; h += NT) {
-    const double f = frac_of(h);
-    int32_t r = 0;
-    for (int o = 0; o < H; ++o) {
-      const double fo = frac_of(o);
-      r += (fo > f) || (fo == f && o < h);
+  // rank in (fraction desc, head asc) order: every thread's heads against
+  // each chunk of fractions
+  constexpr int PER = 16384 / NT;
+  double mine[PER];
+  int32_t rk[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int h = (int)threadIdx.x + u * NT;
+    mine[u] = h < H ? frac_of(h) : 0.0;
+    rk[u] = 0;
+  }
+  for (int c0 = 0; c0 < H; c0 += NT) {
+    const int o = c0 + (int)threadIdx.x;
+    if (o < H) sbuf[threadIdx.x] = frac_of(o);
+    __syncthreads();
+    const int n = min(NT, H - c0);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int h = (int)threadIdx.x + u * NT;
+      if (u * NT < H) {   // block-uniform
+        int32_t r = 0;
+        for (int i = 0; i < n; ++i) {
+          const double fo = sbuf[i];
+          r += (fo > mine[u]) || (fo == mine[u] && c0 + i < h);
+        }
+        rk[u] += r;
+      }
     }
-    srank[h] = r;
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int h = (int)threadIdx.x + u * NT;
+    if (h < H) srank[h] = rk[u];
   }
   __syncthreads();
   int64_t part = 0;
