@@ -633,6 +633,8 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
         for (int n = 0; n < NV; ++n) vop[n] = lds_read_tr_b64(vl + voff[n]);
       }
       lds_wait_all(kop, vop);   // the tile may be overwritten once these reads are done
+      // page i's gate words, taken before page i + 2's loads reuse their registers
+      const u32x4 glnb = g_lnb[buf & (GATED ? 1 : 0)], gpos = g_pos[buf & (GATED ? 1 : 0)];
       if (i + 2 < cnt) dma(B, i + 2, id_n, kwd_n);
       if (i + 3 < cnt) {
         id_n = cids[page0 + i + 3];
@@ -640,7 +642,7 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
       }
       if (i + 1 < cnt) kwm_n = keep4(i + 1);
       asm volatile("" ::: "memory");
-      math(i, kop, vop, kwr, g_lnb[buf & (GATED ? 1 : 0)], g_pos[buf & (GATED ? 1 : 0)]);
+      math(i, kop, vop, kwr, glnb, gpos);
     };
     dma(std::integral_constant<int, 0>{}, 0, cids[page0], keep4(0));
     if (cnt > 1) dma(std::integral_constant<int, 1>{}, 1, cids[page0 + 1], keep4(1));

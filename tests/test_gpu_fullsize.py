@@ -119,6 +119,107 @@ def test_full_size_pipeline(full_c2):
     say("attention checked on", len(sample), "heads; modes agree on all", H)
 
 
+def test_full_size_gated_and_incremental(full_c2):
+    """The two streaming-side rows at full size, in the launch configuration
+    the benchmark times: retention-gated decode over the compacted cache
+    (sampled heads against the float64 oracle, finite everywhere), and one
+    streaming step with in-place eviction on the kept set compacted with 64
+    spare slots per head (append one entry per head, select the same budget,
+    evict in place): selection and the new page table for every head, rows
+    for a sample of heads."""
+    w, pc = full_c2
+    H, G, D = pc.n_heads, w.group, w.head_dim
+    M = w.budget()
+    RES = 64
+    c = upload(pc)
+    seg_np = w.seg_head_begin()
+    seg = cuda(seg_np, np.int32)
+    score = torch.empty(pc.n_pages * 16, dtype=torch.float32, device="cuda")
+    tk.score(c, seg, cuda(np.full(w.n_seg, w.t, np.int32)), score)
+    keep = torch.empty(pc.n_pages * 16, dtype=torch.uint8, device="cuda")
+    kept = torch.empty(H, dtype=torch.int32, device="cuda")
+    bud = cuda(np.full(w.n_seg, M, np.int64))
+    tk.select_global(c, score, seg, bud, keep, kept)
+    cap = -(-(M + H * RES) // 16) + H
+    home = tk.Cache.empty(H, cap, D, torch.bfloat16)
+    used = torch.zeros(1, dtype=torch.int64, device="cuda")
+    tk.compact(c, keep, RES, M, home, used, kept=kept)
+    q_bits = synth.queries(w)
+    q_dev = torch.from_numpy(np.ascontiguousarray(q_bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+    q64 = synth.bf16_bits_to_f32(q_bits).astype(np.float64)
+    scale = 1.0 / math.sqrt(D)
+    nq = H * G
+    out_g = torch.empty((nq, D), dtype=torch.float32, device="cuda")
+    drop_g = torch.empty(nq, dtype=torch.float32, device="cuda")
+    t_dev = cuda(np.full(w.n_seg, w.t, np.int32))
+    tk.decode_attn_gated(home, seg, t_dev, q_dev, G, scale, out_g, drop_g)
+    # streaming step: append one entry per head at t = w.t + 1, then select and evict in place
+    rng = np.random.default_rng(4242)
+    kn = synth.f64_to_bf16_bits(rng.standard_normal((H, D)))
+    vn = synth.f64_to_bf16_bits(rng.standard_normal((H, D)))
+    bn = rng.uniform(0.5, 1.0, H).astype(np.float32)
+    t1 = w.t + 1
+    t1_dev = cuda(np.full(w.n_seg, t1, np.int32))
+    home_off, home_ids = home.page_off.clone(), home.page_ids.clone()
+    tk.append(home, kv_dev(kn, "bf16"), kv_dev(vn, "bf16"), cuda(bn, np.float32), t1_dev)
+    score2 = torch.empty(cap * 16, dtype=torch.float32, device="cuda")
+    tk.score(home, seg, t1_dev, score2)
+    keep2 = torch.empty(cap * 16, dtype=torch.uint8, device="cuda")
+    kept2 = torch.empty(H, dtype=torch.int32, device="cuda")
+    tk.select_global(home, score2, seg, bud, keep2, kept2)
+    new_off = torch.empty(H + 1, dtype=torch.int32, device="cuda")
+    new_ids = torch.empty(cap, dtype=torch.int32, device="cuda")
+    view = tk.compact_inplace(home, keep2, RES, home_off, home_ids, new_off, new_ids, kept=kept2)
+    torch.cuda.synchronize()
+    say("GPU gated decode and in-place step done")
+
+    # ---- oracle state: the kept set of the first selection, then the appended entries ----
+    po, pi, ln = pc.page_off, pc.page_ids, pc.length
+    lnb = [ref.ln_beta(b) for b in ref.gather_heads(pc.beta, po, pi, ln)]
+    pos = ref.gather_heads(pc.pos, po, pi, ln)
+    scores = [ref.score_f32(lnb[h], w.t, pos[h]) for h in range(H)]
+    keep1, kept1 = ref.select_global(scores, seg_np, [M])
+    assert np.array_equal(kept.cpu().numpy(), kept1)
+    sample = list(range(0, H, 17)) + [H - 1]
+    flat_k, flat_v = pc.k.reshape(-1, D), pc.v.reshape(-1, D)
+
+    # ---- gated decode on the sampled heads ----
+    og, dg = out_g.cpu().numpy(), drop_g.cpu().numpy()
+    assert np.all(np.isfinite(og)) and np.all((dg >= 0) & (dg <= 1))
+    K = [kv_f64(flat_k[ref.head_phys_slots(po, pi, ln, h)[keep1[h]]], pc.dtype) for h in sample]
+    V = [kv_f64(flat_v[ref.head_phys_slots(po, pi, ln, h)[keep1[h]]], pc.dtype) for h in sample]
+    gate = [scores[h][keep1[h]].astype(np.float64) for h in sample]
+    qs = np.concatenate([q64[h * G:(h + 1) * G] for h in sample])
+    rows = np.concatenate([np.arange(h * G, (h + 1) * G) for h in sample])
+    wout, wdrop, _ = ref.decode_attn_gated(K, V, qs, G, scale, gate)
+    assert np.max(np.abs(og[rows] - wout)) <= OUT_TOL
+    assert np.all(dg[rows] == 0.0)
+    say("gated decode checked on", len(sample), "heads")
+
+    # ---- in-place step: selection and table for every head, rows for the sample ----
+    lnb_new = ref.ln_beta(bn)
+    lnb2 = [np.append(lnb[h][keep1[h]], lnb_new[h]) for h in range(H)]
+    pos2 = [np.append(pos[h][keep1[h]], np.int32(t1 - 1)) for h in range(H)]
+    scores2 = [ref.score_f32(lnb2[h], t1, pos2[h]) for h in range(H)]
+    keep2w, kept2w = ref.select_global(scores2, seg_np, [M])
+    assert np.array_equal(kept2.cpu().numpy(), kept2w)
+    assert int(kept2w.sum()) == M
+    hpo = home_off.cpu().numpy().astype(np.int64)
+    hpi = home_ids.cpu().numpy().astype(np.int64)
+    wpo, wpi, wln = ref.compact_inplace_layout(kept2w, RES, hpo, hpi)
+    vpo, vpi, vln, vk, vv, vlnb, vpos = download_cache(view)
+    assert np.array_equal(vpo, wpo) and np.array_equal(vln, wln) and np.array_equal(vpi[:wpo[-1]], wpi)
+    vpi = vpi[:wpo[-1]]
+    for h in sample:
+        k_rows = np.concatenate([flat_k[ref.head_phys_slots(po, pi, ln, h)[keep1[h]]], kn[h:h + 1]])
+        v_rows = np.concatenate([flat_v[ref.head_phys_slots(po, pi, ln, h)[keep1[h]]], vn[h:h + 1]])
+        assert np.array_equal(ref.gather_heads(vk, vpo, vpi, vln)[h], k_rows[keep2w[h]]), ("k rows", h)
+        assert np.array_equal(ref.gather_heads(vv, vpo, vpi, vln)[h], v_rows[keep2w[h]]), ("v rows", h)
+        assert np.array_equal(ref.gather_heads(vpos, vpo, vpi, vln)[h], pos2[h][keep2w[h]])
+        assert np.array_equal(f32_bits(ref.gather_heads(vlnb, vpo, vpi, vln)[h]), f32_bits(lnb2[h][keep2w[h]]))
+    say("in-place eviction checked: table on all", H, "heads, rows on", len(sample))
+
+
 def test_full_size_batched_pipeline():
     """The 16-sequence batched workload at full size (4096 KV heads of 16K
     tokens, 16 per-sequence budgets): scores bit-exact for every head,

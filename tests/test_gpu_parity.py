@@ -332,17 +332,24 @@ def test_attention_modes(dtype, d, group):
                ref.decode_attn(kk, vv, q64, group, sc, lse_ref=lse_full.astype(np.float32).astype(np.float64)))
 
 
-@pytest.mark.parametrize("d,group", [(128, 4), (128, 7), (128, 1), (128, 16), (64, 4), (64, 3)])
-def test_gated_attention(d, group):
+@pytest.mark.parametrize("d,group,long", [(128, 4, False), (128, 7, False), (128, 1, False), (128, 16, False),
+                                           (64, 4, False), (64, 3, False), (128, 4, True)])
+def test_gated_attention(d, group, long):
     """Retention-gated decode attention (TRIM-KV section 2, attention
     modulation, at decode time): weights e^{z_j} r_j renormalised, plain and
     mask modes, against the float64 oracle given the float32 scores as ln r.
     Two segments with their own t; beta = 0 and 1 sprinkled in; head 0 has
     beta = 0 everywhere (no weight: out 0, dropped 1), head 1 beta = 0 on its
-    first 40 entries (whole pages of -inf gates before any finite logit)."""
-    rng = np.random.default_rng(900 + d + group)
-    pc = synth.random_ragged_cache(950 + group, n_heads=9, d=d, dtype="bf16", max_len=900, min_len=60, t=1000,
-                                   beta_dist=("beta", 20.0, 1.0))
+    first 40 entries (whole pages of -inf gates before any finite logit).
+    The long case (9 heads of 12K-16K entries) gives every wave of the launch
+    several pages, so the two-page load pipeline runs in its steady state."""
+    rng = np.random.default_rng(900 + d + group + long)
+    if long:
+        pc = synth.random_ragged_cache(960, n_heads=9, d=d, dtype="bf16", max_len=16384, min_len=12000, t=17000,
+                                       beta_dist=("beta", 200.0, 1.0))
+    else:
+        pc = synth.random_ragged_cache(950 + group, n_heads=9, d=d, dtype="bf16", max_len=900, min_len=60, t=1000,
+                                       beta_dist=("beta", 20.0, 1.0))
     pc.length[5] = 0   # an empty head
     beta = pc.beta.reshape(-1)
     for h in range(pc.n_heads):
@@ -356,7 +363,7 @@ def test_gated_attention(d, group):
             beta[sl[40:]] = 1.0
     ov = OracleView(pc)
     seg = np.array([0, 4, pc.n_heads], np.int32)
-    t_seg = np.array([1000, 1003], np.int32)
+    t_seg = np.array([17000, 17003] if long else [1000, 1003], np.int32)
     t_h = seg_t(seg, t_seg, pc.n_heads)
     gate = [g.astype(np.float64) for g in ov.scores(t_h)]
     q_dev, q64 = make_q(rng, pc.n_heads * group, d, "bf16", scale=1.5)
@@ -378,17 +385,21 @@ def test_gated_attention(d, group):
         assert np.all(got[0][:group] == 0) and np.all(got[1][:group] == 1)
 
 
-@pytest.mark.parametrize("d,group", [(128, 4), (128, 7), (128, 1), (128, 16), (64, 4)])
-def test_attention_error_output(d, group):
+@pytest.mark.parametrize("d,group,long", [(128, 4, False), (128, 7, False), (128, 1, False), (128, 16, False),
+                                           (64, 4, False), (128, 4, True)])
+def test_attention_error_output(d, group, long):
     """e_s(A) = ||mu - m_A||_2 (ContourKV section 1) beside the mask-mode
     outputs.  mu and m_A are checked element-wise against the float64
     oracle (2e-3); the norm against the oracle's within the bound those
     imply, 2 * sqrt(D) * 2e-3, and against the norm of the GPU's own mu and
     m_A within fp32 rounding.  Heads with an empty kept set and a fully
     kept set are included, and (D = 128, G = 4) heads of 0, 1, 16 and 17
-    entries."""
-    rng = np.random.default_rng(700 + d + group)
-    if (d, group) == (128, 4):   # edge lengths: no entries, one, one page, a page and one
+    entries.  The long case (9 heads of 12K-16K entries) runs the load
+    pipeline in its steady state (several pages per wave)."""
+    rng = np.random.default_rng(700 + d + group + long)
+    if long:
+        pc = synth.random_ragged_cache(870, n_heads=9, d=d, dtype="bf16", max_len=16384, min_len=12000)
+    elif (d, group) == (128, 4):   # edge lengths: no entries, one, one page, a page and one
         w = W["llama8b_32k"].scaled(layers=1, ctx=900)
         pc = synth.build_cache(w, lengths=np.array([600, 300, 0, 1, 16, 17, 900, 5], np.int32))
     else:
