@@ -304,12 +304,22 @@ def check_attn(got, want):
     assert np.all(np.abs(lse[fin] - wlse[fin]) <= 1e-4 * np.maximum(1, np.abs(wlse[fin])))
 
 
-@pytest.mark.parametrize("dtype,d,group", [("bf16", 128, 4), ("bf16", 128, 7), ("bf16", 128, 1), ("bf16", 128, 2),
-                                           ("bf16", 128, 8), ("bf16", 128, 16), ("bf16", 64, 4), ("bf16", 64, 3),
-                                           ("f32", 64, 1), ("f32", 128, 2)])
-def test_attention_modes(dtype, d, group):
-    rng = np.random.default_rng(d * 100 + group)
-    pc = synth.random_ragged_cache(300 + group, n_heads=7, d=d, dtype=dtype, max_len=700)
+@pytest.mark.parametrize("dtype,d,group,long", [("bf16", 128, 4, False), ("bf16", 128, 7, False),
+                                                ("bf16", 128, 1, False), ("bf16", 128, 2, False),
+                                                ("bf16", 128, 8, False), ("bf16", 128, 16, False),
+                                                ("bf16", 64, 4, False), ("bf16", 64, 3, False),
+                                                ("f32", 64, 1, False), ("f32", 128, 2, False),
+                                                ("bf16", 64, 4, True), ("bf16", 128, 16, True), ("bf16", 128, 1, True),
+                                                ("bf16", 128, 7, True)])
+def test_attention_modes(dtype, d, group, long):
+    """Plain, mask and reference modes against the float64 oracle.  Long
+    cases (7 heads of 12K-16K entries) give every wave several pages, so the
+    load pipeline runs in its steady state."""
+    rng = np.random.default_rng(d * 100 + group + long)
+    if long:
+        pc = synth.random_ragged_cache(330 + group, n_heads=7, d=d, dtype=dtype, max_len=16384, min_len=12000)
+    else:
+        pc = synth.random_ragged_cache(300 + group, n_heads=7, d=d, dtype=dtype, max_len=700)
     # force edge lengths: empty, one entry, one page, page + 1
     ov = OracleView(pc)
     q_dev, q64 = make_q(rng, pc.n_heads * group, d, dtype, scale=1.5)
