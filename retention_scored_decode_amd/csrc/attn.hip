@@ -143,12 +143,31 @@ __global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
   } else {
     b = w.item_off[h], e = w.item_off[h + 1], add = 0;
   }
-  // waves with an empty range (fewer pages than waves) wrote no partial
-  auto has = [&](int it) { return !a.waves || flat_begin(it, a.waves, P) < flat_begin(it + 1, a.waves, P); };
+  // waves with an empty range (fewer pages than waves) wrote no partial; with
+  // at least as many pages as waves every range is nonempty (no divisions)
+  const bool every = !a.waves || P >= a.waves;
+  auto has = [&](int it) { return every || flat_begin(it, a.waves, P) < flat_begin(it + 1, a.waves, P); };
   auto stat = [&](int it, int k) { return w.stats[((size_t)(it + add) * G + g) * 3 + k]; };
   __shared__ float red[2][NT / WAVE];
   __shared__ float sw[NT];
   __shared__ float sacc[NT];
+  // output: SPLIT threads per dimension, each over every SPLIT-th partial;
+  // with w.acc2 (error mode) the dropped keys' sums are merged alongside.
+  // The first UN partials of every thread are requested here, together with
+  // the statistics, so the output does not wait for a further round trip.
+  constexpr int SPLIT = NT / D;
+  constexpr int UN = 8;
+  const bool err = w.acc2 != nullptr;   // block-uniform
+  const int d = t % D, part = t / D;
+  float pv[UN], pv2[UN];
+#pragma unroll
+  for (int u = 0; u < UN; ++u) {
+    const int j = part + u * SPLIT;
+    const bool in = with_out && b + j < e;
+    const size_t at = ((size_t)(b + j + add) * G + g) * D + d;
+    pv[u] = in ? w.acc[at] : 0.f;
+    pv2[u] = in && err ? w.acc2[at] : 0.f;
+  }
   float M = -INFINITY;
   for (int it = b + t; it < e; it += NT)
     if (has(it)) M = fmaxf(M, stat(it, 0));
@@ -199,26 +218,27 @@ __global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
     }
   }
   if (!with_out) return;
-  // output: SPLIT threads per dimension, each over every SPLIT-th partial;
-  // with w.acc2 (error mode) the dropped keys' sums are merged alongside
-  constexpr int SPLIT = NT / D;
-  constexpr int UN = 8;
-  const bool err = w.acc2 != nullptr;   // block-uniform
-  const int d = t % D, part = t / D;
   float s = 0.f, s2 = 0.f;
   for (int it0 = b; it0 < e; it0 += NT) {
     const int n = min(NT, e - it0);
     if (t < n) sw[t] = (M != -INFINITY && has(it0 + t)) ? exp2f(stat(it0 + t, 0) - M) : 0.f;
     lds_barrier();
     for (int j0 = part; j0 < n; j0 += SPLIT * UN) {
+      const bool first = it0 == b && j0 == part;   // the prefetched partials
       float v[UN], v2[UN], wt[UN];
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
         const int j = j0 + u * SPLIT;
         wt[u] = j < n ? sw[j] : 0.f;
         const size_t at = ((size_t)(it0 + j + add) * G + g) * D + d;
-        v[u] = wt[u] != 0.f ? w.acc[at] : 0.f;
-        v2[u] = err && wt[u] != 0.f ? w.acc2[at] : 0.f;
+        // partials of waves without pages hold no data: selected away, never multiplied
+        if (first) {
+          v[u] = wt[u] != 0.f ? pv[u] : 0.f;
+          v2[u] = wt[u] != 0.f ? pv2[u] : 0.f;
+        } else {
+          v[u] = wt[u] != 0.f ? w.acc[at] : 0.f;
+          v2[u] = err && wt[u] != 0.f ? w.acc2[at] : 0.f;
+        }
       }
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
