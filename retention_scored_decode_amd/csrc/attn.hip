@@ -121,16 +121,145 @@ __device__ __forceinline__ int64_t flat_wave(int64_t p, int64_t W, int64_t P) { 
 // Merge all partials of query row g of KV head h: M = max of the partial
 // maxima, kept and dropped sums rescaled to M, O rescaled and divided by the
 // kept sum.  A head without partials has an empty kept set: out = 0,
-// dropped = 1, lse = -inf.  One block per query row; every partial's loads
-// are issued together; fixed summation order.  Partials of head h: fp32
-// path, items item_off[h] .. item_off[h+1]-1; bf16 path, index w + h for
-// every wave w whose range meets the head's pages.
+// dropped = 1, lse = -inf.  Partials of head h: fp32 path, items
+// item_off[h] .. item_off[h+1]-1 (add = 0); bf16 path, index w + h (add = h)
+// for every wave w in [b, e), whose ranges meet the head's pages.  With fewer
+// pages than waves (every = false) waves with an empty range wrote no
+// partial and are skipped.
+//
+// One wave per query row and no block barriers: lane j holds the statistics
+// of partial j, lane l accumulates output dimensions l, l + 64 (D = 128).
+// The first MB partials' outputs are requested together with the
+// statistics, so a row costs one round trip.  Every sum runs in a fixed
+// order (partials ascending per lane, then a xor butterfly), so results are
+// run-to-run identical whichever wave merges.
+template <int D>
+__device__ void merge_row(const AttnArgs& a, int h, int g, int b, int e, int add, bool every, int64_t P,
+                          int with_out) {
+  constexpr int DL = D / WAVE;   // output dimensions per lane
+  constexpr int MB = 16;         // partial outputs per batch of loads
+  const AttnWs& w = a.w;
+  const int G = a.group;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int n = e - b;
+  auto has = [&](int it) { return every || flat_begin(it, a.waves, P) < flat_begin(it + 1, a.waves, P); };
+  const int ss = 3 * G;   // floats between consecutive partials' statistics
+  const float* st = w.stats + (size_t)(b + add) * ss + g * 3;          // partial j: st + j * ss
+  const float* ac = w.acc + ((size_t)(b + add) * G + g) * D + lane;    // partial j, dim lane + 64k: ac + j * G * D + 64k
+  const float* ac2 = w.acc2 ? w.acc2 + ((size_t)(b + add) * G + g) * D + lane : nullptr;
+  const bool err = ac2 != nullptr;   // wave-uniform
+
+  // batch of MB partial outputs starting at partial j0 (zeros past the end)
+  const int gs = G * D;   // floats between consecutive partials of the row
+  float v[MB][DL], v2[MB][DL];
+  auto load = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < MB; ++u)
+#pragma unroll
+      for (int k = 0; k < DL; ++k) {
+        const bool in = j0 + u < n;
+        const int at = (j0 + u) * gs + 64 * k;
+        v[u][k] = in ? ac[at] : 0.f;
+        v2[u][k] = in && err ? ac2[at] : 0.f;
+      }
+  };
+  if (with_out) load(0);   // in flight with the statistics
+  // statistics of partial j = lane (+ 64 per further batch)
+  float m0 = -INFINITY, l0 = 0.f, d0 = 0.f;
+  const bool v0 = lane < n && has(b + lane);
+  if (v0) {
+    m0 = st[lane * ss];
+    l0 = st[lane * ss + 1];
+    d0 = st[lane * ss + 2];
+  }
+  float M = m0;
+  for (int j = WAVE + lane; j - lane < n; j += WAVE)
+    if (j < n && has(b + j)) M = fmaxf(M, st[j * ss]);
+#pragma unroll
+  for (int s = WAVE / 2; s > 0; s >>= 1) M = fmaxf(M, __shfl_xor(M, s, WAVE));
+  // weight of each partial: 2^(m_j - M), zero for partials without data
+  auto weight = [&](float mj, bool valid) { return valid && M != -INFINITY ? exp2f(mj - M) : 0.f; };
+  const float w0 = weight(m0, v0);
+  float la = l0 * w0, ld = d0 * w0;
+  for (int j = WAVE + lane; j - lane < n; j += WAVE) {
+    if (j < n && has(b + j)) {
+      const float wj = weight(st[j * ss], true);
+      la += st[j * ss + 1] * wj;
+      ld += st[j * ss + 2] * wj;
+    }
+  }
+#pragma unroll
+  for (int s = WAVE / 2; s > 0; s >>= 1) {
+    la += __shfl_xor(la, s, WAVE);
+    ld += __shfl_xor(ld, s, WAVE);
+  }
+  if (lane == 0) {
+    const int qh = h * G + g;
+    const float l2 = la > 0.f ? M + log2f(la) : -INFINITY;  // base-2 LSE of the kept set
+    const float lse = l2 * LN2;
+    if (a.lse_out) a.lse_out[qh] = lse;
+    if (w.lse2) w.lse2[qh] = l2;
+    if (a.dropped) {
+      float dm = 1.f;
+      if (la > 0.f) dm = a.lse_ref ? -expm1f(lse - a.lse_ref[qh]) : ld / (la + ld);
+      a.dropped[qh] = dm;
+    }
+  }
+  if (!with_out) return;
+  float s[DL], s2[DL];
+#pragma unroll
+  for (int k = 0; k < DL; ++k) s[k] = s2[k] = 0.f;
+  float wl = w0;   // weight of partial j0 - j0 % 64 + lane
+  for (int j0 = 0; j0 < n; j0 += MB) {
+    if (j0 > 0) {
+      if (j0 % WAVE == 0) {
+        const int j = j0 + lane;
+        const bool vj = j < n && has(b + j);
+        wl = weight(vj ? st[j * ss] : -INFINITY, vj);
+      }
+      load(j0);
+    }
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      // partials without data hold stale words: selected away, never multiplied
+      const float wt = __shfl(wl, j0 % WAVE + u, WAVE);
+      const bool use = j0 + u < n && wt != 0.f;
+#pragma unroll
+      for (int k = 0; k < DL; ++k) {
+        s[k] += use ? v[u][k] * wt : 0.f;
+        if (err) s2[k] += use ? v2[u][k] * wt : 0.f;
+      }
+    }
+  }
+  float q2 = 0.f;
+#pragma unroll
+  for (int k = 0; k < DL; ++k) {
+    const size_t o = ((size_t)h * G + g) * D + lane + 64 * k;
+    const float mA = la > 0.f ? s[k] / la : 0.f;
+    a.out[o] = mA;
+    if (err) {
+      // dense output over every key: kept and dropped sums share the maximum
+      const float mu = la + ld > 0.f ? (s[k] + s2[k]) / (la + ld) : 0.f;
+      if (a.mu) a.mu[o] = mu;
+      q2 += (mu - mA) * (mu - mA);
+    }
+  }
+  if (err) {   // e_s(A) = || mu - m_A ||_2, fixed-order sum over the D dimensions
+#pragma unroll
+    for (int s = WAVE / 2; s > 0; s >>= 1) q2 += __shfl_xor(q2, s, WAVE);
+    if (lane == 0) a.err[(size_t)h * G + g] = sqrtf(q2);
+  }
+}
+
+// Merge kernel: one wave per query row, over the partials the main kernel
+// left in the workspace.
 template <int D>
 __global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
   const AttnWs& w = a.w;
   const int G = a.group;
-  const int h = blockIdx.x / G, g = blockIdx.x % G;
-  const int t = threadIdx.x, lane = t & (WAVE - 1), wid = t / WAVE;
+  const int row = blockIdx.x * (NT / WAVE) + __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+  if (row >= a.n_heads * G) return;   // per-wave exit: no block barriers below
+  const int h = row / G, g = row % G;
   int b, e, add;
   const int64_t P = a.page_off[a.n_heads];
   if (a.waves) {
@@ -146,137 +275,7 @@ __global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
   // waves with an empty range (fewer pages than waves) wrote no partial; with
   // at least as many pages as waves every range is nonempty (no divisions)
   const bool every = !a.waves || P >= a.waves;
-  auto has = [&](int it) { return every || flat_begin(it, a.waves, P) < flat_begin(it + 1, a.waves, P); };
-  auto stat = [&](int it, int k) { return w.stats[((size_t)(it + add) * G + g) * 3 + k]; };
-  __shared__ float red[2][NT / WAVE];
-  __shared__ float sw[NT];
-  __shared__ float sacc[NT];
-  // output: SPLIT threads per dimension, each over every SPLIT-th partial;
-  // with w.acc2 (error mode) the dropped keys' sums are merged alongside.
-  // The first UN partials of every thread are requested here, together with
-  // the statistics, so the output does not wait for a further round trip.
-  constexpr int SPLIT = NT / D;
-  constexpr int UN = 8;
-  const bool err = w.acc2 != nullptr;   // block-uniform
-  const int d = t % D, part = t / D;
-  float pv[UN], pv2[UN];
-#pragma unroll
-  for (int u = 0; u < UN; ++u) {
-    const int j = part + u * SPLIT;
-    const bool in = with_out && b + j < e;
-    const size_t at = ((size_t)(b + j + add) * G + g) * D + d;
-    pv[u] = in ? w.acc[at] : 0.f;
-    pv2[u] = in && err ? w.acc2[at] : 0.f;
-  }
-  float M = -INFINITY;
-  for (int it = b + t; it < e; it += NT)
-    if (has(it)) M = fmaxf(M, stat(it, 0));
-#pragma unroll
-  for (int d = WAVE / 2; d > 0; d >>= 1) M = fmaxf(M, __shfl_xor(M, d, WAVE));
-  if (lane == 0) red[0][wid] = M;
-  lds_barrier();
-  M = red[0][0];
-#pragma unroll
-  for (int i = 1; i < NT / WAVE; ++i) M = fmaxf(M, red[0][i]);
-  lds_barrier();
-  float la = 0.f, ld = 0.f;
-  if (M != -INFINITY) {
-    for (int it = b + t; it < e; it += NT) {
-      if (!has(it)) continue;
-      const float sc = exp2f(stat(it, 0) - M);
-      la += stat(it, 1) * sc;
-      ld += stat(it, 2) * sc;
-    }
-  }
-#pragma unroll
-  for (int d = WAVE / 2; d > 0; d >>= 1) {
-    la += __shfl_xor(la, d, WAVE);
-    ld += __shfl_xor(ld, d, WAVE);
-  }
-  if (lane == 0) {
-    red[0][wid] = la;
-    red[1][wid] = ld;
-  }
-  lds_barrier();
-  la = 0.f;
-  ld = 0.f;
-#pragma unroll
-  for (int i = 0; i < NT / WAVE; ++i) {
-    la += red[0][i];
-    ld += red[1][i];
-  }
-  if (t == 0) {
-    const int qh = h * G + g;
-    const float l2 = la > 0.f ? M + log2f(la) : -INFINITY;  // base-2 LSE of the kept set
-    const float lse = l2 * LN2;
-    if (a.lse_out) a.lse_out[qh] = lse;
-    if (w.lse2) w.lse2[qh] = l2;
-    if (a.dropped) {
-      float dm = 1.f;
-      if (la > 0.f) dm = a.lse_ref ? -expm1f(lse - a.lse_ref[qh]) : ld / (la + ld);
-      a.dropped[qh] = dm;
-    }
-  }
-  if (!with_out) return;
-  float s = 0.f, s2 = 0.f;
-  for (int it0 = b; it0 < e; it0 += NT) {
-    const int n = min(NT, e - it0);
-    if (t < n) sw[t] = (M != -INFINITY && has(it0 + t)) ? exp2f(stat(it0 + t, 0) - M) : 0.f;
-    lds_barrier();
-    for (int j0 = part; j0 < n; j0 += SPLIT * UN) {
-      const bool first = it0 == b && j0 == part;   // the prefetched partials
-      float v[UN], v2[UN], wt[UN];
-#pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        const int j = j0 + u * SPLIT;
-        wt[u] = j < n ? sw[j] : 0.f;
-        const size_t at = ((size_t)(it0 + j + add) * G + g) * D + d;
-        // partials of waves without pages hold no data: selected away, never multiplied
-        if (first) {
-          v[u] = wt[u] != 0.f ? pv[u] : 0.f;
-          v2[u] = wt[u] != 0.f ? pv2[u] : 0.f;
-        } else {
-          v[u] = wt[u] != 0.f ? w.acc[at] : 0.f;
-          v2[u] = err && wt[u] != 0.f ? w.acc2[at] : 0.f;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        s += v[u] * wt[u];
-        s2 += v2[u] * wt[u];
-      }
-    }
-    lds_barrier();
-  }
-  sacc[t] = s;
-  if (err) sw[t] = s2;   // sw is free after the last batch
-  lds_barrier();
-  if (part == 0) {
-    float tot = sacc[d], tot2 = 0.f;
-#pragma unroll
-    for (int q = 1; q < SPLIT; ++q) tot += sacc[q * D + d];
-    const float mA = la > 0.f ? tot / la : 0.f;
-    a.out[((size_t)h * G + g) * D + d] = mA;
-    if (err) {
-      tot2 = sw[d];
-#pragma unroll
-      for (int q = 1; q < SPLIT; ++q) tot2 += sw[q * D + d];
-      // dense output over every key: kept and dropped sums share the maximum
-      const float mu = la + ld > 0.f ? (tot + tot2) / (la + ld) : 0.f;
-      if (a.mu) a.mu[((size_t)h * G + g) * D + d] = mu;
-      sacc[d] = (mu - mA) * (mu - mA);
-    }
-  }
-  if (err) {   // e_s(A) = || mu - m_A ||_2, fixed-order sum over the D dimensions
-    lds_barrier();
-    if (t < WAVE) {
-      float q2 = 0.f;
-      for (int k = t; k < D; k += WAVE) q2 += sacc[k];
-#pragma unroll
-      for (int k = WAVE / 2; k > 0; k >>= 1) q2 += __shfl_xor(q2, k, WAVE);
-      if (t == 0) a.err[(size_t)h * G + g] = sqrtf(q2);
-    }
-  }
+  merge_row<D>(a, h, g, b, e, add, every, P, with_out);
 }
 
 // s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n only
@@ -433,13 +432,30 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
   typedef __attribute__((address_space(1))) const void* gptr;
   typedef __attribute__((address_space(3))) void* lptr;
 
+  // physical pages of a segment's first three CSR pages: they depend only on
+  // the wave's range, so they are requested before the head is known
+  // (indices clamped into the range; a page past the segment is unused)
+  int id0 = cids[p], id1 = cids[min(p + 1, pend - 1)], id2 = cids[min(p + 2, pend - 1)];
   int h = head_of(p);
   while (true) {
     // ---- one head segment: CSR pages [p, send) of head h ----
-    const int hb = pg(h);
-    const int send = min(pend, pg(h + 1));
+    // B operand of QK MFMA u: dims 32u + 8r .. +7 of query head col.  Columns
+    // col >= G repeat query head 0: their logits, weights and outputs follow
+    // column 0's and are never stored.  Requested first, so that the head's
+    // table loads below overlap it, and awaited before the first page load
+    // (nothing is then outstanding at the page loop but the pages).
+    u32x4 qop[KU];
+    {
+      const uint8_t* qrow = (const uint8_t*)a.q + ((size_t)h * G + (col < G ? col : 0)) * D * 2 + 16 * r;
+#pragma unroll
+      for (int u = 0; u < KU; ++u) qop[u] = *reinterpret_cast<const u32x4*>(qrow + 64 * u);
+    }
+    // the head's table words, requested together
+    const int hb = pg(h), he = pg(h + 1), hlen = __builtin_amdgcn_readfirstlane(clen[h]);
+    asm volatile("" ::: "memory");
+    const int send = min(pend, he);
     const int page0 = p, cnt = send - p;
-    const int v0 = clen[h] - (p - hb) * PAGE;
+    const int v0 = hlen - (p - hb) * PAGE;
     const int nv = v0 < 0 ? 0 : (v0 > cnt * PAGE ? cnt * PAGE : v0);   // valid entries of the segment
     const c_u32x4 ckeep = (c_u32x4)(a.keep + (int64_t)page0 * PAGE);   // 16 keep bytes per page
     int t_h = 0;   // decode step of the head's segment (gated modes)
@@ -453,16 +469,6 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
       t_h = __builtin_amdgcn_readfirstlane(((c_i32)a.tseg)[lo]);
     }
 
-    // B operand of QK MFMA u: dims 32u + 8r .. +7 of query head col (zero for col >= G)
-    u32x4 qop[KU];
-    {
-      const uint8_t* qrow = (const uint8_t*)a.q + ((size_t)h * G + (col < G ? col : 0)) * D * 2 + 16 * r;
-#pragma unroll
-      for (int u = 0; u < KU; ++u) {
-        qop[u] = *reinterpret_cast<const u32x4*>(qrow + 64 * u);
-        if (col >= G) qop[u] = (u32x4){0u, 0u, 0u, 0u};
-      }
-    }
     float m = -INFINITY, la = 0.f, ld = 0.f;
     float nm = INFINITY;   // -m, or +inf while m = -inf (every finite logit then forces an update)
     float4_t acc[LOGITS ? 1 : NV], acc2[ERR ? NV : 1];
@@ -633,7 +639,7 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
     // (scalar loads), so no load is issued behind a dependent table read.
     const u32x4 all_kept = (u32x4){~0u, ~0u, ~0u, ~0u};
     auto keep4 = [&](int i) -> u32x4 { return MASKED ? ckeep[i] : all_kept; };
-    int64_t id_n = cnt > 2 ? cids[page0 + 2] : 0;        // page of the next load (i + 2)
+    int64_t id_n = id2;                                  // page of the next load (i + 2)
     u32x4 kwd_n = cnt > 2 ? keep4(2) : all_kept;         // its keep bytes
     u32x4 kwm_n = keep4(0);                              // keep bytes of the next page computed
     auto step = [&](auto B, int i) {
@@ -664,8 +670,9 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
       asm volatile("" ::: "memory");
       math(i, kop, vop, kwr, glnb, gpos);
     };
-    dma(std::integral_constant<int, 0>{}, 0, cids[page0], keep4(0));
-    if (cnt > 1) dma(std::integral_constant<int, 1>{}, 1, cids[page0 + 1], keep4(1));
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));   // the query operand
+    dma(std::integral_constant<int, 0>{}, 0, id0, keep4(0));
+    if (cnt > 1) dma(std::integral_constant<int, 1>{}, 1, id1, keep4(1));
     for (int i = 0; i < cnt; i += 2) {
       step(std::integral_constant<int, 0>{}, i);
       if (i + 1 < cnt) step(std::integral_constant<int, 1>{}, i + 1);
@@ -702,6 +709,9 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
     }
     p = send;
     if (p >= pend) break;
+    id0 = cids[p];
+    id1 = cids[min(p + 1, pend - 1)];
+    id2 = cids[min(p + 2, pend - 1)];
     h = head_of(p);
   }
 }
@@ -881,6 +891,13 @@ int launch_main(const trimkv_cache_t* c, AttnArgs& a, hipStream_t st) {
   return TRIMKV_OK;
 }
 
+// Merge launch: one wave per query row.
+void launch_merge(const trimkv_cache_t* c, const AttnArgs& a, int with_out, hipStream_t st) {
+  const unsigned blocks = (unsigned)(((int64_t)c->n_heads * a.group + NT / WAVE - 1) / (NT / WAVE));
+  if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(blocks), dim3(NT), 0, st, a, with_out);
+  else hipLaunchKernelGGL(k_attn_merge<64>, dim3(blocks), dim3(NT), 0, st, a, with_out);
+}
+
 // Partial slots: fp32 work items, or flat waves + heads.
 int64_t partial_slots(const trimkv_cache_t* c) {
   return c->dtype == TRIMKV_F32 ? max_chunks(c, CHA_F32) : (int64_t)FLAT_WMAX + c->n_heads;
@@ -932,8 +949,7 @@ int launch_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float
   int rc = keep ? launch_main<A_MASK>(c, a, st) : launch_main<A_PLAIN>(c, a, st);
   prof_end(st);
   if (rc) return rc;
-  if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(c->n_heads * group), dim3(NT), 0, st, a, 1);
-  else hipLaunchKernelGGL(k_attn_merge<64>, dim3(c->n_heads * group), dim3(NT), 0, st, a, 1);
+  launch_merge(c, a, 1, st);
   return check_launch();
 }
 
@@ -946,8 +962,7 @@ int launch_decode_attn_err(const trimkv_cache_t* c, const uint8_t* keep, const v
   int rc = launch_main<A_ERR>(c, a, st);
   prof_end(st);
   if (rc) return rc;
-  if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(c->n_heads * group), dim3(NT), 0, st, a, 1);
-  else hipLaunchKernelGGL(k_attn_merge<64>, dim3(c->n_heads * group), dim3(NT), 0, st, a, 1);
+  launch_merge(c, a, 1, st);
   return check_launch();
 }
 
@@ -962,8 +977,7 @@ int launch_decode_attn_gated(const trimkv_cache_t* c, int n_seg, const int32_t* 
   int rc = keep ? launch_main<A_GMASK>(c, a, st) : launch_main<A_GPLAIN>(c, a, st);
   prof_end(st);
   if (rc) return rc;
-  if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(c->n_heads * group), dim3(NT), 0, st, a, 1);
-  else hipLaunchKernelGGL(k_attn_merge<64>, dim3(c->n_heads * group), dim3(NT), 0, st, a, 1);
+  launch_merge(c, a, 1, st);
   return check_launch();
 }
 
@@ -980,8 +994,7 @@ int launch_attn_mass(const trimkv_cache_t* c, const void* q, int group, float sc
   int rc = launch_main<A_LOGITS>(c, a, st);
   prof_end(st);
   if (rc) return rc;
-  if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(c->n_heads * group), dim3(NT), 0, st, a, 0);
-  else hipLaunchKernelGGL(k_attn_merge<64>, dim3(c->n_heads * group), dim3(NT), 0, st, a, 0);
+  launch_merge(c, a, 0, st);
   const int64_t blocks = (c->n_pages + 63) / 64;
   hipLaunchKernelGGL(k_mass, dim3((unsigned)blocks), dim3(256), 0, st, c->page_off, c->len, c->n_heads, group,
                      c->n_pages * PAGE, w, mass);
