@@ -40,7 +40,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cold-reps", type=int, default=10, help="flushed repetitions of the decode stage")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="llama8b_32k")
+    ap.add_argument("--workload", default="llama8b_32k",
+                    help="llama8b_32k (the benchmark step), batched16_16k (the same step on 16 sequences), "
+                         "qwen8b_128k (mass -> dropped-mass budgets -> compaction -> decode), "
+                         "stream_gqa7 (generated steps: append, score, select, attend, evict)")
+    ap.add_argument("--stream-steps", type=int, default=0,
+                    help="generated steps of stream_gqa7 (default: the workload's 8192)")
     ap.add_argument("--calib", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -219,6 +224,10 @@ def main():
     from retention_scored_decode_amd import trimkv as tk
 
     w = synth.WORKLOADS[args.workload]
+    if w.name == "qwen8b_128k":
+        return bench_mass_pipeline(args, w)
+    if w.name == "stream_gqa7":
+        return bench_streaming(args, w)
     dev = "cuda"
     torch.cuda.set_device(0)
     t0 = time.time()
@@ -558,6 +567,282 @@ def cpu_baseline(w, pc, M):
                       "scores + global selection over all %d entries" % (H, ent, N),
             "select_entries_per_s": round(N / (t2 - t1), 1),
             "score_s": round(t1 - t0, 2), "select_s": round(t2 - t1, 2), "attn_s": round(t4 - t3, 3)}
+
+
+def _upload_cache(pc, dev):
+    """Device copy of a synthetic cache: K/V bf16 pools, ln beta (computed on
+    the device, as the benchmark step does) and positions, page table."""
+    import numpy as np
+    import torch
+    from retention_scored_decode_amd import trimkv as tk
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    meta = torch.zeros((pc.n_pages, 2, 16), dtype=torch.int32, device=dev)
+    meta[:, 1, :] = up(pc.pos)
+    tk.log_beta(up(pc.beta), meta, out_page_stride=32)
+    return tk.Cache(bf(pc.k), bf(pc.v), meta, up(pc.page_off), up(pc.page_ids), up(pc.length)), up, bf
+
+
+def _stage_json(algo, t, kt=None, kernels=None):
+    out = {}
+    for s, b in algo.items():
+        gbs = b / t[s] / 1e9
+        out[s] = {"us": round(t[s] * 1e6, 2), "algo_bytes": int(b), "GBps": round(gbs, 1),
+                  "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        if kt is not None and s in kt:
+            out[s]["main_kernel"] = kernels[s]
+            out[s]["main_kernel_us"] = round(kt[s] * 1e6, 2)
+    return out
+
+
+def bench_mass_pipeline(args, w):
+    """Long-context workload (Qwen3-8B shape, 131,072 tokens per KV head):
+    attention mass of every key with the full LSE (ContourKV sections 1 and
+    3), per-head top-1024 by mass with its kept sum, dropped-mass budgets of
+    5% of all entries, per-head top-b_h, compaction and reference-mode decode
+    attention; each stage timed with events on the launch stream."""
+    import numpy as np
+    import torch
+
+    import synth
+    from retention_scored_decode_amd import trimkv as tk
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    pc = synth.build_cache(w, workers=min(16, os.cpu_count() or 1))
+    print("[bench] generated %s in %.1f s" % (w.name, time.time() - t0), file=sys.stderr, flush=True)
+    H, G, D = pc.n_heads, w.group, w.head_dim
+    N = int(pc.length.sum())
+    B = w.budget()
+    scale = 1.0 / math.sqrt(D)
+    c, up, bf = _upload_cache(pc, dev)
+    del pc
+    q = bf(synth.queries(w))
+    seg = up(np.arange(H + 1, dtype=np.int32))
+    topk = up(np.full(H, w.mass_topk, np.int64))
+    mass = torch.empty(c.n_pages * 16, dtype=torch.float32, device=dev)
+    lse = torch.empty(H * G, dtype=torch.float32, device=dev)
+    keep = torch.empty(c.n_pages * 16, dtype=torch.uint8, device=dev)
+    kept = torch.empty(H, dtype=torch.int32, device=dev)
+    ks = torch.empty(H, dtype=torch.float64, device=dev)
+    b = torch.empty(H, dtype=torch.int64, device=dev)
+    dst = tk.Cache.empty(H, -(-B // 16) + H, D, torch.bfloat16, device=dev)
+    used = torch.zeros(1, dtype=torch.int64, device=dev)
+    out = torch.empty((H * G, D), dtype=torch.float32, device=dev)
+    dropped = torch.empty(H * G, dtype=torch.float32, device=dev)
+    ws_mass = tk.workspace(tk.OP_ATTN_MASS, c, 0, G)
+    ws_sel = tk.workspace(tk.OP_SELECT, c, H)
+    ws_cmp = tk.workspace(tk.OP_COMPACT, c)
+    ws_dec = tk.workspace(tk.OP_DECODE_ATTN, dst, 0, G)
+    stages = ["mass", "select_top", "allocate", "select_budget", "compact", "decode_ref"]
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        tk.attn_mass(c, q, G, scale, mass, lse, ws=ws_mass)
+        if ev: ev[1].record()
+        tk.select_global(c, mass, seg, topk, keep, kept, ks, ws=ws_sel)
+        if ev: ev[2].record()
+        tk.allocate(ks, c.length, B, b)
+        if ev: ev[3].record()
+        tk.select_global(c, mass, seg, b, keep, kept, ws=ws_sel)
+        if ev: ev[4].record()
+        tk.compact(c, keep, 0, B, dst, used, ws=ws_cmp, kept=kept)
+        if ev: ev[5].record()
+        tk.decode_attn(dst, q, G, scale, out, dropped, lse_ref=lse, ws=ws_dec)
+        if ev: ev[6].record()
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    t = {s: float(np.mean([e[j].elapsed_time(e[j + 1]) * 1e-3 for e in evs])) for j, s in enumerate(stages)}
+    assert int(b.sum().item()) == B and int(dst.length.sum().item()) == B
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+    pages = int(used.item())
+    small = H * G * D * 2 + H * G * D * 4 + H * G * 8
+    algo = {"mass": 256 * N + 4 * N + H * G * D * 2 + H * G * 4,   # every K row once, the mass plane, q, LSE
+            "select_top": 4 * N,
+            "allocate": 8 * H * 3,
+            "select_budget": 4 * N,
+            "compact": 1040 * B + 4 * pages,
+            "decode_ref": 512 * B + small + 4 * pages + 8 * H}
+    total = sum(t.values())
+    res = {"metric": "long-context mass -> dropped-mass budgets -> compaction -> reference decode, "
+                     "algorithmic GB/s of the whole pipeline",
+           "value": round(sum(algo.values()) / total / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": w.name, "layers": w.layers, "kv_heads": w.kv_heads, "q_per_kv": G,
+                      "head_dim": D, "ctx_per_head": w.ctx, "entries": N, "top_mass": w.mass_topk,
+                      "budget": B, "page": 16},
+           "pipeline_us": round(total * 1e6, 2),
+           "stages": _stage_json(algo, t)}
+    print(json.dumps(res), flush=True)
+
+
+def bench_streaming(args, w):
+    """Streaming workload (28 layers x 4 KV heads, GQA 7, 65,536-token
+    prefill, fixed budget M): the first generated step evicts the prefill to
+    M; every later step appends one entry per KV head, scores, selects M,
+    runs mask-mode attention with the step's queries and evicts.  Eviction
+    out of place into the other of two pools (one spare slot per head), and
+    in place within each head's own pages; steps/s over the generated steps
+    with every step's inputs resident in HBM beforehand."""
+    import numpy as np
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+
+    import synth
+    from retention_scored_decode_amd import trimkv as tk
+
+    dev = "cuda"
+    S = args.stream_steps or w.steps
+    assert S >= 2
+    t0 = time.time()
+    pc = synth.build_cache(w, workers=min(16, os.cpu_count() or 1))
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        steps_in = list(ex.map(lambda s: synth.stream_step(w, s), range(1, S + 1)))
+    print("[bench] generated %s and %d steps in %.1f s" % (w.name, S, time.time() - t0), file=sys.stderr,
+          flush=True)
+    torch.cuda.set_device(0)
+    H, G, D = pc.n_heads, w.group, w.head_dim
+    M = w.budget()
+    N0 = int(pc.length.sum())
+    scale = 1.0 / math.sqrt(D)
+    prefill, up, bf = _upload_cache(pc, dev)
+    del pc
+    beta_all = up(np.stack([x[0] for x in steps_in]))
+    k_all = bf(np.stack([x[1] for x in steps_in]))
+    v_all = bf(np.stack([x[2] for x in steps_in]))
+    q_all = bf(np.stack([x[3] for x in steps_in]))
+    t_all = up(np.arange(w.ctx + 1, w.ctx + S + 1, dtype=np.int32)).view(S, 1)
+    del steps_in
+    seg = up(np.array([0, H], np.int32))
+    bud = up(np.array([M], np.int64))
+    RES = max(64, S)          # spare slots of the in-place home pages: every step's entry of every head fits
+    cap = -(-(M + H) // 16) + H
+    pools = [tk.Cache.empty(H, cap, D, torch.bfloat16, device=dev) for _ in range(2)]
+    cap_h = -(-(M + H * RES) // 16) + H
+    home = tk.Cache.empty(H, cap_h, D, torch.bfloat16, device=dev)
+    score = torch.empty(prefill.n_pages * 16, dtype=torch.float32, device=dev)
+    keep = torch.empty(prefill.n_pages * 16, dtype=torch.uint8, device=dev)
+    kept = torch.empty(H, dtype=torch.int32, device=dev)
+    used = torch.zeros(1, dtype=torch.int64, device=dev)
+    out = torch.empty((H * G, D), dtype=torch.float32, device=dev)
+    dropped = torch.empty(H * G, dtype=torch.float32, device=dev)
+    ws = {}
+    for name, cc in (("pre", prefill), ("pool", pools[0]), ("home", home)):
+        ws[name] = (tk.workspace(tk.OP_SELECT, cc, 1), tk.workspace(tk.OP_DECODE_ATTN, cc, 0, G),
+                    tk.workspace(tk.OP_COMPACT, cc))
+    ws_inp = tk.workspace(tk.OP_COMPACT_INPLACE, home)
+    tables = [(torch.empty(H + 1, dtype=torch.int32, device=dev), torch.empty(cap_h, dtype=torch.int32, device=dev))
+              for _ in range(2)]
+
+    def front(c, s, wsel, watt):
+        """append, score, select and mask-mode attention of step s (1-based)"""
+        i = s - 1
+        tk.append(c, k_all[i], v_all[i], beta_all[i], t_all[i])
+        tk.score(c, seg, t_all[i], score)
+        tk.select_global(c, score, seg, bud, keep, kept, ws=wsel)
+        tk.decode_attn(c, q_all[i], G, scale, out, dropped, keep=keep, ws=watt)
+
+    len0 = prefill.length.clone()
+
+    def step_one(dst, reserve):
+        """step 1 on the prefill cache (its spare slot takes the step's entry),
+        evicting the prefill to M entries into dst"""
+        prefill.length.copy_(len0)           # undo an earlier run's append (untimed)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        front(prefill, 1, ws["pre"][0], ws["pre"][1])
+        tk.compact(prefill, keep, reserve, M, dst, used, ws=ws["pre"][2], kept=kept)
+        e1.record()
+        return e0, e1
+
+    def run_oop(n):
+        """steps 1..n, evicting out of place into the other of two pools"""
+        e0, e1 = step_one(pools[1], 1)
+        wsel, watt, wcmp = ws["pool"]
+        cur = pools[1]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for s in range(2, n + 1):
+            front(cur, s, wsel, watt)
+            nxt = pools[0] if cur is pools[1] else pools[1]
+            tk.compact(cur, keep, 1, M, nxt, used, ws=wcmp, kept=kept)
+            cur = nxt
+        ev[1].record()
+        torch.cuda.synchronize()
+        return cur, e0.elapsed_time(e1) * 1e-3, ev[0].elapsed_time(ev[1]) * 1e-3
+
+    def run_inplace(n):
+        """steps 1..n; step 1 lays the evicted prefill out with RES spare
+        slots per head (the home pages, room for one entry per step), later
+        steps evict in place keeping one spare slot in each head's table"""
+        step_one(home, RES)
+        home_off, home_ids = home.page_off.clone(), home.page_ids.clone()
+        wsel, watt, _ = ws["home"]
+        view = home
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for s in range(2, n + 1):
+            front(view, s, wsel, watt)
+            nt = tables[s % 2]
+            view = tk.compact_inplace(view, keep, 1, home_off, home_ids, nt[0], nt[1], kept=kept, ws=ws_inp)
+        ev[1].record()
+        torch.cuda.synchronize()
+        return view, ev[0].elapsed_time(ev[1]) * 1e-3
+
+    run_oop(min(S, 4))                       # first launches load the kernels
+    run_inplace(min(S, 4))
+    cur, t_first, t_oop = run_oop(S)
+    assert int(cur.length.sum().item()) == M
+    assert tk.validate_cache(cur, t_all[S - 1] + 1) == tk.OK
+    assert bool(torch.isfinite(out).all())
+    view, t_inp = run_inplace(S)
+    assert int(view.length.sum().item()) == M
+    assert tk.validate_cache(view, t_all[S - 1] + 1) == tk.OK
+    S_t = S - 1                              # steady-state steps timed
+
+    # algorithmic bytes of a steady step (M + H entries before eviction, M after)
+    U = M + H
+    pages = -(-(M + H) // 16)   # destination pages, at least (one spare slot per head)
+    small = H * G * D * 2 + H * G * D * 4 + H * G * 4
+    step_algo = {"append": H * (2 * D * 2 + 8), "score": 12 * U, "select": 4 * U,
+                 "attend_mask": 256 * U + 256 * M + small, "compact": 1040 * M + 4 * pages}
+    per_step = sum(step_algo.values())
+    res = {"metric": "streaming eviction steps/s (append, score, global select, mask-mode attention, evict), "
+                     "GQA-7 28x4 heads, 64K prefill",
+           "value": round(S_t / t_oop, 1), "unit": "steps/s", "n_gpus": 1, "steps": S_t, "warmup": 4,
+           "ms_per_step": round(t_oop / S_t * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": w.name, "layers": w.layers, "kv_heads": w.kv_heads, "q_per_kv": G,
+                      "head_dim": D, "prefill": w.ctx, "prefill_entries": N0, "budget": M, "page": 16},
+           "out_of_place": {"steps_per_s": round(S_t / t_oop, 1), "us_per_step": round(t_oop / S_t * 1e6, 2),
+                            "algo_bytes_per_step": per_step,
+                            "GBps": round(per_step * S_t / t_oop / 1e9, 1),
+                            "frac_hbm": round(per_step * S_t / t_oop / 1e9 / HBM_PEAK_GBS, 4),
+                            "step_algo_bytes": step_algo},
+           "in_place": {"steps_per_s": round(S_t / t_inp, 1), "us_per_step": round(t_inp / S_t * 1e6, 2),
+                        "home_spare_slots_per_head": RES},
+           "first_step_us": round(t_first * 1e6, 2),
+           "first_step_what": "append, score, select, mask-mode attention and eviction of the %d-entry "
+                              "prefill (step 1)" % N0,
+           "steps_timed": "steps 2..%d, one pass, no cache flush" % S}
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

@@ -385,9 +385,13 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
   constexpr bool MASKED = MODE == A_MASK || MODE == A_ERR || MODE == A_GMASK;
   constexpr bool ERR = MODE == A_ERR;
   constexpr bool GATED = MODE == A_GPLAIN || MODE == A_GMASK;
-  // load instructions per page; pages in flight are tracked by vmcnt (the
-  // logits mode also stores inside the loop and keeps a single page in flight)
-  constexpr int PER_PAGE = LOGITS ? 0 : 2 * LPP + (GATED ? 2 : 0);
+  // load instructions per page; pages in flight are tracked by vmcnt.  The
+  // logits mode also stores each page's logits inside the loop; those stores
+  // are not counted: loads complete in issue order among themselves, so once
+  // no more than the next page's LPP loads (or stores) are outstanding, the
+  // current page has arrived, whether or not the stores complete in order
+  // with the loads (at worst the wait also covers a store)
+  constexpr int PER_PAGE = LOGITS ? LPP : 2 * LPP + (GATED ? 2 : 0);
   __shared__ u32x4 lds_k[NTA / WAVE][2][16 * CH];
   __shared__ u32x4 lds_v[NTA / WAVE][2][LOGITS ? 1 : 16 * CH];
   const AttnWs& w = a.w;
