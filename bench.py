@@ -57,19 +57,37 @@ def parse():
     return ap.parse_args()
 
 
+# benchmark arguments of the profiled run behind each kernel-trace summary, and what one run holds
+TRACE_RUN = {
+    "llama8b_32k": ("--steps 5 --warmup 1 --cold-reps 2 --no-cpu-baseline",
+                    "A run is 1 + 5 pipeline steps (score, select, mask-mode attention, compaction, plain "
+                    "decode) plus 2 flushed plain-decode repetitions, so the plain-decode average mixes "
+                    "6 warm and 2 cold calls; the extras (error output, gated decode, incremental eviction, "
+                    "recency floor) follow."),
+    "qwen8b_128k": ("--workload qwen8b_128k --steps 3 --warmup 1",
+                    "A run is 1 + 3 passes of the pipeline: attention mass (logits kernel, merge, mass "
+                    "kernel), per-head top-1024 with kept sums, allocation, per-head top-b_h, compaction, "
+                    "reference-mode decode."),
+    "stream_gqa7": ("--workload stream_gqa7 --stream-steps 512",
+                    "A run is 4 + 512 generated steps evicting out of place, then 4 + 512 evicting in place; "
+                    "each step appends, scores, selects, attends (mask mode) and evicts."),
+}
+
+
 def trace_summary(workload, csv_path):
     """Per-kernel call count and average duration from rocprofv3 --stats."""
     import csv
     rows = list(csv.DictReader(open(csv_path)))
+    bargs, what = TRACE_RUN[workload]
     out = os.path.join(ROOT, "profiles", "kernel_stats_%s.md" % workload)
+    d = os.path.dirname(csv_path)
+    tag = os.path.basename(csv_path)[:-len("_kernel_stats.csv")]
     with open(out, "w") as fh:
         fh.write("# Kernel durations, %s workload (rocprofv3 --kernel-trace --stats)\n\n" % workload)
         fh.write("Command (repository root):\n\n    rocprofv3 --kernel-trace --stats --output-format csv "
-                 "-d gpurun_out/prof -o c2 -- python -u bench.py --steps 5 --warmup 1 --cold-reps 2 "
-                 "--no-cpu-baseline\n    python bench.py --trace-summary gpurun_out/prof/c2_kernel_stats.csv\n\n")
-        fh.write("A run is 1 + 5 pipeline steps (score, select, mask-mode attention, compaction, plain "
-                 "decode) plus 2 flushed plain-decode repetitions, so the plain-decode average mixes "
-                 "6 warm and 2 cold calls.\n\n")
+                 "-d %s -o %s -- python -u bench.py %s\n    python bench.py --workload %s --trace-summary %s\n\n"
+                 % (d, tag, bargs, workload, csv_path))
+        fh.write(what + "\n\n")
         fh.write("| kernel | calls | average us | min us | max us | share % |\n|---|---|---|---|---|---|\n")
         for r in rows:
             fh.write("| %s | %s | %.1f | %.1f | %.1f | %s |\n" % (
