@@ -98,7 +98,7 @@ def trace_summary(workload, csv_path):
 
 # main kernel(s) of each stage, as rocprofv3 names them, and the sources they are built from
 STAGE_KERNEL = {
-    "score": ("k_score", ["score.hip", "common.h"]),
+    "score": ("k_score<4>", ["score.hip", "common.h"]),
     "select": ("k_sel_hist<0..2> + k_sel_decide", ["select.hip", "common.h"]),
     "attend_mask": ("k_attn_bf16<128, 1>", ["attn.hip", "common.h"]),
     "compact": ("k_cmp_copy<256>", ["compact.hip", "common.h"]),

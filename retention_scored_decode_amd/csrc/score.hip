@@ -46,7 +46,15 @@ __global__ void __launch_bounds__(256) k_log_beta(const float* __restrict__ beta
     lnb[(i / PAGE) * out_page_stride + i % PAGE] = ln_f32_cr(beta[i]);
 }
 
-// 64 CSR pages per block, 4 slots per thread (16-byte loads and stores).
+// TILES tiles of 64 CSR pages per block, 4 slots per thread (16-byte loads
+// and stores).  A thread's physical pages depend only on its CSR pages, so
+// they are requested before the block's head search; the metadata lines and
+// the heads' table words are then requested together, so a block waits for
+// about four round trips in all.  Large caches take 4 tiles per block
+// (measured against 1, 2 and 8 on the 8B, batched and streaming caches: best
+// or within 2% everywhere; batched 805 MB: 175 us against 187 and 196);
+// small ones take 1, so that the grid still fills the GPU.
+template <int SC_TILES>
 __global__ void __launch_bounds__(256) k_score(const int32_t* __restrict__ page_off,
                                                const int32_t* __restrict__ page_ids,
                                                const int32_t* __restrict__ len,
@@ -55,29 +63,51 @@ __global__ void __launch_bounds__(256) k_score(const int32_t* __restrict__ page_
                                                const int32_t* __restrict__ t, float* __restrict__ score) {
   __shared__ PageHeads sh;
   const int64_t total = page_off[n_heads];
-  const int64_t c0 = (int64_t)blockIdx.x * 64;
-  if (c0 >= total) return;
-  const PageHeads r = block_page_heads(page_off, n_heads, c0, min(c0 + 63, total - 1), &sh);
-  const int64_t c = c0 + (threadIdx.x >> 2);
+  const int64_t b0 = (int64_t)blockIdx.x * (64 * SC_TILES);
+  if (b0 >= total) return;
+  const int64_t blast = min(b0 + 64 * SC_TILES - 1, total - 1);
   const int j0 = (threadIdx.x & 3) * 4;
-  if (c >= total) return;
-  const int h = r.hf == r.hl ? r.hf : head_in_range(page_off, r, c);
-  const int s = upper_index(seg_head_begin, n_seg + 1, h);
-  const int64_t i0 = (c - page_off[h]) * PAGE + j0;
-  const int64_t n = len[h];
-  float4 out = make_float4(qnan(), qnan(), qnan(), qnan());
-  if (i0 < n) {
-    // ln(beta) and positions of one page share a 128-byte block
-    const uint32_t* mp = meta + (int64_t)page_ids[c] * (2 * PAGE) + j0;
-    const float4 l = *reinterpret_cast<const float4*>(mp);
-    const int4 p = *reinterpret_cast<const int4*>(mp + PAGE);
-    const int tt = t[s];
-    out.x = __fmul_rn((float)(tt - p.x), l.x);
-    if (i0 + 1 < n) out.y = __fmul_rn((float)(tt - p.y), l.y);
-    if (i0 + 2 < n) out.z = __fmul_rn((float)(tt - p.z), l.z);
-    if (i0 + 3 < n) out.w = __fmul_rn((float)(tt - p.w), l.w);
+  int64_t cc[SC_TILES];
+  int pid[SC_TILES];
+#pragma unroll
+  for (int k = 0; k < SC_TILES; ++k) {
+    cc[k] = b0 + k * 64 + (threadIdx.x >> 2);
+    pid[k] = cc[k] <= blast ? page_ids[cc[k]] : 0;
   }
-  *reinterpret_cast<float4*>(score + c * PAGE + j0) = out;
+  const PageHeads r = block_page_heads(page_off, n_heads, b0, blast, &sh);
+  // segments of the block's first and last heads (segments are head ranges)
+  const int sf = upper_index(seg_head_begin, n_seg + 1, r.hf);
+  const int sl = r.hl == r.hf ? sf : upper_index(seg_head_begin, n_seg + 1, r.hl);
+  float4 lb[SC_TILES];
+  int4 ps[SC_TILES];
+  int hh[SC_TILES];
+#pragma unroll
+  for (int k = 0; k < SC_TILES; ++k) {
+    if (cc[k] <= blast) {
+      // ln(beta) and positions of one page share a 128-byte block
+      const uint32_t* mp = meta + (int64_t)pid[k] * (2 * PAGE) + j0;
+      lb[k] = *reinterpret_cast<const float4*>(mp);
+      ps[k] = *reinterpret_cast<const int4*>(mp + PAGE);
+      hh[k] = r.hf == r.hl ? r.hf : head_in_range(page_off, r, cc[k]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < SC_TILES; ++k) {
+    if (cc[k] > blast) continue;
+    const int h = hh[k];
+    const int64_t i0 = (cc[k] - page_off[h]) * PAGE + j0;
+    const int64_t n = len[h];
+    float4 out = make_float4(qnan(), qnan(), qnan(), qnan());
+    if (i0 < n) {
+      const int s = sf == sl ? sf : upper_index(seg_head_begin, n_seg + 1, h);
+      const int tt = t[s];
+      out.x = __fmul_rn((float)(tt - ps[k].x), lb[k].x);
+      if (i0 + 1 < n) out.y = __fmul_rn((float)(tt - ps[k].y), lb[k].y);
+      if (i0 + 2 < n) out.z = __fmul_rn((float)(tt - ps[k].z), lb[k].z);
+      if (i0 + 3 < n) out.w = __fmul_rn((float)(tt - ps[k].w), lb[k].w);
+    }
+    *reinterpret_cast<float4*>(score + cc[k] * PAGE + j0) = out;
+  }
 }
 
 // One wave per head: write entry len[h] and bump len[h].
@@ -117,11 +147,15 @@ int launch_log_beta(const float* beta, float* lnb, int64_t n, int out_page_strid
 
 int launch_score(const trimkv_cache_t* c, int n_seg, const int32_t* seg, const int32_t* t, float* score,
                  hipStream_t st) {
-  int64_t blocks = (c->n_pages + 63) / 64;
-  if (blocks == 0) return TRIMKV_OK;
+  const int64_t big = (c->n_pages + 255) / 256;   // blocks of 4 tiles
+  if (big == 0) return TRIMKV_OK;
   prof_begin(st);
-  hipLaunchKernelGGL(k_score, dim3((unsigned)blocks), dim3(256), 0, st, c->page_off, c->page_ids, c->len,
-                     c->meta, c->n_heads, seg, n_seg, t, score);
+  if (big >= 1024)
+    hipLaunchKernelGGL(k_score<4>, dim3((unsigned)big), dim3(256), 0, st, c->page_off, c->page_ids, c->len,
+                       c->meta, c->n_heads, seg, n_seg, t, score);
+  else
+    hipLaunchKernelGGL(k_score<1>, dim3((unsigned)((c->n_pages + 63) / 64)), dim3(256), 0, st, c->page_off,
+                       c->page_ids, c->len, c->meta, c->n_heads, seg, n_seg, t, score);
   prof_end(st);
   return check_launch();
 }

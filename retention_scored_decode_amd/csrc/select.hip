@@ -373,6 +373,7 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
                                                    int want_sum) {
   __shared__ int64_t tmp[NT / WAVE + 1];
   __shared__ double tmpd[NT / WAVE];
+  __shared__ double tmps[RND][NT / WAVE];   // per-round wave sums of kept scores
   __shared__ int red[NT / WAVE];
   __shared__ int sh_c;
   __shared__ int64_t sh_excl;
@@ -462,6 +463,8 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
         j = f;
       }
       if (want_sum) {
+        // every round's wave sums first, then one barrier; each chunk's sum
+        // then adds its waves' sums in the same fixed order as before
 #pragma unroll
         for (int r = 0; r < RND; ++r) {
           const int k = r * CG + grp;
@@ -473,15 +476,21 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
               if (kmr[r] & (1u << q)) sum += (double)ka[r][q];
           }
           for (int d = WAVE / 2; d > 0; d >>= 1) sum += __shfl_xor(sum, d, WAVE);
-          if (lane == 0) tmpd[wid] = sum;
-          lds_barrier();
-          if (mine && threadIdx.x % GT == 0) {
-            double t = 0.0;
-            for (int q = 0; q < GT / WAVE; ++q) t += tmpd[grp * (GT / WAVE) + q];
-            w.part[c0 + k] = t;
-          }
-          lds_barrier();
+          if (lane == 0) tmps[r][wid] = sum;
         }
+        lds_barrier();
+        if (threadIdx.x % GT == 0) {
+#pragma unroll
+          for (int r = 0; r < RND; ++r) {
+            const int k = r * CG + grp;
+            if (k >= i && k < e) {
+              double t = 0.0;
+              for (int q = 0; q < GT / WAVE; ++q) t += tmps[r][grp * (GT / WAVE) + q];
+              w.part[c0 + k] = t;
+            }
+          }
+        }
+        lds_barrier();   // tmps is written again by the block's next segment run
       }
     } else {
       const int cb = st.chunk_begin;
