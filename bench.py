@@ -158,11 +158,10 @@ def pmc_summary(workload, fetch_db, write_db):
     with open(out, "w") as fh:
         fh.write("# HBM traffic per dispatch, %s workload (rocprofv3 PMC)\n\n" % workload)
         fh.write("Commands (repository root, one counter per run):\n\n")
-        for c in ("FETCH_SIZE", "WRITE_SIZE"):
-            fh.write("    rocprofv3 --pmc %s -d gpurun_out/pmc_%s -o run -- python -u bench.py --steps 2 "
-                     "--warmup 1 --cold-reps 1 --no-cpu-baseline --calib\n" % (c, c))
-        fh.write("    python bench.py --pmc-summary gpurun_out/pmc_FETCH_SIZE/run_results.db "
-                 "gpurun_out/pmc_WRITE_SIZE/run_results.db\n\n")
+        for c, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
+            fh.write("    rocprofv3 --pmc %s -d %s -o run -- python -u bench.py --steps 2 "
+                     "--warmup 1 --cold-reps 1 --no-cpu-baseline --calib\n" % (c, os.path.dirname(db)))
+        fh.write("    python bench.py --pmc-summary %s %s\n\n" % (fetch_db, write_db))
         fh.write("Calibration: the 1 GiB device copy reads FETCH_SIZE %.0f KiB and WRITE_SIZE %.0f KiB, "
                  "so traffic = FETCH x %.3f + WRITE x %.3f (KiB -> bytes x 1024).\n\n" % (f_copy, w_copy, fr, fw))
         fh.write("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | traffic MB |\n|---|---|---|---|---|\n")
@@ -231,8 +230,8 @@ def main():
         trace_summary(args.workload, args.trace_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the path is single-GPU (see DESIGN.md for how it would shard); "
-              "run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the path runs on one GPU (across GPUs it would shard by KV head, "
+              "with the global selection's histograms all-reduced); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
