@@ -547,6 +547,27 @@ def test_attention_mass_parity():
     assert np.max(np.abs(lse.cpu().numpy() - want_lse)) <= 1e-4
 
 
+@pytest.mark.parametrize("d,group", [(128, 4), (128, 7), (64, 1), (128, 16)])
+def test_attention_mass_long(d, group):
+    """Attention mass and full LSE on long ragged heads (10 heads of 36K-48K
+    entries, about 30K pages): every wave of the logits kernel streams
+    several pages, two in flight, while storing each page's logits."""
+    rng = np.random.default_rng(1200 + d + group)
+    pc = synth.random_ragged_cache(1210 + group, n_heads=10, d=d, dtype="bf16", max_len=48000, min_len=36000)
+    ov = OracleView(pc)
+    q_dev, q64 = make_q(rng, pc.n_heads * group, d, "bf16", scale=2.0)
+    c = upload(pc)
+    announce("mass long", d, group)
+    mass = torch.full((pc.n_pages * 16,), 5.0, dtype=torch.float32, device="cuda")
+    lse = torch.empty(pc.n_heads * group, dtype=torch.float32, device="cuda")
+    tk.attn_mass(c, q_dev, group, scale_of(d), mass, lse)
+    want_mass, want_lse = ref.attn_mass(ov.k, q64, group, scale_of(d))
+    got = heads_from_plane(mass.cpu().numpy(), pc.page_off, pc.length)
+    for h in range(pc.n_heads):
+        assert np.all(np.abs(got[h] - want_mass[h]) <= 1e-5 * want_mass[h] + 1e-12), h
+    assert np.max(np.abs(lse.cpu().numpy() - want_lse)) <= 1e-4
+
+
 def test_allocation_parity():
     rng = np.random.default_rng(12)
     for trial in range(30):
