@@ -374,6 +374,7 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
   __shared__ int64_t tmp[NT / WAVE + 1];
   __shared__ double tmpd[NT / WAVE];
   __shared__ double tmps[RND][NT / WAVE];   // per-round wave sums of kept scores
+  __shared__ int cnt[RND][NT / WAVE];        // per-round wave counts of kept slots
   __shared__ int red[NT / WAVE];
   __shared__ int sh_c;
   __shared__ int64_t sh_excl;
@@ -446,21 +447,40 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
       };
       if (st.mode == MODE_NORMAL && st.prefix != 0u) mark(std::true_type{});
       else mark(std::false_type{});
-      // kept entries per head: one block sum and one atomic per head run
-      int j = i;
-      while (j < e) {
-        const int h = sm[j].x;
-        int f = j + 1;
-        while (f < e && sm[f].x == h) ++f;
+      // kept entries per head, one atomic per head run: a run of one head
+      // takes one block sum; a run over several heads (short heads) stages
+      // every round's per-wave counts and takes one barrier in all, instead
+      // of a block sum per head (measured both ways: each form is faster in
+      // its own case)
+      if (sm[i].x == sm[e - 1].x) {   // block-uniform
         int n = 0;
 #pragma unroll
         for (int r = 0; r < RND; ++r) {
           const int k = r * CG + grp;
-          if (k >= j && k < f) n += __popc(kmr[r]);
+          if (k >= i && k < e) n += __popc(kmr[r]);
         }
         n = block_sum_i32(n, red);
-        if (threadIdx.x == 0 && n) atomicAdd(kept + h, n);
-        j = f;
+        if (threadIdx.x == 0 && n) atomicAdd(kept + sm[i].x, n);
+      } else {
+#pragma unroll
+        for (int r = 0; r < RND; ++r) {
+          const int k = r * CG + grp;
+          int n = (k >= i && k < e) ? __popc(kmr[r]) : 0;
+          for (int d = WAVE / 2; d > 0; d >>= 1) n += __shfl_xor(n, d, WAVE);
+          if (lane == 0) cnt[r][wid] = n;
+        }
+        lds_barrier();
+        if (threadIdx.x == 0) {
+          int j = i;
+          while (j < e) {
+            const int h = sm[j].x;
+            int n = 0;
+            for (; j < e && sm[j].x == h; ++j)   // chunk j = round j / CG, group j % CG
+              for (int q = 0; q < GT / WAVE; ++q) n += cnt[j / CG][(j % CG) * (GT / WAVE) + q];
+            if (n) atomicAdd(kept + h, n);
+          }
+        }
+        lds_barrier();   // cnt is written again by the block's next segment run
       }
       if (want_sum) {
         // every round's wave sums first, then one barrier; each chunk's sum
