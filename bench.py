@@ -481,9 +481,11 @@ def main():
     stage_out = {}
     for s in stages:
         gbs = algo[s] / t[s] / 1e9
+        p10, med, p90 = (float(x) * 1e6 for x in np.percentile(per[s], [10, 50, 90]))
         stage_out[s] = {"us": round(t[s] * 1e6, 2), "algo_bytes": algo[s], "GBps": round(gbs, 1),
                         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "main_kernel": STAGE_KERNEL[s][0],
-                        "main_kernel_us": round(kt[s] * 1e6, 2)}
+                        "main_kernel_us": round(kt[s] * 1e6, 2),
+                        "p10_us": round(p10, 2), "median_us": round(med, 2), "p90_us": round(p90, 2)}
     err_algo = 512 * N + small + nq * D * 4
     err_t, err_kt = e_t, e_k
     g_algo = algo["decode"] + 8 * kept_total
@@ -605,12 +607,16 @@ def _upload_cache(pc, dev):
     return tk.Cache(bf(pc.k), bf(pc.v), meta, up(pc.page_off), up(pc.page_ids), up(pc.length)), up, bf
 
 
-def _stage_json(algo, t, kt=None, kernels=None):
+def _stage_json(algo, t, per=None, kt=None, kernels=None):
+    import numpy as np
     out = {}
     for s, b in algo.items():
         gbs = b / t[s] / 1e9
         out[s] = {"us": round(t[s] * 1e6, 2), "algo_bytes": int(b), "GBps": round(gbs, 1),
                   "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        if per is not None:
+            p10, med, p90 = (float(x) * 1e6 for x in np.percentile(per[s], [10, 50, 90]))
+            out[s].update({"p10_us": round(p10, 2), "median_us": round(med, 2), "p90_us": round(p90, 2)})
         if kt is not None and s in kt:
             out[s]["main_kernel"] = kernels[s]
             out[s]["main_kernel_us"] = round(kt[s] * 1e6, 2)
@@ -683,7 +689,8 @@ def bench_mass_pipeline(args, w):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    t = {s: float(np.mean([e[j].elapsed_time(e[j + 1]) * 1e-3 for e in evs])) for j, s in enumerate(stages)}
+    per = {s: [e[j].elapsed_time(e[j + 1]) * 1e-3 for e in evs] for j, s in enumerate(stages)}
+    t = {s: float(np.mean(v)) for s, v in per.items()}
     assert int(b.sum().item()) == B and int(dst.length.sum().item()) == B
     assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
     pages = int(used.item())
@@ -705,7 +712,7 @@ def bench_mass_pipeline(args, w):
                       "head_dim": D, "ctx_per_head": w.ctx, "entries": N, "top_mass": w.mass_topk,
                       "budget": B, "page": 16},
            "pipeline_us": round(total * 1e6, 2),
-           "stages": _stage_json(algo, t)}
+           "stages": _stage_json(algo, t, per)}
     print(json.dumps(res), flush=True)
 
 
