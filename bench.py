@@ -550,9 +550,96 @@ def main():
 
 
 def cpu_baseline(w, pc, M):
-    """The oracle, untuned, on one host thread: ln beta + scores + the global
-    selection over every entry, then compaction rows and float64 decode
-    attention over the kept entries of a sample of KV heads."""
+    """The oracle, untuned, on one host thread, over the first segment (the
+    whole cache of a single-sequence workload, the first sequence of a
+    batched one): ln beta + scores + the global selection over every entry
+    of the segment, then float64 decode attention over its kept entries."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import synth
+    from oracle import reference as ref
+
+    with threadpool_limits(limits=1):
+        G, D = w.group, w.head_dim
+        seg = w.seg_head_begin()
+        h0, h1 = int(seg[0]), int(seg[1])
+        heads = list(range(h0, h1))
+        po, pi, ln = pc.page_off, pc.page_ids, pc.length
+        t0 = time.perf_counter()
+        slots = [ref.head_phys_slots(po, pi, ln, h) for h in heads]
+        fb, fp = pc.beta.reshape(-1), pc.pos.reshape(-1)
+        scores = [ref.score_f32(ref.ln_beta(fb[sl]), w.t, fp[sl]) for sl in slots]
+        t1 = time.perf_counter()
+        keep, kept = ref.select_global(scores, [0, len(heads)], [M])
+        t2 = time.perf_counter()
+        kslots = [sl[k] for sl, k in zip(slots, keep)]
+        K = [synth.bf16_bits_to_f32(pc.k.reshape(-1, D)[s]).astype(np.float64) for s in kslots]
+        V = [synth.bf16_bits_to_f32(pc.v.reshape(-1, D)[s]).astype(np.float64) for s in kslots]
+        q = synth.bf16_bits_to_f32(synth.queries(w)).astype(np.float64)
+        qs = np.concatenate([q[h * G:(h + 1) * G] for h in heads])
+        t3 = time.perf_counter()
+        ref.decode_attn(K, V, qs, G, 1.0 / math.sqrt(D))
+        t4 = time.perf_counter()
+    ent = int(sum(len(k) for k in K))
+    gbs = (512 * ent + len(qs) * D * 6) / (t4 - t3) / 1e9
+    N = int(sum(len(x) for x in scores))
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "float64 decode attention over the kept entries of %d KV heads (%d entries, %s); "
+                      "scores + global selection over their %d entries"
+                      % (len(heads), ent, "the whole cache" if w.n_seg == 1 else "the first sequence", N),
+            "select_entries_per_s": round(N / (t2 - t1), 1),
+            "score_s": round(t1 - t0, 2), "select_s": round(t2 - t1, 2), "attn_s": round(t4 - t3, 3)}
+
+
+def cpu_baseline_mass(w, pc, n_heads=32):
+    """The oracle on one host thread for the long-context pipeline, on a
+    sample of KV heads: float64 attention mass and full LSE, the top-1024 by
+    mass with its kept sum, and float64 reference-mode decode attention over
+    the top-b entries (b = 5% of the head, the budget's share per head)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import synth
+    from oracle import reference as ref
+
+    with threadpool_limits(limits=1):
+        G, D = w.group, w.head_dim
+        heads = list(range(n_heads))
+        po, pi, ln = pc.page_off, pc.page_ids, pc.length
+        K = [synth.bf16_bits_to_f32(pc.k.reshape(-1, D)[ref.head_phys_slots(po, pi, ln, h)]).astype(np.float64)
+             for h in heads]
+        V = [synth.bf16_bits_to_f32(pc.v.reshape(-1, D)[ref.head_phys_slots(po, pi, ln, h)]).astype(np.float64)
+             for h in heads]
+        q = synth.bf16_bits_to_f32(synth.queries(w)).astype(np.float64)
+        qs = np.concatenate([q[h * G:(h + 1) * G] for h in heads])
+        t0 = time.perf_counter()
+        mass, lse = ref.attn_mass(K, qs, G, 1.0 / math.sqrt(D))
+        t1 = time.perf_counter()
+        m32 = [m.astype(np.float32) for m in mass]
+        keep, _ = ref.select_global(m32, list(range(n_heads + 1)), [w.mass_topk] * n_heads)
+        ks = np.array([np.sum(m[k].astype(np.float64)) for m, k in zip(m32, keep)])
+        b = int(round(w.budget() / w.n_heads))   # the sample's share of the budget, per head
+        bh, _ = ref.allocate(ks, np.asarray(ln[:n_heads]), b * n_heads)
+        keep2, _ = ref.select_global(m32, list(range(n_heads + 1)), [int(x) for x in bh])
+        t2 = time.perf_counter()
+        ref.decode_attn([k[m] for k, m in zip(K, keep2)], [v[m] for v, m in zip(V, keep2)], qs, G,
+                        1.0 / math.sqrt(D), lse_ref=lse)
+        t3 = time.perf_counter()
+    ent = int(sum(len(k) for k in K))
+    return {"value": round(256 * ent / (t1 - t0) / 1e9, 3), "unit": "GB/s (mass stage)", "cores": 1,
+            "kind": "oracle",
+            "sample": "float64 attention mass and LSE over all %d keys of %d KV heads, top-%d by mass, "
+                      "budgets of %d entries per head on average by dropped mass, top-b_h, reference-mode decode "
+                      "over the kept entries" % (ent, n_heads, w.mass_topk, b),
+            "mass_s": round(t1 - t0, 3), "select_s": round(t2 - t1, 3), "attn_s": round(t3 - t2, 3)}
+
+
+def cpu_baseline_stream(w, pc, n_steps=6):
+    """The oracle on one host thread for the streaming loop: step 1 (the
+    prefill eviction: scores and the global selection; untimed), then
+    n_steps steady generated steps over every head, each with its append,
+    scores, global selection of M, float64 mask-mode attention and eviction."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -561,31 +648,55 @@ def cpu_baseline(w, pc, M):
 
     with threadpool_limits(limits=1):
         H, G, D = pc.n_heads, w.group, w.head_dim
+        M = w.budget()
+        scale = 1.0 / math.sqrt(D)
         po, pi, ln = pc.page_off, pc.page_ids, pc.length
-        t0 = time.perf_counter()
         lnb = [ref.ln_beta(b) for b in ref.gather_heads(pc.beta, po, pi, ln)]
         pos = ref.gather_heads(pc.pos, po, pi, ln)
-        scores = [ref.score_f32(lnb[h], w.t, pos[h]) for h in range(H)]
+
+        def step_inputs(s):
+            beta, kn, vn, qn = synth.stream_step(w, s)
+            return (ref.ln_beta(beta), synth.bf16_bits_to_f32(kn).astype(np.float64),
+                    synth.bf16_bits_to_f32(vn).astype(np.float64), synth.bf16_bits_to_f32(qn).astype(np.float64))
+
+        # step 1: append, score and select on the metadata; K/V of the survivors only
+        t = w.ctx + 1
+        lnb_n, kf, vf, _ = step_inputs(1)
+        lnb = [np.append(lnb[h], lnb_n[h]) for h in range(H)]
+        pos = [np.append(pos[h], np.int32(t - 1)) for h in range(H)]
+        keep, _ = ref.select_global([ref.score_f32(lnb[h], t, pos[h]) for h in range(H)], [0, H], [M])
+        K, V = [], []
+        for h in range(H):
+            sl = ref.head_phys_slots(po, pi, ln, h)[keep[h][:-1]]
+            k = synth.bf16_bits_to_f32(pc.k.reshape(-1, D)[sl]).astype(np.float64)
+            v = synth.bf16_bits_to_f32(pc.v.reshape(-1, D)[sl]).astype(np.float64)
+            if keep[h][-1]:
+                k, v = np.concatenate([k, kf[h:h + 1]]), np.concatenate([v, vf[h:h + 1]])
+            K.append(k)
+            V.append(v)
+        lnb = [lnb[h][keep[h]] for h in range(H)]
+        pos = [pos[h][keep[h]] for h in range(H)]
+        t0 = time.perf_counter()
+        for s in range(2, n_steps + 2):
+            t = w.ctx + s
+            lnb_n, kf, vf, q64 = step_inputs(s)
+            for h in range(H):
+                lnb[h] = np.append(lnb[h], lnb_n[h])
+                pos[h] = np.append(pos[h], np.int32(t - 1))
+                K[h] = np.concatenate([K[h], kf[h:h + 1]])
+                V[h] = np.concatenate([V[h], vf[h:h + 1]])
+            keep, _ = ref.select_global([ref.score_f32(lnb[h], t, pos[h]) for h in range(H)], [0, H], [M])
+            ref.decode_attn(K, V, q64, G, scale, keep=keep)
+            lnb = [lnb[h][keep[h]] for h in range(H)]
+            pos = [pos[h][keep[h]] for h in range(H)]
+            K = [K[h][keep[h]] for h in range(H)]
+            V = [V[h][keep[h]] for h in range(H)]
         t1 = time.perf_counter()
-        keep, kept = ref.select_global(scores, [0, H], [M])
-        t2 = time.perf_counter()
-        sample = list(range(H))                # every KV head
-        kslots = [ref.head_phys_slots(po, pi, ln, h)[keep[h]] for h in sample]
-        K = [synth.bf16_bits_to_f32(pc.k.reshape(-1, D)[s]).astype(np.float64) for s in kslots]
-        V = [synth.bf16_bits_to_f32(pc.v.reshape(-1, D)[s]).astype(np.float64) for s in kslots]
-        q = synth.bf16_bits_to_f32(synth.queries(w)).astype(np.float64)
-        qs = np.concatenate([q[h * G:(h + 1) * G] for h in sample])
-        t3 = time.perf_counter()
-        ref.decode_attn(K, V, qs, G, 1.0 / math.sqrt(D))
-        t4 = time.perf_counter()
-    ent = int(sum(len(k) for k in K))
-    gbs = (512 * ent + len(qs) * D * 6) / (t4 - t3) / 1e9
-    N = int(ln.sum())
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "float64 decode attention over the kept entries of all %d KV heads (%d entries); "
-                      "scores + global selection over all %d entries" % (H, ent, N),
-            "select_entries_per_s": round(N / (t2 - t1), 1),
-            "score_s": round(t1 - t0, 2), "select_s": round(t2 - t1, 2), "attn_s": round(t4 - t3, 3)}
+    per = (t1 - t0) / n_steps
+    return {"value": round(1.0 / per, 4), "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": "generated steps 2..%d over all %d heads (%d entries kept per step); step 1, the prefill "
+                      "eviction, untimed" % (n_steps + 1, H, M),
+            "s_per_step": round(per, 3)}
 
 
 def _upload_cache(pc, dev):
@@ -645,7 +756,6 @@ def bench_mass_pipeline(args, w):
     B = w.budget()
     scale = 1.0 / math.sqrt(D)
     c, up, bf = _upload_cache(pc, dev)
-    del pc
     q = bf(synth.queries(w))
     seg = up(np.arange(H + 1, dtype=np.int32))
     topk = up(np.full(H, w.mass_topk, np.int64))
@@ -713,6 +823,8 @@ def bench_mass_pipeline(args, w):
                       "budget": B, "page": 16},
            "pipeline_us": round(total * 1e6, 2),
            "stages": _stage_json(algo, t, per)}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_mass(w, pc)
     print(json.dumps(res), flush=True)
 
 
@@ -746,7 +858,6 @@ def bench_streaming(args, w):
     N0 = int(pc.length.sum())
     scale = 1.0 / math.sqrt(D)
     prefill, up, bf = _upload_cache(pc, dev)
-    del pc
     beta_all = up(np.stack([x[0] for x in steps_in]))
     k_all = bf(np.stack([x[1] for x in steps_in]))
     v_all = bf(np.stack([x[2] for x in steps_in]))
@@ -866,6 +977,8 @@ def bench_streaming(args, w):
            "first_step_what": "append, score, select, mask-mode attention and eviction of the %d-entry "
                               "prefill (step 1)" % N0,
            "steps_timed": "steps 2..%d, one pass, no cache flush" % S}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_stream(w, pc)
     print(json.dumps(res), flush=True)
 
 
