@@ -81,8 +81,18 @@ __global__ void __launch_bounds__(NT) k_allocate(const double* __restrict__ kept
     for (int u = 0; u < PER; ++u) {
       const int h = (int)threadIdx.x + u * NT;
       if (u * NT < H) {   // block-uniform
+        // eight fractions requested per step, so their LDS latencies overlap
+        // (one dependent read per element took about 20 us at 288 heads)
         int32_t r = 0;
-        for (int i = 0; i < n; ++i) {
+        int i = 0;
+        for (; i + 8 <= n; i += 8) {
+          double fo[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) fo[k] = sbuf[i + k];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) r += (fo[k] > mine[u]) || (fo[k] == mine[u] && c0 + i + k < h);
+        }
+        for (; i < n; ++i) {
           const double fo = sbuf[i];
           r += (fo > mine[u]) || (fo == mine[u] && c0 + i < h);
         }
