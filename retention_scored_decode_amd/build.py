@@ -3,6 +3,7 @@
     python -m retention_scored_decode_amd.build
 """
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -30,14 +31,38 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
           "-I", INCLUDE, "-I", CSRC]
 
 
+# the compiler's per-kernel resource report, read for register spills
+REPORT = ["-Rpass-analysis=kernel-resource-usage"]
+
+
+def scratch_users(report):
+    """(kernel, bytes per lane) for every kernel of a resource report that
+    uses scratch memory.  No kernel may: after a kernel with scratch has run,
+    later kernels of the process measured about 1% slower on an MI355X
+    (the same mask-mode attention, 3.00 -> 3.04 ms), and register spills are
+    the only scratch these kernels would have."""
+    out, name = [], None
+    for line in report.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            out.append((name, int(m.group(1))))
+    return out
+
+
 def _compile(src):
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
     cmd = [HIPCC] + COMMON + EXTRA + UNIT_FLAGS.get(src, []) + (["-ffp-contract=off"] if src in EXACT else []) + \
-        ["-c", os.path.join(CSRC, src), "-o", obj]
+        REPORT + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l and "remark:" not in l)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, err))
+    spills = scratch_users(r.stderr)
+    if spills:
+        raise RuntimeError("%s: kernels use scratch (register spills): %s" % (src, spills))
     return obj
 
 

@@ -47,6 +47,15 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// The value of lane i - D of the same 16-lane DPP row, 0 for the row's
+// first D lanes (row_shr with bound_ctrl off keeps the `old` operand, 0).
+template <int D>
+__device__ __forceinline__ int64_t row_shr(int64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x110 + D, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)((uint64_t)v >> 32), 0x110 + D, 0xF, 0xF, false);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
 // ---------------------------------------------------------------------------
 // Block-wide exclusive scan of one int64 per thread (blockDim.x == NT).
 // `tmp` is LDS of NT/64 + 1 int64.  Returns the exclusive prefix; *total is
@@ -64,14 +73,16 @@ __device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t* tmp,
   }
   if (lane == WAVE - 1) tmp[wid] = x;
   lds_barrier();
-  if (threadIdx.x == 0) {
-    int64_t run = 0;
-    for (int w = 0; w < NT / WAVE; ++w) {
-      int64_t t = tmp[w];
-      tmp[w] = run;
-      run += t;
-    }
-    tmp[NT / WAVE] = run;
+  static_assert(NT / WAVE <= 16, "the wave totals fit one DPP row");
+  if (wid == 0) {   // wave totals scanned in the first row of wave 0: two live registers, not NT/32
+    const int64_t t = lane < NT / WAVE ? tmp[lane] : 0;
+    int64_t s = t;
+    if constexpr (NT / WAVE > 1) s += row_shr<1>(s);
+    if constexpr (NT / WAVE > 2) s += row_shr<2>(s);
+    if constexpr (NT / WAVE > 4) s += row_shr<4>(s);
+    if constexpr (NT / WAVE > 8) s += row_shr<8>(s);
+    if (lane < NT / WAVE) tmp[lane] = s - t;
+    if (lane == NT / WAVE - 1) tmp[NT / WAVE] = s;
   }
   lds_barrier();
   int64_t r = tmp[wid] + x - v;

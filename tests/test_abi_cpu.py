@@ -215,3 +215,16 @@ def test_profile_hook_arguments():
     assert L.trimkv_profile_next(None, None) == tk.OK
     assert L.trimkv_profile_next(X, None) == tk.EINVAL
     assert L.trimkv_profile_next(None, X) == tk.EINVAL
+
+
+def test_build_rejects_kernels_with_scratch():
+    from retention_scored_decode_amd.build import scratch_users
+    rep = "\n".join([
+        "x.hip:9:1: remark: Function Name: k_a [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:9:1: remark:     VGPRs: 64 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:9:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:20:1: remark: Function Name: k_b [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:20:1: remark:     ScratchSize [bytes/lane]: 60 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert scratch_users(rep) == [("k_b", 60)]
+    assert scratch_users(rep.replace(": 60 ", ": 0 ")) == []
