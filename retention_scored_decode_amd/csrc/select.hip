@@ -44,6 +44,7 @@ constexpr int HC = 4;
 __host__ __device__ constexpr int copy_words(int nb) { return nb + 32; }
 constexpr int HIST_WORDS = HC * (2 * copy_words(2048) + copy_words(1024));
 constexpr uint32_t SPIN_LIMIT = 1u << 26;
+constexpr unsigned N_CU = 256;  // compute units of an MI355X
 
 enum { MODE_NORMAL = 0, MODE_ALL = 1, MODE_NONE = 2 };
 
@@ -120,7 +121,7 @@ __global__ void __launch_bounds__(1024) k_sel_prep(const int32_t* __restrict__ p
 // the finished histogram of that pass (every thread gets the result); the
 // block holding the segment's first chunk stores it as the state before the
 // next pass.  The histogram words are loaded together with the state.
-__device__ SegState state_after(const SelWs& w, int s, int pass) {
+__device__ SegState state_after(const SelWs& w, int s, int pass, int cpb) {
   __shared__ int64_t tmp[NT / WAVE + 1];
   __shared__ uint32_t sh_prefix;
   __shared__ int64_t sh_rem, sh_ties;
@@ -165,7 +166,7 @@ __device__ SegState state_after(const SelWs& w, int s, int pass) {
       lds_barrier();
     }
   }
-  if (threadIdx.x == 0 && (int)blockIdx.x == st.chunk_begin / CPB) w.seg[(size_t)(pass + 1) * w.n_seg + s] = st;
+  if (threadIdx.x == 0 && (int)blockIdx.x == st.chunk_begin / cpb) w.seg[(size_t)(pass + 1) * w.n_seg + s] = st;
   return st;
 }
 
@@ -192,10 +193,10 @@ __device__ __forceinline__ float key_floor(uint64_t K) {
 // Marks values as changed at this point so that quantities derived from
 // them are computed where used rather than hoisted out of the segment-run
 // loop (32 extra live registers).  Emits no instruction.
-template <typename T>
-__device__ __forceinline__ void opaque(T (&x)[RND][4]) {
+template <typename T, int R>
+__device__ __forceinline__ void opaque(T (&x)[R][4]) {
 #pragma unroll
-  for (int r = 0; r < RND; ++r)
+  for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(x[r][j]));
 }
@@ -205,19 +206,21 @@ __device__ __forceinline__ void opaque(T (&x)[RND][4]) {
 // flight while the previous pass's bin is located.  The block's histogram is
 // merged into the segment's once per segment run, so the number of device
 // atomics per bin falls with the number of chunks per block.
-template <int PASS>
+template <int PASS, int HB>
 __global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __restrict__ score, SelWs w) {
+  constexpr int RND = HB / CG;   // rounds of CG chunks (shadows the decision kernel's)
+  static_assert(HB % CG == 0 && HB <= CPB, "chunk rounds");
   constexpr int NB = PASS == 2 ? 1024 : 2048;
   constexpr int SH = PASS == 0 ? 32 : PASS == 1 ? 21 : 10;   // key bits below the known prefix
   constexpr int BSH = SH - (PASS == 2 ? 10 : 11);               // shift of this pass's bin
   __shared__ uint32_t lh[NB];
-  __shared__ int4 sm[CPB];
-  const int c0 = blockIdx.x * CPB;
+  __shared__ int4 sm[HB];
+  const int c0 = blockIdx.x * HB;
   int4 mv = make_int4(0, 0, 0, 0);
-  if (threadIdx.x < CPB) mv = w.meta[c0 + threadIdx.x];   // padded by CPB entries
+  if (threadIdx.x < HB) mv = w.meta[c0 + threadIdx.x];   // padded by CPB >= HB entries
   const int T = w.chunk_off[n_heads];
   if (c0 >= T) return;
-  const int nc = min(CPB, T - c0);
+  const int nc = min(HB, T - c0);
   if (threadIdx.x < nc) sm[threadIdx.x] = mv;
   for (int b = threadIdx.x; b < NB; b += NT) lh[b] = 0u;
   lds_barrier();
@@ -234,7 +237,7 @@ __global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __res
       if (k < nc && i0 < (m.w & 0xFFFF)) kv[r] = *reinterpret_cast<const float4*>(score + (int64_t)m.z * PAGE + i0);
     }
     // state for the first segment run while the scores are in flight
-    if (PASS > 0) st0 = state_after(w, sm[0].y, PASS - 1);
+    if (PASS > 0) st0 = state_after(w, sm[0].y, PASS - 1, HB);
 #pragma unroll
     for (int r = 0; r < RND; ++r) {
       a[r][0] = kv[r].x;
@@ -251,7 +254,7 @@ __global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __res
     while (e < nc && sm[e].y == s) ++e;
     SegState st;
     if (PASS == 0) st = w.seg[s];
-    else st = i == 0 ? st0 : state_after(w, s, PASS - 1);
+    else st = i == 0 ? st0 : state_after(w, s, PASS - 1, HB);
     opaque(a);
     if (st.mode == MODE_NORMAL) {
       const uint32_t pre = st.prefix;
@@ -402,7 +405,7 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
       if (k < nc && i0 < (m.w & 0xFFFF)) kv[r] = *reinterpret_cast<const float4*>(score + (int64_t)m.z * PAGE + i0);
     }
     // state for the first segment run while the scores are in flight
-    st0 = state_after(w, sm[0].y, 2);
+    st0 = state_after(w, sm[0].y, 2, CPB);
 #pragma unroll
     for (int r = 0; r < RND; ++r) {
       ka[r][0] = kv[r].x;
@@ -416,7 +419,7 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
     const int sg = sm[i].y;
     int e = i + 1;
     while (e < nc && sm[e].y == sg) ++e;
-    const SegState st = i == 0 ? st0 : state_after(w, sg, 2);
+    const SegState st = i == 0 ? st0 : state_after(w, sg, 2, CPB);
     opaque(ka);
     const bool ranked = st.mode == MODE_NORMAL && st.ties > st.remaining;
     if (!ranked) {
@@ -646,9 +649,19 @@ int launch_select(const trimkv_cache_t* c, const float* score, int n_seg, const 
                      budget, T, w, kept);
   const unsigned hb = (unsigned)((T + CPB - 1) / CPB);
   prof_begin(st);
-  hipLaunchKernelGGL(k_sel_hist<0>, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w);
-  hipLaunchKernelGGL(k_sel_hist<1>, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w);
-  hipLaunchKernelGGL(k_sel_hist<2>, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w);
+  hipLaunchKernelGGL((k_sel_hist<0, CPB>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w);   // 48 VGPRs
+  // Later passes (78 VGPRs at CPB chunks per block: one block per CU), when
+  // there are more blocks with work than CUs (counted as if the pool's pages
+  // were all in use): half the chunks per block, whose fewer live keys (64
+  // VGPRs) let two blocks share a CU.
+  if ((c->n_pages / CP + CPB - 1) / CPB > N_CU) {
+    const unsigned hb2 = (unsigned)((T + CPB / 2 - 1) / (CPB / 2));
+    hipLaunchKernelGGL((k_sel_hist<1, CPB / 2>), dim3(hb2), dim3(NT), 0, st, c->n_heads, score, w);
+    hipLaunchKernelGGL((k_sel_hist<2, CPB / 2>), dim3(hb2), dim3(NT), 0, st, c->n_heads, score, w);
+  } else {
+    hipLaunchKernelGGL((k_sel_hist<1, CPB>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w);
+    hipLaunchKernelGGL((k_sel_hist<2, CPB>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w);
+  }
   hipLaunchKernelGGL(k_sel_decide, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, keep, kept,
                      keptsum != nullptr);
   prof_end(st);
