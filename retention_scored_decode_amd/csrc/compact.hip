@@ -413,7 +413,7 @@ int launch_compact(const trimkv_cache_t* src, const uint8_t* keep, const int32_t
   const int64_t rows_per_block = (int64_t)(NT / (rowb / 16)) * 4;
   const int64_t want = std::max((max_kept_total + rows_per_block - 1) / rows_per_block,
                                 (dst->n_pages + NT - 1) / NT);
-  const unsigned grid = (unsigned)std::min<int64_t>(std::max<int64_t>(want, 1), 8192);
+  const unsigned grid = (unsigned)std::min<int64_t>(std::max<int64_t>(want, 1), 65536);
 #define TRIMKV_COPY(RB)                                                                                      \
   hipLaunchKernelGGL(k_cmp_copy<RB>, dim3(grid), dim3(NT), 0, st, H, (const uint8_t*)src->k,                 \
                      (const uint8_t*)src->v, src->meta, w, dst->page_off, dst->page_ids, (uint8_t*)dst->k,    \
