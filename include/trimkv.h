@@ -125,9 +125,11 @@ int trimkv_score(const trimkv_cache_t* cache, int32_t n_seg, const int32_t* seg_
  * layers and heads, keep the top M_global); TRIM-KV page, section 2 (evict the
  * lowest current scores once the budget is exceeded).
  * Total order: score descending (-0.0 == +0.0, -inf below every finite
- * score, NaN below -inf), then flat head ascending, then slot ascending.
- * Segment s keeps exactly min(max(budget[s], 0), N_s) entries, N_s = valid
- * entries of its heads.
+ * score, NaN below -inf), then flat head ascending, then slot descending:
+ * among equal scores of one head the more recent entry ranks first, so with
+ * beta = 1 everywhere (every score 0) each head keeps its most recent
+ * entries.  Segment s keeps exactly min(max(budget[s], 0), N_s) entries,
+ * N_s = valid entries of its heads.
  *   score:   device fp32 CSR plane (any fp32 key: retention scores or masses)
  *   budget:  device int64 [n_seg]
  *   keep:    device uint8 CSR plane, out: 1 kept, 0 evicted (valid slots),
@@ -135,12 +137,18 @@ int trimkv_score(const trimkv_cache_t* cache, int32_t n_seg, const int32_t* seg_
  *   kept:    device int32 [n_heads], out: kept entries per head
  *   keptsum: device fp64 [n_heads] or NULL, out: sum of the kept scores of
  *            each head (slot order within 1024-slot chunks, chunks in order)
+ *   status:  device int32 [1] or NULL: a failure counter that the call only
+ *            increments (the caller clears it): +1 for every wait on the
+ *            tie ranks of earlier chunks that gave up after its bounded spin
+ *            (never expected; the keep plane of that segment is then not
+ *            exact).  One counter may serve many calls and be read once.
  *   ws:      workspace of trimkv_workspace_size(TRIMKV_OP_SELECT, cache, n_seg, 0) bytes
  * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE.
  */
 int trimkv_select_global(const trimkv_cache_t* cache, const float* score, int32_t n_seg,
                          const int32_t* seg_head_begin, const int64_t* budget, uint8_t* keep,
-                         int32_t* kept, double* keptsum, void* ws, size_t ws_bytes, void* stream);
+                         int32_t* kept, double* keptsum, int32_t* status, void* ws, size_t ws_bytes,
+                         void* stream);
 
 /*
  * trimkv_compact -- physical eviction: stable out-of-place compaction.
@@ -338,13 +346,17 @@ int trimkv_mark_recent(const trimkv_cache_t* cache, int32_t floor, float* plane,
  * Entry len[h] of head h receives k_new[h], v_new[h], ln(beta_new[h]) (as
  * trimkv_log_beta) and position *t - 1; then len[h] += 1.  The head must have
  * a free slot in its pages (trimkv_compact with reserve >= 1); a head without
- * one is left unchanged (trimkv_validate_cache reports it).
+ * one is left unchanged and counted in *status.
  *   k_new, v_new: device [n_heads][head_dim] (cache dtype); beta_new: fp32 [n_heads]
  *   t: device int32 [1]
+ *   status: device int32 [1] or NULL: a failure counter that the call only
+ *           increments (the caller clears it), by the number of heads that
+ *           had no free slot.  One counter may serve a whole decode loop and
+ *           be read once at its end (0: every entry was appended).
  * Errors: EINVAL, EUNSUPPORTED.
  */
 int trimkv_append(trimkv_cache_t* cache, const void* k_new, const void* v_new,
-                  const float* beta_new, const int32_t* t, void* stream);
+                  const float* beta_new, const int32_t* t, int32_t* status, void* stream);
 
 /* Bytes of workspace an operation needs for this cache (0 if none). */
 size_t trimkv_workspace_size(int op, const trimkv_cache_t* cache, int32_t n_seg, int32_t group);

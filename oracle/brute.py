@@ -18,9 +18,10 @@ def retention_exact(beta: float, age: int) -> Fraction:
 
 def select_sorted(entries, budget):
     """entries: list of (score, head, index).  Keep the first min(M, N) of a
-    full sort by score descending, then head, then index ascending; a NaN
-    score ranks below every other score (-inf included)."""
-    ranked = sorted(entries, key=lambda e: (math.isnan(e[0]), 0.0 if math.isnan(e[0]) else -e[0], e[1], e[2]))
+    full sort by score descending, then head ascending, then index
+    descending (the more recent entry of a head first); a NaN score ranks
+    below every other score (-inf included)."""
+    ranked = sorted(entries, key=lambda e: (math.isnan(e[0]), 0.0 if math.isnan(e[0]) else -e[0], e[1], -e[2]))
     return set((h, i) for _, h, i in ranked[:max(0, min(budget, len(ranked)))])
 
 
@@ -52,3 +53,58 @@ def shift_in_place(pool, slots_of_head, keep):
             pool[slots_of_head[j]] = pool[slots_of_head[i]]
             j += 1
     return j
+
+
+def compact_by_appending(rows_by_head, keep, reserve):
+    """Physical eviction built one entry at a time (DBTrimKV Method 4: paged
+    per-head storage; ContourKV section 2: the kept entries are stored, not
+    masked).  Heads in flat order; each kept row of a head, in slot order, is
+    appended to the head's current page, a fresh 16-slot page being opened
+    (numbered in opening order) whenever the head has no free slot; after its
+    rows, pages are opened until the head has `reserve` free slots.
+
+    Returns (page_off, page_ids, lengths, pages) with pages a list of
+    16-slot lists of row tuples (None for a free slot)."""
+    pages, page_off, lengths = [], [0], []
+    for h, rows in enumerate(rows_by_head):
+        mine, n = [], 0
+        for i, r in enumerate(rows):
+            if not keep[h][i]:
+                continue
+            if n == 16 * len(mine):
+                pages.append([None] * 16)
+                mine.append(len(pages) - 1)
+            pages[mine[-1]][n % 16] = r
+            n += 1
+        while 16 * len(mine) - n < reserve:
+            pages.append([None] * 16)
+            mine.append(len(pages) - 1)
+        lengths.append(n)
+        page_off.append(page_off[-1] + len(mine))
+    return page_off, list(range(len(pages))), lengths, pages
+
+
+def largest_remainder_l2(x, total):
+    """All integer vectors b >= 0 with sum(b) == total that minimise
+    sum_h (b_h - x_h)^2, by exhaustive search over compositions of `total`
+    (tiny inputs only).  A classical property of apportionment by largest
+    remainders: its result is such a minimiser, and the only one when the
+    fractional parts of x are distinct."""
+    H = len(x)
+    best, arg = None, []
+
+    def rec(h, left, pre):
+        nonlocal best, arg
+        if h == H - 1:
+            b = pre + [left]
+            d = math.fsum((bi - xi) ** 2 for bi, xi in zip(b, x))
+            if best is None or d < best - 1e-12:
+                best, arg = d, [b]
+            elif abs(d - best) <= 1e-12:
+                arg.append(b)
+            return
+        for v in range(left + 1):
+            rec(h + 1, left - v, pre + [v])
+
+    rec(0, total, [])
+    return arg

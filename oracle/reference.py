@@ -131,8 +131,11 @@ def select_global(scores, seg_head_begin, budgets):
     DBTrimKV Method 3: rank every cached entry of all layers and heads by its
     predicted utility and keep the top M_global; TRIM-KV section 2: when the
     budget is exceeded, the lowest current scores are evicted.  Order: score
-    descending (-0.0 equal to +0.0, -inf last), then flat head ascending,
-    then slot (= position) ascending.  A segment keeps min(M, N) entries.
+    descending (-0.0 equal to +0.0, -inf below every finite score, NaN
+    lowest), then flat head (l, h) ascending, then slot (= position)
+    descending: among equal scores of one head the more recent entry ranks
+    first, so that with beta = 1 everywhere (no decay, every score 0) a head
+    keeps its most recent entries.  A segment keeps min(M, N) entries.
     """
     keep = [np.zeros(len(s), dtype=bool) for s in scores]
     for s in range(len(seg_head_begin) - 1):
@@ -143,7 +146,7 @@ def select_global(scores, seg_head_begin, budgets):
         sc = np.where(sc == 0.0, 0.0, sc)            # -0.0 -> +0.0
         head = np.concatenate([np.full(len(scores[h]), h, np.int64) for h in hs])
         idx = np.concatenate([np.arange(len(scores[h]), dtype=np.int64) for h in hs])
-        order = np.lexsort((idx, head, -sc))
+        order = np.lexsort((-idx, head, -sc))
         m = max(0, min(int(budgets[s]), len(sc)))
         chosen = order[:m]
         for h in hs:
@@ -375,7 +378,7 @@ def allocate_floor(keptsum, length, total_budget, floor):
 def select_floor(per_head_scores, budgets, floor):
     """Per head: the most recent min(w, len_h) entries (the last slots, since
     positions ascend in slot order), plus the top b_h - floor_h of the other
-    entries by score descending, then position ascending (-0.0 == +0.0, NaN
+    entries by score descending, then position descending (-0.0 == +0.0, NaN
     lowest, as in select_global).  Returns keep flags per head."""
     keep = []
     for h, sc in enumerate(per_head_scores):
@@ -387,7 +390,7 @@ def select_floor(per_head_scores, budgets, floor):
         rest = np.where(rest == 0.0, 0.0, rest)
         key = np.where(np.isnan(rest), -np.inf, -rest)        # ascending sort = score descending
         nan_last = np.isnan(rest).astype(np.int64)
-        order = np.lexsort((np.arange(n - fl), key, nan_last))
+        order = np.lexsort((-np.arange(n - fl), key, nan_last))
         m = max(0, min(int(budgets[h]) - fl, n - fl))
         k[order[:m]] = True
         keep.append(k)

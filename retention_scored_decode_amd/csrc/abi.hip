@@ -147,15 +147,15 @@ int trimkv_score(const trimkv_cache_t* c, int32_t n_seg, const int32_t* seg, con
 }
 
 int trimkv_select_global(const trimkv_cache_t* c, const float* score, int32_t n_seg, const int32_t* seg,
-                         const int64_t* budget, uint8_t* keep, int32_t* kept, double* keptsum, void* ws,
-                         size_t ws_bytes, void* stream) {
+                         const int64_t* budget, uint8_t* keep, int32_t* kept, double* keptsum, int32_t* status,
+                         void* ws, size_t ws_bytes, void* stream) {
   int rc;
   if (!cache_shape_ok(c, &rc)) return rc;
   if (n_seg < 1 || n_seg > c->n_heads || !score || !seg || !budget || !keep || !kept || !table_ok(c) ||
       ((uintptr_t)keep & 15))
     return TRIMKV_EINVAL;
   if ((rc = ws_check(ws, ws_bytes, select_ws_layout(c, n_seg).total))) return rc;
-  return launch_select(c, score, n_seg, seg, budget, keep, kept, keptsum, ws, S(stream));
+  return launch_select(c, score, n_seg, seg, budget, keep, kept, keptsum, status, ws, S(stream));
 }
 
 int trimkv_compact(const trimkv_cache_t* src, const uint8_t* keep, const int32_t* kept, int32_t reserve,
@@ -275,12 +275,12 @@ int trimkv_mark_recent(const trimkv_cache_t* c, int32_t floor, float* plane, voi
 }
 
 int trimkv_append(trimkv_cache_t* c, const void* k_new, const void* v_new, const float* beta_new, const int32_t* t,
-                  void* stream) {
+                  int32_t* status, void* stream) {
   int rc;
   if (!cache_shape_ok(c, &rc)) return rc;
   if (!k_new || !v_new || !beta_new || !t || !table_ok(c) || !pools_ok(c)) return TRIMKV_EINVAL;
   if (c->n_heads == 0) return TRIMKV_OK;
-  return launch_append(c, k_new, v_new, beta_new, t, S(stream));
+  return launch_append(c, k_new, v_new, beta_new, t, status, S(stream));
 }
 
 int trimkv_validate_cache(const trimkv_cache_t* c, const int32_t* t, void* ws, size_t ws_bytes, void* stream) {

@@ -186,10 +186,19 @@ __global__ void __launch_bounds__(NTP) k_cmp_index(int n_heads, int reserve, con
     pid = pid_n;
     lds_barrier();   // stage and wtot are rewritten by the next tile
   }
+  // a caller's count above the head's nonzero keep bytes: the pairs this
+  // head owns but did not fill become no-ops for the copy (source slot out
+  // of range), not stale words of an earlier call
+  for (int64_t j = (int64_t)carry + threadIdx.x; j < kh; j += NTP) {
+    const int64_t k = kb + j;
+    if (k >= 0 && k < cap) w.pairs[k] = make_uint2(~0u, ~0u);
+  }
 }
 
 // Grid-stride copy of kept rows: LPR lanes of 16 bytes per row, UNR rows per
-// lane group in flight.  Rows are read at random, written contiguously.  K
+// lane group in flight.  Rows are read at random, written contiguously.  A
+// pair whose source slot lies outside the source pool (left by counts that
+// disagree with the keep plane) copies nothing.  K
 // and V rows are loaded and stored non-temporally: each is touched once, and
 // the compacted pool is read next by decode attention, where write-back lines
 // left in the caches would otherwise be evicted during that read, competing
@@ -201,7 +210,7 @@ __global__ void __launch_bounds__(NT) k_cmp_copy(int n_heads, const uint8_t* __r
                                                  const int32_t* __restrict__ dst_off, int32_t* __restrict__ dst_ids,
                                                  uint8_t* __restrict__ dst_k, uint8_t* __restrict__ dst_v,
                                                  uint32_t* __restrict__ dst_meta, int64_t dst_pages,
-                                                 int64_t pair_cap) {
+                                                 int64_t src_slots) {
   constexpr int LPR = ROWB / 16;  // lanes per row
   constexpr int RPB = NT / LPR;   // rows per block pass
   constexpr int UNR = 4;
@@ -210,7 +219,7 @@ __global__ void __launch_bounds__(NT) k_cmp_copy(int n_heads, const uint8_t* __r
   const int64_t total_dst = min((int64_t)dst_off[n_heads], dst_pages);
   for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < total_dst; i += (int64_t)gridDim.x * NT)
     dst_ids[i] = (int32_t)i;
-  const int64_t total = min(w.total[0], pair_cap);
+  const int64_t total = min(w.total[0], src_slots);   // the pair list holds at most src_slots pairs
   if (total == 0) return;
   const int64_t dcap = dst_pages * PAGE;
   const int part = threadIdx.x % LPR;
@@ -223,7 +232,7 @@ __global__ void __launch_bounds__(NT) k_cmp_copy(int n_heads, const uint8_t* __r
     for (int u = 0; u < UNR; ++u) pr[u] = w.pairs[min(k0 + u * RPB, total - 1)];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int64_t s = pr[u].x;
+      const int64_t s = (int64_t)pr[u].x < src_slots ? (int64_t)pr[u].x : 0;
       kv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src_k + s * ROWB + part * 16));
       vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src_v + s * ROWB + part * 16));
       // lanes 0 and 1 of a row carry its ln(beta) and position
@@ -232,7 +241,7 @@ __global__ void __launch_bounds__(NT) k_cmp_copy(int n_heads, const uint8_t* __r
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t d = pr[u].y;
-      if (k0 + u * RPB < total && d < dcap) {
+      if (k0 + u * RPB < total && d < dcap && (int64_t)pr[u].x < src_slots) {
         __builtin_nontemporal_store(kv[u], reinterpret_cast<u32x4*>(dst_k + d * ROWB + part * 16));
         __builtin_nontemporal_store(vv[u], reinterpret_cast<u32x4*>(dst_v + d * ROWB + part * 16));
         if (part < 2) dst_meta[(d / PAGE) * (2 * PAGE) + part * PAGE + d % PAGE] = mv[u];

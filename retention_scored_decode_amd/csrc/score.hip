@@ -110,7 +110,8 @@ __global__ void __launch_bounds__(256) k_score(const int32_t* __restrict__ page_
   }
 }
 
-// One wave per head: write entry len[h] and bump len[h].
+// One wave per head: write entry len[h] and bump len[h].  A head without a
+// free slot is left unchanged and counted in *status (when given).
 template <typename T, int D>
 __global__ void __launch_bounds__(64) k_append(const int32_t* __restrict__ page_off,
                                                const int32_t* __restrict__ page_ids,
@@ -119,11 +120,14 @@ __global__ void __launch_bounds__(64) k_append(const int32_t* __restrict__ page_
                                                const T* __restrict__ k_new,
                                                const T* __restrict__ v_new,
                                                const float* __restrict__ beta_new,
-                                               const int32_t* __restrict__ t) {
+                                               const int32_t* __restrict__ t, int32_t* __restrict__ status) {
   const int h = blockIdx.x;
   const int n = len[h];
   const int64_t cap = (int64_t)(page_off[h + 1] - page_off[h]) * PAGE;
-  if (n >= cap) return;
+  if (n >= cap) {
+    if (threadIdx.x == 0 && status) atomicAdd(status, 1);
+    return;
+  }
   const int64_t page = page_ids[page_off[h] + n / PAGE];
   const int64_t slot = page * PAGE + n % PAGE;
   for (int d = threadIdx.x; d < D; d += 64) {
@@ -162,20 +166,20 @@ int launch_score(const trimkv_cache_t* c, int n_seg, const int32_t* seg, const i
 
 template <typename T, int D>
 static void append_t(trimkv_cache_t* c, const void* kn, const void* vn, const float* bn, const int32_t* t,
-                     hipStream_t st) {
+                     int32_t* status, hipStream_t st) {
   hipLaunchKernelGGL((k_append<T, D>), dim3(c->n_heads), dim3(64), 0, st, c->page_off, c->page_ids, c->len,
-                     (T*)c->k, (T*)c->v, c->meta, (const T*)kn, (const T*)vn, bn, t);
+                     (T*)c->k, (T*)c->v, c->meta, (const T*)kn, (const T*)vn, bn, t, status);
 }
 
 int launch_append(trimkv_cache_t* c, const void* kn, const void* vn, const float* bn, const int32_t* t,
-                  hipStream_t st) {
+                  int32_t* status, hipStream_t st) {
   if (c->n_heads == 0) return TRIMKV_OK;
   if (c->dtype == TRIMKV_BF16) {
-    if (c->head_dim == 128) append_t<uint16_t, 128>(c, kn, vn, bn, t, st);
-    else append_t<uint16_t, 64>(c, kn, vn, bn, t, st);
+    if (c->head_dim == 128) append_t<uint16_t, 128>(c, kn, vn, bn, t, status, st);
+    else append_t<uint16_t, 64>(c, kn, vn, bn, t, status, st);
   } else {
-    if (c->head_dim == 128) append_t<float, 128>(c, kn, vn, bn, t, st);
-    else append_t<float, 64>(c, kn, vn, bn, t, st);
+    if (c->head_dim == 128) append_t<float, 128>(c, kn, vn, bn, t, status, st);
+    else append_t<float, 64>(c, kn, vn, bn, t, status, st);
   }
   return check_launch();
 }

@@ -1,4 +1,5 @@
-// Exact global top-M per segment over fp32 keys, ties by (head, slot).
+// Exact global top-M per segment over fp32 keys, ties by head ascending, then
+// slot descending (the more recent entry of a head first).
 //
 // DBTrimKV page, Method 3: one global budget M_global; every cached entry of
 // every layer and head is ranked by predicted utility and the top M_global
@@ -12,13 +13,16 @@
 //      device atomics into a per-segment histogram; every block of the next
 //      kernel scans the finished histogram of its segment to narrow the
 //      prefix (no inter-block waits, no cache flushes inside a kernel);
-//   3. one pass over 1024-slot chunks in (head, slot) order: each chunk
-//      counts its ties (key == K*), obtains the ties of all earlier chunks of
-//      its segment by a decoupled look-back (one wave reads 64 predecessor
-//      words at a time; value and flag share one 64-bit word), and keeps
-//      key > K* plus the ties whose rank in the segment is below `need`.
+//   3. one pass over 1024-slot chunks: each chunk keeps key > K*; when the
+//      ties (key == K*) straddle the budget, the segment's chunks are taken
+//      in tie-rank order (heads ascending, within a head chunks descending),
+//      each counts its ties and obtains the ties of every chunk ranked
+//      before it by a decoupled look-back (one wave reads 64 predecessor
+//      words at a time; value and flag share one 64-bit word), and keeps the
+//      ties whose rank in the segment is below `need`, slots descending.
 // CSR order within a segment is head order and, within a head, slot
-// (= position) order, so this realises "score desc, head asc, position asc".
+// (= position) order, so this realises "score desc, head asc, position
+// desc".
 #include <algorithm>
 #include <type_traits>
 
@@ -66,8 +70,8 @@ struct SelWs {
   int n_seg;
   uint32_t* hist;       // [n_seg][HIST_WORDS]
   uint64_t* look;       // [Tmax] look-back words: 0 | flag<<62 | value
-  uint32_t* ticket;     // [2 + n_seg]: [1] error flag, [2 + s] ticket of segment s
-  uint32_t* error;      // nonzero if a look-back wait timed out
+  uint32_t* ticket;     // [2 + n_seg]: [2 + s] ticket of segment s
+  int32_t* status;      // caller's failure counter (nullable): +1 per timed-out look-back wait
   double* part;         // [Tmax]
 };
 
@@ -519,10 +523,14 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
       const int cb = st.chunk_begin;
       const bool act = threadIdx.x < GT;
       for (int pos = i; pos < e; ++pos) {
-        // process the segment's chunk of the next ticket
+        // process the segment's chunk of the next ticket: ticket k is the
+        // k-th chunk in tie-rank order, heads ascending and, within a head,
+        // chunks descending (the more recent entries rank first)
         if (threadIdx.x == 0) sh_c = cb + (int)atomicAdd(w.ticket + 2 + sg, 1u);
         lds_barrier();
-        const int c = sh_c;
+        const int k = sh_c;
+        const int hk = w.meta[k].x;   // the chunks of head hk occupy the same index range in both orders
+        const int c = w.chunk_off[hk] + w.chunk_off[hk + 1] - 1 - k;
         const int4 m = w.meta[c];
         const int nv = m.w & 0xFFFF;
         float a[4] = {0.f, 0.f, 0.f, 0.f};
@@ -533,13 +541,13 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
         uint32_t gtm = 0, eqm = 0;
         if (act) classify(st, a, i0, nv, gtm, eqm);
         int64_t eq_total;
-        int64_t rank = block_exclusive_scan<NT>((int64_t)__popc(eqm), tmp, &eq_total);
+        const int64_t before = block_exclusive_scan<NT>((int64_t)__popc(eqm), tmp, &eq_total);
         if (threadIdx.x < WAVE) {
           int64_t excl = 0;
-          if (c != cb) {
+          if (k != cb) {
             if (lane == 0)
-              __hip_atomic_store(w.look + c, LB_AGG | (uint64_t)eq_total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            int base = c - 1;   // window: chunks base, base-1, ..., base-63
+              __hip_atomic_store(w.look + k, LB_AGG | (uint64_t)eq_total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            int base = k - 1;   // window: tickets base, base-1, ..., base-63
             uint32_t spins = 0;
             while (true) {
               const int jj = base - lane;
@@ -551,8 +559,8 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
               const int first = pm ? __ffsll((long long)pm) - 1 : WAVE;   // nearest prefix in the window
               const uint64_t need = first == WAVE ? ~0ull : ((2ull << first) - 1ull);
               if (zm & need) {  // a predecessor has not published yet
-                if (++spins > SPIN_LIMIT) {  // never expected; keeps every wave finite
-                  if (lane == 0) atomicOr(w.error, 1u);
+                if (++spins > SPIN_LIMIT) {  // never expected; keeps every wave finite, reported
+                  if (lane == 0 && w.status) atomicAdd(w.status, 1);
                   break;
                 }
                 __builtin_amdgcn_s_sleep(1);
@@ -566,16 +574,18 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
             }
           }
           if (lane == 0) {
-            __hip_atomic_store(w.look + c, LB_PREFIX | (uint64_t)(excl + eq_total), __ATOMIC_RELAXED,
+            __hip_atomic_store(w.look + k, LB_PREFIX | (uint64_t)(excl + eq_total), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
             sh_excl = excl;
           }
         }
         lds_barrier();
-        rank += sh_excl;
+        // rank of this thread's last tie: ties of earlier tickets, then the
+        // chunk's ties in later slots; within the thread, slots descending
+        int64_t rank = sh_excl + (eq_total - before - __popc(eqm));
         uint32_t km = gtm;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 3; q >= 0; --q) {
           if (eqm & (1u << q)) {
             if (rank < st.remaining) km |= 1u << q;
             ++rank;
@@ -618,7 +628,7 @@ SelWs carve(const trimkv_cache_t* c, int n_seg, void* ws) {
   w.hist = (uint32_t*)(b + L.off[3]);
   w.look = (uint64_t*)(b + L.off[4]);
   w.ticket = (uint32_t*)(b + L.off[5]);
-  w.error = w.ticket + 1;
+  w.status = nullptr;
   w.part = (double*)(b + L.off[6]);
   return w;
 }
@@ -640,9 +650,10 @@ WsLayout select_ws_layout(const trimkv_cache_t* c, int n_seg) {
 }
 
 int launch_select(const trimkv_cache_t* c, const float* score, int n_seg, const int32_t* seg,
-                  const int64_t* budget, uint8_t* keep, int32_t* kept, double* keptsum, void* ws,
+                  const int64_t* budget, uint8_t* keep, int32_t* kept, double* keptsum, int32_t* status, void* ws,
                   hipStream_t st) {
   SelWs w = carve(c, n_seg, ws);
+  w.status = status;
   const int64_t T = max_chunks(c, CP);
   const int prep_blocks = prep_grid(c->n_heads, T, 1024);
   hipLaunchKernelGGL(k_sel_prep, dim3(prep_blocks), dim3(1024), 0, st, c->page_off, c->len, c->n_heads, n_seg, seg,

@@ -55,7 +55,7 @@ def lib():
         sig = {
             "trimkv_log_beta": [vp, vp, i64, i32, vp],
             "trimkv_score": [cp, i32, vp, vp, vp, vp],
-            "trimkv_select_global": [cp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp],
+            "trimkv_select_global": [cp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_compact": [cp, vp, vp, i32, i64, cp, vp, vp, sz, vp],
             "trimkv_compact_inplace": [cp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_decode_attn": [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp],
@@ -65,7 +65,7 @@ def lib():
             "trimkv_allocate": [vp, vp, i32, i64, vp, vp, vp],
             "trimkv_allocate_floor": [vp, vp, i32, i64, i32, vp, vp, vp],
             "trimkv_mark_recent": [cp, i32, vp, vp],
-            "trimkv_append": [cp, vp, vp, vp, vp, vp],
+            "trimkv_append": [cp, vp, vp, vp, vp, vp, vp],
             "trimkv_workspace_size": [ctypes.c_int, cp, i32, i32],
             "trimkv_validate_cache": [cp, vp, vp, sz, vp],
             "trimkv_strerror": [ctypes.c_int],
@@ -184,13 +184,14 @@ def score(cache: Cache, seg_head_begin: torch.Tensor, t: torch.Tensor, out: torc
 
 def select_global(cache: Cache, score: torch.Tensor, seg_head_begin: torch.Tensor, budget: torch.Tensor,
                   keep: torch.Tensor, kept: torch.Tensor, keptsum: Optional[torch.Tensor] = None,
-                  ws: Optional[torch.Tensor] = None, stream=None):
+                  ws: Optional[torch.Tensor] = None, stream=None, status: Optional[torch.Tensor] = None):
+    """status: optional int32 [1] device counter, incremented by timed-out waits."""
     n_seg = seg_head_begin.numel() - 1
     if ws is None:
         ws = workspace(OP_SELECT, cache, n_seg)
     _check(lib().trimkv_select_global(ctypes.byref(cache.struct()), _p(score), n_seg, _p(seg_head_begin),
-                                      _p(budget), _p(keep), _p(kept), _p(keptsum), _p(ws), ws.numel(),
-                                      _stream(stream)), "trimkv_select_global")
+                                      _p(budget), _p(keep), _p(kept), _p(keptsum), _p(status), _p(ws),
+                                      ws.numel(), _stream(stream)), "trimkv_select_global")
 
 
 def compact(src: Cache, keep: torch.Tensor, reserve: int, max_kept_total: int, dst: Cache,
@@ -274,9 +275,11 @@ def mark_recent(cache: Cache, floor: int, plane: torch.Tensor, stream=None):
 
 
 def append(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, beta_new: torch.Tensor, t: torch.Tensor,
-           stream=None):
+           stream=None, status: Optional[torch.Tensor] = None):
+    """status: optional int32 [1] device counter, incremented by the number
+    of heads that had no free slot."""
     _check(lib().trimkv_append(ctypes.byref(cache.struct()), _p(k_new), _p(v_new), _p(beta_new), _p(t),
-                               _stream(stream)), "trimkv_append")
+                               _p(status), _stream(stream)), "trimkv_append")
 
 
 def profile_next(start, stop):

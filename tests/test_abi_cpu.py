@@ -66,12 +66,12 @@ def test_null_and_inconsistent_arguments():
     # keep and lse_ref together
     assert L.trimkv_decode_attn(ctypes.byref(c), X, X, X, 4, ctypes.c_float(1.0), X, X, None, X, 1 << 30,
                                 None) == tk.EINVAL
-    assert L.trimkv_select_global(ctypes.byref(c), X, 5, X, X, X, X, None, X, 1 << 30, None) == tk.EINVAL
+    assert L.trimkv_select_global(ctypes.byref(c), X, 5, X, X, X, X, None, None, X, 1 << 30, None) == tk.EINVAL
     bad = fake_cache(nulls=("page_off",))
-    assert L.trimkv_select_global(ctypes.byref(bad), X, 1, X, X, X, X, None, X, 1 << 30, None) == tk.EINVAL
+    assert L.trimkv_select_global(ctypes.byref(bad), X, 1, X, X, X, X, None, None, X, 1 << 30, None) == tk.EINVAL
     assert L.trimkv_allocate(X, X, 0, 10, None, X, None) == tk.EINVAL
     assert L.trimkv_allocate(X, X, 4, -1, None, X, None) == tk.EINVAL
-    assert L.trimkv_append(ctypes.byref(c), None, X, X, X, None) == tk.EINVAL
+    assert L.trimkv_append(ctypes.byref(c), None, X, X, X, None, None) == tk.EINVAL
 
 
 def test_decode_err_argument_checks():
@@ -153,8 +153,8 @@ def test_workspace_checks():
     c = fake_cache()
     need = L.trimkv_workspace_size(tk.OP_SELECT, ctypes.byref(c), 1, 0)
     assert need > 0
-    assert L.trimkv_select_global(ctypes.byref(c), X, 1, X, X, X, X, None, X, need - 1, None) == tk.EWORKSPACE
-    assert L.trimkv_select_global(ctypes.byref(c), X, 1, X, X, X, X, None, None, need, None) == tk.EWORKSPACE
+    assert L.trimkv_select_global(ctypes.byref(c), X, 1, X, X, X, X, None, None, X, need - 1, None) == tk.EWORKSPACE
+    assert L.trimkv_select_global(ctypes.byref(c), X, 1, X, X, X, X, None, None, None, need, None) == tk.EWORKSPACE
     need = L.trimkv_workspace_size(tk.OP_DECODE_ATTN, ctypes.byref(c), 0, 4)
     assert L.trimkv_decode_attn(ctypes.byref(c), None, None, X, 4, ctypes.c_float(1.0), X, X, None, X, need - 1,
                                 None) == tk.EWORKSPACE
@@ -201,7 +201,7 @@ def test_keep_plane_alignment_and_slot_width():
     assert L.trimkv_decode_attn(ctypes.byref(src), odd, None, X, 4, ctypes.c_float(1.0), X, X, None, X, need,
                                 None) == tk.EINVAL
     need = L.trimkv_workspace_size(tk.OP_SELECT, ctypes.byref(src), 1, 0)
-    assert L.trimkv_select_global(ctypes.byref(src), X, 1, X, X, odd, X, None, X, need, None) == tk.EINVAL
+    assert L.trimkv_select_global(ctypes.byref(src), X, 1, X, X, odd, X, None, None, X, need, None) == tk.EINVAL
     # compaction carries slots in 32 bits
     huge = fake_cache(n_heads=4, n_pages=1 << 28)
     big_ws = L.trimkv_workspace_size(tk.OP_COMPACT, ctypes.byref(huge), 0, 0)

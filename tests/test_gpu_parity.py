@@ -121,8 +121,10 @@ def run_select(c, plane, seg, budgets, keptsum=False):
     keep = torch.full((c.n_pages * 16,), 7, dtype=torch.uint8, device="cuda")
     kept = torch.full((c.n_heads,), -1, dtype=torch.int32, device="cuda")
     ks = torch.full((c.n_heads,), np.nan, dtype=torch.float64, device="cuda") if keptsum else None
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
     tk.select_global(c, cuda(plane, np.float32), cuda(seg, np.int32), cuda(np.asarray(budgets), np.int64),
-                     keep, kept, ks)
+                     keep, kept, ks, status=status)
+    assert int(status.item()) == 0, "a tie-rank wait timed out"
     return keep.cpu().numpy(), kept.cpu().numpy(), (ks.cpu().numpy() if keptsum else None)
 
 
@@ -271,6 +273,75 @@ def test_compact_ragged_edges():
             for reserve in (0, 1, 17):
                 announce("compact ragged", dtype, d, p_keep, reserve)
                 check_compact(pc, keep, reserve, given_counts=reserve == 1)
+
+
+def test_compact_counts_that_disagree_with_keep():
+    """Per-head counts above or below the keep plane's nonzero bytes: the
+    layout is unspecified, but every access stays inside the pools (pairs
+    the counts reserve and the keep plane does not fill copy nothing), the
+    page table is the prefix sum of the given counts, and the heads before
+    the first wrong count are compacted exactly."""
+    rng = np.random.default_rng(55)
+    pc = synth.random_ragged_cache(321, n_heads=8, d=128, dtype="bf16", max_len=900, min_len=100)
+    keep = [rng.random(int(n)) < 0.4 for n in pc.length]
+    true = np.array([int(k.sum()) for k in keep], np.int64)
+    for delta in ([0, 0, 0, 5, 0, 0, 0, 0], [0, 0, 0, 0, -7, 0, 9, 0], [0, 3, 0, 0, 0, 0, 0, 11]):
+        counts = np.maximum(true + np.array(delta), 0)
+        announce("compact mismatched counts", delta)
+        c = upload(pc)
+        total = int(max(counts.sum(), true.sum()))
+        cap = dst_capacity(pc.n_heads, total, 1)
+        dst = tk.Cache.empty(pc.n_heads, cap, pc.head_dim, c.k.dtype)
+        keep_plane = plane_from_heads([k.astype(np.uint8) for k in keep], pc.page_off, pc.length, pc.n_pages,
+                                      fill=0, dtype=np.uint8)
+        used = torch.zeros(1, dtype=torch.int64, device="cuda")
+        tk.compact(c, cuda(keep_plane), 1, total, dst, used, kept=cuda(counts.astype(np.int32)))
+        torch.cuda.synchronize()
+        po, pi, ln, k, v, lnb, pos = download_cache(dst)
+        wpo, _, wln = ref.compact_layout(counts, 1)
+        assert np.array_equal(po, wpo) and np.array_equal(ln, wln)
+        ov = OracleView(pc)
+        first_bad = int(np.flatnonzero(np.array(delta) != 0)[0])
+        for h in range(first_bad):
+            assert np.array_equal(ref.gather_heads(k, po, pi, ln)[h], ov.k_raw[h][keep[h]]), h
+            assert np.array_equal(ref.gather_heads(pos, po, pi, ln)[h], ov.pos[h][keep[h]]), h
+
+
+def test_append_reports_heads_without_a_free_slot():
+    """trimkv_append into a cache whose heads are partly full: every full
+    head is left unchanged and counted in the status word (which the call
+    only increments); every other head receives the entry."""
+    pc = synth.random_ragged_cache(77, n_heads=6, d=64, dtype="bf16", max_len=70, min_len=40)
+    rng = np.random.default_rng(77)
+    keep = [np.ones(int(n), bool) for n in pc.length]
+    # compact without spare slots, so heads whose kept count is a multiple of 16 are full
+    for h in (1, 4):
+        keep[h][:] = False
+        keep[h][:32] = True
+    c = upload(pc)
+    cap = dst_capacity(pc.n_heads, int(pc.length.sum()), 0)
+    dst = tk.Cache.empty(pc.n_heads, cap, pc.head_dim, c.k.dtype)
+    keep_plane = plane_from_heads([k.astype(np.uint8) for k in keep], pc.page_off, pc.length, pc.n_pages,
+                                  fill=0, dtype=np.uint8)
+    used = torch.zeros(1, dtype=torch.int64, device="cuda")
+    tk.compact(c, cuda(keep_plane), 0, int(pc.length.sum()), dst, used)
+    len0 = dst.length.cpu().numpy().copy()
+    full = (len0 % 16 == 0)
+    assert full[1] and full[4]
+    status = torch.full((1,), 5, dtype=torch.int32, device="cuda")
+    t = int(pc.pos.max()) + 2
+    kn = synth.f64_to_bf16_bits(rng.standard_normal((pc.n_heads, 64)))
+    for rep in range(2):
+        tk.append(dst, kv_dev(kn, "bf16"), kv_dev(kn, "bf16"), cuda(np.full(pc.n_heads, 0.5, np.float32)),
+                  cuda(np.array([t + rep], np.int32)), status=status)
+    torch.cuda.synchronize()
+    n_full = int(full.sum())
+    # second call: heads that had one free slot are full after the first append
+    one_free = (len0 % 16 == 15)
+    assert int(status.item()) == 5 + 2 * n_full + int(one_free.sum())
+    ln = dst.length.cpu().numpy()
+    want = len0 + np.where(full, 0, np.where(one_free, 1, 2))
+    assert np.array_equal(ln, want)
 
 
 # --------------------------------------------------------------------------

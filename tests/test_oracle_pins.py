@@ -222,15 +222,30 @@ def test_select_constant_beta_is_sliding_window():
             assert np.array_equal(keep[h], want), (M, h)
 
 
-def test_select_beta_one_keeps_first_in_flat_order():
-    H, n = 4, 20
-    scores = [ref.score_f32(ref.ln_beta(np.ones(n, np.float32)), 50, np.arange(n)) for _ in range(H)]
-    for M in (0, 5, 20, 33, 80, 100):
-        keep, _ = ref.select_global(scores, [0, H], [M])
-        flat = np.concatenate(keep)
-        want = np.zeros(H * n, bool)
-        want[:min(M, H * n)] = True
-        assert np.array_equal(flat, want)
+def test_select_beta_one_retains_all_or_most_recent():
+    """beta = 1 for every entry: no decay, every score is 0.  A budget of at
+    least N keeps every entry; a smaller one fills the heads in (l, h) order,
+    and every head it reaches keeps its most recent entries (a suffix of the
+    head in position order)."""
+    rng = np.random.default_rng(23)
+    for trial in range(60):
+        H = int(rng.integers(1, 7))
+        lens = rng.integers(0, 40, H)
+        t = 64
+        scores = [ref.score_f32(ref.ln_beta(np.ones(n, np.float32)), t, np.sort(rng.choice(t, n, replace=False)))
+                  for n in lens]
+        N = int(lens.sum())
+        for M in (0, 1, int(rng.integers(0, N + 1)), max(N - 1, 0), N, N + 3):
+            keep, kept = ref.select_global(scores, [0, H], [M])
+            left = min(M, N)
+            for h in range(H):
+                k = min(left, int(lens[h]))
+                want = np.zeros(int(lens[h]), bool)
+                want[int(lens[h]) - k:] = True
+                assert np.array_equal(keep[h], want), (trial, M, h)
+                left -= k
+            if M >= N:
+                assert all(k.all() for k in keep)
 
 
 def test_select_segments_independent():
@@ -261,6 +276,32 @@ def test_compaction_round_trip_and_layout():
         for h in range(6):
             assert np.array_equal(out["k"][h], rows["k"][h][keep[h]])
             assert np.all(np.diff(out["pos"][h]) > 0)     # positions stay ascending
+
+
+def test_compaction_equals_page_by_page_appending():
+    """The compacted layout built constructively: every head's kept rows are
+    appended one at a time into fresh 16-slot pages opened in order, with
+    `reserve` free slots left per head (brute force, pure Python).  The
+    oracle's page table, lengths and rows read back through its CSR must
+    equal that construction."""
+    rng = np.random.default_rng(29)
+    for trial in range(60):
+        H = int(rng.integers(1, 7))
+        lens = rng.integers(0, 70, H)
+        rows = [[(h, i, int(rng.integers(1 << 30))) for i in range(int(n))] for h, n in enumerate(lens)]
+        keep = [rng.random(int(n)) < rng.uniform(0.0, 1.0) for n in lens]
+        reserve = int(rng.choice([0, 1, 3, 16, 17]))
+        bpo, bpi, bln, bpages = brute.compact_by_appending(rows, [k.tolist() for k in keep], reserve)
+        po, pi, ln, out = ref.compact({"r": [np.array(r, dtype=object).reshape(-1, 3) for r in rows]}, keep,
+                                      reserve)
+        assert list(po) == bpo and list(pi) == bpi and list(ln) == bln, trial
+        for h in range(H):
+            got = [tuple(int(v) for v in out["r"][h][j]) for j in range(int(ln[h]))]
+            back = [bpages[bpi[bpo[h] + j // 16]][j % 16] for j in range(bln[h])]
+            assert got == back, (trial, h)
+            # free slots: the head's pages hold exactly `reserve` or more spare slots, fewer than 16 + reserve
+            spare = 16 * (bpo[h + 1] - bpo[h]) - bln[h]
+            assert reserve <= spare < reserve + 16 or (spare == 0 and reserve == 0)
 
 
 def test_inplace_compaction_layout_and_sequential_shift():
@@ -552,6 +593,27 @@ def test_recency_floor_selection_and_allocation():
             assert np.array_equal(bt, fl)
         if w == 0:
             assert np.array_equal(bt, ref.allocate(ks, lens, B)[0])
+
+
+def test_allocation_is_the_least_squares_apportionment():
+    """Uncapped allocation against a property of largest-remainder
+    apportionment: among integer budgets with the right total it minimises
+    sum (b_h - x_h)^2, x_h = B mbar_h / S (brute force over every
+    composition of B); with distinct fractional parts it is the unique
+    minimiser.  Lengths never bind here."""
+    rng = np.random.default_rng(27)
+    for trial in range(150):
+        H = int(rng.integers(1, 5))
+        ks = rng.random(H)
+        B = int(rng.integers(0, 14))
+        b, mbar = ref.allocate(ks, [10 ** 6] * H, B)
+        S = math.fsum(1.0 - k for k in ks)
+        x = [B * (1.0 - k) / S for k in ks]
+        mins = brute.largest_remainder_l2(x, B)
+        assert list(b) in mins, (trial, list(b), mins)
+        fr = [xi - math.floor(xi) for xi in x]
+        if len(set(round(f, 9) for f in fr)) == H:
+            assert len(mins) == 1
 
 
 def test_allocation_rules():
