@@ -156,6 +156,37 @@ def select_global(scores, seg_head_begin, budgets):
     return keep, kept
 
 
+def select_flat(score, head, pos, budget):
+    """The selection of select_global for one segment given as flat arrays
+    (any entry order): keep mask of the top min(M, N) entries under the same
+    total order (score descending with -0.0 equal to +0.0 and NaN lowest,
+    then head ascending, then position descending).  The M-th key comes from
+    a partial sort (numpy partition) instead of a full sort: every entry
+    ranked above it is kept, and the entries equal to it are ranked by
+    (head, position) for the places left.  For long runs of selections
+    (one per decode step)."""
+    key = -np.asarray(score, np.float32)    # exact; ascending = score descending; NaN last
+    n = len(key)
+    m = max(0, min(int(budget), n))
+    keep = np.zeros(n, dtype=bool)
+    if m == 0:
+        return keep
+    if m == n:
+        keep[:] = True
+        return keep
+    kth = np.partition(key, m - 1)[m - 1]
+    if np.isnan(kth):
+        above, ties = ~np.isnan(key), np.isnan(key)
+    else:
+        above, ties = key < kth, key == kth
+    keep[above] = True
+    need = m - int(above.sum())
+    idx = np.flatnonzero(ties)
+    order = np.lexsort((-np.asarray(pos, np.int64)[idx], np.asarray(head, np.int64)[idx]))
+    keep[idx[order[:need]]] = True
+    return keep
+
+
 # --------------------------------------------------------------------------
 # a3: stable out-of-place compaction with prefix-sum page ids
 # --------------------------------------------------------------------------

@@ -204,6 +204,27 @@ def test_select_equals_full_sort(kind):
             assert sum(kept[seg[s]:seg[s + 1]]) == min(max(budgets[s], 0), sum(lens[seg[s]:seg[s + 1]]))
 
 
+@pytest.mark.parametrize("kind", SORT_KINDS)
+def test_select_flat_equals_full_sort(kind):
+    """The partial-sort selection over flat, shuffled entries keeps exactly
+    the set of a brute-force full sort (pure Python)."""
+    rng = np.random.default_rng(SORT_KINDS.index(kind) + 300)
+    for trial in range(150):
+        H = int(rng.integers(1, 7))
+        lens = rng.integers(0, 40, H)
+        scores = _random_scores(rng, kind, lens)
+        head = np.concatenate([np.full(n, h) for h, n in enumerate(lens)] + [np.zeros(0, int)])
+        pos = np.concatenate([np.sort(rng.choice(500, n, replace=False)) for n in lens] + [np.zeros(0, int)])
+        sc = np.concatenate(scores + [np.zeros(0, np.float32)])
+        perm = rng.permutation(len(sc))
+        N = len(sc)
+        for M in (0, 1, max(N - 1, 0), N, N + 4, int(rng.integers(0, N + 1))):
+            keep = ref.select_flat(sc[perm], head[perm], pos[perm], M)
+            got = set((int(head[perm][j]), int(pos[perm][j])) for j in np.flatnonzero(keep))
+            want = brute.select_sorted([(float(sc[j]), int(head[j]), int(pos[j])) for j in range(N)], M)
+            assert got == want, (trial, M)
+
+
 def test_select_constant_beta_is_sliding_window():
     # beta = c in (0,1) everywhere: the score only depends on age, so the
     # kept set is the newest floor(M/H) of every head plus one more for the
