@@ -240,6 +240,28 @@ int trimkv_decode_attn(const trimkv_cache_t* cache, const uint8_t* keep, const f
                        float* lse_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * trimkv_decode_attn_noalloc -- trimkv_decode_attn without a workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * outputs and kernels as trimkv_decode_attn, minus ws / ws_bytes: the
+ * partial results live in a static scratch array of
+ * TRIMKV_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds
+ * until the process ends.  The call allocates and frees nothing.  All calls
+ * on one GPU share that GPU's scratch: calls that overlap on one GPU (other
+ * streams, other host threads without ordering) race; calls ordered on one
+ * stream do not.  No part of the scratch needs clearing between calls.
+ * Errors: as trimkv_decode_attn; EWORKSPACE when the call would need more
+ * than TRIMKV_NOALLOC_SCRATCH_BYTES of partial results (about
+ * (waves + n_heads) * group * (head_dim + 3) * 4 bytes, waves = 2048 for the
+ * bf16 kernels on an MI355X); EHIP if the scratch address cannot be
+ * obtained.
+ */
+#define TRIMKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int trimkv_decode_attn_noalloc(const trimkv_cache_t* cache, const uint8_t* keep, const float* lse_ref,
+                               const void* q, int32_t group, float scale, float* out, float* dropped,
+                               float* lse_out, void* stream);
+
+/*
  * trimkv_decode_attn_gated -- retention-gated decode attention.
  * TRIM-KV page, section 2 (attention modulation: the retention score
  * multiplies the attention weights; the page applies it in training) used

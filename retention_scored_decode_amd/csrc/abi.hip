@@ -215,6 +215,19 @@ int trimkv_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float
   return launch_decode_attn(c, keep, lse_ref, q, group, scale, out, dropped, lse_out, ws, S(stream));
 }
 
+int trimkv_decode_attn_noalloc(const trimkv_cache_t* c, const uint8_t* keep, const float* lse_ref, const void* q,
+                               int32_t group, float scale, float* out, float* dropped, float* lse_out, void* stream) {
+  int rc;
+  if (!cache_shape_ok(c, &rc)) return rc;
+  if (group < 1 || group > 16) return TRIMKV_EUNSUPPORTED;
+  if ((keep && lse_ref) || !q || !out || !dropped || !table_ok(c) || !pools_ok(c) || ((uintptr_t)keep & 15))
+    return TRIMKV_EINVAL;
+  // a bound that needs no device query: too large for the scratch whatever the launch
+  if (noalloc_min_bytes(c, group) > (int64_t)TRIMKV_NOALLOC_SCRATCH_BYTES) return TRIMKV_EWORKSPACE;
+  if (c->n_heads == 0) return TRIMKV_OK;
+  return launch_decode_attn_noalloc(c, keep, lse_ref, q, group, scale, out, dropped, lse_out, S(stream));
+}
+
 int trimkv_decode_attn_gated(const trimkv_cache_t* c, int32_t n_seg, const int32_t* seg, const int32_t* t,
                              const uint8_t* keep, const void* q, int32_t group, float scale, float* out, float* dropped,
                              float* lse_out, void* ws, size_t ws_bytes, void* stream) {

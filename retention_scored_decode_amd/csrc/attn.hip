@@ -19,11 +19,18 @@
 // identical.  fp32 caches (small configurations) use one block per
 // (head, 16-page chunk) and VALU arithmetic.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
 #include "common.h"
 #include "launch.h"
+
+// Scratch of trimkv_decode_attn_noalloc: the partials of the flat split (or
+// the fp32 work list) live here instead of in a caller's workspace.  Each
+// GPU holds its own copy for the life of the process; host code reaches it
+// only through the address hipGetSymbolAddress returns for that device.
+static __device__ __align__(256) unsigned char scratch[TRIMKV_NOALLOC_SCRATCH_BYTES];
 
 namespace trimkv {
 
@@ -842,8 +849,8 @@ __global__ void __launch_bounds__(256) k_mass(const int32_t* __restrict__ page_o
 }
 
 
-AttnWs carve(const trimkv_cache_t* c, int group, void* ws, bool mass, bool err = false) {
-  WsLayout L = mass ? mass_ws_layout(c, group) : err ? err_ws_layout(c, group) : attn_ws_layout(c, group);
+AttnWs carve(const trimkv_cache_t* c, int group, void* ws, bool mass, bool err = false, int64_t slots = -1) {
+  WsLayout L = mass ? mass_ws_layout(c, group) : err ? err_ws_layout(c, group) : attn_ws_layout(c, group, slots);
   char* b = (char*)ws;
   AttnWs w;
   w.item_off = (int32_t*)(b + L.off[0]);
@@ -909,8 +916,8 @@ int64_t partial_slots(const trimkv_cache_t* c) {
 
 }  // namespace
 
-WsLayout attn_ws_layout(const trimkv_cache_t* c, int group) {
-  const int64_t S = partial_slots(c);
+WsLayout attn_ws_layout(const trimkv_cache_t* c, int group, int64_t slots) {
+  const int64_t S = slots >= 0 ? slots : partial_slots(c);
   const int64_t T = c->dtype == TRIMKV_F32 ? max_chunks(c, CHA_F32) : 0;
   WsLayout L;
   L.add(((int64_t)c->n_heads + 1) * 4);
@@ -939,10 +946,13 @@ WsLayout mass_ws_layout(const trimkv_cache_t* c, int group) {
   return L;
 }
 
-int launch_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float* lse_ref, const void* q,
-                       int group, float scale, float* out, float* dropped, float* lse_out, void* ws,
-                       hipStream_t st) {
-  AttnWs w = carve(c, group, ws, false);
+namespace {
+
+// The decode call on a workspace laid out for `slots` partial slots (-1:
+// the public layout, sized for the most waves a launch may use).
+int decode_attn_on(const trimkv_cache_t* c, const uint8_t* keep, const float* lse_ref, const void* q, int group,
+                   float scale, float* out, float* dropped, float* lse_out, void* ws, int64_t slots, hipStream_t st) {
+  AttnWs w = carve(c, group, ws, false, false, slots);
   const bool f32 = c->dtype == TRIMKV_F32;
   if (f32)
     hipLaunchKernelGGL(k_attn_prep, dim3(prep_grid(c->n_heads, max_chunks(c, CHA_F32), 2048)), dim3(1024), 0, st,
@@ -955,6 +965,57 @@ int launch_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float
   if (rc) return rc;
   launch_merge(c, a, 1, st);
   return check_launch();
+}
+
+// Address of this device's scratch, looked up once per device (with that
+// device current) and kept.
+std::mutex g_scratch_mu;
+constexpr int SCRATCH_MAX_DEV = 64;
+void* g_scratch_ptr[SCRATCH_MAX_DEV] = {};
+
+int device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return TRIMKV_EHIP;
+  if (dev < 0 || dev >= SCRATCH_MAX_DEV) return TRIMKV_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return TRIMKV_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TRIMKV_OK;
+}
+
+}  // namespace
+
+int launch_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float* lse_ref, const void* q,
+                       int group, float scale, float* out, float* dropped, float* lse_out, void* ws,
+                       hipStream_t st) {
+  return decode_attn_on(c, keep, lse_ref, q, group, scale, out, dropped, lse_out, ws, -1, st);
+}
+
+int64_t noalloc_min_bytes(const trimkv_cache_t* c, int group) {
+  const int64_t slots = c->dtype == TRIMKV_F32 ? max_chunks(c, CHA_F32) : (int64_t)c->n_heads + 1;
+  return (int64_t)attn_ws_layout(c, group, slots).total;
+}
+
+int launch_decode_attn_noalloc(const trimkv_cache_t* c, const uint8_t* keep, const float* lse_ref, const void* q,
+                               int group, float scale, float* out, float* dropped, float* lse_out, hipStream_t st) {
+  // partial slots: the waves this launch will use (plus one per head), not
+  // the most any launch may use, so that the scratch stays small
+  int64_t slots = max_chunks(c, CHA_F32);
+  if (c->dtype != TRIMKV_F32) {
+    int waves;
+    if (keep) waves = c->head_dim == 128 ? resident_waves(k_attn_bf16<128, A_MASK>) : resident_waves(k_attn_bf16<64, A_MASK>);
+    else waves = c->head_dim == 128 ? resident_waves(k_attn_bf16<128, A_PLAIN>) : resident_waves(k_attn_bf16<64, A_PLAIN>);
+    slots = (int64_t)waves + c->n_heads;
+  }
+  if (attn_ws_layout(c, group, slots).total > (size_t)TRIMKV_NOALLOC_SCRATCH_BYTES) return TRIMKV_EWORKSPACE;
+  void* ws = nullptr;
+  const int rc = device_scratch(&ws);
+  if (rc) return rc;
+  return decode_attn_on(c, keep, lse_ref, q, group, scale, out, dropped, lse_out, ws, slots, st);
 }
 
 int launch_decode_attn_err(const trimkv_cache_t* c, const uint8_t* keep, const void* q, int group, float scale,

@@ -34,7 +34,7 @@ inline int64_t max_chunks(const trimkv_cache_t* c, int cp) { return c->n_pages /
 WsLayout select_ws_layout(const trimkv_cache_t* c, int n_seg);
 WsLayout err_ws_layout(const trimkv_cache_t* c, int group);
 WsLayout compact_ws_layout(const trimkv_cache_t* c);
-WsLayout attn_ws_layout(const trimkv_cache_t* c, int group);
+WsLayout attn_ws_layout(const trimkv_cache_t* c, int group, int64_t slots = -1);
 WsLayout mass_ws_layout(const trimkv_cache_t* c, int group);
 
 int launch_log_beta(const float* beta, float* lnb, int64_t n, int out_page_stride, hipStream_t st);
@@ -58,6 +58,10 @@ int launch_decode_attn_err(const trimkv_cache_t* c, const uint8_t* keep, const v
 int launch_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float* lse_ref, const void* q,
                        int group, float scale, float* out, float* dropped, float* lse_out, void* ws,
                        hipStream_t st);
+// allocation-free decode: partials in a static per-device scratch array
+int64_t noalloc_min_bytes(const trimkv_cache_t* c, int group);
+int launch_decode_attn_noalloc(const trimkv_cache_t* c, const uint8_t* keep, const float* lse_ref, const void* q,
+                               int group, float scale, float* out, float* dropped, float* lse_out, hipStream_t st);
 int launch_attn_mass(const trimkv_cache_t* c, const void* q, int group, float scale, float* mass,
                      float* lse_full, void* ws, hipStream_t st);
 int launch_allocate_floor(const double* keptsum, const int32_t* len, int n_heads, int64_t budget, int floor_w,

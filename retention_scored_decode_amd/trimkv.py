@@ -22,6 +22,7 @@ OP_SCORE, OP_SELECT, OP_COMPACT, OP_DECODE_ATTN, OP_ATTN_MASS, OP_VALIDATE, OP_D
 
 EXPORTS = ["trimkv_log_beta", "trimkv_score", "trimkv_select_global", "trimkv_compact",
            "trimkv_decode_attn", "trimkv_decode_attn_gated", "trimkv_decode_attn_err", "trimkv_attn_mass",
+           "trimkv_decode_attn_noalloc",
            "trimkv_allocate", "trimkv_compact_inplace",
            "trimkv_allocate_floor", "trimkv_mark_recent", "trimkv_append",
            "trimkv_workspace_size", "trimkv_validate_cache", "trimkv_strerror", "trimkv_profile_next"]
@@ -59,6 +60,7 @@ def lib():
             "trimkv_compact": [cp, vp, vp, i32, i64, cp, vp, vp, sz, vp],
             "trimkv_compact_inplace": [cp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_decode_attn": [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp],
+            "trimkv_decode_attn_noalloc": [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp],
             "trimkv_decode_attn_err": [cp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_decode_attn_gated": [cp, i32, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp],
             "trimkv_attn_mass": [cp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp],
@@ -226,6 +228,15 @@ def decode_attn(cache: Cache, q: torch.Tensor, group: int, scale: float, out: to
     _check(lib().trimkv_decode_attn(ctypes.byref(cache.struct()), _p(keep), _p(lse_ref), _p(q), int(group),
                                     float(scale), _p(out), _p(dropped), _p(lse_out), _p(ws), ws.numel(),
                                     _stream(stream)), "trimkv_decode_attn")
+
+
+def decode_attn_noalloc(cache: Cache, q: torch.Tensor, group: int, scale: float, out: torch.Tensor,
+                        dropped: torch.Tensor, keep: Optional[torch.Tensor] = None,
+                        lse_ref: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None, stream=None):
+    """decode_attn without a workspace (the library's static per-GPU scratch)."""
+    _check(lib().trimkv_decode_attn_noalloc(ctypes.byref(cache.struct()), _p(keep), _p(lse_ref), _p(q), int(group),
+                                            float(scale), _p(out), _p(dropped), _p(lse_out), _stream(stream)),
+           "trimkv_decode_attn_noalloc")
 
 
 def decode_attn_gated(cache: Cache, seg: torch.Tensor, t: torch.Tensor, q: torch.Tensor, group: int, scale: float,

@@ -18,7 +18,7 @@ def declared():
 
 def test_exports_every_declared_symbol():
     names = declared()
-    assert len(names) == 17
+    assert len(names) == 18
     L = tk.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -228,3 +228,19 @@ def test_build_rejects_kernels_with_scratch():
     ])
     assert scratch_users(rep) == [("k_b", 60)]
     assert scratch_users(rep.replace(": 60 ", ": 0 ")) == []
+
+
+def test_noalloc_decode_rejects_calls_beyond_its_scratch():
+    """The allocation-free decode refuses, before any device call, a cache
+    whose partials cannot fit the static scratch, and checks its arguments
+    as the workspace variant does."""
+    L = tk.lib()
+    big = fake_cache(n_heads=1 << 20, n_pages=1 << 22)
+    f = lambda c, g=4, keep=None, lse=None, q=X: L.trimkv_decode_attn_noalloc(
+        ctypes.byref(c), keep, lse, q, g, ctypes.c_float(0.1), X, X, None, None)
+    assert f(big) == tk.EWORKSPACE
+    c = fake_cache()
+    assert f(c, g=17) == tk.EUNSUPPORTED
+    assert f(c, q=None) == tk.EINVAL
+    assert f(c, keep=X, lse=X) == tk.EINVAL
+    assert f(fake_cache(head_dim=96)) == tk.EUNSUPPORTED
