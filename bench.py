@@ -352,6 +352,16 @@ def main():
                            args.steps)
     assert bool(torch.isfinite(err).all())
 
+    # scores formed inside the selection's first pass (trimkv_score_select):
+    # the score and select stages in one call, same outputs
+    score2 = torch.empty_like(score)
+    keep2 = torch.empty_like(keep)
+    kept2 = torch.empty_like(kept)
+    f_t, f_k = timed_calls(lambda: tk.score_select(src, seg, t_dev, budget, score2, keep2, kept2, ws=ws_sel),
+                           args.steps)
+    n_csr = int(pc.page_off[-1]) * 16
+    assert torch.equal(keep2[:n_csr], keep[:n_csr]) and torch.equal(kept2, kept)
+
     # retention-gated decode attention (TRIM-KV section 2 modulation, at
     # decode time) over the compacted cache the last step left: the decode
     # stage's reads plus ln beta and position of every kept entry
@@ -491,7 +501,14 @@ def main():
     err_t, err_kt = e_t, e_k
     g_algo = algo["decode"] + 8 * kept_total
     g_tm, g_km = g_t, g_k
-    extras = {"attend_err": {"us": round(err_t * 1e6, 2), "algo_bytes": err_algo,
+    extras = {"score_select": {"us": round(f_t * 1e6, 2), "main_kernels_us": round(f_k * 1e6, 2),
+                               "score_plus_select_us": round((t["score"] + t["select"]) * 1e6, 2),
+                               "select_equivalent_us": round((f_t - t["score"]) * 1e6, 2),
+                               "entries_per_s": round(N / f_t, 1),
+                               "what": "trimkv_score_select: scores formed inside the selection's first pass "
+                                       "(the score and select stages in one call, bit-identical outputs); "
+                                       "select_equivalent = this call minus the score stage"},
+              "attend_err": {"us": round(err_t * 1e6, 2), "algo_bytes": err_algo,
                              "GBps": round(err_algo / err_t / 1e9, 1),
                              "frac_hbm": round(err_algo / err_t / 1e9 / HBM_PEAK_GBS, 4),
                              "main_kernel": "k_attn_bf16<128, 3>", "main_kernel_us": round(err_kt * 1e6, 2),
@@ -1028,8 +1045,37 @@ def bench_streaming(args, w):
         torch.cuda.synchronize()
         return view, ev[0].elapsed_time(ev[1]) * 1e-3
 
+    from retention_scored_decode_amd.stream import StreamLoop
+    banks = {"k": k_all, "v": v_all, "beta": beta_all, "q": q_all, "t": t_all}
+
+    def run_loop(n, graph):
+        """steps 1..n out of place through StreamLoop (scores formed inside
+        the selection's first pass): steps 2..n launched eagerly, or captured
+        in graphs of 64 steps and replayed"""
+        step_one(pools[0], 1)
+        loop = StreamLoop(pools, M, G, scale, banks, first=1)
+        if graph:
+            loop.capture(n - 1)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        if graph:
+            loop.replay()
+        else:
+            loop.run(n - 1)
+        ev[1].record()
+        torch.cuda.synchronize()
+        assert int(loop.status.sum().item()) == 0
+        return loop, ev[0].elapsed_time(ev[1]) * 1e-3
+
     run_oop(min(S, 4))                       # first launches load the kernels
     run_inplace(min(S, 4))
+    run_loop(min(S, 4), False)
+    run_loop(min(S, 4), True)
+    loop_e, t_staged = run_loop(S, False)
+    len_e = loop_e.cache.length.clone()
+    loop_g, t_graph = run_loop(S, True)
+    assert torch.equal(loop_g.cache.length, len_e)
+    del loop_e, loop_g
     cur, t_first, t_oop = run_oop(S)
     assert int(cur.length.sum().item()) == M
     assert tk.validate_cache(cur, t_all[S - 1] + 1) == tk.OK
@@ -1060,6 +1106,14 @@ def bench_streaming(args, w):
                             "step_algo_bytes": step_algo},
            "in_place": {"steps_per_s": round(S_t / t_inp, 1), "us_per_step": round(t_inp / S_t * 1e6, 2),
                         "home_spare_slots_per_head": RES},
+           "fused_score_select": {"steps_per_s": round(S_t / t_staged, 1),
+                                  "us_per_step": round(t_staged / S_t * 1e6, 2),
+                                  "what": "out of place, trimkv_score_select in place of score + select"},
+           "hip_graph": {"steps_per_s": round(S_t / t_graph, 1), "us_per_step": round(t_graph / S_t * 1e6, 2),
+                         "GBps": round(per_step * S_t / t_graph / 1e9, 1),
+                         "frac_hbm": round(per_step * S_t / t_graph / 1e9 / HBM_PEAK_GBS, 4),
+                         "what": "the fused-score steps captured in HIP graphs of 64 steps and replayed, "
+                                 "against the same steps launched eagerly (fused_score_select)"},
            "first_step_us": round(t_first * 1e6, 2),
            "first_step_what": "append, score, select, mask-mode attention and eviction of the %d-entry "
                               "prefill (step 1)" % N0,

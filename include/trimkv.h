@@ -151,6 +151,24 @@ int trimkv_select_global(const trimkv_cache_t* cache, const float* score, int32_
                          void* stream);
 
 /*
+ * trimkv_score_select -- trimkv_score and trimkv_select_global in one call:
+ * the retention score of every valid slot is formed inside the selection's
+ * first pass (DBTrimKV page, Method 2: r = beta^(t-i), ln r = (t - i) ln beta;
+ * Method 3: one global top M over every layer and head), so the score plane
+ * is written once and not read back for the first histogram.
+ * Outputs are bit for bit those of trimkv_score (score, NaN in padding
+ * slots) followed by trimkv_select_global on that plane.
+ *   n_seg, seg_head_begin, t: as trimkv_score;  budget: as trimkv_select_global
+ *   score:   device fp32 CSR plane, out (16-byte aligned)
+ *   keep, kept, keptsum, status: as trimkv_select_global
+ *   ws:      trimkv_workspace_size(TRIMKV_OP_SELECT, cache, n_seg, 0) bytes
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE.
+ */
+int trimkv_score_select(const trimkv_cache_t* cache, int32_t n_seg, const int32_t* seg_head_begin,
+                        const int32_t* t, const int64_t* budget, float* score, uint8_t* keep, int32_t* kept,
+                        double* keptsum, int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * trimkv_compact -- physical eviction: stable out-of-place compaction.
  * DBTrimKV page, Method 4 (paged per-head variable length); ContourKV page,
  * section 2 (the budget must shrink storage, not just mask it).

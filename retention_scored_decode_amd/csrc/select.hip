@@ -48,6 +48,7 @@ constexpr int HC = 4;
 __host__ __device__ constexpr int copy_words(int nb) { return nb + 32; }
 constexpr int HIST_WORDS = HC * (2 * copy_words(2048) + copy_words(1024));
 constexpr uint32_t SPIN_LIMIT = 1u << 26;
+
 constexpr unsigned N_CU = 256;  // compute units of an MI355X
 
 enum { MODE_NORMAL = 0, MODE_ALL = 1, MODE_NONE = 2 };
@@ -205,13 +206,27 @@ __device__ __forceinline__ void opaque(T (&x)[R][4]) {
     for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(x[r][j]));
 }
 
+// Inputs of the retention score, for the pass that forms the scores itself.
+struct ScoreSrc {
+  const int32_t* page_ids;   // physical page of each CSR page
+  const uint32_t* meta;      // [n_pages][2][16]: ln beta bits, positions
+  const int32_t* t;          // decode step of each segment
+  float* score;              // CSR plane, written
+};
+
 // Block b histograms chunks [b*CPB, b*CPB + CPB), CG chunks per round
 // (GT threads of 4 slots per chunk): metadata first, then every key load in
 // flight while the previous pass's bin is located.  The block's histogram is
 // merged into the segment's once per segment run, so the number of device
 // atomics per bin falls with the number of chunks per block.
-template <int PASS, int HB>
-__global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __restrict__ score, SelWs w) {
+// FUSED (pass 0 only): the retention score of every slot is formed here from
+// its page's ln beta and position, fp32(t - pos) * ln beta with one rounding
+// exactly as trimkv_score forms it, written to the CSR score plane (NaN in
+// padding slots) and histogrammed in the same pass.
+template <int PASS, int HB, bool FUSED = false>
+__global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __restrict__ score, SelWs w,
+                                                 ScoreSrc src) {
+  static_assert(!FUSED || PASS == 0, "scores are formed in the first pass");
   constexpr int RND = HB / CG;   // rounds of CG chunks (shadows the decision kernel's)
   static_assert(HB % CG == 0 && HB <= CPB, "chunk rounds");
   constexpr int NB = PASS == 2 ? 1024 : 2048;
@@ -233,12 +248,50 @@ __global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __res
   SegState st0;
   {
     float4 kv[RND];
+    if constexpr (FUSED) {
+      // page ids, then every page's ln beta and positions in flight at once
+      int pid[RND];
 #pragma unroll
-    for (int r = 0; r < RND; ++r) {
-      const int k = r * CG + grp;
-      const int4 m = umeta(sm, k);
-      kv[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (k < nc && i0 < (m.w & 0xFFFF)) kv[r] = *reinterpret_cast<const float4*>(score + (int64_t)m.z * PAGE + i0);
+      for (int r = 0; r < RND; ++r) {
+        const int k = r * CG + grp;
+        const int4 m = umeta(sm, k);
+        pid[r] = (k < nc && i0 < (m.w >> 16) * PAGE) ? src.page_ids[m.z + i0 / PAGE] : -1;
+      }
+      float4 lb[RND];
+      int4 ps[RND];
+#pragma unroll
+      for (int r = 0; r < RND; ++r) {
+        if (pid[r] >= 0) {
+          const uint32_t* mp = src.meta + (int64_t)pid[r] * (2 * PAGE) + (i0 % PAGE);
+          lb[r] = *reinterpret_cast<const float4*>(mp);
+          ps[r] = *reinterpret_cast<const int4*>(mp + PAGE);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < RND; ++r) {
+        const int k = r * CG + grp;
+        const int4 m = umeta(sm, k);
+        kv[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (pid[r] >= 0) {
+          const int nv = m.w & 0xFFFF;
+          const int tt = src.t[m.y];
+          float4 o = make_float4(qnan(), qnan(), qnan(), qnan());
+          if (i0 < nv) o.x = __fmul_rn((float)(tt - ps[r].x), lb[r].x);
+          if (i0 + 1 < nv) o.y = __fmul_rn((float)(tt - ps[r].y), lb[r].y);
+          if (i0 + 2 < nv) o.z = __fmul_rn((float)(tt - ps[r].z), lb[r].z);
+          if (i0 + 3 < nv) o.w = __fmul_rn((float)(tt - ps[r].w), lb[r].w);
+          *reinterpret_cast<float4*>(src.score + (int64_t)m.z * PAGE + i0) = o;
+          kv[r] = o;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < RND; ++r) {
+        const int k = r * CG + grp;
+        const int4 m = umeta(sm, k);
+        kv[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (k < nc && i0 < (m.w & 0xFFFF)) kv[r] = *reinterpret_cast<const float4*>(score + (int64_t)m.z * PAGE + i0);
+      }
     }
     // state for the first segment run while the scores are in flight
     if (PASS > 0) st0 = state_after(w, sm[0].y, PASS - 1, HB);
@@ -649,9 +702,13 @@ WsLayout select_ws_layout(const trimkv_cache_t* c, int n_seg) {
   return L;
 }
 
-int launch_select(const trimkv_cache_t* c, const float* score, int n_seg, const int32_t* seg,
-                  const int64_t* budget, uint8_t* keep, int32_t* kept, double* keptsum, int32_t* status, void* ws,
-                  hipStream_t st) {
+namespace {
+
+// The selection's kernels; with `src.score` set, the first pass forms the
+// scores itself (score + select in one call).
+int select_kernels(const trimkv_cache_t* c, const float* score, int n_seg, const int32_t* seg,
+                   const int64_t* budget, uint8_t* keep, int32_t* kept, double* keptsum, int32_t* status, void* ws,
+                   ScoreSrc src, hipStream_t st) {
   SelWs w = carve(c, n_seg, ws);
   w.status = status;
   const int64_t T = max_chunks(c, CP);
@@ -660,18 +717,21 @@ int launch_select(const trimkv_cache_t* c, const float* score, int n_seg, const 
                      budget, T, w, kept);
   const unsigned hb = (unsigned)((T + CPB - 1) / CPB);
   prof_begin(st);
-  hipLaunchKernelGGL((k_sel_hist<0, CPB>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w);   // 48 VGPRs
+  if (src.score)
+    hipLaunchKernelGGL((k_sel_hist<0, CPB, true>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);
+  else
+    hipLaunchKernelGGL((k_sel_hist<0, CPB>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);   // 48 VGPRs
   // Later passes (78 VGPRs at CPB chunks per block: one block per CU), when
   // there are more blocks with work than CUs (counted as if the pool's pages
   // were all in use): half the chunks per block, whose fewer live keys (64
   // VGPRs) let two blocks share a CU.
   if ((c->n_pages / CP + CPB - 1) / CPB > N_CU) {
     const unsigned hb2 = (unsigned)((T + CPB / 2 - 1) / (CPB / 2));
-    hipLaunchKernelGGL((k_sel_hist<1, CPB / 2>), dim3(hb2), dim3(NT), 0, st, c->n_heads, score, w);
-    hipLaunchKernelGGL((k_sel_hist<2, CPB / 2>), dim3(hb2), dim3(NT), 0, st, c->n_heads, score, w);
+    hipLaunchKernelGGL((k_sel_hist<1, CPB / 2>), dim3(hb2), dim3(NT), 0, st, c->n_heads, score, w, src);
+    hipLaunchKernelGGL((k_sel_hist<2, CPB / 2>), dim3(hb2), dim3(NT), 0, st, c->n_heads, score, w, src);
   } else {
-    hipLaunchKernelGGL((k_sel_hist<1, CPB>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w);
-    hipLaunchKernelGGL((k_sel_hist<2, CPB>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w);
+    hipLaunchKernelGGL((k_sel_hist<1, CPB>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);
+    hipLaunchKernelGGL((k_sel_hist<2, CPB>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);
   }
   hipLaunchKernelGGL(k_sel_decide, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, keep, kept,
                      keptsum != nullptr);
@@ -680,6 +740,21 @@ int launch_select(const trimkv_cache_t* c, const float* score, int n_seg, const 
     hipLaunchKernelGGL(k_sel_headsum, dim3((unsigned)((c->n_heads + 255) / 256)), dim3(256), 0, st, c->n_heads, w,
                        keptsum);
   return check_launch();
+}
+
+}  // namespace
+
+int launch_select(const trimkv_cache_t* c, const float* score, int n_seg, const int32_t* seg,
+                  const int64_t* budget, uint8_t* keep, int32_t* kept, double* keptsum, int32_t* status, void* ws,
+                  hipStream_t st) {
+  return select_kernels(c, score, n_seg, seg, budget, keep, kept, keptsum, status, ws, ScoreSrc{}, st);
+}
+
+int launch_score_select(const trimkv_cache_t* c, int n_seg, const int32_t* seg, const int32_t* t,
+                        const int64_t* budget, float* score, uint8_t* keep, int32_t* kept, double* keptsum,
+                        int32_t* status, void* ws, hipStream_t st) {
+  return select_kernels(c, score, n_seg, seg, budget, keep, kept, keptsum, status, ws,
+                        ScoreSrc{c->page_ids, c->meta, t, score}, st);
 }
 
 }  // namespace trimkv

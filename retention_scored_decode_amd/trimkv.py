@@ -22,7 +22,7 @@ OP_SCORE, OP_SELECT, OP_COMPACT, OP_DECODE_ATTN, OP_ATTN_MASS, OP_VALIDATE, OP_D
 
 EXPORTS = ["trimkv_log_beta", "trimkv_score", "trimkv_select_global", "trimkv_compact",
            "trimkv_decode_attn", "trimkv_decode_attn_gated", "trimkv_decode_attn_err", "trimkv_attn_mass",
-           "trimkv_decode_attn_noalloc",
+           "trimkv_decode_attn_noalloc", "trimkv_score_select",
            "trimkv_allocate", "trimkv_compact_inplace",
            "trimkv_allocate_floor", "trimkv_mark_recent", "trimkv_append",
            "trimkv_workspace_size", "trimkv_validate_cache", "trimkv_strerror", "trimkv_profile_next"]
@@ -58,6 +58,7 @@ def lib():
             "trimkv_score": [cp, i32, vp, vp, vp, vp],
             "trimkv_select_global": [cp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_compact": [cp, vp, vp, i32, i64, cp, vp, vp, sz, vp],
+            "trimkv_score_select": [cp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_compact_inplace": [cp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_decode_attn": [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp],
             "trimkv_decode_attn_noalloc": [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp],
@@ -194,6 +195,18 @@ def select_global(cache: Cache, score: torch.Tensor, seg_head_begin: torch.Tenso
     _check(lib().trimkv_select_global(ctypes.byref(cache.struct()), _p(score), n_seg, _p(seg_head_begin),
                                       _p(budget), _p(keep), _p(kept), _p(keptsum), _p(status), _p(ws),
                                       ws.numel(), _stream(stream)), "trimkv_select_global")
+
+
+def score_select(cache: Cache, seg_head_begin: torch.Tensor, t: torch.Tensor, budget: torch.Tensor,
+                 score: torch.Tensor, keep: torch.Tensor, kept: torch.Tensor, keptsum: Optional[torch.Tensor] = None,
+                 ws: Optional[torch.Tensor] = None, stream=None, status: Optional[torch.Tensor] = None):
+    """score() and select_global() in one call (scores formed in the first pass)."""
+    n_seg = seg_head_begin.numel() - 1
+    if ws is None:
+        ws = workspace(OP_SELECT, cache, n_seg)
+    _check(lib().trimkv_score_select(ctypes.byref(cache.struct()), n_seg, _p(seg_head_begin), _p(t), _p(budget),
+                                     _p(score), _p(keep), _p(kept), _p(keptsum), _p(status), _p(ws), ws.numel(),
+                                     _stream(stream)), "trimkv_score_select")
 
 
 def compact(src: Cache, keep: torch.Tensor, reserve: int, max_kept_total: int, dst: Cache,

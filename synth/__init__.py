@@ -156,6 +156,8 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 def _draw_beta(rng: np.random.Generator, dist, n: int) -> np.ndarray:
     if dist[0] == "beta":
         return rng.beta(dist[1], dist[2], n)
+    if dist[0] == "const":   # the same retention for every entry (closed-form cases)
+        return np.full(n, float(dist[1]))
     if dist[0] == "mix":
         w, (a1, b1), (a2, b2) = dist[1], dist[2], dist[3]
         u = rng.random(n)

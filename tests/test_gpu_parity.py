@@ -113,6 +113,64 @@ def test_score_parity(name):
     assert np.all(np.isnan(plane[:total][~valid]))
 
 
+def _score_select_case(pc, seg, t_seg, budgets):
+    """trimkv_score_select against trimkv_score then trimkv_select_global on
+    the same cache (score plane, keep plane, kept counts and kept sums bit
+    for bit), and both against the oracle."""
+    c = upload(pc)
+    ov = OracleView(pc)
+    n = pc.n_pages * 16
+    seg_d, t_d, b_d = cuda(seg, np.int32), cuda(np.asarray(t_seg, np.int32)), cuda(np.asarray(budgets), np.int64)
+    s1 = torch.full((n,), 123.0, dtype=torch.float32, device="cuda")
+    s2 = torch.full((n,), 321.0, dtype=torch.float32, device="cuda")
+    k1 = torch.full((n,), 7, dtype=torch.uint8, device="cuda")
+    k2 = torch.full((n,), 9, dtype=torch.uint8, device="cuda")
+    kept1 = torch.full((pc.n_heads,), -1, dtype=torch.int32, device="cuda")
+    kept2 = torch.full((pc.n_heads,), -2, dtype=torch.int32, device="cuda")
+    ks1 = torch.empty(pc.n_heads, dtype=torch.float64, device="cuda")
+    ks2 = torch.empty(pc.n_heads, dtype=torch.float64, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tk.score(c, seg_d, t_d, s1)
+    tk.select_global(c, s1, seg_d, b_d, k1, kept1, ks1, status=status)
+    tk.score_select(c, seg_d, t_d, b_d, s2, k2, kept2, ks2, status=status)
+    total = int(pc.page_off[-1]) * 16
+    assert np.array_equal(f32_bits(s1.cpu().numpy()[:total]), f32_bits(s2.cpu().numpy()[:total]))
+    assert np.array_equal(k1.cpu().numpy()[:total], k2.cpu().numpy()[:total])
+    assert np.array_equal(kept1.cpu().numpy(), kept2.cpu().numpy())
+    assert np.array_equal(ks1.cpu().numpy().view(np.uint64), ks2.cpu().numpy().view(np.uint64))
+    assert int(status.item()) == 0
+    want_keep, want_kept = ref.select_global(ov.scores(seg_t(seg, t_seg, pc.n_heads)), seg, budgets)
+    got = heads_from_plane(k2.cpu().numpy(), pc.page_off, pc.length)
+    for h in range(pc.n_heads):
+        assert np.array_equal(got[h].astype(bool), want_keep[h]), h
+    assert np.array_equal(kept2.cpu().numpy(), want_kept)
+
+
+@pytest.mark.parametrize("name", ["tiny", "c2s", "c3s", "c5s"])
+def test_score_select_parity(name):
+    w = SMALL[name]
+    announce("score_select", name)
+    pc = synth.build_cache(w)
+    seg = w.seg_head_begin()
+    t_seg = [w.t + 1 + 5 * s for s in range(w.n_seg)]
+    _score_select_case(pc, seg, t_seg, [w.budget()] * w.n_seg)
+
+
+def test_score_select_ties_and_ragged():
+    """beta = 1 (every score 0: a budget below N fills heads in order, each
+    keeping its most recent entries), beta = 0 (-inf), and ragged heads with
+    segments ending inside 32-chunk blocks."""
+    for seed, dist in ((31, ("beta", 5.0, 1.0)), (32, ("const", 1.0)), (33, ("const", 0.0)),
+                       (34, ("const", 0.5))):
+        pc = synth.random_ragged_cache(seed, n_heads=23, d=64, dtype="bf16", max_len=5000, beta_dist=dist)
+        seg = np.array([0, 5, 17, 23], np.int32)
+        N = [int(pc.length[seg[s]:seg[s + 1]].sum()) for s in range(3)]
+        t = int(pc.pos.max()) + 1
+        for budgets in ([n // 3 for n in N], [0, 1, max(N[2] - 1, 0)], [n + 2 for n in N]):
+            announce("score_select ragged", dist, budgets)
+            _score_select_case(pc, seg, [t, t + 3, t + 9], budgets)
+
+
 # --------------------------------------------------------------------------
 # a2: selection on identical fp32 scores
 # --------------------------------------------------------------------------
@@ -928,3 +986,88 @@ def test_streaming_steps_inplace():
             assert np.array_equal(ref.gather_heads(k, po, pi, ln)[h], st["k"][h])
             assert np.array_equal(ref.gather_heads(v, po, pi, ln)[h], st["v"][h])
     assert tk.validate_cache(cur, cuda(np.array([w.ctx + w.steps + 1], np.int32))) == tk.OK
+
+
+# --------------------------------------------------------------------------
+# the streaming step captured in HIP graphs
+# --------------------------------------------------------------------------
+def test_streaming_graph_capture():
+    """Steps 3..S of the scaled streaming workload replayed from captured
+    graphs (one per step) against the same steps run eagerly:
+    kept counts, outputs, dropped mass, page tables and the final pools bit
+    for bit after every replay, with eager work and synchronisations between
+    replays; the final state against the oracle."""
+    from retention_scored_decode_amd.stream import StreamLoop
+
+    w = SMALL["c5s"].scaled(steps=24)
+    S = w.steps
+    pc = synth.build_cache(w)
+    H, G, D = pc.n_heads, w.group, w.head_dim
+    M = w.budget()
+    sc = scale_of(D)
+    steps_in = [synth.stream_step(w, s) for s in range(1, S + 1)]
+    banks = {"k": kv_dev(np.stack([x[1] for x in steps_in]), "bf16"),
+             "v": kv_dev(np.stack([x[2] for x in steps_in]), "bf16"),
+             "beta": cuda(np.stack([x[0] for x in steps_in]), np.float32),
+             "q": kv_dev(np.stack([x[3] for x in steps_in]), "bf16"),
+             "t": cuda(np.arange(w.ctx + 1, w.ctx + S + 1, dtype=np.int32).reshape(S, 1))}
+    prefill = upload(pc)
+    len0 = prefill.length.clone()
+
+    def start():
+        """step 1 (the prefill eviction) into a fresh pair of pools"""
+        pools = [tk.Cache.empty(H, dst_capacity(H, M, 1), D, torch.bfloat16) for _ in range(2)]
+        prefill.length.copy_(len0)
+        t = cuda(np.array([w.ctx + 1], np.int32))
+        tk.append(prefill, banks["k"][0], banks["v"][0], banks["beta"][0], t)
+        score = torch.empty(prefill.n_pages * 16, dtype=torch.float32, device="cuda")
+        keep = torch.empty(prefill.n_pages * 16, dtype=torch.uint8, device="cuda")
+        kept = torch.empty(H, dtype=torch.int32, device="cuda")
+        seg = cuda(np.array([0, H], np.int32))
+        tk.score(prefill, seg, t, score)
+        tk.select_global(prefill, score, seg, cuda(np.array([M], np.int64)), keep, kept)
+        tk.compact(prefill, keep, 1, M, pools[0], torch.zeros(1, dtype=torch.int64, device="cuda"), kept=kept)
+        return StreamLoop(pools, M, G, sc, banks, first=1)
+
+    def state(loop):
+        torch.cuda.synchronize()
+        c = loop.cache
+        return (loop.kept.cpu().numpy(), loop.out.cpu().numpy().view(np.uint32),
+                loop.dropped.cpu().numpy().view(np.uint32), c.page_off.cpu().numpy(), c.length.cpu().numpy())
+
+    eager = start()
+    want = []
+    for s in range(2, S + 1):
+        eager.run(1)
+        want.append(state(eager))
+    graph = start()
+    graph.run(1)                      # step 2 eagerly (the library's first-call set-up done), then capture
+    assert all(np.array_equal(a, b) for a, b in zip(state(graph), want[0]))
+    graph.capture(S - 2, chunk=1)     # one graph per step, so every step can be checked
+    noise = torch.arange(1 << 16, dtype=torch.float32, device="cuda")
+    for s in range(3, S + 1):
+        announce("graph replay step", s)
+        graph.replay(1)
+        noise.mul_(1.0001).add_(1.0)          # eager work between replays
+        got = state(graph)
+        for a, b in zip(got, want[s - 2]):
+            assert np.array_equal(a, b), s
+    assert int(graph.status.sum().item()) == 0 and int(eager.status.sum().item()) == 0
+    ge, gg = download_cache(eager.cache), download_cache(graph.cache)
+    for i in (3, 4, 5, 6):   # K, V, ln(beta), positions of every head
+        for x, y in zip(ref.gather_heads(ge[i], ge[0], ge[1], ge[2]), ref.gather_heads(gg[i], gg[0], gg[1], gg[2])):
+            assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+    # the final state against the oracle: positions and ln(beta) of every head
+    ov = OracleView(pc)
+    lnb, pos = ov.lnb, ov.pos
+    for s in range(1, S + 1):
+        t = w.ctx + s
+        lnb = [np.append(lnb[h], ref.ln_beta(steps_in[s - 1][0])[h]) for h in range(H)]
+        pos = [np.append(pos[h], np.int32(t - 1)) for h in range(H)]
+        keep, _ = ref.select_global([ref.score_f32(lnb[h], t, pos[h]) for h in range(H)], [0, H], [M])
+        lnb = [lnb[h][keep[h]] for h in range(H)]
+        pos = [pos[h][keep[h]] for h in range(H)]
+    gpos = ref.gather_heads(gg[6], gg[0], gg[1], gg[2])
+    glnb = ref.gather_heads(gg[5], gg[0], gg[1], gg[2])
+    for h in range(H):
+        assert np.array_equal(gpos[h], pos[h]) and np.array_equal(f32_bits(glnb[h]), f32_bits(lnb[h])), h
