@@ -159,10 +159,11 @@ def pmc_summary(workload, fetch_db, write_db):
     with open(out, "w") as fh:
         fh.write("# HBM traffic per dispatch, %s workload (rocprofv3 PMC)\n\n" % workload)
         fh.write("Commands (repository root, one counter per run):\n\n")
+        wl = "" if workload == "llama8b_32k" else "--workload %s " % workload
         for c, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
-            fh.write("    rocprofv3 --pmc %s -d %s -o run -- python -u bench.py --steps 2 "
-                     "--warmup 1 --cold-reps 1 --no-cpu-baseline --calib\n" % (c, os.path.dirname(db)))
-        fh.write("    python bench.py --pmc-summary %s %s\n\n" % (fetch_db, write_db))
+            fh.write("    rocprofv3 --pmc %s -d %s -o run -- python -u bench.py %s--steps 2 "
+                     "--warmup 1 --cold-reps 1 --no-cpu-baseline --calib\n" % (c, os.path.dirname(db), wl))
+        fh.write("    python bench.py %s--pmc-summary %s %s\n\n" % (wl, fetch_db, write_db))
         fh.write("Calibration: the 1 GiB device copy reads FETCH_SIZE %.0f KiB and WRITE_SIZE %.0f KiB, "
                  "so traffic = FETCH x %.3f + WRITE x %.3f (KiB -> bytes x 1024).\n\n" % (f_copy, w_copy, fr, fw))
         fh.write("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | traffic MB |\n|---|---|---|---|---|\n")
@@ -190,6 +191,18 @@ def traffic_for(workload, stage):
         return None
     k = blob.get("kernels", {}).get(kname)
     return None if k is None else int(k["traffic_bytes"])
+
+
+def calib_copy(dev):
+    """A plain 1 GiB device-to-device copy (reads 1 GiB, writes 1 GiB): the
+    reference the traffic counters are scaled by."""
+    import torch
+    src_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    src_buf.fill_(3)
+    torch.cuda.synchronize()
+    dst_buf.copy_(src_buf)
+    torch.cuda.synchronize()
 
 
 def timed_calls(call, reps):
@@ -473,12 +486,7 @@ def main():
     t_cold = float(np.median(cold))
 
     if args.calib:
-        src_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        src_buf.fill_(3)
-        torch.cuda.synchronize()
-        flush.copy_(src_buf)        # reads 1 GiB, writes 1 GiB
-        torch.cuda.synchronize()
-        del src_buf
+        calib_copy(dev)
 
     kept_total = int(kept_np.sum())
     small = nq * D * 2 + nq * D * 4 + nq * 4
@@ -905,6 +913,8 @@ def bench_mass_pipeline(args, w):
     wall = time.perf_counter() - wall0
     per = {s: [e[j].elapsed_time(e[j + 1]) * 1e-3 for e in evs] for j, s in enumerate(stages)}
     t = {s: float(np.mean(v)) for s, v in per.items()}
+    if args.calib:
+        calib_copy(dev)
     assert int(b.sum().item()) == B and int(dst.length.sum().item()) == B
     assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
     pages = int(used.item())

@@ -45,10 +45,14 @@ constexpr int CHA_F32 = 16;     // pages per work item of the fp32 kernel (one k
 constexpr int NT = 256;
 constexpr int GMAX = 16;
 constexpr int FLAT_WMAX = 8192;   // most waves of one bf16 launch (workspace bound)
-// Threads per block of the bf16 kernel: four waves, each staging two K and
-// two V pages (16 KB at D = 128) in LDS.  Measured against two- and one-wave
-// blocks (more waves per CU): those were 5% and 25% slower.
-constexpr int NTA = 256;
+// Threads per block of the bf16 kernel: eight waves, each staging two K and
+// two V pages (16 KB at D = 128) in LDS, one block per CU.  Each SIMD then
+// holds two waves of the same block (waves w and w + 4), which keep their
+// progress even by wave priority (below).  Measured against four-wave
+// blocks (two per CU), two- and one-wave blocks: those were 1-2%, 5% and 25%
+// slower.
+constexpr int NTA = 512;
+constexpr int SIMD_PAIR = 4;   // waves w and w ^ SIMD_PAIR share a SIMD
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -416,7 +420,14 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
   const int64_t P = pg(H);
   const int W = a.waves;
   const int wave = blockIdx.x * (NTA / WAVE) + wu;
+  // pages done by each wave of the block: the wave behind its SIMD partner
+  // takes the higher issue priority, so that the two finish together
+  // instead of the older one first (the younger, then alone on its SIMD,
+  // keeping half as many pages in flight)
+  __shared__ int prog[NTA / WAVE];
+  if (lane == 0) prog[wu] = 0;
   int p = (int)flat_begin(wave, W, P);
+  const int pbeg = p;
   const int pend = (int)flat_begin(wave + 1, W, P);
   if (p >= pend) return;   // per-wave exit: no block barriers below
 
@@ -670,6 +681,13 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
         for (int n = 0; n < NV; ++n) vop[n] = lds_read_tr_b64(vl + voff[n]);
       }
       lds_wait_all(kop, vop);   // the tile may be overwritten once these reads are done
+      {
+        const int done = page0 - pbeg + i;
+        if (lane == 0) prog[wu] = done;
+        const int other = __builtin_amdgcn_readfirstlane(prog[wu ^ SIMD_PAIR]);
+        if (done <= other) __builtin_amdgcn_s_setprio(2);
+        else __builtin_amdgcn_s_setprio(0);
+      }
       // page i's gate words, taken before page i + 2's loads reuse their registers
       const u32x4 glnb = g_lnb[buf & (GATED ? 1 : 0)], gpos = g_pos[buf & (GATED ? 1 : 0)];
       if (i + 2 < cnt) dma(B, i + 2, id_n, kwd_n);
