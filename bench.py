@@ -69,9 +69,15 @@ TRACE_RUN = {
                     "A run is 1 + 3 passes of the pipeline: attention mass (logits kernel, merge, mass "
                     "kernel), per-head top-1024 with kept sums, allocation, per-head top-b_h, compaction, "
                     "reference-mode decode."),
-    "stream_gqa7": ("--workload stream_gqa7 --stream-steps 512",
-                    "A run is 4 + 512 generated steps evicting out of place, then 4 + 512 evicting in place; "
-                    "each step appends, scores, selects, attends (mask mode) and evicts."),
+    "stream_gqa7": ("--workload stream_gqa7 --stream-steps 512 --no-cpu-baseline",
+                    "A run is 4 + 512 generated steps for each variant: evicting out of place, in place "
+                    "(stable shift), in place by tail fill (scores formed in the selection), and out of place "
+                    "through the step loop launched eagerly and replayed from HIP graphs; each step appends, "
+                    "scores, selects, attends (mask mode) and evicts."),
+    "batched16_16k": ("--workload batched16_16k --steps 3 --warmup 1 --cold-reps 1 --no-cpu-baseline",
+                      "A run is 1 + 3 pipeline steps of the 16-sequence workload (score, select with 16 "
+                      "segments, mask-mode attention, compaction, plain decode) plus 1 flushed decode and the "
+                      "extras (error output, gated decode, incremental eviction, recency floor)."),
 }
 
 
@@ -1037,6 +1043,29 @@ def bench_streaming(args, w):
         torch.cuda.synchronize()
         return cur, e0.elapsed_time(e1) * 1e-3, ev[0].elapsed_time(ev[1]) * 1e-3
 
+    ws_tf = tk.workspace(tk.OP_EVICT_TAILFILL, home)
+
+    def run_tailfill(n):
+        """steps 1..n; step 1 lays the evicted prefill out in the home pages
+        as run_inplace does, later steps score and select in one call and
+        evict by tail fill (only the kept entries that fill holes move)"""
+        step_one(home, RES)
+        home_off, home_ids = home.page_off.clone(), home.page_ids.clone()
+        wsel, watt, _ = ws["home"]
+        view = home
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for s in range(2, n + 1):
+            i = s - 1
+            tk.append(view, k_all[i], v_all[i], beta_all[i], t_all[i])
+            tk.score_select(view, seg, t_all[i], bud, score, keep, kept, ws=wsel)
+            tk.decode_attn(view, q_all[i], G, scale, out, dropped, keep=keep, ws=watt)
+            nt = tables[s % 2]
+            view = tk.evict_tailfill(view, keep, 1, home_off, home_ids, nt[0], nt[1], kept=kept, ws=ws_tf)
+        ev[1].record()
+        torch.cuda.synchronize()
+        return view, ev[0].elapsed_time(ev[1]) * 1e-3
+
     def run_inplace(n):
         """steps 1..n; step 1 lays the evicted prefill out with RES spare
         slots per head (the home pages, room for one entry per step), later
@@ -1079,6 +1108,9 @@ def bench_streaming(args, w):
 
     run_oop(min(S, 4))                       # first launches load the kernels
     run_inplace(min(S, 4))
+    run_tailfill(min(S, 4))
+    view_tf, t_tf = run_tailfill(S)
+    assert int(view_tf.length.sum().item()) == M
     run_loop(min(S, 4), False)
     run_loop(min(S, 4), True)
     loop_e, t_staged = run_loop(S, False)
@@ -1102,6 +1134,11 @@ def bench_streaming(args, w):
     step_algo = {"append": H * (2 * D * 2 + 8), "score": 12 * U, "select": 4 * U,
                  "attend_mask": 256 * U + 256 * M + small, "compact": 1040 * M + 4 * pages}
     per_step = sum(step_algo.values())
+    # tail fill: the same append, score, select and attention bytes, then at
+    # most H rows moved (520 B read + 520 B written each: a step drops H
+    # entries) and the keep bytes the eviction scans
+    tf_step = (step_algo["append"] + step_algo["score"] + step_algo["select"] + step_algo["attend_mask"]
+               + 1040 * H + U)
     res = {"metric": "streaming eviction steps/s (append, score, global select, mask-mode attention, evict), "
                      "GQA-7 28x4 heads, 64K prefill",
            "value": round(S_t / t_oop, 1), "unit": "steps/s", "n_gpus": 1, "steps": S_t, "warmup": 4,
@@ -1116,6 +1153,13 @@ def bench_streaming(args, w):
                             "step_algo_bytes": step_algo},
            "in_place": {"steps_per_s": round(S_t / t_inp, 1), "us_per_step": round(t_inp / S_t * 1e6, 2),
                         "home_spare_slots_per_head": RES},
+           "tail_fill": {"steps_per_s": round(S_t / t_tf, 1), "us_per_step": round(t_tf / S_t * 1e6, 2),
+                         "GBps": round(tf_step * S_t / t_tf / 1e9, 1),
+                         "frac_hbm": round(tf_step * S_t / t_tf / 1e9 / HBM_PEAK_GBS, 4),
+                         "algo_bytes_per_step": tf_step,
+                         "what": "in place in the home pages, scores formed inside the selection, eviction by "
+                                 "tail fill: only the kept entries that fill holes below the new length move "
+                                 "(at most the step's %d drops)" % H},
            "fused_score_select": {"steps_per_s": round(S_t / t_staged, 1),
                                   "us_per_step": round(t_staged / S_t * 1e6, 2),
                                   "what": "out of place, trimkv_score_select in place of score + select"},

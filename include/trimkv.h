@@ -27,7 +27,8 @@
  *  - Page size is 16 entries.  Logical page c (0-based) of head h is CSR
  *    entry page_off[h] + c; it lives in physical page page_ids[page_off[h]+c].
  *    Entry i of head h is slot i % 16 of its logical page i / 16; entries
- *    i < len[h] are valid, and their positions ascend with i.
+ *    i < len[h] are valid, and their positions are distinct; they ascend
+ *    with i except after trimkv_evict_tailfill.
  *  - Pools: k, v [n_pages][16][head_dim] (bf16 or fp32); meta
  *    [n_pages][2][16] 32-bit words: for page p, meta[p][0][j] holds ln(beta)
  *    (fp32 bits) of slot j and meta[p][1][j] its token position (int32).  A
@@ -89,7 +90,8 @@ enum {
   TRIMKV_OP_ATTN_MASS = 4,
   TRIMKV_OP_VALIDATE = 5,
   TRIMKV_OP_DECODE_ERR = 6,
-  TRIMKV_OP_COMPACT_INPLACE = 7
+  TRIMKV_OP_COMPACT_INPLACE = 7,
+  TRIMKV_OP_EVICT_TAILFILL = 8
 };
 
 /*
@@ -125,12 +127,13 @@ int trimkv_score(const trimkv_cache_t* cache, int32_t n_seg, const int32_t* seg_
  * layers and heads, keep the top M_global); TRIM-KV page, section 2 (evict the
  * lowest current scores once the budget is exceeded).
  * Total order: score descending (-0.0 == +0.0, -inf below every finite
- * score, NaN below -inf), then flat head ascending, then slot descending:
- * among equal scores of one head the more recent entry ranks first, so with
- * beta = 1 everywhere (every score 0) each head keeps its most recent
- * entries.  Segment s keeps exactly min(max(budget[s], 0), N_s) entries,
+ * score, NaN below -inf), then flat head ascending, then position
+ * descending (read from meta): among equal scores of one head the more
+ * recent entry ranks first, so with beta = 1 everywhere (every score 0) each
+ * head keeps its most recent entries.  Segment s keeps exactly min(max(budget[s], 0), N_s) entries,
  * N_s = valid entries of its heads.
  *   score:   device fp32 CSR plane (any fp32 key: retention scores or masses)
+ *   cache->meta: positions rank tied entries (required)
  *   budget:  device int64 [n_seg]
  *   keep:    device uint8 CSR plane, out: 1 kept, 0 evicted (valid slots),
  *            0 in padding slots
@@ -231,6 +234,29 @@ int trimkv_compact(const trimkv_cache_t* src, const uint8_t* keep, const int32_t
 int trimkv_compact_inplace(trimkv_cache_t* cache, const uint8_t* keep, const int32_t* kept, int32_t reserve,
                            const int32_t* home_off, const int32_t* home_ids, int32_t* new_page_off,
                            int32_t* new_page_ids, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * trimkv_evict_tailfill -- eviction in place that moves only the entries it
+ * must.  DBTrimKV page, Method 4 (paged per-head storage) and ContourKV
+ * page, section 2 (eviction must shrink storage), for streaming decode,
+ * where each step drops a few entries per head.
+ * Per head with kept_h kept entries: the dropped entries among its first
+ * kept_h slots (holes) take, one each, the kept entries from slot kept_h on,
+ * both counted in slot order; every other kept entry stays in its slot.  At
+ * most the head's drops move.  The page table and len are then as
+ * trimkv_compact_inplace writes them.  Afterwards the head's slots are no
+ * longer in position order: selection ranks ties by position and attention
+ * is order-free, so both are unaffected; trimkv_mark_recent and
+ * trimkv_validate_cache's ascending-position check assume position order
+ * and do not apply to such a cache.
+ *   arguments: as trimkv_compact_inplace
+ *   ws: trimkv_workspace_size(TRIMKV_OP_EVICT_TAILFILL, cache, 0, 0) bytes
+ *       (a 4-byte slot per CSR slot for the holes)
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE.
+ */
+int trimkv_evict_tailfill(trimkv_cache_t* cache, const uint8_t* keep, const int32_t* kept, int32_t reserve,
+                          const int32_t* home_off, const int32_t* home_ids, int32_t* new_page_off,
+                          int32_t* new_page_ids, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * trimkv_decode_attn -- renormalised GQA decode attention with dropped mass.

@@ -108,3 +108,20 @@ def largest_remainder_l2(x, total):
 
     rec(0, total, [])
     return arg
+
+
+def tailfill_in_place(pool, slots_of_head, keep):
+    """Tail-filled eviction of one head, one entry at a time: walking the
+    slots from the front, each dropped slot below the new length takes the
+    next kept entry found walking from the new length on.  pool is a list of
+    per-physical-slot values, modified in place; returns the new length."""
+    n_keep = sum(1 for k in keep if k)
+    src = n_keep
+    for i in range(n_keep):
+        if keep[i]:
+            continue
+        while not keep[src]:
+            src += 1
+        pool[slots_of_head[i]] = pool[slots_of_head[src]]
+        src += 1
+    return n_keep

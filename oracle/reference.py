@@ -125,7 +125,7 @@ def score_f32(lnb, t, pos) -> np.ndarray:
 # --------------------------------------------------------------------------
 # a2: one global top-M per segment, ties by (head, position)
 # --------------------------------------------------------------------------
-def select_global(scores, seg_head_begin, budgets):
+def select_global(scores, seg_head_begin, budgets, positions=None):
     """Keep flags per head (slot order) and kept count per head.
 
     DBTrimKV Method 3: rank every cached entry of all layers and heads by its
@@ -136,6 +136,9 @@ def select_global(scores, seg_head_begin, budgets):
     descending: among equal scores of one head the more recent entry ranks
     first, so that with beta = 1 everywhere (no decay, every score 0) a head
     keeps its most recent entries.  A segment keeps min(M, N) entries.
+    positions: per-head token positions in slot order, for caches whose slots
+    are not in position order (tail-filled eviction); by default the slot
+    index stands for the position.
     """
     keep = [np.zeros(len(s), dtype=bool) for s in scores]
     for s in range(len(seg_head_begin) - 1):
@@ -146,7 +149,8 @@ def select_global(scores, seg_head_begin, budgets):
         sc = np.where(sc == 0.0, 0.0, sc)            # -0.0 -> +0.0
         head = np.concatenate([np.full(len(scores[h]), h, np.int64) for h in hs])
         idx = np.concatenate([np.arange(len(scores[h]), dtype=np.int64) for h in hs])
-        order = np.lexsort((-idx, head, -sc))
+        pos = idx if positions is None else np.concatenate([np.asarray(positions[h], np.int64) for h in hs])
+        order = np.lexsort((-pos, head, -sc))
         m = max(0, min(int(budgets[s]), len(sc)))
         chosen = order[:m]
         for h in hs:
@@ -237,6 +241,32 @@ def compact_inplace_layout(kept, reserve, home_off, home_ids):
     page_ids = np.concatenate([home_ids[home_off[h]:home_off[h] + pages[h]] for h in range(len(kept))] +
                               [np.zeros(0, np.int64)])
     return page_off, page_ids, kept.copy()
+
+
+def evict_tailfill_order(keep, reserve=0, home_off=None, home_ids=None):
+    """Eviction in place that moves only what it must (DBTrimKV Method 4:
+    per-head paged storage; ContourKV section 2: storage shrinks), for the
+    streaming loop.  Per head with kept count k: the dropped entries among
+    its first k slots (holes) take, one each, the kept entries from slot k on
+    (movers), both in slot order; every other kept entry stays in its slot.
+    Slot order then no longer follows position order.
+
+    Returns, per head, the old slot index held by each new slot 0..k-1; with
+    home_off / home_ids also the new page table (as
+    compact_inplace_layout)."""
+    order = []
+    for k in keep:
+        k = np.asarray(k, bool)
+        n_keep = int(k.sum())
+        o = np.arange(n_keep, dtype=np.int64)
+        holes = np.flatnonzero(~k[:n_keep])
+        movers = n_keep + np.flatnonzero(k[n_keep:])
+        o[holes] = movers
+        order.append(o)
+    if home_off is None:
+        return order
+    kept = [len(o) for o in order]
+    return order, compact_inplace_layout(kept, reserve, home_off, home_ids)
 
 
 # --------------------------------------------------------------------------

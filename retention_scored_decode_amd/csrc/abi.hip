@@ -128,6 +128,7 @@ size_t trimkv_workspace_size(int op, const trimkv_cache_t* c, int32_t n_seg, int
     case TRIMKV_OP_VALIDATE: return 256;
     case TRIMKV_OP_DECODE_ERR: return (group >= 1 && group <= 16) ? err_ws_layout(c, group).total : 0;
     case TRIMKV_OP_COMPACT_INPLACE: return (size_t)c->n_heads * 4 + 256;
+    case TRIMKV_OP_EVICT_TAILFILL: return tailfill_ws_layout(c).total;
     default: return 0;
   }
 }
@@ -151,8 +152,9 @@ int trimkv_select_global(const trimkv_cache_t* c, const float* score, int32_t n_
                          void* ws, size_t ws_bytes, void* stream) {
   int rc;
   if (!cache_shape_ok(c, &rc)) return rc;
+  // meta: positions rank ties within a head
   if (n_seg < 1 || n_seg > c->n_heads || !score || !seg || !budget || !keep || !kept || !table_ok(c) ||
-      ((uintptr_t)keep & 15))
+      (c->n_pages > 0 && !c->meta) || ((uintptr_t)keep & 15))
     return TRIMKV_EINVAL;
   if ((rc = ws_check(ws, ws_bytes, select_ws_layout(c, n_seg).total))) return rc;
   return launch_select(c, score, n_seg, seg, budget, keep, kept, keptsum, status, ws, S(stream));
@@ -212,6 +214,25 @@ int trimkv_compact_inplace(trimkv_cache_t* c, const uint8_t* keep, const int32_t
   if (c->n_heads == 0) return TRIMKV_OK;
   return launch_compact_inplace(c, keep, kept, reserve, home_off, home_ids, new_page_off, new_page_ids, ws,
                                 S(stream));
+}
+
+int trimkv_evict_tailfill(trimkv_cache_t* c, const uint8_t* keep, const int32_t* kept, int32_t reserve,
+                          const int32_t* home_off, const int32_t* home_ids, int32_t* new_page_off,
+                          int32_t* new_page_ids, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if (!cache_shape_ok(c, &rc)) return rc;
+  if (!keep || reserve < 0 || !home_off || !home_ids || !new_page_off || !new_page_ids || !table_ok(c) ||
+      !pools_ok(c) || ((uintptr_t)keep & 15))
+    return TRIMKV_EINVAL;
+  // the new table is written while the current one is still read
+  if (new_page_off == c->page_off || new_page_ids == c->page_ids || new_page_off == home_off ||
+      new_page_ids == home_ids)
+    return TRIMKV_EINVAL;
+  if (c->n_pages * PAGE > (int64_t)UINT32_MAX) return TRIMKV_EUNSUPPORTED;
+  if ((rc = ws_check(ws, ws_bytes, tailfill_ws_layout(c).total))) return rc;
+  if (c->n_heads == 0) return TRIMKV_OK;
+  return launch_evict_tailfill(c, keep, kept, reserve, home_off, home_ids, new_page_off, new_page_ids, ws,
+                               S(stream));
 }
 
 int trimkv_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float* lse_ref, const void* q,

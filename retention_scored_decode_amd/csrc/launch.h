@@ -34,6 +34,7 @@ inline int64_t max_chunks(const trimkv_cache_t* c, int cp) { return c->n_pages /
 WsLayout select_ws_layout(const trimkv_cache_t* c, int n_seg);
 WsLayout err_ws_layout(const trimkv_cache_t* c, int group);
 WsLayout compact_ws_layout(const trimkv_cache_t* c);
+WsLayout tailfill_ws_layout(const trimkv_cache_t* c);
 WsLayout attn_ws_layout(const trimkv_cache_t* c, int group, int64_t slots = -1);
 WsLayout mass_ws_layout(const trimkv_cache_t* c, int group);
 
@@ -53,6 +54,9 @@ int launch_compact(const trimkv_cache_t* src, const uint8_t* keep, const int32_t
 int launch_compact_inplace(trimkv_cache_t* c, const uint8_t* keep, const int32_t* kept, int reserve,
                            const int32_t* home_off, const int32_t* home_ids, int32_t* new_off, int32_t* new_ids,
                            void* ws, hipStream_t st);
+int launch_evict_tailfill(trimkv_cache_t* c, const uint8_t* keep, const int32_t* kept, int reserve,
+                          const int32_t* home_off, const int32_t* home_ids, int32_t* new_off, int32_t* new_ids,
+                          void* ws, hipStream_t st);
 int launch_decode_attn_gated(const trimkv_cache_t* c, int n_seg, const int32_t* seg, const int32_t* t,
                              const uint8_t* keep, const void* q, int group, float scale, float* out, float* dropped,
                              float* lse_out, void* ws, hipStream_t st);

@@ -1,5 +1,5 @@
 // Exact global top-M per segment over fp32 keys, ties by head ascending, then
-// slot descending (the more recent entry of a head first).
+// position descending (the more recent entry of a head first).
 //
 // DBTrimKV page, Method 3: one global budget M_global; every cached entry of
 // every layer and head is ranked by predicted utility and the top M_global
@@ -13,16 +13,14 @@
 //      device atomics into a per-segment histogram; every block of the next
 //      kernel scans the finished histogram of its segment to narrow the
 //      prefix (no inter-block waits, no cache flushes inside a kernel);
-//   3. one pass over 1024-slot chunks: each chunk keeps key > K*; when the
-//      ties (key == K*) straddle the budget, the segment's chunks are taken
-//      in tie-rank order (heads ascending, within a head chunks descending),
-//      each counts its ties and obtains the ties of every chunk ranked
-//      before it by a decoupled look-back (one wave reads 64 predecessor
-//      words at a time; value and flag share one 64-bit word), and keeps the
-//      ties whose rank in the segment is below `need`, slots descending.
-// CSR order within a segment is head order and, within a head, slot
-// (= position) order, so this realises "score desc, head asc, position
-// desc".
+//   3. one pass over 1024-slot chunks: each chunk keeps key > K*.  When the
+//      ties (key == K*) straddle the budget, the segment's heads are taken
+//      in order by a per-segment ticket; each counts its ties, obtains the
+//      ties of every earlier head by a decoupled look-back (one wave reads 64
+//      predecessor words at a time; value and flag share one 64-bit word),
+//      and keeps its q most recent ties, q = clamp(need - earlier ties, 0,
+//      ties), found by a radix selection over their positions (read from the
+//      cache's metadata, so slot order does not matter).
 #include <algorithm>
 #include <type_traits>
 
@@ -367,6 +365,18 @@ __device__ __forceinline__ double block_sum_f64(double v, double* tmpd) {
   return r;
 }
 
+// The block's sum in every thread.
+__device__ __forceinline__ int block_sum_all_i32(int v, int* red) {
+  for (int d = WAVE / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, WAVE);
+  if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = v;
+  lds_barrier();
+  int r = 0;
+#pragma unroll
+  for (int i = 0; i < NT / WAVE; ++i) r += red[i];
+  lds_barrier();
+  return r;
+}
+
 __device__ __forceinline__ int block_sum_i32(int v, int* red) {
   for (int d = WAVE / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, WAVE);
   if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = v;
@@ -430,7 +440,8 @@ __device__ __forceinline__ uint32_t keep_word(uint32_t km) {
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __restrict__ score, SelWs w,
                                                    uint8_t* __restrict__ keep, int32_t* __restrict__ kept,
-                                                   int want_sum) {
+                                                   int want_sum, const int32_t* __restrict__ page_ids,
+                                                   const uint32_t* __restrict__ meta) {
   __shared__ int64_t tmp[NT / WAVE + 1];
   __shared__ double tmpd[NT / WAVE];
   __shared__ double tmps[RND][NT / WAVE];   // per-round wave sums of kept scores
@@ -438,6 +449,9 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
   __shared__ int red[NT / WAVE];
   __shared__ int sh_c;
   __shared__ int64_t sh_excl;
+  __shared__ uint32_t lhist[256];   // ranked ties: histogram of position bytes
+  __shared__ uint32_t sh_pre;
+  __shared__ int64_t sh_rem;
   __shared__ int4 sm[CPB];
   const int c0 = blockIdx.x * CPB;
   int4 mv = make_int4(0, 0, 0, 0);
@@ -573,40 +587,74 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
         lds_barrier();   // tmps is written again by the block's next segment run
       }
     } else {
+      // Ties straddle the budget: they rank by head ascending, then position
+      // descending.  Heads are taken in the order of a per-segment ticket,
+      // one head per ticket and block: the block counts the head's keys above
+      // K* and its ties, obtains the ties of every earlier head by a
+      // decoupled look-back over the tickets, keeps the head's q most recent
+      // ties (a radix selection on their positions when 0 < q < ties), then
+      // writes the head's keep bytes.  A ticket is taken only when its head
+      // is processed, so every head a block waits for belongs to a block
+      // that is already running.  Slot order never matters here, so caches
+      // whose slots are not in position order rank the same.
+      // Control flow of this loop stays wave-uniform at both ends (the ticket
+      // is taken and the head's count stored by the whole of wave 0, never
+      // under a one-thread branch): with one-thread branches at both ends
+      // the compiler threaded them into a nested loop whose inner back edge,
+      // taken by every lane but thread 0, re-read the previous ticket, so
+      // those lanes never left the loop.
       const int cb = st.chunk_begin;
-      const bool act = threadIdx.x < GT;
-      for (int pos = i; pos < e; ++pos) {
-        // process the segment's chunk of the next ticket: ticket k is the
-        // k-th chunk in tie-rank order, heads ascending and, within a head,
-        // chunks descending (the more recent entries rank first)
-        if (threadIdx.x == 0) sh_c = cb + (int)atomicAdd(w.ticket + 2 + sg, 1u);
-        lds_barrier();
-        const int k = sh_c;
-        const int hk = w.meta[k].x;   // the chunks of head hk occupy the same index range in both orders
-        const int c = w.chunk_off[hk] + w.chunk_off[hk + 1] - 1 - k;
-        const int4 m = w.meta[c];
-        const int nv = m.w & 0xFFFF;
-        float a[4] = {0.f, 0.f, 0.f, 0.f};
-        if (act && i0 < nv) {
-          const float4 sv = *reinterpret_cast<const float4*>(score + (int64_t)m.z * PAGE + i0);
-          a[0] = sv.x; a[1] = sv.y; a[2] = sv.z; a[3] = sv.w;
+      const int h_first = __builtin_amdgcn_readfirstlane(w.meta[cb].x);
+      const int n_th = __builtin_amdgcn_readfirstlane(w.meta[st.chunk_end - 1].x) - h_first + 1;
+      const int wave0 = __builtin_amdgcn_readfirstlane(wid) == 0;
+      const float f_gt = key_floor((uint64_t)st.prefix + 1), f_eq = key_floor(st.prefix);
+      const bool nan_tie = st.prefix == 0u;   // K* is the key of NaN
+      auto tie_of = [&](float x, bool& gt, bool& eq) {
+        if (nan_tie) {
+          gt = x == x;
+          eq = !gt;
+        } else {
+          gt = x >= f_gt;
+          eq = x == f_eq;
         }
-        uint32_t gtm = 0, eqm = 0;
-        if (act) classify(st, a, i0, nv, gtm, eqm);
-        int64_t eq_total;
-        const int64_t before = block_exclusive_scan<NT>((int64_t)__popc(eqm), tmp, &eq_total);
-        if (threadIdx.x < WAVE) {
+      };
+      while (true) {
+        if (wave0) {
+          // lane 0 adds 1, the others 0: lane 0's old value is the ticket
+          const uint32_t v = atomicAdd(w.ticket + 2 + sg, lane == 0 ? 1u : 0u);
+          sh_c = __builtin_amdgcn_readfirstlane((int)v);
+        }
+        lds_barrier();
+        const int t = __builtin_amdgcn_readfirstlane(sh_c);
+        lds_barrier();   // every thread has read sh_c
+        if (t >= n_th) break;
+        const int h = h_first + t;
+        const int ch0 = w.chunk_off[h], ch1 = w.chunk_off[h + 1];
+        // 1. ties of the head (one slot per thread per chunk)
+        int n_eq = 0;
+        for (int c = ch0; c < ch1; ++c) {
+          const int4 m = w.meta[c];
+          const bool valid = (int)threadIdx.x < (m.w & 0xFFFF);
+          if (valid) {
+            bool gt, eq;
+            tie_of(score[(int64_t)m.z * PAGE + threadIdx.x], gt, eq);
+            n_eq += eq;
+          }
+        }
+        const int64_t eq_h = __builtin_amdgcn_readfirstlane(block_sum_all_i32(n_eq, red));   // < 2^31 (one head)
+        // 2. ties of the earlier heads of the segment (look-back over tickets)
+        if (wave0) {
           int64_t excl = 0;
-          if (k != cb) {
+          if (t != 0) {
             if (lane == 0)
-              __hip_atomic_store(w.look + k, LB_AGG | (uint64_t)eq_total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            int base = k - 1;   // window: tickets base, base-1, ..., base-63
+              __hip_atomic_store(w.look + cb + t, LB_AGG | (uint64_t)eq_h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            int base = t - 1;   // window: tickets base, base-1, ..., base-63
             uint32_t spins = 0;
             while (true) {
               const int jj = base - lane;
-              // before the segment's first chunk: a zero prefix
-              const uint64_t v = jj >= cb ? __hip_atomic_load(w.look + jj, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                          : LB_PREFIX;
+              // before the segment's first ticket: a zero prefix
+              const uint64_t v = jj >= 0 ? __hip_atomic_load(w.look + cb + jj, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                         : LB_PREFIX;
               const uint64_t zm = __ballot(v == 0ull);
               const uint64_t pm = __ballot((v & ~LB_VAL) == LB_PREFIX);
               const int first = pm ? __ffsll((long long)pm) - 1 : WAVE;   // nearest prefix in the window
@@ -627,35 +675,100 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
             }
           }
           if (lane == 0) {
-            __hip_atomic_store(w.look + k, LB_PREFIX | (uint64_t)(excl + eq_total), __ATOMIC_RELAXED,
+            __hip_atomic_store(w.look + cb + t, LB_PREFIX | (uint64_t)(excl + eq_h), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
             sh_excl = excl;
           }
         }
         lds_barrier();
-        // rank of this thread's last tie: ties of earlier tickets, then the
-        // chunk's ties in later slots; within the thread, slots descending
-        int64_t rank = sh_excl + (eq_total - before - __popc(eqm));
-        uint32_t km = gtm;
+        // ties of this head kept (0 .. eq_h)
+        const int64_t q = __builtin_amdgcn_readfirstlane((int)min(max(st.remaining - sh_excl, (int64_t)0), eq_h));
+        lds_barrier();
+        // 3. q < ties: the q-th largest position among the head's ties
+        //    (positions are distinct within a head), by four 8-bit passes
+        uint32_t pstar = 0u;
+        if (q > 0 && q < eq_h) {
+          int64_t rem = q;
+          for (int pass = 0; pass < 4; ++pass) {
+            const int sh = 24 - 8 * pass;
+            if (threadIdx.x < 256) lhist[threadIdx.x] = 0u;
+            lds_barrier();
+            for (int c = ch0; c < ch1; ++c) {
+              const int4 m = w.meta[c];
+              if ((int)threadIdx.x < (m.w & 0xFFFF)) {
+                bool gt, eq;
+                tie_of(score[(int64_t)m.z * PAGE + threadIdx.x], gt, eq);
+                if (eq) {
+                  const int64_t pid = page_ids[m.z + (int)threadIdx.x / PAGE];
+                  const uint32_t pos = meta[pid * (2 * PAGE) + PAGE + threadIdx.x % PAGE];
+                  if (pass == 0 || (pos >> (sh + 8)) == pstar) atomicAdd(&lhist[(pos >> sh) & 255u], 1u);
+                }
+              }
+            }
+            lds_barrier();
+            if (wave0) {
+              // bins 4*lane .. 4*lane+3; counts of the bins above, from the top
+              uint32_t cb4[4];
+              int64_t own = 0;
 #pragma unroll
-        for (int q = 3; q >= 0; --q) {
-          if (eqm & (1u << q)) {
-            if (rank < st.remaining) km |= 1u << q;
-            ++rank;
+              for (int u = 0; u < 4; ++u) {
+                cb4[u] = lhist[4 * lane + u];
+                own += cb4[u];
+              }
+              int64_t above = own;   // inclusive suffix sum over lanes >= lane
+              for (int d = 1; d < WAVE; d <<= 1) {
+                const int64_t o = __shfl_down(above, d, WAVE);
+                if (lane + d < WAVE) above += o;
+              }
+              above -= own;          // keys in bins of higher lanes
+              if (above < rem && rem <= above + own) {
+                int64_t cum = above;
+                for (int u = 3; u >= 0; --u) {
+                  if (cum + cb4[u] >= rem) {
+                    sh_pre = (pstar << 8) | (uint32_t)(4 * lane + u);
+                    sh_rem = rem - cum;
+                    break;
+                  }
+                  cum += cb4[u];
+                }
+              }
+            }
+            lds_barrier();
+            pstar = sh_pre;
+            rem = sh_rem;
+            lds_barrier();
           }
         }
-        if (act && i0 < (m.w >> 16) * PAGE)
-          *reinterpret_cast<uint32_t*>(keep + (int64_t)m.z * PAGE + i0) = keep_word(km);
-        const int n = block_sum_i32(__popc(km), red);
-        if (threadIdx.x == 0 && n) atomicAdd(kept + m.x, n);
-        if (want_sum) {
-          double sum = 0.0;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (km & (1u << q)) sum += (double)a[q];
-          const double bs = block_sum_f64(sum, tmpd);
-          if (threadIdx.x == 0) w.part[c] = bs;
+        // 4. keep bytes of the head, kept count, kept-score sums per chunk
+        int nk = 0;
+        for (int c = ch0; c < ch1; ++c) {
+          const int4 m = w.meta[c];
+          const bool valid = (int)threadIdx.x < (m.w & 0xFFFF);
+          float x = 0.f;
+          bool k1 = false;
+          if (valid) {
+            x = score[(int64_t)m.z * PAGE + threadIdx.x];
+            bool gt, eq;
+            tie_of(x, gt, eq);
+            k1 = gt;
+            if (eq && q > 0) {
+              if (q == eq_h) {
+                k1 = true;
+              } else {
+                const int64_t pid = page_ids[m.z + (int)threadIdx.x / PAGE];
+                k1 = meta[pid * (2 * PAGE) + PAGE + threadIdx.x % PAGE] >= pstar;
+              }
+            }
+          }
+          if ((int)threadIdx.x < (m.w >> 16) * PAGE) keep[(int64_t)m.z * PAGE + threadIdx.x] = k1 ? 1 : 0;
+          nk += k1;
+          if (want_sum) {
+            const double bs = block_sum_f64(k1 ? (double)x : 0.0, tmpd);
+            if (threadIdx.x == 0) w.part[c] = bs;
+          }
         }
+        nk = block_sum_all_i32(nk, red);
+        if (wave0) kept[h] = nk;   // one value, stored by the whole wave
       }
     }
     i = e;
@@ -734,7 +847,7 @@ int select_kernels(const trimkv_cache_t* c, const float* score, int n_seg, const
     hipLaunchKernelGGL((k_sel_hist<2, CPB>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);
   }
   hipLaunchKernelGGL(k_sel_decide, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, keep, kept,
-                     keptsum != nullptr);
+                     keptsum != nullptr, c->page_ids, c->meta);
   prof_end(st);
   if (keptsum)
     hipLaunchKernelGGL(k_sel_headsum, dim3((unsigned)((c->n_heads + 255) / 256)), dim3(256), 0, st, c->n_heads, w,

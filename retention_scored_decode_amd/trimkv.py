@@ -18,11 +18,12 @@ LIB_PATH = os.path.join(_HERE, "libtrimkv.so")
 PAGE = 16
 F32, BF16 = 0, 1
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ECAPACITY, EHIP, EINVARIANT = 0, -1, -2, -3, -4, -5, -6
-OP_SCORE, OP_SELECT, OP_COMPACT, OP_DECODE_ATTN, OP_ATTN_MASS, OP_VALIDATE, OP_DECODE_ERR, OP_COMPACT_INPLACE = range(8)
+(OP_SCORE, OP_SELECT, OP_COMPACT, OP_DECODE_ATTN, OP_ATTN_MASS, OP_VALIDATE, OP_DECODE_ERR, OP_COMPACT_INPLACE,
+ OP_EVICT_TAILFILL) = range(9)
 
 EXPORTS = ["trimkv_log_beta", "trimkv_score", "trimkv_select_global", "trimkv_compact",
            "trimkv_decode_attn", "trimkv_decode_attn_gated", "trimkv_decode_attn_err", "trimkv_attn_mass",
-           "trimkv_decode_attn_noalloc", "trimkv_score_select",
+           "trimkv_decode_attn_noalloc", "trimkv_score_select", "trimkv_evict_tailfill",
            "trimkv_allocate", "trimkv_compact_inplace",
            "trimkv_allocate_floor", "trimkv_mark_recent", "trimkv_append",
            "trimkv_workspace_size", "trimkv_validate_cache", "trimkv_strerror", "trimkv_profile_next"]
@@ -60,6 +61,7 @@ def lib():
             "trimkv_compact": [cp, vp, vp, i32, i64, cp, vp, vp, sz, vp],
             "trimkv_score_select": [cp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_compact_inplace": [cp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp],
+            "trimkv_evict_tailfill": [cp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_decode_attn": [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp],
             "trimkv_decode_attn_noalloc": [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp],
             "trimkv_decode_attn_err": [cp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp],
@@ -229,6 +231,19 @@ def compact_inplace(cache: Cache, keep: torch.Tensor, reserve: int, home_off: to
     _check(lib().trimkv_compact_inplace(ctypes.byref(cache.struct()), _p(keep), _p(kept), int(reserve),
                                         _p(home_off), _p(home_ids), _p(new_page_off), _p(new_page_ids),
                                         _p(ws), ws.numel(), _stream(stream)), "trimkv_compact_inplace")
+    return Cache(cache.k, cache.v, cache.meta, new_page_off, new_page_ids, cache.length)
+
+
+def evict_tailfill(cache: Cache, keep: torch.Tensor, reserve: int, home_off: torch.Tensor, home_ids: torch.Tensor,
+                   new_page_off: torch.Tensor, new_page_ids: torch.Tensor, kept: Optional[torch.Tensor] = None,
+                   ws: Optional[torch.Tensor] = None, stream=None) -> Cache:
+    """Evict in place, moving only the kept entries that fill holes; returns
+    the new view (same pools and length tensor, the new page table)."""
+    if ws is None:
+        ws = workspace(OP_EVICT_TAILFILL, cache)
+    _check(lib().trimkv_evict_tailfill(ctypes.byref(cache.struct()), _p(keep), _p(kept), int(reserve),
+                                       _p(home_off), _p(home_ids), _p(new_page_off), _p(new_page_ids),
+                                       _p(ws), ws.numel(), _stream(stream)), "trimkv_evict_tailfill")
     return Cache(cache.k, cache.v, cache.meta, new_page_off, new_page_ids, cache.length)
 
 

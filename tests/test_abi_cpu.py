@@ -18,7 +18,7 @@ def declared():
 
 def test_exports_every_declared_symbol():
     names = declared()
-    assert len(names) == 19
+    assert len(names) == 20
     L = tk.lib()
     for n in names:
         assert hasattr(L, n), n

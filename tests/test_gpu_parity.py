@@ -989,6 +989,169 @@ def test_streaming_steps_inplace():
 
 
 # --------------------------------------------------------------------------
+# tail-filled eviction (only the entries that fill holes move)
+# --------------------------------------------------------------------------
+def _keep_patterns(rng, lengths):
+    keep = []
+    for h, n in enumerate(lengths):
+        n = int(n)
+        pat = h % 6
+        if pat == 0:
+            kp = np.ones(n, bool)
+        elif pat == 1:
+            kp = np.zeros(n, bool)
+        elif pat == 2:
+            kp = rng.random(n) < 0.3
+        elif pat == 3:
+            kp = np.ones(n, bool)
+            kp[min(2, n - 1):min(3, n)] = False
+        elif pat == 4:
+            kp = rng.random(n) < 0.97
+        else:
+            kp = np.arange(n) % 2 == 0
+        keep.append(kp)
+    return keep
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
+def test_evict_tailfill(dtype, d):
+    """trimkv_evict_tailfill against the oracle's tail-fill order: every
+    head's rows, ln(beta) and positions in their new slot order, the page
+    table (home prefix) and lengths; lengths 0, 1, 16, 17 and up to 2500;
+    counts given and counted."""
+    rng = np.random.default_rng(1300 + d)
+    pc = synth.random_ragged_cache(1400 + d, n_heads=12, d=d, dtype=dtype, max_len=2500, reserve=20)
+    pc.length[:4] = [0, 1, 16, 17]
+    ov = OracleView(pc)
+    H = pc.n_heads
+    home_off, home_ids = pc.page_off.astype(np.int64), pc.page_ids.astype(np.int64)
+    for reserve, kept_given in ((0, True), (3, False), (40, True)):
+        keep = _keep_patterns(rng, pc.length)
+        announce("evict tail-fill", dtype, d, "reserve", reserve)
+        cur = upload(pc)
+        plane = plane_from_heads([k.astype(np.uint8) for k in keep], pc.page_off, pc.length, pc.n_pages, 0,
+                                 np.uint8)
+        wk = np.array([int(k.sum()) for k in keep], np.int32)
+        new_off = torch.full((H + 1,), -1, dtype=torch.int32, device="cuda")
+        new_ids = torch.full((int(home_off[-1]),), -1, dtype=torch.int32, device="cuda")
+        view = tk.evict_tailfill(cur, cuda(plane), reserve, cuda(home_off, np.int32), cuda(home_ids, np.int32),
+                                 new_off, new_ids, kept=cuda(wk) if kept_given else None)
+        order, (wpo, wpi, wlen) = ref.evict_tailfill_order(keep, reserve, home_off, home_ids)
+        po, pi, ln, k, v, lnb, pos = download_cache(view)
+        assert np.array_equal(po, wpo) and np.array_equal(ln, wlen) and np.array_equal(pi[:wpo[-1]], wpi)
+        pi = pi[:max(int(wpo[-1]), 1)]
+        for name, now, was in (("k", k, ov.k_raw), ("v", v, ov.v_raw), ("pos", pos, ov.pos)):
+            got = ref.gather_heads(now, po, pi, ln)
+            for h in range(H):
+                assert np.array_equal(got[h], was[h][order[h]]), (name, h)
+        got = ref.gather_heads(lnb, po, pi, ln)
+        for h in range(H):
+            assert np.array_equal(f32_bits(got[h]), f32_bits(ov.lnb[h][order[h]])), ("lnb", h)
+
+
+def test_streaming_steps_tailfill():
+    """The streaming loop with tail-filled eviction: append -> score ->
+    select -> mask-mode attention -> evict in place, the oracle tracking each
+    head's slot order (its selection ranks ties by position); kept counts,
+    page tables, rows, ln(beta) and positions in slot order every step, and
+    attention within tolerance."""
+    w = SMALL["c5s"]
+    pc = synth.build_cache(w)
+    ov = OracleView(pc)
+    H, G, D = pc.n_heads, w.group, w.head_dim
+    M = w.budget()
+    sc = scale_of(D)
+    cur = upload(pc)
+    home_off, home_ids = cur.page_off.clone(), cur.page_ids.clone()
+    home_off_np, home_ids_np = pc.page_off.astype(np.int64), pc.page_ids.astype(np.int64)
+    tables = [(torch.empty(H + 1, dtype=torch.int32, device="cuda"),
+               torch.empty(int(home_off_np[-1]), dtype=torch.int32, device="cuda")) for _ in range(2)]
+    st = {"lnb": ov.lnb, "pos": ov.pos, "k": ov.k_raw, "v": ov.v_raw}
+    seg = cuda(np.array([0, H], np.int32))
+    bud = cuda(np.array([M], np.int64))
+    status = torch.zeros(2, dtype=torch.int32, device="cuda")
+    for s in range(1, w.steps + 1):
+        t = w.ctx + s
+        announce("stream step tail-fill", s)
+        beta, kn, vn, qn = synth.stream_step(w, s)
+        t_dev = cuda(np.array([t], np.int32))
+        tk.append(cur, kv_dev(kn, "bf16"), kv_dev(vn, "bf16"), cuda(beta, np.float32), t_dev, status=status[0:1])
+        score = torch.empty(cur.n_pages * 16, dtype=torch.float32, device="cuda")
+        keep = torch.empty(cur.n_pages * 16, dtype=torch.uint8, device="cuda")
+        kept = torch.empty(H, dtype=torch.int32, device="cuda")
+        tk.score_select(cur, seg, t_dev, bud, score, keep, kept, status=status[1:2])
+        out = torch.empty((H * G, D), dtype=torch.float32, device="cuda")
+        dropped = torch.empty(H * G, dtype=torch.float32, device="cuda")
+        tk.decode_attn(cur, kv_dev(qn, "bf16"), G, sc, out, dropped, keep=keep)
+        no, ni = tables[s % 2]
+        cur = tk.evict_tailfill(cur, keep, 1, home_off, home_ids, no, ni, kept=kept)
+        lnb_new = ref.ln_beta(beta)
+        for h in range(H):
+            st["lnb"][h] = np.append(st["lnb"][h], lnb_new[h])
+            st["pos"][h] = np.append(st["pos"][h], np.int32(t - 1))
+            st["k"][h] = np.concatenate([st["k"][h], kn[h:h + 1]])
+            st["v"][h] = np.concatenate([st["v"][h], vn[h:h + 1]])
+        scores = [ref.score_f32(st["lnb"][h], t, st["pos"][h]) for h in range(H)]
+        wkeep, wkept = ref.select_global(scores, [0, H], [M], positions=st["pos"])
+        assert np.array_equal(kept.cpu().numpy(), wkept), s
+        q64 = synth.bf16_bits_to_f32(qn).astype(np.float64)
+        kf = [synth.bf16_bits_to_f32(x).astype(np.float64) for x in st["k"]]
+        vf = [synth.bf16_bits_to_f32(x).astype(np.float64) for x in st["v"]]
+        wout, wdrop, _ = ref.decode_attn(kf, vf, q64, G, sc, keep=wkeep)
+        assert np.max(np.abs(out.cpu().numpy() - wout)) <= OUT_TOL, s
+        assert np.max(np.abs(dropped.cpu().numpy() - wdrop)) <= DROP_TOL, s
+        order, (wpo, wpi, wlen) = ref.evict_tailfill_order(wkeep, 1, home_off_np, home_ids_np)
+        st = {name: [x[h][order[h]] for h in range(H)] for name, x in st.items()}
+        po, pi, ln, k, v, lnb, pos = download_cache(cur)
+        assert np.array_equal(po, wpo) and np.array_equal(ln, wlen) and np.array_equal(pi[:wpo[-1]], wpi), s
+        pi = pi[:wpo[-1]]
+        for h in range(H):
+            assert np.array_equal(ref.gather_heads(pos, po, pi, ln)[h], st["pos"][h]), (s, h)
+            assert np.array_equal(f32_bits(ref.gather_heads(lnb, po, pi, ln)[h]), f32_bits(st["lnb"][h]))
+            assert np.array_equal(ref.gather_heads(k, po, pi, ln)[h], st["k"][h])
+            assert np.array_equal(ref.gather_heads(v, po, pi, ln)[h], st["v"][h])
+    assert int(status.sum().item()) == 0
+
+
+@pytest.mark.parametrize("kind", ["alpha3", "equal", "zeros", "nan"])
+def test_select_ties_out_of_position_order(kind):
+    """Caches whose slots hold positions in shuffled order within every head
+    (as after tail-filled eviction), with tie-heavy scores: the selection
+    ranks ties by position, as the oracle given the positions; segments end
+    inside 32-chunk blocks; heads of many chunks."""
+    rng = np.random.default_rng(1500 + ["alpha3", "equal", "zeros", "nan"].index(kind))
+    pc = synth.random_ragged_cache(1600, n_heads=14, d=64, dtype="bf16", max_len=9000)
+    # shuffle positions within every head's slots
+    for h in range(pc.n_heads):
+        sl = ref.head_phys_slots(pc.page_off, pc.page_ids, pc.length, h)
+        flat = pc.pos.reshape(-1)
+        flat[sl] = flat[sl][rng.permutation(len(sl))]
+    ov = OracleView(pc)
+    lens = pc.length
+    if kind == "alpha3":
+        sc = [rng.choice([-1.5, -0.25, 0.0], n).astype(np.float32) for n in lens]
+    elif kind == "equal":
+        sc = [np.full(n, -0.5, np.float32) for n in lens]
+    elif kind == "zeros":
+        sc = [rng.choice([0.0, -0.0], n).astype(np.float32) for n in lens]
+    else:
+        sc = [np.where(rng.random(n) < 0.2, np.nan, rng.choice([-np.inf, -2.0, 1.5], n)).astype(np.float32)
+              for n in lens]
+    seg = np.array([0, 3, 9, 14], np.int32)
+    N = [int(lens[seg[s]:seg[s + 1]].sum()) for s in range(3)]
+    c = upload(pc)
+    plane = plane_from_heads(sc, pc.page_off, pc.length, pc.n_pages)
+    for budgets in ([n // 3 for n in N], [int(rng.integers(1, n + 1)) for n in N], [1, 0, N[2] - 1]):
+        announce("select out of position order", kind, budgets)
+        keep, kept, _ = run_select(c, plane, seg, budgets)
+        want_keep, want_kept = ref.select_global(sc, seg, budgets, positions=ov.pos)
+        got = heads_from_plane(keep, pc.page_off, pc.length)
+        for h in range(pc.n_heads):
+            assert np.array_equal(got[h].astype(bool), want_keep[h]), (budgets, h)
+        assert np.array_equal(kept, want_kept)
+
+
+# --------------------------------------------------------------------------
 # the streaming step captured in HIP graphs
 # --------------------------------------------------------------------------
 def test_streaming_graph_capture():

@@ -66,7 +66,9 @@ class GpuRun:
         self.snap = {}
 
 
-def run_gpu(w, pc, steps_in, inplace):
+def run_gpu(w, pc, steps_in, mode):
+    inplace = mode != "out_of_place"
+    tailfill = mode == "tail_fill"
     S, H, G, D = w.steps, pc.n_heads, w.group, w.head_dim
     M = w.budget()
     scale = 1.0 / math.sqrt(D)
@@ -94,7 +96,7 @@ def run_gpu(w, pc, steps_in, inplace):
     pools = [tk.Cache.empty(H, cap, D, torch.bfloat16) for _ in range(1 if inplace else 2)]
     tables = [(torch.empty(H + 1, dtype=torch.int32, device="cuda"),
                torch.empty(cap, dtype=torch.int32, device="cuda")) for _ in range(2)]
-    ws_inp = tk.workspace(tk.OP_COMPACT_INPLACE, pools[0])
+    ws_inp = tk.workspace(tk.OP_EVICT_TAILFILL if tailfill else tk.OP_COMPACT_INPLACE, pools[0])
     ws_of = lambda c: (tk.workspace(tk.OP_SELECT, c, 1), tk.workspace(tk.OP_DECODE_ATTN, c, 0, G),
                        tk.workspace(tk.OP_COMPACT, c))
     ws_pre, ws_pool = ws_of(prefill), ws_of(pools[0])
@@ -106,15 +108,23 @@ def run_gpu(w, pc, steps_in, inplace):
         wsel, watt, wcmp = ws_pre if s == 1 else ws_pool
         tk.append(cur, k_all[i], v_all[i], beta_all[i], t_all[i], status=st_app)
         tk.score(cur, seg, t_all[i], score)
-        tk.select_global(cur, score, seg, bud, keep, kept, ws=wsel, status=st_sel)
+        if tailfill:   # the fused score + select, on slots out of position order
+            tk.score_select(cur, seg, t_all[i], bud, score, keep, kept, ws=wsel, status=st_sel)
+        else:
+            tk.score(cur, seg, t_all[i], score)
+            tk.select_global(cur, score, seg, bud, keep, kept, ws=wsel, status=st_sel)
         tk.decode_attn(cur, q_all[i], G, scale, out, dropped, keep=keep, ws=watt)
         if s in samples:
             snap = {"cur_off": cur.page_off.cpu().numpy(), "cur_len": cur.length.cpu().numpy()}
             snap["keep"] = keep[:int(snap["cur_off"][-1]) * 16].cpu().numpy()
             snap["out"], snap["dropped"] = out.cpu().numpy(), dropped.cpu().numpy()
+            if tailfill:   # positions of the slots the keep plane refers to
+                snap["cur_pos"] = ref.gather_heads(cur.meta[:, 1, :].cpu().numpy(), snap["cur_off"],
+                                                   cur.page_ids.cpu().numpy(), snap["cur_len"])
         if inplace and s > 1:
             nt = tables[s % 2]
-            nxt = tk.compact_inplace(cur, keep, 1, home[0], home[1], nt[0], nt[1], kept=kept, ws=ws_inp)
+            evict = tk.evict_tailfill if tailfill else tk.compact_inplace
+            nxt = evict(cur, keep, 1, home[0], home[1], nt[0], nt[1], kept=kept, ws=ws_inp)
         else:
             nxt = pools[s % len(pools)]
             tk.compact(cur, keep, res1 if s == 1 else 1, M, nxt, used, ws=wcmp, kept=kept)
@@ -213,15 +223,16 @@ def oracle_state(stream_run):
     return res
 
 
-@pytest.mark.parametrize("inplace", [False, True], ids=["out_of_place", "in_place"])
-def test_full_streaming_run(stream_run, oracle_state, inplace):
+@pytest.mark.parametrize("mode", ["out_of_place", "in_place", "tail_fill"])
+def test_full_streaming_run(stream_run, oracle_state, mode):
     w, pc, steps_in = stream_run
     kept_hist, osnap = oracle_state
     S, H, G, D = w.steps, pc.n_heads, w.group, w.head_dim
     M = w.budget()
+    inplace, tailfill = mode != "out_of_place", mode == "tail_fill"
     t0 = time.time()
-    r = run_gpu(w, pc, steps_in, inplace)
-    say("GPU ran", S, "steps", "in place" if inplace else "out of place", "in %.1f s" % (time.time() - t0))
+    r = run_gpu(w, pc, steps_in, mode)
+    say("GPU ran", S, "steps", mode, "in %.1f s" % (time.time() - t0))
     assert r.status == (0, 0), "failure counters (append, select)"
     # every step: kept per head, page offsets and lengths
     assert np.array_equal(r.kept, kept_hist), np.argwhere(r.kept != kept_hist)[:5]
@@ -239,18 +250,25 @@ def test_full_streaming_run(stream_run, oracle_state, inplace):
     for s, g in sorted(r.snap.items()):
         o = osnap[s]
         got = heads_from_plane(g["keep"], g["cur_off"], g["cur_len"])
-        for h in range(H):
-            assert np.array_equal(got[h].astype(bool), o["keep"][h]), (s, "keep", h)
         gpos, glnb = g["pos"], g["lnb"]
+        # tail-filled slots are not in position order: compare in position order
+        srt = [np.argsort(gpos[h], kind="stable") if tailfill else slice(None) for h in range(H)]
         for h in range(H):
-            assert np.array_equal(gpos[h], o["pos"][h][o["keep"][h]]), (s, "pos", h)
-            assert np.array_equal(f32_bits(glnb[h]), f32_bits(o["lnb"][h][o["keep"][h]])), (s, "lnb", h)
+            if tailfill:
+                assert np.array_equal(np.sort(g["cur_pos"][h][got[h].astype(bool)]),
+                                      o["pos"][h][o["keep"][h]]), (s, "keep", h)
+            else:
+                assert np.array_equal(got[h].astype(bool), o["keep"][h]), (s, "keep", h)
+            assert np.array_equal(gpos[h][srt[h]], o["pos"][h][o["keep"][h]]), (s, "pos", h)
+            assert np.array_equal(f32_bits(glnb[h][srt[h]]), f32_bits(o["lnb"][h][o["keep"][h]])), (s, "lnb", h)
         q64 = kv_f64(steps_in[s - 1][3], "bf16")
         K, V, kp = [], [], []
         for h in SAMPLE_HEADS:
             kk, vv = entry_rows(w, pc, steps_in, h, o["pos"][h])
             kr, vr = g["rows"][h]
-            assert np.array_equal(kr, kk[o["keep"][h]]) and np.array_equal(vr, vv[o["keep"][h]]), (s, "rows", h)
+            j = SAMPLE_HEADS.index(h)
+            kr, vr = kr[srt[h]], vr[srt[h]]
+            assert np.array_equal(kr, kk[o["keep"][h]]) and np.array_equal(vr, vv[o["keep"][h]]), (s, "rows", h, j)
             K.append(kv_f64(kk, "bf16"))
             V.append(kv_f64(vv, "bf16"))
             kp.append(o["keep"][h])

@@ -325,6 +325,62 @@ def test_compaction_equals_page_by_page_appending():
             assert reserve <= spare < reserve + 16 or (spare == 0 and reserve == 0)
 
 
+def test_tailfill_eviction_order():
+    """Tail-filled eviction against a one-entry-at-a-time walk (brute force,
+    pure Python): the kept rows of every head fill its first slots, entries
+    kept below the new length stay where they were, and exactly the drops
+    below the new length move."""
+    rng = np.random.default_rng(37)
+    for trial in range(40):
+        H = int(rng.integers(1, 6))
+        length = rng.integers(0, 70, H)
+        home_pages = -(-length // 16) + rng.integers(0, 3, H)
+        home_off = np.concatenate([[0], np.cumsum(home_pages)]).astype(np.int64)
+        home_ids = rng.permutation(int(home_off[-1]) + 2)[:home_off[-1]].astype(np.int64)
+        pool = list(rng.integers(0, 1 << 30, (int(home_off[-1]) + 2) * 16))
+        keep = [rng.random(int(n)) < rng.uniform(0.0, 1.0) for n in length]
+        slots = [[int(home_ids[home_off[h] + i // 16]) * 16 + i % 16 for i in range(int(length[h]))]
+                 for h in range(H)]
+        rows = [[pool[x] for x in slots[h]] for h in range(H)]
+        reserve = int(rng.integers(0, 20))
+        order, (po, pi, ln) = ref.evict_tailfill_order(keep, reserve, home_off, home_ids)
+        for h in range(H):
+            n = brute.tailfill_in_place(pool, slots[h], keep[h].tolist())
+            assert n == int(ln[h]) == len(order[h])
+            got = [pool[slots[h][j]] for j in range(n)]
+            assert got == [rows[h][i] for i in order[h]], (trial, h)
+            assert sorted(order[h].tolist()) == np.flatnonzero(keep[h]).tolist()
+            stay = [j for j in range(n) if keep[h][j]]
+            assert all(order[h][j] == j for j in stay)
+            assert sum(1 for j in range(n) if order[h][j] != j) == int((~keep[h][:n]).sum())
+
+
+def test_select_ties_rank_by_position_in_any_slot_order():
+    """With positions given (slots out of position order), ties rank by
+    position descending within a head: equal to a brute-force sort on
+    (score, head, -position), and the same keep set as the slot-ordered
+    cache that holds the same entries."""
+    rng = np.random.default_rng(38)
+    for trial in range(200):
+        H = int(rng.integers(1, 6))
+        lens = rng.integers(0, 30, H)
+        kind = SORT_KINDS[trial % len(SORT_KINDS)]
+        scores = _random_scores(rng, kind, lens)
+        pos = [np.sort(rng.choice(200, int(n), replace=False)) for n in lens]
+        perm = [rng.permutation(int(n)) for n in lens]
+        sp = [s[p] for s, p in zip(scores, perm)]
+        pp = [x[p] for x, p in zip(pos, perm)]
+        M = int(rng.integers(0, int(lens.sum()) + 3))
+        keep, kept = ref.select_global(sp, [0, H], [M], positions=pp)
+        want = brute.select_sorted([(float(sp[h][i]), h, int(pp[h][i])) for h in range(H) for i in range(int(lens[h]))],
+                                   M)
+        got = set((h, int(pp[h][i])) for h in range(H) for i in np.flatnonzero(keep[h]))
+        assert got == want, trial
+        k2, kept2 = ref.select_global(scores, [0, H], [M])
+        assert set((h, int(pos[h][i])) for h in range(H) for i in np.flatnonzero(k2[h])) == got
+        assert np.array_equal(kept, kept2)
+
+
 def test_inplace_compaction_layout_and_sequential_shift():
     """In-place eviction: a one-entry-at-a-time shift over a tiny pool (brute
     force, in pure Python) leaves every head's kept rows, in order, in the
