@@ -427,7 +427,7 @@ __device__ __forceinline__ uint32_t keep_word(uint32_t km) {
 }
 
 // ---------------------------------------------------------------------------
-// decide: block b handles chunk positions b*CPB .. b*CPB + CPB - 1.  The state
+// decide: block b handles chunk positions b*CB .. b*CB + CB - 1.  The state
 // after the last radix pass is computed once per segment run of the block.
 // In the common case every key equal to K* is kept and chunks are
 // independent: keep words, then one kept-count atomic per head run.  When
@@ -438,47 +438,50 @@ __device__ __forceinline__ uint32_t keep_word(uint32_t km) {
 // processed, so every chunk a block waits for belongs to a block that is
 // already running.  Optional per-chunk kept-score sums (fixed-order trees).
 // ---------------------------------------------------------------------------
+template <int CB>
 __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __restrict__ score, SelWs w,
                                                    uint8_t* __restrict__ keep, int32_t* __restrict__ kept,
                                                    int want_sum, const int32_t* __restrict__ page_ids,
                                                    const uint32_t* __restrict__ meta) {
+  constexpr int RNDB = CB / CG;   // rounds of CG chunks
+  static_assert(CB % CG == 0 && CB <= CPB, "chunk rounds");
   __shared__ int64_t tmp[NT / WAVE + 1];
   __shared__ double tmpd[NT / WAVE];
-  __shared__ double tmps[RND][NT / WAVE];   // per-round wave sums of kept scores
-  __shared__ int cnt[RND][NT / WAVE];        // per-round wave counts of kept slots
+  __shared__ double tmps[RNDB][NT / WAVE];   // per-round wave sums of kept scores
+  __shared__ int cnt[RNDB][NT / WAVE];        // per-round wave counts of kept slots
   __shared__ int red[NT / WAVE];
   __shared__ int sh_c;
   __shared__ int64_t sh_excl;
   __shared__ uint32_t lhist[256];   // ranked ties: histogram of position bytes
   __shared__ uint32_t sh_pre;
   __shared__ int64_t sh_rem;
-  __shared__ int4 sm[CPB];
-  const int c0 = blockIdx.x * CPB;
+  __shared__ int4 sm[CB];
+  const int c0 = blockIdx.x * CB;
   int4 mv = make_int4(0, 0, 0, 0);
-  if (threadIdx.x < CPB) mv = w.meta[c0 + threadIdx.x];   // padded by CPB entries
+  if (threadIdx.x < CB) mv = w.meta[c0 + threadIdx.x];   // padded by CPB >= CB entries
   const int T = w.chunk_off[n_heads];
   if (c0 >= T) return;
-  const int nc = min(CPB, T - c0);
+  const int nc = min(CB, T - c0);
   if (threadIdx.x < nc) sm[threadIdx.x] = mv;
   lds_barrier();
   const int lane = threadIdx.x & (WAVE - 1), wid = threadIdx.x / WAVE;
   const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / GT), i0 = (threadIdx.x % GT) * 4;
   // scores of the block's own chunk positions, all loads in flight at once
-  float ka[RND][4];
+  float ka[RNDB][4];
   SegState st0;
   {
-    float4 kv[RND];
+    float4 kv[RNDB];
 #pragma unroll
-    for (int r = 0; r < RND; ++r) {
+    for (int r = 0; r < RNDB; ++r) {
       const int k = r * CG + grp;
       const int4 m = umeta(sm, k);
       kv[r] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (k < nc && i0 < (m.w & 0xFFFF)) kv[r] = *reinterpret_cast<const float4*>(score + (int64_t)m.z * PAGE + i0);
     }
     // state for the first segment run while the scores are in flight
-    st0 = state_after(w, sm[0].y, 2, CPB);
+    st0 = state_after(w, sm[0].y, 2, CB);
 #pragma unroll
-    for (int r = 0; r < RND; ++r) {
+    for (int r = 0; r < RNDB; ++r) {
       ka[r][0] = kv[r].x;
       ka[r][1] = kv[r].y;
       ka[r][2] = kv[r].z;
@@ -490,16 +493,16 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
     const int sg = sm[i].y;
     int e = i + 1;
     while (e < nc && sm[e].y == sg) ++e;
-    const SegState st = i == 0 ? st0 : state_after(w, sg, 2, CPB);
+    const SegState st = i == 0 ? st0 : state_after(w, sg, 2, CB);
     opaque(ka);
     const bool ranked = st.mode == MODE_NORMAL && st.ties > st.remaining;
     if (!ranked) {
       // every tie is kept: key >= K*, i.e. (K* above the key of NaN) one
       // comparison with the smallest value whose key is K*
-      uint32_t kmr[RND];
+      uint32_t kmr[RNDB];
       auto mark = [&](auto cmp_only) {
 #pragma unroll
-        for (int r = 0; r < RND; ++r) {
+        for (int r = 0; r < RNDB; ++r) {
           const int k = r * CG + grp;
           kmr[r] = 0;
           if (k >= i && k < e) {
@@ -529,7 +532,7 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
       if (sm[i].x == sm[e - 1].x) {   // block-uniform
         int n = 0;
 #pragma unroll
-        for (int r = 0; r < RND; ++r) {
+        for (int r = 0; r < RNDB; ++r) {
           const int k = r * CG + grp;
           if (k >= i && k < e) n += __popc(kmr[r]);
         }
@@ -537,7 +540,7 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
         if (threadIdx.x == 0 && n) atomicAdd(kept + sm[i].x, n);
       } else {
 #pragma unroll
-        for (int r = 0; r < RND; ++r) {
+        for (int r = 0; r < RNDB; ++r) {
           const int k = r * CG + grp;
           int n = (k >= i && k < e) ? __popc(kmr[r]) : 0;
           for (int d = WAVE / 2; d > 0; d >>= 1) n += __shfl_xor(n, d, WAVE);
@@ -560,7 +563,7 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
         // every round's wave sums first, then one barrier; each chunk's sum
         // then adds its waves' sums in the same fixed order as before
 #pragma unroll
-        for (int r = 0; r < RND; ++r) {
+        for (int r = 0; r < RNDB; ++r) {
           const int k = r * CG + grp;
           const bool mine = k >= i && k < e;
           double sum = 0.0;
@@ -575,7 +578,7 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
         lds_barrier();
         if (threadIdx.x % GT == 0) {
 #pragma unroll
-          for (int r = 0; r < RND; ++r) {
+          for (int r = 0; r < RNDB; ++r) {
             const int k = r * CG + grp;
             if (k >= i && k < e) {
               double t = 0.0;
@@ -828,26 +831,56 @@ int select_kernels(const trimkv_cache_t* c, const float* score, int n_seg, const
   const int prep_blocks = prep_grid(c->n_heads, T, 1024);
   hipLaunchKernelGGL(k_sel_prep, dim3(prep_blocks), dim3(1024), 0, st, c->page_off, c->len, c->n_heads, n_seg, seg,
                      budget, T, w, kept);
-  const unsigned hb = (unsigned)((T + CPB - 1) / CPB);
+  // Chunks per block: 32 for pools of at least 4,096 chunks (about 4M
+  // entries); smaller pools take 16, 8 or 4, the fewest that still gives at
+  // most 256 blocks, so that a small selection (a streaming step's 0.5M
+  // entries) spreads over many CUs instead of a dozen.  Counted, like the
+  // grids, from the pool's capacity.
+  const int cb = T >= 4096 ? CPB : T <= 4 * (int64_t)N_CU ? 4 : T <= 8 * (int64_t)N_CU ? 8 : 16;
+  const unsigned hb = (unsigned)((T + cb - 1) / cb);
   prof_begin(st);
-  if (src.score)
-    hipLaunchKernelGGL((k_sel_hist<0, CPB, true>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);
-  else
-    hipLaunchKernelGGL((k_sel_hist<0, CPB>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);   // 48 VGPRs
-  // Later passes (78 VGPRs at CPB chunks per block: one block per CU), when
-  // there are more blocks with work than CUs (counted as if the pool's pages
-  // were all in use): half the chunks per block, whose fewer live keys (64
-  // VGPRs) let two blocks share a CU.
-  if ((c->n_pages / CP + CPB - 1) / CPB > N_CU) {
-    const unsigned hb2 = (unsigned)((T + CPB / 2 - 1) / (CPB / 2));
-    hipLaunchKernelGGL((k_sel_hist<1, CPB / 2>), dim3(hb2), dim3(NT), 0, st, c->n_heads, score, w, src);
-    hipLaunchKernelGGL((k_sel_hist<2, CPB / 2>), dim3(hb2), dim3(NT), 0, st, c->n_heads, score, w, src);
-  } else {
-    hipLaunchKernelGGL((k_sel_hist<1, CPB>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);
-    hipLaunchKernelGGL((k_sel_hist<2, CPB>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);
+#define TRIMKV_SEL_PASSES(CBV)                                                                                    \
+  {                                                                                                                \
+    if (src.score)                                                                                                 \
+      hipLaunchKernelGGL((k_sel_hist<0, CBV, true>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);       \
+    else                                                                                                           \
+      hipLaunchKernelGGL((k_sel_hist<0, CBV>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);             \
+    hipLaunchKernelGGL((k_sel_hist<1, CBV>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);               \
+    hipLaunchKernelGGL((k_sel_hist<2, CBV>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);               \
   }
-  hipLaunchKernelGGL(k_sel_decide, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, keep, kept,
-                     keptsum != nullptr, c->page_ids, c->meta);
+  if (cb == CPB) {
+    if (src.score)
+      hipLaunchKernelGGL((k_sel_hist<0, CPB, true>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);
+    else
+      hipLaunchKernelGGL((k_sel_hist<0, CPB>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);   // 48 VGPRs
+    // Later passes (78 VGPRs at CPB chunks per block: one block per CU), when
+    // there are more blocks with work than CUs (counted as if the pool's pages
+    // were all in use): half the chunks per block, whose fewer live keys (64
+    // VGPRs) let two blocks share a CU.
+    if ((c->n_pages / CP + CPB - 1) / CPB > N_CU) {
+      const unsigned hb2 = (unsigned)((T + CPB / 2 - 1) / (CPB / 2));
+      hipLaunchKernelGGL((k_sel_hist<1, CPB / 2>), dim3(hb2), dim3(NT), 0, st, c->n_heads, score, w, src);
+      hipLaunchKernelGGL((k_sel_hist<2, CPB / 2>), dim3(hb2), dim3(NT), 0, st, c->n_heads, score, w, src);
+    } else {
+      hipLaunchKernelGGL((k_sel_hist<1, CPB>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);
+      hipLaunchKernelGGL((k_sel_hist<2, CPB>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);
+    }
+    hipLaunchKernelGGL(k_sel_decide<CPB>, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, keep, kept,
+                       keptsum != nullptr, c->page_ids, c->meta);
+  } else if (cb == 16) {
+    TRIMKV_SEL_PASSES(16)
+    hipLaunchKernelGGL(k_sel_decide<16>, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, keep, kept,
+                       keptsum != nullptr, c->page_ids, c->meta);
+  } else if (cb == 8) {
+    TRIMKV_SEL_PASSES(8)
+    hipLaunchKernelGGL(k_sel_decide<8>, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, keep, kept,
+                       keptsum != nullptr, c->page_ids, c->meta);
+  } else {
+    TRIMKV_SEL_PASSES(4)
+    hipLaunchKernelGGL(k_sel_decide<4>, dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, keep, kept,
+                       keptsum != nullptr, c->page_ids, c->meta);
+  }
+#undef TRIMKV_SEL_PASSES
   prof_end(st);
   if (keptsum)
     hipLaunchKernelGGL(k_sel_headsum, dim3((unsigned)((c->n_heads + 255) / 256)), dim3(256), 0, st, c->n_heads, w,

@@ -113,13 +113,26 @@ def test_score_parity(name):
     assert np.all(np.isnan(plane[:total][~valid]))
 
 
-def _score_select_case(pc, seg, t_seg, budgets):
+def pad_pool(c: tk.Cache, extra_pages: int) -> tk.Cache:
+    """The same cache in a pool with extra_pages more (unused) pages."""
+    P, N = c.n_pages, c.n_pages + extra_pages
+
+    def grow(x):
+        y = torch.zeros((N,) + tuple(x.shape[1:]), dtype=x.dtype, device=x.device)
+        y[:P] = x
+        return y
+    return tk.Cache(grow(c.k), grow(c.v), grow(c.meta), c.page_off, grow(c.page_ids), c.length)
+
+
+def _score_select_case(pc, seg, t_seg, budgets, extra_pages=0):
     """trimkv_score_select against trimkv_score then trimkv_select_global on
     the same cache (score plane, keep plane, kept counts and kept sums bit
     for bit), and both against the oracle."""
     c = upload(pc)
+    if extra_pages:
+        c = pad_pool(c, extra_pages)
     ov = OracleView(pc)
-    n = pc.n_pages * 16
+    n = c.n_pages * 16
     seg_d, t_d, b_d = cuda(seg, np.int32), cuda(np.asarray(t_seg, np.int32)), cuda(np.asarray(budgets), np.int64)
     s1 = torch.full((n,), 123.0, dtype=torch.float32, device="cuda")
     s2 = torch.full((n,), 321.0, dtype=torch.float32, device="cuda")
@@ -169,6 +182,24 @@ def test_score_select_ties_and_ragged():
         for budgets in ([n // 3 for n in N], [0, 1, max(N[2] - 1, 0)], [n + 2 for n in N]):
             announce("score_select ragged", dist, budgets)
             _score_select_case(pc, seg, [t, t + 3, t + 9], budgets)
+
+
+@pytest.mark.parametrize("chunks", [0, 1500, 3000, 4200])
+def test_score_select_block_sizes(chunks):
+    """The selection takes 4, 8, 16 or 32 chunks of 64 pages per block by the
+    pool's capacity (about n_pages / 64 + heads chunks): the same ragged
+    caches in pools of growing capacity (extra pages unused) give the same
+    outputs, equal to the oracle's, with ties below and straddling the
+    budget."""
+    for seed, dist in ((41, ("beta", 5.0, 1.0)), (42, ("const", 1.0))):
+        pc = synth.random_ragged_cache(seed, n_heads=23, d=64, dtype="bf16", max_len=5000, beta_dist=dist)
+        seg = np.array([0, 5, 17, 23], np.int32)
+        N = [int(pc.length[seg[s]:seg[s + 1]].sum()) for s in range(3)]
+        t = int(pc.pos.max()) + 1
+        extra = max(chunks * 64 - pc.n_pages, 0)
+        announce("score_select block size", chunks, dist, extra)
+        for budgets in ([n // 3 for n in N], [1, max(N[1] - 7, 0), N[2] + 1]):
+            _score_select_case(pc, seg, [t, t + 3, t + 9], budgets, extra_pages=extra)
 
 
 # --------------------------------------------------------------------------
