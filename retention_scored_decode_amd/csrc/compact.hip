@@ -376,7 +376,7 @@ __global__ void __launch_bounds__(NTP) k_cmp_shift(int n_heads, int reserve, con
 // so it is unaffected; attention is order-free).
 //
 // One block per head: a first walk over the head's first kept_h slots ranks
-// its holes (block scan per window of NTP slots) and lists their physical
+// its holes (block scan per window of 4 NTP slots, 4 per thread) and lists their physical
 // slots in the workspace at the head's CSR offset; a second walk over the
 // rest ranks the movers, and mover r moves to hole r (LPR lanes of 16 bytes
 // per row).  Counts that disagree with the keep plane move only
@@ -393,7 +393,7 @@ __global__ void __launch_bounds__(NTP) k_cmp_tailfill(int n_heads, int reserve, 
                                                       uint32_t* __restrict__ meta, uint32_t* __restrict__ holes) {
   constexpr int LPR = ROWB / 16;          // lanes per row
   constexpr int GROUPS = NTP / LPR;       // rows moved at once by the block
-  __shared__ uint32_t s_src[NTP], s_dst[NTP];
+  __shared__ uint32_t s_src[4 * NTP], s_dst[4 * NTP];   // a window's movers (4 slots per thread)
   __shared__ int64_t red[NWP + 1];
   const int h = blockIdx.x, tid = threadIdx.x, lane = tid & (WAVE - 1), wid = tid / WAVE;
   auto pages_of = [&](int j) -> int64_t {
@@ -423,27 +423,36 @@ __global__ void __launch_bounds__(NTP) k_cmp_tailfill(int n_heads, int reserve, 
   const int kh = min(max(head_kept[h], 0), nv);
   uint32_t* const hl = holes + (int64_t)p0 * PAGE;   // this head's hole list (its CSR slots)
   auto phys = [&](int i) -> uint32_t { return (uint32_t)page_ids[p0 + i / PAGE] * PAGE + i % PAGE; };
-  // 1. holes: dropped slots below kh, in slot order
+  // 1. holes: dropped slots below kh, in slot order (4 consecutive slots
+  //    per thread: one 4-byte keep load, one block scan per 4,096 slots)
+  const uint8_t* kh_bytes = keep + (int64_t)p0 * PAGE;   // the head's keep bytes, in slot order
   int n_holes = 0;
-  for (int s0 = 0; s0 < kh; s0 += NTP) {
-    const int i = s0 + tid;
-    const int hole = i < kh && keep[((int64_t)p0 + i / PAGE) * PAGE + i % PAGE] == 0;
+  for (int s0 = 0; s0 < kh; s0 += 4 * NTP) {
+    const int i = s0 + 4 * tid;   // a multiple of 4: its 4 bytes lie in one page
+    const uint32_t kb = i < kh ? *reinterpret_cast<const uint32_t*>(kh_bytes + i) : ~0u;
+    uint32_t bits = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bits |= (uint32_t)(i + j < kh && ((kb >> (8 * j)) & 0xFFu) == 0) << j;
     int64_t tot;
-    const int r = (int)block_exclusive_scan<NTP>(hole, red, &tot);
-    if (hole) hl[n_holes + r] = phys(i);
+    int r = (int)block_exclusive_scan<NTP>(__popc(bits), red, &tot);
+    for (uint32_t b = bits; b; b &= b - 1) hl[n_holes + r++] = phys(i + __builtin_ctz(b));
     n_holes += __builtin_amdgcn_readfirstlane((int)tot);   // block-uniform: the loop below stays uniform
   }
   __syncthreads();   // the hole list (global memory) is complete and visible to the block
   // 2. movers: kept slots from kh on; mover r takes hole r
   int n_movers = 0;
-  for (int s0 = kh; s0 < nv && n_movers < n_holes; s0 += NTP) {
-    const int i = s0 + tid;
-    const int mover = i < nv && keep[((int64_t)p0 + i / PAGE) * PAGE + i % PAGE] != 0;
+  for (int s0 = kh & ~3; s0 < nv && n_movers < n_holes; s0 += 4 * NTP) {
+    const int i = s0 + 4 * tid;
+    const uint32_t kb = i < nv ? *reinterpret_cast<const uint32_t*>(kh_bytes + i) : 0u;
+    uint32_t bits = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      bits |= (uint32_t)(i + j >= kh && i + j < nv && ((kb >> (8 * j)) & 0xFFu) != 0) << j;
     int64_t tot;
-    const int r = (int)block_exclusive_scan<NTP>(mover, red, &tot);
+    int r = (int)block_exclusive_scan<NTP>(__popc(bits), red, &tot);
     const int n_here = min(__builtin_amdgcn_readfirstlane((int)tot), n_holes - n_movers);
-    if (mover && r < n_here) {
-      s_src[r] = phys(i);
+    for (uint32_t b = bits; b && r < n_here; b &= b - 1, ++r) {
+      s_src[r] = phys(i + __builtin_ctz(b));
       s_dst[r] = hl[n_movers + r];
     }
     lds_barrier();
