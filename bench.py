@@ -637,7 +637,7 @@ def host_cpu():
 
 def baseline_threads():
     """Host threads of the parallel oracle run: every CPU the process may run
-    on, at most 16 (a one-GPU machine's CPU share)."""
+    on, at most 16 (the host share that goes with one GPU of an 8-GPU node)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:

@@ -849,10 +849,16 @@ int select_kernels(const trimkv_cache_t* c, const float* score, int n_seg, const
     hipLaunchKernelGGL((k_sel_hist<2, CBV>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);               \
   }
   if (cb == CPB) {
-    if (src.score)
-      hipLaunchKernelGGL((k_sel_hist<0, CPB, true>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);
-    else
+    if (src.score) {
+      // the pass that also forms the scores holds 94 VGPRs at CPB chunks per
+      // block (one block per CU) and 54 at half (two): half measured faster
+      // (8B pool: score + select 67.0 -> 64.4 us; the plain passes are
+      // slower at half there, 56.1 -> 57.7 us for select)
+      const unsigned hb0 = (unsigned)((T + CPB / 2 - 1) / (CPB / 2));
+      hipLaunchKernelGGL((k_sel_hist<0, CPB / 2, true>), dim3(hb0), dim3(NT), 0, st, c->n_heads, score, w, src);
+    } else {
       hipLaunchKernelGGL((k_sel_hist<0, CPB>), dim3(hb), dim3(NT), 0, st, c->n_heads, score, w, src);   // 48 VGPRs
+    }
     // Later passes (78 VGPRs at CPB chunks per block: one block per CU), when
     // there are more blocks with work than CUs (counted as if the pool's pages
     // were all in use): half the chunks per block, whose fewer live keys (64
