@@ -139,10 +139,10 @@ int trimkv_score(const trimkv_cache_t* cache, int32_t n_seg, const int32_t* seg_
  *            0 in padding slots
  *   kept:    device int32 [n_heads], out: kept entries per head
  *   keptsum: device fp64 [n_heads] or NULL, out: sum of the kept scores of
- *            each head (slot order within 1024-slot chunks, chunks in order)
+ *            each head (a fixed-order tree within each 1024-slot chunk, chunks in order)
  *   status:  device int32 [1] or NULL: a failure counter that the call only
  *            increments (the caller clears it): +1 for every wait on the
- *            tie ranks of earlier chunks that gave up after its bounded spin
+ *            tie counts of earlier heads that gave up after its bounded spin
  *            (never expected; the keep plane of that segment is then not
  *            exact).  One counter may serve many calls and be read once.
  *   ws:      workspace of trimkv_workspace_size(TRIMKV_OP_SELECT, cache, n_seg, 0) bytes
