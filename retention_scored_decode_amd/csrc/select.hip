@@ -68,7 +68,7 @@ struct SelWs {
   SegState* seg;        // [4][n_seg]: state before radix pass 0, 1, 2 and the final state
   int n_seg;
   uint32_t* hist;       // [n_seg][HIST_WORDS]
-  uint64_t* look;       // [Tmax] look-back words: 0 | flag<<62 | value
+  uint64_t* look;       // [Tmax > n_heads] tie look-back word of each head: 0 | flag<<62 | value
   uint32_t* ticket;     // [2 + n_seg]: [2 + s] ticket of segment s
   int32_t* status;      // caller's failure counter (nullable): +1 per timed-out look-back wait
   double* part;         // [Tmax]
@@ -606,6 +606,8 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
       // the compiler threaded them into a nested loop whose inner back edge,
       // taken by every lane but thread 0, re-read the previous ticket, so
       // those lanes never left the loop.
+      // look-back words are indexed by head (heads of different segments are
+      // disjoint; a head without pages has no chunk but still takes a ticket)
       const int cb = st.chunk_begin;
       const int h_first = __builtin_amdgcn_readfirstlane(w.meta[cb].x);
       const int n_th = __builtin_amdgcn_readfirstlane(w.meta[st.chunk_end - 1].x) - h_first + 1;
@@ -650,13 +652,13 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
           int64_t excl = 0;
           if (t != 0) {
             if (lane == 0)
-              __hip_atomic_store(w.look + cb + t, LB_AGG | (uint64_t)eq_h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_store(w.look + h, LB_AGG | (uint64_t)eq_h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             int base = t - 1;   // window: tickets base, base-1, ..., base-63
             uint32_t spins = 0;
             while (true) {
               const int jj = base - lane;
               // before the segment's first ticket: a zero prefix
-              const uint64_t v = jj >= 0 ? __hip_atomic_load(w.look + cb + jj, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+              const uint64_t v = jj >= 0 ? __hip_atomic_load(w.look + h_first + jj, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                          : LB_PREFIX;
               const uint64_t zm = __ballot(v == 0ull);
               const uint64_t pm = __ballot((v & ~LB_VAL) == LB_PREFIX);
@@ -678,7 +680,7 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
             }
           }
           if (lane == 0) {
-            __hip_atomic_store(w.look + cb + t, LB_PREFIX | (uint64_t)(excl + eq_h), __ATOMIC_RELAXED,
+            __hip_atomic_store(w.look + h, LB_PREFIX | (uint64_t)(excl + eq_h), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
             sh_excl = excl;
           }

@@ -2,6 +2,7 @@
 inputs.  Integer and selection results must match bit for bit; attention
 outputs within 2e-3 max-abs and dropped mass within 1e-5 of the float64
 oracle on the bf16-rounded inputs."""
+import dataclasses
 import math
 import os
 
@@ -181,6 +182,41 @@ def test_score_select_ties_and_ragged():
         t = int(pc.pos.max()) + 1
         for budgets in ([n // 3 for n in N], [0, 1, max(N[2] - 1, 0)], [n + 2 for n in N]):
             announce("score_select ragged", dist, budgets)
+            _score_select_case(pc, seg, [t, t + 3, t + 9], budgets)
+
+
+def empty_heads(pc, heads):
+    """The same cache with the given heads emptied: no pages, length 0 (their
+    physical pages stay in the pool, unused, at the end of the page list)."""
+    po, ids = pc.page_off, pc.page_ids
+    length = pc.length.copy()
+    keep_ids, dropped, off = [], [], [0]
+    for h in range(pc.n_heads):
+        seg_ids = list(ids[po[h]:po[h + 1]])
+        if h in heads:
+            length[h] = 0
+            dropped += seg_ids
+        else:
+            keep_ids += seg_ids
+        off.append(len(keep_ids))
+    rest = list(ids[po[-1]:])
+    page_ids = np.array(keep_ids + dropped + rest, np.int32)
+    return dataclasses.replace(pc, page_off=np.array(off, np.int32), page_ids=page_ids, length=length)
+
+
+def test_score_select_ties_with_empty_heads():
+    """A head without pages takes a tie ticket but has no chunk, so a segment
+    can hold more heads than chunks: segments whose ties straddle the budget,
+    with empty heads at their start, inside them and at their end."""
+    for seed, dist in ((51, ("const", 1.0)), (52, ("const", 0.5)), (53, ("beta", 5.0, 1.0))):
+        pc = synth.random_ragged_cache(seed, n_heads=23, d=64, dtype="bf16", max_len=3000, min_len=40,
+                                       beta_dist=dist)
+        pc = empty_heads(pc, {1, 2, 3, 6, 8, 10, 11, 12, 13, 14, 18, 22})
+        seg = np.array([0, 8, 16, 23], np.int32)
+        N = [int(pc.length[seg[s]:seg[s + 1]].sum()) for s in range(3)]
+        t = int(pc.pos.max()) + 1
+        for budgets in ([n // 3 for n in N], [n // 2 + 1 for n in N], [1, max(N[1] - 1, 0), N[2]]):
+            announce("score_select empty heads", dist, budgets)
             _score_select_case(pc, seg, [t, t + 3, t + 9], budgets)
 
 
