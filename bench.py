@@ -37,8 +37,9 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 50 on the 8B workload, 20 on the batched and 128K ones)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed warm-up steps (default 5)")
     ap.add_argument("--cold-reps", type=int, default=10, help="flushed repetitions of the decode stage")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="llama8b_32k",
@@ -55,7 +56,12 @@ def parse():
     ap.add_argument("--trace-summary", metavar="KERNEL_STATS_CSV",
                     help="write profiles/kernel_stats_<workload>.md from a rocprofv3 --kernel-trace --stats "
                          "csv of this benchmark, then exit")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 50 if args.workload == "llama8b_32k" else 20
+    if args.warmup is None:
+        args.warmup = 5
+    return args
 
 
 # decode calls over the retained cache after each eviction in a pipeline step
@@ -1138,11 +1144,35 @@ def bench_streaming(args, w):
         assert int(loop.status.sum().item()) == 0
         return loop, ev[0].elapsed_time(ev[1]) * 1e-3
 
+    def run_loop_tf(n, graph):
+        """steps 1..n evicting in place by tail fill through StreamLoop:
+        steps 2..n launched eagerly, or captured in graphs of 64 steps and
+        replayed"""
+        step_one(home, RES)
+        loop = StreamLoop([home], M, G, scale, banks, first=1, evict="tail_fill")
+        if graph:
+            loop.capture(n - 1)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        if graph:
+            loop.replay()
+        else:
+            loop.run(n - 1)
+        ev[1].record()
+        torch.cuda.synchronize()
+        assert int(loop.status.sum().item()) == 0
+        return loop, ev[0].elapsed_time(ev[1]) * 1e-3
+
     run_oop(min(S, 4))                       # first launches load the kernels
     run_inplace(min(S, 4))
     run_tailfill(min(S, 4))
     view_tf, t_tf = run_tailfill(S)
     assert int(view_tf.length.sum().item()) == M
+    len_tf = view_tf.length.clone()
+    run_loop_tf(min(S, 4), True)
+    loop_tf, t_tf_graph = run_loop_tf(S, True)
+    assert torch.equal(loop_tf.cache.length, len_tf)
+    del loop_tf
     run_loop(min(S, 4), False)
     run_loop(min(S, 4), True)
     loop_e, t_staged = run_loop(S, False)
@@ -1195,6 +1225,9 @@ def bench_streaming(args, w):
                          "what": "in place in the home pages, scores formed inside the selection, eviction by "
                                  "tail fill: only the kept entries that fill holes below the new length move "
                                  "(at most the step's %d drops)" % H},
+           "tail_fill_hip_graph": {"steps_per_s": round(S_t / t_tf_graph, 1),
+                                   "us_per_step": round(t_tf_graph / S_t * 1e6, 2),
+                                   "what": "the tail-fill steps captured in HIP graphs of 64 steps and replayed"},
            "fused_score_select": {"steps_per_s": round(S_t / t_staged, 1),
                                   "us_per_step": round(t_staged / S_t * 1e6, 2),
                                   "what": "out of place, trimkv_score_select in place of score + select"},

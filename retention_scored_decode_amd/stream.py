@@ -5,8 +5,11 @@ A step (TRIM-KV page, section 2: a new entry per head with its retention;
 the lowest current scores are evicted once the budget is exceeded) appends
 one entry per KV head, scores every entry at the step's t, selects the
 global top M, runs mask-mode decode attention with the step's queries
-(renormalised output and dropped mass), and evicts into the other of two
-pools (one spare slot per head for the next append).
+(renormalised output and dropped mass), and evicts, keeping one spare slot
+per head for the next append.  Eviction is either out of place, into the
+other of two pools, or in place by tail fill: the cache stays in its home
+pages and only the kept entries that fill holes below a head's new length
+move, the new page table going to the other of two table buffers.
 
 Every per-step quantity is read from device memory (t included), so a run
 of steps can be captured once and replayed: capture() records the next n
@@ -26,25 +29,36 @@ from . import trimkv as tk
 
 
 class StreamLoop:
-    """Streaming steps over two ping-pong pools.
+    """Streaming steps.
 
-    pools:  two Cache objects of equal capacity, at least
-            ceil((M + n_heads) / 16) + n_heads pages each;
+    pools:  out of place, two Cache objects of equal capacity, at least
+            ceil((M + n_heads) / 16) + n_heads pages each; the current cache
+            is pools[0].  Tail fill, one Cache: the current cache, whose page
+            table is the home list of every head (room for M entries plus one
+            spare slot per head and step to come).
     banks:  device tensors of per-step inputs, step entry first:
             k [S, H, D], v [S, H, D] (cache dtype), beta [S, H] float32,
             q [S, H * group, D] (cache dtype), t [S, 1] int32 (the decode
             step; entry s is appended at position t[s] - 1);
-    first:  the bank entry of the next step; the current cache is pools[0].
+    first:  the bank entry of the next step;
+    evict:  "out_of_place" or "tail_fill".
     """
 
-    def __init__(self, pools: List[tk.Cache], budget: int, group: int, scale: float, banks: dict, first: int = 0):
-        assert len(pools) == 2 and pools[0].n_pages == pools[1].n_pages
-        dev = pools[0].k.device
-        H, D = pools[0].n_heads, pools[0].head_dim
+    def __init__(self, pools: List[tk.Cache], budget: int, group: int, scale: float, banks: dict, first: int = 0,
+                 evict: str = "out_of_place"):
+        assert evict in ("out_of_place", "tail_fill")
+        self.tail_fill = evict == "tail_fill"
+        if self.tail_fill:
+            assert len(pools) == 1
+        else:
+            assert len(pools) == 2 and pools[0].n_pages == pools[1].n_pages
+        base = pools[0]
+        dev = base.k.device
+        H, D = base.n_heads, base.head_dim
         self.pools, self.M, self.G, self.scale = pools, int(budget), int(group), float(scale)
         self.banks = banks
         self.next = int(first)
-        n = pools[0].n_pages * tk.PAGE
+        n = base.n_pages * tk.PAGE
         self.score = torch.empty(n, dtype=torch.float32, device=dev)
         self.keep = torch.empty(n, dtype=torch.uint8, device=dev)
         self.kept = torch.empty(H, dtype=torch.int32, device=dev)
@@ -53,27 +67,38 @@ class StreamLoop:
         self.dropped = torch.empty(H * group, dtype=torch.float32, device=dev)
         self.seg = torch.tensor([0, H], dtype=torch.int32, device=dev)
         self.bud = torch.tensor([self.M], dtype=torch.int64, device=dev)
-        self.ws_sel = tk.workspace(tk.OP_SELECT, pools[0], 1)
-        self.ws_att = tk.workspace(tk.OP_DECODE_ATTN, pools[0], 0, group)
-        self.ws_cmp = tk.workspace(tk.OP_COMPACT, pools[0])
+        self.ws_sel = tk.workspace(tk.OP_SELECT, base, 1)
+        self.ws_att = tk.workspace(tk.OP_DECODE_ATTN, base, 0, group)
+        if self.tail_fill:
+            self.home_off, self.home_ids = base.page_off.clone(), base.page_ids.clone()
+            self.tables = [(torch.empty_like(base.page_off), torch.empty_like(base.page_ids)) for _ in range(2)]
+            self.ws_ev = tk.workspace(tk.OP_EVICT_TAILFILL, base)
+        else:
+            self.ws_ev = tk.workspace(tk.OP_COMPACT, base)
         # failure counters (append: heads without a free slot; select: timed-out waits)
         self.status = torch.zeros(2, dtype=torch.int32, device=dev)
-        self.cur = 0          # index of the pool holding the current cache
+        self.view = base      # the current cache
         self.graphs: list = []
 
-    def _step(self, i: int, src: tk.Cache, dst: tk.Cache):
+    def _step(self, i: int, src: tk.Cache) -> tk.Cache:
+        """Step of bank entry i on cache src; returns the cache after eviction."""
         b = self.banks
         tk.append(src, b["k"][i], b["v"][i], b["beta"][i], b["t"][i], status=self.status[0:1])
         tk.score_select(src, self.seg, b["t"][i], self.bud, self.score, self.keep, self.kept, ws=self.ws_sel,
                         status=self.status[1:2])
         tk.decode_attn(src, b["q"][i], self.G, self.scale, self.out, self.dropped, keep=self.keep, ws=self.ws_att)
-        tk.compact(src, self.keep, 1, self.M, dst, self.used, ws=self.ws_cmp, kept=self.kept)
+        if self.tail_fill:
+            off, ids = self.tables[i % 2]
+            return tk.evict_tailfill(src, self.keep, 1, self.home_off, self.home_ids, off, ids, kept=self.kept,
+                                     ws=self.ws_ev)
+        dst = self.pools[1] if src.k.data_ptr() == self.pools[0].k.data_ptr() else self.pools[0]
+        tk.compact(src, self.keep, 1, self.M, dst, self.used, ws=self.ws_ev, kept=self.kept)
+        return dst
 
     def run(self, n: int = 1):
         """The next n steps, launched eagerly."""
         for _ in range(n):
-            self._step(self.next, self.pools[self.cur], self.pools[1 - self.cur])
-            self.cur = 1 - self.cur
+            self.view = self._step(self.next, self.view)
             self.next += 1
 
     def capture(self, n: int, chunk: int = 64):
@@ -82,30 +107,29 @@ class StreamLoop:
         must have run (an eager step in this process first)."""
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
-        graphs, i, cur = [], self.next, self.cur
+        graphs, i, view = [], self.next, self.view
         with torch.cuda.stream(side):
             while i < self.next + n:
                 g = torch.cuda.CUDAGraph()
                 m = min(chunk, self.next + n - i)
                 with torch.cuda.graph(g, stream=side):
                     for _ in range(m):
-                        self._step(i, self.pools[cur], self.pools[1 - cur])
-                        cur = 1 - cur
+                        view = self._step(i, view)
                         i += 1
-                graphs.append((g, m))
+                graphs.append((g, m, view))
         torch.cuda.current_stream().wait_stream(side)
         self.graphs = graphs
 
     def replay(self, graphs: int = -1):
         """Run the captured steps: the next `graphs` graphs (all by default)."""
         k = len(self.graphs) if graphs < 0 else min(graphs, len(self.graphs))
-        for g, m in self.graphs[:k]:
+        for g, m, view in self.graphs[:k]:
             g.replay()
-            self.cur = (self.cur + m) % 2
+            self.view = view
             self.next += m
         self.graphs = self.graphs[k:]
 
     @property
     def cache(self) -> tk.Cache:
-        """The current cache (the pool the last step evicted into)."""
-        return self.pools[self.cur]
+        """The current cache (the one the last step evicted into)."""
+        return self.view

@@ -1221,12 +1221,14 @@ def test_select_ties_out_of_position_order(kind):
 # --------------------------------------------------------------------------
 # the streaming step captured in HIP graphs
 # --------------------------------------------------------------------------
-def test_streaming_graph_capture():
+@pytest.mark.parametrize("evict", ["out_of_place", "tail_fill"])
+def test_streaming_graph_capture(evict):
     """Steps 3..S of the scaled streaming workload replayed from captured
-    graphs (one per step) against the same steps run eagerly:
-    kept counts, outputs, dropped mass, page tables and the final pools bit
-    for bit after every replay, with eager work and synchronisations between
-    replays; the final state against the oracle."""
+    graphs (one per step) against the same steps run eagerly, evicting out
+    of place or in place by tail fill: kept counts, outputs, dropped mass,
+    page tables and the final pools bit for bit after every replay, with
+    eager work and synchronisations between replays; the final state
+    against the oracle."""
     from retention_scored_decode_amd.stream import StreamLoop
 
     w = SMALL["c5s"].scaled(steps=24)
@@ -1245,8 +1247,14 @@ def test_streaming_graph_capture():
     len0 = prefill.length.clone()
 
     def start():
-        """step 1 (the prefill eviction) into a fresh pair of pools"""
-        pools = [tk.Cache.empty(H, dst_capacity(H, M, 1), D, torch.bfloat16) for _ in range(2)]
+        """step 1 (the prefill eviction) into a fresh pair of pools, or into
+        home pages with a spare slot per head for every later step"""
+        if evict == "tail_fill":
+            pools = [tk.Cache.empty(H, dst_capacity(H, M, S), D, torch.bfloat16)]
+            reserve = S
+        else:
+            pools = [tk.Cache.empty(H, dst_capacity(H, M, 1), D, torch.bfloat16) for _ in range(2)]
+            reserve = 1
         prefill.length.copy_(len0)
         t = cuda(np.array([w.ctx + 1], np.int32))
         tk.append(prefill, banks["k"][0], banks["v"][0], banks["beta"][0], t)
@@ -1256,8 +1264,8 @@ def test_streaming_graph_capture():
         seg = cuda(np.array([0, H], np.int32))
         tk.score(prefill, seg, t, score)
         tk.select_global(prefill, score, seg, cuda(np.array([M], np.int64)), keep, kept)
-        tk.compact(prefill, keep, 1, M, pools[0], torch.zeros(1, dtype=torch.int64, device="cuda"), kept=kept)
-        return StreamLoop(pools, M, G, sc, banks, first=1)
+        tk.compact(prefill, keep, reserve, M, pools[0], torch.zeros(1, dtype=torch.int64, device="cuda"), kept=kept)
+        return StreamLoop(pools, M, G, sc, banks, first=1, evict=evict)
 
     def state(loop):
         torch.cuda.synchronize()
@@ -1300,4 +1308,5 @@ def test_streaming_graph_capture():
     gpos = ref.gather_heads(gg[6], gg[0], gg[1], gg[2])
     glnb = ref.gather_heads(gg[5], gg[0], gg[1], gg[2])
     for h in range(H):
-        assert np.array_equal(gpos[h], pos[h]) and np.array_equal(f32_bits(glnb[h]), f32_bits(lnb[h])), h
+        o = np.argsort(gpos[h], kind="stable")   # tail fill keeps the entries, not their slot order
+        assert np.array_equal(gpos[h][o], pos[h]) and np.array_equal(f32_bits(glnb[h][o]), f32_bits(lnb[h])), h
