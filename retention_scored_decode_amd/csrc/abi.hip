@@ -86,12 +86,14 @@ thread_local hipEvent_t g_prof_start = nullptr;
 thread_local hipEvent_t g_prof_stop = nullptr;
 }  // namespace
 
+// A measurement aid: a failed record leaves the caller's events unrecorded,
+// which the caller sees when it reads them; the call itself goes on.
 void trimkv::prof_begin(hipStream_t st) {
-  if (g_prof_start) hipEventRecord(g_prof_start, st);
+  if (g_prof_start) (void)hipEventRecord(g_prof_start, st);
 }
 
 void trimkv::prof_end(hipStream_t st) {
-  if (g_prof_stop) hipEventRecord(g_prof_stop, st);
+  if (g_prof_stop) (void)hipEventRecord(g_prof_stop, st);
   g_prof_start = g_prof_stop = nullptr;
 }
 

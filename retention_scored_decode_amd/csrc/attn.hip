@@ -889,11 +889,13 @@ int resident_waves(K kernel) {
   static thread_local Entry cache[16];
   static thread_local int used = 0;
   int dev = 0;
-  hipGetDevice(&dev);
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   for (int i = 0; i < used; ++i)
     if (cache[i].k == (const void*)kernel && cache[i].dev == dev) return cache[i].waves;
+  // failed queries fall back to an MI355X's 256 CUs and one block per CU:
+  // the split stays correct for any wave count
   int cus = 0, blocks = 0;
-  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, NTA, 0) != hipSuccess) blocks = 1;
   const int wv = std::min(FLAT_WMAX, std::max(1, blocks) * std::max(1, cus) * (NTA / WAVE));
   if (used < 16) cache[used++] = Entry{(const void*)kernel, dev, wv};

@@ -36,8 +36,7 @@ constexpr int CS = CP * PAGE;   // slots per chunk
 constexpr int NT = 1024;        // threads per histogram and decision block
 constexpr int GT = CS / 4;      // threads per chunk (4 slots each)
 constexpr int CG = NT / GT;     // chunks in flight per block: thread t works on chunk t / GT of each round
-constexpr int CPB = 32;         // chunks per block
-constexpr int RND = CPB / CG;   // rounds of CG chunks
+constexpr int CPB = 32;         // chunks per block (most)
 static_assert(CPB % CG == 0 && CPB <= NT, "chunk rounds");
 // Histogram layout per segment and pass: HC copies (block b adds into copy
 // b % HC), 32 words apart, so that each copy's bins take only a quarter of
@@ -225,7 +224,7 @@ template <int PASS, int HB, bool FUSED = false>
 __global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __restrict__ score, SelWs w,
                                                  ScoreSrc src) {
   static_assert(!FUSED || PASS == 0, "scores are formed in the first pass");
-  constexpr int RND = HB / CG;   // rounds of CG chunks (shadows the decision kernel's)
+  constexpr int RND = HB / CG;   // rounds of CG chunks
   static_assert(HB % CG == 0 && HB <= CPB, "chunk rounds");
   constexpr int NB = PASS == 2 ? 1024 : 2048;
   constexpr int SH = PASS == 0 ? 32 : PASS == 1 ? 21 : 10;   // key bits below the known prefix
@@ -329,8 +328,12 @@ __global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __res
             for (int j = 0; j < 4; ++j) {
               if (i0 + j < nv) {
                 bool in;
-                if constexpr (decltype(exact)::value) in = PASS == 0 || (score_key(a[r][j]) >> SH) == pre;
-                else in = a[r][j] >= flo && !(a[r][j] >= fhi);
+                if constexpr (decltype(exact)::value) {
+                  if constexpr (PASS == 0) in = true;   // no prefix yet: every valid key
+                  else in = (score_key(a[r][j]) >> SH) == pre;
+                } else {
+                  in = a[r][j] >= flo && !(a[r][j] >= fhi);
+                }
                 if (in) atomicAdd(&lh[(score_key(a[r][j]) >> BSH) & (NB - 1)], 1u);
               }
             }
@@ -431,12 +434,12 @@ __device__ __forceinline__ uint32_t keep_word(uint32_t km) {
 // after the last radix pass is computed once per segment run of the block.
 // In the common case every key equal to K* is kept and chunks are
 // independent: keep words, then one kept-count atomic per head run.  When
-// the ties straddle the budget (more keys equal K* than `need`), the chunks
-// of that segment are processed in the order of a per-segment ticket, one at
-// a time (by the block's first GT threads), with a decoupled look-back for
-// the ties of earlier chunks; a ticket is taken only when its chunk is
-// processed, so every chunk a block waits for belongs to a block that is
-// already running.  Optional per-chunk kept-score sums (fixed-order trees).
+// the ties straddle the budget (more keys equal K* than `need`), the heads
+// of that segment are processed in the order of a per-segment ticket, one
+// head per ticket and block, with a decoupled look-back for the ties of
+// earlier heads; a ticket is taken only when its head is processed, so
+// every head a block waits for belongs to a block that is already running.
+// Optional per-chunk kept-score sums (fixed-order trees).
 // ---------------------------------------------------------------------------
 template <int CB>
 __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __restrict__ score, SelWs w,
@@ -445,7 +448,6 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
                                                    const uint32_t* __restrict__ meta) {
   constexpr int RNDB = CB / CG;   // rounds of CG chunks
   static_assert(CB % CG == 0 && CB <= CPB, "chunk rounds");
-  __shared__ int64_t tmp[NT / WAVE + 1];
   __shared__ double tmpd[NT / WAVE];
   __shared__ double tmps[RNDB][NT / WAVE];   // per-round wave sums of kept scores
   __shared__ int cnt[RNDB][NT / WAVE];        // per-round wave counts of kept slots
