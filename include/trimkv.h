@@ -21,6 +21,12 @@
  *  - Outputs never alias inputs, except trimkv_append (in place).
  *  - Calls that share a workspace or output buffers must be ordered (same
  *    stream or explicit events); otherwise they race.
+ *  - State the library keeps between calls (host side, none of it holds
+ *    caller data): the resident-wave count of each decode kernel per device
+ *    (one occupancy query, cached per host thread); the per-device address
+ *    of the static scratch of trimkv_decode_attn_noalloc (32 MiB of device
+ *    memory held until the process ends); and the events that
+ *    trimkv_profile_next arms for the next call (per host thread).
  *
  * Data layout ("paged, per-head variable length", DBTrimKV page, Method 4)
  *  - A head is one flat KV head h = (b * L + l) * H_kv + h_kv.
