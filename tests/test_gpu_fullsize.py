@@ -2,10 +2,13 @@
 configuration the benchmark times (score -> select -> mask-mode attention ->
 compaction -> plain decode on the compacted cache).
 
-Selection and the compacted page table are checked for every head; scores,
-compacted rows and both attention modes on a sample of heads spread over the
-layers (the float64 oracle gathers only those heads).  Well under a minute,
-most of it generating the 4 GB synthetic cache and the oracle's selection."""
+Scores, selection, the compacted page table and rows, and the plain decode
+over the compacted cache (the timed attention call) are checked for every
+head; mask-mode attention over the full cache against the float64 oracle on
+a sample of heads spread over the layers (its float64 keys for all 8.4M
+entries would take 8.6 GB), and against the plain decode on every head.
+About a minute, most of it generating the 4 GB synthetic cache and the
+oracle's selection."""
 import math
 import os
 import time
@@ -82,7 +85,7 @@ def test_full_size_pipeline(full_c2):
     assert int(want_kept.sum()) == M
     say("selection bit-exact")
 
-    # ---- compaction: page table for every head, rows for a sample ----
+    # ---- compaction: page table and rows for every head ----
     dpo, dpi, dln, dk, dv, dlnb, dpos = download_cache(dst)
     wpo, _, wln = ref.compact_layout(want_kept, 0)
     assert np.array_equal(dpo, wpo) and np.array_equal(dln, wln)
@@ -90,16 +93,28 @@ def test_full_size_pipeline(full_c2):
     assert np.array_equal(dpi[:int(wpo[-1])], np.arange(int(wpo[-1]), dtype=np.int32))
     sample = list(range(0, H, 17)) + [H - 1]
     flat_k, flat_v = pc.k.reshape(-1, D), pc.v.reshape(-1, D)
-    for h in sample:
-        src = ref.head_phys_slots(po, pi, ln, h)[want_keep[h]]
-        assert np.array_equal(ref.gather_heads(dk, dpo, dpi, dln)[h], flat_k[src]), ("k rows", h)
-        assert np.array_equal(ref.gather_heads(dv, dpo, dpi, dln)[h], flat_v[src]), ("v rows", h)
-        assert np.array_equal(f32_bits(ref.gather_heads(dlnb, dpo, dpi, dln)[h]), f32_bits(lnb[h][want_keep[h]]))
-        assert np.array_equal(ref.gather_heads(dpos, dpo, dpi, dln)[h], pos[h][want_keep[h]])
-    say("compaction checked")
+    src_of = [ref.head_phys_slots(po, pi, ln, h)[want_keep[h]] for h in range(H)]   # kept source slots, in order
+    src_all = np.concatenate(src_of)
+    assert np.array_equal(np.concatenate(ref.gather_heads(dk, dpo, dpi, dln)), flat_k[src_all]), "k rows"
+    assert np.array_equal(np.concatenate(ref.gather_heads(dv, dpo, dpi, dln)), flat_v[src_all]), "v rows"
+    assert np.array_equal(f32_bits(np.concatenate(ref.gather_heads(dlnb, dpo, dpi, dln))),
+                          f32_bits(np.concatenate([lnb[h][want_keep[h]] for h in range(H)])))
+    assert np.array_equal(np.concatenate(ref.gather_heads(dpos, dpo, dpi, dln)),
+                          np.concatenate([pos[h][want_keep[h]] for h in range(H)]))
+    say("compaction checked on every head")
 
-    # ---- attention on the sampled heads, both modes ----
+    # ---- plain decode over the compacted cache (the benchmark's call), every head ----
     om, dm, op, dp, lp = (x.cpu().numpy() for x in (out_m, drop_m, out_p, drop_p, lse_p))
+    Ka = [kv_f64(flat_k[src_of[h]], pc.dtype) for h in range(H)]
+    Va = [kv_f64(flat_v[src_of[h]], pc.dtype) for h in range(H)]
+    wout_a, _, wlse_a = ref.decode_attn(Ka, Va, q64, G, scale)
+    del Ka, Va
+    assert np.max(np.abs(op - wout_a)) <= OUT_TOL
+    assert np.all(dp == 0.0)
+    assert np.all(np.abs(lp - wlse_a) <= 1e-4 * np.maximum(1, np.abs(wlse_a)))
+    say("plain decode checked on every head: max |out - oracle| %.2e" % float(np.max(np.abs(op - wout_a))))
+
+    # ---- both modes on the sampled heads ----
     K = [kv_f64(flat_k[ref.head_phys_slots(po, pi, ln, h)], pc.dtype) for h in sample]
     V = [kv_f64(flat_v[ref.head_phys_slots(po, pi, ln, h)], pc.dtype) for h in sample]
     qs = np.concatenate([q64[h * G:(h + 1) * G] for h in sample])
