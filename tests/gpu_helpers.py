@@ -99,3 +99,31 @@ def f32_bits(a):
 
 def scale_of(d):
     return 1.0 / math.sqrt(d)
+
+
+def decode_by_heads(kv_of, q64, group, scale, dtype, heads, keep_of=None, lse_ref=None, gate_of=None, batch=32):
+    """The float64 oracle's decode attention over many heads, a batch of heads
+    at a time so that only one batch's float64 K and V are held.  kv_of(h)
+    gives head h's raw K and V rows (cache dtype), keep_of(h) its keep mask
+    (None: every row); lse_ref is indexed by query row; gate_of(h), if given,
+    head h's ln r per row (retention-gated attention).  Returns out, dropped
+    and LSE for the query rows of `heads`, in order."""
+    outs, drops, lses = [], [], []
+    for i in range(0, len(heads), batch):
+        hs = heads[i:i + batch]
+        K, V = [], []
+        for h in hs:
+            k, v = kv_of(h)
+            K.append(kv_f64(k, dtype))
+            V.append(kv_f64(v, dtype))
+        rows = np.concatenate([np.arange(h * group, (h + 1) * group) for h in hs])
+        keep = None if keep_of is None else [keep_of(h) for h in hs]
+        if gate_of is not None:
+            o, d, l = ref.decode_attn_gated(K, V, q64[rows], group, scale, [gate_of(h) for h in hs], keep=keep)
+        else:
+            o, d, l = ref.decode_attn(K, V, q64[rows], group, scale, keep=keep,
+                                      lse_ref=None if lse_ref is None else lse_ref[rows])
+        outs.append(o)
+        drops.append(d)
+        lses.append(l)
+    return np.concatenate(outs), np.concatenate(drops), np.concatenate(lses)

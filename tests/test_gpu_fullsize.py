@@ -2,13 +2,12 @@
 configuration the benchmark times (score -> select -> mask-mode attention ->
 compaction -> plain decode on the compacted cache).
 
-Scores, selection, the compacted page table and rows, and the plain decode
-over the compacted cache (the timed attention call) are checked for every
-head; mask-mode attention over the full cache against the float64 oracle on
-a sample of heads spread over the layers (its float64 keys for all 8.4M
-entries would take 8.6 GB), and against the plain decode on every head.
-About a minute, most of it generating the 4 GB synthetic cache and the
-oracle's selection."""
+Every head is checked against the oracle: scores and selection bit for
+bit, the compacted page table and rows, mask-mode attention over the full
+cache and the plain decode over the compacted cache (the timed call) within
+the attention tolerances (the float64 oracle takes a batch of heads at a
+time).  The batched workload checks mask-mode attention over its 67M-entry
+cache on a sample of heads, and against the plain decode on every head."""
 import math
 import os
 import time
@@ -20,7 +19,8 @@ import torch
 import synth
 from oracle import reference as ref
 from retention_scored_decode_amd import trimkv as tk
-from gpu_helpers import DROP_TOL, OUT_TOL, cuda, download_cache, f32_bits, heads_from_plane, kv_dev, kv_f64, upload
+from gpu_helpers import (DROP_TOL, OUT_TOL, cuda, decode_by_heads, download_cache, f32_bits, heads_from_plane,
+                         kv_dev, kv_f64, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -91,7 +91,6 @@ def test_full_size_pipeline(full_c2):
     assert np.array_equal(dpo, wpo) and np.array_equal(dln, wln)
     assert int(used.item()) == int(wpo[-1])
     assert np.array_equal(dpi[:int(wpo[-1])], np.arange(int(wpo[-1]), dtype=np.int32))
-    sample = list(range(0, H, 17)) + [H - 1]
     flat_k, flat_v = pc.k.reshape(-1, D), pc.v.reshape(-1, D)
     src_of = [ref.head_phys_slots(po, pi, ln, h)[want_keep[h]] for h in range(H)]   # kept source slots, in order
     src_all = np.concatenate(src_of)
@@ -105,43 +104,31 @@ def test_full_size_pipeline(full_c2):
 
     # ---- plain decode over the compacted cache (the benchmark's call), every head ----
     om, dm, op, dp, lp = (x.cpu().numpy() for x in (out_m, drop_m, out_p, drop_p, lse_p))
-    Ka = [kv_f64(flat_k[src_of[h]], pc.dtype) for h in range(H)]
-    Va = [kv_f64(flat_v[src_of[h]], pc.dtype) for h in range(H)]
-    wout_a, _, wlse_a = ref.decode_attn(Ka, Va, q64, G, scale)
-    del Ka, Va
+    wout_a, _, wlse_a = decode_by_heads(lambda h: (flat_k[src_of[h]], flat_v[src_of[h]]), q64, G, scale, pc.dtype,
+                                        list(range(H)))
     assert np.max(np.abs(op - wout_a)) <= OUT_TOL
     assert np.all(dp == 0.0)
     assert np.all(np.abs(lp - wlse_a) <= 1e-4 * np.maximum(1, np.abs(wlse_a)))
     say("plain decode checked on every head: max |out - oracle| %.2e" % float(np.max(np.abs(op - wout_a))))
 
-    # ---- both modes on the sampled heads ----
-    K = [kv_f64(flat_k[ref.head_phys_slots(po, pi, ln, h)], pc.dtype) for h in sample]
-    V = [kv_f64(flat_v[ref.head_phys_slots(po, pi, ln, h)], pc.dtype) for h in sample]
-    qs = np.concatenate([q64[h * G:(h + 1) * G] for h in sample])
-    rows = np.concatenate([np.arange(h * G, (h + 1) * G) for h in sample])
-    kp = [want_keep[h] for h in sample]
-    wout, wdrop, _ = ref.decode_attn(K, V, qs, G, scale, keep=kp)
-    assert np.max(np.abs(om[rows] - wout)) <= OUT_TOL
-    assert np.max(np.abs(dm[rows] - wdrop)) <= DROP_TOL
-    wout2, _, wlse2 = ref.decode_attn([k[m] for k, m in zip(K, kp)], [v[m] for v, m in zip(V, kp)], qs, G, scale)
-    assert np.max(np.abs(op[rows] - wout2)) <= OUT_TOL
-    assert np.all(dp[rows] == 0.0)
-    assert np.all(np.abs(lp[rows] - wlse2) <= 1e-4 * np.maximum(1, np.abs(wlse2)))
-    # properties at every head: finite outputs, dropped mass in [0, 1], both modes agree on the kept set
-    assert np.all(np.isfinite(om)) and np.all(np.isfinite(op))
-    assert np.all((dm >= 0) & (dm <= 1))
+    # ---- mask-mode attention over the full cache, every head (16 heads at a time) ----
+    slots = [ref.head_phys_slots(po, pi, ln, h) for h in range(H)]
+    wout, wdrop, _ = decode_by_heads(lambda h: (flat_k[slots[h]], flat_v[slots[h]]), q64, G, scale, pc.dtype,
+                                     list(range(H)), keep_of=lambda h: want_keep[h], batch=16)
+    assert np.max(np.abs(om - wout)) <= OUT_TOL
+    assert np.max(np.abs(dm - wdrop)) <= DROP_TOL
     assert np.max(np.abs(op - om)) <= OUT_TOL
-    say("attention checked on", len(sample), "heads; modes agree on all", H)
+    say("mask-mode attention checked on every head: max |out - oracle| %.2e, |dropped - oracle| %.2e"
+        % (float(np.max(np.abs(om - wout))), float(np.max(np.abs(dm - wdrop)))))
 
 
 def test_full_size_gated_and_incremental(full_c2):
     """The two streaming-side rows at full size, in the launch configuration
-    the benchmark times: retention-gated decode over the compacted cache
-    (sampled heads against the float64 oracle, finite everywhere), and one
-    streaming step with in-place eviction on the kept set compacted with 64
-    spare slots per head (append one entry per head, select the same budget,
-    evict in place): selection and the new page table for every head, rows
-    for a sample of heads."""
+    the benchmark times: retention-gated decode over the compacted cache, and
+    one streaming step with in-place eviction on the kept set compacted with
+    64 spare slots per head (append one entry per head, select the same
+    budget, evict in place).  Every head is checked against the oracle:
+    gated outputs, selection, the new page table and the moved rows."""
     w, pc = full_c2
     H, G, D = pc.n_heads, w.group, w.head_dim
     M = w.budget()
@@ -195,23 +182,18 @@ def test_full_size_gated_and_incremental(full_c2):
     scores = [ref.score_f32(lnb[h], w.t, pos[h]) for h in range(H)]
     keep1, kept1 = ref.select_global(scores, seg_np, [M])
     assert np.array_equal(kept.cpu().numpy(), kept1)
-    sample = list(range(0, H, 17)) + [H - 1]
     flat_k, flat_v = pc.k.reshape(-1, D), pc.v.reshape(-1, D)
+    src_of = [ref.head_phys_slots(po, pi, ln, h)[keep1[h]] for h in range(H)]   # kept source slots, in order
 
-    # ---- gated decode on the sampled heads ----
+    # ---- gated decode, every head ----
     og, dg = out_g.cpu().numpy(), drop_g.cpu().numpy()
-    assert np.all(np.isfinite(og)) and np.all((dg >= 0) & (dg <= 1))
-    K = [kv_f64(flat_k[ref.head_phys_slots(po, pi, ln, h)[keep1[h]]], pc.dtype) for h in sample]
-    V = [kv_f64(flat_v[ref.head_phys_slots(po, pi, ln, h)[keep1[h]]], pc.dtype) for h in sample]
-    gate = [scores[h][keep1[h]].astype(np.float64) for h in sample]
-    qs = np.concatenate([q64[h * G:(h + 1) * G] for h in sample])
-    rows = np.concatenate([np.arange(h * G, (h + 1) * G) for h in sample])
-    wout, wdrop, _ = ref.decode_attn_gated(K, V, qs, G, scale, gate)
-    assert np.max(np.abs(og[rows] - wout)) <= OUT_TOL
-    assert np.all(dg[rows] == 0.0)
-    say("gated decode checked on", len(sample), "heads")
+    wout, _, _ = decode_by_heads(lambda h: (flat_k[src_of[h]], flat_v[src_of[h]]), q64, G, scale, pc.dtype,
+                                 list(range(H)), gate_of=lambda h: scores[h][keep1[h]].astype(np.float64))
+    assert np.max(np.abs(og - wout)) <= OUT_TOL
+    assert np.all(dg == 0.0)
+    say("gated decode checked on every head: max |out - oracle| %.2e" % float(np.max(np.abs(og - wout))))
 
-    # ---- in-place step: selection and table for every head, rows for the sample ----
+    # ---- in-place step: selection, table, rows and metadata for every head ----
     lnb_new = ref.ln_beta(bn)
     lnb2 = [np.append(lnb[h][keep1[h]], lnb_new[h]) for h in range(H)]
     pos2 = [np.append(pos[h][keep1[h]], np.int32(t1 - 1)) for h in range(H)]
@@ -225,22 +207,25 @@ def test_full_size_gated_and_incremental(full_c2):
     vpo, vpi, vln, vk, vv, vlnb, vpos = download_cache(view)
     assert np.array_equal(vpo, wpo) and np.array_equal(vln, wln) and np.array_equal(vpi[:wpo[-1]], wpi)
     vpi = vpi[:wpo[-1]]
-    for h in sample:
-        k_rows = np.concatenate([flat_k[ref.head_phys_slots(po, pi, ln, h)[keep1[h]]], kn[h:h + 1]])
-        v_rows = np.concatenate([flat_v[ref.head_phys_slots(po, pi, ln, h)[keep1[h]]], vn[h:h + 1]])
-        assert np.array_equal(ref.gather_heads(vk, vpo, vpi, vln)[h], k_rows[keep2w[h]]), ("k rows", h)
-        assert np.array_equal(ref.gather_heads(vv, vpo, vpi, vln)[h], v_rows[keep2w[h]]), ("v rows", h)
-        assert np.array_equal(ref.gather_heads(vpos, vpo, vpi, vln)[h], pos2[h][keep2w[h]])
-        assert np.array_equal(f32_bits(ref.gather_heads(vlnb, vpo, vpi, vln)[h]), f32_bits(lnb2[h][keep2w[h]]))
-    say("in-place eviction checked: table on all", H, "heads, rows on", len(sample))
+    gk, gv, gpos, glnb = (ref.gather_heads(x, vpo, vpi, vln) for x in (vk, vv, vpos, vlnb))
+    for h in range(H):
+        k_rows = np.concatenate([flat_k[src_of[h]], kn[h:h + 1]])
+        v_rows = np.concatenate([flat_v[src_of[h]], vn[h:h + 1]])
+        assert np.array_equal(gk[h], k_rows[keep2w[h]]), ("k rows", h)
+        assert np.array_equal(gv[h], v_rows[keep2w[h]]), ("v rows", h)
+        assert np.array_equal(gpos[h], pos2[h][keep2w[h]]), ("positions", h)
+        assert np.array_equal(f32_bits(glnb[h]), f32_bits(lnb2[h][keep2w[h]])), ("ln beta", h)
+    say("in-place eviction checked on all", H, "heads: table, rows and metadata")
 
 
 def test_full_size_batched_pipeline():
     """The 16-sequence batched workload at full size (4096 KV heads of 16K
     tokens, 16 per-sequence budgets): scores bit-exact for every head,
     selection bit-exact for every segment against the oracle on the same
-    fp32 scores, compacted page table for every head, rows and both attention
-    modes on a sample of heads."""
+    fp32 scores, compacted page table and rows for every head, the plain
+    decode over the compacted cache against the float64 oracle on every
+    head, mask-mode attention against the oracle on a sample of heads and
+    against the plain decode on every head."""
     w = synth.WORKLOADS["batched16_16k"]
     t0 = time.time()
     pc = synth.build_cache(w, workers=min(16, os.cpu_count() or 1))
@@ -295,14 +280,22 @@ def test_full_size_batched_pipeline():
     assert int(used.item()) == int(wpo[-1])
     sample = list(range(0, H, 331)) + [H - 1]
     flat_k, flat_v = pc.k.reshape(-1, D), pc.v.reshape(-1, D)
-    for h in sample:
-        src = ref.head_phys_slots(po, pi, ln, h)[want_keep[h]]
-        assert np.array_equal(ref.gather_heads(dk, dpo, dpi, dln)[h], flat_k[src]), ("k rows", h)
-        assert np.array_equal(ref.gather_heads(dv, dpo, dpi, dln)[h], flat_v[src]), ("v rows", h)
-        assert np.array_equal(ref.gather_heads(dpos, dpo, dpi, dln)[h], pos[h][want_keep[h]])
-    say("compaction checked")
+    src_of = [ref.head_phys_slots(po, pi, ln, h)[want_keep[h]] for h in range(H)]   # kept source slots, in order
+    src_all = np.concatenate(src_of)
+    assert np.array_equal(np.concatenate(ref.gather_heads(dk, dpo, dpi, dln)), flat_k[src_all]), "k rows"
+    assert np.array_equal(np.concatenate(ref.gather_heads(dv, dpo, dpi, dln)), flat_v[src_all]), "v rows"
+    assert np.array_equal(np.concatenate(ref.gather_heads(dpos, dpo, dpi, dln)),
+                          np.concatenate([pos[h][want_keep[h]] for h in range(H)]))
+    assert np.array_equal(f32_bits(np.concatenate(ref.gather_heads(dlnb, dpo, dpi, dln))),
+                          f32_bits(np.concatenate([lnb[h][want_keep[h]] for h in range(H)])))
+    del src_all
+    say("compaction checked on every head")
 
     om, dm, op, dp = (x.cpu().numpy() for x in (out_m, drop_m, out_p, drop_p))
+    wout_a, _, _ = decode_by_heads(lambda h: (flat_k[src_of[h]], flat_v[src_of[h]]), q64, G, scale, pc.dtype,
+                                   list(range(H)), batch=256)
+    assert np.max(np.abs(op - wout_a)) <= OUT_TOL
+    say("plain decode checked on every head: max |out - oracle| %.2e" % float(np.max(np.abs(op - wout_a))))
     K = [kv_f64(flat_k[ref.head_phys_slots(po, pi, ln, h)], pc.dtype) for h in sample]
     V = [kv_f64(flat_v[ref.head_phys_slots(po, pi, ln, h)], pc.dtype) for h in sample]
     qs = np.concatenate([q64[h * G:(h + 1) * G] for h in sample])
@@ -323,8 +316,8 @@ def test_full_size_long_context_mass_pipeline():
     per-head top-1024 by mass, dropped-mass budgets, per-head top-b_h,
     compaction and reference-mode attention, then the recency-floor variant.
     Selections and allocations are checked for every head against the oracle on the same
-    fp32 masses and fp64 kept sums; masses, rows and attention on a sample
-    of heads against the float64 oracle."""
+    fp32 masses and fp64 kept sums; masses, full LSE, compacted rows and
+    reference-mode attention for every head against the float64 oracle."""
     w = synth.WORKLOADS["qwen8b_128k"]
     t0 = time.time()
     pc = synth.build_cache(w, workers=min(16, os.cpu_count() or 1))
@@ -360,18 +353,18 @@ def test_full_size_long_context_mass_pipeline():
 
     po, pi, ln = pc.page_off, pc.page_ids, pc.length
     gm = heads_from_plane(mass.cpu().numpy(), po, ln)
-    # masses and full LSE on sampled heads (float64 oracle)
-    sample = [0, 97, 200, H - 1]
+    # masses and full LSE, every head (float64 oracle, eight heads at a time)
     flat_k, flat_v = pc.k.reshape(-1, D), pc.v.reshape(-1, D)
-    K = [kv_f64(flat_k[ref.head_phys_slots(po, pi, ln, h)], pc.dtype) for h in sample]
-    V = [kv_f64(flat_v[ref.head_phys_slots(po, pi, ln, h)], pc.dtype) for h in sample]
-    qs = np.concatenate([q64[h * G:(h + 1) * G] for h in sample])
-    rows = np.concatenate([np.arange(h * G, (h + 1) * G) for h in sample])
-    wm, wlse = ref.attn_mass(K, qs, G, scale)
-    for i, h in enumerate(sample):
-        assert np.all(np.abs(gm[h] - wm[i]) <= 1e-5 * wm[i] + 1e-12), ("mass", h)
-    assert np.max(np.abs(lse.cpu().numpy()[rows] - wlse)) <= 1e-4
-    say("mass checked on", len(sample), "heads")
+    slots = [ref.head_phys_slots(po, pi, ln, h) for h in range(H)]
+    wlse = np.empty(H * G)
+    for h0 in range(0, H, 8):
+        hs = list(range(h0, min(H, h0 + 8)))
+        rows = np.arange(h0 * G, (hs[-1] + 1) * G)
+        wm, wlse[rows] = ref.attn_mass([kv_f64(flat_k[slots[h]], pc.dtype) for h in hs], q64[rows], G, scale)
+        for i, h in enumerate(hs):
+            assert np.all(np.abs(gm[h] - wm[i]) <= 1e-5 * wm[i] + 1e-12), ("mass", h)
+    assert np.max(np.abs(lse.cpu().numpy() - wlse)) <= 1e-4
+    say("mass and full LSE checked on all", H, "heads")
     # selections and allocation, every head, on the same fp32 masses
     want1, _ = ref.select_global(gm, segs, [w.mass_topk] * H)
     got1 = heads_from_plane(keep1, po, ln)
@@ -391,24 +384,27 @@ def test_full_size_long_context_mass_pipeline():
         assert np.array_equal(got2[h].astype(bool), want2[h]), ("budget keep", h)
     assert np.array_equal(kept.cpu().numpy(), want_kept2)
     say("selections and allocation checked on all", H, "heads")
-    # compaction: page table for every head, rows on the sample
+    # compaction: page table, rows and positions for every head
     dpo, dpi, dln, dk, dv, _, dpos = download_cache(dst)
     wpo, _, wln = ref.compact_layout(want_kept2, 0)
     assert np.array_equal(dpo, wpo) and np.array_equal(dln, wln)
     pos = ref.gather_heads(pc.pos, po, pi, ln)
-    for h in sample:
-        src = ref.head_phys_slots(po, pi, ln, h)[want2[h]]
-        assert np.array_equal(ref.gather_heads(dk, dpo, dpi, dln)[h], flat_k[src]), ("k rows", h)
-        assert np.array_equal(ref.gather_heads(dpos, dpo, dpi, dln)[h], pos[h][want2[h]])
-    # reference-mode attention on the sample
-    kp = [want2[h] for h in sample]
-    wout, wdrop, _ = ref.decode_attn([k[m] for k, m in zip(K, kp)], [v[m] for v, m in zip(V, kp)], qs, G, scale,
-                                     lse_ref=wlse)
+    src_of = [slots[h][want2[h]] for h in range(H)]   # kept source slots, in order
+    src_all = np.concatenate(src_of)
+    assert np.array_equal(np.concatenate(ref.gather_heads(dk, dpo, dpi, dln)), flat_k[src_all]), "k rows"
+    assert np.array_equal(np.concatenate(ref.gather_heads(dv, dpo, dpi, dln)), flat_v[src_all]), "v rows"
+    assert np.array_equal(np.concatenate(ref.gather_heads(dpos, dpo, dpi, dln)),
+                          np.concatenate([pos[h][want2[h]] for h in range(H)]))
+    del src_all
+    # reference-mode attention over the compacted cache, every head: outputs
+    # over the kept rows, dropped mass against the oracle's full LSE
+    wout, wdrop, _ = decode_by_heads(lambda h: (flat_k[src_of[h]], flat_v[src_of[h]]), q64, G, scale, pc.dtype,
+                                     list(range(H)), lse_ref=wlse)
     o, dr = out.cpu().numpy(), dropped.cpu().numpy()
-    assert np.max(np.abs(o[rows] - wout)) <= OUT_TOL
-    assert np.max(np.abs(dr[rows] - wdrop)) <= DROP_TOL
-    assert np.all(np.isfinite(o)) and np.all((dr >= -DROP_TOL) & (dr <= 1 + DROP_TOL))
-    say("compaction and attention checked on", len(sample), "heads")
+    assert np.max(np.abs(o - wout)) <= OUT_TOL
+    assert np.max(np.abs(dr - wdrop)) <= DROP_TOL
+    say("compaction and attention checked on all", H, "heads: max |out - oracle| %.2e, |dropped - oracle| %.2e"
+        % (float(np.max(np.abs(o - wout))), float(np.max(np.abs(dr - wdrop)))))
     # ContourKV recency floor (w = 128) on the same masses: allocation and
     # selection for every head
     wf = 128
@@ -428,9 +424,9 @@ def test_full_size_streaming_steps():
     """The streaming workload at full size (112 KV heads, 64K-token prefill,
     GQA 7, fixed budget of 458,752 entries, one reserve slot per head): the
     first three generated steps (append, score, select, mask-mode attention,
-    compaction into the other pool).  Selection and the compacted page table,
-    positions and ln(beta) are checked for every head at every step; K/V rows
-    and attention on a sample of heads."""
+    compaction into the other pool).  Selection, mask-mode attention and the
+    compacted page table, rows, positions and ln(beta) are checked for every
+    head at every step."""
     w = synth.WORKLOADS["stream_gqa7"]
     t0 = time.time()
     pc = synth.build_cache(w, workers=min(16, os.cpu_count() or 1))
@@ -442,13 +438,11 @@ def test_full_size_streaming_steps():
     cap = -(-(M + H) // 16) + H
     pools = [tk.Cache.empty(H, cap, D, torch.bfloat16) for _ in range(2)]
     po, pi, ln = pc.page_off, pc.page_ids, pc.length
-    sample = [0, 45, H - 1]
-    flat_k, flat_v = pc.k.reshape(-1, D), pc.v.reshape(-1, D)
-    # oracle state: ln(beta) and positions of every head; K/V rows of the sample
+    # oracle state of every head: ln(beta), positions, K/V rows (slot order)
     st_lnb = [ref.ln_beta(b) for b in ref.gather_heads(pc.beta, po, pi, ln)]
     st_pos = ref.gather_heads(pc.pos, po, pi, ln)
-    st_k = {h: flat_k[ref.head_phys_slots(po, pi, ln, h)] for h in sample}
-    st_v = {h: flat_v[ref.head_phys_slots(po, pi, ln, h)] for h in sample}
+    st_k = ref.gather_heads(pc.k, po, pi, ln)
+    st_v = ref.gather_heads(pc.v, po, pi, ln)
     seg = cuda(np.array([0, H], np.int32))
     bud = cuda(np.array([M], np.int64))
     for s in range(1, 4):
@@ -474,7 +468,6 @@ def test_full_size_streaming_steps():
         for h in range(H):
             st_lnb[h] = np.append(st_lnb[h], lnb_new[h])
             st_pos[h] = np.append(st_pos[h], np.int32(t - 1))
-        for h in sample:
             st_k[h] = np.concatenate([st_k[h], kn[h:h + 1]])
             st_v[h] = np.concatenate([st_v[h], vn[h:h + 1]])
         scores = [ref.score_f32(st_lnb[h], t, st_pos[h]) for h in range(H)]
@@ -484,22 +477,18 @@ def test_full_size_streaming_steps():
         for h in range(H):
             assert np.array_equal(got[h].astype(bool), wkeep[h]), (s, "keep", h)
         assert np.array_equal(kept.cpu().numpy(), wkept), s
-        # attention on the sample (float64 oracle over the step's full cache)
+        # mask-mode attention, every head (float64 oracle over the step's full cache)
         q64 = synth.bf16_bits_to_f32(qn).astype(np.float64)
-        qs = np.concatenate([q64[h * G:(h + 1) * G] for h in sample])
-        rows = np.concatenate([np.arange(h * G, (h + 1) * G) for h in sample])
-        K = [kv_f64(st_k[h], "bf16") for h in sample]
-        V = [kv_f64(st_v[h], "bf16") for h in sample]
-        wout, wdrop, _ = ref.decode_attn(K, V, qs, G, scale, keep=[wkeep[h] for h in sample])
+        wout, wdrop, _ = decode_by_heads(lambda h: (st_k[h], st_v[h]), q64, G, scale, "bf16", list(range(H)),
+                                         keep_of=lambda h: wkeep[h], batch=16)
         o, dr = out.cpu().numpy(), dropped.cpu().numpy()
-        assert np.max(np.abs(o[rows] - wout)) <= OUT_TOL, s
-        assert np.max(np.abs(dr[rows] - wdrop)) <= DROP_TOL, s
-        # compaction: every head's page table, positions and ln(beta); rows on the sample
+        assert np.max(np.abs(o - wout)) <= OUT_TOL, s
+        assert np.max(np.abs(dr - wdrop)) <= DROP_TOL, s
+        # compaction: every head's page table, rows, positions and ln(beta)
         st_lnb = [st_lnb[h][wkeep[h]] for h in range(H)]
         st_pos = [st_pos[h][wkeep[h]] for h in range(H)]
-        for h in sample:
-            st_k[h] = st_k[h][wkeep[h]]
-            st_v[h] = st_v[h][wkeep[h]]
+        st_k = [st_k[h][wkeep[h]] for h in range(H)]
+        st_v = [st_v[h][wkeep[h]] for h in range(H)]
         dpo, dpi, dln, dk, dv, dlnb, dpos = download_cache(dst)
         wpo, _, wln = ref.compact_layout(wkept, 1)
         assert np.array_equal(dpo, wpo) and np.array_equal(dln, wln), s
@@ -508,8 +497,8 @@ def test_full_size_streaming_steps():
             assert np.array_equal(gpos[h], st_pos[h]), (s, "pos", h)
             assert np.array_equal(f32_bits(glnb[h]), f32_bits(st_lnb[h])), (s, "lnb", h)
         gk, gv = ref.gather_heads(dk, dpo, dpi, dln), ref.gather_heads(dv, dpo, dpi, dln)
-        for h in sample:
+        for h in range(H):
             assert np.array_equal(gk[h], st_k[h]) and np.array_equal(gv[h], st_v[h]), (s, "rows", h)
-        say("step", s, "checked: selection and metadata on all", H, "heads; rows and attention on", len(sample))
+        say("step", s, "checked on all", H, "heads: selection, attention, rows and metadata")
         cur = dst
     assert tk.validate_cache(cur, cuda(np.array([w.ctx + 4], np.int32))) == tk.OK
