@@ -178,6 +178,33 @@ int trimkv_score_select(const trimkv_cache_t* cache, int32_t n_seg, const int32_
                         double* keptsum, int32_t* status, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * trimkv_append_score_select -- a generated step's append, score and
+ * selection in one call, for streaming decode: trimkv_append followed by
+ * trimkv_score_select, with the new entries written by the selection's first
+ * kernel (one launch fewer per step).
+ * TRIM-KV page, section 2 (a new entry per head with its retention, then the
+ * lowest current scores are evicted once the budget is exceeded); DBTrimKV
+ * page, Methods 2-3.
+ * Entry len[h] of head h receives k_new[h], v_new[h], ln(beta_new[h]) and
+ * position t[s] - 1, s the head's segment, and len[h] += 1, for every head
+ * with a free slot; then every entry is scored at its segment's t and the top
+ * budget[s] of each segment are kept.  With one segment the outputs, the
+ * cache included, are bit for bit those of trimkv_append(t) followed by
+ * trimkv_score_select.
+ *   k_new, v_new, beta_new: as trimkv_append
+ *   n_seg, seg_head_begin, t, budget, score, keep, kept, keptsum: as trimkv_score_select
+ *   append_status: as trimkv_append's status (heads without a free slot)
+ *   select_status: as trimkv_select_global's status
+ *   ws:      trimkv_workspace_size(TRIMKV_OP_SELECT, cache, n_seg, 0) bytes
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE.
+ */
+int trimkv_append_score_select(trimkv_cache_t* cache, const void* k_new, const void* v_new,
+                               const float* beta_new, int32_t n_seg, const int32_t* seg_head_begin,
+                               const int32_t* t, const int64_t* budget, float* score, uint8_t* keep,
+                               int32_t* kept, double* keptsum, int32_t* append_status, int32_t* select_status,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/*
  * trimkv_compact -- physical eviction: stable out-of-place compaction.
  * DBTrimKV page, Method 4 (paged per-head variable length); ContourKV page,
  * section 2 (the budget must shrink storage, not just mask it).

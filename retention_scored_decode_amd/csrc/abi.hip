@@ -174,6 +174,21 @@ int trimkv_score_select(const trimkv_cache_t* c, int32_t n_seg, const int32_t* s
   return launch_score_select(c, n_seg, seg, t, budget, score, keep, kept, keptsum, status, ws, S(stream));
 }
 
+int trimkv_append_score_select(trimkv_cache_t* c, const void* k_new, const void* v_new, const float* beta_new,
+                               int32_t n_seg, const int32_t* seg, const int32_t* t, const int64_t* budget,
+                               float* score, uint8_t* keep, int32_t* kept, double* keptsum, int32_t* append_status,
+                               int32_t* select_status, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if (!cache_shape_ok(c, &rc)) return rc;
+  if (!k_new || !v_new || !beta_new || !pools_ok(c) || n_seg < 1 || n_seg > c->n_heads || !seg || !t || !budget ||
+      !score || !keep || !kept || !table_ok(c) || (c->n_pages > 0 && !c->meta) || ((uintptr_t)keep & 15) ||
+      ((uintptr_t)score & 15))
+    return TRIMKV_EINVAL;
+  if ((rc = ws_check(ws, ws_bytes, select_ws_layout(c, n_seg).total))) return rc;
+  return launch_append_score_select(c, k_new, v_new, beta_new, n_seg, seg, t, budget, score, keep, kept, keptsum,
+                                    append_status, select_status, ws, S(stream));
+}
+
 int trimkv_compact(const trimkv_cache_t* src, const uint8_t* keep, const int32_t* kept, int32_t reserve,
                    int64_t max_kept_total, trimkv_cache_t* dst, int64_t* pages_used, void* ws, size_t ws_bytes,
                    void* stream) {

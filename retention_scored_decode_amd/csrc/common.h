@@ -203,9 +203,11 @@ struct PrepLDS {
   int32_t len[PREP_HMAX];
 };
 
+// grow (LDS list only): count one more entry in every head with a free slot
+// (an append that the lengths in memory do not show yet).
 template <int NT>
 __device__ int prep_chunks(const int32_t* __restrict__ page_off, const int32_t* __restrict__ len, int n_heads,
-                           int cp, PrepLDS& L, int64_t* tmp, int32_t* __restrict__ chunk_off_g) {
+                           int cp, PrepLDS& L, int64_t* tmp, int32_t* __restrict__ chunk_off_g, bool grow = false) {
   const bool lds = n_heads <= PREP_HMAX;
   int64_t carry = 0;
   for (int base = 0; base < n_heads; base += NT) {
@@ -216,7 +218,8 @@ __device__ int prep_chunks(const int32_t* __restrict__ page_off, const int32_t* 
       n = ((int64_t)b - a + cp - 1) / cp;
       if (lds) {
         L.pg[h] = a;
-        L.len[h] = len[h];
+        const int32_t n0 = len[h];
+        L.len[h] = n0 + ((grow && (int64_t)n0 < ((int64_t)b - a) * PAGE) ? 1 : 0);
         if (h == n_heads - 1) L.pg[n_heads] = b;
       }
     }

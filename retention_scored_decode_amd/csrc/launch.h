@@ -49,6 +49,10 @@ int launch_select(const trimkv_cache_t* c, const float* score, int n_seg, const 
 int launch_score_select(const trimkv_cache_t* c, int n_seg, const int32_t* seg, const int32_t* t,
                         const int64_t* budget, float* score, uint8_t* keep, int32_t* kept, double* keptsum,
                         int32_t* status, void* ws, hipStream_t st);
+int launch_append_score_select(trimkv_cache_t* c, const void* k_new, const void* v_new, const float* beta_new,
+                               int n_seg, const int32_t* seg, const int32_t* t, const int64_t* budget, float* score,
+                               uint8_t* keep, int32_t* kept, double* keptsum, int32_t* append_status,
+                               int32_t* select_status, void* ws, hipStream_t st);
 int launch_compact(const trimkv_cache_t* src, const uint8_t* keep, const int32_t* kept, int reserve,
                    int64_t max_kept_total, trimkv_cache_t* dst, int64_t* pages_used, void* ws, hipStream_t st);
 int launch_compact_inplace(trimkv_cache_t* c, const uint8_t* keep, const int32_t* kept, int reserve,

@@ -26,6 +26,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "ln_cr.h"
 
 namespace trimkv {
 
@@ -80,15 +81,37 @@ __device__ __forceinline__ uint32_t* pass_hist(const SelWs& w, int s, int pass) 
   return w.hist + (size_t)s * HIST_WORDS + (pass == 0 ? 0 : pass == 1 ? 1 : 2) * HC * copy_words(2048);
 }
 
+// The step's new entries, when the selection also appends them (one per
+// head, at slot len[h] with position t_s - 1 of the head's segment s, as
+// trimkv_append writes them); k_new == null: no append.
+struct AppendSrc {
+  const uint8_t* k_new;    // [n_heads][row bytes]
+  const uint8_t* v_new;
+  const float* beta_new;   // [n_heads]
+  uint8_t* k;              // the cache's K and V planes, rows of `rowb` bytes
+  uint8_t* v;
+  uint32_t* meta;          // [n_pages][2][16]: ln beta bits, positions
+  const int32_t* page_ids;
+  const int32_t* t;        // decode step of each segment
+  int rowb;                // bytes per K or V row
+  int elt;                 // bytes per element (2: bf16, 4: fp32)
+  int32_t* status;         // +1 per head without a free slot (nullable)
+};
+
 // ---------------------------------------------------------------------------
 // prep: chunk list + metadata + segment state (block 0); every block clears
-// histograms, kept[] and look-back words.
+// histograms, kept[] and look-back words.  With an append, every head with
+// a free slot gets its new entry here (one wave per head) and the chunk list
+// counts it; the lengths themselves are raised by the first histogram pass
+// (no selection kernel reads them), except with more heads than the LDS
+// list holds: then this kernel runs as one block and raises them itself,
+// before it reads them.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024) k_sel_prep(const int32_t* __restrict__ page_off,
-                                                   const int32_t* __restrict__ len, int n_heads, int n_seg,
+                                                   int32_t* __restrict__ len, int n_heads, int n_seg,
                                                    const int32_t* __restrict__ seg_hb,
                                                    const int64_t* __restrict__ budget, int64_t tmax, SelWs w,
-                                                   int32_t* __restrict__ kept) {
+                                                   int32_t* __restrict__ kept, AppendSrc ap) {
   const size_t gtid = (size_t)blockIdx.x * 1024 + threadIdx.x, gstride = (size_t)gridDim.x * 1024;
   for (size_t i = gtid; i < (size_t)n_seg * HIST_WORDS; i += gstride) w.hist[i] = 0u;
   for (size_t i = gtid; i < (size_t)tmax; i += gstride) w.look[i] = 0ull;
@@ -96,7 +119,57 @@ __global__ void __launch_bounds__(1024) k_sel_prep(const int32_t* __restrict__ p
   for (size_t i = gtid; i < (size_t)n_seg + 2; i += gstride) w.ticket[i] = 0u;
   __shared__ int64_t tmp[1024 / WAVE + 1];
   __shared__ PrepLDS L;
-  const int T = prep_chunks<1024>(page_off, len, n_heads, CP, L, tmp, w.chunk_off);
+  const bool grow = ap.k_new != nullptr;
+  if (grow) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int nw = gridDim.x * (1024 / WAVE);
+    for (int h = __builtin_amdgcn_readfirstlane(blockIdx.x * (1024 / WAVE) + threadIdx.x / WAVE); h < n_heads;
+         h += nw) {
+      const int n = len[h];
+      const int64_t cap = (int64_t)(page_off[h + 1] - page_off[h]) * PAGE;
+      if (n >= cap) {
+        if (lane == 0 && ap.status) atomicAdd(ap.status, 1);
+        continue;
+      }
+      const int64_t page = ap.page_ids[page_off[h] + n / PAGE];
+      const int64_t slot = page * PAGE + n % PAGE;
+      // element-wise, as trimkv_append copies (inputs need only element alignment)
+      if (ap.elt == 2) {
+        const uint16_t* kn = reinterpret_cast<const uint16_t*>(ap.k_new) + (int64_t)h * (ap.rowb / 2);
+        const uint16_t* vn = reinterpret_cast<const uint16_t*>(ap.v_new) + (int64_t)h * (ap.rowb / 2);
+        uint16_t* kd = reinterpret_cast<uint16_t*>(ap.k) + slot * (ap.rowb / 2);
+        uint16_t* vd = reinterpret_cast<uint16_t*>(ap.v) + slot * (ap.rowb / 2);
+        for (int d = lane; d < ap.rowb / 2; d += WAVE) {
+          kd[d] = kn[d];
+          vd[d] = vn[d];
+        }
+      } else {
+        const uint32_t* kn = reinterpret_cast<const uint32_t*>(ap.k_new) + (int64_t)h * (ap.rowb / 4);
+        const uint32_t* vn = reinterpret_cast<const uint32_t*>(ap.v_new) + (int64_t)h * (ap.rowb / 4);
+        uint32_t* kd = reinterpret_cast<uint32_t*>(ap.k) + slot * (ap.rowb / 4);
+        uint32_t* vd = reinterpret_cast<uint32_t*>(ap.v) + slot * (ap.rowb / 4);
+        for (int d = lane; d < ap.rowb / 4; d += WAVE) {
+          kd[d] = kn[d];
+          vd[d] = vn[d];
+        }
+      }
+      if (lane == 0) {
+        const int s = upper_index(seg_hb, n_seg + 1, h);
+        ap.meta[page * (2 * PAGE) + n % PAGE] = __float_as_uint(ln_f32_cr(ap.beta_new[h]));
+        ap.meta[page * (2 * PAGE) + PAGE + n % PAGE] = (uint32_t)(ap.t[s] - 1);
+      }
+    }
+    if (n_heads > PREP_HMAX) {   // one block: the lengths are raised before they are read
+      __syncthreads();           // every wave has read its heads' old lengths
+      for (int h = threadIdx.x; h < n_heads; h += 1024) {
+        const int n = len[h];
+        if ((int64_t)n < (int64_t)(page_off[h + 1] - page_off[h]) * PAGE) len[h] = n + 1;
+      }
+      __syncthreads();
+    }
+  }
+  const int T = prep_chunks<1024>(page_off, len, n_heads, CP, L, tmp, w.chunk_off,
+                                  grow && n_heads <= PREP_HMAX);
   const bool single = n_heads > PREP_HMAX;   // then one block and a global scan
   if (blockIdx.x == 0) {
     for (int s = threadIdx.x; s < n_seg; s += 1024) {
@@ -209,6 +282,8 @@ struct ScoreSrc {
   const uint32_t* meta;      // [n_pages][2][16]: ln beta bits, positions
   const int32_t* t;          // decode step of each segment
   float* score;              // CSR plane, written
+  int32_t* grow_len;         // with an append planned by prep: the lengths to raise (block 0), else null
+  const int32_t* page_off;
 };
 
 // Block b histograms chunks [b*CPB, b*CPB + CPB), CG chunks per round
@@ -232,6 +307,13 @@ __global__ void __launch_bounds__(NT) k_sel_hist(int n_heads, const float* __res
   __shared__ uint32_t lh[NB];
   __shared__ int4 sm[HB];
   const int c0 = blockIdx.x * HB;
+  if (PASS == 0 && src.grow_len && blockIdx.x == 0) {
+    // the append planned by prep: every head with a free slot grows by one
+    for (int h = threadIdx.x; h < n_heads; h += NT) {
+      const int n = src.grow_len[h];
+      if ((int64_t)n < (int64_t)(src.page_off[h + 1] - src.page_off[h]) * PAGE) src.grow_len[h] = n + 1;
+    }
+  }
   int4 mv = make_int4(0, 0, 0, 0);
   if (threadIdx.x < HB) mv = w.meta[c0 + threadIdx.x];   // padded by CPB >= HB entries
   const int T = w.chunk_off[n_heads];
@@ -828,13 +910,15 @@ namespace {
 // scores itself (score + select in one call).
 int select_kernels(const trimkv_cache_t* c, const float* score, int n_seg, const int32_t* seg,
                    const int64_t* budget, uint8_t* keep, int32_t* kept, double* keptsum, int32_t* status, void* ws,
-                   ScoreSrc src, hipStream_t st) {
+                   ScoreSrc src, AppendSrc ap, hipStream_t st) {
   SelWs w = carve(c, n_seg, ws);
   w.status = status;
   const int64_t T = max_chunks(c, CP);
   const int prep_blocks = prep_grid(c->n_heads, T, 1024);
+  if (ap.k_new && c->n_heads <= PREP_HMAX) src.grow_len = c->len;   // raised by the first pass
+  src.page_off = c->page_off;
   hipLaunchKernelGGL(k_sel_prep, dim3(prep_blocks), dim3(1024), 0, st, c->page_off, c->len, c->n_heads, n_seg, seg,
-                     budget, T, w, kept);
+                     budget, T, w, kept, ap);
   // Chunks per block: 32 for pools of at least 4,096 chunks (about 4M
   // entries); smaller pools take 16, 8 or 4, the fewest that still gives at
   // most 256 blocks, so that a small selection (a streaming step's 0.5M
@@ -903,14 +987,25 @@ int select_kernels(const trimkv_cache_t* c, const float* score, int n_seg, const
 int launch_select(const trimkv_cache_t* c, const float* score, int n_seg, const int32_t* seg,
                   const int64_t* budget, uint8_t* keep, int32_t* kept, double* keptsum, int32_t* status, void* ws,
                   hipStream_t st) {
-  return select_kernels(c, score, n_seg, seg, budget, keep, kept, keptsum, status, ws, ScoreSrc{}, st);
+  return select_kernels(c, score, n_seg, seg, budget, keep, kept, keptsum, status, ws, ScoreSrc{}, AppendSrc{}, st);
 }
 
 int launch_score_select(const trimkv_cache_t* c, int n_seg, const int32_t* seg, const int32_t* t,
                         const int64_t* budget, float* score, uint8_t* keep, int32_t* kept, double* keptsum,
                         int32_t* status, void* ws, hipStream_t st) {
   return select_kernels(c, score, n_seg, seg, budget, keep, kept, keptsum, status, ws,
-                        ScoreSrc{c->page_ids, c->meta, t, score}, st);
+                        ScoreSrc{c->page_ids, c->meta, t, score, nullptr, nullptr}, AppendSrc{}, st);
+}
+
+int launch_append_score_select(trimkv_cache_t* c, const void* k_new, const void* v_new, const float* beta_new,
+                               int n_seg, const int32_t* seg, const int32_t* t, const int64_t* budget, float* score,
+                               uint8_t* keep, int32_t* kept, double* keptsum, int32_t* append_status,
+                               int32_t* select_status, void* ws, hipStream_t st) {
+  const int elt = c->dtype == TRIMKV_BF16 ? 2 : 4;
+  AppendSrc ap{(const uint8_t*)k_new, (const uint8_t*)v_new, beta_new, (uint8_t*)c->k, (uint8_t*)c->v, c->meta,
+               c->page_ids, t, c->head_dim * elt, elt, append_status};
+  return select_kernels(c, score, n_seg, seg, budget, keep, kept, keptsum, select_status, ws,
+                        ScoreSrc{c->page_ids, c->meta, t, score, nullptr, nullptr}, ap, st);
 }
 
 }  // namespace trimkv

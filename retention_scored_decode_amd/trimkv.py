@@ -23,7 +23,7 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ECAPACITY, EHIP, EINVARIANT = 0, -1, -2, -
 
 EXPORTS = ["trimkv_log_beta", "trimkv_score", "trimkv_select_global", "trimkv_compact",
            "trimkv_decode_attn", "trimkv_decode_attn_gated", "trimkv_decode_attn_err", "trimkv_attn_mass",
-           "trimkv_decode_attn_noalloc", "trimkv_score_select", "trimkv_evict_tailfill",
+           "trimkv_decode_attn_noalloc", "trimkv_score_select", "trimkv_append_score_select", "trimkv_evict_tailfill",
            "trimkv_allocate", "trimkv_compact_inplace",
            "trimkv_allocate_floor", "trimkv_mark_recent", "trimkv_append",
            "trimkv_workspace_size", "trimkv_validate_cache", "trimkv_strerror", "trimkv_profile_next"]
@@ -60,6 +60,7 @@ def lib():
             "trimkv_select_global": [cp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_compact": [cp, vp, vp, i32, i64, cp, vp, vp, sz, vp],
             "trimkv_score_select": [cp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "trimkv_append_score_select": [cp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_compact_inplace": [cp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_evict_tailfill": [cp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_decode_attn": [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp],
@@ -209,6 +210,22 @@ def score_select(cache: Cache, seg_head_begin: torch.Tensor, t: torch.Tensor, bu
     _check(lib().trimkv_score_select(ctypes.byref(cache.struct()), n_seg, _p(seg_head_begin), _p(t), _p(budget),
                                      _p(score), _p(keep), _p(kept), _p(keptsum), _p(status), _p(ws), ws.numel(),
                                      _stream(stream)), "trimkv_score_select")
+
+
+def append_score_select(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, beta_new: torch.Tensor,
+                        seg_head_begin: torch.Tensor, t: torch.Tensor, budget: torch.Tensor, score: torch.Tensor,
+                        keep: torch.Tensor, kept: torch.Tensor, keptsum: Optional[torch.Tensor] = None,
+                        ws: Optional[torch.Tensor] = None, stream=None, append_status: Optional[torch.Tensor] = None,
+                        select_status: Optional[torch.Tensor] = None):
+    """append() then score_select() in one call (the new entries are written
+    by the selection's first kernel)."""
+    n_seg = seg_head_begin.numel() - 1
+    if ws is None:
+        ws = workspace(OP_SELECT, cache, n_seg)
+    _check(lib().trimkv_append_score_select(ctypes.byref(cache.struct()), _p(k_new), _p(v_new), _p(beta_new), n_seg,
+                                            _p(seg_head_begin), _p(t), _p(budget), _p(score), _p(keep), _p(kept),
+                                            _p(keptsum), _p(append_status), _p(select_status), _p(ws), ws.numel(),
+                                            _stream(stream)), "trimkv_append_score_select")
 
 
 def compact(src: Cache, keep: torch.Tensor, reserve: int, max_kept_total: int, dst: Cache,

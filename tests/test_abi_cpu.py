@@ -18,7 +18,7 @@ def declared():
 
 def test_exports_every_declared_symbol():
     names = declared()
-    assert len(names) == 20
+    assert len(names) == 21
     L = tk.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -112,6 +112,31 @@ def test_gated_argument_checks():
     assert g(ctypes.byref(c), 1, X, X, None, X, 17, F, X, X, None, X, need, None) == tk.EUNSUPPORTED
     f32 = fake_cache(dtype=tk.F32, head_dim=64)
     assert g(ctypes.byref(f32), 1, X, X, None, X, 4, F, X, X, None, X, 1 << 30, None) == tk.EUNSUPPORTED
+
+
+def test_append_score_select_argument_checks():
+    """trimkv_append_score_select: the append's inputs (as trimkv_append) and
+    the fused selection's (as trimkv_score_select), the selection workspace."""
+    L = tk.lib()
+    c = fake_cache()
+    need = L.trimkv_workspace_size(tk.OP_SELECT, ctypes.byref(c), 1, 0)
+    f = L.trimkv_append_score_select
+    args = [X, X, X, 1, X, X, X, X, X, X, None, None, None, X]
+    for i in (0, 1, 2, 4, 5, 6, 7, 8, 9):   # every required pointer
+        bad = list(args)
+        bad[i] = None
+        assert f(ctypes.byref(c), *bad, need, None) == tk.EINVAL, i
+    for n_seg in (0, 5):
+        bad = list(args)
+        bad[3] = n_seg
+        assert f(ctypes.byref(c), *bad, need, None) == tk.EINVAL, n_seg
+    for i in (7, 8):   # score and keep: 16-byte aligned
+        bad = list(args)
+        bad[i] = ctypes.c_void_p(0x10008)
+        assert f(ctypes.byref(c), *bad, need, None) == tk.EINVAL, i
+    assert f(ctypes.byref(c), *args, need - 1, None) == tk.EWORKSPACE
+    assert f(ctypes.byref(fake_cache(head_dim=96)), *args, 1 << 30, None) == tk.EUNSUPPORTED
+    assert f(ctypes.byref(fake_cache(nulls=("k",))), *args, 1 << 30, None) == tk.EINVAL
 
 
 def test_compact_inplace_argument_checks():

@@ -1,0 +1,202 @@
+"""The streaming step's fused calls against the separate calls they replace,
+bit for bit, and against the oracle: trimkv_append_score_select (the step's
+append written by the selection's first kernel) must leave the cache, the
+score plane and the selection exactly as trimkv_append followed by
+trimkv_score_select (TRIM-KV page, section 2: a new entry per head with its
+retention, then the lowest current scores are evicted once the budget is
+exceeded)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import reference as ref
+from retention_scored_decode_amd import trimkv as tk
+from gpu_helpers import OracleView, cuda, download_cache, f32_bits, heads_from_plane, kv_dev, upload
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def announce(*a):
+    print("[case]", *a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    tk.lib()
+
+
+def clone_cache(c: tk.Cache) -> tk.Cache:
+    return tk.Cache(c.k.clone(), c.v.clone(), c.meta.clone(), c.page_off.clone(), c.page_ids.clone(),
+                    c.length.clone())
+
+
+def same_cache(a: tk.Cache, b: tk.Cache):
+    for x, y in zip(download_cache(a), download_cache(b)):
+        assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8))
+
+
+def step_pair(ca, cb, kn, vn, beta, seg, t_dev, bud, dtype, keptsum=False):
+    """The separate calls on ca, the fused call on cb; returns both outputs."""
+    H = ca.n_heads
+    n = ca.n_pages * 16
+    outs = []
+    for fused, c in ((False, ca), (True, cb)):
+        score = torch.full((n,), 7.0, dtype=torch.float32, device="cuda")
+        keep = torch.full((n,), 9, dtype=torch.uint8, device="cuda")
+        kept = torch.empty(H, dtype=torch.int32, device="cuda")
+        ks = torch.empty(H, dtype=torch.float64, device="cuda") if keptsum else None
+        status = torch.zeros(2, dtype=torch.int32, device="cuda")
+        if fused:
+            tk.append_score_select(c, kv_dev(kn, dtype), kv_dev(vn, dtype), cuda(beta, np.float32), seg, t_dev,
+                                   bud, score, keep, kept, keptsum=ks, append_status=status[0:1],
+                                   select_status=status[1:2])
+        else:
+            tk.append(c, kv_dev(kn, dtype), kv_dev(vn, dtype), cuda(beta, np.float32), t_dev[0:1], status=status[0:1])
+            tk.score_select(c, seg, t_dev, bud, score, keep, kept, keptsum=ks, status=status[1:2])
+        torch.cuda.synchronize()
+        outs.append(dict(score=score.cpu().numpy(), keep=keep.cpu().numpy(), kept=kept.cpu().numpy(),
+                         ks=None if ks is None else ks.cpu().numpy(), status=status.cpu().numpy()))
+    a, b = outs
+    assert np.array_equal(f32_bits(a["score"]), f32_bits(b["score"]))
+    assert np.array_equal(a["keep"], b["keep"]) and np.array_equal(a["kept"], b["kept"])
+    if keptsum:
+        assert np.array_equal(a["ks"].view(np.uint64), b["ks"].view(np.uint64))
+    assert np.array_equal(a["status"], b["status"])
+    same_cache(ca, cb)
+    return a
+
+
+def test_append_score_select_matches_separate_calls():
+    """Scaled streaming cache (one spare slot per head): four generated steps,
+    each followed by tail-filled eviction of both caches; the fused call's
+    cache, scores, keep plane, kept counts and kept sums equal the separate
+    calls' bit for bit, and the selection equals the oracle's."""
+    w = W["stream_gqa7"].scaled(layers=2, ctx=2000, budget_abs=1024, steps=4)
+    pc = synth.build_cache(w)
+    ov = OracleView(pc)
+    H, D = pc.n_heads, w.head_dim
+    M = w.budget()
+    ca = upload(pc)
+    cb = clone_cache(ca)
+    home_off, home_ids = ca.page_off.clone(), ca.page_ids.clone()
+    tables = {n: [(torch.zeros_like(home_off), torch.zeros_like(home_ids)) for _ in range(2)] for n in "ab"}
+    seg = cuda(np.array([0, H], np.int32))
+    bud = cuda(np.array([M], np.int64))
+    lnb, pos = ov.lnb, ov.pos
+    for s in range(1, w.steps + 1):
+        t = w.ctx + s
+        announce("append+score+select, stream step", s)
+        beta, kn, vn, _ = synth.stream_step(w, s)
+        out = step_pair(ca, cb, kn, vn, beta, seg, cuda(np.array([t], np.int32)), bud, "bf16", keptsum=True)
+        assert out["status"].tolist() == [0, 0]
+        # oracle: append, score, select over the slot-ordered state
+        lnb_new = ref.ln_beta(beta)
+        lnb = [np.append(lnb[h], lnb_new[h]) for h in range(H)]
+        pos = [np.append(pos[h], np.int32(t - 1)) for h in range(H)]
+        scores = [ref.score_f32(lnb[h], t, pos[h]) for h in range(H)]
+        wkeep, wkept = ref.select_global(scores, [0, H], [M], positions=pos)
+        assert np.array_equal(out["kept"], wkept), s
+        po, ln = ca.page_off.cpu().numpy(), ca.length.cpu().numpy()
+        got = heads_from_plane(out["keep"], po, ln)
+        for h in range(H):
+            assert np.array_equal(got[h].astype(bool), wkeep[h]), (s, h)
+            assert np.array_equal(f32_bits(heads_from_plane(out["score"], po, ln)[h]), f32_bits(scores[h])), (s, h)
+        kept_dev = cuda(out["kept"], np.int32)
+        keep = cuda(out["keep"], np.uint8)
+        ca = tk.evict_tailfill(ca, keep, 1, home_off, home_ids, *tables["a"][s % 2], kept=kept_dev)
+        cb = tk.evict_tailfill(cb, keep, 1, home_off, home_ids, *tables["b"][s % 2], kept=kept_dev)
+        order, _ = ref.evict_tailfill_order(wkeep, 1, home_off.cpu().numpy().astype(np.int64),
+                                            home_ids.cpu().numpy().astype(np.int64))
+        lnb = [lnb[h][order[h]] for h in range(H)]
+        pos = [pos[h][order[h]] for h in range(H)]
+        same_cache(ca, cb)
+
+
+def test_append_score_select_full_heads_and_segments():
+    """Heads without a free slot are left unchanged and counted, as
+    trimkv_append does; with several segments every head's new entry takes
+    its own segment's step (position t_s - 1) and is scored at it."""
+    w = W["stream_gqa7"].scaled(batch=3, layers=2, ctx=300, per_seq_segments=True, reserve=0)
+    H = w.n_heads
+    rng = np.random.default_rng(11)
+    lengths = rng.integers(250, 301, H).astype(np.int32)
+    lengths[::3] = 288                               # 18 full pages, no free slot
+    pc = synth.build_cache(w, lengths=lengths)
+    full = (lengths % 16) == 0
+    ov = OracleView(pc)
+    ca = upload(pc)
+    cb = clone_cache(ca)
+    segs = w.seg_head_begin()
+    t = np.array([400, 333, 512], np.int32)
+    M = 500
+    beta = rng.uniform(0.0, 1.0, H).astype(np.float32)
+    beta[:4] = [0.0, 1.0, 2 ** -149, 0.5]
+    kn = synth.f64_to_bf16_bits(rng.standard_normal((H, w.head_dim)))
+    vn = synth.f64_to_bf16_bits(rng.standard_normal((H, w.head_dim)))
+    n = ca.n_pages * 16
+    score = torch.empty(n, dtype=torch.float32, device="cuda")
+    keep = torch.empty(n, dtype=torch.uint8, device="cuda")
+    kept = torch.empty(H, dtype=torch.int32, device="cuda")
+    status = torch.zeros(2, dtype=torch.int32, device="cuda")
+    announce("append+score+select, 3 segments, full heads", int(full.sum()))
+    tk.append_score_select(cb, kv_dev(kn, "bf16"), kv_dev(vn, "bf16"), cuda(beta), cuda(segs), cuda(t),
+                           cuda(np.full(3, M, np.int64)), score, keep, kept, append_status=status[0:1],
+                           select_status=status[1:2])
+    torch.cuda.synchronize()
+    assert status.cpu().numpy().tolist() == [int(full.sum()), 0]
+    seg_of = np.searchsorted(segs, np.arange(H), side="right") - 1
+    lnb_new = ref.ln_beta(beta)
+    lnb, pos, kr, vr = ov.lnb, ov.pos, ov.k_raw, ov.v_raw
+    for h in range(H):
+        if not full[h]:
+            lnb[h] = np.append(lnb[h], lnb_new[h])
+            pos[h] = np.append(pos[h], np.int32(t[seg_of[h]] - 1))
+            kr[h] = np.concatenate([kr[h], kn[h:h + 1]])
+            vr[h] = np.concatenate([vr[h], vn[h:h + 1]])
+    po, pi, ln, k, v, glnb, gpos = download_cache(cb)
+    assert np.array_equal(ln, lengths + (~full))
+    for h in range(H):
+        assert np.array_equal(ref.gather_heads(gpos, po, pi, ln)[h], pos[h]), h
+        assert np.array_equal(f32_bits(ref.gather_heads(glnb, po, pi, ln)[h]), f32_bits(lnb[h])), h
+        assert np.array_equal(ref.gather_heads(k, po, pi, ln)[h], kr[h]), h
+        assert np.array_equal(ref.gather_heads(v, po, pi, ln)[h], vr[h]), h
+    scores = [ref.score_f32(lnb[h], int(t[seg_of[h]]), pos[h]) for h in range(H)]
+    got_s = heads_from_plane(score.cpu().numpy(), po, ln)
+    for h in range(H):
+        assert np.array_equal(f32_bits(got_s[h]), f32_bits(scores[h])), h
+    wkeep, wkept = ref.select_global(scores, segs, [M] * 3, positions=pos)
+    assert np.array_equal(kept.cpu().numpy(), wkept)
+    got = heads_from_plane(keep.cpu().numpy(), po, ln)
+    for h in range(H):
+        assert np.array_equal(got[h].astype(bool), wkeep[h]), h
+    # one segment per call with the same step everywhere: the separate calls agree
+    w1 = w.scaled(per_seq_segments=False)
+    cc = upload(pc)
+    cd = clone_cache(cc)
+    step_pair(cc, cd, kn, vn, beta, cuda(np.array([0, H], np.int32)), cuda(np.array([400], np.int32)),
+              cuda(np.array([w1.budget() // 2], np.int64)), "bf16")
+
+
+def test_append_score_select_many_heads():
+    """More heads than the selection's LDS head list (4,096): the first
+    kernel then runs as one block and raises the lengths itself; fp32 cache,
+    D = 64."""
+    w = W["tiny"].scaled(layers=2100, kv_heads=2, ctx=40, reserve=1, budget_abs=60000)
+    H = w.n_heads
+    assert H > 4096
+    pc = synth.build_cache(w)
+    ca = upload(pc)
+    cb = clone_cache(ca)
+    rng = np.random.default_rng(5)
+    beta = rng.beta(5.0, 1.0, H).astype(np.float32)
+    kn = rng.standard_normal((H, w.head_dim)).astype(np.float32)
+    vn = rng.standard_normal((H, w.head_dim)).astype(np.float32)
+    announce("append+score+select, heads", H)
+    out = step_pair(ca, cb, kn, vn, beta, cuda(np.array([0, H], np.int32)), cuda(np.array([w.ctx + 1], np.int32)),
+                    cuda(np.array([w.budget()], np.int64)), "f32")
+    assert out["status"].tolist() == [0, 0]
+    assert np.array_equal(ca.length.cpu().numpy(), pc.length + 1)
