@@ -97,7 +97,8 @@ enum {
   TRIMKV_OP_VALIDATE = 5,
   TRIMKV_OP_DECODE_ERR = 6,
   TRIMKV_OP_COMPACT_INPLACE = 7,
-  TRIMKV_OP_EVICT_TAILFILL = 8
+  TRIMKV_OP_EVICT_TAILFILL = 8,
+  TRIMKV_OP_DECODE_EVICT = 9
 };
 
 /*
@@ -290,6 +291,30 @@ int trimkv_compact_inplace(trimkv_cache_t* cache, const uint8_t* keep, const int
 int trimkv_evict_tailfill(trimkv_cache_t* cache, const uint8_t* keep, const int32_t* kept, int32_t reserve,
                           const int32_t* home_off, const int32_t* home_ids, int32_t* new_page_off,
                           int32_t* new_page_ids, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * trimkv_decode_attn_evict_tailfill -- an eviction step's attention and
+ * its in-place eviction in one call, for streaming decode: mask-mode
+ * trimkv_decode_attn over the cache as it is, then trimkv_evict_tailfill of
+ * the same keep plane, with the attention's merge and the eviction in one
+ * launch after the attention's main kernel (neither waits for the other).
+ * ContourKV page, problem definition and section 3 (renormalised output
+ * over the kept set, dropped mass); DBTrimKV page, Method 4 and ContourKV
+ * page, section 2 (the eviction).
+ * Outputs (out, dropped, the cache's rows, len and the new table) are bit
+ * for bit those of the two calls.
+ *   keep, q, group, scale, out, dropped: as trimkv_decode_attn (mask mode)
+ *   kept:    device int32 [n_heads], the selection's counts (required)
+ *   reserve, home_off, home_ids, new_page_off, new_page_ids: as
+ *            trimkv_evict_tailfill
+ *   ws: trimkv_workspace_size(TRIMKV_OP_DECODE_EVICT, cache, 0, group) bytes
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE.
+ */
+int trimkv_decode_attn_evict_tailfill(trimkv_cache_t* cache, const uint8_t* keep, const int32_t* kept,
+                                      const void* q, int32_t group, float scale, float* out, float* dropped,
+                                      int32_t reserve, const int32_t* home_off, const int32_t* home_ids,
+                                      int32_t* new_page_off, int32_t* new_page_ids, void* ws, size_t ws_bytes,
+                                      void* stream);
 
 /*
  * trimkv_decode_attn -- renormalised GQA decode attention with dropped mass.

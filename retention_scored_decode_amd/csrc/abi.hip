@@ -131,6 +131,7 @@ size_t trimkv_workspace_size(int op, const trimkv_cache_t* c, int32_t n_seg, int
     case TRIMKV_OP_DECODE_ERR: return (group >= 1 && group <= 16) ? err_ws_layout(c, group).total : 0;
     case TRIMKV_OP_COMPACT_INPLACE: return (size_t)c->n_heads * 4 + 256;
     case TRIMKV_OP_EVICT_TAILFILL: return tailfill_ws_layout(c).total;
+    case TRIMKV_OP_DECODE_EVICT: return (group >= 1 && group <= 16) ? attn_evict_ws_layout(c, group).total : 0;
     default: return 0;
   }
 }
@@ -250,6 +251,27 @@ int trimkv_evict_tailfill(trimkv_cache_t* c, const uint8_t* keep, const int32_t*
   if (c->n_heads == 0) return TRIMKV_OK;
   return launch_evict_tailfill(c, keep, kept, reserve, home_off, home_ids, new_page_off, new_page_ids, ws,
                                S(stream));
+}
+
+int trimkv_decode_attn_evict_tailfill(trimkv_cache_t* c, const uint8_t* keep, const int32_t* kept, const void* q,
+                                      int32_t group, float scale, float* out, float* dropped, int32_t reserve,
+                                      const int32_t* home_off, const int32_t* home_ids, int32_t* new_page_off,
+                                      int32_t* new_page_ids, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if (!cache_shape_ok(c, &rc)) return rc;
+  if (group < 1 || group > 16) return TRIMKV_EUNSUPPORTED;
+  if (!keep || !kept || !q || !out || !dropped || reserve < 0 || !home_off || !home_ids || !new_page_off ||
+      !new_page_ids || !table_ok(c) || !pools_ok(c) || ((uintptr_t)keep & 15))
+    return TRIMKV_EINVAL;
+  // the new table is written while the current one is still read
+  if (new_page_off == c->page_off || new_page_ids == c->page_ids || new_page_off == home_off ||
+      new_page_ids == home_ids)
+    return TRIMKV_EINVAL;
+  if (c->n_pages * PAGE > (int64_t)UINT32_MAX) return TRIMKV_EUNSUPPORTED;
+  if ((rc = ws_check(ws, ws_bytes, attn_evict_ws_layout(c, group).total))) return rc;
+  if (c->n_heads == 0) return TRIMKV_OK;
+  return launch_decode_attn_evict_tailfill(c, keep, kept, q, group, scale, out, dropped, reserve, home_off, home_ids,
+                                           new_page_off, new_page_ids, ws, S(stream));
 }
 
 int trimkv_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float* lse_ref, const void* q,

@@ -25,6 +25,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "tailfill.h"
 
 // Scratch of trimkv_decode_attn_noalloc: the partials of the flat split (or
 // the fp32 work list) live here instead of in a caller's workspace.  Each
@@ -262,13 +263,11 @@ __device__ void merge_row(const AttnArgs& a, int h, int g, int b, int e, int add
   }
 }
 
-// Merge kernel: one wave per query row, over the partials the main kernel
-// left in the workspace.
+// Query row `row` of the merge (wave-uniform); rows past the last return.
 template <int D>
-__global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
+__device__ void merge_query_row(const AttnArgs& a, int row, int with_out) {
   const AttnWs& w = a.w;
   const int G = a.group;
-  const int row = blockIdx.x * (NT / WAVE) + __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
   if (row >= a.n_heads * G) return;   // per-wave exit: no block barriers below
   const int h = row / G, g = row % G;
   int b, e, add;
@@ -287,6 +286,29 @@ __global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
   // at least as many pages as waves every range is nonempty (no divisions)
   const bool every = !a.waves || P >= a.waves;
   merge_row<D>(a, h, g, b, e, add, every, P, with_out);
+}
+
+// Merge kernel: one wave per query row, over the partials the main kernel
+// left in the workspace.
+template <int D>
+__global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
+  merge_query_row<D>(a, blockIdx.x * (NT / WAVE) + __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), with_out);
+}
+
+// The merge beside a tail-filled eviction of the same cache, in one launch:
+// neither reads what the other writes (the merge reads the partials and the
+// page offsets, the eviction the keep plane and the rows, and writes rows,
+// lengths and a new table), and both wait only for the main kernel.  Blocks
+// [0, merge_blocks) merge, one wave per query row; each later block evicts
+// one head.
+template <int D, int ROWB>
+__global__ void __launch_bounds__(tf::NT) k_attn_merge_evict(AttnArgs a, tf::Args t, int merge_blocks) {
+  __shared__ tf::LDS L;
+  if ((int)blockIdx.x < merge_blocks) {   // block-uniform
+    merge_query_row<D>(a, blockIdx.x * (tf::NT / WAVE) + __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), 1);
+    return;
+  }
+  tf::evict_head<ROWB>(blockIdx.x - merge_blocks, t, L);
 }
 
 // s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n only
@@ -1013,6 +1035,46 @@ int launch_decode_attn(const trimkv_cache_t* c, const uint8_t* keep, const float
                        int group, float scale, float* out, float* dropped, float* lse_out, void* ws,
                        hipStream_t st) {
   return decode_attn_on(c, keep, lse_ref, q, group, scale, out, dropped, lse_out, ws, -1, st);
+}
+
+WsLayout attn_evict_ws_layout(const trimkv_cache_t* c, int group) {
+  WsLayout L = attn_ws_layout(c, group);
+  L.add(c->n_pages * PAGE * 4);   // the eviction's hole lists (a word per CSR slot)
+  return L;
+}
+
+int launch_decode_attn_evict_tailfill(trimkv_cache_t* c, const uint8_t* keep, const int32_t* kept, const void* q,
+                                      int group, float scale, float* out, float* dropped, int reserve,
+                                      const int32_t* home_off, const int32_t* home_ids, int32_t* new_off,
+                                      int32_t* new_ids, void* ws, hipStream_t st) {
+  const int elt = c->dtype == TRIMKV_BF16 ? 2 : 4;
+  const int rowb = c->head_dim * elt;
+  if (rowb != 128 && rowb != 256 && rowb != 512) return TRIMKV_EUNSUPPORTED;
+  AttnWs w = carve(c, group, ws, false, false);
+  const WsLayout L = attn_evict_ws_layout(c, group);
+  uint32_t* holes = (uint32_t*)((char*)ws + L.off[4]);
+  if (c->dtype == TRIMKV_F32)
+    hipLaunchKernelGGL(k_attn_prep, dim3(prep_grid(c->n_heads, max_chunks(c, CHA_F32), 2048)), dim3(1024), 0, st,
+                       c->page_off, c->len, c->n_heads, CHA_F32, w);
+  AttnArgs a{c->page_off, c->page_ids, c->len, c->k, c->v, keep, q, c->n_heads, group, scale * LOG2E,
+             c->n_pages * PAGE, CHA_F32, 0, w, nullptr, out, dropped, nullptr};
+  prof_begin(st);
+  const int rc = launch_main<A_MASK>(c, a, st);
+  prof_end(st);
+  if (rc) return rc;
+  const tf::Args t{c->n_heads, reserve, c->page_off, c->page_ids, c->len, keep, kept, home_off, home_ids, new_off,
+                   new_ids, (uint8_t*)c->k, (uint8_t*)c->v, c->meta, holes};
+  const int rows_per_block = tf::NT / WAVE;
+  const int mb = (int)(((int64_t)c->n_heads * group + rows_per_block - 1) / rows_per_block);
+  const dim3 grid((unsigned)(mb + c->n_heads)), blk(tf::NT);
+  if (c->head_dim == 128) {
+    if (rowb == 256) hipLaunchKernelGGL((k_attn_merge_evict<128, 256>), grid, blk, 0, st, a, t, mb);
+    else hipLaunchKernelGGL((k_attn_merge_evict<128, 512>), grid, blk, 0, st, a, t, mb);
+  } else {
+    if (rowb == 128) hipLaunchKernelGGL((k_attn_merge_evict<64, 128>), grid, blk, 0, st, a, t, mb);
+    else hipLaunchKernelGGL((k_attn_merge_evict<64, 256>), grid, blk, 0, st, a, t, mb);
+  }
+  return check_launch();
 }
 
 int64_t noalloc_min_bytes(const trimkv_cache_t* c, int group) {

@@ -21,6 +21,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "tailfill.h"
 
 namespace trimkv {
 
@@ -364,112 +365,11 @@ __global__ void __launch_bounds__(NTP) k_cmp_shift(int n_heads, int reserve, con
   if (tid == 0) len[h] = (int32_t)min((int64_t)carry, nh * PAGE);
 }
 
-// ---------------------------------------------------------------------------
-// Tail-filled eviction in place: head h keeps its kept entries in its first
-// kept_h slots; the dropped entries among those slots (holes) take, one each,
-// the kept entries from slot kept_h on (movers), both counted in slot order,
-// and every other entry stays where it is.  Only as many rows move as there
-// are holes, at most the head's drops, so a streaming step that drops a few
-// entries per head moves a few rows.  Holes lie below kept_h and movers at
-// or above it, so no move reads a row that another move writes.  Slot order
-// then no longer follows position order (selection ranks ties by position,
-// so it is unaffected; attention is order-free).
-//
-// One block per head: a first walk over the head's first kept_h slots ranks
-// its holes (block scan per window of 4 NTP slots, 4 per thread) and lists their physical
-// slots in the workspace at the head's CSR offset; a second walk over the
-// rest ranks the movers, and mover r moves to hole r (LPR lanes of 16 bytes
-// per row).  Counts that disagree with the keep plane move only
-// min(holes, movers) rows.
+// In-place eviction by tail fill: one block per head (tailfill.h).
 template <int ROWB>
-__global__ void __launch_bounds__(NTP) k_cmp_tailfill(int n_heads, int reserve, const int32_t* __restrict__ page_off,
-                                                      const int32_t* __restrict__ page_ids,
-                                                      int32_t* __restrict__ len, const uint8_t* __restrict__ keep,
-                                                      const int32_t* __restrict__ head_kept,
-                                                      const int32_t* __restrict__ home_off,
-                                                      const int32_t* __restrict__ home_ids,
-                                                      int32_t* __restrict__ new_off, int32_t* __restrict__ new_ids,
-                                                      uint8_t* __restrict__ pk, uint8_t* __restrict__ pv,
-                                                      uint32_t* __restrict__ meta, uint32_t* __restrict__ holes) {
-  constexpr int LPR = ROWB / 16;          // lanes per row
-  constexpr int GROUPS = NTP / LPR;       // rows moved at once by the block
-  __shared__ uint32_t s_src[4 * NTP], s_dst[4 * NTP];   // a window's movers (4 slots per thread)
-  __shared__ int64_t red[NWP + 1];
-  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & (WAVE - 1), wid = tid / WAVE;
-  auto pages_of = [&](int j) -> int64_t {
-    const int64_t want = ((int64_t)max(head_kept[j], 0) + reserve + PAGE - 1) / PAGE;
-    return min(want, (int64_t)home_off[j + 1] - home_off[j]);
-  };
-  // the new page list: a prefix sum over the earlier heads, then the head's home prefix
-  int64_t pb = 0;
-  for (int j = tid; j < h; j += NTP) pb += pages_of(j);
-  pb = wave_sum(pb);
-  if (lane == 0) red[wid] = pb;
-  lds_barrier();
-  pb = 0;
-#pragma unroll
-  for (int i = 0; i < NWP; ++i) pb += red[i];
-  const int64_t nh = pages_of(h);
-  const int64_t hb = home_off[h];
-  for (int64_t c = tid; c < nh; c += NTP) new_ids[pb + c] = home_ids[hb + c];
-  if (tid == 0) {
-    new_off[h] = (int32_t)pb;
-    if (h == n_heads - 1) new_off[n_heads] = (int32_t)(pb + nh);
-  }
-  lds_barrier();   // red is the scans' scratch below
-
-  int p0;
-  const int nv = head_valid(page_off, len, h, &p0);
-  const int kh = min(max(head_kept[h], 0), nv);
-  uint32_t* const hl = holes + (int64_t)p0 * PAGE;   // this head's hole list (its CSR slots)
-  auto phys = [&](int i) -> uint32_t { return (uint32_t)page_ids[p0 + i / PAGE] * PAGE + i % PAGE; };
-  // 1. holes: dropped slots below kh, in slot order (4 consecutive slots
-  //    per thread: one 4-byte keep load, one block scan per 4,096 slots)
-  const uint8_t* kh_bytes = keep + (int64_t)p0 * PAGE;   // the head's keep bytes, in slot order
-  int n_holes = 0;
-  for (int s0 = 0; s0 < kh; s0 += 4 * NTP) {
-    const int i = s0 + 4 * tid;   // a multiple of 4: its 4 bytes lie in one page
-    const uint32_t kb = i < kh ? *reinterpret_cast<const uint32_t*>(kh_bytes + i) : ~0u;
-    uint32_t bits = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bits |= (uint32_t)(i + j < kh && ((kb >> (8 * j)) & 0xFFu) == 0) << j;
-    int64_t tot;
-    int r = (int)block_exclusive_scan<NTP>(__popc(bits), red, &tot);
-    for (uint32_t b = bits; b; b &= b - 1) hl[n_holes + r++] = phys(i + __builtin_ctz(b));
-    n_holes += __builtin_amdgcn_readfirstlane((int)tot);   // block-uniform: the loop below stays uniform
-  }
-  __syncthreads();   // the hole list (global memory) is complete and visible to the block
-  // 2. movers: kept slots from kh on; mover r takes hole r
-  int n_movers = 0;
-  for (int s0 = kh & ~3; s0 < nv && n_movers < n_holes; s0 += 4 * NTP) {
-    const int i = s0 + 4 * tid;
-    const uint32_t kb = i < nv ? *reinterpret_cast<const uint32_t*>(kh_bytes + i) : 0u;
-    uint32_t bits = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      bits |= (uint32_t)(i + j >= kh && i + j < nv && ((kb >> (8 * j)) & 0xFFu) != 0) << j;
-    int64_t tot;
-    int r = (int)block_exclusive_scan<NTP>(__popc(bits), red, &tot);
-    const int n_here = min(__builtin_amdgcn_readfirstlane((int)tot), n_holes - n_movers);
-    for (uint32_t b = bits; b && r < n_here; b &= b - 1, ++r) {
-      s_src[r] = phys(i + __builtin_ctz(b));
-      s_dst[r] = hl[n_movers + r];
-    }
-    lds_barrier();
-    const int part = tid % LPR;
-    for (int q = tid / LPR; q < n_here; q += GROUPS) {
-      const int64_t s = s_src[q], d = s_dst[q];
-      const u32x4 kv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pk + s * ROWB + part * 16));
-      const u32x4 vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pv + s * ROWB + part * 16));
-      const uint32_t mv = meta[(s / PAGE) * (2 * PAGE) + (part & 1) * PAGE + s % PAGE];
-      __builtin_nontemporal_store(kv, reinterpret_cast<u32x4*>(pk + d * ROWB + part * 16));
-      __builtin_nontemporal_store(vv, reinterpret_cast<u32x4*>(pv + d * ROWB + part * 16));
-      if (part < 2) meta[(d / PAGE) * (2 * PAGE) + part * PAGE + d % PAGE] = mv;
-    }
-    n_movers += n_here;
-    lds_barrier();   // s_src and s_dst are rewritten by the next window
-  }
-  if (tid == 0) len[h] = (int32_t)min((int64_t)kh, nh * PAGE);
+__global__ void __launch_bounds__(tf::NT) k_cmp_tailfill(tf::Args a) {
+  __shared__ tf::LDS L;
+  tf::evict_head<ROWB>(blockIdx.x, a, L);
 }
 
 CmpWs carve(const trimkv_cache_t* c, void* ws) {
@@ -538,10 +438,9 @@ int launch_evict_tailfill(trimkv_cache_t* c, const uint8_t* keep, const int32_t*
     hipLaunchKernelGGL(k_cmp_count, dim3(H), dim3(NTP), 0, st, c->page_off, c->len, keep, w);
   }
   const int elt = c->dtype == TRIMKV_BF16 ? 2 : 4;
-#define TRIMKV_TAILFILL(RB)                                                                                        \
-  hipLaunchKernelGGL(k_cmp_tailfill<RB>, dim3(H), dim3(NTP), 0, st, H, reserve, c->page_off, c->page_ids, c->len, \
-                     keep, w.head_kept, home_off, home_ids, new_off, new_ids, (uint8_t*)c->k, (uint8_t*)c->v,      \
-                     c->meta, holes)
+  const tf::Args ta{H, reserve, c->page_off, c->page_ids, c->len, keep, w.head_kept, home_off, home_ids, new_off,
+                    new_ids, (uint8_t*)c->k, (uint8_t*)c->v, c->meta, holes};
+#define TRIMKV_TAILFILL(RB) hipLaunchKernelGGL(k_cmp_tailfill<RB>, dim3(H), dim3(tf::NT), 0, st, ta)
   prof_begin(st);
   switch (c->head_dim * elt) {
     case 128: TRIMKV_TAILFILL(128); break;

@@ -36,6 +36,7 @@ WsLayout err_ws_layout(const trimkv_cache_t* c, int group);
 WsLayout compact_ws_layout(const trimkv_cache_t* c);
 WsLayout tailfill_ws_layout(const trimkv_cache_t* c);
 WsLayout attn_ws_layout(const trimkv_cache_t* c, int group, int64_t slots = -1);
+WsLayout attn_evict_ws_layout(const trimkv_cache_t* c, int group);
 WsLayout mass_ws_layout(const trimkv_cache_t* c, int group);
 
 int launch_log_beta(const float* beta, float* lnb, int64_t n, int out_page_stride, hipStream_t st);
@@ -58,6 +59,10 @@ int launch_compact(const trimkv_cache_t* src, const uint8_t* keep, const int32_t
 int launch_compact_inplace(trimkv_cache_t* c, const uint8_t* keep, const int32_t* kept, int reserve,
                            const int32_t* home_off, const int32_t* home_ids, int32_t* new_off, int32_t* new_ids,
                            void* ws, hipStream_t st);
+int launch_decode_attn_evict_tailfill(trimkv_cache_t* c, const uint8_t* keep, const int32_t* kept, const void* q,
+                                      int group, float scale, float* out, float* dropped, int reserve,
+                                      const int32_t* home_off, const int32_t* home_ids, int32_t* new_off,
+                                      int32_t* new_ids, void* ws, hipStream_t st);
 int launch_evict_tailfill(trimkv_cache_t* c, const uint8_t* keep, const int32_t* kept, int reserve,
                           const int32_t* home_off, const int32_t* home_ids, int32_t* new_off, int32_t* new_ids,
                           void* ws, hipStream_t st);

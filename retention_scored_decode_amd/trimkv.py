@@ -19,11 +19,12 @@ PAGE = 16
 F32, BF16 = 0, 1
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ECAPACITY, EHIP, EINVARIANT = 0, -1, -2, -3, -4, -5, -6
 (OP_SCORE, OP_SELECT, OP_COMPACT, OP_DECODE_ATTN, OP_ATTN_MASS, OP_VALIDATE, OP_DECODE_ERR, OP_COMPACT_INPLACE,
- OP_EVICT_TAILFILL) = range(9)
+ OP_EVICT_TAILFILL, OP_DECODE_EVICT) = range(10)
 
 EXPORTS = ["trimkv_log_beta", "trimkv_score", "trimkv_select_global", "trimkv_compact",
            "trimkv_decode_attn", "trimkv_decode_attn_gated", "trimkv_decode_attn_err", "trimkv_attn_mass",
            "trimkv_decode_attn_noalloc", "trimkv_score_select", "trimkv_append_score_select", "trimkv_evict_tailfill",
+           "trimkv_decode_attn_evict_tailfill",
            "trimkv_allocate", "trimkv_compact_inplace",
            "trimkv_allocate_floor", "trimkv_mark_recent", "trimkv_append",
            "trimkv_workspace_size", "trimkv_validate_cache", "trimkv_strerror", "trimkv_profile_next"]
@@ -63,6 +64,8 @@ def lib():
             "trimkv_append_score_select": [cp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_compact_inplace": [cp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp],
             "trimkv_evict_tailfill": [cp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp],
+            "trimkv_decode_attn_evict_tailfill": [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, i32, vp, vp, vp, vp,
+                                                  vp, sz, vp],
             "trimkv_decode_attn": [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp],
             "trimkv_decode_attn_noalloc": [cp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp],
             "trimkv_decode_attn_err": [cp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp],
@@ -261,6 +264,22 @@ def evict_tailfill(cache: Cache, keep: torch.Tensor, reserve: int, home_off: tor
     _check(lib().trimkv_evict_tailfill(ctypes.byref(cache.struct()), _p(keep), _p(kept), int(reserve),
                                        _p(home_off), _p(home_ids), _p(new_page_off), _p(new_page_ids),
                                        _p(ws), ws.numel(), _stream(stream)), "trimkv_evict_tailfill")
+    return Cache(cache.k, cache.v, cache.meta, new_page_off, new_page_ids, cache.length)
+
+
+def decode_attn_evict_tailfill(cache: Cache, keep: torch.Tensor, kept: torch.Tensor, q: torch.Tensor, group: int,
+                               scale: float, out: torch.Tensor, dropped: torch.Tensor, reserve: int,
+                               home_off: torch.Tensor, home_ids: torch.Tensor, new_page_off: torch.Tensor,
+                               new_page_ids: torch.Tensor, ws: Optional[torch.Tensor] = None, stream=None) -> Cache:
+    """Mask-mode decode_attn(), then evict_tailfill() of the same keep plane,
+    the merge and the eviction in one launch; returns the new view."""
+    if ws is None:
+        ws = workspace(OP_DECODE_EVICT, cache, 0, group)
+    _check(lib().trimkv_decode_attn_evict_tailfill(ctypes.byref(cache.struct()), _p(keep), _p(kept), _p(q), int(group),
+                                                   ctypes.c_float(scale), _p(out), _p(dropped), int(reserve),
+                                                   _p(home_off), _p(home_ids), _p(new_page_off), _p(new_page_ids),
+                                                   _p(ws), ws.numel(), _stream(stream)),
+           "trimkv_decode_attn_evict_tailfill")
     return Cache(cache.k, cache.v, cache.meta, new_page_off, new_page_ids, cache.length)
 
 

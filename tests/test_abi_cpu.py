@@ -18,7 +18,7 @@ def declared():
 
 def test_exports_every_declared_symbol():
     names = declared()
-    assert len(names) == 21
+    assert len(names) == 22
     L = tk.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -137,6 +137,40 @@ def test_append_score_select_argument_checks():
     assert f(ctypes.byref(c), *args, need - 1, None) == tk.EWORKSPACE
     assert f(ctypes.byref(fake_cache(head_dim=96)), *args, 1 << 30, None) == tk.EUNSUPPORTED
     assert f(ctypes.byref(fake_cache(nulls=("k",))), *args, 1 << 30, None) == tk.EINVAL
+
+
+def test_decode_attn_evict_tailfill_argument_checks():
+    """trimkv_decode_attn_evict_tailfill: mask mode (keep and kept required),
+    the eviction's table rules, its own workspace (the decode workspace plus
+    the hole lists)."""
+    L = tk.lib()
+    c = fake_cache()
+    F = ctypes.c_float(1.0)
+    need = L.trimkv_workspace_size(tk.OP_DECODE_EVICT, ctypes.byref(c), 0, 4)
+    assert need > L.trimkv_workspace_size(tk.OP_DECODE_ATTN, ctypes.byref(c), 0, 4)
+    f = L.trimkv_decode_attn_evict_tailfill
+    A, B, C, D = (ctypes.c_void_p(x) for x in (0x21000, 0x22000, 0x23000, 0x24000))
+    args = [X, X, X, 4, F, X, X, 1, A, B, C, D, X]
+    assert f(ctypes.byref(c), *args[:12], X, need - 1, None) == tk.EWORKSPACE
+    for i in (0, 1, 2, 5, 6, 8, 9, 10, 11):
+        bad = list(args)
+        bad[i] = None
+        assert f(ctypes.byref(c), *bad, need, None) == tk.EINVAL, i
+    bad = list(args)
+    bad[7] = -1
+    assert f(ctypes.byref(c), *bad, need, None) == tk.EINVAL
+    for i, alias in ((10, 0x5000), (11, 0x6000), (10, 0x21000), (11, 0x22000)):   # the new table aliases
+        bad = list(args)
+        bad[i] = ctypes.c_void_p(alias)
+        assert f(ctypes.byref(c), *bad, need, None) == tk.EINVAL, (i, alias)
+    bad = list(args)
+    bad[0] = ctypes.c_void_p(0x10008)   # keep: 16-byte aligned
+    assert f(ctypes.byref(c), *bad, need, None) == tk.EINVAL
+    bad = list(args)
+    bad[3] = 17
+    assert f(ctypes.byref(c), *bad, need, None) == tk.EUNSUPPORTED
+    huge = fake_cache(n_pages=1 << 28)
+    assert f(ctypes.byref(huge), *args, 1 << 40, None) == tk.EUNSUPPORTED
 
 
 def test_compact_inplace_argument_checks():

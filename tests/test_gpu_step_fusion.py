@@ -200,3 +200,93 @@ def test_append_score_select_many_heads():
                     cuda(np.array([w.budget()], np.int64)), "f32")
     assert out["status"].tolist() == [0, 0]
     assert np.array_equal(ca.length.cpu().numpy(), pc.length + 1)
+
+
+@pytest.mark.parametrize("shape", ["bf16_d128", "bf16_d64", "f32_d64"])
+def test_decode_attn_evict_tailfill_matches_separate_calls(shape):
+    """trimkv_decode_attn_evict_tailfill against mask-mode trimkv_decode_attn
+    followed by trimkv_evict_tailfill: outputs, dropped mass, rows, lengths
+    and the new tables bit for bit over four streaming steps, and the
+    outputs within tolerance of the oracle."""
+    base = W["stream_gqa7"].scaled(layers=2, ctx=1500, budget_abs=900, steps=4)
+    if shape == "bf16_d64":
+        base = base.scaled(head_dim=64)
+    elif shape == "f32_d64":
+        base = base.scaled(head_dim=64, dtype="f32", group=3)
+    w = base
+    dt = w.dtype
+    pc = synth.build_cache(w)
+    ov = OracleView(pc)
+    H, G, D = pc.n_heads, w.group, w.head_dim
+    M = w.budget()
+    sc = D ** -0.5
+    ca = upload(pc)
+    cb = clone_cache(ca)
+    home_off, home_ids = ca.page_off.clone(), ca.page_ids.clone()
+    tables = {n: [(torch.zeros_like(home_off), torch.zeros_like(home_ids)) for _ in range(2)] for n in "ab"}
+    seg = cuda(np.array([0, H], np.int32))
+    bud = cuda(np.array([M], np.int64))
+    st = {"lnb": ov.lnb, "pos": ov.pos, "k": ov.k_raw, "v": ov.v_raw}
+    rng = np.random.default_rng(77)
+    for s in range(1, w.steps + 1):
+        t = w.ctx + s
+        announce("attention + tail fill,", shape, "step", s)
+        beta = rng.beta(5.0, 1.0, H).astype(np.float32)
+        kn = rng.standard_normal((H, D))
+        vn = rng.standard_normal((H, D))
+        qn = rng.standard_normal((H * G, D))
+        conv = synth.f64_to_bf16_bits if dt == "bf16" else (lambda x: x.astype(np.float32))
+        kn, vn, qn = conv(kn), conv(vn), conv(qn)
+        t_dev = cuda(np.array([t], np.int32))
+        outs = []
+        for name in "ab":
+            c = ca if name == "a" else cb
+            n = c.n_pages * 16
+            score = torch.empty(n, dtype=torch.float32, device="cuda")
+            keep = torch.empty(n, dtype=torch.uint8, device="cuda")
+            kept = torch.empty(H, dtype=torch.int32, device="cuda")
+            tk.append_score_select(c, kv_dev(kn, dt), kv_dev(vn, dt), cuda(beta), seg, t_dev, bud, score, keep, kept)
+            used = int(c.page_off[H].item()) * 16   # the keep plane's slots under the current table
+            out = torch.full((H * G, D), 5.0, dtype=torch.float32, device="cuda")
+            dropped = torch.full((H * G,), 5.0, dtype=torch.float32, device="cuda")
+            no, ni = tables[name][s % 2]
+            if name == "a":
+                tk.decode_attn(c, kv_dev(qn, dt), G, sc, out, dropped, keep=keep)
+                v = tk.evict_tailfill(c, keep, 1, home_off, home_ids, no, ni, kept=kept)
+            else:
+                v = tk.decode_attn_evict_tailfill(c, keep, kept, kv_dev(qn, dt), G, sc, out, dropped, 1, home_off,
+                                                  home_ids, no, ni)
+            torch.cuda.synchronize()
+            outs.append((out.cpu().numpy(), dropped.cpu().numpy(), keep[:used].cpu().numpy(), kept.cpu().numpy()))
+            if name == "a":
+                ca = v
+            else:
+                cb = v
+        (oa, da, ka, na), (ob, db, kb, nb) = outs
+        assert np.array_equal(ka, kb) and np.array_equal(na, nb)
+        assert np.array_equal(f32_bits(oa), f32_bits(ob)) and np.array_equal(f32_bits(da), f32_bits(db)), s
+        same_cache(ca, cb)
+        # oracle: the step's selection and attention over the slot-ordered state
+        lnb_new = ref.ln_beta(beta)
+        for h in range(H):
+            st["lnb"][h] = np.append(st["lnb"][h], lnb_new[h])
+            st["pos"][h] = np.append(st["pos"][h], np.int32(t - 1))
+            st["k"][h] = np.concatenate([st["k"][h], kn[h:h + 1]])
+            st["v"][h] = np.concatenate([st["v"][h], vn[h:h + 1]])
+        scores = [ref.score_f32(st["lnb"][h], t, st["pos"][h]) for h in range(H)]
+        wkeep, wkept = ref.select_global(scores, [0, H], [M], positions=st["pos"])
+        assert np.array_equal(na, wkept), s
+        tof = synth.bf16_bits_to_f32 if dt == "bf16" else (lambda x: x)
+        q64 = tof(qn).astype(np.float64)
+        kf = [tof(x).astype(np.float64) for x in st["k"]]
+        vf = [tof(x).astype(np.float64) for x in st["v"]]
+        wout, wdrop, _ = ref.decode_attn(kf, vf, q64, G, sc, keep=wkeep)
+        assert np.max(np.abs(oa - wout)) <= 2e-3, s
+        assert np.max(np.abs(da - wdrop)) <= 1e-5, s
+        order, _ = ref.evict_tailfill_order(wkeep, 1, home_off.cpu().numpy().astype(np.int64),
+                                            home_ids.cpu().numpy().astype(np.int64))
+        st = {nm: [x[h][order[h]] for h in range(H)] for nm, x in st.items()}
+        po, pi, ln, k, v, glnb, gpos = download_cache(cb)
+        for h in range(H):
+            assert np.array_equal(ref.gather_heads(gpos, po, pi, ln)[h], st["pos"][h]), (s, h)
+            assert np.array_equal(ref.gather_heads(k, po, pi, ln)[h], st["k"][h]), (s, h)
