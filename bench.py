@@ -80,9 +80,10 @@ TRACE_RUN = {
                     "reference-mode decode."),
     "stream_gqa7": ("--workload stream_gqa7 --stream-steps 512 --no-cpu-baseline",
                     "A run is 4 + 512 generated steps for each variant: evicting out of place, in place "
-                    "(stable shift), in place by tail fill (scores formed in the selection), and out of place "
-                    "through the step loop launched eagerly and replayed from HIP graphs; each step appends, "
-                    "scores, selects, attends (mask mode) and evicts."),
+                    "(stable shift), in place by tail fill (scores formed in the selection) as separate calls "
+                    "and as two fused calls per step, the fused tail-fill steps replayed from HIP graphs, and "
+                    "out of place through the step loop launched eagerly and replayed from HIP graphs; each "
+                    "step appends, scores, selects, attends (mask mode) and evicts."),
     "batched16_16k": ("--workload batched16_16k --steps 3 --warmup 1 --cold-reps 1 --no-cpu-baseline",
                       "A run is 1 + 3 pipeline steps of the 16-sequence workload (score, select with 16 "
                       "segments, mask-mode attention, compaction, plain decode of 8 tokens) plus 3 single "
@@ -1082,11 +1083,14 @@ def bench_streaming(args, w):
         return cur, e0.elapsed_time(e1) * 1e-3, ev[0].elapsed_time(ev[1]) * 1e-3
 
     ws_tf = tk.workspace(tk.OP_EVICT_TAILFILL, home)
+    ws_de = tk.workspace(tk.OP_DECODE_EVICT, home, 0, G)
 
-    def run_tailfill(n):
+    def run_tailfill(n, fused=False):
         """steps 1..n; step 1 lays the evicted prefill out in the home pages
         as run_inplace does, later steps score and select in one call and
-        evict by tail fill (only the kept entries that fill holes move)"""
+        evict by tail fill (only the kept entries that fill holes move).
+        fused: each later step is two calls, append + score + select, then
+        attention + eviction (the merge beside the eviction in one launch)"""
         step_one(home, RES)
         home_off, home_ids = home.page_off.clone(), home.page_ids.clone()
         wsel, watt, _ = ws["home"]
@@ -1095,10 +1099,16 @@ def bench_streaming(args, w):
         ev[0].record()
         for s in range(2, n + 1):
             i = s - 1
+            nt = tables[s % 2]
+            if fused:
+                tk.append_score_select(view, k_all[i], v_all[i], beta_all[i], seg, t_all[i], bud, score, keep, kept,
+                                       ws=wsel)
+                view = tk.decode_attn_evict_tailfill(view, keep, kept, q_all[i], G, scale, out, dropped, 1, home_off,
+                                                     home_ids, nt[0], nt[1], ws=ws_de)
+                continue
             tk.append(view, k_all[i], v_all[i], beta_all[i], t_all[i])
             tk.score_select(view, seg, t_all[i], bud, score, keep, kept, ws=wsel)
             tk.decode_attn(view, q_all[i], G, scale, out, dropped, keep=keep, ws=watt)
-            nt = tables[s % 2]
             view = tk.evict_tailfill(view, keep, 1, home_off, home_ids, nt[0], nt[1], kept=kept, ws=ws_tf)
         ev[1].record()
         torch.cuda.synchronize()
@@ -1166,9 +1176,15 @@ def bench_streaming(args, w):
     run_oop(min(S, 4))                       # first launches load the kernels
     run_inplace(min(S, 4))
     run_tailfill(min(S, 4))
+    run_tailfill(min(S, 4), fused=True)
     view_tf, t_tf = run_tailfill(S)
     assert int(view_tf.length.sum().item()) == M
     len_tf = view_tf.length.clone()
+    out_tf, drop_tf = out.clone(), dropped.clone()
+    view_tff, t_tff = run_tailfill(S, fused=True)
+    # the fused calls give the separate calls' results bit for bit
+    assert torch.equal(view_tff.length, len_tf) and torch.equal(out, out_tf) and torch.equal(dropped, drop_tf)
+    del out_tf, drop_tf
     run_loop_tf(min(S, 4), True)
     loop_tf, t_tf_graph = run_loop_tf(S, True)
     assert torch.equal(loop_tf.cache.length, len_tf)
@@ -1201,13 +1217,14 @@ def bench_streaming(args, w):
     # entries) and the keep bytes the eviction scans
     tf_step = (step_algo["append"] + step_algo["score"] + step_algo["select"] + step_algo["attend_mask"]
                + 1040 * H + U)
-    # value: the fastest complete step, eviction in place by tail fill (the
-    # same kept sets as the other modes at every step; their rates follow)
+    # value: the fastest complete step, eviction in place by tail fill as two
+    # fused calls (the same kept sets as the other modes at every step, and
+    # the separate calls' results bit for bit; their rates follow)
     res = {"metric": "streaming eviction steps/s (append, score, global select, mask-mode attention, evict), "
                      "GQA-7 28x4 heads, 64K prefill",
-           "value": round(S_t / t_tf, 1), "unit": "steps/s", "n_gpus": 1, "steps": S_t, "warmup": 4,
-           "ms_per_step": round(t_tf / S_t * 1e3, 4), "higher_is_better": True, "scaling": "weak",
-           "value_mode": "tail_fill",
+           "value": round(S_t / t_tff, 1), "unit": "steps/s", "n_gpus": 1, "steps": S_t, "warmup": 4,
+           "ms_per_step": round(t_tff / S_t * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+           "value_mode": "tail_fill_fused",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": w.name, "layers": w.layers, "kv_heads": w.kv_heads, "q_per_kv": G,
                       "head_dim": D, "prefill": w.ctx, "prefill_entries": N0, "budget": M, "page": 16},
@@ -1218,6 +1235,14 @@ def bench_streaming(args, w):
                             "step_algo_bytes": step_algo},
            "in_place": {"steps_per_s": round(S_t / t_inp, 1), "us_per_step": round(t_inp / S_t * 1e6, 2),
                         "home_spare_slots_per_head": RES},
+           "tail_fill_fused": {"steps_per_s": round(S_t / t_tff, 1), "us_per_step": round(t_tff / S_t * 1e6, 2),
+                               "GBps": round(tf_step * S_t / t_tff / 1e9, 1),
+                               "frac_hbm": round(tf_step * S_t / t_tff / 1e9 / HBM_PEAK_GBS, 4),
+                               "algo_bytes_per_step": tf_step,
+                               "what": "tail fill as two calls per step: trimkv_append_score_select (the append "
+                                       "written by the selection's first kernel), then "
+                                       "trimkv_decode_attn_evict_tailfill (the attention's merge and the eviction "
+                                       "in one launch); the same outputs as tail_fill, bit for bit"},
            "tail_fill": {"steps_per_s": round(S_t / t_tf, 1), "us_per_step": round(t_tf / S_t * 1e6, 2),
                          "GBps": round(tf_step * S_t / t_tf / 1e9, 1),
                          "frac_hbm": round(tf_step * S_t / t_tf / 1e9 / HBM_PEAK_GBS, 4),
@@ -1227,7 +1252,8 @@ def bench_streaming(args, w):
                                  "(at most the step's %d drops)" % H},
            "tail_fill_hip_graph": {"steps_per_s": round(S_t / t_tf_graph, 1),
                                    "us_per_step": round(t_tf_graph / S_t * 1e6, 2),
-                                   "what": "the tail-fill steps captured in HIP graphs of 64 steps and replayed"},
+                                   "what": "the fused tail-fill steps captured in HIP graphs of 64 steps and "
+                                           "replayed"},
            "fused_score_select": {"steps_per_s": round(S_t / t_staged, 1),
                                   "us_per_step": round(t_staged / S_t * 1e6, 2),
                                   "what": "out of place, trimkv_score_select in place of score + select"},

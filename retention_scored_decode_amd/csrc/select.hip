@@ -98,75 +98,87 @@ struct AppendSrc {
   int32_t* status;         // +1 per head without a free slot (nullable)
 };
 
+// One wave's append of head h (after trimkv_append): entry len[h] takes the
+// new row, ln beta and position t_s - 1; a head without a free slot is
+// counted.  The row, beta and step are loaded before the length is known.
+__device__ __forceinline__ void append_head(int h, const int32_t* __restrict__ page_off, const int32_t* len,
+                                            int n_seg, const int32_t* __restrict__ seg_hb, const AppendSrc& ap) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int s = upper_index(seg_hb, n_seg + 1, h);
+  const float b = ap.beta_new[h];
+  const int tt = ap.t[s];
+  const int n = len[h];
+  const int64_t cap = (int64_t)(page_off[h + 1] - page_off[h]) * PAGE;
+  if (n >= cap) {
+    if (lane == 0 && ap.status) atomicAdd(ap.status, 1);
+    return;
+  }
+  const int64_t page = ap.page_ids[page_off[h] + n / PAGE];
+  const int64_t slot = page * PAGE + n % PAGE;
+  // element-wise, as trimkv_append copies (inputs need only element alignment)
+  if (ap.elt == 2) {
+    const uint16_t* kn = reinterpret_cast<const uint16_t*>(ap.k_new) + (int64_t)h * (ap.rowb / 2);
+    const uint16_t* vn = reinterpret_cast<const uint16_t*>(ap.v_new) + (int64_t)h * (ap.rowb / 2);
+    uint16_t* kd = reinterpret_cast<uint16_t*>(ap.k) + slot * (ap.rowb / 2);
+    uint16_t* vd = reinterpret_cast<uint16_t*>(ap.v) + slot * (ap.rowb / 2);
+    for (int d = lane; d < ap.rowb / 2; d += WAVE) {
+      kd[d] = kn[d];
+      vd[d] = vn[d];
+    }
+  } else {
+    const uint32_t* kn = reinterpret_cast<const uint32_t*>(ap.k_new) + (int64_t)h * (ap.rowb / 4);
+    const uint32_t* vn = reinterpret_cast<const uint32_t*>(ap.v_new) + (int64_t)h * (ap.rowb / 4);
+    uint32_t* kd = reinterpret_cast<uint32_t*>(ap.k) + slot * (ap.rowb / 4);
+    uint32_t* vd = reinterpret_cast<uint32_t*>(ap.v) + slot * (ap.rowb / 4);
+    for (int d = lane; d < ap.rowb / 4; d += WAVE) {
+      kd[d] = kn[d];
+      vd[d] = vn[d];
+    }
+  }
+  if (lane == 0) {
+    ap.meta[page * (2 * PAGE) + n % PAGE] = __float_as_uint(ln_f32_cr(b));
+    ap.meta[page * (2 * PAGE) + PAGE + n % PAGE] = (uint32_t)(tt - 1);
+  }
+}
+
 // ---------------------------------------------------------------------------
-// prep: chunk list + metadata + segment state (block 0); every block clears
-// histograms, kept[] and look-back words.  With an append, every head with
-// a free slot gets its new entry here (one wave per head) and the chunk list
-// counts it; the lengths themselves are raised by the first histogram pass
-// (no selection kernel reads them), except with more heads than the LDS
-// list holds: then this kernel runs as one block and raises them itself,
-// before it reads them.
+// prep: chunk list + metadata + segment state (block 0); the first n_prep
+// blocks clear histograms, kept[] and look-back words.  With an append, the
+// chunk list counts one more entry in every head with a free slot, and the
+// entries themselves are written by further blocks, one wave per head,
+// beside the prep blocks (neither reads what the other writes); the lengths
+// are raised by the first histogram pass, which no selection kernel before
+// it needs.  With more heads than the LDS list holds, one block does
+// everything in order: the appends, the lengths, then the list.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024) k_sel_prep(const int32_t* __restrict__ page_off,
                                                    int32_t* __restrict__ len, int n_heads, int n_seg,
                                                    const int32_t* __restrict__ seg_hb,
                                                    const int64_t* __restrict__ budget, int64_t tmax, SelWs w,
-                                                   int32_t* __restrict__ kept, AppendSrc ap) {
-  const size_t gtid = (size_t)blockIdx.x * 1024 + threadIdx.x, gstride = (size_t)gridDim.x * 1024;
+                                                   int32_t* __restrict__ kept, AppendSrc ap, int n_prep) {
+  const bool grow = ap.k_new != nullptr;
+  constexpr int WPB = 1024 / WAVE;
+  if (grow && (int)blockIdx.x >= n_prep) {   // append blocks (block-uniform; no barriers)
+    const int h = (blockIdx.x - n_prep) * WPB + __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+    if (h < n_heads) append_head(h, page_off, len, n_seg, seg_hb, ap);
+    return;
+  }
+  const size_t gtid = (size_t)blockIdx.x * 1024 + threadIdx.x, gstride = (size_t)n_prep * 1024;
   for (size_t i = gtid; i < (size_t)n_seg * HIST_WORDS; i += gstride) w.hist[i] = 0u;
   for (size_t i = gtid; i < (size_t)tmax; i += gstride) w.look[i] = 0ull;
   for (size_t i = gtid; i < (size_t)n_heads; i += gstride) kept[i] = 0;
   for (size_t i = gtid; i < (size_t)n_seg + 2; i += gstride) w.ticket[i] = 0u;
   __shared__ int64_t tmp[1024 / WAVE + 1];
   __shared__ PrepLDS L;
-  const bool grow = ap.k_new != nullptr;
-  if (grow) {
-    const int lane = threadIdx.x & (WAVE - 1);
-    const int nw = gridDim.x * (1024 / WAVE);
-    for (int h = __builtin_amdgcn_readfirstlane(blockIdx.x * (1024 / WAVE) + threadIdx.x / WAVE); h < n_heads;
-         h += nw) {
+  if (grow && n_heads > PREP_HMAX) {   // one block (n_prep = 1, no append blocks)
+    for (int h = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE); h < n_heads; h += WPB)
+      append_head(h, page_off, len, n_seg, seg_hb, ap);
+    __syncthreads();   // every wave has read its heads' old lengths
+    for (int h = threadIdx.x; h < n_heads; h += 1024) {
       const int n = len[h];
-      const int64_t cap = (int64_t)(page_off[h + 1] - page_off[h]) * PAGE;
-      if (n >= cap) {
-        if (lane == 0 && ap.status) atomicAdd(ap.status, 1);
-        continue;
-      }
-      const int64_t page = ap.page_ids[page_off[h] + n / PAGE];
-      const int64_t slot = page * PAGE + n % PAGE;
-      // element-wise, as trimkv_append copies (inputs need only element alignment)
-      if (ap.elt == 2) {
-        const uint16_t* kn = reinterpret_cast<const uint16_t*>(ap.k_new) + (int64_t)h * (ap.rowb / 2);
-        const uint16_t* vn = reinterpret_cast<const uint16_t*>(ap.v_new) + (int64_t)h * (ap.rowb / 2);
-        uint16_t* kd = reinterpret_cast<uint16_t*>(ap.k) + slot * (ap.rowb / 2);
-        uint16_t* vd = reinterpret_cast<uint16_t*>(ap.v) + slot * (ap.rowb / 2);
-        for (int d = lane; d < ap.rowb / 2; d += WAVE) {
-          kd[d] = kn[d];
-          vd[d] = vn[d];
-        }
-      } else {
-        const uint32_t* kn = reinterpret_cast<const uint32_t*>(ap.k_new) + (int64_t)h * (ap.rowb / 4);
-        const uint32_t* vn = reinterpret_cast<const uint32_t*>(ap.v_new) + (int64_t)h * (ap.rowb / 4);
-        uint32_t* kd = reinterpret_cast<uint32_t*>(ap.k) + slot * (ap.rowb / 4);
-        uint32_t* vd = reinterpret_cast<uint32_t*>(ap.v) + slot * (ap.rowb / 4);
-        for (int d = lane; d < ap.rowb / 4; d += WAVE) {
-          kd[d] = kn[d];
-          vd[d] = vn[d];
-        }
-      }
-      if (lane == 0) {
-        const int s = upper_index(seg_hb, n_seg + 1, h);
-        ap.meta[page * (2 * PAGE) + n % PAGE] = __float_as_uint(ln_f32_cr(ap.beta_new[h]));
-        ap.meta[page * (2 * PAGE) + PAGE + n % PAGE] = (uint32_t)(ap.t[s] - 1);
-      }
+      if ((int64_t)n < (int64_t)(page_off[h + 1] - page_off[h]) * PAGE) len[h] = n + 1;
     }
-    if (n_heads > PREP_HMAX) {   // one block: the lengths are raised before they are read
-      __syncthreads();           // every wave has read its heads' old lengths
-      for (int h = threadIdx.x; h < n_heads; h += 1024) {
-        const int n = len[h];
-        if ((int64_t)n < (int64_t)(page_off[h + 1] - page_off[h]) * PAGE) len[h] = n + 1;
-      }
-      __syncthreads();
-    }
+    __syncthreads();
   }
   const int T = prep_chunks<1024>(page_off, len, n_heads, CP, L, tmp, w.chunk_off,
                                   grow && n_heads <= PREP_HMAX);
@@ -185,7 +197,7 @@ __global__ void __launch_bounds__(1024) k_sel_prep(const int32_t* __restrict__ p
       w.seg[s] = st;
     }
   }
-  for (int c = blockIdx.x * 1024 + threadIdx.x; c < T; c += gridDim.x * 1024) {
+  for (int c = blockIdx.x * 1024 + threadIdx.x; c < T; c += n_prep * 1024) {
     const ChunkInfo ci = chunk_info(L, w.chunk_off, page_off, len, n_heads, CP, c);
     const int s = upper_index(seg_hb, n_seg + 1, ci.h);
     w.meta[c] = make_int4(ci.h, s, ci.page0, ci.nv | (ci.npg << 16));
@@ -917,8 +929,10 @@ int select_kernels(const trimkv_cache_t* c, const float* score, int n_seg, const
   const int prep_blocks = prep_grid(c->n_heads, T, 1024);
   if (ap.k_new && c->n_heads <= PREP_HMAX) src.grow_len = c->len;   // raised by the first pass
   src.page_off = c->page_off;
-  hipLaunchKernelGGL(k_sel_prep, dim3(prep_blocks), dim3(1024), 0, st, c->page_off, c->len, c->n_heads, n_seg, seg,
-                     budget, T, w, kept, ap);
+  // append blocks (one wave per head) beside the prep blocks, unless one block must do everything
+  const int app_blocks = ap.k_new && c->n_heads <= PREP_HMAX ? (c->n_heads + 15) / 16 : 0;
+  hipLaunchKernelGGL(k_sel_prep, dim3(prep_blocks + app_blocks), dim3(1024), 0, st, c->page_off, c->len, c->n_heads,
+                     n_seg, seg, budget, T, w, kept, ap, prep_blocks);
   // Chunks per block: 32 for pools of at least 4,096 chunks (about 4M
   // entries); smaller pools take 16, 8 or 4, the fewest that still gives at
   // most 256 blocks, so that a small selection (a streaming step's 0.5M

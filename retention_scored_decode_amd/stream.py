@@ -6,7 +6,9 @@ the lowest current scores are evicted once the budget is exceeded) appends
 one entry per KV head, scores every entry at the step's t, selects the
 global top M, runs mask-mode decode attention with the step's queries
 (renormalised output and dropped mass), and evicts, keeping one spare slot
-per head for the next append.  Eviction is either out of place, into the
+per head for the next append.  With tail fill the step is, by default, two
+fused calls: the append written by the selection's first kernel, and the
+attention's merge beside the eviction in one launch.  Eviction is either out of place, into the
 other of two pools, or in place by tail fill: the cache stays in its home
 pages and only the kept entries that fill holes below a head's new length
 move, the new page table going to the other of two table buffers.
@@ -41,13 +43,17 @@ class StreamLoop:
             q [S, H * group, D] (cache dtype), t [S, 1] int32 (the decode
             step; entry s is appended at position t[s] - 1);
     first:  the bank entry of the next step;
-    evict:  "out_of_place" or "tail_fill".
+    evict:  "out_of_place" or "tail_fill";
+    fused:  tail fill only: a step is two calls, trimkv_append_score_select
+            and trimkv_decode_attn_evict_tailfill (the same results as the
+            four separate calls, with two launches fewer).
     """
 
     def __init__(self, pools: List[tk.Cache], budget: int, group: int, scale: float, banks: dict, first: int = 0,
-                 evict: str = "out_of_place"):
+                 evict: str = "out_of_place", fused: bool = True):
         assert evict in ("out_of_place", "tail_fill")
         self.tail_fill = evict == "tail_fill"
+        self.fused = fused and self.tail_fill
         if self.tail_fill:
             assert len(pools) == 1
         else:
@@ -73,6 +79,8 @@ class StreamLoop:
             self.home_off, self.home_ids = base.page_off.clone(), base.page_ids.clone()
             self.tables = [(torch.empty_like(base.page_off), torch.empty_like(base.page_ids)) for _ in range(2)]
             self.ws_ev = tk.workspace(tk.OP_EVICT_TAILFILL, base)
+            if self.fused:
+                self.ws_att = tk.workspace(tk.OP_DECODE_EVICT, base, 0, group)
         else:
             self.ws_ev = tk.workspace(tk.OP_COMPACT, base)
         # failure counters (append: heads without a free slot; select: timed-out waits)
@@ -83,6 +91,14 @@ class StreamLoop:
     def _step(self, i: int, src: tk.Cache) -> tk.Cache:
         """Step of bank entry i on cache src; returns the cache after eviction."""
         b = self.banks
+        if self.fused:
+            tk.append_score_select(src, b["k"][i], b["v"][i], b["beta"][i], self.seg, b["t"][i], self.bud, self.score,
+                                   self.keep, self.kept, ws=self.ws_sel, append_status=self.status[0:1],
+                                   select_status=self.status[1:2])
+            off, ids = self.tables[i % 2]
+            return tk.decode_attn_evict_tailfill(src, self.keep, self.kept, b["q"][i], self.G, self.scale, self.out,
+                                                 self.dropped, 1, self.home_off, self.home_ids, off, ids,
+                                                 ws=self.ws_att)
         tk.append(src, b["k"][i], b["v"][i], b["beta"][i], b["t"][i], status=self.status[0:1])
         tk.score_select(src, self.seg, b["t"][i], self.bud, self.score, self.keep, self.kept, ws=self.ws_sel,
                         status=self.status[1:2])

@@ -1221,14 +1221,14 @@ def test_select_ties_out_of_position_order(kind):
 # --------------------------------------------------------------------------
 # the streaming step captured in HIP graphs
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("evict", ["out_of_place", "tail_fill"])
+@pytest.mark.parametrize("evict", ["out_of_place", "tail_fill", "tail_fill_separate"])
 def test_streaming_graph_capture(evict):
     """Steps 3..S of the scaled streaming workload replayed from captured
     graphs (one per step) against the same steps run eagerly, evicting out
-    of place or in place by tail fill: kept counts, outputs, dropped mass,
-    page tables and the final pools bit for bit after every replay, with
-    eager work and synchronisations between replays; the final state
-    against the oracle."""
+    of place or in place by tail fill (as two fused calls per step, or as the
+    four separate calls): kept counts, outputs, dropped mass, page tables and
+    the final pools bit for bit after every replay, with eager work and
+    synchronisations between replays; the final state against the oracle."""
     from retention_scored_decode_amd.stream import StreamLoop
 
     w = SMALL["c5s"].scaled(steps=24)
@@ -1249,7 +1249,7 @@ def test_streaming_graph_capture(evict):
     def start():
         """step 1 (the prefill eviction) into a fresh pair of pools, or into
         home pages with a spare slot per head for every later step"""
-        if evict == "tail_fill":
+        if evict.startswith("tail_fill"):
             pools = [tk.Cache.empty(H, dst_capacity(H, M, S), D, torch.bfloat16)]
             reserve = S
         else:
@@ -1265,7 +1265,8 @@ def test_streaming_graph_capture(evict):
         tk.score(prefill, seg, t, score)
         tk.select_global(prefill, score, seg, cuda(np.array([M], np.int64)), keep, kept)
         tk.compact(prefill, keep, reserve, M, pools[0], torch.zeros(1, dtype=torch.int64, device="cuda"), kept=kept)
-        return StreamLoop(pools, M, G, sc, banks, first=1, evict=evict)
+        return StreamLoop(pools, M, G, sc, banks, first=1, evict="tail_fill" if evict.startswith("tail_fill") else evict,
+                          fused=evict == "tail_fill")
 
     def state(loop):
         torch.cuda.synchronize()

@@ -6,11 +6,13 @@ once the budget is exceeded the lowest current scores are evicted).
 
 The oracle tracks the state of every step (ln beta, position and head of
 every entry; selection by the oracle's partial-sort selection on its own
-float32 scores) and the GPU runs the same 8,192 steps twice: evicting out of
-place into the other of two pools, and in place within each head's own
-pages.  Checked:
+float32 scores) and the GPU runs the same 8,192 steps in four ways:
+evicting out of place into the other of two pools; in place within each
+head's own pages by a stable shift; in place by tail fill; and by tail fill
+as two fused calls per step (trimkv_append_score_select, then
+trimkv_decode_attn_evict_tailfill).  Checked:
   - every step: kept entries per head, the new page offsets and lengths,
-    bit for bit (both variants);
+    bit for bit (every variant);
   - steps 1-16, every 256th step and the last: the whole keep plane, the
     positions and ln beta of every retained entry, the K/V rows of sampled
     heads, and mask-mode attention on sampled heads against the float64
@@ -68,7 +70,8 @@ class GpuRun:
 
 def run_gpu(w, pc, steps_in, mode):
     inplace = mode != "out_of_place"
-    tailfill = mode == "tail_fill"
+    tailfill = mode.startswith("tail_fill")
+    fused = mode == "tail_fill_fused"   # two calls per step: append + score + select, attention + eviction
     S, H, G, D = w.steps, pc.n_heads, w.group, w.head_dim
     M = w.budget()
     scale = 1.0 / math.sqrt(D)
@@ -100,36 +103,47 @@ def run_gpu(w, pc, steps_in, mode):
     ws_of = lambda c: (tk.workspace(tk.OP_SELECT, c, 1), tk.workspace(tk.OP_DECODE_ATTN, c, 0, G),
                        tk.workspace(tk.OP_COMPACT, c))
     ws_pre, ws_pool = ws_of(prefill), ws_of(pools[0])
+    ws_de = tk.workspace(tk.OP_DECODE_EVICT, pools[0], 0, G) if fused else None
     r = GpuRun(S, H)
     samples = set(sample_steps(S))
     cur, home = prefill, None
     for s in range(1, S + 1):
         i = s - 1
         wsel, watt, wcmp = ws_pre if s == 1 else ws_pool
-        tk.append(cur, k_all[i], v_all[i], beta_all[i], t_all[i], status=st_app)
-        tk.score(cur, seg, t_all[i], score)
-        if tailfill:   # the fused score + select, on slots out of position order
-            tk.score_select(cur, seg, t_all[i], bud, score, keep, kept, ws=wsel, status=st_sel)
+        snap = None
+        if fused and s > 1:
+            tk.append_score_select(cur, k_all[i], v_all[i], beta_all[i], seg, t_all[i], bud, score, keep, kept,
+                                   ws=wsel, append_status=st_app, select_status=st_sel)
         else:
-            tk.score(cur, seg, t_all[i], score)
-            tk.select_global(cur, score, seg, bud, keep, kept, ws=wsel, status=st_sel)
-        tk.decode_attn(cur, q_all[i], G, scale, out, dropped, keep=keep, ws=watt)
+            tk.append(cur, k_all[i], v_all[i], beta_all[i], t_all[i], status=st_app)
+            if tailfill:   # the fused score + select, on slots out of position order
+                tk.score_select(cur, seg, t_all[i], bud, score, keep, kept, ws=wsel, status=st_sel)
+            else:
+                tk.score(cur, seg, t_all[i], score)
+                tk.select_global(cur, score, seg, bud, keep, kept, ws=wsel, status=st_sel)
         if s in samples:
             snap = {"cur_off": cur.page_off.cpu().numpy(), "cur_len": cur.length.cpu().numpy()}
             snap["keep"] = keep[:int(snap["cur_off"][-1]) * 16].cpu().numpy()
-            snap["out"], snap["dropped"] = out.cpu().numpy(), dropped.cpu().numpy()
             if tailfill:   # positions of the slots the keep plane refers to
                 snap["cur_pos"] = ref.gather_heads(cur.meta[:, 1, :].cpu().numpy(), snap["cur_off"],
                                                    cur.page_ids.cpu().numpy(), snap["cur_len"])
-        if inplace and s > 1:
+        if fused and s > 1:   # attention, then eviction in place, the merge beside the eviction
             nt = tables[s % 2]
-            evict = tk.evict_tailfill if tailfill else tk.compact_inplace
-            nxt = evict(cur, keep, 1, home[0], home[1], nt[0], nt[1], kept=kept, ws=ws_inp)
+            nxt = tk.decode_attn_evict_tailfill(cur, keep, kept, q_all[i], G, scale, out, dropped, 1, home[0],
+                                                home[1], nt[0], nt[1], ws=ws_de)
         else:
-            nxt = pools[s % len(pools)]
-            tk.compact(cur, keep, res1 if s == 1 else 1, M, nxt, used, ws=wcmp, kept=kept)
-            if inplace:
-                home = (nxt.page_off.clone(), nxt.page_ids.clone())
+            tk.decode_attn(cur, q_all[i], G, scale, out, dropped, keep=keep, ws=watt)
+            if inplace and s > 1:
+                nt = tables[s % 2]
+                evict = tk.evict_tailfill if tailfill else tk.compact_inplace
+                nxt = evict(cur, keep, 1, home[0], home[1], nt[0], nt[1], kept=kept, ws=ws_inp)
+            else:
+                nxt = pools[s % len(pools)]
+                tk.compact(cur, keep, res1 if s == 1 else 1, M, nxt, used, ws=wcmp, kept=kept)
+                if inplace:
+                    home = (nxt.page_off.clone(), nxt.page_ids.clone())
+        if s in samples:
+            snap["out"], snap["dropped"] = out.cpu().numpy(), dropped.cpu().numpy()
         r.kept[i].copy_(kept)
         r.length[i].copy_(nxt.length)
         r.off[i].copy_(nxt.page_off)
@@ -223,13 +237,13 @@ def oracle_state(stream_run):
     return res
 
 
-@pytest.mark.parametrize("mode", ["out_of_place", "in_place", "tail_fill"])
+@pytest.mark.parametrize("mode", ["out_of_place", "in_place", "tail_fill", "tail_fill_fused"])
 def test_full_streaming_run(stream_run, oracle_state, mode):
     w, pc, steps_in = stream_run
     kept_hist, osnap = oracle_state
     S, H, G, D = w.steps, pc.n_heads, w.group, w.head_dim
     M = w.budget()
-    inplace, tailfill = mode != "out_of_place", mode == "tail_fill"
+    inplace, tailfill = mode != "out_of_place", mode.startswith("tail_fill")
     t0 = time.time()
     r = run_gpu(w, pc, steps_in, mode)
     say("GPU ran", S, "steps", mode, "in %.1f s" % (time.time() - t0))
