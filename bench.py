@@ -20,6 +20,7 @@ rate (entries/s) is reported beside it, with per-stage figures, the roofline
 of the dominant stage and the CPU oracle timed on a sample.
 """
 import argparse
+import gc
 import json
 import math
 import os
@@ -1173,7 +1174,17 @@ def bench_streaming(args, w):
         assert int(loop.status.sum().item()) == 0
         return loop, ev[0].elapsed_time(ev[1]) * 1e-3
 
+    # no collector pauses inside the timed runs
+    gc.collect()
+    gc.disable()
     run_oop(min(S, 4))                       # first launches load the kernels
+    # step 1 on its own, before any HIP graph exists: it is five launches, so
+    # the host is barely ahead of the GPU, and after the graph runs below
+    # release their graphs the same launches took milliseconds to enqueue
+    torch.cuda.synchronize()
+    e_first = step_one(pools[1], 1)
+    torch.cuda.synchronize()
+    t_first = e_first[0].elapsed_time(e_first[1]) * 1e-3
     run_inplace(min(S, 4))
     run_tailfill(min(S, 4))
     run_tailfill(min(S, 4), fused=True)
@@ -1196,7 +1207,7 @@ def bench_streaming(args, w):
     loop_g, t_graph = run_loop(S, True)
     assert torch.equal(loop_g.cache.length, len_e)
     del loop_e, loop_g
-    cur, t_first, t_oop = run_oop(S)
+    cur, _, t_oop = run_oop(S)
     assert int(cur.length.sum().item()) == M
     assert tk.validate_cache(cur, t_all[S - 1] + 1) == tk.OK
     assert bool(torch.isfinite(out).all())
@@ -1266,6 +1277,7 @@ def bench_streaming(args, w):
            "first_step_what": "append, score, select, mask-mode attention and eviction of the %d-entry "
                               "prefill (step 1)" % N0,
            "steps_timed": "steps 2..%d, one pass, no cache flush" % S}
+    gc.enable()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_stream(w, pc)
     print(json.dumps(res), flush=True)
