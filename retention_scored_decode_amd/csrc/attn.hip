@@ -66,7 +66,7 @@ struct AttnWs {
   float* acc;          // [Smax][G][D]     partials: unnormalised outputs
   float* acc2;         // [Smax][G][D]     partials of the dropped keys (error mode), else null
   float* lse2;         // [H * G] base-2 LSE (mass op)
-  float* logits;       // [G][n_pages * 16] (mass op)
+  float* logits;       // [n_pages][G][16] (mass op): page-major, so a page's logits are one 64 * G-byte run
 };
 
 struct AttnArgs {
@@ -80,7 +80,6 @@ struct AttnArgs {
   int n_heads;
   int group;
   float scale2;          // scale * log2(e)
-  int64_t plane;         // logits plane stride (n_pages * 16)
   int cha;               // pages per work item (fp32 path)
   int waves;             // waves of the launch (bf16 path; 0 = fp32 work list)
   AttnWs w;
@@ -620,7 +619,7 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
     if (slow && m == -INFINITY) pj[0] = pj[1] = pj[2] = pj[3] = 0.f;
     if (LOGITS) {
       if (col < G) {
-        float* dst = w.logits + (int64_t)col * a.plane + (int64_t)(page0 + i) * PAGE + 4 * r;
+        float* dst = w.logits + ((int64_t)(page0 + i) * G + col) * PAGE + 4 * r;
         if (full) {
           *reinterpret_cast<float4*>(dst) = make_float4(s[0] * a.scale2, s[1] * a.scale2, s[2] * a.scale2,
                                                         s[3] * a.scale2);
@@ -801,7 +800,7 @@ __global__ void __launch_bounds__(NT) k_attn_f32(AttnArgs a) {
       float dot = 0.f;
       for (int d = 0; d < D; ++d) dot = fmaf(sq[g][d], krow[d], dot);
       z = dot * a.scale2;
-      if (LOGITS) w.logits[(int64_t)g * a.plane + (int64_t)(page0 + p) * PAGE + t % PAGE] = z;
+      if (LOGITS) w.logits[((int64_t)(page0 + p) * G + g) * PAGE + t % PAGE] = z;
     }
     sp[g][t] = z;
   }
@@ -855,7 +854,7 @@ __global__ void __launch_bounds__(NT) k_attn_f32(AttnArgs a) {
 // mass[j] = (1/G) sum_g 2^(z2_gj - lse2_g); NaN in padding slots.
 // 64 CSR pages per block, 4 slots per thread.
 __global__ void __launch_bounds__(256) k_mass(const int32_t* __restrict__ page_off, const int32_t* __restrict__ len,
-                                              int n_heads, int group, int64_t plane, const AttnWs w,
+                                              int n_heads, int group, const AttnWs w,
                                               float* __restrict__ mass) {
   __shared__ PageHeads sh;
   const int64_t total = page_off[n_heads];
@@ -873,7 +872,7 @@ __global__ void __launch_bounds__(256) k_mass(const int32_t* __restrict__ page_o
   if (i0 < n) {
     float s[4] = {0.f, 0.f, 0.f, 0.f};
     for (int g = 0; g < group; ++g) {
-      const float4 z = *reinterpret_cast<const float4*>(w.logits + (int64_t)g * plane + slot);
+      const float4 z = *reinterpret_cast<const float4*>(w.logits + (c * group + g) * PAGE + j0);
       const float l2 = w.lse2[(size_t)h * group + g];
       s[0] += exp2f(z.x - l2);
       s[1] += exp2f(z.y - l2);
@@ -1000,7 +999,7 @@ int decode_attn_on(const trimkv_cache_t* c, const uint8_t* keep, const float* ls
     hipLaunchKernelGGL(k_attn_prep, dim3(prep_grid(c->n_heads, max_chunks(c, CHA_F32), 2048)), dim3(1024), 0, st,
                        c->page_off, c->len, c->n_heads, CHA_F32, w);
   AttnArgs a{c->page_off, c->page_ids, c->len, c->k, c->v, keep, q, c->n_heads, group, scale * LOG2E,
-             c->n_pages * PAGE, CHA_F32, 0, w, lse_ref, out, dropped, lse_out};
+             CHA_F32, 0, w, lse_ref, out, dropped, lse_out};
   prof_begin(st);
   int rc = keep ? launch_main<A_MASK>(c, a, st) : launch_main<A_PLAIN>(c, a, st);
   prof_end(st);
@@ -1057,7 +1056,7 @@ int launch_decode_attn_evict_tailfill(trimkv_cache_t* c, const uint8_t* keep, co
     hipLaunchKernelGGL(k_attn_prep, dim3(prep_grid(c->n_heads, max_chunks(c, CHA_F32), 2048)), dim3(1024), 0, st,
                        c->page_off, c->len, c->n_heads, CHA_F32, w);
   AttnArgs a{c->page_off, c->page_ids, c->len, c->k, c->v, keep, q, c->n_heads, group, scale * LOG2E,
-             c->n_pages * PAGE, CHA_F32, 0, w, nullptr, out, dropped, nullptr};
+             CHA_F32, 0, w, nullptr, out, dropped, nullptr};
   prof_begin(st);
   const int rc = launch_main<A_MASK>(c, a, st);
   prof_end(st);
@@ -1104,7 +1103,7 @@ int launch_decode_attn_err(const trimkv_cache_t* c, const uint8_t* keep, const v
                            float* out, float* dropped, float* mu, float* err, void* ws, hipStream_t st) {
   AttnWs w = carve(c, group, ws, false, true);
   AttnArgs a{c->page_off, c->page_ids, c->len, c->k, c->v, keep, q, c->n_heads, group, scale * LOG2E,
-             c->n_pages * PAGE, CHA_F32, 0, w, nullptr, out, dropped, nullptr, mu, err};
+             CHA_F32, 0, w, nullptr, out, dropped, nullptr, mu, err};
   prof_begin(st);
   int rc = launch_main<A_ERR>(c, a, st);
   prof_end(st);
@@ -1118,7 +1117,7 @@ int launch_decode_attn_gated(const trimkv_cache_t* c, int n_seg, const int32_t* 
                              float* lse_out, void* ws, hipStream_t st) {
   AttnWs w = carve(c, group, ws, false);
   AttnArgs a{c->page_off, c->page_ids, c->len, c->k, c->v, keep, q, c->n_heads, group, scale * LOG2E,
-             c->n_pages * PAGE, CHA_F32, 0, w, nullptr, out, dropped, lse_out, nullptr, nullptr,
+             CHA_F32, 0, w, nullptr, out, dropped, lse_out, nullptr, nullptr,
              c->meta, seg, t, n_seg};
   prof_begin(st);
   int rc = keep ? launch_main<A_GMASK>(c, a, st) : launch_main<A_GPLAIN>(c, a, st);
@@ -1136,15 +1135,15 @@ int launch_attn_mass(const trimkv_cache_t* c, const void* q, int group, float sc
     hipLaunchKernelGGL(k_attn_prep, dim3(prep_grid(c->n_heads, max_chunks(c, CHA_F32), 2048)), dim3(1024), 0, st,
                        c->page_off, c->len, c->n_heads, CHA_F32, w);
   AttnArgs a{c->page_off, c->page_ids, c->len, c->k, c->v, nullptr, q, c->n_heads, group, scale * LOG2E,
-             c->n_pages * PAGE, CHA_F32, 0, w, nullptr, nullptr, nullptr, lse_full};
+             CHA_F32, 0, w, nullptr, nullptr, nullptr, lse_full};
   prof_begin(st);
   int rc = launch_main<A_LOGITS>(c, a, st);
   prof_end(st);
   if (rc) return rc;
   launch_merge(c, a, 0, st);
   const int64_t blocks = (c->n_pages + 63) / 64;
-  hipLaunchKernelGGL(k_mass, dim3((unsigned)blocks), dim3(256), 0, st, c->page_off, c->len, c->n_heads, group,
-                     c->n_pages * PAGE, w, mass);
+  hipLaunchKernelGGL(k_mass, dim3((unsigned)blocks), dim3(256), 0, st, c->page_off, c->len, c->n_heads, group, w,
+                     mass);
   return check_launch();
 }
 
