@@ -98,9 +98,10 @@ struct AppendSrc {
   int32_t* status;         // +1 per head without a free slot (nullable)
 };
 
-// One wave's append of head h (after trimkv_append): entry len[h] takes the
-// new row, ln beta and position t_s - 1; a head without a free slot is
-// counted.  The row, beta and step are loaded before the length is known.
+// One wave's append of head h, as trimkv_append writes it: entry len[h]
+// takes the new row, ln beta and position t_s - 1 (s the head's segment); a
+// head without a free slot is counted.  Beta and the step are requested
+// before the length is known.
 __device__ __forceinline__ void append_head(int h, const int32_t* __restrict__ page_off, const int32_t* len,
                                             int n_seg, const int32_t* __restrict__ seg_hb, const AppendSrc& ap) {
   const int lane = threadIdx.x & (WAVE - 1);
