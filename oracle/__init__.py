@@ -20,7 +20,12 @@ written from the pages:
 ``brute`` restates selection and attention in pure Python for tiny inputs.
 
 Parity status: every function is pinned by the CPU tests in
-``tests/test_oracle_pins.py`` except the readings listed there as
-"parity unpinned" (tie direction, compaction layout, page-table format,
-allocation remainder rule), which only the written specification fixes.
+``tests/test_oracle_pins.py``.  Three readings stay "parity unpinned",
+fixed only by the written specification and not by the pages: the direction
+of ties across heads (within a head, the more recent entry first is pinned
+by the beta = 1 invariant); the compaction layout and page-table format as
+rules (the oracle is pinned against an independent construction of the
+same rule); and the allocation's re-offer of units that a cap turns away
+(the uncapped largest-remainder rule is pinned by its least-squares
+property).
 """
