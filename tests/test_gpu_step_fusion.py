@@ -290,3 +290,79 @@ def test_decode_attn_evict_tailfill_matches_separate_calls(shape):
         for h in range(H):
             assert np.array_equal(ref.gather_heads(gpos, po, pi, ln)[h], st["pos"][h]), (s, h)
             assert np.array_equal(ref.gather_heads(k, po, pi, ln)[h], st["k"][h]), (s, h)
+
+
+def test_fused_step_ragged_edge_cases():
+    """Both fused calls on a ragged cache: heads without pages, heads of one
+    entry, lengths on and off page boundaries (heads whose pages are full get
+    no entry and are counted), budgets of a third, one entry, nothing and
+    more than everything, beta = 0 for some new entries (score -inf), G = 8
+    query heads per KV head; against the separate calls bit for bit."""
+    w = W["stream_gqa7"].scaled(layers=5, kv_heads=8, group=8, ctx=300, reserve=0, beta_block=None)
+    H, D, G = w.n_heads, w.head_dim, w.group
+    rng = np.random.default_rng(3)
+    lens = rng.integers(0, 301, H).astype(np.int32)
+    lens[:6] = [0, 1, 16, 17, 288, 300]            # empty, one entry, full page, one over, full pages
+    pc = synth.build_cache(w, lengths=lens)
+    ca = upload(pc)
+    cb = clone_cache(ca)
+    home_off, home_ids = ca.page_off.clone(), ca.page_ids.clone()
+    tables = {n: [(torch.zeros_like(home_off), torch.zeros_like(home_ids)) for _ in range(2)] for n in "ab"}
+    seg = cuda(np.array([0, H], np.int32))
+    total = int(lens.sum())
+    for s, M in enumerate((total // 3, 1, 0, total + 100)):
+        t = w.ctx + s + 1
+        beta = rng.beta(5.0, 1.0, H).astype(np.float32)
+        beta[::5] = 0.0   # the new entry scores -inf: ranked below every other entry
+        kn = synth.f64_to_bf16_bits(rng.standard_normal((H, D)))
+        vn = synth.f64_to_bf16_bits(rng.standard_normal((H, D)))
+        qn = synth.f64_to_bf16_bits(rng.standard_normal((H * G, D)))
+        len_before = ca.length.cpu().numpy().astype(np.int64)
+        po_now = ca.page_off.cpu().numpy().astype(np.int64)
+        cap = (po_now[1:] - po_now[:-1]) * 16           # slots under the current table
+        valid_after = np.minimum(len_before + 1, cap)   # a head with a free slot gains its new entry
+        announce("fused step, ragged cache, budget", M)
+        outs = []
+        for name in "ab":
+            c = ca if name == "a" else cb
+            n = c.n_pages * 16
+            score = torch.empty(n, dtype=torch.float32, device="cuda")
+            keep = torch.empty(n, dtype=torch.uint8, device="cuda")
+            kept = torch.empty(H, dtype=torch.int32, device="cuda")
+            status = torch.zeros(2, dtype=torch.int32, device="cuda")
+            t_dev = cuda(np.array([t], np.int32))
+            bud = cuda(np.array([M], np.int64))
+            out = torch.full((H * G, D), 5.0, dtype=torch.float32, device="cuda")
+            dropped = torch.full((H * G,), 5.0, dtype=torch.float32, device="cuda")
+            no, ni = tables[name][s % 2]
+            used = int(c.page_off[H].item()) * 16   # keep-plane slots under the current table
+            if name == "a":
+                tk.append(c, kv_dev(kn, "bf16"), kv_dev(vn, "bf16"), cuda(beta), t_dev, status=status[0:1])
+                tk.score_select(c, seg, t_dev, bud, score, keep, kept, status=status[1:2])
+                tk.decode_attn(c, kv_dev(qn, "bf16"), G, D ** -0.5, out, dropped, keep=keep)
+                v = tk.evict_tailfill(c, keep, 1, home_off, home_ids, no, ni, kept=kept)
+            else:
+                tk.append_score_select(c, kv_dev(kn, "bf16"), kv_dev(vn, "bf16"), cuda(beta), seg, t_dev, bud, score,
+                                       keep, kept, append_status=status[0:1], select_status=status[1:2])
+                v = tk.decode_attn_evict_tailfill(c, keep, kept, kv_dev(qn, "bf16"), G, D ** -0.5, out, dropped, 1,
+                                                  home_off, home_ids, no, ni)
+            torch.cuda.synchronize()
+            outs.append((f32_bits(score[:used].cpu().numpy()), keep[:used].cpu().numpy(), kept.cpu().numpy(),
+                         f32_bits(out.cpu().numpy()), f32_bits(dropped.cpu().numpy()), status.cpu().numpy()))
+            if name == "a":
+                ca = v
+            else:
+                cb = v
+        for x, y in zip(*outs):
+            assert np.array_equal(x, y), M
+        same_cache(ca, cb)
+        kept_np, st = outs[0][2], outs[0][5]
+        assert st.tolist() == [int((len_before >= cap).sum()), 0], M
+        assert int(kept_np.sum()) == min(M, int(valid_after.sum())), M
+        assert np.all(kept_np <= valid_after)
+        d = np.asarray(outs[0][4]).view(np.float32)
+        assert np.all(np.isfinite(d)) and np.all((d >= 0) & (d <= 1))
+        # heads that keep nothing: output 0, dropped 1
+        none = np.repeat(kept_np == 0, G)
+        o = np.asarray(outs[0][3]).view(np.float32).reshape(H * G, D)
+        assert np.all(o[none] == 0.0) and np.all(d[none] == 1.0)
