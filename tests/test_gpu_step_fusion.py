@@ -366,3 +366,37 @@ def test_fused_step_ragged_edge_cases():
         none = np.repeat(kept_np == 0, G)
         o = np.asarray(outs[0][3]).view(np.float32).reshape(H * G, D)
         assert np.all(o[none] == 0.0) and np.all(d[none] == 1.0)
+
+
+def test_append_score_select_ln_beta_hard_cases():
+    """The fused call stores ln beta as trimkv_log_beta does: the correctly
+    rounded float32 logarithm, checked on the hard-rounding inputs (ln within
+    a few float64 ulps of a float32 rounding midpoint), the special values
+    and random betas, one new entry per head of a 2,048-head cache."""
+    from test_oracle_pins import HARD_LN_INPUTS
+    w = W["tiny"].scaled(layers=1024, kv_heads=2, ctx=20, reserve=1, budget_abs=30000)
+    H = w.n_heads
+    pc = synth.build_cache(w)
+    c = upload(pc)
+    rng = np.random.default_rng(9)
+    hard = np.array(HARD_LN_INPUTS, np.uint32).view(np.float32)
+    specials = np.array([0.0, 1.0, 2 ** -149, 2 ** -126, 0.5, 1 - 2 ** -24], np.float32)
+    beta = rng.uniform(0.0, 1.0, H).astype(np.float32)
+    beta[:hard.size] = hard
+    beta[hard.size:hard.size + specials.size] = specials
+    kn = rng.standard_normal((H, w.head_dim)).astype(np.float32)
+    vn = rng.standard_normal((H, w.head_dim)).astype(np.float32)
+    n = c.n_pages * 16
+    score = torch.empty(n, dtype=torch.float32, device="cuda")
+    keep = torch.empty(n, dtype=torch.uint8, device="cuda")
+    kept = torch.empty(H, dtype=torch.int32, device="cuda")
+    announce("append+score+select, ln beta of", hard.size, "hard inputs")
+    tk.append_score_select(c, kv_dev(kn, "f32"), kv_dev(vn, "f32"), cuda(beta), cuda(np.array([0, H], np.int32)),
+                           cuda(np.array([w.ctx + 1], np.int32)), cuda(np.array([w.budget()], np.int64)), score, keep,
+                           kept)
+    torch.cuda.synchronize()
+    po, pi, ln, _, _, glnb, gpos = download_cache(c)
+    glnb_h, gpos_h = ref.gather_heads(glnb, po, pi, ln), ref.gather_heads(gpos, po, pi, ln)
+    new_lnb = np.array([glnb_h[h][-1] for h in range(H)], np.float32)
+    assert np.array_equal(f32_bits(new_lnb), f32_bits(ref.ln_beta(beta)))
+    assert all(gpos_h[h][-1] == w.ctx for h in range(H))
