@@ -877,12 +877,21 @@ __global__ void __launch_bounds__(NT) k_sel_decide(int n_heads, const float* __r
   }
 }
 
-__global__ void k_sel_headsum(int n_heads, SelWs w, double* __restrict__ keptsum) {
-  const int h = blockIdx.x * blockDim.x + threadIdx.x;
-  if (h >= n_heads) return;
+// Kept-score sum of each head: its chunks' sums added in chunk order.  One
+// wave per head: the lanes load 64 chunk sums at once, and the additions
+// run in chunk order through lane shuffles (every lane forms the same sum).
+__global__ void __launch_bounds__(256) k_sel_headsum(int n_heads, SelWs w, double* __restrict__ keptsum) {
+  const int h = blockIdx.x * (256 / WAVE) + __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+  if (h >= n_heads) return;   // per-wave exit: no block barriers
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int c0 = w.chunk_off[h], c1 = w.chunk_off[h + 1];
   double s = 0.0;
-  for (int c = w.chunk_off[h]; c < w.chunk_off[h + 1]; ++c) s += w.part[c];
-  keptsum[h] = s;
+  for (int b = c0; b < c1; b += WAVE) {
+    const double v = b + lane < c1 ? w.part[b + lane] : 0.0;
+    const int n = min(WAVE, c1 - b);
+    for (int j = 0; j < n; ++j) s += __shfl(v, j, WAVE);
+  }
+  if (lane == 0) keptsum[h] = s;
 }
 
 SelWs carve(const trimkv_cache_t* c, int n_seg, void* ws) {
@@ -992,7 +1001,7 @@ int select_kernels(const trimkv_cache_t* c, const float* score, int n_seg, const
 #undef TRIMKV_SEL_PASSES
   prof_end(st);
   if (keptsum)
-    hipLaunchKernelGGL(k_sel_headsum, dim3((unsigned)((c->n_heads + 255) / 256)), dim3(256), 0, st, c->n_heads, w,
+    hipLaunchKernelGGL(k_sel_headsum, dim3((unsigned)((c->n_heads + 3) / 4)), dim3(256), 0, st, c->n_heads, w,
                        keptsum);
   return check_launch();
 }
