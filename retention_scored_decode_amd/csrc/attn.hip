@@ -853,16 +853,23 @@ __global__ void __launch_bounds__(NT) k_attn_f32(AttnArgs a) {
 
 // mass[j] = (1/G) sum_g 2^(z2_gj - lse2_g); NaN in padding slots.
 // 64 CSR pages per block, 4 slots per thread.
+template <int GM>
 __global__ void __launch_bounds__(256) k_mass(const int32_t* __restrict__ page_off, const int32_t* __restrict__ len,
-                                              int n_heads, int group, const AttnWs w,
+                                              int n_heads, int group, int64_t n_pages, const AttnWs w,
                                               float* __restrict__ mass) {
   __shared__ PageHeads sh;
-  const int64_t total = page_off[n_heads];
   const int64_t c0 = (int64_t)blockIdx.x * 64;
-  if (c0 >= total) return;
-  const PageHeads r = block_page_heads(page_off, n_heads, c0, min(c0 + 63, total - 1), &sh);
   const int64_t c = c0 + (threadIdx.x >> 2);
   const int j0 = (threadIdx.x & 3) * 4;
+  // a page's logits depend only on the page: requested before the block's
+  // head search (pages past the pool read nothing)
+  float4 zg[GM];
+#pragma unroll
+  for (int g = 0; g < GM; ++g)
+    if (g < group && c < n_pages) zg[g] = *reinterpret_cast<const float4*>(w.logits + (c * group + g) * PAGE + j0);
+  const int64_t total = page_off[n_heads];
+  if (c0 >= total) return;
+  const PageHeads r = block_page_heads(page_off, n_heads, c0, min(c0 + 63, total - 1), &sh);
   if (c >= total) return;
   const int h = r.hf == r.hl ? r.hf : head_in_range(page_off, r, c);
   const int64_t i0 = (c - page_off[h]) * PAGE + j0;
@@ -871,13 +878,16 @@ __global__ void __launch_bounds__(256) k_mass(const int32_t* __restrict__ page_o
   float o[4] = {qnan(), qnan(), qnan(), qnan()};
   if (i0 < n) {
     float s[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int g = 0; g < group; ++g) {
-      const float4 z = *reinterpret_cast<const float4*>(w.logits + (c * group + g) * PAGE + j0);
-      const float l2 = w.lse2[(size_t)h * group + g];
-      s[0] += exp2f(z.x - l2);
-      s[1] += exp2f(z.y - l2);
-      s[2] += exp2f(z.z - l2);
-      s[3] += exp2f(z.w - l2);
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+      if (g < group) {
+        const float4 z = zg[g];
+        const float l2 = w.lse2[(size_t)h * group + g];
+        s[0] += exp2f(z.x - l2);
+        s[1] += exp2f(z.y - l2);
+        s[2] += exp2f(z.z - l2);
+        s[3] += exp2f(z.w - l2);
+      }
     }
     const float inv = 1.f / (float)group;
 #pragma unroll
@@ -1142,8 +1152,15 @@ int launch_attn_mass(const trimkv_cache_t* c, const void* q, int group, float sc
   if (rc) return rc;
   launch_merge(c, a, 0, st);
   const int64_t blocks = (c->n_pages + 63) / 64;
-  hipLaunchKernelGGL(k_mass, dim3((unsigned)blocks), dim3(256), 0, st, c->page_off, c->len, c->n_heads, group, w,
-                     mass);
+  if (group <= 4)
+    hipLaunchKernelGGL(k_mass<4>, dim3((unsigned)blocks), dim3(256), 0, st, c->page_off, c->len, c->n_heads, group,
+                       c->n_pages, w, mass);
+  else if (group <= 8)
+    hipLaunchKernelGGL(k_mass<8>, dim3((unsigned)blocks), dim3(256), 0, st, c->page_off, c->len, c->n_heads, group,
+                       c->n_pages, w, mass);
+  else
+    hipLaunchKernelGGL(k_mass<GMAX>, dim3((unsigned)blocks), dim3(256), 0, st, c->page_off, c->len, c->n_heads, group,
+                       c->n_pages, w, mass);
   return check_launch();
 }
 
