@@ -406,6 +406,11 @@ __device__ __forceinline__ uint32_t pick4(u32x4 v, int q) {
 // One running maximum per query head (shared by the four 16-lane rows) is
 // raised only when a logit exceeds it by more than RESCALE_T, a wave-uniform
 // branch; the common page costs one FMA and one exp2 per logit.
+// Where a wave's range crosses into another head (D = 128, all modes but
+// A_ERR and A_LOGITS), the next segment's first two pages, and for groups of
+// up to 8 query heads its query rows (staged in LDS), are requested during
+// the last page of the segment before, so that the crossing costs no load
+// latency.
 // ---------------------------------------------------------------------------
 template <int D, int MODE>
 __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
@@ -417,6 +422,12 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
   constexpr bool MASKED = MODE == A_MASK || MODE == A_ERR || MODE == A_GMASK;
   constexpr bool ERR = MODE == A_ERR;
   constexpr bool GATED = MODE == A_GPLAIN || MODE == A_GMASK;
+  // Segments requested ahead, during the last page of the segment before
+  // (D = 128).  Not in the error mode, whose second accumulator leaves no
+  // registers to spare, nor in the logits mode, whose ranges hold hundreds of
+  // pages, nor for D = 64, where the registers it takes would halve the
+  // blocks per compute unit.
+  constexpr bool XS = D == 128 && !ERR && !LOGITS;
   // load instructions per page; pages in flight are tracked by vmcnt.  The
   // logits mode also stores each page's logits inside the loop; those stores
   // are not counted: loads complete in issue order among themselves, so once
@@ -426,6 +437,11 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
   constexpr int PER_PAGE = LOGITS ? LPP : 2 * LPP + (GATED ? 2 : 0);
   __shared__ u32x4 lds_k[NTA / WAVE][2][16 * CH];
   __shared__ u32x4 lds_v[NTA / WAVE][2][LOGITS ? 1 : 16 * CH];
+  // the next segment's query rows (G x D bf16, row-major), one area of 128
+  // chunks per wave: rows of up to 8 query heads (larger groups load the
+  // query at the segment's start)
+  constexpr int QSL = XS ? 128 : 1;
+  __shared__ u32x4 lds_q[NTA / WAVE][QSL];
   const AttnWs& w = a.w;
   const int lane = threadIdx.x & 63, r = lane >> 4, col = lane & 15, wv = threadIdx.x >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(wv);
@@ -475,31 +491,135 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
   typedef __attribute__((address_space(1))) const void* gptr;
   typedef __attribute__((address_space(3))) void* lptr;
 
-  // physical pages of a segment's first three CSR pages: they depend only on
-  // the wave's range, so they are requested before the head is known
-  // (indices clamped into the range; a page past the segment is unused)
-  int id0 = cids[p], id1 = cids[min(p + 1, pend - 1)], id2 = cids[min(p + 2, pend - 1)];
-  int h = head_of(p);
+  // where a segment starts at CSR page s: its head (the first head from hh
+  // on whose pages reach past s), its end, its valid entries, its first two
+  // physical pages and their keep words (indices clamped into the wave's
+  // range: a page past the segment is unused); scalar loads only
+  const u32x4 all_kept_c = (u32x4){~0u, ~0u, ~0u, ~0u};
+  struct Seg { int h, send, nv, id0, id1, id2; u32x4 kw0, kw1; };
+  auto seg_at = [&](int s, int hh) -> Seg {
+    Seg g;
+    // the physical pages and keep words depend only on s: requested first
+    g.id0 = cids[s];
+    g.id1 = cids[min(s + 1, pend - 1)];
+    g.id2 = cids[min(s + 2, pend - 1)];
+    g.kw0 = g.kw1 = all_kept_c;
+    if (MASKED) {
+      const c_u32x4 ck = (c_u32x4)a.keep;   // 16 keep bytes per page
+      g.kw0 = ck[s];
+      g.kw1 = ck[min(s + 1, pend - 1)];   // unused where the segment has one page
+    }
+    int hb = pg(hh), he = pg(hh + 1), hlen = __builtin_amdgcn_readfirstlane(clen[hh]);
+    while (he <= s) {   // heads without pages hold no page
+      ++hh;
+      hb = he;
+      he = pg(hh + 1);
+      hlen = __builtin_amdgcn_readfirstlane(clen[hh]);
+    }
+    g.h = hh;
+    g.send = min(pend, he);
+    const int cnt = g.send - s, v0 = hlen - (s - hb) * PAGE;
+    g.nv = v0 < 0 ? 0 : (v0 > cnt * PAGE ? cnt * PAGE : v0);
+    return g;
+  };
+  u32x4 g_lnb[GATED ? 2 : 1], g_pos[GATED ? 2 : 1];
+  // page i's loads into tile buffer B; phys = its physical page, kw4 = its 16
+  // keep bytes (mask mode), nvv = the valid entries of its segment.  Gated
+  // modes: ln beta bits and positions of keys 4r..4r+3 of the page in
+  // register buffer B (loaded with the page, two pages in flight like the tiles)
+  auto dma = [&](auto B, int i, int64_t phys, u32x4 kw4, int nvv) {
+    constexpr int buf = decltype(B)::value;
+    const uint8_t* kpage = kbase + phys * (PAGE * D * 2);
+    const uint8_t* vpage = vbase + phys * (PAGE * D * 2);
+#pragma unroll
+    for (int u = 0; u < LPP; ++u)
+      __builtin_amdgcn_global_load_lds((gptr)(kpage + gk[u]), (lptr)(&lds_k[wu][buf][64 * u]), 16, 0, CPOL_NT);
+    if (!LOGITS) {
+      const bool full = (i + 1) * PAGE <= nvv;   // wave-uniform
+      if ((MODE == A_PLAIN || MODE == A_GPLAIN || ERR) && full) {
+#pragma unroll
+        for (int u = 0; u < LPP; ++u)
+          __builtin_amdgcn_global_load_lds((gptr)(vpage + gv[u]), (lptr)(&lds_v[wu][buf][64 * u]), 16, 0, CPOL_NT);
+      } else {
+#pragma unroll
+        for (int u = 0; u < LPP; ++u) {
+          const int row = (64 * u + lane) / CH;
+          bool need = i * PAGE + row < nvv;
+          if (MODE == A_MASK || MODE == A_GMASK) need &= ((pick4(kw4, row >> 2) >> (8 * (row & 3))) & 0xFFu) != 0;
+          // rows that take no part read zeros
+          const uint8_t* src = need ? vpage + gv[u] : reinterpret_cast<const uint8_t*>(kZeroChunks) + 16 * lane;
+          __builtin_amdgcn_global_load_lds((gptr)src, (lptr)(&lds_v[wu][buf][64 * u]), 16, 0, 0);
+        }
+      }
+    }
+    if (GATED) {   // counted in PER_PAGE: issued after the page's tiles
+      const uint32_t* mrow = a.meta + phys * (2 * PAGE) + 4 * r;
+      g_lnb[buf & (GATED ? 1 : 0)] = *reinterpret_cast<const u32x4*>(mrow);
+      g_pos[buf & (GATED ? 1 : 0)] = *reinterpret_cast<const u32x4*>(mrow + PAGE);
+    }
+  };
+  // B operand of QK MFMA u for head hq: dims 32u + 8r .. +7 of query head
+  // col.  Columns col >= G repeat query head 0: their logits, weights and
+  // outputs follow column 0's and are never stored.
+  auto load_q = [&](int hq, u32x4 (&qo)[KU]) {
+    const uint8_t* qrow = (const uint8_t*)a.q + ((size_t)hq * G + (col < G ? col : 0)) * D * 2 + 16 * r;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) qo[u] = *reinterpret_cast<const u32x4*>(qrow + 64 * u);
+  };
+  // Query rows of head hq copied into the wave's LDS area by the same
+  // asynchronous loads as the pages, so that the next segment's query is
+  // requested ahead of that segment like its pages: one load instruction per
+  // 64 chunks, lanes past the rows idle (every instruction has lane 0
+  // active, so each one is issued and counted).
+  const int qch = G * D / 8;   // 16-byte chunks of the rows
+  const bool qst = XS && qch <= QSL;
+  auto stage_q = [&](int hq) {
+    const uint8_t* qh = (const uint8_t*)a.q + (size_t)hq * G * D * 2;
+#pragma unroll
+    for (int c = 0; c < (QSL + 63) / 64; ++c) {
+      if (64 * c < qch) {   // wave-uniform
+        if (64 * c + lane < qch)
+          __builtin_amdgcn_global_load_lds((gptr)(qh + 16 * (64 * c + lane)), (lptr)(&lds_q[wu][64 * c]), 16, 0, 0);
+      }
+    }
+  };
+  // each segment's first two pages (and staged query) are requested before
+  // the segment starts: the first segment's here, each later one's during
+  // the last page of the segment before it (both tiles are free by then).
+  // The compiler's own waits do not count the asynchronous LDS loads, so a
+  // query held in registers across them would be awaited with every page in
+  // flight; staged in LDS, it is awaited by the explicit counts only.
+  Seg nx = seg_at(p, head_of(p));
+  if (XS) {
+    if (qst) stage_q(nx.h);
+    dma(std::integral_constant<int, 0>{}, 0, nx.id0, nx.kw0, nx.nv);
+    if (nx.send - p > 1) dma(std::integral_constant<int, 1>{}, 1, nx.id1, nx.kw1, nx.nv);
+  }
   while (true) {
     // ---- one head segment: CSR pages [p, send) of head h ----
-    // B operand of QK MFMA u: dims 32u + 8r .. +7 of query head col.  Columns
-    // col >= G repeat query head 0: their logits, weights and outputs follow
-    // column 0's and are never stored.  Requested first, so that the head's
-    // table loads below overlap it, and awaited before the first page load
-    // (nothing is then outstanding at the page loop but the pages).
-    u32x4 qop[KU];
-    {
-      const uint8_t* qrow = (const uint8_t*)a.q + ((size_t)h * G + (col < G ? col : 0)) * D * 2 + 16 * r;
-#pragma unroll
-      for (int u = 0; u < KU; ++u) qop[u] = *reinterpret_cast<const u32x4*>(qrow + 64 * u);
-    }
-    // the head's table words, requested together
-    const int hb = pg(h), he = pg(h + 1), hlen = __builtin_amdgcn_readfirstlane(clen[h]);
-    asm volatile("" ::: "memory");
-    const int send = min(pend, he);
+    const Seg cur = nx;
+    const int h = cur.h, send = cur.send, nv = cur.nv;
     const int page0 = p, cnt = send - p;
-    const int v0 = hlen - (p - hb) * PAGE;
-    const int nv = v0 < 0 ? 0 : (v0 > cnt * PAGE ? cnt * PAGE : v0);   // valid entries of the segment
+    u32x4 qop[KU];
+    if (qst) {
+      // the staged query rows and the segment's first page, issued in that
+      // order and followed by at most the second page's loads, have arrived
+      // once no more than one page's loads are outstanding
+      __builtin_amdgcn_s_waitcnt(wait_vm(PER_PAGE));
+      const uint32_t ql = lds_addr(&lds_q[wu][0]) + (col < G ? col : 0) * D * 2 + 16 * r;
+#pragma unroll
+      for (int u = 0; u < KU; ++u) qop[u] = lds_read_b128(ql + 64 * u);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < KU; ++u) asm volatile("" : "+v"(qop[u]));
+    } else {
+      load_q(h, qop);
+      __builtin_amdgcn_s_waitcnt(wait_vm(0));
+      if (!XS) {   // the segment's first two pages, requested only now
+        dma(std::integral_constant<int, 0>{}, 0, cur.id0, cur.kw0, nv);
+        if (cnt > 1) dma(std::integral_constant<int, 1>{}, 1, cur.id1, cur.kw1, nv);
+      }
+    }
     const c_u32x4 ckeep = (c_u32x4)(a.keep + (int64_t)page0 * PAGE);   // 16 keep bytes per page
     int t_h = 0;   // decode step of the head's segment (gated modes)
     if (GATED) {
@@ -511,6 +631,8 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
       }
       t_h = __builtin_amdgcn_readfirstlane(((c_i32)a.tseg)[lo]);
     }
+    const bool has_next = send < pend;   // wave-uniform
+    if (XS && has_next) nx = seg_at(send, h + 1);
 
     float m = -INFINITY, la = 0.f, ld = 0.f;
     float nm = INFINITY;   // -m, or +inf while m = -inf (every finite logit then forces an update)
@@ -520,50 +642,15 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int n = 0; n < (ERR ? NV : 1); ++n) acc2[n] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-    // page i's loads; phys = its physical page, kw4 = its 16 keep bytes (mask mode)
-    // gated modes: ln beta bits and positions of keys 4r..4r+3 of the page in
-    // buffer b (loaded with the page, two pages in flight like the tiles)
-    u32x4 g_lnb[GATED ? 2 : 1], g_pos[GATED ? 2 : 1];
-    auto dma = [&](auto B, int i, int64_t phys, u32x4 kw4) {
-      constexpr int buf = decltype(B)::value;
-      const uint8_t* kpage = kbase + phys * (PAGE * D * 2);
-      const uint8_t* vpage = vbase + phys * (PAGE * D * 2);
-#pragma unroll
-      for (int u = 0; u < LPP; ++u)
-        __builtin_amdgcn_global_load_lds((gptr)(kpage + gk[u]), (lptr)(&lds_k[wu][buf][64 * u]), 16, 0, CPOL_NT);
-      if (!LOGITS) {
-        const bool full = (i + 1) * PAGE <= nv;   // wave-uniform
-        if ((MODE == A_PLAIN || MODE == A_GPLAIN || ERR) && full) {
-#pragma unroll
-          for (int u = 0; u < LPP; ++u)
-            __builtin_amdgcn_global_load_lds((gptr)(vpage + gv[u]), (lptr)(&lds_v[wu][buf][64 * u]), 16, 0, CPOL_NT);
-        } else {
-#pragma unroll
-          for (int u = 0; u < LPP; ++u) {
-            const int row = (64 * u + lane) / CH;
-            bool need = i * PAGE + row < nv;
-            if (MODE == A_MASK || MODE == A_GMASK) need &= ((pick4(kw4, row >> 2) >> (8 * (row & 3))) & 0xFFu) != 0;
-            // rows that take no part read zeros
-            const uint8_t* src = need ? vpage + gv[u] : reinterpret_cast<const uint8_t*>(kZeroChunks) + 16 * lane;
-            __builtin_amdgcn_global_load_lds((gptr)src, (lptr)(&lds_v[wu][buf][64 * u]), 16, 0, 0);
-          }
-        }
-      }
-      if (GATED) {   // counted in PER_PAGE: issued after the page's tiles
-        const uint32_t* mrow = a.meta + phys * (2 * PAGE) + 4 * r;
-        g_lnb[buf & (GATED ? 1 : 0)] = *reinterpret_cast<const u32x4*>(mrow);
-        g_pos[buf & (GATED ? 1 : 0)] = *reinterpret_cast<const u32x4*>(mrow + PAGE);
-      }
-    };
-
   auto math = [&](int i, const u32x4 (&kop)[KU], const short4_t (&vop)[LOGITS ? 1 : NV], uint32_t kwr,
-                  u32x4 glnb, u32x4 gpos) {
+                  u32x4 glnb, u32x4 gpos, auto&& after_qk) {
     // ---- S = K q^T ----
     float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < KU; ++u)
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[u]),
                                                   __builtin_bit_cast(bf16x8_t, qop[u]), s, 0, 0, 0);
+    after_qk();   // the query operand is free from here on
     // base-2 offset of each logit: 0, or ln r * log2(e) with ln r formed as
     // the score kernel forms it (one fp32 product)
     float gate[4] = {0.f, 0.f, 0.f, 0.f};
@@ -682,11 +769,12 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
     // (scalar loads), so no load is issued behind a dependent table read.
     const u32x4 all_kept = (u32x4){~0u, ~0u, ~0u, ~0u};
     auto keep4 = [&](int i) -> u32x4 { return MASKED ? ckeep[i] : all_kept; };
-    int64_t id_n = id2;                                  // page of the next load (i + 2)
+    int64_t id_n = cur.id2;                                 // page of the next load (i + 2)
     u32x4 kwd_n = cnt > 2 ? keep4(2) : all_kept;         // its keep bytes
     u32x4 kwm_n = keep4(0);                              // keep bytes of the next page computed
-    auto step = [&](auto B, int i) {
-      constexpr int buf = decltype(B)::value;
+    // B: the tile buffer, i & 1 (a constant, or at run time for the last page)
+    auto step = [&](auto B, int i, auto LAST) {
+      const int buf = B;
       const u32x4 kwm = kwm_n;
       const uint32_t kwr = pick4(kwm, r);   // keep word of keys 4r..4r+3 (mask mode)
       asm volatile("" ::: "memory");
@@ -710,25 +798,38 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
         else __builtin_amdgcn_s_setprio(0);
       }
       // page i's gate words, taken before page i + 2's loads reuse their registers
-      const u32x4 glnb = g_lnb[buf & (GATED ? 1 : 0)], gpos = g_pos[buf & (GATED ? 1 : 0)];
-      if (i + 2 < cnt) dma(B, i + 2, id_n, kwd_n);
+      const u32x4 glnb = (buf & 1) ? g_lnb[GATED ? 1 : 0] : g_lnb[0];
+      const u32x4 gpos = (buf & 1) ? g_pos[GATED ? 1 : 0] : g_pos[0];
+      if constexpr (!decltype(LAST)::value) {
+        if (i + 2 < cnt) dma(B, i + 2, id_n, kwd_n, nv);
+      }
       if (i + 3 < cnt) {
         id_n = cids[page0 + i + 3];
         kwd_n = keep4(i + 3);
       }
       if (i + 1 < cnt) kwm_n = keep4(i + 1);
       asm volatile("" ::: "memory");
-      math(i, kop, vop, kwr, glnb, gpos);
+      math(i, kop, vop, kwr, glnb, gpos, [&] {
+        if constexpr (XS && decltype(LAST)::value == 1) {
+          // the segment's last page, once its logits are formed, where
+          // another segment follows: that segment's query operand, then its
+          // first two pages (both tiles are free by now)
+          if (qst) stage_q(nx.h);
+          dma(std::integral_constant<int, 0>{}, 0, nx.id0, nx.kw0, nx.nv);
+          if (nx.send - send > 1) dma(std::integral_constant<int, 1>{}, 1, nx.id1, nx.kw1, nx.nv);
+        }
+      });
     };
-    __builtin_amdgcn_s_waitcnt(wait_vm(0));   // the query operand
-    dma(std::integral_constant<int, 0>{}, 0, id0, keep4(0));
-    if (cnt > 1) dma(std::integral_constant<int, 1>{}, 1, id1, keep4(1));
-    for (int i = 0; i < cnt; i += 2) {
-      step(std::integral_constant<int, 0>{}, i);
-      if (i + 1 < cnt) step(std::integral_constant<int, 1>{}, i + 1);
-    }
+    constexpr std::integral_constant<int, 0> B0{};
+    constexpr std::integral_constant<int, 1> B1{};
+    // kinds of step: a page before the last, the last page where another
+    // segment follows, the wave's last page
+    constexpr std::integral_constant<int, 0> MID{};
+    constexpr std::integral_constant<int, 1> NEXT{};
+    constexpr std::integral_constant<int, 2> LASTSEG{};
 
     // ---- partial of this segment: the maximum is common to the four rows ----
+    auto finish = [&] {
     const size_t part = (size_t)wave + h;
     la += __shfl_xor(la, 16, WAVE);
     la += __shfl_xor(la, 32, WAVE);
@@ -757,12 +858,35 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
         }
       }
     }
+    };
+    if constexpr (!XS) {
+      for (int i = 0; i < cnt; i += 2) {
+        step(B0, i, MID);
+        if (i + 1 < cnt) step(B1, i + 1, MID);
+      }
+      finish();
+      if (!has_next) break;
+      p = send;
+      nx = seg_at(p, h + 1);
+      continue;
+    }
+    int i = 0;
+    for (; i + 2 < cnt; i += 2) {
+      step(B0, i, MID);
+      step(B1, i + 1, MID);
+    }
+    if (i + 1 < cnt) step(B0, i++, MID);
+    // the last page: one code path whichever its buffer; the wave's last
+    // segment leaves the loop on its own path, so that every path around the
+    // loop issues the next segment's loads
+    if (!has_next) {
+      step(i & 1, i, LASTSEG);
+      finish();
+      break;
+    }
+    step(i & 1, i, NEXT);
+    finish();
     p = send;
-    if (p >= pend) break;
-    id0 = cids[p];
-    id1 = cids[min(p + 1, pend - 1)];
-    id2 = cids[min(p + 2, pend - 1)];
-    h = head_of(p);
   }
 }
 
