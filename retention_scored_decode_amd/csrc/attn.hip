@@ -53,6 +53,9 @@ constexpr int FLAT_WMAX = 8192;   // most waves of one bf16 launch (workspace bo
 // blocks (two per CU), two- and one-wave blocks: those were 1-2%, 5% and 25%
 // slower.
 constexpr int NTA = 512;
+// floats of a partial's statistics per query head: the kept keys' base-2
+// maximum and sum relative to it, the dropped keys' sum and maximum
+constexpr int NST = 4;
 constexpr int SIMD_PAIR = 4;   // waves w and w ^ SIMD_PAIR share a SIMD
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -62,7 +65,7 @@ enum { A_PLAIN = 0, A_MASK = 1, A_LOGITS = 2, A_ERR = 3, A_GPLAIN = 4, A_GMASK =
 struct AttnWs {
   int32_t* item_off;   // [H + 1]          (fp32 work list)
   int4* item;          // [Tmax + 4]       (fp32 work list: head, first CSR page, valid entries, pages)
-  float* stats;        // [Smax][G][3]     partials: base-2 running max, kept sum, dropped sum
+  float* stats;        // [Smax][G][NST]   partials: base-2 kept max, kept sum, dropped sum, dropped max
   float* acc;          // [Smax][G][D]     partials: unnormalised outputs
   float* acc2;         // [Smax][G][D]     partials of the dropped keys (error mode), else null
   float* lse2;         // [H * G] base-2 LSE (mass op)
@@ -129,14 +132,16 @@ __global__ void __launch_bounds__(1024) k_attn_prep(const int32_t* __restrict__ 
 __device__ __forceinline__ int64_t flat_begin(int64_t w, int64_t W, int64_t P) { return w * P / W; }
 __device__ __forceinline__ int64_t flat_wave(int64_t p, int64_t W, int64_t P) { return ((p + 1) * W - 1) / P; }
 
-// Merge all partials of query row g of KV head h: M = max of the partial
-// maxima, kept and dropped sums rescaled to M, O rescaled and divided by the
-// kept sum.  A head without partials has an empty kept set: out = 0,
-// dropped = 1, lse = -inf.  Partials of head h: fp32 path, items
-// item_off[h] .. item_off[h+1]-1 (add = 0); bf16 path, index w + h (add = h)
-// for every wave w in [b, e), whose ranges meet the head's pages.  With fewer
-// pages than waves (every = false) waves with an empty range wrote no
-// partial and are skipped.
+// Merge all partials of query row g of KV head h.  The kept keys' sums are
+// rescaled to Mk, the largest partial kept maximum, the dropped keys' to Md,
+// the largest dropped maximum; O is rescaled like the kept sums and divided
+// by theirs, and the dropped mass is Ld 2^Md / (Lk 2^Mk + Ld 2^Md), formed
+// relative to the larger of the two.  A head without partials has an empty
+// kept set: out = 0, dropped = 1, lse = -inf.  Partials of head h: fp32
+// path, items item_off[h] .. item_off[h+1]-1 (add = 0); bf16 path, index
+// w + h (add = h) for every wave w in [b, e), whose ranges meet the head's
+// pages.  With fewer pages than waves (every = false) waves with an empty
+// range wrote no partial and are skipped.
 //
 // One wave per query row and no block barriers: lane j holds the statistics
 // of partial j, lane l accumulates output dimensions l, l + 64 (D = 128).
@@ -144,7 +149,9 @@ __device__ __forceinline__ int64_t flat_wave(int64_t p, int64_t W, int64_t P) { 
 // statistics, so a row costs one round trip.  Every sum runs in a fixed
 // order (partials ascending per lane, then a xor butterfly), so results are
 // run-to-run identical whichever wave merges.
-template <int D>
+// ERR_OK = false compiles out the error mode's dense output (callers that
+// never pass acc2).
+template <int D, bool ERR_OK = true>
 __device__ void merge_row(const AttnArgs& a, int h, int g, int b, int e, int add, bool every, int64_t P,
                           int with_out) {
   constexpr int DL = D / WAVE;   // output dimensions per lane
@@ -154,11 +161,11 @@ __device__ void merge_row(const AttnArgs& a, int h, int g, int b, int e, int add
   const int lane = threadIdx.x & (WAVE - 1);
   const int n = e - b;
   auto has = [&](int it) { return every || flat_begin(it, a.waves, P) < flat_begin(it + 1, a.waves, P); };
-  const int ss = 3 * G;   // floats between consecutive partials' statistics
-  const float* st = w.stats + (size_t)(b + add) * ss + g * 3;          // partial j: st + j * ss
+  const int ss = NST * G;   // floats between consecutive partials' statistics
+  const float* st = w.stats + (size_t)(b + add) * ss + g * NST;        // partial j: st + j * ss
   const float* ac = w.acc + ((size_t)(b + add) * G + g) * D + lane;    // partial j, dim lane + 64k: ac + j * G * D + 64k
   const float* ac2 = w.acc2 ? w.acc2 + ((size_t)(b + add) * G + g) * D + lane : nullptr;
-  const bool err = ac2 != nullptr;   // wave-uniform
+  const bool err = ERR_OK && ac2 != nullptr;   // wave-uniform
 
   // batch of MB partial outputs starting at partial j0 (zeros past the end)
   const int gs = G * D;   // floats between consecutive partials of the row
@@ -167,36 +174,46 @@ __device__ void merge_row(const AttnArgs& a, int h, int g, int b, int e, int add
 #pragma unroll
     for (int u = 0; u < MB; ++u)
 #pragma unroll
-      for (int k = 0; k < DL; ++k) {
-        const bool in = j0 + u < n;
-        const int at = (j0 + u) * gs + 64 * k;
-        v[u][k] = in ? ac[at] : 0.f;
-        v2[u][k] = in && err ? ac2[at] : 0.f;
-      }
+      for (int k = 0; k < DL; ++k) v[u][k] = j0 + u < n ? ac[(j0 + u) * gs + 64 * k] : 0.f;
+    if (err) {
+#pragma unroll
+      for (int u = 0; u < MB; ++u)
+#pragma unroll
+        for (int k = 0; k < DL; ++k) v2[u][k] = j0 + u < n ? ac2[(j0 + u) * gs + 64 * k] : 0.f;
+    }
   };
   if (with_out) load(0);   // in flight with the statistics
   // statistics of partial j = lane (+ 64 per further batch)
-  float m0 = -INFINITY, l0 = 0.f, d0 = 0.f;
+  float m0 = -INFINITY, l0 = 0.f, d0 = 0.f, md0 = -INFINITY;
   const bool v0 = lane < n && has(b + lane);
   if (v0) {
     m0 = st[lane * ss];
     l0 = st[lane * ss + 1];
     d0 = st[lane * ss + 2];
+    md0 = st[lane * ss + 3];
   }
-  float M = m0;
+  float Mk = m0, Md = md0;
   for (int j = WAVE + lane; j - lane < n; j += WAVE)
-    if (j < n && has(b + j)) M = fmaxf(M, st[j * ss]);
+    if (j < n && has(b + j)) {
+      Mk = fmaxf(Mk, st[j * ss]);
+      Md = fmaxf(Md, st[j * ss + 3]);
+    }
 #pragma unroll
-  for (int s = WAVE / 2; s > 0; s >>= 1) M = fmaxf(M, __shfl_xor(M, s, WAVE));
-  // weight of each partial: 2^(m_j - M), zero for partials without data
-  auto weight = [&](float mj, bool valid) { return valid && M != -INFINITY ? exp2f(mj - M) : 0.f; };
-  const float w0 = weight(m0, v0);
-  float la = l0 * w0, ld = d0 * w0;
+  for (int s = WAVE / 2; s > 0; s >>= 1) {
+    Mk = fmaxf(Mk, __shfl_xor(Mk, s, WAVE));
+    Md = fmaxf(Md, __shfl_xor(Md, s, WAVE));
+  }
+  // weights of each partial: 2^(m_j - Mk) and 2^(md_j - Md), zero for
+  // partials without data and for a set without a finite logit
+  auto weight = [&](float mj, float M, bool valid) { return valid && M != -INFINITY ? exp2f(mj - M) : 0.f; };
+  const float w0 = weight(m0, Mk, v0), wd0 = weight(md0, Md, v0);
+  // explicit roundings (no contraction left to the compiler), so that every
+  // instantiation of the merge gives the same bits
+  float la = __fmul_rn(l0, w0), ld = __fmul_rn(d0, wd0);
   for (int j = WAVE + lane; j - lane < n; j += WAVE) {
     if (j < n && has(b + j)) {
-      const float wj = weight(st[j * ss], true);
-      la += st[j * ss + 1] * wj;
-      ld += st[j * ss + 2] * wj;
+      la = fmaf(st[j * ss + 1], weight(st[j * ss], Mk, true), la);
+      ld = fmaf(st[j * ss + 2], weight(st[j * ss + 3], Md, true), ld);
     }
   }
 #pragma unroll
@@ -204,15 +221,20 @@ __device__ void merge_row(const AttnArgs& a, int h, int g, int b, int e, int add
     la += __shfl_xor(la, s, WAVE);
     ld += __shfl_xor(ld, s, WAVE);
   }
+  // the kept and dropped sums relative to the larger maximum T (ek, ed: the
+  // scale factors; a set without a finite logit has a zero sum)
+  const float T = fmaxf(Mk, Md);
+  const float ek = la > 0.f ? exp2f(Mk - T) : 0.f, ed = ld > 0.f ? exp2f(Md - T) : 0.f;
+  const float lat = __fmul_rn(la, ek), ldt = __fmul_rn(ld, ed), den = __fadd_rn(lat, ldt);
   if (lane == 0) {
     const int qh = h * G + g;
-    const float l2 = la > 0.f ? M + log2f(la) : -INFINITY;  // base-2 LSE of the kept set
+    const float l2 = la > 0.f ? Mk + log2f(la) : -INFINITY;  // base-2 LSE of the kept set
     const float lse = l2 * LN2;
     if (a.lse_out) a.lse_out[qh] = lse;
     if (w.lse2) w.lse2[qh] = l2;
     if (a.dropped) {
       float dm = 1.f;
-      if (la > 0.f) dm = a.lse_ref ? -expm1f(lse - a.lse_ref[qh]) : ld / (la + ld);
+      if (la > 0.f) dm = a.lse_ref ? -expm1f(lse - a.lse_ref[qh]) : ldt / den;
       a.dropped[qh] = dm;
     }
   }
@@ -220,25 +242,32 @@ __device__ void merge_row(const AttnArgs& a, int h, int g, int b, int e, int add
   float s[DL], s2[DL];
 #pragma unroll
   for (int k = 0; k < DL; ++k) s[k] = s2[k] = 0.f;
-  float wl = w0;   // weight of partial j0 - j0 % 64 + lane
+  float wl = w0, wdl = wd0;   // weights of partial j0 - j0 % 64 + lane
   for (int j0 = 0; j0 < n; j0 += MB) {
     if (j0 > 0) {
       if (j0 % WAVE == 0) {
         const int j = j0 + lane;
         const bool vj = j < n && has(b + j);
-        wl = weight(vj ? st[j * ss] : -INFINITY, vj);
+        wl = weight(vj ? st[j * ss] : -INFINITY, Mk, vj);
+        if (err) wdl = weight(vj ? st[j * ss + 3] : -INFINITY, Md, vj);
       }
       load(j0);
     }
+    // partials without data hold stale words: selected away, never multiplied
 #pragma unroll
     for (int u = 0; u < MB; ++u) {
-      // partials without data hold stale words: selected away, never multiplied
       const float wt = __shfl(wl, j0 % WAVE + u, WAVE);
       const bool use = j0 + u < n && wt != 0.f;
 #pragma unroll
-      for (int k = 0; k < DL; ++k) {
-        s[k] += use ? v[u][k] * wt : 0.f;
-        if (err) s2[k] += use ? v2[u][k] * wt : 0.f;
+      for (int k = 0; k < DL; ++k) s[k] = use ? fmaf(v[u][k], wt, s[k]) : s[k];
+    }
+    if (err) {   // the dropped keys' outputs, against their own maximum
+#pragma unroll
+      for (int u = 0; u < MB; ++u) {
+        const float wt = __shfl(wdl, j0 % WAVE + u, WAVE);
+        const bool use = j0 + u < n && wt != 0.f;
+#pragma unroll
+        for (int k = 0; k < DL; ++k) s2[k] = use ? fmaf(v2[u][k], wt, s2[k]) : s2[k];
       }
     }
   }
@@ -249,8 +278,8 @@ __device__ void merge_row(const AttnArgs& a, int h, int g, int b, int e, int add
     const float mA = la > 0.f ? s[k] / la : 0.f;
     a.out[o] = mA;
     if (err) {
-      // dense output over every key: kept and dropped sums share the maximum
-      const float mu = la + ld > 0.f ? (s[k] + s2[k]) / (la + ld) : 0.f;
+      // dense output over every key: both sums relative to T
+      const float mu = den > 0.f ? fmaf(s[k], ek, __fmul_rn(s2[k], ed)) / den : 0.f;
       if (a.mu) a.mu[o] = mu;
       q2 += (mu - mA) * (mu - mA);
     }
@@ -263,7 +292,7 @@ __device__ void merge_row(const AttnArgs& a, int h, int g, int b, int e, int add
 }
 
 // Query row `row` of the merge (wave-uniform); rows past the last return.
-template <int D>
+template <int D, bool ERR_OK = true>
 __device__ void merge_query_row(const AttnArgs& a, int row, int with_out) {
   const AttnWs& w = a.w;
   const int G = a.group;
@@ -284,14 +313,15 @@ __device__ void merge_query_row(const AttnArgs& a, int row, int with_out) {
   // waves with an empty range (fewer pages than waves) wrote no partial; with
   // at least as many pages as waves every range is nonempty (no divisions)
   const bool every = !a.waves || P >= a.waves;
-  merge_row<D>(a, h, g, b, e, add, every, P, with_out);
+  merge_row<D, ERR_OK>(a, h, g, b, e, add, every, P, with_out);
 }
 
 // Merge kernel: one wave per query row, over the partials the main kernel
-// left in the workspace.
-template <int D>
+// left in the workspace (ERR: the error mode's launches, which pass acc2).
+template <int D, bool ERR>
 __global__ void __launch_bounds__(NT) k_attn_merge(AttnArgs a, int with_out) {
-  merge_query_row<D>(a, blockIdx.x * (NT / WAVE) + __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), with_out);
+  merge_query_row<D, ERR>(a, blockIdx.x * (NT / WAVE) + __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE),
+                          with_out);
 }
 
 // The merge beside a tail-filled eviction of the same cache, in one launch:
@@ -304,7 +334,7 @@ template <int D, int ROWB>
 __global__ void __launch_bounds__(tf::NT) k_attn_merge_evict(AttnArgs a, tf::Args t, int merge_blocks) {
   __shared__ tf::LDS L;
   if ((int)blockIdx.x < merge_blocks) {   // block-uniform
-    merge_query_row<D>(a, blockIdx.x * (tf::NT / WAVE) + __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), 1);
+    merge_query_row<D, false>(a, blockIdx.x * (tf::NT / WAVE) + __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE), 1);
     return;
   }
   tf::evict_head<ROWB>(blockIdx.x - merge_blocks, t, L);
@@ -403,9 +433,12 @@ __device__ __forceinline__ uint32_t pick4(u32x4 v, int q) {
 //                 transposing LDS read; P is split into a bf16 truncation and
 //                 a bf16 remainder (two MFMAs), so each weight carries a
 //                 relative error below 2^-16.
-// One running maximum per query head (shared by the four 16-lane rows) is
-// raised only when a logit exceeds it by more than RESCALE_T, a wave-uniform
-// branch; the common page costs one FMA and one exp2 per logit.
+// One running maximum per query head (shared by the four 16-lane rows), and
+// in the mask modes a second one for the dropped keys, is raised only when a
+// logit exceeds it by more than RESCALE_T, a wave-uniform branch; the common
+// page costs one FMA and one exp2 per logit.  With its own maximum the kept
+// set's weights stay in range however far the dropped keys' logits lie above
+// them (retention gates can put them hundreds of units apart).
 // Where a wave's range crosses into another head (D = 128, all modes but
 // A_ERR and A_LOGITS), the next segment's first two pages, and for groups of
 // up to 8 query heads its query rows (staged in LDS), are requested during
@@ -413,7 +446,7 @@ __device__ __forceinline__ uint32_t pick4(u32x4 v, int q) {
 // latency.
 // ---------------------------------------------------------------------------
 template <int D, int MODE>
-__global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
+__global__ void __launch_bounds__(NTA, D == 64 ? 4 : 2) k_attn_bf16(AttnArgs a) {
   typedef Tile<D> TL;
   constexpr int CH = TL::CH, LPP = TL::LPP;
   constexpr int KU = D / 32;    // QK MFMAs per page
@@ -636,6 +669,7 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
 
     float m = -INFINITY, la = 0.f, ld = 0.f;
     float nm = INFINITY;   // -m, or +inf while m = -inf (every finite logit then forces an update)
+    float md = -INFINITY, nmd = INFINITY;   // the same for the dropped keys (mask modes)
     float4_t acc[LOGITS ? 1 : NV], acc2[ERR ? NV : 1];
 #pragma unroll
     for (int n = 0; n < (LOGITS ? 1 : NV); ++n) acc[n] = (float4_t){0.f, 0.f, 0.f, 0.f};
@@ -661,49 +695,81 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
     }
     const int i0 = i * PAGE + 4 * r;          // entry of key 4r within the item
     const bool full = (i + 1) * PAGE <= nv;   // wave-uniform
+    // keys 4r..4r+3 in the kept set (mask modes: kept and valid; the other
+    // modes keep every key).  Dropped keys are weighed against a running
+    // maximum of their own, so that a kept set far below the dropped keys
+    // keeps its relative weights instead of underflowing against them.
+    bool kj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kj[j] = !MASKED || (((kwr >> (8 * j)) & 0xFFu) && (full || i0 + j < nv));
     float pj[4];
     bool slow = !full;
     if (full) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pj[j] = fmaf(s[j], a.scale2, GATED ? gate[j] + nm : nm);
-      // NaN (gated: a -inf gate while m = -inf) takes the exact path too
+      for (int j = 0; j < 4; ++j) {
+        const float off = kj[j] ? nm : nmd;
+        pj[j] = fmaf(s[j], a.scale2, GATED ? gate[j] + off : off);
+      }
+      // NaN (gated: a -inf gate while the maximum is -inf) takes the exact path too
       slow = __any(!(fmaxf(fmaxf(pj[0], pj[1]), fmaxf(pj[2], pj[3])) <= RESCALE_T));
     }
     if (slow) {
       float z[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) z[j] = i0 + j < nv ? (GATED ? fmaf(s[j], a.scale2, gate[j]) : s[j] * a.scale2) : -INFINITY;
-      float pm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-      pm = fmaxf(pm, __shfl_xor(pm, 16, WAVE));
-      pm = fmaxf(pm, __shfl_xor(pm, 32, WAVE));   // maximum of the page for query head col
-      const float mn = fmaxf(m, pm);
+      // maxima of the page for query head col, kept and dropped keys
+      float pk = -INFINITY, pdm = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (kj[j]) pk = fmaxf(pk, z[j]);
+        else pdm = fmaxf(pdm, z[j]);
+      }
+      pk = fmaxf(pk, __shfl_xor(pk, 16, WAVE));
+      pk = fmaxf(pk, __shfl_xor(pk, 32, WAVE));
+      const float mn = fmaxf(m, pk);
       float alpha = 1.f;
       if (mn != -INFINITY) {
         alpha = exp2f(m - mn);   // 0 while m = -inf
         m = mn;
         nm = -mn;
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pj[j] = z[j] - m;
       la *= alpha;
-      ld *= alpha;
+      float alphad = 1.f;
+      if (MASKED) {
+        pdm = fmaxf(pdm, __shfl_xor(pdm, 16, WAVE));
+        pdm = fmaxf(pdm, __shfl_xor(pdm, 32, WAVE));
+        const float mnd = fmaxf(md, pdm);
+        if (mnd != -INFINITY) {
+          alphad = exp2f(md - mnd);
+          md = mnd;
+          nmd = -mnd;
+        }
+        ld *= alphad;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pj[j] = z[j] - (kj[j] ? m : md);
       if (!LOGITS) {
-        // output row g = 4r + j belongs to query head 4r + j: its factor lives in lane 4r + j
+        // output row g = 4r + j belongs to query head 4r + j: its factors live in lane 4r + j
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float aj = __shfl(alpha, 4 * r + j, WAVE);
 #pragma unroll
           for (int n = 0; n < NV; ++n) acc[n][j] *= aj;
           if (ERR) {
+            const float adj = __shfl(alphad, 4 * r + j, WAVE);
 #pragma unroll
-            for (int n = 0; n < NV; ++n) acc2[n][j] *= aj;
+            for (int n = 0; n < NV; ++n) acc2[n][j] *= adj;
           }
         }
       }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) pj[j] = __builtin_amdgcn_exp2f(pj[j]);   // exp2(-inf) = 0
-    if (slow && m == -INFINITY) pj[0] = pj[1] = pj[2] = pj[3] = 0.f;
+    if (slow) {   // a key whose set has no finite logit yet weighs nothing (-inf - -inf)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if ((kj[j] ? m : md) == -INFINITY) pj[j] = 0.f;
+    }
     if (LOGITS) {
       if (col < G) {
         float* dst = w.logits + ((int64_t)(page0 + i) * G + col) * PAGE + 4 * r;
@@ -724,11 +790,10 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
       float sk = 0.f, sd = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bool kept = ((kwr >> (8 * j)) & 0xFFu) && (full || i0 + j < nv);
-        sk += kept ? pj[j] : 0.f;
-        sd += kept ? 0.f : pj[j];
-        if (ERR) pd[j] = kept ? 0.f : pj[j];
-        if (!kept) pj[j] = 0.f;
+        sk += kj[j] ? pj[j] : 0.f;
+        sd += kj[j] ? 0.f : pj[j];
+        if (ERR) pd[j] = kj[j] ? 0.f : pj[j];
+        if (!kj[j]) pj[j] = 0.f;
       }
       la += sk;
       ld += sd;
@@ -828,7 +893,7 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
     constexpr std::integral_constant<int, 1> NEXT{};
     constexpr std::integral_constant<int, 2> LASTSEG{};
 
-    // ---- partial of this segment: the maximum is common to the four rows ----
+    // ---- partial of this segment: the maxima are common to the four rows ----
     auto finish = [&] {
     const size_t part = (size_t)wave + h;
     la += __shfl_xor(la, 16, WAVE);
@@ -836,10 +901,11 @@ __global__ void __launch_bounds__(NTA) k_attn_bf16(AttnArgs a) {
     ld += __shfl_xor(ld, 16, WAVE);
     ld += __shfl_xor(ld, 32, WAVE);
     if (r == 0 && col < G) {
-      float* st = w.stats + (part * G + col) * 3;
+      float* st = w.stats + (part * G + col) * NST;
       st[0] = m;
       st[1] = la;
       st[2] = ld;
+      st[3] = md;
     }
     if (!LOGITS) {
       // lane (r, col) holds O[query head 4r + j][dim 16n + col]
@@ -942,18 +1008,22 @@ __global__ void __launch_bounds__(NT) k_attn_f32(AttnArgs a) {
     return r;
   };
   for (int g = 0; g < G; ++g) {
+    // kept and dropped keys, each against its own maximum
     const float z = sp[g][t];
-    const float M = block_reduce(z, true);
+    const float Mk = block_reduce(kept ? z : -INFINITY, true);
+    const float Md = block_reduce(valid && !kept ? z : -INFINITY, true);
+    const float M = kept ? Mk : Md;
     const float pr = (M == -INFINITY || !valid) ? 0.f : exp2f(z - M);
     const float ka = block_reduce(kept ? pr : 0.f, false);
     const float kd = block_reduce(kept ? 0.f : pr, false);
     __syncthreads();
     sp[g][t] = kept ? pr : 0.f;
     if (t == 0) {
-      float* st = w.stats + ((size_t)item * G + g) * 3;
-      st[0] = M;
+      float* st = w.stats + ((size_t)item * G + g) * NST;
+      st[0] = Mk;
       st[1] = ka;
       st[2] = kd;
+      st[3] = Md;
     }
   }
   __syncthreads();
@@ -1080,8 +1150,14 @@ int launch_main(const trimkv_cache_t* c, AttnArgs& a, hipStream_t st) {
 // Merge launch: one wave per query row.
 void launch_merge(const trimkv_cache_t* c, const AttnArgs& a, int with_out, hipStream_t st) {
   const unsigned blocks = (unsigned)(((int64_t)c->n_heads * a.group + NT / WAVE - 1) / (NT / WAVE));
-  if (c->head_dim == 128) hipLaunchKernelGGL(k_attn_merge<128>, dim3(blocks), dim3(NT), 0, st, a, with_out);
-  else hipLaunchKernelGGL(k_attn_merge<64>, dim3(blocks), dim3(NT), 0, st, a, with_out);
+  const bool err = a.w.acc2 != nullptr;
+  if (c->head_dim == 128) {
+    if (err) hipLaunchKernelGGL((k_attn_merge<128, true>), dim3(blocks), dim3(NT), 0, st, a, with_out);
+    else hipLaunchKernelGGL((k_attn_merge<128, false>), dim3(blocks), dim3(NT), 0, st, a, with_out);
+  } else {
+    if (err) hipLaunchKernelGGL((k_attn_merge<64, true>), dim3(blocks), dim3(NT), 0, st, a, with_out);
+    else hipLaunchKernelGGL((k_attn_merge<64, false>), dim3(blocks), dim3(NT), 0, st, a, with_out);
+  }
 }
 
 // Partial slots: fp32 work items, or flat waves + heads.
@@ -1097,7 +1173,7 @@ WsLayout attn_ws_layout(const trimkv_cache_t* c, int group, int64_t slots) {
   WsLayout L;
   L.add(((int64_t)c->n_heads + 1) * 4);
   L.add((T + 4) * 16);
-  L.add(S * group * 3 * 4);
+  L.add(S * group * NST * 4);
   L.add(S * group * (int64_t)c->head_dim * 4);
   return L;
 }
@@ -1114,7 +1190,7 @@ WsLayout mass_ws_layout(const trimkv_cache_t* c, int group) {
   WsLayout L;
   L.add(((int64_t)c->n_heads + 1) * 4);
   L.add((T + 4) * 16);
-  L.add(S * group * 3 * 4);
+  L.add(S * group * NST * 4);
   L.add(0);
   L.add((int64_t)c->n_heads * group * 4);
   L.add((int64_t)group * c->n_pages * PAGE * 4);

@@ -659,6 +659,55 @@ def test_attention_edge_lengths_and_determinism():
         assert np.array_equal(f32_bits(x), f32_bits(y))           # run-to-run identical
 
 
+@pytest.mark.parametrize("group", [4, 8, 9])
+def test_attention_ranges_across_many_heads(group):
+    """Wave ranges that cross many heads: 1,200 KV heads of 0-266 entries
+    (about 10K pages, some five per wave on a 256-CU GPU), so that most
+    waves take several head segments.  Some heads have no pages at all,
+    some keep their pages with no entries, some hold one entry.  At each
+    crossing the next segment's first pages, and for G <= 8 its query rows,
+    are requested during the segment's last page; G = 9 loads the query at
+    the segment's start instead.  Plain, mask and (G = 4) retention-gated
+    modes against the float64 oracle, and run-to-run identical."""
+    rng = np.random.default_rng(1300 + group)
+    pc = synth.random_ragged_cache(1300 + group, n_heads=1200, d=128, dtype="bf16", max_len=266)
+    assert (np.diff(pc.page_off) == 0).any()   # heads without pages
+    pc.length[::53] = 0                         # pages without entries
+    pc.length[7::61] = np.minimum(pc.length[7::61], 1)
+    ov = OracleView(pc)
+    q_dev, q64 = make_q(rng, pc.n_heads * group, 128, "bf16", scale=1.5)
+    c = upload(pc)
+    sc = scale_of(128)
+    keep = [rng.random(int(n)) < 0.4 for n in pc.length]
+    plane = plane_from_heads([k.astype(np.uint8) for k in keep], pc.page_off, pc.length, pc.n_pages, 0, np.uint8)
+    announce("attn many heads plain", group)
+    a = run_attn(c, q_dev, group, sc)
+    check_attn(a, ref.decode_attn(ov.k, ov.v, q64, group, sc))
+    empty = np.repeat(pc.length == 0, group)
+    assert np.all(a[0][empty] == 0) and np.all(a[1][empty] == 1.0)
+    b = run_attn(c, q_dev, group, sc)
+    for x, y in zip(a, b):
+        assert np.array_equal(f32_bits(x), f32_bits(y))
+    announce("attn many heads mask", group)
+    check_attn(run_attn(c, q_dev, group, sc, keep_plane=plane),
+               ref.decode_attn(ov.k, ov.v, q64, group, sc, keep=keep))
+    if group == 4:
+        t = int(pc.pos.max()) + 5
+        seg = np.array([0, pc.n_heads], np.int32)
+        t_seg = np.array([t], np.int32)
+        gate = [g.astype(np.float64) for g in ov.scores(seg_t(seg, t_seg, pc.n_heads))]
+        nq = pc.n_heads * group
+        for kp in (None, keep):
+            announce("attn many heads gated", "mask" if kp is not None else "plain")
+            out = torch.full((nq, 128), np.nan, dtype=torch.float32, device="cuda")
+            dropped = torch.full((nq,), np.nan, dtype=torch.float32, device="cuda")
+            lse = torch.full((nq,), np.nan, dtype=torch.float32, device="cuda")
+            tk.decode_attn_gated(c, cuda(seg), cuda(t_seg), q_dev, group, sc, out, dropped,
+                                 keep=None if kp is None else cuda(plane), lse_out=lse)
+            check_attn(tuple(x.cpu().numpy() for x in (out, dropped, lse)),
+                       ref.decode_attn_gated(ov.k, ov.v, q64, group, sc, gate, keep=kp))
+
+
 # --------------------------------------------------------------------------
 # the eviction step end to end (a0 -> a1 -> a2 -> a4 mask -> a3 -> a4 plain)
 # --------------------------------------------------------------------------
