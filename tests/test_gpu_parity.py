@@ -708,6 +708,47 @@ def test_attention_ranges_across_many_heads(group):
                        ref.decode_attn_gated(ov.k, ov.v, q64, group, sc, gate, keep=kp))
 
 
+@pytest.mark.parametrize("dtype,d,group", [("bf16", 128, 4), ("bf16", 64, 3), ("f32", 64, 2)])
+def test_attention_extreme_logits(dtype, d, group):
+    """Queries scaled by 40, so that logits spread over hundreds of units, and
+    keep masks that keep each KV head's keys with the lowest 30% of logits
+    for its first query head (a random 30% on the odd heads): the kept set
+    lies far below the dropped keys (about 150 units for those query heads)
+    and must still be renormalised over itself, its weights taken against
+    its own maximum instead of underflowing against the dropped keys'.
+    Plain and mask modes against the float64 oracle; the error mode's dense
+    output on the bf16 cases."""
+    rng = np.random.default_rng(1500 + d + group)
+    pc = synth.random_ragged_cache(1500 + group, n_heads=9, d=d, dtype=dtype, max_len=900, min_len=40)
+    ov = OracleView(pc)
+    q_dev, q64 = make_q(rng, pc.n_heads * group, d, dtype, scale=40.0)
+    c = upload(pc)
+    sc = scale_of(d)
+    keep = []
+    for h, n in enumerate(pc.length):
+        z = ov.k[h] @ q64[h * group]
+        keep.append(z < np.quantile(z, 0.3) if h % 2 == 0 else rng.random(int(n)) < 0.3)
+    plane = plane_from_heads([k.astype(np.uint8) for k in keep], pc.page_off, pc.length, pc.n_pages, 0, np.uint8)
+    announce("attn extreme plain", dtype, d, group)
+    check_attn(run_attn(c, q_dev, group, sc), ref.decode_attn(ov.k, ov.v, q64, group, sc))
+    announce("attn extreme mask", dtype, d, group)
+    got = run_attn(c, q_dev, group, sc, keep_plane=plane)
+    want = ref.decode_attn(ov.k, ov.v, q64, group, sc, keep=keep)
+    check_attn(got, want)
+    if dtype == "bf16":
+        nq = pc.n_heads * group
+        out = torch.full((nq, d), np.nan, dtype=torch.float32, device="cuda")
+        mu = torch.full((nq, d), np.nan, dtype=torch.float32, device="cuda")
+        dropped = torch.full((nq,), np.nan, dtype=torch.float32, device="cuda")
+        err = torch.full((nq,), np.nan, dtype=torch.float32, device="cuda")
+        announce("attn extreme err", d, group)
+        tk.decode_attn_err(c, q_dev, group, sc, cuda(plane), out, dropped, err, mu=mu)
+        wmu, _, _ = ref.decode_attn(ov.k, ov.v, q64, group, sc)
+        assert np.max(np.abs(out.cpu().numpy() - want[0])) <= OUT_TOL
+        assert np.max(np.abs(mu.cpu().numpy() - wmu)) <= OUT_TOL
+        assert np.max(np.abs(dropped.cpu().numpy() - want[1])) <= DROP_TOL
+
+
 # --------------------------------------------------------------------------
 # the eviction step end to end (a0 -> a1 -> a2 -> a4 mask -> a3 -> a4 plain)
 # --------------------------------------------------------------------------
