@@ -290,7 +290,7 @@ def test_select_parity_workloads(name):
     check_select(pc, scores, seg, [w.budget()] * w.n_seg)
 
 
-KINDS = ["alpha3", "equal", "zeros", "inf", "cont", "nan"]
+KINDS = ["alpha3", "equal", "zeros", "inf", "cont", "nan", "ulps", "denorm"]
 
 
 @pytest.mark.parametrize("kind", KINDS)
@@ -311,6 +311,13 @@ def test_select_parity_adversarial(kind):
         elif kind == "nan":   # NaN ranks below every score, -inf included
             sc = [np.where(rng.random(n) < 0.2, np.nan,
                            rng.choice([-np.inf, -2.0, -0.0, 0.0, 1.5], n)).astype(np.float32) for n in lens]
+        elif kind == "ulps":   # a few units in the last place apart: one bin until the last radix pass
+            base = np.float32(-0.75).view(np.int32)
+            sc = [(base + rng.integers(0, 24, n).astype(np.int32)).view(np.float32) for n in lens]
+        elif kind == "denorm":   # subnormals of both signs beside zeros and the smallest normals
+            pool = np.array([0.0, -0.0, 1e-45, -1e-45, 3e-39, -3e-39, 1.2e-38, -1.2e-38, 1e-40, -1e-40],
+                            np.float32)
+            sc = [rng.choice(pool, n) for n in lens]
         else:
             sc = [(-rng.random(n) * 50).astype(np.float32) for n in lens]
         n_seg = int(rng.integers(1, 4))
