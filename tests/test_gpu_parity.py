@@ -674,8 +674,8 @@ def test_attention_ranges_across_many_heads(group):
     some keep their pages with no entries, some hold one entry.  At each
     crossing the next segment's first pages, and for G <= 8 its query rows,
     are requested during the segment's last page; G = 9 loads the query at
-    the segment's start instead.  Plain, mask and (G = 4) retention-gated
-    modes against the float64 oracle, and run-to-run identical."""
+    the segment's start instead.  Plain, mask and retention-gated (plain and
+    mask) modes against the float64 oracle, and run-to-run identical."""
     rng = np.random.default_rng(1300 + group)
     pc = synth.random_ragged_cache(1300 + group, n_heads=1200, d=128, dtype="bf16", max_len=266)
     assert (np.diff(pc.page_off) == 0).any()   # heads without pages
@@ -698,21 +698,20 @@ def test_attention_ranges_across_many_heads(group):
     announce("attn many heads mask", group)
     check_attn(run_attn(c, q_dev, group, sc, keep_plane=plane),
                ref.decode_attn(ov.k, ov.v, q64, group, sc, keep=keep))
-    if group == 4:
-        t = int(pc.pos.max()) + 5
-        seg = np.array([0, pc.n_heads], np.int32)
-        t_seg = np.array([t], np.int32)
-        gate = [g.astype(np.float64) for g in ov.scores(seg_t(seg, t_seg, pc.n_heads))]
-        nq = pc.n_heads * group
-        for kp in (None, keep):
-            announce("attn many heads gated", "mask" if kp is not None else "plain")
-            out = torch.full((nq, 128), np.nan, dtype=torch.float32, device="cuda")
-            dropped = torch.full((nq,), np.nan, dtype=torch.float32, device="cuda")
-            lse = torch.full((nq,), np.nan, dtype=torch.float32, device="cuda")
-            tk.decode_attn_gated(c, cuda(seg), cuda(t_seg), q_dev, group, sc, out, dropped,
-                                 keep=None if kp is None else cuda(plane), lse_out=lse)
-            check_attn(tuple(x.cpu().numpy() for x in (out, dropped, lse)),
-                       ref.decode_attn_gated(ov.k, ov.v, q64, group, sc, gate, keep=kp))
+    t = int(pc.pos.max()) + 5
+    seg = np.array([0, pc.n_heads], np.int32)
+    t_seg = np.array([t], np.int32)
+    gate = [g.astype(np.float64) for g in ov.scores(seg_t(seg, t_seg, pc.n_heads))]
+    nq = pc.n_heads * group
+    for kp in (None, keep):
+        announce("attn many heads gated", group, "mask" if kp is not None else "plain")
+        out = torch.full((nq, 128), np.nan, dtype=torch.float32, device="cuda")
+        dropped = torch.full((nq,), np.nan, dtype=torch.float32, device="cuda")
+        lse = torch.full((nq,), np.nan, dtype=torch.float32, device="cuda")
+        tk.decode_attn_gated(c, cuda(seg), cuda(t_seg), q_dev, group, sc, out, dropped,
+                             keep=None if kp is None else cuda(plane), lse_out=lse)
+        check_attn(tuple(x.cpu().numpy() for x in (out, dropped, lse)),
+                   ref.decode_attn_gated(ov.k, ov.v, q64, group, sc, gate, keep=kp))
 
 
 @pytest.mark.parametrize("dtype,d,group", [("bf16", 128, 4), ("bf16", 64, 3), ("f32", 64, 2)])
