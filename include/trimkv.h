@@ -328,7 +328,9 @@ int trimkv_decode_attn_evict_tailfill(trimkv_cache_t* cache, const uint8_t* keep
  *   lse_out[qh] = ln sum_{A} e^{z_j}                        (-inf if A is empty)
  * With lse_ref (reference log-sum-exp of a larger set no longer stored,
  * e.g. from trimkv_attn_mass), dropped[qh] = 1 - exp(lse_out - lse_ref).
- * keep and lse_ref must not both be given.
+ * keep and lse_ref must not both be given.  The kept and the dropped keys'
+ * weights are each formed against their own running maximum (fp32), so out
+ * stays the kept set's average however far the dropped logits lie above it.
  *   q:       device [n_heads * group][head_dim], same dtype as K/V
  *   group:   1 .. 16
  *   out:     device fp32 [n_heads * group][head_dim]
