@@ -878,6 +878,35 @@ def test_allocation_parity():
         assert np.array_equal(mb.cpu().numpy(), wm)
 
 
+@pytest.mark.parametrize("kind", ["magnitudes", "small_alphabet", "many_heads"])
+def test_allocation_adversarial(kind):
+    """The allocation (ContourKV section 3) on inputs that stress its fp64
+    arithmetic and its ranking: dropped masses spread over 600 decades, a
+    three-value alphabet (exact ties in the fractional parts, broken by the
+    lower head), and 4,096 heads (one block ranks them all)."""
+    rng = np.random.default_rng({"magnitudes": 31, "small_alphabet": 32, "many_heads": 33}[kind])
+    for trial in range(8):
+        if kind == "magnitudes":
+            H = int(rng.integers(2, 300))
+            ks = 10.0 ** rng.uniform(-300, 300, H)
+            ks[rng.random(H) < 0.1] = 0.0
+        elif kind == "small_alphabet":
+            H = int(rng.integers(2, 300))
+            ks = rng.choice([1.0, 2.0, 3.0], H)
+        else:
+            H = 4096
+            ks = rng.random(H)
+        ln = rng.integers(0, 3000, H).astype(np.int32)
+        B = int(rng.integers(0, int(ln.sum()) + 1)) if trial % 3 else int(ln.sum() // 2)
+        announce("allocate adversarial", kind, trial, H, B)
+        b = torch.full((H,), -1, dtype=torch.int64, device="cuda")
+        mb = torch.empty(H, dtype=torch.float64, device="cuda")
+        tk.allocate(cuda(ks, np.float64), cuda(ln, np.int32), B, b, mb)
+        wb, wm = ref.allocate(ks, ln, B)
+        assert np.array_equal(b.cpu().numpy(), wb), trial
+        assert np.array_equal(mb.cpu().numpy(), wm)
+
+
 def test_dropped_mass_budget_pipeline():
     """Top-s mass per head -> dropped mass -> budget -> per-head top-b ->
     compaction -> attention against the full-cache reference LSE."""
